@@ -1,0 +1,318 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself: closed forms,
+special cases that reduce to library routines, brute force on tiny inputs and invariants the
+pages state.  CPU only."""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from block_sparse_video_reblock_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _sdpa(Q, K, V):
+    q = torch.from_numpy(Q)[None, None]
+    k = torch.from_numpy(K)[None, None]
+    v = torch.from_numpy(V)[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(q, k, v)[0, 0].numpy()
+
+
+# ------------------------------------------------------------------ page facts (golden file)
+
+def test_page_facts_shapes():
+    """The headline shape on the node page: 72,576 video tokens = 1,134 blocks of 64."""
+    with open(os.path.join(GOLDEN, "page_facts.json")) as f:
+        facts = json.load(f)
+    wl = synth.WORKLOADS["clip10s_bf16"]
+    assert wl.tokens == facts["headline_tokens"]
+    assert wl.n_blocks == facts["headline_blocks"]
+    assert facts["headline_tokens"] == facts["headline_blocks"] * facts["block_tokens"]
+    assert O.LEAF == facts["block_tokens"]
+    for r in facts["topk_ratios"]:
+        k = O.topk_count(wl.n_blocks, r)
+        assert 1 <= k <= wl.n_blocks and k <= r * wl.n_blocks + 1e-6
+
+
+# ------------------------------------------------------- density 1.0 = dense softmax attention
+
+@pytest.mark.parametrize("mode", ["reweight", "meanpool"])
+def test_density_one_is_dense(tiny_inputs, mode):
+    wl, Q, K, V = tiny_inputs
+    nb = wl.n_blocks
+    rng = np.random.default_rng(7)
+    pq, pk = rng.permutation(wl.tokens), rng.permutation(wl.tokens)
+    lists = np.tile(np.arange(nb), (nb, 1))
+    out, lse = O.sparse_attention_head(Q, K, V, pq, pk, lists, mode=mode)
+    ref = _sdpa(Q, K, V)
+    assert np.max(np.abs(out - ref)) < 1e-12
+    lg = Q @ K.T / math.sqrt(Q.shape[1])
+    m = lg.max(axis=1)
+    assert np.max(np.abs(lse - (m + np.log(np.exp(lg - m[:, None]).sum(axis=1))))) < 1e-10
+
+
+def test_dense_helper_matches_sdpa(tiny_inputs):
+    _, Q, K, V = tiny_inputs
+    out, _ = O.dense_attention_head(Q[:300], K, V)
+    assert np.max(np.abs(out - _sdpa(Q[:300], K, V))) < 1e-12
+
+
+# --------------------------------------------------------------- Reweight: anchor and Jensen
+
+def test_anchor_restores_block_mass(tiny_inputs):
+    """For the anchor (mean) query, exp(s qa.kt_j + b_j) equals the block's exact exp-mass."""
+    wl, Q, K, V = tiny_inputs
+    s = 1 / math.sqrt(Q.shape[1])
+    pk = np.random.default_rng(1).permutation(wl.tokens)
+    kt, vt, b = O.summaries(Q, K, V, pk)
+    qa = Q.mean(axis=0)
+    Kb = K[pk].reshape(wl.n_blocks, 64, -1)
+    mass = np.exp(s * Kb @ qa).sum(axis=1)
+    assert np.max(np.abs(np.exp(s * kt @ qa + b) / mass - 1)) < 1e-12
+
+
+def test_identical_queries_make_layer_exact(tiny_inputs):
+    """If every query equals the anchor, both branches are exact and the layer equals dense
+    attention at any budget (checks summaries, the compressed branch and the merge)."""
+    wl, Q, K, V = tiny_inputs
+    Qc = np.tile(Q[123], (wl.tokens, 1))
+    rng = np.random.default_rng(3)
+    pq, pk = rng.permutation(wl.tokens), rng.permutation(wl.tokens)
+    nb = wl.n_blocks
+    lists = np.sort(np.stack([rng.choice(nb, 5, replace=False) for _ in range(nb)]), axis=1)
+    out, lse = O.sparse_attention_head(Qc, K, V, pq, pk, lists)
+    ref = _sdpa(Qc, K, V)
+    assert np.max(np.abs(out - ref)) < 1e-10
+    # compressed branch alone equals exact attention restricted to the unselected blocks
+    _, _, _, _, Oc, lc = O.sparse_attention_head(Qc, K, V, pq, pk, lists, return_branches=True)
+    mask = np.ones(nb, bool)
+    mask[lists[0]] = False
+    keys = pk.reshape(nb, 64)[mask].ravel()
+    rows = pq[:64]
+    assert np.max(np.abs(Oc[rows] - _sdpa(Qc[rows], K[keys], V[keys]))) < 1e-10
+
+
+def test_bias_is_entropy_and_meanpool_underestimates(tiny_inputs):
+    wl, Q, K, V = tiny_inputs
+    s = 1 / math.sqrt(Q.shape[1])
+    pk = np.arange(wl.tokens)
+    kt, vt, b = O.summaries(Q, K, V, pk)
+    Kb = K.reshape(wl.n_blocks, 64, -1)
+    x = s * Kb @ Q.mean(axis=0)
+    w = np.exp(x - x.max(axis=1, keepdims=True))
+    w /= w.sum(axis=1, keepdims=True)
+    ent = -(w * np.log(w)).sum(axis=1)
+    assert np.max(np.abs(b - ent)) < 1e-10
+    assert np.all(b >= 0) and np.all(b <= math.log(64) + 1e-12)
+    # Jensen: exp(mean logit) * 64 <= sum exp(logit) for every query and block
+    kbar, _, bm = O.summaries(Q, K, V, pk, mode="meanpool")
+    assert np.allclose(bm, math.log(64))
+    lg = s * np.einsum("qd,jtd->qjt", Q[:200], Kb)
+    true = np.log(np.exp(lg).sum(axis=2))
+    est = s * Q[:200] @ kbar.T + math.log(64)
+    assert np.all(true - est >= -1e-12)
+
+
+# --------------------------------------------------------------------------------- Reblock
+
+def test_reblock_perm_is_bijection_with_full_leaves(tiny_inputs):
+    wl, Q, K, V = tiny_inputs
+    pq, pk, prq, prk = O.reblock_head(Q, K)
+    for p, pr in ((pq, prq), (pk, prk)):
+        assert np.array_equal(np.sort(p), np.arange(wl.tokens))
+        leaves = p.reshape(-1, 64)
+        assert leaves.shape == (wl.n_blocks, 64)
+        assert np.all(np.diff(leaves, axis=1) > 0)       # ascending token id inside a leaf
+        assert pr.shape == (O.tree_levels(wl.n_blocks), wl.tokens)
+        assert np.array_equal(O.partition_from_projections(pr, wl.tokens), p)
+
+
+def test_reblock_invariances(tiny_inputs):
+    """The layout depends on Q, K only through Mahalanobis cosines: invariant to a common
+    rotation of Q and K, to scaling either side, and to the choice of metric factor."""
+    wl, Q, K, V = tiny_inputs
+    base = O.reblock_head(Q, K)[:2]
+    R = np.linalg.qr(np.random.default_rng(5).standard_normal((Q.shape[1],) * 2))[0]
+    for variant in (O.reblock_head(Q @ R, K @ R), O.reblock_head(3.7 * Q, 0.2 * K),
+                    O.reblock_head(Q, K, kind="cholesky")):
+        assert np.array_equal(variant[0], base[0])
+        assert np.array_equal(variant[1], base[1])
+
+
+def _naive_tree(X, M, leaf):
+    """Independent partitioner: explicit Mahalanobis-cosine Gram matrix, principal direction
+    from numpy.linalg.eigh of the centred Gram (kernel PCA), full stable sort."""
+    G = X @ M @ X.T
+    d = np.sqrt(np.diag(G))
+    Cos = G / np.outer(d, d)
+    out = [np.arange(X.shape[0])]
+    while any(g.size > leaf for g in out):
+        nxt = []
+        for ids in out:
+            m = ids.size // leaf
+            if m < 2:
+                nxt.append(ids)
+                continue
+            n = ids.size
+            H = np.eye(n) - 1.0 / n
+            Kc = H @ Cos[np.ix_(ids, ids)] @ H
+            lam, E = np.linalg.eigh(Kc)
+            e = E[:, -1]
+            i0 = np.flatnonzero(np.diag(Kc) > 1e-14)[0]
+            if e[i0] < 0:
+                e = -e
+            order = sorted(range(n), key=lambda a: (e[a], ids[a]))
+            cut = (m // 2) * leaf
+            nxt += [np.sort(ids[order[:cut]]), np.sort(ids[order[cut:]])]
+        out = nxt
+    return np.concatenate(out)
+
+
+def test_partition_matches_kernel_pca_partitioner(tiny_inputs):
+    wl, Q, K, V = tiny_inputs
+    Qs, Ks = Q[:1216], K[:1216]     # 1,216 tokens: 19 leaves, so odd groups occur
+    Mk = O.second_moment(Ks)
+    perm, _ = O.partition(O.metric_embed(Qs, Mk), 64, iters=300)
+    assert np.array_equal(perm, _naive_tree(Qs, Mk, 64))
+
+
+def _planted():
+    """12 queries in 3 tight clusters of 4 under the keys' metric, with large nuisance
+    components along directions the keys barely use (so plain cosine or the inverse metric
+    would group them differently)."""
+    rng = np.random.default_rng(11)
+    D = 4
+    K = rng.standard_normal((400, D)) * np.array([3.0, 1.0, 0.05, 0.05])
+    Mk = K.T @ K / K.shape[0]
+    Fi = np.linalg.inv(O.metric_factor(Mk, "cholesky"))
+    centres = [np.array([math.cos(a), math.sin(a), 0, 0]) for a in (0.0, 1.1, 2.9)]
+    Q, label = [], []
+    for c in range(3):
+        for _ in range(4):
+            u = centres[c] + 0.01 * rng.standard_normal(D) * np.array([1, 1, 0, 0])
+            q = Fi @ u * rng.uniform(0.5, 2.0)
+            q[2:] += rng.normal(0, 2.0, size=2)
+            Q.append(q)
+            label.append(c)
+    perm = rng.permutation(12)             # scatter the clusters over token ids
+    Q = np.array(Q)[perm]
+    label = np.array(label)[perm]
+    return Q, K, Mk, label
+
+
+def _brute_force_leaves(Q, M, leaf=4):
+    G = Q @ M @ Q.T
+    d = np.sqrt(np.diag(G))
+    dist = 1 - G / np.outer(d, d)
+    n = Q.shape[0]
+    best, arg = np.inf, None
+
+    def parts(rest):
+        if not rest:
+            yield []
+            return
+        first = rest[0]
+        for others in itertools.combinations(rest[1:], leaf - 1):
+            grp = (first,) + others
+            remaining = [r for r in rest if r not in grp]
+            for tail in parts(remaining):
+                yield [grp] + tail
+
+    for P in parts(list(range(n))):
+        cost = sum(dist[a, b] for g in P for a, b in itertools.combinations(g, 2))
+        if cost < best:
+            best, arg = cost, P
+    return sorted(tuple(sorted(g)) for g in arg)
+
+
+def test_partition_matches_brute_force_on_planted_clusters():
+    Q, K, Mk, label = _planted()
+    planted = sorted(tuple(np.flatnonzero(label == c)) for c in range(3))
+    assert _brute_force_leaves(Q, Mk) == planted
+    # the test is sensitive to the metric: plain cosine and the inverse metric disagree
+    assert _brute_force_leaves(Q, np.eye(4)) != planted
+    assert _brute_force_leaves(Q, np.linalg.inv(Mk)) != planted
+    perm_q = O.reblock_head(Q, K, leaf=4)[0]
+    assert sorted(tuple(sorted(g)) for g in perm_q.reshape(-1, 4)) == planted
+
+
+def test_split_tie_break_and_odd_sizes():
+    """Equal projections go left in ascending token id; a group of m blocks keeps floor(m/2)
+    on the left; a group with no spread splits by token id."""
+    U = np.zeros((3 * 4, 3))
+    perm, proj = O.partition(U, leaf=4)
+    assert np.array_equal(perm, np.arange(12))
+    assert np.all(proj == 0)
+    # projections given directly: one level, 3 blocks -> left gets 1 block (4 tokens)
+    p = np.array([[5, 1, 1, 1, 0, 9, 1, 2, 3, 1, 7, 0]], dtype=np.float32)
+    perm = O.partition_from_projections(np.vstack([p, np.zeros_like(p)]), 12, leaf=4)
+    assert list(perm[:4]) == [1, 2, 4, 11]
+
+
+# ----------------------------------------------------------------------------- top-K
+
+def test_topk_matches_stable_sort_brute_force():
+    rng = np.random.default_rng(2)
+    S = rng.integers(0, 6, size=(40, 23)).astype(np.float32)    # many exact ties
+    for k in (1, 5, 11, 23):
+        got = O.topk_lists(S, k)
+        for i in range(S.shape[0]):
+            ref = sorted(sorted(range(23), key=lambda j: (-float(S[i, j]), j))[:k])
+            assert list(got[i]) == ref
+
+
+def test_topk_count_rounding_and_clamp():
+    assert O.topk_count(1134, 0.1) == 113
+    assert O.topk_count(256, 0.2) == 51
+    assert O.topk_count(256, 0.3) == 76
+    assert O.topk_count(64, 0.25) == 16
+    assert O.topk_count(256, 1.0) == 256
+    assert O.topk_count(10, 0.7) == 7
+    assert O.topk_count(100, 1e-6) == 1
+
+
+def test_block_score_sums(tiny_inputs):
+    """Row sums of S are s * 64-mean of the query block dotted with nb times the key mean."""
+    wl, Q, K, V = tiny_inputs
+    rng = np.random.default_rng(4)
+    pq, pk = rng.permutation(wl.tokens), rng.permutation(wl.tokens)
+    S = O.block_scores(Q, K, pq, pk)
+    s = 1 / math.sqrt(Q.shape[1])
+    for i in (0, 7, wl.n_blocks - 1):
+        qb = Q[pq[64 * i:64 * i + 64]].sum(axis=0) / 64
+        assert abs(S[i].sum() - s * wl.n_blocks * qb @ K.mean(axis=0)) < 1e-9
+    assert abs(S.sum() - s * wl.n_blocks ** 2 * Q.mean(axis=0) @ K.mean(axis=0)) < 1e-8
+
+
+# ------------------------------------------------------- directional claims of the pages
+
+def test_recall_rises_with_density_and_reblock_beats_fixed_tiles(tiny_inputs):
+    wl, Q, K, V = tiny_inputs
+    nb = wl.n_blocks
+    pq, pk, _, _ = O.reblock_head(Q, K)
+    S = O.block_scores(Q, K, pq, pk).astype(np.float32)
+    rec = [O.recall_head(Q, K, pq, pk, O.topk_lists(S, O.topk_count(nb, r)))
+           for r in (0.1, 0.2, 0.3, 1.0)]
+    assert rec[0] < rec[1] < rec[2] < rec[3]
+    assert abs(rec[3] - 1) < 1e-12
+    fp = synth.fixed_tile_perm(wl.grid)
+    k = O.topk_count(nb, wl.topk_ratio)
+    Sf = O.block_scores(Q, K, fp, fp).astype(np.float32)
+    r_fixed = O.recall_head(Q, K, fp, fp, O.topk_lists(Sf, k))
+    r_reblock = O.recall_head(Q, K, pq, pk, O.topk_lists(S, k))
+    assert r_reblock > r_fixed + 0.05
+
+
+def test_reweight_lowers_log_mass_error(tiny_inputs):
+    wl, Q, K, V = tiny_inputs
+    pq, pk, _, _ = O.reblock_head(Q, K)
+    k = O.topk_count(wl.n_blocks, wl.topk_ratio)
+    lists = O.topk_lists(O.block_scores(Q, K, pq, pk).astype(np.float32), k)
+    e_rw = O.log_mass_error_head(Q, K, V, pq, pk, lists, mode="reweight")
+    e_mp = O.log_mass_error_head(Q, K, V, pq, pk, lists, mode="meanpool")
+    assert e_rw < e_mp
