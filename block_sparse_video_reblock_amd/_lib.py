@@ -1,0 +1,217 @@
+"""ctypes binding of libbsattn.so.  Argument marshalling only: torch supplies device memory and
+the current stream; every step of the layer runs in the library's HIP kernels.  There is no
+fallback: if the library is missing or a call fails, an exception is raised."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libbsattn.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "bsattn.h")
+
+BSA_OK, BSA_E_ARG, BSA_E_UNSUPPORTED, BSA_E_WORKSPACE, BSA_E_HIP = 0, -1, -2, -3, -4
+BSA_F32, BSA_BF16 = 0, 1
+BSA_MEANPOOL, BSA_EXACT_ONLY, BSA_COMPRESSED_ONLY = 1, 2, 4
+BLOCK = 64
+
+
+class BsaDesc(ctypes.Structure):
+    _fields_ = [("heads", ctypes.c_int32), ("tokens", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class BsaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"bsattn status {status}: {msg}")
+        self.status = status
+
+
+_P = ctypes.c_void_p
+_SIGS = {
+    "bsa_status_str": (ctypes.c_char_p, [ctypes.c_int32]),
+    "bsa_last_error": (ctypes.c_char_p, []),
+    "bsa_topk_count": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_float]),
+    "bsa_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(BsaDesc)]),
+    "bsa_reblock": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), _P, _P, _P, _P, _P, _P,
+                                     ctypes.c_size_t, _P]),
+    "bsa_select": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), _P, _P, _P, _P, ctypes.c_float,
+                                    ctypes.c_int32, _P, _P, _P, ctypes.c_size_t, _P]),
+    "bsa_sparse_attn": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), _P, _P, _P, _P, _P, _P,
+                                         ctypes.c_int32, ctypes.c_uint32, ctypes.c_float, _P, _P,
+                                         _P, ctypes.c_size_t, _P]),
+    "bsa_summaries": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), _P, _P, _P, _P, ctypes.c_uint32,
+                                       ctypes.c_float, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "bsa_partition_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int32]),
+    "bsa_reblock_from_projections": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
+                                                      ctypes.c_size_t, _P]),
+    "bsa_topk_from_scores": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P,
+                                              _P, _P]),
+}
+
+_lib = None
+
+
+def header_functions() -> list:
+    """Names of the functions include/bsattn.h declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(bsa_\w+)\s*\(", text, re.M)))
+
+
+def lib():
+    """Load libbsattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m block_sparse_video_reblock_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def check(status: int) -> None:
+    if status != BSA_OK:
+        raise BsaError(status, lib().bsa_last_error().decode())
+
+
+# ------------------------------------------------------------------------ torch helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev_ptr(t, dtype=None):
+    torch = _torch()
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"tensor dtype {t.dtype} != {dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+
+def desc_for(x) -> BsaDesc:
+    torch = _torch()
+    if x.dim() != 3:
+        raise ValueError("expected [heads][tokens][head_dim]")
+    dt = {torch.bfloat16: BSA_BF16, torch.float32: BSA_F32}.get(x.dtype)
+    if dt is None:
+        raise ValueError(f"unsupported dtype {x.dtype}")
+    return BsaDesc(x.shape[0], x.shape[1], x.shape[2], dt)
+
+
+def workspace(desc: BsaDesc, device="cuda"):
+    n = lib().bsa_workspace_bytes(ctypes.byref(desc))
+    if n == 0:
+        raise BsaError(BSA_E_ARG, lib().bsa_last_error().decode() or "invalid descriptor")
+    return _torch().empty(n, dtype=_torch().uint8, device=device)
+
+
+def topk_count(n_blocks: int, ratio: float) -> int:
+    return int(lib().bsa_topk_count(n_blocks, ratio))
+
+
+def reblock(q, k, ws=None, with_proj=False):
+    """(perm_q, perm_k[, proj]) int32 [H][N] (and float [H][2][levels][N])."""
+    torch = _torch()
+    d = desc_for(q)
+    ws = workspace(d, q.device) if ws is None else ws
+    H, N = q.shape[0], q.shape[1]
+    perm_q = torch.empty(H, N, dtype=torch.int32, device=q.device)
+    perm_k = torch.empty_like(perm_q)
+    levels = max(0, (N // BLOCK - 1).bit_length())
+    proj = torch.empty(H, 2, levels, N, dtype=torch.float32, device=q.device) if with_proj else None
+    check(lib().bsa_reblock(ctypes.byref(d), _dev_ptr(q, q.dtype), _dev_ptr(k, q.dtype),
+                            _dev_ptr(perm_q), _dev_ptr(perm_k), _dev_ptr(proj), _dev_ptr(ws),
+                            ws.numel(), _stream()))
+    return (perm_q, perm_k, proj) if with_proj else (perm_q, perm_k)
+
+
+def select(q, k, perm_q, perm_k, topk_ratio=0.0, topk_blocks=0, ws=None, with_scores=False):
+    """lists int32 [H][nb][K] (and scores float [H][nb][nb])."""
+    torch = _torch()
+    d = desc_for(q)
+    ws = workspace(d, q.device) if ws is None else ws
+    H, nb = q.shape[0], q.shape[1] // BLOCK
+    K = topk_blocks if topk_blocks > 0 else topk_count(nb, topk_ratio)
+    if K < 1:
+        raise BsaError(BSA_E_ARG, f"topk_ratio {topk_ratio} is not in (0, 1]")
+    lists = torch.empty(H, nb, K, dtype=torch.int32, device=q.device)
+    scores = torch.empty(H, nb, nb, dtype=torch.float32, device=q.device) if with_scores else None
+    check(lib().bsa_select(ctypes.byref(d), _dev_ptr(q, q.dtype), _dev_ptr(k, q.dtype),
+                           _dev_ptr(perm_q, torch.int32), _dev_ptr(perm_k, torch.int32),
+                           float(topk_ratio), int(topk_blocks), _dev_ptr(lists), _dev_ptr(scores),
+                           _dev_ptr(ws), ws.numel(), _stream()))
+    return (lists, scores) if with_scores else lists
+
+
+def sparse_attn(q, k, v, perm_q, perm_k, lists, flags=0, scale=0.0, ws=None, with_lse=False,
+                out=None):
+    torch = _torch()
+    d = desc_for(q)
+    ws = workspace(d, q.device) if ws is None else ws
+    o = torch.empty_like(q) if out is None else out
+    lse = torch.empty(q.shape[0], q.shape[1], dtype=torch.float32, device=q.device) \
+        if with_lse else None
+    check(lib().bsa_sparse_attn(ctypes.byref(d), _dev_ptr(q, q.dtype), _dev_ptr(k, q.dtype),
+                                _dev_ptr(v, q.dtype), _dev_ptr(perm_q, torch.int32),
+                                _dev_ptr(perm_k, torch.int32), _dev_ptr(lists, torch.int32),
+                                int(lists.shape[-1]), int(flags), float(scale),
+                                _dev_ptr(o, q.dtype), _dev_ptr(lse), _dev_ptr(ws), ws.numel(),
+                                _stream()))
+    return (o, lse) if with_lse else o
+
+
+def summaries(q, k, v, perm_k, flags=0, scale=0.0, ws=None):
+    """fp32 (kt [H][nb][D], vt [H][nb][D], bias [H][nb])."""
+    torch = _torch()
+    d = desc_for(q)
+    ws = workspace(d, q.device) if ws is None else ws
+    H, N, D = q.shape
+    nb = N // BLOCK
+    kt = torch.empty(H, nb, D, dtype=torch.float32, device=q.device)
+    vt = torch.empty_like(kt)
+    bias = torch.empty(H, nb, dtype=torch.float32, device=q.device)
+    check(lib().bsa_summaries(ctypes.byref(d), _dev_ptr(q, q.dtype), _dev_ptr(k, q.dtype),
+                              _dev_ptr(v, q.dtype), _dev_ptr(perm_k, torch.int32), int(flags),
+                              float(scale), _dev_ptr(kt), _dev_ptr(vt), _dev_ptr(bias),
+                              _dev_ptr(ws), ws.numel(), _stream()))
+    return kt, vt, bias
+
+
+def reblock_from_projections(proj):
+    """proj float [P][levels][N] (by token id) -> perm int32 [P][N]."""
+    torch = _torch()
+    P, _, N = proj.shape
+    n = lib().bsa_partition_workspace_bytes(P, N)
+    if n == 0:
+        raise BsaError(BSA_E_ARG, "invalid problem shape")
+    ws = torch.empty(n, dtype=torch.uint8, device=proj.device)
+    perm = torch.empty(P, N, dtype=torch.int32, device=proj.device)
+    check(lib().bsa_reblock_from_projections(P, N, _dev_ptr(proj, torch.float32), _dev_ptr(perm),
+                                             _dev_ptr(ws), n, _stream()))
+    return perm
+
+
+def topk_from_scores(scores, topk):
+    """scores float [rows][nb] -> lists int32 [rows][topk]."""
+    torch = _torch()
+    rows, nb = scores.shape
+    lists = torch.empty(rows, topk, dtype=torch.int32, device=scores.device)
+    check(lib().bsa_topk_from_scores(rows, nb, topk, _dev_ptr(scores, torch.float32),
+                                     _dev_ptr(lists), _stream()))
+    return lists

@@ -1,0 +1,370 @@
+// C ABI of the Spark-Attn layer: argument validation (on the host, before any HIP call),
+// workspace carving and launch sequencing.  The operations themselves are documented in
+// include/bsattn.h; every step runs in the HIP kernels of this directory.
+#include "bsattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "internal.h"
+#include "tree.h"
+
+namespace {
+
+thread_local char g_err[320] = "";
+
+bsa_status fail(bsa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bsa_status ok() {
+  g_err[0] = '\0';
+  return BSA_OK;
+}
+
+bsa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(BSA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Architecture check, cached per device.  BSATTN_ARCH_OVERRIDE replaces the queried name (used
+// by the host tests to exercise the rejection path without a GPU).
+bsa_status check_device() {
+  const char* ovr = std::getenv("BSATTN_ARCH_OVERRIDE");
+  if (ovr != nullptr) {
+    if (std::strncmp(ovr, "gfx950", 6) != 0)
+      return fail(BSA_E_UNSUPPORTED, "device architecture %s is not gfx950", ovr);
+    return ok();
+  }
+  static std::atomic<int> cache[64];  // 0 unknown, 1 gfx950, 2 other
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(BSA_E_UNSUPPORTED, "device index %d out of range", dev);
+  int c = cache[dev].load();
+  if (c == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDeviceProperties");
+    c = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    cache[dev].store(c);
+  }
+  if (c != 1) return fail(BSA_E_UNSUPPORTED, "device %d is not gfx950", dev);
+  return ok();
+}
+
+bool is_bf16(const bsa_desc* d) { return d->dtype == BSA_BF16; }
+
+bsa_status check_desc(const bsa_desc* d) {
+  if (d == nullptr) return fail(BSA_E_ARG, "desc is null");
+  if (d->heads < 1) return fail(BSA_E_ARG, "heads = %d must be >= 1", d->heads);
+  if (d->tokens < BSA_BLOCK || d->tokens % BSA_BLOCK != 0)
+    return fail(BSA_E_ARG, "tokens = %d must be a positive multiple of 64", d->tokens);
+  if (d->tokens > BSA_MAX_TOKENS)
+    return fail(BSA_E_ARG, "tokens = %d exceeds %d", d->tokens, BSA_MAX_TOKENS);
+  if (d->dtype != BSA_F32 && d->dtype != BSA_BF16)
+    return fail(BSA_E_UNSUPPORTED, "dtype %d is not supported", d->dtype);
+  if (!((d->dtype == BSA_BF16 && d->head_dim == 128) || (d->dtype == BSA_F32 && d->head_dim == 64)))
+    return fail(BSA_E_UNSUPPORTED, "(dtype %s, head_dim %d) is not supported; use (bf16, 128) "
+                "or (f32, 64)", d->dtype == BSA_BF16 ? "bf16" : "f32", d->head_dim);
+  if ((int64_t)d->heads * d->tokens > (int64_t)1 << 30)
+    return fail(BSA_E_ARG, "heads * tokens = %lld is too large",
+                (long long)d->heads * d->tokens);
+  return ok();
+}
+
+float resolve_scale(const bsa_desc* d, float scale) {
+  return scale == 0.f ? 1.f / std::sqrt(float(d->head_dim)) : scale;
+}
+
+// ----------------------------------------------------------------- workspace layouts
+struct AttnWs {
+  size_t anchor_partial, anchor, kt, vt, bias, ktsw, vtsw, ksw, vsw, total;
+};
+
+AttnWs attn_layout(const bsa_desc* d) {
+  const size_t H = d->heads, N = d->tokens, D = d->head_dim, nb = N / 64;
+  const size_t nt = bsa::summary_tiles(int(nb));
+  AttnWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
+  w.anchor_partial = take(H * bsa::ceil_div(long(N), bsa::kColChunk) * D * 4);
+  w.anchor = take(H * D * 4);
+  w.kt = take(H * nb * D * 4);
+  w.vt = take(H * nb * D * 4);
+  w.bias = take(H * nt * 64 * 4);
+  if (is_bf16(d)) {
+    w.ktsw = take(H * nt * 64 * D * 2);
+    w.vtsw = take(H * nt * 64 * D * 2);
+    w.ksw = take(H * N * D * 2);
+    w.vsw = take(H * N * D * 2);
+  }
+  w.total = off;
+  return w;
+}
+
+struct SelWs {
+  size_t qm, km, scores, total;
+};
+
+SelWs select_layout(const bsa_desc* d) {
+  const size_t H = d->heads, N = d->tokens, D = d->head_dim, nb = N / 64;
+  SelWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
+  w.qm = take(H * nb * D * 4);
+  w.km = take(H * nb * D * 4);
+  w.scores = take(H * nb * nb * 4);
+  w.total = off;
+  return w;
+}
+
+char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+bsa_status check_ws(const void* ws, size_t have, size_t need) {
+  if (have < need)
+    return fail(BSA_E_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", have,
+                need);
+  if (need > 0 && ws == nullptr) return fail(BSA_E_ARG, "workspace pointer is null");
+  return ok();
+}
+
+// anchor + summaries into the attention workspace (shared by bsa_summaries / bsa_sparse_attn)
+hipError_t run_summaries(const bsa_desc* d, const AttnWs& L, void* ws, const void* q,
+                         const void* k, const void* v, const int32_t* perm_k, bool meanpool,
+                         float scale, float* kt, float* vt, float* bias, int ldb, bool swizzle,
+                         hipStream_t s) {
+  const bool bf = is_bf16(d);
+  float* anchor = reinterpret_cast<float*>(at(ws, L.anchor));
+  hipError_t e = hipSuccess;
+  if (!meanpool) {
+    e = bsa::launch_anchor(bf, q, d->heads, d->tokens, d->head_dim,
+                           reinterpret_cast<float*>(at(ws, L.anchor_partial)), anchor, s);
+    if (e != hipSuccess) return e;
+  }
+  return bsa::launch_summaries(bf, k, v, perm_k, anchor, d->heads, d->tokens, d->head_dim, scale,
+                               meanpool, kt, vt, bias, ldb, swizzle ? at(ws, L.ksw) : nullptr,
+                               swizzle ? at(ws, L.vsw) : nullptr, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* bsa_status_str(int32_t st) {
+  switch (st) {
+    case BSA_OK: return "ok";
+    case BSA_E_ARG: return "invalid argument";
+    case BSA_E_UNSUPPORTED: return "unsupported";
+    case BSA_E_WORKSPACE: return "workspace too small";
+    case BSA_E_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* bsa_last_error(void) { return g_err; }
+
+int32_t bsa_topk_count(int32_t n_blocks, float ratio) {
+  if (n_blocks < 1 || !(ratio > 0.f && ratio <= 1.f)) return -1;
+  long k = (long)std::floor(double(ratio) * double(n_blocks) + 1e-6);
+  if (k < 1) k = 1;
+  if (k > n_blocks) k = n_blocks;
+  return int32_t(k);
+}
+
+size_t bsa_workspace_bytes(const bsa_desc* d) {
+  if (check_desc(d) != BSA_OK) return 0;
+  size_t a = attn_layout(d).total, s = select_layout(d).total;
+  size_t r = bsa::reblock_ws_bytes(d->heads, d->tokens, d->head_dim);
+  size_t m = a > s ? a : s;
+  return m > r ? m : r;
+}
+
+bsa_status bsa_reblock(const bsa_desc* d, const void* q, const void* k, int32_t* perm_q,
+                       int32_t* perm_k, float* proj_opt, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  bsa_status st = check_desc(d);
+  if (st != BSA_OK) return st;
+  if (!q || !k || !perm_q || !perm_k) return fail(BSA_E_ARG, "null tensor pointer");
+  st = check_ws(ws, ws_bytes, bsa::reblock_ws_bytes(d->heads, d->tokens, d->head_dim));
+  if (st != BSA_OK) return st;
+  st = check_device();
+  if (st != BSA_OK) return st;
+  return hip_status(bsa::launch_reblock(is_bf16(d), q, k, d->heads, d->tokens, d->head_dim,
+                                        perm_q, perm_k, proj_opt, ws, stream),
+                    "reblock launch");
+}
+
+bsa_status bsa_select(const bsa_desc* d, const void* q, const void* k, const int32_t* perm_q,
+                      const int32_t* perm_k, float topk_ratio, int32_t topk_blocks,
+                      int32_t* lists, float* scores_opt, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  bsa_status st = check_desc(d);
+  if (st != BSA_OK) return st;
+  if (!q || !k || !perm_q || !perm_k || !lists) return fail(BSA_E_ARG, "null tensor pointer");
+  const int nb = d->tokens / BSA_BLOCK;
+  int K;
+  if (topk_blocks > 0) {
+    if (topk_blocks > nb) return fail(BSA_E_ARG, "topk_blocks = %d exceeds %d blocks",
+                                      topk_blocks, nb);
+    K = topk_blocks;
+  } else {
+    if (topk_blocks < 0) return fail(BSA_E_ARG, "topk_blocks = %d is negative", topk_blocks);
+    K = bsa_topk_count(nb, topk_ratio);
+    if (K < 1) return fail(BSA_E_ARG, "topk_ratio = %g is not in (0, 1]", double(topk_ratio));
+  }
+  const SelWs L = select_layout(d);
+  st = check_ws(ws, ws_bytes, L.total);
+  if (st != BSA_OK) return st;
+  st = check_device();
+  if (st != BSA_OK) return st;
+  const bool bf = is_bf16(d);
+  float* qm = reinterpret_cast<float*>(at(ws, L.qm));
+  float* km = reinterpret_cast<float*>(at(ws, L.km));
+  float* S = scores_opt ? scores_opt : reinterpret_cast<float*>(at(ws, L.scores));
+  hipError_t e = bsa::launch_block_means(bf, q, perm_q, d->heads, d->tokens, d->head_dim, qm,
+                                         stream);
+  if (e == hipSuccess)
+    e = bsa::launch_block_means(bf, k, perm_k, d->heads, d->tokens, d->head_dim, km, stream);
+  if (e == hipSuccess)
+    e = bsa::launch_block_scores(qm, km, d->heads, nb, d->head_dim,
+                                 1.f / std::sqrt(float(d->head_dim)), S, stream);
+  if (e == hipSuccess) e = bsa::launch_topk(S, d->heads * nb, nb, K, lists, stream);
+  return hip_status(e, "select launch");
+}
+
+bsa_status bsa_summaries(const bsa_desc* d, const void* q, const void* k, const void* v,
+                         const int32_t* perm_k, uint32_t flags, float scale, float* kt,
+                         float* vt, float* bias, void* ws, size_t ws_bytes, hipStream_t stream) {
+  bsa_status st = check_desc(d);
+  if (st != BSA_OK) return st;
+  if (!q || !k || !v || !perm_k || !kt || !vt || !bias)
+    return fail(BSA_E_ARG, "null tensor pointer");
+  if (flags & ~uint32_t(BSA_MEANPOOL)) return fail(BSA_E_ARG, "unknown flags 0x%x", flags);
+  if (!(std::isfinite(scale) && scale >= 0.f)) return fail(BSA_E_ARG, "bad scale %g", scale);
+  const AttnWs L = attn_layout(d);
+  st = check_ws(ws, ws_bytes, L.total);
+  if (st != BSA_OK) return st;
+  st = check_device();
+  if (st != BSA_OK) return st;
+  return hip_status(run_summaries(d, L, ws, q, k, v, perm_k, (flags & BSA_MEANPOOL) != 0,
+                                  resolve_scale(d, scale), kt, vt, bias, d->tokens / BSA_BLOCK,
+                                  false, stream),
+                    "summaries launch");
+}
+
+bsa_status bsa_sparse_attn(const bsa_desc* d, const void* q, const void* k, const void* v,
+                           const int32_t* perm_q, const int32_t* perm_k, const int32_t* lists,
+                           int32_t topk, uint32_t flags, float scale, void* o, float* lse_opt,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  bsa_status st = check_desc(d);
+  if (st != BSA_OK) return st;
+  if (!q || !k || !v || !perm_q || !perm_k || !lists || !o)
+    return fail(BSA_E_ARG, "null tensor pointer");
+  const int nb = d->tokens / BSA_BLOCK;
+  if (topk < 1 || topk > nb) return fail(BSA_E_ARG, "topk = %d is not in [1, %d]", topk, nb);
+  const uint32_t known = BSA_MEANPOOL | BSA_EXACT_ONLY | BSA_COMPRESSED_ONLY;
+  if (flags & ~known) return fail(BSA_E_ARG, "unknown flags 0x%x", flags);
+  if ((flags & BSA_EXACT_ONLY) && (flags & BSA_COMPRESSED_ONLY))
+    return fail(BSA_E_ARG, "BSA_EXACT_ONLY and BSA_COMPRESSED_ONLY are exclusive");
+  if (!(std::isfinite(scale) && scale >= 0.f)) return fail(BSA_E_ARG, "bad scale %g", scale);
+  const AttnWs L = attn_layout(d);
+  st = check_ws(ws, ws_bytes, L.total);
+  if (st != BSA_OK) return st;
+  st = check_device();
+  if (st != BSA_OK) return st;
+
+  const bool bf = is_bf16(d);
+  const float sc = resolve_scale(d, scale);
+  const int nt = bsa::summary_tiles(nb);
+  float* kt = reinterpret_cast<float*>(at(ws, L.kt));
+  float* vt = reinterpret_cast<float*>(at(ws, L.vt));
+  float* bias = reinterpret_cast<float*>(at(ws, L.bias));
+  hipError_t e = run_summaries(d, L, ws, q, k, v, perm_k, (flags & BSA_MEANPOOL) != 0, sc, kt,
+                               vt, bias, nt * 64, bf, stream);
+  if (e == hipSuccess && bf)
+    e = bsa::launch_summary_tiles(kt, vt, bias, d->heads, nb, at(ws, L.ktsw), at(ws, L.vtsw),
+                                  stream);
+  if (e != hipSuccess) return hip_status(e, "summaries launch");
+  bsa::AttnLaunch a{};
+  a.H = d->heads;
+  a.N = d->tokens;
+  a.nb = nb;
+  a.topk = topk;
+  a.n_exact = (flags & BSA_COMPRESSED_ONLY) ? 0 : topk;
+  a.n_comp = (flags & BSA_EXACT_ONLY) ? 0 : nt;
+  a.scale = sc;
+  a.q = q;
+  a.perm_q = perm_q;
+  a.lists = lists;
+  a.bias = bias;
+  a.o = o;
+  a.lse = lse_opt;
+  if (bf) {
+    a.ksw = at(ws, L.ksw);
+    a.vsw = at(ws, L.vsw);
+    a.ktsw = at(ws, L.ktsw);
+    a.vtsw = at(ws, L.vtsw);
+    e = bsa::launch_attn_bf16(a, stream);
+  } else {
+    a.k = k;
+    a.v = v;
+    a.perm_k = perm_k;
+    a.kt = kt;
+    a.vt = vt;
+    e = bsa::launch_attn_f32(a, stream);
+  }
+  return hip_status(e, "attention launch");
+}
+
+size_t bsa_partition_workspace_bytes(int32_t problems, int32_t tokens) {
+  if (problems < 1 || tokens < BSA_BLOCK || tokens % BSA_BLOCK || tokens > BSA_MAX_TOKENS)
+    return 0;
+  return bsa::partition_ws_bytes(problems, tokens);
+}
+
+bsa_status bsa_reblock_from_projections(int32_t problems, int32_t tokens, const float* proj,
+                                        int32_t* perm, void* ws, size_t ws_bytes,
+                                        hipStream_t stream) {
+  if (problems < 1) return fail(BSA_E_ARG, "problems = %d must be >= 1", problems);
+  if (tokens < BSA_BLOCK || tokens % BSA_BLOCK || tokens > BSA_MAX_TOKENS)
+    return fail(BSA_E_ARG, "tokens = %d must be a positive multiple of 64 up to %d", tokens,
+                BSA_MAX_TOKENS);
+  if ((int64_t)problems * tokens > (int64_t)1 << 30)
+    return fail(BSA_E_ARG, "problems * tokens is too large");
+  if (!perm || (!proj && bsa::tree_levels(tokens / BSA_BLOCK) > 0))
+    return fail(BSA_E_ARG, "null tensor pointer");
+  bsa_status st = check_ws(ws, ws_bytes, bsa::partition_ws_bytes(problems, tokens));
+  if (st != BSA_OK) return st;
+  st = check_device();
+  if (st != BSA_OK) return st;
+  return hip_status(bsa::launch_partition_from_proj(problems, tokens, proj, perm, ws, stream),
+                    "partition launch");
+}
+
+bsa_status bsa_topk_from_scores(int32_t rows, int32_t n_blocks, int32_t topk,
+                                const float* scores, int32_t* lists, hipStream_t stream) {
+  if (rows < 1 || n_blocks < 1) return fail(BSA_E_ARG, "rows and n_blocks must be >= 1");
+  if (topk < 1 || topk > n_blocks)
+    return fail(BSA_E_ARG, "topk = %d is not in [1, %d]", topk, n_blocks);
+  if ((int64_t)rows * n_blocks > (int64_t)1 << 31) return fail(BSA_E_ARG, "too many scores");
+  if (!scores || !lists) return fail(BSA_E_ARG, "null tensor pointer");
+  bsa_status st = check_device();
+  if (st != BSA_OK) return st;
+  return hip_status(bsa::launch_topk(scores, rows, n_blocks, topk, lists, stream),
+                    "top-K launch");
+}
+
+}  // extern "C"

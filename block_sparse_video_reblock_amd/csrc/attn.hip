@@ -1,0 +1,384 @@
+// Two-branch block-sparse attention for gfx950: exact branch over the selected key blocks,
+// compressed branch over the anchor-weighted block summaries, log-sum-exp merge and the
+// inverse query permutation, in one kernel.
+//
+// [comfyui-wiki.com "Spark-H3 ...", "What Spark-Attn changes"]: an exact branch fully computes
+// the top-ranked key/value blocks while a compressed branch covers the rest; Spark-Reweight
+// replaces mean-pooled summaries by weighted summaries plus a log-mass bias.
+// [comfy.icu "MiniMax H3 Spark Attention (SM89)", "What it's doing under the hood"]: the
+// approximate branch keeps a real Q per query and downsamples only K/V.
+//
+// Both branches are softmax attentions of the same 64 queries, so a single online softmax over
+// the exact key tiles followed by the summary tiles (selected blocks masked to -inf) is the
+// log-sum-exp merge of the two branch results.
+//
+// bf16 kernel layout (D = 128): one workgroup of 4 waves per (head, query block).  Every wave
+// keeps all 64 queries of the block in registers and takes every 4th tile of the work list
+// (exact tiles first, then summary tiles), so the waves run independent online softmaxes that
+// are merged at the end.  Scores are computed transposed, S^T = K Q^T, with
+// v_mfma_f32_32x32x16_bf16: the accumulator layout of S^T is then directly the B operand of
+// O^T = V^T P^T.  K/V tiles arrive pre-swizzled (see summaries.hip) so that every wave load
+// is 1 KiB contiguous and no LDS transpose is needed.
+#include "common.h"
+#include "internal.h"
+
+namespace bsa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kMaxSelWords = (1 << 22) / 64 / 32;   // bitmap words for the largest nb
+
+BSA_DEV bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+BSA_DEV bf16x8_t pack8(const f32x16_t& s, int base) {
+  uint4 u;
+  u.x = pack_bf16x2(s[base + 0], s[base + 1]);
+  u.y = pack_bf16x2(s[base + 2], s[base + 3]);
+  u.z = pack_bf16x2(s[base + 4], s[base + 5]);
+  u.w = pack_bf16x2(s[base + 6], s[base + 7]);
+  return as_bf16x8(u);
+}
+
+// Map workgroup ids so that each XCD (ids are dealt round-robin over 8 XCDs) processes a
+// contiguous range of (head, query block) pairs: neighbouring query blocks of one head (tree
+// neighbours, which select overlapping key blocks) then share that XCD's L2.
+BSA_DEV int xcd_remap(int bid, int total) {
+  const int q = total >> 3, r = total & 7;
+  const int x = bid & 7, k = bid >> 3;
+  return x * q + min(x, r) + k;
+}
+
+__global__ __launch_bounds__(256, 1) void k_attn_bf16(
+    const uint16_t* __restrict__ q, const int32_t* __restrict__ perm_q,
+    const uint4* __restrict__ ksw, const uint4* __restrict__ vsw,
+    const uint4* __restrict__ ktsw, const uint4* __restrict__ vtsw,
+    const float* __restrict__ bias, const int32_t* __restrict__ lists, int H, int N, int nb,
+    int topk, int n_exact, int n_comp, float scale_log2, uint16_t* __restrict__ o,
+    float* __restrict__ lse) {
+  constexpr int D = 128;
+  __shared__ uint32_t sel_bits[kMaxSelWords];
+  __shared__ float sm_m[4][64];
+  __shared__ float sm_l[4][64];
+  __shared__ float sm_o[64 * 129];
+
+  const int logical = xcd_remap(blockIdx.x, H * nb);
+  const int h = logical / nb, i = logical - h * nb;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int ntiles = summary_tiles(nb);
+  const int32_t* list = lists + ((size_t)h * nb + i) * topk;
+
+  // bitmap of this query block's selected key blocks (masks them in the compressed branch)
+  const int words = (nb + 31) >> 5;
+  for (int w = tid; w < words; w += 256) sel_bits[w] = 0u;
+  __syncthreads();
+  for (int t = tid; t < topk; t += 256) {
+    const int j = list[t];
+    atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
+  }
+
+  // queries of the block, as the B operand of S^T = K Q^T: lane holds query 32n + l32,
+  // head-dim elements 16c + 8g .. +8
+  const int32_t* pq = perm_q + (size_t)h * N + (size_t)i * kBlk;
+  bf16x8_t qr[2][8];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int tok = pq[32 * n + l32];
+    const uint4* row = reinterpret_cast<const uint4*>(q + ((size_t)h * N + tok) * D);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) qr[n][c] = as_bf16x8(row[2 * c + g]);
+  }
+  __syncthreads();
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][n][r] = 0.f;
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.f, 0.f};
+
+  const int n_items = n_exact + n_comp;
+  const float* bias_h = bias + (size_t)h * ntiles * 64;
+  for (int it = wave; it < n_items; it += 4) {
+    const bool exact = it < n_exact;
+    const uint4 *kb, *vb;
+    int key0 = 0;
+    if (exact) {
+      const size_t blk = (size_t)h * nb + list[it];
+      kb = ksw + blk * 1024;
+      vb = vsw + blk * 1024;
+    } else {
+      const int tau = it - n_exact;
+      const size_t blk = (size_t)h * ntiles + tau;
+      kb = ktsw + blk * 1024;
+      vb = vtsw + blk * 1024;
+      key0 = tau * 64;
+    }
+    // S^T tiles: [key half hh][query half n]; lane holds query 32n + l32 and keys
+    // 32hh + 8(r/4) + 4g + (r%4), r = 0..15.  K is streamed one 32-key half at a time.
+    f32x16_t s[2][2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      uint4 kr[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) kr[c] = kb[(hh * 8 + c) * 64 + lane];
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        f32x16_t t;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t[r] = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[c]), qr[n][c], t, 0, 0, 0);
+        s[hh][n] = t;
+      }
+    }
+
+    if (exact) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[hh][n][r] *= scale_log2;
+    } else {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * hh + 8 * (r >> 2) + 4 * g + (r & 3);
+          const bool masked = key >= nb || ((sel_bits[key >> 5] >> (key & 31)) & 1u);
+          const float b = masked ? -INFINITY : bias_h[key] * kLog2e;
+#pragma unroll
+          for (int n = 0; n < 2; ++n) s[hh][n][r] = s[hh][n][r] * scale_log2 + b;
+        }
+    }
+
+    // online softmax per query half (lanes l and l^32 hold the same query)
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[hh][n][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run[n], mx);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run[n] - m_use);
+      float rs = 0.f;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(s[hh][n][r] - m_use);
+          s[hh][n][r] = p;
+          rs += p;
+        }
+      rs += __shfl_xor(rs, 32, 64);
+      l_run[n] = l_run[n] * alpha + rs;
+      m_run[n] = m_new;
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[a][n][r] *= alpha;
+    }
+
+    // O^T[d chunk a][query half n] += V^T[a][key chunk c] P^T[c][n]; the B operand of key
+    // chunk c is registers 8(c%2)..+8 of S^T tile (c/2, n).  V is streamed per key half.
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      uint4 vr[8];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) vr[a * 2 + cc] = vb[(a * 4 + 2 * hh + cc) * 64 + lane];
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+          const bf16x8_t pb = pack8(s[hh][n], 8 * cc);
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+            acc[a][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vr[a * 2 + cc]), pb,
+                                                                acc[a][n], 0, 0, 0);
+        }
+    }
+  }
+
+  // merge the four waves' online-softmax states
+  if (g == 0) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      sm_m[wave][32 * n + l32] = m_run[n];
+      sm_l[wave][32 * n + l32] = l_run[n];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int qq = 32 * n + l32;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][qq]);
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) L += sm_l[w][qq] * __builtin_amdgcn_exp2f(sm_m[w][qq] - Mu);
+    const float f = (L > 0.f) ? __builtin_amdgcn_exp2f(m_run[n] - Mu) / L : 0.f;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][n][r] *= f;
+  }
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int idx = (32 * n + l32) * 129 + 32 * a + 8 * (r >> 2) + 4 * g + (r & 3);
+            sm_o[idx] = (w == 0) ? acc[a][n][r] : sm_o[idx] + acc[a][n][r];
+          }
+    }
+    __syncthreads();
+  }
+
+  // inverse permutation: row qq of the block is token perm_q[64 i + qq]
+  {
+    const int qq = tid >> 2, part = tid & 3;
+    const int tok = pq[qq];
+    uint4* dst = reinterpret_cast<uint4*>(o + ((size_t)h * N + tok) * D + part * 32);
+    const float* src = sm_o + qq * 129 + part * 32;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      uint4 u;
+      u.x = pack_bf16x2(src[8 * v + 0], src[8 * v + 1]);
+      u.y = pack_bf16x2(src[8 * v + 2], src[8 * v + 3]);
+      u.z = pack_bf16x2(src[8 * v + 4], src[8 * v + 5]);
+      u.w = pack_bf16x2(src[8 * v + 6], src[8 * v + 7]);
+      dst[v] = u;
+    }
+    if (lse != nullptr && part == 0) {
+      float M = -INFINITY;
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][qq]);
+      const float Mu = (M == -INFINITY) ? 0.f : M;
+      float L = 0.f;
+      for (int w = 0; w < 4; ++w) L += sm_l[w][qq] * __builtin_amdgcn_exp2f(sm_m[w][qq] - Mu);
+      lse[(size_t)h * N + tok] = (L > 0.f) ? (Mu + __log2f(L)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+// fp32 path (D = 64): one wave per (head, query block), one query per lane, K/V tiles staged
+// in LDS.  Plain fp32 FMA arithmetic.
+__global__ __launch_bounds__(64) void k_attn_f32(
+    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
+    const int32_t* __restrict__ perm_q, const int32_t* __restrict__ perm_k,
+    const float* __restrict__ kt, const float* __restrict__ vt, const float* __restrict__ bias,
+    const int32_t* __restrict__ lists, int H, int N, int nb, int topk, int n_exact, int n_comp,
+    float scale_log2, float* __restrict__ o, float* __restrict__ lse) {
+  constexpr int D = 64;
+  __shared__ float sk[64][D + 1];
+  __shared__ float sv[64][D + 1];
+  __shared__ float sb[64];
+  __shared__ uint32_t sel_bits[kMaxSelWords];
+  const int logical = xcd_remap(blockIdx.x, H * nb);
+  const int h = logical / nb, i = logical - h * nb;
+  const int t = threadIdx.x;
+  const int ntiles = summary_tiles(nb);
+  const int32_t* list = lists + ((size_t)h * nb + i) * topk;
+  const int words = (nb + 31) >> 5;
+  for (int w = t; w < words; w += 64) sel_bits[w] = 0u;
+  __syncthreads();
+  for (int x = t; x < topk; x += 64) atomicOr(&sel_bits[list[x] >> 5], 1u << (list[x] & 31));
+
+  const int tok = perm_q[(size_t)h * N + (size_t)i * kBlk + t];
+  float qv[D], acc[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    qv[d] = q[((size_t)h * N + tok) * D + d];
+    acc[d] = 0.f;
+  }
+  float m_run = -INFINITY, l_run = 0.f;
+  const float* bias_h = bias + (size_t)h * ntiles * 64;
+  for (int it = 0; it < n_exact + n_comp; ++it) {
+    const bool exact = it < n_exact;
+    __syncthreads();
+    if (exact) {
+      const int j = list[it];
+      const int ktok = perm_k[(size_t)h * N + (size_t)j * kBlk + t];
+      for (int d = 0; d < D; ++d) {
+        sk[t][d] = k[((size_t)h * N + ktok) * D + d];
+        sv[t][d] = v[((size_t)h * N + ktok) * D + d];
+      }
+      sb[t] = 0.f;
+    } else {
+      const int key = (it - n_exact) * 64 + t;
+      const bool masked = key >= nb || ((sel_bits[key >> 5] >> (key & 31)) & 1u);
+      for (int d = 0; d < D; ++d) {
+        sk[t][d] = key < nb ? kt[((size_t)h * nb + key) * D + d] : 0.f;
+        sv[t][d] = key < nb ? vt[((size_t)h * nb + key) * D + d] : 0.f;
+      }
+      sb[t] = masked ? -INFINITY : bias_h[key] * kLog2e;
+    }
+    __syncthreads();
+    float x[64];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 64; ++r) {
+      float dot = 0.f;
+#pragma unroll
+      for (int d = 0; d < D; ++d) dot = fmaf(qv[d], sk[r][d], dot);
+      x[r] = dot * scale_log2 + sb[r];
+      mx = fmaxf(mx, x[r]);
+    }
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2f(m_run - m_use);
+    l_run *= alpha;
+#pragma unroll
+    for (int d = 0; d < D; ++d) acc[d] *= alpha;
+#pragma unroll
+    for (int r = 0; r < 64; ++r) {
+      const float p = exp2f(x[r] - m_use);
+      l_run += p;
+#pragma unroll
+      for (int d = 0; d < D; ++d) acc[d] = fmaf(p, sv[r][d], acc[d]);
+    }
+    m_run = m_new;
+  }
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  for (int d = 0; d < D; ++d) o[((size_t)h * N + tok) * D + d] = acc[d] * inv;
+  if (lse != nullptr)
+    lse[(size_t)h * N + tok] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_attn_bf16(const AttnLaunch& a, hipStream_t s) {
+  const int grid = a.H * a.nb;
+  k_attn_bf16<<<grid, 256, 0, s>>>(
+      static_cast<const uint16_t*>(a.q), a.perm_q, static_cast<const uint4*>(a.ksw),
+      static_cast<const uint4*>(a.vsw), static_cast<const uint4*>(a.ktsw),
+      static_cast<const uint4*>(a.vtsw), a.bias, a.lists, a.H, a.N, a.nb, a.topk, a.n_exact,
+      a.n_comp, a.scale * kLog2e, static_cast<uint16_t*>(a.o), a.lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_f32(const AttnLaunch& a, hipStream_t s) {
+  const int grid = a.H * a.nb;
+  k_attn_f32<<<grid, 64, 0, s>>>(
+      static_cast<const float*>(a.q), static_cast<const float*>(a.k),
+      static_cast<const float*>(a.v), a.perm_q, a.perm_k, a.kt, a.vt, a.bias, a.lists, a.H, a.N,
+      a.nb, a.topk, a.n_exact, a.n_comp, a.scale * kLog2e, static_cast<float*>(a.o), a.lse);
+  return hipGetLastError();
+}
+
+}  // namespace bsa

@@ -1,0 +1,60 @@
+// Device-side helpers shared by the gfx950 kernels: bf16 conversion, MFMA operand types,
+// wave64 reductions, orderable float keys.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define BSA_DEV __device__ __forceinline__
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+
+constexpr int kWave = 64;
+constexpr int kBlock = 64;
+
+// bf16 <-> fp32 (round to nearest even; inputs are finite)
+BSA_DEV float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+BSA_DEV uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+BSA_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
+}
+
+template <typename T> BSA_DEV float load_as_f32(const T* p);
+template <> BSA_DEV float load_as_f32<float>(const float* p) { return *p; }
+template <> BSA_DEV float load_as_f32<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+
+// wave64 reductions (xor butterfly over all 64 lanes)
+BSA_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+BSA_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+BSA_DEV int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Monotone map float -> uint32 (a < b  <=>  key(a) < key(b)); -0.0 maps like +0.0.
+BSA_DEV uint32_t orderable_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// number of set bits of a 64-bit lane mask below this lane
+BSA_DEV int lanes_below(uint64_t mask) {
+  const int lane = threadIdx.x & 63;
+  return __popcll(mask & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+}

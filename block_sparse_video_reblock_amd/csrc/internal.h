@@ -1,0 +1,68 @@
+// Host-side launchers of the gfx950 kernels.  Shapes are validated by the C-ABI layer before
+// any of these is called; each launcher only enqueues kernels on `stream` and returns the
+// launch status.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bsa {
+
+constexpr int kBlk = 64;
+constexpr int kColChunk = 512;     // tokens per partial of the anchor / column-sum reduction
+
+__host__ __device__ inline int ceil_div(long a, long b) { return int((a + b - 1) / b); }
+__host__ __device__ inline int summary_tiles(int nb) { return ceil_div(nb, 64); }
+
+// ---------------------------------------------------------------- summaries (stage 4)
+// anchor[h][d] = mean over tokens of x[h][.][d]; partial: float [H][ceil(N/kColChunk)][D]
+hipError_t launch_anchor(bool bf16, const void* x, int H, int N, int D, float* partial,
+                         float* anchor, hipStream_t s);
+// per key block j: fp32 summaries kt/vt [H][nb][D], bias [H][ldb]; optionally (bf16 only)
+// the block-swizzled copies of K and V used by the attention kernel.
+hipError_t launch_summaries(bool bf16, const void* k, const void* v, const int32_t* perm_k,
+                            const float* anchor, int H, int N, int D, float scale, bool meanpool,
+                            float* kt, float* vt, float* bias, int ldb, void* ksw, void* vsw,
+                            hipStream_t s);
+// swizzled bf16 summary tiles for the attention kernel; pads bias rows >= nb with -inf
+hipError_t launch_summary_tiles(const float* kt, const float* vt, float* bias, int H, int nb,
+                                void* ktsw, void* vtsw, hipStream_t s);
+
+// ------------------------------------------------------------ attention (stages 3, 4, 5)
+struct AttnLaunch {
+  int H, N, nb, topk, n_exact, n_comp;     // n_exact = topk or 0, n_comp = tiles or 0
+  float scale;
+  const void* q;
+  const int32_t* perm_q;
+  const int32_t* lists;
+  const float* bias;                        // [H][tiles*64], -inf on pads
+  void* o;
+  float* lse;
+  // bf16 path: swizzled tiles
+  const void *ksw, *vsw, *ktsw, *vtsw;
+  // f32 path: plain tensors and fp32 summaries
+  const void *k, *v;
+  const int32_t* perm_k;
+  const float *kt, *vt;
+};
+hipError_t launch_attn_bf16(const AttnLaunch& a, hipStream_t s);
+hipError_t launch_attn_f32(const AttnLaunch& a, hipStream_t s);
+
+// ------------------------------------------------------------------- select (stage 2)
+hipError_t launch_block_means(bool bf16, const void* x, const int32_t* perm, int H, int N, int D,
+                              float* means, hipStream_t s);
+hipError_t launch_block_scores(const float* qm, const float* km, int H, int nb, int D,
+                               float scale, float* scores, hipStream_t s);
+hipError_t launch_topk(const float* scores, int rows, int nb, int k, int32_t* lists,
+                       hipStream_t s);
+
+// ------------------------------------------------------------------ reblock (stage 1)
+size_t reblock_ws_bytes(int H, int N, int D);
+hipError_t launch_reblock(bool bf16, const void* q, const void* k, int H, int N, int D,
+                          int32_t* perm_q, int32_t* perm_k, float* proj_opt, void* ws,
+                          hipStream_t s);
+size_t partition_ws_bytes(int P, int N);
+hipError_t launch_partition_from_proj(int P, int N, const float* proj, int32_t* perm, void* ws,
+                                      hipStream_t s);
+
+}  // namespace bsa

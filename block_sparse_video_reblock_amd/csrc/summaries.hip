@@ -1,0 +1,239 @@
+// Compressed-branch summaries (Spark-Reweight) and the block-swizzled K/V copies that feed the
+// bf16 attention kernel.
+//
+// [comfyui-wiki.com "Spark-H3 ...", "What Spark-Attn changes" and its figure]: mean pooling
+// puts exp(E[x]) where the attention needs E[exp(x)]; weighted summaries plus a log-mass bias
+// restore the missing mass, scored against one anchor per head, the mean video query.  For key
+// block j with anchor logits x_t = s qa.k_t:  w = softmax(x), kt_j = sum w_t k_t,
+// vt_j = sum w_t v_t, b_j = logsumexp(x) - s qa.kt_j, so exp(s qa.kt_j + b_j) = sum_t exp(x_t).
+// The fixed-block baseline (mean pooling) uses plain means and b_j = ln 64.
+//
+// Swizzled tile layouts (64 rows x 128 bf16 = 16 KiB, stored as 16 pieces x 64 lanes x 16 B,
+// piece-major) match the MFMA operand registers of the attention kernel:
+//   K layout, piece hh*8 + c, lane l: row 32hh + (l%32), elements 16c + 8(l/32) + 0..7
+//   V layout, piece a*4 + c, lane l: element 32a + (l%32) of rows
+//             16c + 4(l/32) + {0,1,2,3,8,9,10,11}
+#include "common.h"
+#include "internal.h"
+
+namespace bsa {
+namespace {
+
+// V-layout row of slot t (0..7) for key chunk c and lane group g
+BSA_DEV int vrow(int c, int g, int t) { return 16 * c + 8 * (t >> 2) + 4 * g + (t & 3); }
+
+// ---------------------------------------------------------------- anchor: column means
+template <typename T>
+__global__ __launch_bounds__(256) void k_colsum(const T* __restrict__ x, int N, int D,
+                                                float* __restrict__ partial) {
+  // grid (chunks, H); thread -> column d (D <= 128), 2 row phases
+  const int chunk = blockIdx.x, h = blockIdx.y, nch = gridDim.x;
+  const int d = threadIdx.x % D, ph = threadIdx.x / D, nph = 256 / D;
+  const int t0 = chunk * kColChunk, t1 = min(N, t0 + kColChunk);
+  __shared__ float red[256];
+  float acc = 0.f;
+  for (int t = t0 + ph; t < t1; t += nph) acc += load_as_f32(x + ((size_t)h * N + t) * D + d);
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  if (ph == 0) {
+    float s = 0.f;
+    for (int p = 0; p < nph; ++p) s += red[p * D + d];
+    partial[((size_t)h * nch + chunk) * D + d] = s;
+  }
+}
+
+__global__ void k_colsum_finish(const float* __restrict__ partial, int nch, int N, int D,
+                                float* __restrict__ out) {
+  const int h = blockIdx.x, d = threadIdx.x;
+  if (d >= D) return;
+  float s = 0.f;
+  for (int c = 0; c < nch; ++c) s += partial[((size_t)h * nch + c) * D + d];
+  out[(size_t)h * D + d] = s / float(N);
+}
+
+// ----------------------------------------------------------- per key block summaries
+// grid (nb, H), 256 threads.  LDS holds the gathered block as fp32.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_summaries(
+    const T* __restrict__ k, const T* __restrict__ v, const int32_t* __restrict__ perm_k,
+    const float* __restrict__ anchor, int N, float scale, int meanpool, float* __restrict__ kt,
+    float* __restrict__ vt, float* __restrict__ bias, int ldb, uint4* __restrict__ ksw,
+    uint4* __restrict__ vsw) {
+  __shared__ float sk[64][D + 1];
+  __shared__ float sv[64][D + 1];
+  __shared__ float sw[64];
+  __shared__ float sred[2][D];
+  __shared__ float s_lse;
+  const int j = blockIdx.x, h = blockIdx.y, nb = gridDim.x;
+  const int tid = threadIdx.x;
+  const int32_t* pk = perm_k + (size_t)h * N + (size_t)j * kBlk;
+  for (int e = tid; e < 64 * D; e += 256) {
+    const int r = e / D, d = e - r * D;
+    const size_t src = ((size_t)h * N + pk[r]) * D + d;
+    sk[r][d] = load_as_f32(k + src);
+    sv[r][d] = load_as_f32(v + src);
+  }
+  __syncthreads();
+  if (tid < 64) {
+    float w;
+    if (meanpool) {
+      w = 1.f / 64.f;
+      if (tid == 0) s_lse = logf(64.f);
+    } else {
+      const float* qa = anchor + (size_t)h * D;
+      float x = 0.f;
+      for (int d = 0; d < D; ++d) x = fmaf(qa[d], sk[tid][d], x);
+      x *= scale;
+      const float mx = wave_max(x);
+      const float e = expf(x - mx);
+      const float se = wave_sum(e);
+      w = e / se;
+      if (tid == 0) s_lse = mx + logf(se);
+    }
+    sw[tid] = w;
+  }
+  __syncthreads();
+  // weighted sums: thread -> element d; rows 0..31 and 32..63 summed separately
+  for (int e = tid; e < D; e += 256) {
+    float a0 = 0.f, a1 = 0.f, b0 = 0.f, b1 = 0.f;
+    for (int r = 0; r < 32; ++r) {
+      a0 = fmaf(sw[r], sk[r][e], a0);
+      b0 = fmaf(sw[r], sv[r][e], b0);
+      a1 = fmaf(sw[r + 32], sk[r + 32][e], a1);
+      b1 = fmaf(sw[r + 32], sv[r + 32][e], b1);
+    }
+    const size_t dst = ((size_t)h * nb + j) * D + e;
+    kt[dst] = a0 + a1;
+    vt[dst] = b0 + b1;
+    sred[0][e] = a0 + a1;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    float b;
+    if (meanpool) {
+      b = s_lse;
+    } else {
+      const float* qa = anchor + (size_t)h * D;
+      float x = 0.f;
+      for (int d = tid; d < D; d += 64) x = fmaf(qa[d], sred[0][d], x);
+      x = wave_sum(x);
+      b = s_lse - scale * x;
+    }
+    if (tid == 0) bias[(size_t)h * ldb + j] = b;
+  }
+  // block-swizzled bf16 copies (bf16 path only)
+  if (ksw != nullptr) {
+    uint4* kdst = ksw + ((size_t)h * nb + j) * 1024;
+    uint4* vdst = vsw + ((size_t)h * nb + j) * 1024;
+    for (int u = tid; u < 1024; u += 256) {
+      const int p = u >> 6, l = u & 63, g = l >> 5, l32 = l & 31;
+      {  // K layout
+        const int hh = p >> 3, c = p & 7;
+        const float* src = &sk[32 * hh + l32][16 * c + 8 * g];
+        uint4 o;
+        o.x = pack_bf16x2(src[0], src[1]);
+        o.y = pack_bf16x2(src[2], src[3]);
+        o.z = pack_bf16x2(src[4], src[5]);
+        o.w = pack_bf16x2(src[6], src[7]);
+        kdst[u] = o;
+      }
+      {  // V layout
+        const int a = p >> 2, c = p & 3, d = 32 * a + l32;
+        uint4 o;
+        o.x = pack_bf16x2(sv[vrow(c, g, 0)][d], sv[vrow(c, g, 1)][d]);
+        o.y = pack_bf16x2(sv[vrow(c, g, 2)][d], sv[vrow(c, g, 3)][d]);
+        o.z = pack_bf16x2(sv[vrow(c, g, 4)][d], sv[vrow(c, g, 5)][d]);
+        o.w = pack_bf16x2(sv[vrow(c, g, 6)][d], sv[vrow(c, g, 7)][d]);
+        vdst[u] = o;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------- swizzled bf16 summary tiles (D = 128)
+// grid (tiles, H), 256 threads
+__global__ __launch_bounds__(256) void k_summary_tiles(const float* __restrict__ kt,
+                                                       const float* __restrict__ vt,
+                                                       float* __restrict__ bias, int nb,
+                                                       uint4* __restrict__ ktsw,
+                                                       uint4* __restrict__ vtsw) {
+  constexpr int D = 128;
+  __shared__ float sk[64][D + 1];
+  __shared__ float sv[64][D + 1];
+  const int tau = blockIdx.x, h = blockIdx.y, ntiles = gridDim.x;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < 64 * D; e += 256) {
+    const int r = e / D, d = e - r * D;
+    const int row = tau * 64 + r;
+    const bool ok = row < nb;
+    sk[r][d] = ok ? kt[((size_t)h * nb + row) * D + d] : 0.f;
+    sv[r][d] = ok ? vt[((size_t)h * nb + row) * D + d] : 0.f;
+  }
+  if (tid < 64 && tau * 64 + tid >= nb) bias[(size_t)h * ntiles * 64 + tau * 64 + tid] = -INFINITY;
+  __syncthreads();
+  uint4* kdst = ktsw + ((size_t)h * ntiles + tau) * 1024;
+  uint4* vdst = vtsw + ((size_t)h * ntiles + tau) * 1024;
+  for (int u = tid; u < 1024; u += 256) {
+    const int p = u >> 6, l = u & 63, g = l >> 5, l32 = l & 31;
+    {
+      const int hh = p >> 3, c = p & 7;
+      const float* src = &sk[32 * hh + l32][16 * c + 8 * g];
+      uint4 o;
+      o.x = pack_bf16x2(src[0], src[1]);
+      o.y = pack_bf16x2(src[2], src[3]);
+      o.z = pack_bf16x2(src[4], src[5]);
+      o.w = pack_bf16x2(src[6], src[7]);
+      kdst[u] = o;
+    }
+    {
+      const int a = p >> 2, c = p & 3, d = 32 * a + l32;
+      uint4 o;
+      o.x = pack_bf16x2(sv[vrow(c, g, 0)][d], sv[vrow(c, g, 1)][d]);
+      o.y = pack_bf16x2(sv[vrow(c, g, 2)][d], sv[vrow(c, g, 3)][d]);
+      o.z = pack_bf16x2(sv[vrow(c, g, 4)][d], sv[vrow(c, g, 5)][d]);
+      o.w = pack_bf16x2(sv[vrow(c, g, 6)][d], sv[vrow(c, g, 7)][d]);
+      vdst[u] = o;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_anchor(bool bf16, const void* x, int H, int N, int D, float* partial,
+                         float* anchor, hipStream_t s) {
+  const int nch = ceil_div(N, kColChunk);
+  dim3 grid(nch, H);
+  if (bf16)
+    k_colsum<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), N, D, partial);
+  else
+    k_colsum<float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), N, D, partial);
+  k_colsum_finish<<<H, 128, 0, s>>>(partial, nch, N, D, anchor);
+  return hipGetLastError();
+}
+
+hipError_t launch_summaries(bool bf16, const void* k, const void* v, const int32_t* perm_k,
+                            const float* anchor, int H, int N, int D, float scale, bool meanpool,
+                            float* kt, float* vt, float* bias, int ldb, void* ksw, void* vsw,
+                            hipStream_t s) {
+  dim3 grid(N / kBlk, H);
+  if (bf16)
+    k_summaries<uint16_t, 128><<<grid, 256, 0, s>>>(
+        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), perm_k, anchor, N,
+        scale, meanpool ? 1 : 0, kt, vt, bias, ldb, static_cast<uint4*>(ksw),
+        static_cast<uint4*>(vsw));
+  else
+    k_summaries<float, 64><<<grid, 256, 0, s>>>(
+        static_cast<const float*>(k), static_cast<const float*>(v), perm_k, anchor, N, scale,
+        meanpool ? 1 : 0, kt, vt, bias, ldb, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_summary_tiles(const float* kt, const float* vt, float* bias, int H, int nb,
+                                void* ktsw, void* vtsw, hipStream_t s) {
+  dim3 grid(summary_tiles(nb), H);
+  k_summary_tiles<<<grid, 256, 0, s>>>(kt, vt, bias, nb, static_cast<uint4*>(ktsw),
+                                       static_cast<uint4*>(vtsw));
+  return hipGetLastError();
+}
+
+}  // namespace bsa

@@ -1,0 +1,157 @@
+// Capacity-constrained tree bookkeeping shared by the reblock kernels: group geometry,
+// workgroup scans, the radix select of a split threshold and the stable two-way partition.
+//
+// [comfy.icu "MiniMax H3 Spark Attention (SM89)", "What it's doing under the hood"]: a
+// capacity-constrained tree partition down to exactly 64-token leaves.  Reading used here: a
+// group of m blocks (m >= 2) sends the floor(m/2)*64 tokens of smallest (projection, token id)
+// to its left child, the rest to the right; children are laid out left first, so every group
+// of every level occupies one contiguous position range and the final leaf order is
+// depth-first.  Inside a group positions always hold ascending token ids (the partition is
+// stable and starts from the identity), so "lower token id" is "lower position".
+#pragma once
+#include "common.h"
+
+namespace bsa {
+
+enum GroupKind { kGroupNone = 0, kGroupCopy = 1, kGroupSplit = 2 };
+
+// Node g of level `level` (g's bits, most significant first, are the left/right turns).
+// Returns kGroupSplit for a group of m >= 2 blocks, kGroupCopy for a leaf that must be carried
+// to the next level's buffer (reported once, by its leftmost descendant index), kGroupNone
+// otherwise.
+__host__ __device__ inline int group_geom(int nb, int level, int g, int& b0, int& m) {
+  b0 = 0;
+  m = nb;
+  for (int l = level - 1; l >= 0; --l) {
+    if (m < 2) return (g & ((2 << l) - 1)) == 0 ? kGroupCopy : kGroupNone;
+    const int left = m >> 1;
+    if ((g >> l) & 1) {
+      b0 += left;
+      m -= left;
+    } else {
+      m = left;
+    }
+  }
+  return m >= 2 ? kGroupSplit : kGroupCopy;
+}
+
+// The group (at `level`) that contains block b, and its geometry.
+__host__ __device__ inline int group_of_block(int nb, int level, int b, int& b0, int& m) {
+  int g = 0;
+  b0 = 0;
+  m = nb;
+  for (int l = 0; l < level; ++l) {
+    if (m < 2) return -1;
+    const int left = m >> 1;
+    if (b >= b0 + left) {
+      g = 2 * g + 1;
+      b0 += left;
+      m -= left;
+    } else {
+      g = 2 * g;
+      m = left;
+    }
+  }
+  return g;
+}
+
+__host__ __device__ inline int tree_levels(int nb) {
+  int L = 0;
+  while ((1 << L) < nb) ++L;
+  return L;
+}
+
+// Exclusive scan of one int per thread over a 256-thread workgroup; returns the total in
+// *total.  `sm` needs 4 ints of LDS.  Contains workgroup barriers.
+BSA_DEV int block_excl_scan(int v, int* sm, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  __syncthreads();
+  if (lane == 63) sm[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int s = sm[w];
+    before += (w < wave) ? s : 0;
+    all += s;
+  }
+  *total = all;
+  return before + incl - v;
+}
+
+// Radix select over n keys (any address space): the threshold T such that the `want`
+// smallest keys are all keys < T plus the first *take keys == T in index order.
+// Needs 256 ints of LDS in `hist` and 6 in `sm`.  256-thread workgroup, contains barriers.
+BSA_DEV uint32_t block_select_smallest(const float* keys, int n, int want, int* hist, int* sm,
+                                       int* take) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, pmask = 0;
+  int remaining = want;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < n; i += 256) {
+      const uint32_t key = orderable_key(keys[i]);
+      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+    }
+    __syncthreads();
+    const int c = hist[tid];  // thread t owns bin t (ascending)
+    int total;
+    const int excl = block_excl_scan(c, sm, &total);
+    // the digit is the bin where the running count first reaches `remaining`
+    if (excl < remaining && excl + c >= remaining) {
+      sm[4] = tid;
+      sm[5] = excl;
+    }
+    __syncthreads();
+    const int digit = sm[4];
+    remaining -= sm[5];
+    prefix |= uint32_t(digit) << shift;
+    pmask |= 255u << shift;
+    __syncthreads();
+  }
+  *take = remaining;
+  return prefix;
+}
+
+// Stable two-way partition of the n entries in[0..n) by keys[0..n) around (T, take):
+// entries with key < T, and the first `take` entries with key == T, go (in order) to
+// out[0..want), the others (in order) to out[want..n).  Each thread handles one contiguous
+// run of indices.  Needs 8 ints of LDS in `sm`.  Contains barriers.
+BSA_DEV void block_partition(const float* keys, const int32_t* in, int32_t* out, int n,
+                             int want, uint32_t T, int take, int* sm) {
+  const int tid = threadIdx.x;
+  const int run = (n + 255) / 256;
+  const int i0 = min(n, tid * run), i1 = min(n, i0 + run);
+  int c_lt = 0, c_eq = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = orderable_key(keys[i]);
+    c_lt += key < T;
+    c_eq += key == T;
+  }
+  int tot;
+  const int eq_before = block_excl_scan(c_eq, sm, &tot);
+  const int eq_taken = max(0, min(take - eq_before, c_eq));
+  const int left_before = block_excl_scan(c_lt + eq_taken, sm, &tot);
+  int li = left_before, ri = want + (i0 - left_before), eq_seen = eq_before;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = orderable_key(keys[i]);
+    bool left = key < T;
+    if (key == T) {
+      left = eq_seen < take;
+      ++eq_seen;
+    }
+    if (left)
+      out[li++] = in[i];
+    else
+      out[ri++] = in[i];
+  }
+}
+
+}  // namespace bsa

@@ -1,0 +1,150 @@
+/* bsattn.h -- C ABI of the MI355X (gfx950) Spark-Attn block-sparse attention layer.
+ *
+ * The layer, as the pages describe it (page titles below), runs in five stages:
+ *   (1) reblock:  per-head second moments M_K = E[k k^T] (used to compare queries) and
+ *                 M_Q = E[q q^T] (used to compare keys) define a Mahalanobis cosine; a
+ *                 capacity-constrained hierarchical tree partition puts queries, and
+ *                 separately keys, into leaves of exactly 64 tokens.  Only a permutation is
+ *                 produced; Q/K/V values are never modified.
+ *                 [comfy.icu "MiniMax H3 Spark Attention (SM89)", "What it's doing under the
+ *                 hood"; comfyui-wiki.com "Spark-H3 ...", "What Spark-Attn changes"]
+ *   (2) select:   block scores and a per-query-block top-K at a topk_ratio (or fixed
+ *                 topk_blocks) budget.  [comfy.icu page, "Inputs you'll actually set"]
+ *   (3) exact branch over the selected key blocks, flash-style.
+ *   (4) compressed branch over the unselected blocks: anchor-weighted key/value summaries
+ *                 plus a log-mass bias (Spark-Reweight); every query keeps its own Q.
+ *                 [comfyui-wiki.com page, "What Spark-Attn changes" and its figure]
+ *   (5) log-sum-exp merge of the two branches and the inverse permutation to token order.
+ *
+ * Conventions shared by every call
+ *   - Tensors are dense, row-major [heads][tokens][head_dim] device buffers, batch 1.
+ *   - Supported (dtype, head_dim): (BSA_BF16, 128) and (BSA_F32, 64).  tokens must be a
+ *     positive multiple of 64, at most BSA_MAX_TOKENS.
+ *   - A permutation perm[h][p] holds the token id placed at position p.  Query block i is
+ *     positions [64 i, 64 i + 64) of perm_q; key block j is positions [64 j, 64 j + 64) of
+ *     perm_k; V follows K.  nb = tokens / 64.
+ *   - Every pointer is a device pointer owned by the caller; the library allocates nothing and
+ *     keeps no state beyond a per-device architecture check.  `ws` is caller-provided
+ *     scratch of at least bsa_workspace_bytes(desc) bytes (contents need not be initialised
+ *     and are clobbered).
+ *   - Calls are asynchronous on `stream`.  The return value reports argument validation and
+ *     launch errors; argument checks run on the host before any HIP call.  There is no silent
+ *     fallback: an unsupported input is an error (BSA_E_ARG / BSA_E_UNSUPPORTED), never a
+ *     different code path.  bsa_last_error() gives a message for the calling thread.
+ *   - Results are deterministic: identical inputs give bitwise-identical outputs.
+ */
+#ifndef BSATTN_H
+#define BSATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BSA_OK = 0,
+  BSA_E_ARG = -1,          /* bad argument: null pointer, shape, budget, flags, scale */
+  BSA_E_UNSUPPORTED = -2,  /* (dtype, head_dim) not supported, or the device is not gfx950 */
+  BSA_E_WORKSPACE = -3,    /* ws too small */
+  BSA_E_HIP = -4           /* a HIP runtime call or kernel launch failed */
+} bsa_status;
+
+typedef enum { BSA_F32 = 0, BSA_BF16 = 1 } bsa_dtype;
+
+#define BSA_BLOCK 64
+#define BSA_MAX_TOKENS (1 << 22)
+
+typedef struct {
+  int32_t heads;     /* >= 1 */
+  int32_t tokens;    /* N, multiple of 64 */
+  int32_t head_dim;  /* D */
+  int32_t dtype;     /* bsa_dtype */
+} bsa_desc;
+
+/* sparse_attn flags */
+#define BSA_MEANPOOL 1u        /* fixed-block baseline: mean-pooled summaries, bias ln 64 */
+#define BSA_EXACT_ONLY 2u      /* debug: output only the exact branch (O_e, lse_e) */
+#define BSA_COMPRESSED_ONLY 4u /* debug: output only the compressed branch (O_c, lse_c) */
+
+const char* bsa_status_str(int32_t status);
+/* Message describing the last failed call on this thread ("" if none). */
+const char* bsa_last_error(void);
+
+/* Blocks selected per query block for a budget ratio (comfy.icu page, "Inputs you'll actually
+ * set": topk_ratio).  K = clamp(floor(ratio * nb + 1e-6), 1, nb), computed in double from the
+ * float ratio.  Returns -1 if nb < 1 or ratio is not in (0, 1]. */
+int32_t bsa_topk_count(int32_t n_blocks, float ratio);
+
+/* Scratch bytes that bsa_reblock, bsa_select, bsa_summaries and bsa_sparse_attn need for this
+ * descriptor (one buffer serves all of them).  0 for an invalid descriptor. */
+size_t bsa_workspace_bytes(const bsa_desc* desc);
+
+/* (1) Reblock.  perm_q[h][.] (query layout, from M_K) and perm_k[h][.] (key layout, from
+ * M_Q), each int32 [heads][tokens].  Leaves are in depth-first (left first) order, tokens in
+ * ascending id inside a leaf.  If proj_opt is non-null it receives the fp32 projection every
+ * token got at every split level, by token id: float [heads][2][levels][tokens] with side 0 =
+ * queries, 1 = keys, levels = ceil(log2 nb) (0 where the token's group was already a leaf). */
+bsa_status bsa_reblock(const bsa_desc* desc, const void* q, const void* k,
+                       int32_t* perm_q, int32_t* perm_k, float* proj_opt,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* (2) Select.  Block scores S[h][i][j] = s * mean(query block i) . mean(key block j) with
+ * s = 1/sqrt(D); per row the K largest (ties to the lower j), written ascending to
+ * lists[h][i][0..K).  K = topk_blocks if topk_blocks > 0 (must be <= nb), else
+ * bsa_topk_count(nb, topk_ratio).  scores_opt, if non-null, receives S (float [heads][nb][nb]).
+ */
+bsa_status bsa_select(const bsa_desc* desc, const void* q, const void* k,
+                      const int32_t* perm_q, const int32_t* perm_k,
+                      float topk_ratio, int32_t topk_blocks,
+                      int32_t* lists, float* scores_opt,
+                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* (3)+(4)+(5) Sparse attention.  For query block i of head h and each of its queries q:
+ * the exact branch attends over the keys of blocks lists[h][i][0..topk) (each list
+ * strictly ascending, entries in [0, nb)); the compressed branch attends over every other
+ * block j with logit s q.kt_j + b_j and value vt_j, where (kt, vt, b) are the block summaries of
+ * bsa_summaries; the branches merge by log-sum-exp and row p of block i is written to output
+ * row perm_q[h][p].  o has the input dtype, [heads][tokens][head_dim]; lse_opt (float
+ * [heads][tokens], natural log) receives the merged log-sum-exp of the scaled logits.
+ * scale = 0 means 1/sqrt(D).  flags: BSA_MEANPOOL, and at most one of BSA_EXACT_ONLY /
+ * BSA_COMPRESSED_ONLY (an empty branch gives lse = -inf and a zero row).  With
+ * topk = nb (every block selected) this is dense softmax attention. */
+bsa_status bsa_sparse_attn(const bsa_desc* desc, const void* q, const void* k, const void* v,
+                           const int32_t* perm_q, const int32_t* perm_k,
+                           const int32_t* lists, int32_t topk, uint32_t flags, float scale,
+                           void* o, float* lse_opt,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* (4) Block summaries alone (the compressed branch's keys, values and biases), fp32:
+ * kt[h][j][D], vt[h][j][D], bias[h][j].  Reweight (default): anchor qa = mean of the head's
+ * queries, x_t = s qa.k_t over block j's keys, w = softmax(x), kt = sum w_t k_t,
+ * vt = sum w_t v_t, b = logsumexp(x) - s qa.kt.  BSA_MEANPOOL: plain means and b = ln 64. */
+bsa_status bsa_summaries(const bsa_desc* desc, const void* q, const void* k, const void* v,
+                         const int32_t* perm_k, uint32_t flags, float scale,
+                         float* kt, float* vt, float* bias,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Parity hook for (1): the tree partition with every level's projections supplied.
+ * proj: float [problems][levels][tokens] by token id (levels = ceil(log2(tokens/64)));
+ * perm: int32 [problems][tokens].  Each split sends the floor(m/2)*64 tokens of smallest
+ * (projection, token id) of an m-block group to the left child; -0.0 equals +0.0; NaN is
+ * an error of the caller (the order of NaN projections is unspecified).  Needs
+ * bsa_partition_workspace_bytes(problems, tokens) bytes of ws. */
+size_t bsa_partition_workspace_bytes(int32_t problems, int32_t tokens);
+bsa_status bsa_reblock_from_projections(int32_t problems, int32_t tokens, const float* proj,
+                                        int32_t* perm, void* ws, size_t ws_bytes,
+                                        hipStream_t stream);
+
+/* Parity hook for (2): top-K of given scores.  scores: float [rows][n_blocks];
+ * lists: int32 [rows][topk], each ascending; ties go to the lower block index; -0.0 equals
+ * +0.0. */
+bsa_status bsa_topk_from_scores(int32_t rows, int32_t n_blocks, int32_t topk,
+                                const float* scores, int32_t* lists, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BSATTN_H */

@@ -1,0 +1,229 @@
+"""GPU parity of the select, summaries and attention stages against the CPU oracle, each fed
+the same inputs (the oracle's permutations and lists where a stage consumes them).  The bars:
+bit-exact for lists and permutations, max-abs 1e-4 for fp32 outputs, rel-L2 1e-2 and max-abs
+3e-2 for bf16 outputs."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from block_sparse_video_reblock_amd import _lib as ops
+from block_sparse_video_reblock_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def to_dev(x, dtype):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV).to(dtype)
+
+
+def rel_l2(a, b):
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+@pytest.fixture(scope="module")
+def mid():
+    """Two heads of the 16,384-token bf16 workload with the oracle's layouts and lists."""
+    wl = synth.WORKLOADS["mid_bf16"]
+    q, k, v = synth.make_qkv(wl, heads=[0, 1])
+    H = q.shape[0]
+    perms = [O.reblock_head(q[h].astype(np.float64), k[h].astype(np.float64))[:2]
+             for h in range(H)]
+    pq = np.stack([p[0] for p in perms]).astype(np.int32)
+    pk = np.stack([p[1] for p in perms]).astype(np.int32)
+    K = O.topk_count(wl.n_blocks, wl.topk_ratio)
+    lists = np.stack([O.topk_lists(O.block_scores(q[h].astype(np.float64),
+                                                  k[h].astype(np.float64), pq[h], pk[h])
+                                   .astype(np.float32), K) for h in range(H)]).astype(np.int32)
+    return wl, q, k, v, pq, pk, lists
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    wl = synth.WORKLOADS["tiny_f32"]
+    q, k, v = synth.make_qkv(wl)
+    pq, pk, _, _ = O.reblock_head(q[0].astype(np.float64), k[0].astype(np.float64))
+    K = O.topk_count(wl.n_blocks, wl.topk_ratio)
+    lists = O.topk_lists(O.block_scores(q[0].astype(np.float64), k[0].astype(np.float64),
+                                        pq, pk).astype(np.float32), K)
+    return wl, q, k, v, pq[None].astype(np.int32), pk[None].astype(np.int32), \
+        lists[None].astype(np.int32)
+
+
+# ----------------------------------------------------------------------- top-K hook
+
+@pytest.mark.parametrize("rows,nb,k", [(37, 64, 16), (300, 256, 51), (50, 1134, 113),
+                                       (9, 70, 70), (5, 1, 1), (64, 1620, 162)])
+def test_topk_hook_bitexact(rows, nb, k):
+    rng = np.random.default_rng(rows * 7 + nb)
+    S = rng.standard_normal((rows, nb)).astype(np.float32)
+    S[: rows // 2] = np.round(S[: rows // 2] * 2) / 2          # many exact ties
+    S[0, : min(nb, 5)] = -0.0
+    S[1, : min(nb, 5)] = 0.0
+    got = ops.topk_from_scores(torch.from_numpy(S).to(DEV), k).cpu().numpy()
+    assert np.array_equal(got, O.topk_lists(S, k))
+
+
+# ------------------------------------------------------------------- partition hook
+
+def test_partition_hook_bitexact_oracle_projections(tiny, mid):
+    for wl, q, k in ((tiny[0], tiny[1], tiny[2]), (mid[0], mid[1], mid[2])):
+        projs, perms = [], []
+        for h in range(q.shape[0]):
+            pq, pk, prq, prk = O.reblock_head(q[h].astype(np.float64), k[h].astype(np.float64))
+            projs += [prq, prk]
+            perms += [pq, pk]
+        got = ops.reblock_from_projections(torch.from_numpy(np.stack(projs)).to(DEV))
+        assert np.array_equal(got.cpu().numpy(), np.stack(perms))
+
+
+@pytest.mark.parametrize("n_blocks", [1, 2, 3, 37, 70, 129])
+def test_partition_hook_bitexact_random_ties(n_blocks):
+    rng = np.random.default_rng(n_blocks)
+    N = 64 * n_blocks
+    L = O.tree_levels(n_blocks)
+    proj = rng.integers(-3, 4, size=(3, max(L, 1), N)).astype(np.float32)[:, :L]
+    proj[0] *= 0.0                                              # all ties, including -0.0
+    proj[1] = rng.standard_normal((L, N)).astype(np.float32)
+    got = ops.reblock_from_projections(torch.from_numpy(np.ascontiguousarray(proj)).to(DEV))
+    ref = np.stack([O.partition_from_projections(proj[p], N) for p in range(3)])
+    assert np.array_equal(got.cpu().numpy(), ref)
+
+
+# ------------------------------------------------------------------------ summaries
+
+@pytest.mark.parametrize("mode", ["reweight", "meanpool"])
+def test_summaries_parity(mid, tiny, mode):
+    flags = ops.BSA_MEANPOOL if mode == "meanpool" else 0
+    for wl, q, k, v, pq, pk, lists in (mid, tiny):
+        dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+        kt, vt, b = ops.summaries(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt),
+                                  torch.from_numpy(pk).to(DEV), flags=flags)
+        for h in range(q.shape[0]):
+            rkt, rvt, rb = O.summaries(q[h], k[h], v[h], pk[h], mode=mode)
+            assert np.max(np.abs(kt[h].cpu().numpy() - rkt)) < 2e-5 * max(1, np.abs(rkt).max())
+            assert np.max(np.abs(vt[h].cpu().numpy() - rvt)) < 2e-5 * max(1, np.abs(rvt).max())
+            assert np.max(np.abs(b[h].cpu().numpy() - rb)) < 2e-5
+
+
+# ------------------------------------------------------------------------ attention
+
+def _oracle_attn(q, k, v, pq, pk, lists, mode="reweight", branches=False):
+    outs = [O.sparse_attention_head(q[h], k[h], v[h], pq[h], pk[h], lists[h], mode=mode,
+                                    return_branches=branches) for h in range(q.shape[0])]
+    return [np.stack([o[i] for o in outs]) for i in range(len(outs[0]))]
+
+
+def test_attention_parity_f32_tiny(tiny):
+    wl, q, k, v, pq, pk, lists = tiny
+    dt = torch.float32
+    o, lse = ops.sparse_attn(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt),
+                             torch.from_numpy(pq).to(DEV), torch.from_numpy(pk).to(DEV),
+                             torch.from_numpy(lists).to(DEV), with_lse=True)
+    ro, rl = _oracle_attn(q, k, v, pq, pk, lists)
+    assert np.max(np.abs(o.cpu().numpy() - ro)) < 1e-4
+    assert np.max(np.abs(lse.cpu().numpy() - rl)) < 1e-4
+
+
+@pytest.mark.parametrize("mode", ["reweight", "meanpool"])
+def test_attention_parity_bf16_mid(mid, mode):
+    wl, q, k, v, pq, pk, lists = mid
+    flags = ops.BSA_MEANPOOL if mode == "meanpool" else 0
+    dt = torch.bfloat16
+    o, lse = ops.sparse_attn(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt),
+                             torch.from_numpy(pq).to(DEV), torch.from_numpy(pk).to(DEV),
+                             torch.from_numpy(lists).to(DEV), flags=flags, with_lse=True)
+    ro, rl = _oracle_attn(q, k, v, pq, pk, lists, mode=mode)
+    got = o.float().cpu().numpy()
+    assert rel_l2(got, ro) < 1e-2
+    assert np.max(np.abs(got - ro)) < 3e-2
+    assert np.max(np.abs(lse.cpu().numpy() - rl)) < 3e-2
+
+
+def test_attention_branches_bf16(mid):
+    wl, q, k, v, pq, pk, lists = mid
+    dt = torch.bfloat16
+    args = (to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), torch.from_numpy(pq).to(DEV),
+            torch.from_numpy(pk).to(DEV), torch.from_numpy(lists).to(DEV))
+    oe, le = ops.sparse_attn(*args, flags=ops.BSA_EXACT_ONLY, with_lse=True)
+    oc, lc = ops.sparse_attn(*args, flags=ops.BSA_COMPRESSED_ONLY, with_lse=True)
+    _, _, ro_e, rl_e, ro_c, rl_c = _oracle_attn(q, k, v, pq, pk, lists, branches=True)
+    for got, ref in ((oe, ro_e), (oc, ro_c)):
+        g = got.float().cpu().numpy()
+        assert rel_l2(g, ref) < 1e-2 and np.max(np.abs(g - ref)) < 3e-2
+    assert np.max(np.abs(le.cpu().numpy() - rl_e)) < 3e-2
+    assert np.max(np.abs(lc.cpu().numpy() - rl_c)) < 3e-2
+
+
+def test_density_one_is_dense_bf16(mid):
+    wl, q, k, v, pq, pk, lists = mid
+    H, N, D = q.shape
+    nb = N // 64
+    allb = np.tile(np.arange(nb, dtype=np.int32), (H, nb, 1))
+    ident = synth.identity_perm(H, N)
+    dt = torch.bfloat16
+    o = ops.sparse_attn(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt),
+                        torch.from_numpy(ident).to(DEV), torch.from_numpy(ident).to(DEV),
+                        torch.from_numpy(allb).to(DEV))
+    rows = np.arange(0, N, 37)
+    ref = np.stack([O.dense_attention_head(q[h], k[h], v[h], rows=rows)[0] for h in range(H)])
+    got = o.float().cpu().numpy()[:, rows]
+    assert rel_l2(got, ref) < 1e-2 and np.max(np.abs(got - ref)) < 3e-2
+
+
+@pytest.mark.parametrize("n_blocks,topk", [(70, 9), (1, 1), (2, 1), (65, 65)])
+def test_attention_ragged_shapes_bf16(n_blocks, topk):
+    """Summary tiles with a ragged tail, a single block, density 1 with a partial tile."""
+    rng = np.random.default_rng(n_blocks)
+    H, N, D = 2, 64 * n_blocks, 128
+    q, k, v = (synth.bf16_round(rng.standard_normal((H, N, D)).astype(np.float32) * s)
+               for s in (0.3, 1.0, 1.0))
+    pq = np.stack([rng.permutation(N) for _ in range(H)]).astype(np.int32)
+    pk = np.stack([rng.permutation(N) for _ in range(H)]).astype(np.int32)
+    lists = np.sort(np.stack([[rng.choice(n_blocks, topk, replace=False) for _ in range(n_blocks)]
+                              for _ in range(H)]), axis=-1).astype(np.int32)
+    dt = torch.bfloat16
+    o, lse = ops.sparse_attn(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt),
+                             torch.from_numpy(pq).to(DEV), torch.from_numpy(pk).to(DEV),
+                             torch.from_numpy(lists).to(DEV), with_lse=True)
+    ro, rl = _oracle_attn(q, k, v, pq, pk, lists)
+    g = o.float().cpu().numpy()
+    assert rel_l2(g, ro) < 1e-2 and np.max(np.abs(g - ro)) < 3e-2
+    assert np.max(np.abs(lse.cpu().numpy() - rl)) < 3e-2
+
+
+def test_attention_is_deterministic(mid):
+    wl, q, k, v, pq, pk, lists = mid
+    dt = torch.bfloat16
+    args = (to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), torch.from_numpy(pq).to(DEV),
+            torch.from_numpy(pk).to(DEV), torch.from_numpy(lists).to(DEV))
+    a = ops.sparse_attn(*args)
+    b = ops.sparse_attn(*args)
+    assert torch.equal(a, b)
+
+
+# --------------------------------------------------------------------------- select
+
+def test_select_parity(mid, tiny):
+    for wl, q, k, v, pq, pk, lists in (mid, tiny):
+        dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+        got_l, got_s = ops.select(to_dev(q, dt), to_dev(k, dt), torch.from_numpy(pq).to(DEV),
+                                  torch.from_numpy(pk).to(DEV), topk_ratio=wl.topk_ratio,
+                                  with_scores=True)
+        got_l, got_s = got_l.cpu().numpy(), got_s.cpu().numpy()
+        K = O.topk_count(wl.n_blocks, wl.topk_ratio)
+        for h in range(q.shape[0]):
+            S = O.block_scores(q[h], k[h], pq[h], pk[h])
+            assert np.max(np.abs(got_s[h] - S)) < 1e-5 * max(1.0, np.abs(S).max())
+            # selection is exact on the GPU's own fp32 scores
+            assert np.array_equal(got_l[h], O.topk_lists(got_s[h], K))
+            # and agrees with the oracle's lists except where scores tie within 1e-5
+            for i in range(S.shape[0]):
+                a, b = set(got_l[h, i]), set(lists[h, i])
+                if a != b:
+                    kth = np.sort(S[i])[::-1][K - 1]
+                    for j in a ^ b:
+                        assert abs(S[i, j] - kth) <= 1e-5

@@ -1,0 +1,141 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every function the
+header declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+
+import pytest
+
+from block_sparse_video_reblock_amd import _lib
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        from block_sparse_video_reblock_amd import build
+        build.build()
+    return _lib.lib()
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails before any device work
+
+
+def desc(h=2, n=4096, d=128, dt=_lib.BSA_BF16):
+    return ctypes.byref(_lib.BsaDesc(h, n, d, dt))
+
+
+def test_exports_every_declared_function(L):
+    names = _lib.header_functions()
+    assert len(names) >= 11
+    for name in names:
+        assert hasattr(L, name), name
+
+
+def test_topk_count(L):
+    assert L.bsa_topk_count(1134, 0.1) == 113
+    assert L.bsa_topk_count(256, 0.2) == 51
+    assert L.bsa_topk_count(256, 0.3) == 76
+    assert L.bsa_topk_count(64, 0.25) == 16
+    assert L.bsa_topk_count(256, 1.0) == 256
+    assert L.bsa_topk_count(10, 0.7) == 7
+    assert L.bsa_topk_count(100, 1e-6) == 1
+    assert L.bsa_topk_count(100, 0.0) == -1
+    assert L.bsa_topk_count(100, 1.5) == -1
+    assert L.bsa_topk_count(0, 0.5) == -1
+
+
+def test_topk_count_matches_oracle(L):
+    import oracle
+    for nb in (1, 2, 7, 64, 256, 1134, 1620):
+        for r in (0.05, 0.1, 0.2, 0.25, 0.3, 0.7, 1.0):
+            assert L.bsa_topk_count(nb, r) == oracle.topk_count(nb, r)
+
+
+def test_workspace_bytes(L):
+    assert L.bsa_workspace_bytes(desc()) > 0
+    assert L.bsa_workspace_bytes(desc(n=100)) == 0
+    assert L.bsa_workspace_bytes(desc(d=64)) == 0                 # bf16 needs head_dim 128
+    assert L.bsa_workspace_bytes(desc(d=64, dt=_lib.BSA_F32)) > 0
+    assert L.bsa_workspace_bytes(None) == 0
+
+
+@pytest.mark.parametrize("d,code", [
+    ((0, 4096, 128, _lib.BSA_BF16), _lib.BSA_E_ARG),
+    ((2, 4000, 128, _lib.BSA_BF16), _lib.BSA_E_ARG),
+    ((2, 0, 128, _lib.BSA_BF16), _lib.BSA_E_ARG),
+    ((2, 4096, 64, _lib.BSA_BF16), _lib.BSA_E_UNSUPPORTED),
+    ((2, 4096, 128, _lib.BSA_F32), _lib.BSA_E_UNSUPPORTED),
+    ((2, 4096, 128, 7), _lib.BSA_E_UNSUPPORTED),
+    ((2, 1 << 23, 128, _lib.BSA_BF16), _lib.BSA_E_ARG),
+])
+def test_descriptor_errors(L, d, code):
+    st = L.bsa_sparse_attn(ctypes.byref(_lib.BsaDesc(*d)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                           4, 0, 0.0, FAKE, None, FAKE, 1 << 40, None)
+    assert st == code
+    assert L.bsa_last_error()
+
+
+def test_sparse_attn_argument_errors(L):
+    big = 1 << 40
+    args = [FAKE] * 6
+    # null tensor
+    assert L.bsa_sparse_attn(desc(), None, *args[1:], 4, 0, 0.0, FAKE, None, FAKE, big,
+                             None) == _lib.BSA_E_ARG
+    # topk out of range (nb = 64)
+    for k in (0, 65):
+        assert L.bsa_sparse_attn(desc(), *args, k, 0, 0.0, FAKE, None, FAKE, big,
+                                 None) == _lib.BSA_E_ARG
+    # unknown and exclusive flags
+    assert L.bsa_sparse_attn(desc(), *args, 4, 8, 0.0, FAKE, None, FAKE, big,
+                             None) == _lib.BSA_E_ARG
+    assert L.bsa_sparse_attn(desc(), *args, 4, 6, 0.0, FAKE, None, FAKE, big,
+                             None) == _lib.BSA_E_ARG
+    # bad scale
+    for sc in (-1.0, float("nan"), float("inf")):
+        assert L.bsa_sparse_attn(desc(), *args, 4, 0, sc, FAKE, None, FAKE, big,
+                                 None) == _lib.BSA_E_ARG
+    # workspace too small / null
+    assert L.bsa_sparse_attn(desc(), *args, 4, 0, 0.0, FAKE, None, FAKE, 16,
+                             None) == _lib.BSA_E_WORKSPACE
+    assert L.bsa_sparse_attn(desc(), *args, 4, 0, 0.0, FAKE, None, None, big,
+                             None) == _lib.BSA_E_ARG
+
+
+def test_select_argument_errors(L):
+    big = 1 << 40
+    a = [FAKE] * 4
+    assert L.bsa_select(desc(), *a, 0.0, 0, FAKE, None, FAKE, big, None) == _lib.BSA_E_ARG
+    assert L.bsa_select(desc(), *a, 1.5, 0, FAKE, None, FAKE, big, None) == _lib.BSA_E_ARG
+    assert L.bsa_select(desc(), *a, 0.1, 65, FAKE, None, FAKE, big, None) == _lib.BSA_E_ARG
+    assert L.bsa_select(desc(), *a, 0.1, -2, FAKE, None, FAKE, big, None) == _lib.BSA_E_ARG
+    assert L.bsa_select(desc(), *a, 0.1, 0, None, None, FAKE, big, None) == _lib.BSA_E_ARG
+    assert L.bsa_select(desc(), *a, 0.1, 0, FAKE, None, FAKE, 8, None) == _lib.BSA_E_WORKSPACE
+
+
+def test_reblock_and_hook_argument_errors(L):
+    big = 1 << 40
+    assert L.bsa_reblock(desc(), None, FAKE, FAKE, FAKE, None, FAKE, big, None) == _lib.BSA_E_ARG
+    assert L.bsa_reblock(desc(), FAKE, FAKE, FAKE, FAKE, None, FAKE, 8,
+                         None) == _lib.BSA_E_WORKSPACE
+    assert L.bsa_reblock_from_projections(0, 128, FAKE, FAKE, FAKE, big, None) == _lib.BSA_E_ARG
+    assert L.bsa_reblock_from_projections(2, 100, FAKE, FAKE, FAKE, big, None) == _lib.BSA_E_ARG
+    assert L.bsa_reblock_from_projections(2, 128, None, FAKE, FAKE, big, None) == _lib.BSA_E_ARG
+    assert L.bsa_reblock_from_projections(2, 128, FAKE, FAKE, FAKE, 4,
+                                          None) == _lib.BSA_E_WORKSPACE
+    assert L.bsa_topk_from_scores(4, 10, 0, FAKE, FAKE, None) == _lib.BSA_E_ARG
+    assert L.bsa_topk_from_scores(4, 10, 11, FAKE, FAKE, None) == _lib.BSA_E_ARG
+    assert L.bsa_topk_from_scores(0, 10, 1, FAKE, FAKE, None) == _lib.BSA_E_ARG
+    assert L.bsa_topk_from_scores(4, 10, 3, None, FAKE, None) == _lib.BSA_E_ARG
+    assert L.bsa_summaries(desc(), FAKE, FAKE, FAKE, FAKE, 2, 0.0, FAKE, FAKE, FAKE, FAKE, big,
+                           None) == _lib.BSA_E_ARG
+
+
+def test_architecture_is_checked(L, monkeypatch):
+    monkeypatch.setenv("BSATTN_ARCH_OVERRIDE", "gfx942")
+    st = L.bsa_topk_from_scores(4, 10, 3, FAKE, FAKE, None)
+    assert st == _lib.BSA_E_UNSUPPORTED
+    assert b"gfx942" in L.bsa_last_error()
+
+
+def test_status_strings(L):
+    for code in (0, -1, -2, -3, -4):
+        assert L.bsa_status_str(code)
