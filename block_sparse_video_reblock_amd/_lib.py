@@ -41,6 +41,11 @@ _SIGS = {
     "bsa_sparse_attn": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), _P, _P, _P, _P, _P, _P,
                                          ctypes.c_int32, ctypes.c_uint32, ctypes.c_float, _P, _P,
                                          _P, ctypes.c_size_t, _P]),
+    "bsa_prepare_kv": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), _P, _P, _P, _P, ctypes.c_uint32,
+                                        ctypes.c_float, _P, ctypes.c_size_t, _P]),
+    "bsa_attend": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), _P, _P, _P, _P, _P, _P,
+                                    ctypes.c_int32, ctypes.c_uint32, ctypes.c_float, _P, _P, _P,
+                                    ctypes.c_size_t, _P]),
     "bsa_summaries": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), _P, _P, _P, _P, ctypes.c_uint32,
                                        ctypes.c_float, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "bsa_partition_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int32]),
@@ -174,6 +179,27 @@ def sparse_attn(q, k, v, perm_q, perm_k, lists, flags=0, scale=0.0, ws=None, wit
                                 _dev_ptr(o, q.dtype), _dev_ptr(lse), _dev_ptr(ws), ws.numel(),
                                 _stream()))
     return (o, lse) if with_lse else o
+
+
+def prepare_kv(q, k, v, perm_k, ws, flags=0, scale=0.0):
+    """Anchor, summaries and swizzled key/value copies into ws (first phase of sparse_attn)."""
+    torch = _torch()
+    d = desc_for(q)
+    check(lib().bsa_prepare_kv(ctypes.byref(d), _dev_ptr(q, q.dtype), _dev_ptr(k, q.dtype),
+                               _dev_ptr(v, q.dtype), _dev_ptr(perm_k, torch.int32), int(flags),
+                               float(scale), _dev_ptr(ws), ws.numel(), _stream()))
+
+
+def attend(q, k, v, perm_q, perm_k, lists, ws, out, flags=0, scale=0.0, lse=None):
+    """Attention kernel alone on a ws filled by prepare_kv (second phase of sparse_attn)."""
+    torch = _torch()
+    d = desc_for(q)
+    check(lib().bsa_attend(ctypes.byref(d), _dev_ptr(q, q.dtype), _dev_ptr(k, q.dtype),
+                           _dev_ptr(v, q.dtype), _dev_ptr(perm_q, torch.int32),
+                           _dev_ptr(perm_k, torch.int32), _dev_ptr(lists, torch.int32),
+                           int(lists.shape[-1]), int(flags), float(scale), _dev_ptr(out, q.dtype),
+                           _dev_ptr(lse), _dev_ptr(ws), ws.numel(), _stream()))
+    return out
 
 
 def summaries(q, k, v, perm_k, flags=0, scale=0.0, ws=None):

@@ -265,30 +265,34 @@ bsa_status bsa_summaries(const bsa_desc* d, const void* q, const void* k, const 
                     "summaries launch");
 }
 
-bsa_status bsa_sparse_attn(const bsa_desc* d, const void* q, const void* k, const void* v,
-                           const int32_t* perm_q, const int32_t* perm_k, const int32_t* lists,
-                           int32_t topk, uint32_t flags, float scale, void* o, float* lse_opt,
-                           void* ws, size_t ws_bytes, hipStream_t stream) {
+namespace {
+
+bsa_status check_attn_args(const bsa_desc* d, const void* q, const void* k, const void* v,
+                           const int32_t* perm_k, uint32_t flags, float scale) {
   bsa_status st = check_desc(d);
   if (st != BSA_OK) return st;
-  if (!q || !k || !v || !perm_q || !perm_k || !lists || !o)
-    return fail(BSA_E_ARG, "null tensor pointer");
-  const int nb = d->tokens / BSA_BLOCK;
-  if (topk < 1 || topk > nb) return fail(BSA_E_ARG, "topk = %d is not in [1, %d]", topk, nb);
+  if (!q || !k || !v || !perm_k) return fail(BSA_E_ARG, "null tensor pointer");
   const uint32_t known = BSA_MEANPOOL | BSA_EXACT_ONLY | BSA_COMPRESSED_ONLY;
   if (flags & ~known) return fail(BSA_E_ARG, "unknown flags 0x%x", flags);
   if ((flags & BSA_EXACT_ONLY) && (flags & BSA_COMPRESSED_ONLY))
     return fail(BSA_E_ARG, "BSA_EXACT_ONLY and BSA_COMPRESSED_ONLY are exclusive");
   if (!(std::isfinite(scale) && scale >= 0.f)) return fail(BSA_E_ARG, "bad scale %g", scale);
-  const AttnWs L = attn_layout(d);
-  st = check_ws(ws, ws_bytes, L.total);
-  if (st != BSA_OK) return st;
-  st = check_device();
-  if (st != BSA_OK) return st;
+  return ok();
+}
 
+bsa_status check_attend_args(const bsa_desc* d, const int32_t* perm_q, const int32_t* lists,
+                             int32_t topk, void* o) {
+  if (!perm_q || !lists || !o) return fail(BSA_E_ARG, "null tensor pointer");
+  const int nb = d->tokens / BSA_BLOCK;
+  if (topk < 1 || topk > nb) return fail(BSA_E_ARG, "topk = %d is not in [1, %d]", topk, nb);
+  return ok();
+}
+
+hipError_t do_prepare(const bsa_desc* d, const AttnWs& L, void* ws, const void* q,
+                      const void* k, const void* v, const int32_t* perm_k, uint32_t flags,
+                      float sc, hipStream_t stream) {
   const bool bf = is_bf16(d);
-  const float sc = resolve_scale(d, scale);
-  const int nt = bsa::summary_tiles(nb);
+  const int nb = d->tokens / BSA_BLOCK, nt = bsa::summary_tiles(nb);
   float* kt = reinterpret_cast<float*>(at(ws, L.kt));
   float* vt = reinterpret_cast<float*>(at(ws, L.vt));
   float* bias = reinterpret_cast<float*>(at(ws, L.bias));
@@ -297,7 +301,14 @@ bsa_status bsa_sparse_attn(const bsa_desc* d, const void* q, const void* k, cons
   if (e == hipSuccess && bf)
     e = bsa::launch_summary_tiles(kt, vt, bias, d->heads, nb, at(ws, L.ktsw), at(ws, L.vtsw),
                                   stream);
-  if (e != hipSuccess) return hip_status(e, "summaries launch");
+  return e;
+}
+
+hipError_t do_attend(const bsa_desc* d, const AttnWs& L, void* ws, const void* q,
+                     const void* k, const void* v, const int32_t* perm_q,
+                     const int32_t* perm_k, const int32_t* lists, int32_t topk, uint32_t flags,
+                     float sc, void* o, float* lse, hipStream_t stream) {
+  const int nb = d->tokens / BSA_BLOCK, nt = bsa::summary_tiles(nb);
   bsa::AttnLaunch a{};
   a.H = d->heads;
   a.N = d->tokens;
@@ -309,24 +320,77 @@ bsa_status bsa_sparse_attn(const bsa_desc* d, const void* q, const void* k, cons
   a.q = q;
   a.perm_q = perm_q;
   a.lists = lists;
-  a.bias = bias;
+  a.bias = reinterpret_cast<const float*>(at(ws, L.bias));
   a.o = o;
-  a.lse = lse_opt;
-  if (bf) {
+  a.lse = lse;
+  if (is_bf16(d)) {
     a.ksw = at(ws, L.ksw);
     a.vsw = at(ws, L.vsw);
     a.ktsw = at(ws, L.ktsw);
     a.vtsw = at(ws, L.vtsw);
-    e = bsa::launch_attn_bf16(a, stream);
-  } else {
-    a.k = k;
-    a.v = v;
-    a.perm_k = perm_k;
-    a.kt = kt;
-    a.vt = vt;
-    e = bsa::launch_attn_f32(a, stream);
+    return bsa::launch_attn_bf16(a, stream);
   }
-  return hip_status(e, "attention launch");
+  a.k = k;
+  a.v = v;
+  a.perm_k = perm_k;
+  a.kt = reinterpret_cast<const float*>(at(ws, L.kt));
+  a.vt = reinterpret_cast<const float*>(at(ws, L.vt));
+  return bsa::launch_attn_f32(a, stream);
+}
+
+}  // namespace
+
+bsa_status bsa_prepare_kv(const bsa_desc* d, const void* q, const void* k, const void* v,
+                          const int32_t* perm_k, uint32_t flags, float scale, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  bsa_status st = check_attn_args(d, q, k, v, perm_k, flags, scale);
+  if (st != BSA_OK) return st;
+  const AttnWs L = attn_layout(d);
+  st = check_ws(ws, ws_bytes, L.total);
+  if (st != BSA_OK) return st;
+  st = check_device();
+  if (st != BSA_OK) return st;
+  return hip_status(do_prepare(d, L, ws, q, k, v, perm_k, flags, resolve_scale(d, scale), stream),
+                    "prepare launch");
+}
+
+bsa_status bsa_attend(const bsa_desc* d, const void* q, const void* k, const void* v,
+                      const int32_t* perm_q, const int32_t* perm_k, const int32_t* lists,
+                      int32_t topk, uint32_t flags, float scale, void* o, float* lse_opt,
+                      void* ws, size_t ws_bytes, hipStream_t stream) {
+  bsa_status st = check_attn_args(d, q, k, v, perm_k, flags, scale);
+  if (st != BSA_OK) return st;
+  st = check_attend_args(d, perm_q, lists, topk, o);
+  if (st != BSA_OK) return st;
+  const AttnWs L = attn_layout(d);
+  st = check_ws(ws, ws_bytes, L.total);
+  if (st != BSA_OK) return st;
+  st = check_device();
+  if (st != BSA_OK) return st;
+  return hip_status(do_attend(d, L, ws, q, k, v, perm_q, perm_k, lists, topk, flags,
+                              resolve_scale(d, scale), o, lse_opt, stream),
+                    "attention launch");
+}
+
+bsa_status bsa_sparse_attn(const bsa_desc* d, const void* q, const void* k, const void* v,
+                           const int32_t* perm_q, const int32_t* perm_k, const int32_t* lists,
+                           int32_t topk, uint32_t flags, float scale, void* o, float* lse_opt,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  bsa_status st = check_attn_args(d, q, k, v, perm_k, flags, scale);
+  if (st != BSA_OK) return st;
+  st = check_attend_args(d, perm_q, lists, topk, o);
+  if (st != BSA_OK) return st;
+  const AttnWs L = attn_layout(d);
+  st = check_ws(ws, ws_bytes, L.total);
+  if (st != BSA_OK) return st;
+  st = check_device();
+  if (st != BSA_OK) return st;
+  const float sc = resolve_scale(d, scale);
+  hipError_t e = do_prepare(d, L, ws, q, k, v, perm_k, flags, sc, stream);
+  if (e != hipSuccess) return hip_status(e, "prepare launch");
+  return hip_status(do_attend(d, L, ws, q, k, v, perm_q, perm_k, lists, topk, flags, sc, o,
+                              lse_opt, stream),
+                    "attention launch");
 }
 
 size_t bsa_partition_workspace_bytes(int32_t problems, int32_t tokens) {

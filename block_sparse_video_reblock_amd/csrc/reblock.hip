@@ -1,6 +1,33 @@
-// Reblock (stage 1): per-head second moments, Mahalanobis-cosine embedding and the
-// capacity-constrained hierarchical tree partition into 64-token leaves.  See tree.h for the
-// split rule and the layout invariants.
+// Reblock (stage 1) for gfx950: per-head second moments, Mahalanobis-cosine normalisation and
+// the capacity-constrained hierarchical tree partition into 64-token leaves.
+//
+// [comfy.icu "MiniMax H3 Spark Attention (SM89)", "What it's doing under the hood"]: queries are
+// compared through M_K = E[k k^T] and keys through M_Q = E[q q^T] (a Mahalanobis cosine); a
+// capacity-constrained tree partition splits them into exactly-64-token leaves, recomputed per
+// layer, step and head; Q/K/V are never modified, only the permutation.
+// [comfyui-wiki.com "Spark-H3 ...", "What Spark-Attn changes"]: two queries are alike when their
+// attention score patterns over the keys are alike; the partitioner splits until every leaf has
+// the block size, in O(N log N).
+//
+// Split rule (plain reading, see tree.h): principal direction of the group in the metric, found
+// by 8 power steps from the group's smallest token id, and a capacity cut at floor(m/2) blocks.
+//
+// Formulation on the GPU.  With y_i = x_i / sqrt(x_i^T M x_i) and any F with F^T F = M, the unit
+// vectors of the metric are u_i = F y_i.  Writing the power step v <- C_u v / |C_u v| in terms of
+// w = F^T v gives   z = C_y w,  t = M z,  w <- t / sqrt(z . t),   start w0 = M (y_i0 - mu),
+// and the projection u_i . v = y_i . w.  So no factorisation of M is needed: the kernels keep
+// the group covariance of y (C_y) and M, both 128 x 128 fp32.
+//
+// Per level and group: C_y is accumulated by MFMA from bf16 splits of the centred values
+// d = y - shift (shift = the parent group's mean, so cancellation stays small):
+// d = hi + mid + lo (three bf16 terms) and the six products down to 2^-24 relative size are
+// accumulated in fp32 (two terms, dropping lo lo^T, leave errors near 1e-5 in the projections of
+// ill-conditioned groups; three terms match an exact covariance).  Wide levels
+// (few large groups) split each group over several workgroups and reduce the partials in a fixed
+// order; narrow levels run one fused workgroup per group.  All reductions have a fixed order,
+// so results are deterministic.
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 #include "tree.h"
@@ -8,10 +35,688 @@
 namespace bsa {
 namespace {
 
-__global__ void k_identity(int N, int32_t* __restrict__ out) {
+constexpr int kMomChunk = 2048;   // tokens per partial of the second-moment reduction
+constexpr int kSlots = 32;        // workgroups per problem at the wide levels
+constexpr int kIters = 8;         // power steps per split
+constexpr int kStageStride = 72;  // bf16 elements per LDS row of the staged (transposed) chunk
+
+BSA_DEV bf16x8_t lds_bf16x8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
+}
+
+// Register-resident D x D accumulator: 4 waves, each holding TILES 32 x 32 MFMA tiles.
+template <int D>
+struct Cov {
+  static constexpr int AC = D / 32;
+  static constexpr int TILES = AC * AC / 4;
+  BSA_DEV static int ac(int w, int t) { return D == 128 ? w : (w >> 1); }
+  BSA_DEV static int bc(int w, int t) { return D == 128 ? t : (w & 1); }
+};
+
+template <int D>
+struct StageLds {
+  uint16_t hi[D][kStageStride];
+  uint16_t mid[D][kStageStride];
+  uint16_t lo[D][kStageStride];
+};
+
+template <typename T, int E>
+BSA_DEV void load_row(const T* p, float* out);
+template <>
+BSA_DEV void load_row<uint16_t, 32>(const uint16_t* p, float* out) {
+  const uint4* v = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 u = v[i];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      out[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
+      out[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+    }
+  }
+}
+template <>
+BSA_DEV void load_row<float, 16>(const float* p, float* out) {
+  const float4* v = reinterpret_cast<const float4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 u = v[i];
+    out[4 * i] = u.x;
+    out[4 * i + 1] = u.y;
+    out[4 * i + 2] = u.z;
+    out[4 * i + 3] = u.w;
+  }
+}
+
+// One 64-position chunk of the covariance accumulation.  Thread (s = tid/4, q = tid%4) stages
+// token s, elements [q E, q E + E) of d = x * scale - shift; dpart accumulates d.
+// tokmap == nullptr means position = token id; inv_n == nullptr means scale 1.
+// TERMS = 1: d is exact in bf16 (raw bf16 inputs).  TERMS = 3: d = hi + mid + lo (bf16 each,
+// 24 significant bits) and the products hi hi, hi mid, mid hi, hi lo, lo hi, mid mid are
+// accumulated; the dropped terms are below fp32 rounding of the sum.
+template <typename T, int D, int TERMS>
+BSA_DEV void stats_chunk(const T* __restrict__ X, const int32_t* __restrict__ tokmap,
+                         const float* __restrict__ inv_n, int c0, const float* sh_shift,
+                         StageLds<D>& st, f32x16_t* acc, float* dpart) {
+  constexpr int E = D / 4;
+  const int tid = threadIdx.x, s = tid >> 2, q = tid & 3;
+  const int tok = tokmap ? tokmap[c0 + s] : c0 + s;
+  const float sc = inv_n ? inv_n[tok] : 1.f;
+  float xv[E];
+  load_row<T, E>(X + (size_t)tok * D + q * E, xv);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const float d = xv[e] * sc - sh_shift[q * E + e];
+    dpart[e] += d;
+    const uint16_t h = f32_to_bf16(d);
+    st.hi[q * E + e][s] = h;
+    if (TERMS == 3) {
+      const float r1 = d - bf16_to_f32(h);
+      const uint16_t m = f32_to_bf16(r1);
+      st.mid[q * E + e][s] = m;
+      st.lo[q * E + e][s] = f32_to_bf16(r1 - bf16_to_f32(m));
+    }
+  }
+  __syncthreads();
+  const int lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+    for (int t = 0; t < Cov<D>::TILES; ++t) {
+      const int ra = 32 * Cov<D>::ac(w, t) + l32, rb = 32 * Cov<D>::bc(w, t) + l32;
+      const int col = 16 * ks + 8 * g;
+      const bf16x8_t aH = lds_bf16x8(&st.hi[ra][col]);
+      const bf16x8_t bH = lds_bf16x8(&st.hi[rb][col]);
+      acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aH, bH, acc[t], 0, 0, 0);
+      if (TERMS == 3) {
+        const bf16x8_t aM = lds_bf16x8(&st.mid[ra][col]);
+        const bf16x8_t bM = lds_bf16x8(&st.mid[rb][col]);
+        const bf16x8_t aL = lds_bf16x8(&st.lo[ra][col]);
+        const bf16x8_t bL = lds_bf16x8(&st.lo[rb][col]);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aH, bM, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aM, bH, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aH, bL, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aL, bH, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aM, bM, acc[t], 0, 0, 0);
+      }
+    }
+  }
+  __syncthreads();
+}
+
+template <int D>
+BSA_DEV void zero_acc(f32x16_t* acc) {
+#pragma unroll
+  for (int t = 0; t < Cov<D>::TILES; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
+}
+
+// Sum the per-thread d partials over the 64 token slots: result in out[D] (LDS).
+// red needs 4*D floats of LDS.
+template <int D>
+BSA_DEV void reduce_dpart(const float* dpart, float* red, float* out) {
+  constexpr int E = D / 4;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, q = tid & 3;
+  float v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    float x = dpart[e];
+    // lanes with the same q: xor over lane bits 2..5
+    x += __shfl_xor(x, 4, 64);
+    x += __shfl_xor(x, 8, 64);
+    x += __shfl_xor(x, 16, 64);
+    x += __shfl_xor(x, 32, 64);
+    v[e] = x;
+  }
+  if (lane < 4) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) red[w * D + q * E + e] = v[e];
+  }
+  __syncthreads();
+  for (int d = tid; d < D; d += 256) out[d] = red[d] + red[D + d] + red[2 * D + d] + red[3 * D + d];
+  __syncthreads();
+}
+
+// Register dump order of an accumulator: element ((w*TILES + t)*16 + r)*64 + lane.
+template <int D>
+BSA_DEV void store_acc(float* dst, const f32x16_t* acc) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int t = 0; t < Cov<D>::TILES; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dst[((w * Cov<D>::TILES + t) * 16 + r) * 64 + lane] = acc[t][r];
+}
+template <int D>
+BSA_DEV void add_acc(const float* src, f32x16_t* acc) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int t = 0; t < Cov<D>::TILES; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[t][r] += src[((w * Cov<D>::TILES + t) * 16 + r) * 64 + lane];
+}
+
+// (a, b) coordinates of accumulator element (t, r) of this lane
+template <int D>
+BSA_DEV int acc_row(int t, int r) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  return 32 * Cov<D>::ac(w, t) + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+template <int D>
+BSA_DEV int acc_col(int t) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  return 32 * Cov<D>::bc(w, t) + (lane & 31);
+}
+
+// out = C v for the symmetric register-resident C (column form).  red: AC*D floats of LDS.
+template <int D>
+BSA_DEV void cov_matvec(const f32x16_t* acc, const float* v, float* out, float* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int t = 0; t < Cov<D>::TILES; ++t) {
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s = fmaf(acc[t][r], v[acc_row<D>(t, r)], s);
+    s += __shfl_xor(s, 32, 64);
+    if (lane < 32) red[Cov<D>::ac(w, t) * D + acc_col<D>(t)] = s;
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < D; b += 256) {
+    float s = 0.f;
+#pragma unroll
+    for (int a = 0; a < Cov<D>::AC; ++a) s += red[a * D + b];
+    out[b] = s;
+  }
+  __syncthreads();
+}
+
+// M held in registers: thread t owns row t / R, columns [(t % R) * D / R, +D / R), R = 256 / D.
+template <int D>
+struct MRegs {
+  static constexpr int R = 256 / D;
+  static constexpr int W = D / R;
+  float m[W];
+  BSA_DEV void load(const float* M) {
+    const int row = threadIdx.x / R, c0 = (threadIdx.x % R) * W;
+#pragma unroll
+    for (int i = 0; i < W; ++i) m[i] = M[row * D + c0 + i];
+  }
+  BSA_DEV void matvec(const float* v, float* out) const {
+    const int row = threadIdx.x / R, c0 = (threadIdx.x % R) * W;
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < W; ++i) s = fmaf(m[i], v[c0 + i], s);
+#pragma unroll
+    for (int o = 1; o < R; o <<= 1) s += __shfl_xor(s, o, 64);
+    if (threadIdx.x % R == 0) out[row] = s;
+    __syncthreads();
+  }
+};
+
+// dot product of two LDS vectors, result broadcast to all threads.  sm: 4 floats.
+template <int D>
+BSA_DEV float block_dot(const float* a, const float* b, float* sm) {
+  const int tid = threadIdx.x;
+  float s = tid < D ? a[tid] * b[tid] : 0.f;
+  s = wave_sum(s);
+  if ((tid & 63) == 0) sm[tid >> 6] = s;
+  __syncthreads();
+  const float r = sm[0] + sm[1] + sm[2] + sm[3];
+  __syncthreads();
+  return r;
+}
+
+struct DirLds {
+  float shift[128];
+  float mu[128];
+  float e0[128];
+  float w[128];
+  float z[128];
+  float t[128];
+  float red[4 * 128];
+  float sm[8];
+  int flag;
+};
+
+// Finish a group's statistics and find its split direction.  On entry acc holds
+// sum (y - shift)(y - shift)^T over the group's n tokens and L.mu holds sum (y - shift).
+// On exit L.w holds the direction w (zero for a group without spread) and L.mu the mean.
+template <typename T, int D>
+BSA_DEV void group_direction(f32x16_t* acc, DirLds& L, const MRegs<D>& M, int n,
+                             const T* __restrict__ X, const int32_t* __restrict__ tokmap,
+                             const float* __restrict__ inv_n, int pos0) {
+  const int tid = threadIdx.x;
+  const float inv = 1.f / float(n);
+  if (tid < D) L.z[tid] = L.mu[tid] * inv;  // delta = mean - shift
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < Cov<D>::TILES; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      acc[t][r] = acc[t][r] * inv - L.z[acc_row<D>(t, r)] * L.z[acc_col<D>(t)];
+  if (tid < D) L.mu[tid] = L.shift[tid] + L.z[tid];
+  __syncthreads();
+  // start vector: the first position (smallest token id) whose centred vector is non-zero
+  bool found = false;
+  for (int p = pos0; p < pos0 + n; ++p) {
+    const int tok = tokmap[p];
+    if (tid == 0) L.flag = 0;
+    __syncthreads();
+    if (tid < D) {
+      const float e = load_as_f32(X + (size_t)tok * D + tid) * inv_n[tok] - L.mu[tid];
+      L.e0[tid] = e;
+      if (e != 0.f) L.flag = 1;
+    }
+    __syncthreads();
+    found = L.flag != 0;
+    __syncthreads();
+    if (found) break;
+  }
+  if (!found) {
+    if (tid < D) L.w[tid] = 0.f;
+    __syncthreads();
+    return;
+  }
+  M.matvec(L.e0, L.w);
+  for (int it = 0; it < kIters; ++it) {
+    cov_matvec<D>(acc, L.w, L.z, L.red);
+    M.matvec(L.z, L.t);
+    const float nrm2 = block_dot<D>(L.z, L.t, L.sm);
+    if (!(nrm2 > 0.f)) {
+      if (tid < D) L.w[tid] = 0.f;
+      __syncthreads();
+      return;
+    }
+    const float rn = 1.f / sqrtf(nrm2);
+    if (tid < D) L.w[tid] = L.t[tid] * rn;
+    __syncthreads();
+  }
+  const float o = block_dot<D>(L.e0, L.w, L.sm);
+  if (o < 0.f && tid < D) L.w[tid] = -L.w[tid];
+  __syncthreads();
+}
+
+// projections of 64 positions [c0, c0+64): key = inv_n * (x . w); 4 threads per position
+template <typename T, int D>
+BSA_DEV void project_chunk(const T* __restrict__ X, const int32_t* __restrict__ tokmap,
+                           const float* __restrict__ inv_n, int c0, const float* w,
+                           float* __restrict__ keys, float* __restrict__ proj_out) {
+  constexpr int E = D / 4;
+  const int tid = threadIdx.x, s = tid >> 2, q = tid & 3;
+  const int tok = tokmap[c0 + s];
+  float xv[E];
+  load_row<T, E>(X + (size_t)tok * D + q * E, xv);
+  float a = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) a = fmaf(xv[e], w[q * E + e], a);
+  a += __shfl_xor(a, 1, 64);
+  a += __shfl_xor(a, 2, 64);
+  if (q == 0) {
+    const float key = a * inv_n[tok];
+    keys[c0 + s] = key;
+    if (proj_out) proj_out[tok] = key;
+  }
+}
+
+struct ProblemArgs {
+  const void* q;
+  const void* k;
+  int H, N, nb, L;
+  const float* mom;        // [H][2][D][D]: side 0 = M_Q, side 1 = M_K
+  const float* inv_n;      // [P][N]
+  const int32_t* in;       // [P][N]
+  int32_t* out;            // [P][N]
+  float* keys;             // [P][N]
+  float* mu_prev;          // [P][G][D] parent means (level - 1)
+  float* mu_cur;           // [P][G][D]
+  float* wdir;             // [P][G][D]
+  float* partial;          // [P][kSlots][D*D + D]
+  float* proj;             // optional [H][2][L][N]
+  int level, G, slices;
+};
+
+// problem p = 2h + side; side 0 partitions the queries under M_K, side 1 the keys under M_Q
+template <typename T, int D>
+BSA_DEV const T* problem_x(const ProblemArgs& a, int p) {
+  const T* base = static_cast<const T*>((p & 1) ? a.k : a.q);
+  return base + (size_t)(p >> 1) * a.N * D;
+}
+template <int D>
+BSA_DEV const float* problem_metric(const ProblemArgs& a, int p) {
+  return a.mom + ((size_t)(p >> 1) * 2 + ((p & 1) ? 0 : 1)) * D * D;
+}
+BSA_DEV float* problem_proj(const ProblemArgs& a, int p) {
+  return a.proj ? a.proj + ((size_t)p * a.L + a.level) * a.N : nullptr;
+}
+
+// ------------------------------------------------------------------- second moments
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_moments(const T* __restrict__ q,
+                                                 const T* __restrict__ k, int N,
+                                                 float* __restrict__ partial) {
+  constexpr int TERMS = sizeof(T) == 4 ? 3 : 1;
+  __shared__ StageLds<D> st;
+  __shared__ float zero[D];
+  const int chunk = blockIdx.x, side = blockIdx.y, h = blockIdx.z, nch = gridDim.x;
+  const T* X = (side ? k : q) + (size_t)h * N * D;
+  if (threadIdx.x < D) zero[threadIdx.x] = 0.f;
+  __syncthreads();
+  f32x16_t acc[Cov<D>::TILES];
+  zero_acc<D>(acc);
+  float dpart[D / 4];
+#pragma unroll
+  for (int e = 0; e < D / 4; ++e) dpart[e] = 0.f;
+  const int t1 = min(N, (chunk + 1) * kMomChunk);
+  for (int c0 = chunk * kMomChunk; c0 < t1; c0 += kBlk)
+    stats_chunk<T, D, TERMS>(X, nullptr, nullptr, c0, zero, st, acc, dpart);
+  store_acc<D>(partial + (((size_t)h * 2 + side) * nch + chunk) * D * D, acc);
+}
+
+// Sum the partials in order, divide by N, write M canonical and (bf16 path) its 3-term bf16 split
+template <int D>
+__global__ __launch_bounds__(256) void k_moments_finish(const float* __restrict__ partial,
+                                                        int nch, int N, float* __restrict__ mom,
+                                                        uint16_t* __restrict__ msplit) {
+  const int side = blockIdx.x, h = blockIdx.y;
+  f32x16_t acc[Cov<D>::TILES];
+  zero_acc<D>(acc);
+  const size_t mi = (size_t)h * 2 + side;
+  for (int c = 0; c < nch; ++c) add_acc<D>(partial + (mi * nch + c) * D * D, acc);
+  const float inv = 1.f / float(N);
+#pragma unroll
+  for (int t = 0; t < Cov<D>::TILES; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int a = acc_row<D>(t, r), b = acc_col<D>(t);
+      const float m = acc[t][r] * inv;
+      mom[mi * D * D + a * D + b] = m;
+      if (msplit) {
+        const uint16_t h1 = f32_to_bf16(m);
+        const float r1 = m - bf16_to_f32(h1);
+        const uint16_t h2 = f32_to_bf16(r1);
+        const uint16_t h3 = f32_to_bf16(r1 - bf16_to_f32(h2));
+        msplit[(mi * 3 + 0) * D * D + a * D + b] = h1;
+        msplit[(mi * 3 + 1) * D * D + a * D + b] = h2;
+        msplit[(mi * 3 + 2) * D * D + a * D + b] = h3;
+      }
+    }
+}
+
+// ---------------------------------------------------------------- metric norms (bf16)
+// inv_n[p][t] = 1 / sqrt(x_t^T M x_t) (0 if that is 0) and per-64-token sums of y = x inv_n.
+// Y^T = M X^T by MFMA with M in three bf16 terms; wave w computes rows [32w, 32w+32).
+__global__ __launch_bounds__(256) void k_norms_bf16(ProblemArgs a, const uint16_t* __restrict__ msplit,
+                                                    float* __restrict__ inv_n_out,
+                                                    float* __restrict__ ysum) {
+  constexpr int D = 128;
+  __shared__ float red[4][64];
+  __shared__ float s_inv[64];
+  __shared__ float s_half[D];
+  const int chunk = blockIdx.x, p = blockIdx.y, nch = gridDim.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  const uint16_t* X = problem_x<uint16_t, D>(a, p);
+  const int mi = (p >> 1) * 2 + ((p & 1) ? 0 : 1);
+  const uint16_t* Ms = msplit + (size_t)mi * 3 * D * D;
+  const int c0 = chunk * kBlk;
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int tok = c0 + 32 * n + l32;
+    const uint16_t* xr = X + (size_t)tok * D;
+    f32x16_t acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const bf16x8_t xb = lds_bf16x8(xr + 16 * c + 8 * g);
+#pragma unroll
+      for (int s = 0; s < 3; ++s) {
+        const bf16x8_t mb = lds_bf16x8(Ms + (size_t)s * D * D + (32 * w + l32) * D + 16 * c + 8 * g);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mb, xb, acc, 0, 0, 0);
+      }
+    }
+    // lane holds (M x_tok)[b] for b = 32w + 8j + 4g + i
+    float part = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint2 u = *reinterpret_cast<const uint2*>(xr + 32 * w + 8 * j + 4 * g);
+      part = fmaf(acc[4 * j + 0], __uint_as_float(u.x << 16), part);
+      part = fmaf(acc[4 * j + 1], __uint_as_float(u.x & 0xFFFF0000u), part);
+      part = fmaf(acc[4 * j + 2], __uint_as_float(u.y << 16), part);
+      part = fmaf(acc[4 * j + 3], __uint_as_float(u.y & 0xFFFF0000u), part);
+    }
+    part += __shfl_xor(part, 32, 64);
+    if (g == 0) red[w][32 * n + l32] = part;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    const float n2 = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+    const float inv = n2 > 0.f ? 1.f / sqrtf(n2) : 0.f;
+    s_inv[tid] = inv;
+    inv_n_out[(size_t)p * a.N + c0 + tid] = inv;
+  }
+  __syncthreads();
+  // sum of y over the chunk, two threads per element
+  {
+    const int d = tid & (D - 1), half = tid >> 7;
+    float s = 0.f;
+    for (int t = 32 * half; t < 32 * half + 32; ++t)
+      s = fmaf(bf16_to_f32(X[(size_t)(c0 + t) * D + d]), s_inv[t], s);
+    if (half == 1) s_half[d] = s;
+    __syncthreads();
+    if (half == 0) ysum[((size_t)p * nch + chunk) * D + d] = s + s_half[d];
+  }
+}
+
+// fp32 path (D = 64): plain FMA, M in LDS; thread (s = tid/4, q = tid%4) -> token s, rows
+// [16q, 16q+16) of M x
+__global__ __launch_bounds__(256) void k_norms_f32(ProblemArgs a, float* __restrict__ inv_n_out,
+                                                   float* __restrict__ ysum) {
+  constexpr int D = 64;
+  __shared__ float sm[D][D + 1];
+  __shared__ float sx[64][D + 1];
+  __shared__ float s_inv[64];
+  const int chunk = blockIdx.x, p = blockIdx.y, nch = gridDim.x;
+  const int tid = threadIdx.x, s = tid >> 2, q = tid & 3;
+  const float* X = problem_x<float, D>(a, p);
+  const float* M = problem_metric<D>(a, p);
+  const int c0 = chunk * kBlk;
+  for (int e = tid; e < D * D; e += 256) sm[e / D][e % D] = M[e];
+  for (int e = tid; e < 64 * D; e += 256) sx[e / D][e % D] = X[(size_t)c0 * D + e];
+  __syncthreads();
+  float part = 0.f;
+  for (int b = 16 * q; b < 16 * q + 16; ++b) {
+    float y = 0.f;
+    for (int c = 0; c < D; ++c) y = fmaf(sm[b][c], sx[s][c], y);
+    part = fmaf(y, sx[s][b], part);
+  }
+  part += __shfl_xor(part, 1, 64);
+  part += __shfl_xor(part, 2, 64);
+  if (q == 0) {
+    const float inv = part > 0.f ? 1.f / sqrtf(part) : 0.f;
+    s_inv[s] = inv;
+    inv_n_out[(size_t)p * a.N + c0 + s] = inv;
+  }
+  __syncthreads();
+  if (tid < D) {
+    float acc = 0.f;
+    for (int t = 0; t < 64; ++t) acc = fmaf(sx[t][tid], s_inv[t], acc);
+    ysum[((size_t)p * nch + chunk) * D + tid] = acc;
+  }
+}
+
+// mu_root[p] = (1/N) sum of the chunk sums, stored as the "parent mean" of level 0
+template <int D>
+__global__ void k_root_mean(const float* __restrict__ ysum, int nch, int N, int G,
+                            float* __restrict__ mu) {
+  const int p = blockIdx.x, d = threadIdx.x;
+  if (d >= D) return;
+  float s = 0.f;
+  for (int c = 0; c < nch; ++c) s += ysum[((size_t)p * nch + c) * D + d];
+  mu[(size_t)p * G * D + d] = s / float(N);
+}
+
+// ---------------------------------------------------------------------- wide levels
+// grid (slices, G, P): partial statistics of one slice of one group
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_wide_stats(ProblemArgs a) {
+  __shared__ StageLds<D> st;
+  __shared__ float shift[D];
+  __shared__ float red[4 * D];
+  __shared__ float dsum[D];
+  const int s = blockIdx.x, g = blockIdx.y, p = blockIdx.z;
+  int b0, m;
+  if (group_geom(a.nb, a.level, g, b0, m) != kGroupSplit) return;
+  const int sb0 = b0 + (int)((long)s * m / a.slices), sb1 = b0 + (int)((long)(s + 1) * m / a.slices);
+  const T* X = problem_x<T, D>(a, p);
+  const int32_t* tokmap = a.in + (size_t)p * a.N;
+  const float* inv_n = a.inv_n + (size_t)p * a.N;
+  if (threadIdx.x < D)
+    shift[threadIdx.x] = a.mu_prev[((size_t)p * a.G + (g >> 1)) * D + threadIdx.x];
+  __syncthreads();
+  f32x16_t acc[Cov<D>::TILES];
+  zero_acc<D>(acc);
+  float dpart[D / 4];
+#pragma unroll
+  for (int e = 0; e < D / 4; ++e) dpart[e] = 0.f;
+  for (int b = sb0; b < sb1; ++b)
+    stats_chunk<T, D, 3>(X, tokmap, inv_n, b * kBlk, shift, st, acc, dpart);
+  reduce_dpart<D>(dpart, red, dsum);
+  float* slot = a.partial + ((size_t)p * kSlots + g * a.slices + s) * (D * D + D);
+  store_acc<D>(slot, acc);
+  if (threadIdx.x < D) slot[D * D + threadIdx.x] = dsum[threadIdx.x];
+}
+
+// grid (G, P): reduce the slices of a group and find its direction
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_wide_dir(ProblemArgs a) {
+  __shared__ DirLds L;
+  const int g = blockIdx.x, p = blockIdx.y;
+  int b0, m;
+  if (group_geom(a.nb, a.level, g, b0, m) != kGroupSplit) return;
+  f32x16_t acc[Cov<D>::TILES];
+  zero_acc<D>(acc);
+  const float* base = a.partial + ((size_t)p * kSlots + g * a.slices) * (D * D + D);
+  float ds = 0.f;
+  for (int s = 0; s < a.slices; ++s) {
+    add_acc<D>(base + (size_t)s * (D * D + D), acc);
+    if (threadIdx.x < D) ds += base[(size_t)s * (D * D + D) + D * D + threadIdx.x];
+  }
+  if (threadIdx.x < D) {
+    L.mu[threadIdx.x] = ds;
+    L.shift[threadIdx.x] = a.mu_prev[((size_t)p * a.G + (g >> 1)) * D + threadIdx.x];
+  }
+  __syncthreads();
+  MRegs<D> M;
+  M.load(problem_metric<D>(a, p));
+  group_direction<T, D>(acc, L, M, m * kBlk, problem_x<T, D>(a, p), a.in + (size_t)p * a.N,
+                        a.inv_n + (size_t)p * a.N, b0 * kBlk);
+  if (threadIdx.x < D) {
+    a.mu_cur[((size_t)p * a.G + g) * D + threadIdx.x] = L.mu[threadIdx.x];
+    a.wdir[((size_t)p * a.G + g) * D + threadIdx.x] = L.w[threadIdx.x];
+  }
+}
+
+// grid (nb, P): projections of one block's positions onto its group's direction
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_wide_proj(ProblemArgs a) {
+  __shared__ float w[D];
+  const int blk = blockIdx.x, p = blockIdx.y;
+  int b0, m;
+  const int g = group_of_block(a.nb, a.level, blk, b0, m);
+  if (g < 0 || m < 2) return;
+  if (threadIdx.x < D) w[threadIdx.x] = a.wdir[((size_t)p * a.G + g) * D + threadIdx.x];
+  __syncthreads();
+  project_chunk<T, D>(problem_x<T, D>(a, p), a.in + (size_t)p * a.N, a.inv_n + (size_t)p * a.N,
+                      blk * kBlk, w, a.keys + (size_t)p * a.N, problem_proj(a, p));
+}
+
+// grid (G, P): split threshold and stable partition (also carries leaves to the next buffer)
+__global__ __launch_bounds__(256) void k_wide_split(ProblemArgs a) {
+  __shared__ int hist[256];
+  __shared__ int sm[8];
+  const int g = blockIdx.x;
   const size_t p = blockIdx.y;
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < N; i += gridDim.x * 256)
-    out[p * N + i] = i;
+  int b0, m;
+  const int kind = group_geom(a.nb, a.level, g, b0, m);
+  if (kind == kGroupNone) return;
+  const size_t base = p * a.N + (size_t)b0 * kBlk;
+  const int n = m * kBlk;
+  if (kind == kGroupCopy) {
+    for (int i = threadIdx.x; i < n; i += 256) a.out[base + i] = a.in[base + i];
+    return;
+  }
+  const int want = (m >> 1) * kBlk;
+  int take;
+  const uint32_t T = block_select_smallest(a.keys + base, n, want, hist, sm, &take);
+  block_partition(a.keys + base, a.in + base, a.out + base, n, want, T, take, sm);
+}
+
+// -------------------------------------------------------------------- narrow levels
+// grid (G, P): one workgroup does the whole split of one group
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_narrow_level(ProblemArgs a) {
+  __shared__ StageLds<D> st;
+  __shared__ DirLds L;
+  __shared__ int hist[256];
+  __shared__ int sm[8];
+  const int g = blockIdx.x, p = blockIdx.y;
+  int b0, m;
+  const int kind = group_geom(a.nb, a.level, g, b0, m);
+  if (kind == kGroupNone) return;
+  const size_t base = (size_t)p * a.N + (size_t)b0 * kBlk;
+  const int n = m * kBlk;
+  if (kind == kGroupCopy) {
+    for (int i = threadIdx.x; i < n; i += 256) a.out[base + i] = a.in[base + i];
+    return;
+  }
+  const T* X = problem_x<T, D>(a, p);
+  const int32_t* tokmap = a.in + (size_t)p * a.N;
+  const float* inv_n = a.inv_n + (size_t)p * a.N;
+  if (threadIdx.x < D)
+    L.shift[threadIdx.x] = a.mu_prev[((size_t)p * a.G + (g >> 1)) * D + threadIdx.x];
+  __syncthreads();
+  f32x16_t acc[Cov<D>::TILES];
+  zero_acc<D>(acc);
+  {
+    float dpart[D / 4];
+#pragma unroll
+    for (int e = 0; e < D / 4; ++e) dpart[e] = 0.f;
+    for (int b = b0; b < b0 + m; ++b)
+      stats_chunk<T, D, 3>(X, tokmap, inv_n, b * kBlk, L.shift, st, acc, dpart);
+    reduce_dpart<D>(dpart, L.red, L.mu);
+  }
+  MRegs<D> M;
+  M.load(problem_metric<D>(a, p));
+  group_direction<T, D>(acc, L, M, n, X, tokmap, inv_n, b0 * kBlk);
+  if (threadIdx.x < D) a.mu_cur[((size_t)p * a.G + g) * D + threadIdx.x] = L.mu[threadIdx.x];
+  float* keys = a.keys + (size_t)p * a.N;
+  for (int b = b0; b < b0 + m; ++b)
+    project_chunk<T, D>(X, tokmap, inv_n, b * kBlk, L.w, keys, problem_proj(a, p));
+  __syncthreads();
+  const int want = (m >> 1) * kBlk;
+  int take;
+  const uint32_t T_ = block_select_smallest(a.keys + base, n, want, hist, sm, &take);
+  block_partition(a.keys + base, a.in + base, a.out + base, n, want, T_, take, sm);
+}
+
+// ------------------------------------------------------------------------- helpers
+__global__ void k_fill_identity(int N, int32_t* __restrict__ out) {
+  const size_t p = blockIdx.y;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < N; i += gridDim.x * 256) out[p * N + i] = i;
+}
+
+__global__ void k_fill_zero(size_t n, float* __restrict__ out) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    out[i] = 0.f;
+}
+
+// perm[side][h][.] = pos[2h + side][.]
+__global__ void k_split_out(int H, int N, const int32_t* __restrict__ pos,
+                            int32_t* __restrict__ perm_q, int32_t* __restrict__ perm_k) {
+  const size_t p = blockIdx.y;
+  int32_t* dst = ((p & 1) ? perm_k : perm_q) + (p >> 1) * (size_t)N;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < N; i += gridDim.x * 256) dst[i] = pos[p * N + i];
 }
 
 // keys[p][pos] = proj[p][level][in[p][pos]]
@@ -22,8 +727,107 @@ __global__ void k_gather_keys(int N, int L, int level, const float* __restrict__
     keys[p * N + i] = proj[(p * L + level) * N + in[p * N + i]];
 }
 
-// One workgroup per (group, problem) of a level: select the split threshold over the group's
-// keys (by position) and write the stable partition of the group's tokens.
+struct RebLayout {
+  size_t mom, mom_partial, msplit, inv_n, ysum, pos0, pos1, keys, mu0, mu1, wdir, partial, total;
+  int L, G, nch_mom, nch_n;
+};
+
+size_t al(size_t x) { return (x + 255) & ~size_t(255); }
+
+RebLayout reb_layout(int H, int N, int D) {
+  RebLayout r{};
+  const size_t P = 2 * (size_t)H, nb = N / kBlk;
+  r.L = tree_levels((int)nb);
+  r.G = r.L > 0 ? (1 << (r.L - 1)) : 1;
+  r.nch_mom = ceil_div(N, kMomChunk);
+  r.nch_n = (int)nb;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += al(bytes); return o; };
+  r.mom = take((size_t)H * 2 * D * D * 4);
+  r.mom_partial = take((size_t)H * 2 * r.nch_mom * D * D * 4);
+  r.msplit = take((size_t)H * 2 * 3 * D * D * 2);
+  r.inv_n = take(P * N * 4);
+  r.ysum = take(P * r.nch_n * D * 4);
+  r.pos0 = take(P * N * 4);
+  r.pos1 = take(P * N * 4);
+  r.keys = take(P * N * 4);
+  r.mu0 = take(P * r.G * D * 4);
+  r.mu1 = take(P * r.G * D * 4);
+  r.wdir = take(P * r.G * D * 4);
+  r.partial = take(P * kSlots * (size_t)(D * D + D) * 4);
+  r.total = off;
+  return r;
+}
+
+template <typename T, int D>
+hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm_q,
+                       int32_t* perm_k, float* proj_opt, void* ws, hipStream_t s) {
+  const RebLayout R = reb_layout(H, N, D);
+  char* w = static_cast<char*>(ws);
+  const int P = 2 * H, nb = N / kBlk;
+  const dim3 gridN(min(ceil_div(N, 256), 1024), P);
+  float* mom = reinterpret_cast<float*>(w + R.mom);
+  uint16_t* msplit = sizeof(T) == 2 ? reinterpret_cast<uint16_t*>(w + R.msplit) : nullptr;
+  k_moments<T, D><<<dim3(R.nch_mom, 2, H), 256, 0, s>>>(
+      static_cast<const T*>(q), static_cast<const T*>(k), N,
+      reinterpret_cast<float*>(w + R.mom_partial));
+  k_moments_finish<D><<<dim3(2, H), 256, 0, s>>>(reinterpret_cast<float*>(w + R.mom_partial),
+                                                 R.nch_mom, N, mom, msplit);
+  ProblemArgs a{};
+  a.q = q;
+  a.k = k;
+  a.H = H;
+  a.N = N;
+  a.nb = nb;
+  a.L = R.L;
+  a.mom = mom;
+  a.inv_n = reinterpret_cast<float*>(w + R.inv_n);
+  a.keys = reinterpret_cast<float*>(w + R.keys);
+  a.wdir = reinterpret_cast<float*>(w + R.wdir);
+  a.partial = reinterpret_cast<float*>(w + R.partial);
+  a.proj = proj_opt;
+  a.G = R.G;
+  float* mu[2] = {reinterpret_cast<float*>(w + R.mu0), reinterpret_cast<float*>(w + R.mu1)};
+  int32_t* pos[2] = {reinterpret_cast<int32_t*>(w + R.pos0), reinterpret_cast<int32_t*>(w + R.pos1)};
+  float* ysum = reinterpret_cast<float*>(w + R.ysum);
+  if (sizeof(T) == 2)
+    k_norms_bf16<<<dim3(R.nch_n, P), 256, 0, s>>>(a, msplit, reinterpret_cast<float*>(w + R.inv_n),
+                                                  ysum);
+  else
+    k_norms_f32<<<dim3(R.nch_n, P), 256, 0, s>>>(a, reinterpret_cast<float*>(w + R.inv_n), ysum);
+  // level -1 parent mean = mean of all y (the mean of level 0's single group)
+  k_root_mean<D><<<P, 128, 0, s>>>(ysum, R.nch_n, N, R.G, mu[1]);
+  if (proj_opt && R.L > 0) {
+    const size_t n = (size_t)P * R.L * N;
+    k_fill_zero<<<(unsigned)std::min<size_t>((n + 255) / 256, 4096), 256, 0, s>>>(n, proj_opt);
+  }
+  k_fill_identity<<<gridN, 256, 0, s>>>(N, pos[0]);
+  for (int level = 0; level < R.L; ++level) {
+    a.level = level;
+    a.in = pos[level & 1];
+    a.out = pos[(level + 1) & 1];
+    a.mu_prev = mu[(level + 1) & 1];
+    a.mu_cur = mu[level & 1];
+    const int G = 1 << level;
+    const int min_m = nb >> level;  // smallest group size at this level
+    int slices = min(kSlots >> min(level, 5), min_m);
+    if (slices < 1) slices = 1;
+    a.slices = slices;
+    if (slices > 1) {
+      k_wide_stats<T, D><<<dim3(slices, G, P), 256, 0, s>>>(a);
+      k_wide_dir<T, D><<<dim3(G, P), 256, 0, s>>>(a);
+      k_wide_proj<T, D><<<dim3(nb, P), 256, 0, s>>>(a);
+      k_wide_split<<<dim3(G, P), 256, 0, s>>>(a);
+    } else {
+      k_narrow_level<T, D><<<dim3(G, P), 256, 0, s>>>(a);
+    }
+  }
+  k_split_out<<<gridN, 256, 0, s>>>(H, N, pos[R.L & 1], perm_q, perm_k);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------- partition from given projections
+// One workgroup per (group, problem) of a level, keys already gathered by position.
 __global__ __launch_bounds__(256) void k_split_level(int N, int nb, int level,
                                                      const float* __restrict__ keys,
                                                      const int32_t* __restrict__ in,
@@ -59,8 +863,8 @@ hipError_t launch_partition_from_proj(int P, int N, const float* proj, int32_t* 
   int32_t* buf[2];
   buf[L & 1] = perm;
   buf[(L + 1) & 1] = tmp;
-  const dim3 grid_n(ceil_div(N, 256) < 1024 ? ceil_div(N, 256) : 1024, P);
-  k_identity<<<grid_n, 256, 0, s>>>(N, buf[0]);
+  const dim3 grid_n(min(ceil_div(N, 256), 1024), P);
+  k_fill_identity<<<grid_n, 256, 0, s>>>(N, buf[0]);
   for (int level = 0; level < L; ++level) {
     k_gather_keys<<<grid_n, 256, 0, s>>>(N, L, level, proj, buf[level & 1], keys);
     k_split_level<<<dim3(1 << level, P), 256, 0, s>>>(N, nb, level, keys, buf[level & 1],
@@ -69,12 +873,13 @@ hipError_t launch_partition_from_proj(int P, int N, const float* proj, int32_t* 
   return hipGetLastError();
 }
 
-size_t reblock_ws_bytes(int H, int N, int D) { return 256; }
+size_t reblock_ws_bytes(int H, int N, int D) { return reb_layout(H, N, D).total; }
 
 hipError_t launch_reblock(bool bf16, const void* q, const void* k, int H, int N, int D,
                           int32_t* perm_q, int32_t* perm_k, float* proj_opt, void* ws,
                           hipStream_t s) {
-  return hipErrorNotSupported;
+  if (bf16) return run_reblock<uint16_t, 128>(q, k, H, N, perm_q, perm_k, proj_opt, ws, s);
+  return run_reblock<float, 64>(q, k, H, N, perm_q, perm_k, proj_opt, ws, s);
 }
 
 }  // namespace bsa

@@ -26,8 +26,10 @@ head h.  The scene (Fourier features, cluster seeds, drifts, shifts) uses layer 
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 
 import numpy as np
 
@@ -75,12 +77,19 @@ def _rng(*words) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence(list(words))))
 
 
+def bf16_round_(x: np.ndarray) -> np.ndarray:
+    """In place: round finite float32 values to the nearest bfloat16 (ties to even)."""
+    bits = x.view(np.uint32)
+    lsb = (bits >> 16) & np.uint32(1)
+    bits += np.uint32(0x7FFF)
+    bits += lsb
+    bits &= np.uint32(0xFFFF0000)
+    return x
+
+
 def bf16_round(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to the nearest bfloat16 (ties to even); returns float32."""
-    x = np.ascontiguousarray(x, dtype=np.float32)
-    bits = x.view(np.uint32).astype(np.uint64)
-    bits = (bits + 0x7FFF + ((bits >> 16) & 1)) & 0xFFFF0000
-    return bits.astype(np.uint32).view(np.float32)
+    """Round finite float32 values to the nearest bfloat16 (ties to even); returns float32."""
+    return bf16_round_(np.array(x, dtype=np.float32, copy=True))
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -143,13 +152,15 @@ def make_qkv(wl: Workload, layer: int = 0, heads=None):
         base.append((phi @ G.astype(np.float32)) + mu.astype(np.float32)[region])
     N = wl.tokens
     out = np.empty((3, len(heads), N, D), dtype=np.float32)
-    for slot, h in enumerate(heads):
+
+    def one_head(slot):
+        h = heads[slot]
         gh = _rng(wl.seed_id, layer, 1 + h)
         for x in range(3):
-            eps = gh.standard_normal((N, D), dtype=np.float32)
+            eps = out[x, slot]
+            gh.standard_normal(dtype=np.float32, out=eps)
             eps *= np.float32(0.5)
             eps += base[x]
-            out[x, slot] = eps
         if wl.rotate_q:
             rot = _haar(gh, D).astype(np.float32)
             out[0, slot] = out[0, slot] @ rot
@@ -158,10 +169,14 @@ def make_qkv(wl: Workload, layer: int = 0, heads=None):
         qk = np.einsum("ij,ij->i", out[0, slot][qi].astype(np.float64),
                        out[1, slot][ki].astype(np.float64)) / math.sqrt(D)
         out[0, slot] *= np.float32(2.0 / qk.std())
-    if wl.dtype == "bf16":
-        for x in range(3):
-            for slot in range(len(heads)):
-                out[x, slot] = bf16_round(out[x, slot])
+        if wl.dtype == "bf16":
+            for x in range(3):
+                bf16_round_(out[x, slot])
+
+    # heads are independent streams; numpy releases the GIL in the bulk operations
+    workers = max(1, min(len(heads), 16, len(os.sched_getaffinity(0))))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(one_head, range(len(heads))))
     return out[0], out[1], out[2]
 
 

@@ -118,6 +118,20 @@ bsa_status bsa_sparse_attn(const bsa_desc* desc, const void* q, const void* k, c
                            void* o, float* lse_opt,
                            void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Two-phase form of bsa_sparse_attn, for callers that time the phases separately or reuse the
+ * prepared key side.  bsa_prepare_kv computes the anchor and the block summaries (and, for
+ * bf16, block-contiguous copies of K and V in the MFMA operand order) into ws;
+ * bsa_attend then runs the attention kernel alone.  bsa_attend must receive the same desc, k, v,
+ * perm_k, flags and scale as the bsa_prepare_kv call that filled ws, with nothing else written
+ * to ws in between; with that, prepare followed by attend equals bsa_sparse_attn. */
+bsa_status bsa_prepare_kv(const bsa_desc* desc, const void* q, const void* k, const void* v,
+                          const int32_t* perm_k, uint32_t flags, float scale,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+bsa_status bsa_attend(const bsa_desc* desc, const void* q, const void* k, const void* v,
+                      const int32_t* perm_q, const int32_t* perm_k,
+                      const int32_t* lists, int32_t topk, uint32_t flags, float scale,
+                      void* o, float* lse_opt, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* (4) Block summaries alone (the compressed branch's keys, values and biases), fp32:
  * kt[h][j][D], vt[h][j][D], bias[h][j].  Reweight (default): anchor qa = mean of the head's
  * queries, x_t = s qa.k_t over block j's keys, w = softmax(x), kt = sum w_t k_t,
