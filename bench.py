@@ -66,6 +66,9 @@ def main():
     ap.add_argument("--workload", default="clip10s_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run three device-to-device copies of MIB MiB (a plain copy kernel "
+                         "of known traffic, for scaling the HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer shards by head with no communication, so "
@@ -74,6 +77,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {args.calibrate_copy} MiB three times")
+        return
 
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     from block_sparse_video_reblock_amd import _lib as ops

@@ -31,12 +31,17 @@ constexpr int kMaxSelWords = (1 << 22) / 64 / 32;   // bitmap words for the larg
 
 BSA_DEV bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// Running-max slack: the online softmax keeps a stale maximum until a row's new maximum exceeds
+// it by more than this (log2 units), so probabilities stay below 2^8 and the accumulator is
+// rescaled only when the maximum really moves.  The result is the same softmax.
+constexpr float kMaxSlack = 8.f;
+
 BSA_DEV bf16x8_t pack8(const f32x16_t& s, int base) {
   uint4 u;
-  u.x = pack_bf16x2(s[base + 0], s[base + 1]);
-  u.y = pack_bf16x2(s[base + 2], s[base + 3]);
-  u.z = pack_bf16x2(s[base + 4], s[base + 5]);
-  u.w = pack_bf16x2(s[base + 6], s[base + 7]);
+  u.x = cvt_pk_bf16(s[base + 0], s[base + 1]);
+  u.y = cvt_pk_bf16(s[base + 2], s[base + 3]);
+  u.z = cvt_pk_bf16(s[base + 4], s[base + 5]);
+  u.w = cvt_pk_bf16(s[base + 6], s[base + 7]);
   return as_bf16x8(u);
 }
 
@@ -49,7 +54,7 @@ BSA_DEV int xcd_remap(int bid, int total) {
   return x * q + min(x, r) + k;
 }
 
-__global__ __launch_bounds__(256, 1) void k_attn_bf16(
+__global__ __launch_bounds__(256, 2) void k_attn_bf16(
     const uint16_t* __restrict__ q, const int32_t* __restrict__ perm_q,
     const uint4* __restrict__ ksw, const uint4* __restrict__ vsw,
     const uint4* __restrict__ ktsw, const uint4* __restrict__ vtsw,
@@ -61,6 +66,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(
   __shared__ float sm_m[4][64];
   __shared__ float sm_l[4][64];
   __shared__ float sm_o[64 * 129];
+  __shared__ uint4 sq[2][8][64];  // the queries in B-operand order (see below)
 
   const int logical = xcd_remap(blockIdx.x, H * nb);
   const int h = logical / nb, i = logical - h * nb;
@@ -69,8 +75,9 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(
   const int ntiles = summary_tiles(nb);
   const int32_t* list = lists + ((size_t)h * nb + i) * topk;
 
-  // bitmap of this query block's selected key blocks (masks them in the compressed branch)
-  const int words = (nb + 31) >> 5;
+  // bitmap of this query block's selected key blocks (masks them in the compressed branch);
+  // cleared over every summary row, padding included
+  const int words = (summary_tiles(nb) * 64 + 31) >> 5;
   for (int w = tid; w < words; w += 256) sel_bits[w] = 0u;
   __syncthreads();
   for (int t = tid; t < topk; t += 256) {
@@ -80,14 +87,12 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(
 
   // queries of the block, as the B operand of S^T = K Q^T: lane holds query 32n + l32,
   // head-dim elements 16c + 8g .. +8
+  // (sq[n][c][lane] = the 8 elements 16c + 8g .. +8 of query 32n + l32), loaded once
   const int32_t* pq = perm_q + (size_t)h * N + (size_t)i * kBlk;
-  bf16x8_t qr[2][8];
-#pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const int tok = pq[32 * n + l32];
-    const uint4* row = reinterpret_cast<const uint4*>(q + ((size_t)h * N + tok) * D);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) qr[n][c] = as_bf16x8(row[2 * c + g]);
+  for (int u = tid; u < 2 * 8 * 64; u += 256) {
+    const int n = u >> 9, c = (u >> 6) & 7, ln = u & 63;
+    const int tok = pq[32 * n + (ln & 31)];
+    sq[n][c][ln] = reinterpret_cast<const uint4*>(q + ((size_t)h * N + tok) * D)[2 * c + (ln >> 5)];
   }
   __syncthreads();
 
@@ -118,14 +123,16 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(
       vb = vtsw + blk * 1024;
       key0 = tau * 64;
     }
-    // S^T tiles: [key half hh][query half n]; lane holds query 32n + l32 and keys
-    // 32hh + 8(r/4) + 4g + (r%4), r = 0..15.  K is streamed one 32-key half at a time.
-    f32x16_t s[2][2];
-#pragma unroll
+    // one 32-key half of the tile at a time, each with its own online-softmax update
+#pragma unroll 1
     for (int hh = 0; hh < 2; ++hh) {
       uint4 kr[8];
 #pragma unroll
       for (int c = 0; c < 8; ++c) kr[c] = kb[(hh * 8 + c) * 64 + lane];
+      // keep the query operands in LDS: re-read them per use instead of pinning 64 registers
+      asm volatile("" ::: "memory");
+      // S^T[n]: lane holds query 32n + l32 and keys 32hh + 8(r/4) + 4g + (r%4), r = 0..15
+      f32x16_t s[2];
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
         f32x16_t t;
@@ -133,75 +140,75 @@ __global__ __launch_bounds__(256, 1) void k_attn_bf16(
         for (int r = 0; r < 16; ++r) t[r] = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c)
-          t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[c]), qr[n][c], t, 0, 0, 0);
-        s[hh][n] = t;
+          t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[c]), as_bf16x8(sq[n][c][lane]),
+                                                      t, 0, 0, 0);
+        s[n] = t;
       }
-    }
-
-    if (exact) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[hh][n][r] *= scale_log2;
-    } else {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + 32 * hh + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool masked = key >= nb || ((sel_bits[key >> 5] >> (key & 31)) & 1u);
-          const float b = masked ? -INFINITY : bias_h[key] * kLog2e;
-#pragma unroll
-          for (int n = 0; n < 2; ++n) s[hh][n][r] = s[hh][n][r] * scale_log2 + b;
-        }
-    }
-
-    // online softmax per query half (lanes l and l^32 hold the same query)
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[hh][n][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run[n], mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[n] - m_use);
-      float rs = 0.f;
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(s[hh][n][r] - m_use);
-          s[hh][n][r] = p;
-          rs += p;
-        }
-      rs += __shfl_xor(rs, 32, 64);
-      l_run[n] = l_run[n] * alpha + rs;
-      m_run[n] = m_new;
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[a][n][r] *= alpha;
-    }
-
-    // O^T[d chunk a][query half n] += V^T[a][key chunk c] P^T[c][n]; the B operand of key
-    // chunk c is registers 8(c%2)..+8 of S^T tile (c/2, n).  V is streamed per key half.
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
       uint4 vr[8];
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) vr[a * 2 + cc] = vb[(a * 4 + 2 * hh + cc) * 64 + lane];
+      // logits in log2 units: s * scale_log2, plus bias * log2 e for summary rows (-inf if
+      // the block is selected or past the end)
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        float mx = -INFINITY;
+        if (exact) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[n][r]);
+          mx *= scale_log2;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            // rows past nb carry bias -inf (padding); selected blocks are masked here
+            const int key = key0 + 32 * hh + 8 * (r >> 2) + 4 * g + (r & 3);
+            const float bv = bias_h[key] * kLog2e;
+            const bool sel = (sel_bits[key >> 5] >> (key & 31)) & 1u;
+            s[n][r] = fmaf(s[n][r], scale_log2, sel ? -INFINITY : bv);
+            mx = fmaxf(mx, s[n][r]);
+          }
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        // lazy rescale: move the running max only when it grows by more than kMaxSlack
+        const bool grow = mx > m_run[n] + kMaxSlack;
+        if (__any(grow)) {
+          const float m_new = grow ? mx : m_run[n];
+          const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[n] - m_new) : 1.f;
+          m_run[n] = m_new;
+          l_run[n] *= alpha;
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][n][r] *= alpha;
+        }
+        const float m_use = (m_run[n] == -INFINITY) ? 0.f : m_run[n];
+        float rs = 0.f;
+        if (exact) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float pr = __builtin_amdgcn_exp2f(fmaf(s[n][r], scale_log2, -m_use));
+            s[n][r] = pr;
+            rs += pr;
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float pr = __builtin_amdgcn_exp2f(s[n][r] - m_use);
+            s[n][r] = pr;
+            rs += pr;
+          }
+        }
+        rs += __shfl_xor(rs, 32, 64);
+        l_run[n] += rs;
+      }
+      // O^T[d chunk a][n] += V^T[a][key chunk c] P^T[c][n], c = 2hh + cc; the B operand of
+      // chunk c is registers 8cc..8cc+8 of S^T[n]
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
-          const bf16x8_t pb = pack8(s[hh][n], 8 * cc);
+          const bf16x8_t pb = pack8(s[n], 8 * cc);
 #pragma unroll
           for (int a = 0; a < 4; ++a)
             acc[a][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vr[a * 2 + cc]), pb,

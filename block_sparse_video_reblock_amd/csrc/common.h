@@ -25,6 +25,14 @@ BSA_DEV uint32_t pack_bf16x2(float lo, float hi) {
   return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
 }
 
+// hardware round-to-nearest-even pack of two floats (v_cvt_pk_bf16_f32)
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+BSA_DEV uint32_t cvt_pk_bf16(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 template <typename T> BSA_DEV float load_as_f32(const T* p);
 template <> BSA_DEV float load_as_f32<float>(const float* p) { return *p; }
 template <> BSA_DEV float load_as_f32<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }

@@ -211,13 +211,13 @@ BSA_DEV int acc_col(int t) {
 
 // out = C v for the symmetric register-resident C (column form).  red: AC*D floats of LDS.
 template <int D>
-BSA_DEV void cov_matvec(const f32x16_t* acc, const float* v, float* out, float* red) {
+BSA_DEV void cov_matvec(const f32x16_t* acc, const float* v, float vs, float* out, float* red) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
   for (int t = 0; t < Cov<D>::TILES; ++t) {
     float s = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s = fmaf(acc[t][r], v[acc_row<D>(t, r)], s);
+    for (int r = 0; r < 16; ++r) s = fmaf(acc[t][r], v[acc_row<D>(t, r)] * vs, s);
     s += __shfl_xor(s, 32, 64);
     if (lane < 32) red[Cov<D>::ac(w, t) * D + acc_col<D>(t)] = s;
   }
@@ -252,6 +252,24 @@ struct MRegs {
     if (threadIdx.x % R == 0) out[row] = s;
     __syncthreads();
   }
+  // out = M v, and returns v . out to every thread (sm: 4 floats of LDS).  One barrier.
+  BSA_DEV float matvec_dot(const float* v, float* out, float* sm) const {
+    const int row = threadIdx.x / R, c0 = (threadIdx.x % R) * W;
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < W; ++i) s = fmaf(m[i], v[c0 + i], s);
+#pragma unroll
+    for (int o = 1; o < R; o <<= 1) s += __shfl_xor(s, o, 64);
+    float d = 0.f;
+    if (threadIdx.x % R == 0) {
+      out[row] = s;
+      d = s * v[row];
+    }
+    d = wave_sum(d);
+    if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = d;
+    __syncthreads();
+    return sm[0] + sm[1] + sm[2] + sm[3];
+  }
 };
 
 // dot product of two LDS vectors, result broadcast to all threads.  sm: 4 floats.
@@ -282,6 +300,8 @@ struct DirLds {
 // Finish a group's statistics and find its split direction.  On entry acc holds
 // sum (y - shift)(y - shift)^T over the group's n tokens and L.mu holds sum (y - shift).
 // On exit L.w holds the direction w (zero for a group without spread) and L.mu the mean.
+// Power step (w form): z = C_y w, t = M z, w <- t / sqrt(z . t); the normalisation is applied
+// when the next step reads t.
 template <typename T, int D>
 BSA_DEV void group_direction(f32x16_t* acc, DirLds& L, const MRegs<D>& M, int n,
                              const T* __restrict__ X, const int32_t* __restrict__ tokmap,
@@ -318,20 +338,20 @@ BSA_DEV void group_direction(f32x16_t* acc, DirLds& L, const MRegs<D>& M, int n,
     __syncthreads();
     return;
   }
-  M.matvec(L.e0, L.w);
+  M.matvec(L.e0, L.t);
+  float rn = 1.f;
   for (int it = 0; it < kIters; ++it) {
-    cov_matvec<D>(acc, L.w, L.z, L.red);
-    M.matvec(L.z, L.t);
-    const float nrm2 = block_dot<D>(L.z, L.t, L.sm);
+    cov_matvec<D>(acc, L.t, rn, L.z, L.red);
+    const float nrm2 = M.matvec_dot(L.z, L.t, L.sm);
     if (!(nrm2 > 0.f)) {
       if (tid < D) L.w[tid] = 0.f;
       __syncthreads();
       return;
     }
-    const float rn = 1.f / sqrtf(nrm2);
-    if (tid < D) L.w[tid] = L.t[tid] * rn;
-    __syncthreads();
+    rn = 1.f / sqrtf(nrm2);
   }
+  if (tid < D) L.w[tid] = L.t[tid] * rn;
+  __syncthreads();
   const float o = block_dot<D>(L.e0, L.w, L.sm);
   if (o < 0.f && tid < D) L.w[tid] = -L.w[tid];
   __syncthreads();
@@ -365,13 +385,15 @@ struct ProblemArgs {
   int H, N, nb, L;
   const float* mom;        // [H][2][D][D]: side 0 = M_Q, side 1 = M_K
   const float* inv_n;      // [P][N]
-  const int32_t* in;       // [P][N]
-  int32_t* out;            // [P][N]
-  float* keys;             // [P][N]
-  float* mu_prev;          // [P][G][D] parent means (level - 1)
-  float* mu_cur;           // [P][G][D]
+  int32_t* perm_q;         // [H][N] positions of side 0 (query layouts), updated in place
+  int32_t* perm_k;         // [H][N] positions of side 1 (key layouts)
+  int32_t* tmp;            // [P][N] partition scratch
+  float* keys;             // [P][N] projections by position
+  float* mu;               // [P][2^L][D] group means, heap order (node (l, g) at 2^l - 1 + g)
+  const float* mu_root;    // [P][D] mean of all y (the parent shift of level 0)
   float* wdir;             // [P][G][D]
   float* partial;          // [P][kSlots][D*D + D]
+  const int* lists;        // [L][G] active (m >= 2) nodes per level, ascending
   float* proj;             // optional [H][2][L][N]
   int level, G, slices;
 };
@@ -386,8 +408,29 @@ template <int D>
 BSA_DEV const float* problem_metric(const ProblemArgs& a, int p) {
   return a.mom + ((size_t)(p >> 1) * 2 + ((p & 1) ? 0 : 1)) * D * D;
 }
-BSA_DEV float* problem_proj(const ProblemArgs& a, int p) {
-  return a.proj ? a.proj + ((size_t)p * a.L + a.level) * a.N : nullptr;
+BSA_DEV int32_t* problem_pos(const ProblemArgs& a, int p) {
+  return ((p & 1) ? a.perm_k : a.perm_q) + (size_t)(p >> 1) * a.N;
+}
+BSA_DEV float* problem_proj(const ProblemArgs& a, int p, int level) {
+  return a.proj ? a.proj + ((size_t)p * a.L + level) * a.N : nullptr;
+}
+template <int D>
+BSA_DEV const float* parent_mean(const ProblemArgs& a, int p, int level, int g) {
+  if (level == 0) return a.mu_root + (size_t)p * D;
+  return a.mu + ((size_t)p * ((size_t)1 << a.L) + (1 << (level - 1)) - 1 + (g >> 1)) * D;
+}
+template <int D>
+BSA_DEV float* group_mean(const ProblemArgs& a, int p, int level, int g) {
+  return a.mu + ((size_t)p * ((size_t)1 << a.L) + (1 << level) - 1 + g) * D;
+}
+
+// Stable in-place two-way partition of one group's positions around (T, take).
+BSA_DEV void partition_in_place(const float* keys, int32_t* pos, int32_t* tmp, int n, int want,
+                                uint32_t T, int take, int* sm) {
+  block_partition(keys, pos, tmp, n, want, T, take, sm);
+  __syncthreads();
+  for (int i = threadIdx.x; i < n; i += 256) pos[i] = tmp[i];
+  __syncthreads();
 }
 
 // ------------------------------------------------------------------- second moments
@@ -413,55 +456,63 @@ __global__ __launch_bounds__(256) void k_moments(const T* __restrict__ q,
   store_acc<D>(partial + (((size_t)h * 2 + side) * nch + chunk) * D * D, acc);
 }
 
-// Sum the partials in order, divide by N, write M canonical and (bf16 path) its 3-term bf16 split
+// One thread per matrix element: sum the partials in order, divide by N, write M canonical
+// and (bf16 path) its 3-term bf16 split.  grid (D*D/256, 2, H).
 template <int D>
 __global__ __launch_bounds__(256) void k_moments_finish(const float* __restrict__ partial,
                                                         int nch, int N, float* __restrict__ mom,
                                                         uint16_t* __restrict__ msplit) {
-  const int side = blockIdx.x, h = blockIdx.y;
-  f32x16_t acc[Cov<D>::TILES];
-  zero_acc<D>(acc);
+  const int e = blockIdx.x * 256 + threadIdx.x;  // register-dump index
+  const int side = blockIdx.y, h = blockIdx.z;
   const size_t mi = (size_t)h * 2 + side;
-  for (int c = 0; c < nch; ++c) add_acc<D>(partial + (mi * nch + c) * D * D, acc);
-  const float inv = 1.f / float(N);
-#pragma unroll
-  for (int t = 0; t < Cov<D>::TILES; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int a = acc_row<D>(t, r), b = acc_col<D>(t);
-      const float m = acc[t][r] * inv;
-      mom[mi * D * D + a * D + b] = m;
-      if (msplit) {
-        const uint16_t h1 = f32_to_bf16(m);
-        const float r1 = m - bf16_to_f32(h1);
-        const uint16_t h2 = f32_to_bf16(r1);
-        const uint16_t h3 = f32_to_bf16(r1 - bf16_to_f32(h2));
-        msplit[(mi * 3 + 0) * D * D + a * D + b] = h1;
-        msplit[(mi * 3 + 1) * D * D + a * D + b] = h2;
-        msplit[(mi * 3 + 2) * D * D + a * D + b] = h3;
-      }
-    }
+  float s = 0.f;
+  for (int c = 0; c < nch; ++c) s += partial[(mi * nch + c) * D * D + e];
+  const float m = s / float(N);
+  // register-dump index -> (wave, tile, reg, lane) -> (a, b)
+  const int lane = e & 63, r = (e >> 6) & 15, wt = e >> 10;
+  const int w = wt / Cov<D>::TILES, t = wt % Cov<D>::TILES;
+  const int ac = D == 128 ? w : (w >> 1), bc = D == 128 ? t : (w & 1);
+  const int a = 32 * ac + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), b = 32 * bc + (lane & 31);
+  mom[mi * D * D + a * D + b] = m;
+  if (msplit) {
+    const uint16_t h1 = f32_to_bf16(m);
+    const float r1 = m - bf16_to_f32(h1);
+    const uint16_t h2 = f32_to_bf16(r1);
+    const uint16_t h3 = f32_to_bf16(r1 - bf16_to_f32(h2));
+    msplit[(mi * 3 + 0) * D * D + a * D + b] = h1;
+    msplit[(mi * 3 + 1) * D * D + a * D + b] = h2;
+    msplit[(mi * 3 + 2) * D * D + a * D + b] = h3;
+  }
 }
 
 // ---------------------------------------------------------------- metric norms (bf16)
-// inv_n[p][t] = 1 / sqrt(x_t^T M x_t) (0 if that is 0) and per-64-token sums of y = x inv_n.
-// Y^T = M X^T by MFMA with M in three bf16 terms; wave w computes rows [32w, 32w+32).
+// inv_n[p][t] = 1 / sqrt(x_t^T M x_t) (0 if that is 0) and per-workgroup sums of y = x inv_n.
+// Y^T = M X^T by MFMA with M in three bf16 terms held in registers: wave w owns rows
+// [32w, 32w+32) of M; the workgroup walks kNormTok tokens in tiles of 32.
+constexpr int kNormTok = 512;
 __global__ __launch_bounds__(256) void k_norms_bf16(ProblemArgs a, const uint16_t* __restrict__ msplit,
                                                     float* __restrict__ inv_n_out,
                                                     float* __restrict__ ysum) {
   constexpr int D = 128;
-  __shared__ float red[4][64];
-  __shared__ float s_inv[64];
+  __shared__ float red[4][32];
+  __shared__ float s_inv[32];
   __shared__ float s_half[D];
   const int chunk = blockIdx.x, p = blockIdx.y, nch = gridDim.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const uint16_t* X = problem_x<uint16_t, D>(a, p);
   const int mi = (p >> 1) * 2 + ((p & 1) ? 0 : 1);
   const uint16_t* Ms = msplit + (size_t)mi * 3 * D * D;
-  const int c0 = chunk * kBlk;
+  bf16x8_t mreg[3][8];
 #pragma unroll
-  for (int n = 0; n < 2; ++n) {
-    const int tok = c0 + 32 * n + l32;
+  for (int s = 0; s < 3; ++s)
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      mreg[s][c] = lds_bf16x8(Ms + (size_t)s * D * D + (32 * w + l32) * D + 16 * c + 8 * g);
+  const int d = tid & (D - 1), half = tid >> 7;
+  float ys = 0.f;
+  const int t_end = min(a.N, (chunk + 1) * kNormTok);
+  for (int c0 = chunk * kNormTok; c0 < t_end; c0 += 32) {
+    const int tok = c0 + l32;
     const uint16_t* xr = X + (size_t)tok * D;
     f32x16_t acc;
 #pragma unroll
@@ -470,10 +521,8 @@ __global__ __launch_bounds__(256) void k_norms_bf16(ProblemArgs a, const uint16_
     for (int c = 0; c < 8; ++c) {
       const bf16x8_t xb = lds_bf16x8(xr + 16 * c + 8 * g);
 #pragma unroll
-      for (int s = 0; s < 3; ++s) {
-        const bf16x8_t mb = lds_bf16x8(Ms + (size_t)s * D * D + (32 * w + l32) * D + 16 * c + 8 * g);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mb, xb, acc, 0, 0, 0);
-      }
+      for (int s = 0; s < 3; ++s)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mreg[s][c], xb, acc, 0, 0, 0);
     }
     // lane holds (M x_tok)[b] for b = 32w + 8j + 4g + i
     float part = 0.f;
@@ -486,30 +535,25 @@ __global__ __launch_bounds__(256) void k_norms_bf16(ProblemArgs a, const uint16_
       part = fmaf(acc[4 * j + 3], __uint_as_float(u.y & 0xFFFF0000u), part);
     }
     part += __shfl_xor(part, 32, 64);
-    if (g == 0) red[w][32 * n + l32] = part;
-  }
-  __syncthreads();
-  if (tid < 64) {
-    const float n2 = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
-    const float inv = n2 > 0.f ? 1.f / sqrtf(n2) : 0.f;
-    s_inv[tid] = inv;
-    inv_n_out[(size_t)p * a.N + c0 + tid] = inv;
-  }
-  __syncthreads();
-  // sum of y over the chunk, two threads per element
-  {
-    const int d = tid & (D - 1), half = tid >> 7;
-    float s = 0.f;
-    for (int t = 32 * half; t < 32 * half + 32; ++t)
-      s = fmaf(bf16_to_f32(X[(size_t)(c0 + t) * D + d]), s_inv[t], s);
-    if (half == 1) s_half[d] = s;
+    if (g == 0) red[w][l32] = part;
     __syncthreads();
-    if (half == 0) ysum[((size_t)p * nch + chunk) * D + d] = s + s_half[d];
+    if (tid < 32) {
+      const float n2 = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+      const float inv = n2 > 0.f ? 1.f / sqrtf(n2) : 0.f;
+      s_inv[tid] = inv;
+      inv_n_out[(size_t)p * a.N + c0 + tid] = inv;
+    }
+    __syncthreads();
+    for (int t = 16 * half; t < 16 * half + 16; ++t)
+      ys = fmaf(bf16_to_f32(X[(size_t)(c0 + t) * D + d]), s_inv[t], ys);
   }
+  if (half == 1) s_half[d] = ys;
+  __syncthreads();
+  if (half == 0) ysum[((size_t)p * nch + chunk) * D + d] = ys + s_half[d];
 }
 
 // fp32 path (D = 64): plain FMA, M in LDS; thread (s = tid/4, q = tid%4) -> token s, rows
-// [16q, 16q+16) of M x
+// [16q, 16q+16) of M x.  One workgroup per 64 tokens.
 __global__ __launch_bounds__(256) void k_norms_f32(ProblemArgs a, float* __restrict__ inv_n_out,
                                                    float* __restrict__ ysum) {
   constexpr int D = 64;
@@ -545,15 +589,31 @@ __global__ __launch_bounds__(256) void k_norms_f32(ProblemArgs a, float* __restr
   }
 }
 
-// mu_root[p] = (1/N) sum of the chunk sums, stored as the "parent mean" of level 0
+// mu_root[p] = (1/N) sum of the chunk sums
 template <int D>
-__global__ void k_root_mean(const float* __restrict__ ysum, int nch, int N, int G,
-                            float* __restrict__ mu) {
+__global__ void k_root_mean(const float* __restrict__ ysum, int nch, int N,
+                            float* __restrict__ mu_root) {
   const int p = blockIdx.x, d = threadIdx.x;
   if (d >= D) return;
   float s = 0.f;
   for (int c = 0; c < nch; ++c) s += ysum[((size_t)p * nch + c) * D + d];
-  mu[(size_t)p * G * D + d] = s / float(N);
+  mu_root[(size_t)p * D + d] = s / float(N);
+}
+
+// active-node lists: lists[l][0..count) = the nodes g of level l with m >= 2, ascending
+__global__ __launch_bounds__(256) void k_group_lists(int nb, int G, int* __restrict__ lists) {
+  __shared__ int sm[8];
+  const int level = blockIdx.x, n = 1 << level;
+  int run = 0;
+  for (int base = 0; base < n; base += 256) {
+    const int g = base + threadIdx.x;
+    int b0, m;
+    const int f = (g < n && group_geom(nb, level, g, b0, m) == kGroupSplit) ? 1 : 0;
+    int tot;
+    const int ex = block_excl_scan(f, sm, &tot);
+    if (f) lists[(size_t)level * G + run + ex] = g;
+    run += tot;
+  }
 }
 
 // ---------------------------------------------------------------------- wide levels
@@ -569,10 +629,9 @@ __global__ __launch_bounds__(256) void k_wide_stats(ProblemArgs a) {
   if (group_geom(a.nb, a.level, g, b0, m) != kGroupSplit) return;
   const int sb0 = b0 + (int)((long)s * m / a.slices), sb1 = b0 + (int)((long)(s + 1) * m / a.slices);
   const T* X = problem_x<T, D>(a, p);
-  const int32_t* tokmap = a.in + (size_t)p * a.N;
+  const int32_t* tokmap = problem_pos(a, p);
   const float* inv_n = a.inv_n + (size_t)p * a.N;
-  if (threadIdx.x < D)
-    shift[threadIdx.x] = a.mu_prev[((size_t)p * a.G + (g >> 1)) * D + threadIdx.x];
+  if (threadIdx.x < D) shift[threadIdx.x] = parent_mean<D>(a, p, a.level, g)[threadIdx.x];
   __syncthreads();
   f32x16_t acc[Cov<D>::TILES];
   zero_acc<D>(acc);
@@ -604,15 +663,15 @@ __global__ __launch_bounds__(256) void k_wide_dir(ProblemArgs a) {
   }
   if (threadIdx.x < D) {
     L.mu[threadIdx.x] = ds;
-    L.shift[threadIdx.x] = a.mu_prev[((size_t)p * a.G + (g >> 1)) * D + threadIdx.x];
+    L.shift[threadIdx.x] = parent_mean<D>(a, p, a.level, g)[threadIdx.x];
   }
   __syncthreads();
   MRegs<D> M;
   M.load(problem_metric<D>(a, p));
-  group_direction<T, D>(acc, L, M, m * kBlk, problem_x<T, D>(a, p), a.in + (size_t)p * a.N,
+  group_direction<T, D>(acc, L, M, m * kBlk, problem_x<T, D>(a, p), problem_pos(a, p),
                         a.inv_n + (size_t)p * a.N, b0 * kBlk);
   if (threadIdx.x < D) {
-    a.mu_cur[((size_t)p * a.G + g) * D + threadIdx.x] = L.mu[threadIdx.x];
+    group_mean<D>(a, p, a.level, g)[threadIdx.x] = L.mu[threadIdx.x];
     a.wdir[((size_t)p * a.G + g) * D + threadIdx.x] = L.w[threadIdx.x];
   }
 }
@@ -627,77 +686,128 @@ __global__ __launch_bounds__(256) void k_wide_proj(ProblemArgs a) {
   if (g < 0 || m < 2) return;
   if (threadIdx.x < D) w[threadIdx.x] = a.wdir[((size_t)p * a.G + g) * D + threadIdx.x];
   __syncthreads();
-  project_chunk<T, D>(problem_x<T, D>(a, p), a.in + (size_t)p * a.N, a.inv_n + (size_t)p * a.N,
-                      blk * kBlk, w, a.keys + (size_t)p * a.N, problem_proj(a, p));
+  project_chunk<T, D>(problem_x<T, D>(a, p), problem_pos(a, p), a.inv_n + (size_t)p * a.N,
+                      blk * kBlk, w, a.keys + (size_t)p * a.N, problem_proj(a, p, a.level));
 }
 
-// grid (G, P): split threshold and stable partition (also carries leaves to the next buffer)
-__global__ __launch_bounds__(256) void k_wide_split(ProblemArgs a) {
-  __shared__ int hist[256];
-  __shared__ int sm[8];
-  const int g = blockIdx.x;
-  const size_t p = blockIdx.y;
-  int b0, m;
-  const int kind = group_geom(a.nb, a.level, g, b0, m);
-  if (kind == kGroupNone) return;
-  const size_t base = p * a.N + (size_t)b0 * kBlk;
-  const int n = m * kBlk;
-  if (kind == kGroupCopy) {
-    for (int i = threadIdx.x; i < n; i += 256) a.out[base + i] = a.in[base + i];
-    return;
-  }
-  const int want = (m >> 1) * kBlk;
-  int take;
-  const uint32_t T = block_select_smallest(a.keys + base, n, want, hist, sm, &take);
-  block_partition(a.keys + base, a.in + base, a.out + base, n, want, T, take, sm);
-}
-
-// -------------------------------------------------------------------- narrow levels
-// grid (G, P): one workgroup does the whole split of one group
-template <typename T, int D>
-__global__ __launch_bounds__(256) void k_narrow_level(ProblemArgs a) {
-  __shared__ StageLds<D> st;
-  __shared__ DirLds L;
-  __shared__ int hist[256];
-  __shared__ int sm[8];
+// grid (G, P), 1024 threads: split threshold and stable in-place partition of one group
+__global__ __launch_bounds__(1024) void k_wide_split(ProblemArgs a) {
+  __shared__ int hist[16 * 256];
+  __shared__ int sm[40];
   const int g = blockIdx.x, p = blockIdx.y;
   int b0, m;
-  const int kind = group_geom(a.nb, a.level, g, b0, m);
-  if (kind == kGroupNone) return;
-  const size_t base = (size_t)p * a.N + (size_t)b0 * kBlk;
-  const int n = m * kBlk;
-  if (kind == kGroupCopy) {
-    for (int i = threadIdx.x; i < n; i += 256) a.out[base + i] = a.in[base + i];
-    return;
-  }
+  if (group_geom(a.nb, a.level, g, b0, m) != kGroupSplit) return;
+  const size_t off = (size_t)b0 * kBlk;
+  const int n = m * kBlk, want = (m >> 1) * kBlk;
+  const float* keys = a.keys + (size_t)p * a.N + off;
+  int32_t* pos = problem_pos(a, p) + off;
+  int32_t* tmp = a.tmp + (size_t)p * a.N + off;
+  int take;
+  const uint32_t T = select_smallest_w<1024>(keys, n, want, hist, sm, &take);
+  partition_w<1024>(keys, pos, tmp, n, want, T, take, sm);
+  for (int i = threadIdx.x; i < n; i += 1024) pos[i] = tmp[i];
+}
+
+// ------------------------------------------------------------------ subtree levels
+// grid (roots, P): each workgroup owns the subtree of one active node of level `ls` and does
+// every split of levels [ls, le) inside it, one group at a time, in place.
+template <typename T, int D>
+__global__ __launch_bounds__(256, 2) void k_subtree(ProblemArgs a, int ls, int le) {
+  __shared__ StageLds<D> st;
+  __shared__ DirLds L;
+  __shared__ int hist[4 * 256];
+  __shared__ int sm[16];
+  const int g0 = a.lists[(size_t)ls * a.G + blockIdx.x], p = blockIdx.y;
   const T* X = problem_x<T, D>(a, p);
-  const int32_t* tokmap = a.in + (size_t)p * a.N;
+  int32_t* pos = problem_pos(a, p);
+  int32_t* tmp = a.tmp + (size_t)p * a.N;
+  float* keys = a.keys + (size_t)p * a.N;
   const float* inv_n = a.inv_n + (size_t)p * a.N;
-  if (threadIdx.x < D)
-    L.shift[threadIdx.x] = a.mu_prev[((size_t)p * a.G + (g >> 1)) * D + threadIdx.x];
-  __syncthreads();
-  f32x16_t acc[Cov<D>::TILES];
-  zero_acc<D>(acc);
-  {
-    float dpart[D / 4];
-#pragma unroll
-    for (int e = 0; e < D / 4; ++e) dpart[e] = 0.f;
-    for (int b = b0; b < b0 + m; ++b)
-      stats_chunk<T, D, 3>(X, tokmap, inv_n, b * kBlk, L.shift, st, acc, dpart);
-    reduce_dpart<D>(dpart, L.red, L.mu);
-  }
   MRegs<D> M;
   M.load(problem_metric<D>(a, p));
-  group_direction<T, D>(acc, L, M, n, X, tokmap, inv_n, b0 * kBlk);
-  if (threadIdx.x < D) a.mu_cur[((size_t)p * a.G + g) * D + threadIdx.x] = L.mu[threadIdx.x];
-  float* keys = a.keys + (size_t)p * a.N;
-  for (int b = b0; b < b0 + m; ++b)
-    project_chunk<T, D>(X, tokmap, inv_n, b * kBlk, L.w, keys, problem_proj(a, p));
+  for (int level = ls; level < le; ++level) {
+    const int depth = level - ls;
+    for (int g = g0 << depth; g < ((g0 + 1) << depth); ++g) {
+      int b0, m;
+      if (group_geom(a.nb, level, g, b0, m) != kGroupSplit) continue;
+      const int n = m * kBlk;
+      if (threadIdx.x < D) L.shift[threadIdx.x] = parent_mean<D>(a, p, level, g)[threadIdx.x];
+      __syncthreads();
+      f32x16_t acc[Cov<D>::TILES];
+      zero_acc<D>(acc);
+      {
+        float dpart[D / 4];
+#pragma unroll
+        for (int e = 0; e < D / 4; ++e) dpart[e] = 0.f;
+        for (int b = b0; b < b0 + m; ++b)
+          stats_chunk<T, D, 3>(X, pos, inv_n, b * kBlk, L.shift, st, acc, dpart);
+        reduce_dpart<D>(dpart, L.red, L.mu);
+      }
+      group_direction<T, D>(acc, L, M, n, X, pos, inv_n, b0 * kBlk);
+      if (threadIdx.x < D) group_mean<D>(a, p, level, g)[threadIdx.x] = L.mu[threadIdx.x];
+      for (int b = b0; b < b0 + m; ++b)
+        project_chunk<T, D>(X, pos, inv_n, b * kBlk, L.w, keys, problem_proj(a, p, level));
+      __syncthreads();
+      const size_t off = (size_t)b0 * kBlk;
+      const int want = (m >> 1) * kBlk;
+      int take;
+      const uint32_t T_ = select_smallest_w<256>(keys + off, n, want, hist, sm, &take);
+      partition_w<256>(keys + off, pos + off, tmp + off, n, want, T_, take, sm);
+      for (int i = threadIdx.x; i < n; i += 256) pos[off + i] = tmp[off + i];
+      __syncthreads();
+    }
+  }
+}
+
+// grid (roots, P): subtrees whose root spans at most kSmallBlocks blocks.  The root's positions
+// and keys stay in LDS for all remaining levels; splits use rank selection (small_split).
+constexpr int kSmallBlocks = 8;
+template <typename T, int D>
+__global__ __launch_bounds__(256, 2) void k_subtree_small(ProblemArgs a, int ls) {
+  __shared__ StageLds<D> st;
+  __shared__ DirLds L;
+  __shared__ int32_t spos[kSmallBlocks * kBlk];
+  __shared__ int32_t stmp[kSmallBlocks * kBlk];
+  __shared__ float skeys[kSmallBlocks * kBlk];
+  __shared__ int sm[8];
+  const int g0 = a.lists[(size_t)ls * a.G + blockIdx.x], p = blockIdx.y;
+  int rb0, rm;
+  group_geom(a.nb, ls, g0, rb0, rm);
+  const T* X = problem_x<T, D>(a, p);
+  int32_t* pos = problem_pos(a, p) + (size_t)rb0 * kBlk;
+  const float* inv_n = a.inv_n + (size_t)p * a.N;
+  for (int i = threadIdx.x; i < rm * kBlk; i += 256) spos[i] = pos[i];
+  MRegs<D> M;
+  M.load(problem_metric<D>(a, p));
   __syncthreads();
-  const int want = (m >> 1) * kBlk;
-  int take;
-  const uint32_t T_ = block_select_smallest(a.keys + base, n, want, hist, sm, &take);
-  block_partition(a.keys + base, a.in + base, a.out + base, n, want, T_, take, sm);
+  for (int level = ls; level < a.L; ++level) {
+    const int depth = level - ls;
+    for (int g = g0 << depth; g < ((g0 + 1) << depth); ++g) {
+      int b0, m;
+      if (group_geom(a.nb, level, g, b0, m) != kGroupSplit) continue;
+      const int lb0 = b0 - rb0, n = m * kBlk;
+      if (threadIdx.x < D) L.shift[threadIdx.x] = parent_mean<D>(a, p, level, g)[threadIdx.x];
+      __syncthreads();
+      f32x16_t acc[Cov<D>::TILES];
+      zero_acc<D>(acc);
+      {
+        float dpart[D / 4];
+#pragma unroll
+        for (int e = 0; e < D / 4; ++e) dpart[e] = 0.f;
+        for (int b = lb0; b < lb0 + m; ++b)
+          stats_chunk<T, D, 3>(X, spos, inv_n, b * kBlk, L.shift, st, acc, dpart);
+        reduce_dpart<D>(dpart, L.red, L.mu);
+      }
+      group_direction<T, D>(acc, L, M, n, X, spos, inv_n, lb0 * kBlk);
+      if (threadIdx.x < D) group_mean<D>(a, p, level, g)[threadIdx.x] = L.mu[threadIdx.x];
+      float* proj = problem_proj(a, p, level);
+      for (int b = lb0; b < lb0 + m; ++b)
+        project_chunk<T, D>(X, spos, inv_n, b * kBlk, L.w, skeys, proj);
+      __syncthreads();
+      small_split<256>(skeys + lb0 * kBlk, spos + lb0 * kBlk, stmp, n, (m >> 1) * kBlk, sm);
+    }
+  }
+  for (int i = threadIdx.x; i < rm * kBlk; i += 256) pos[i] = spos[i];
 }
 
 // ------------------------------------------------------------------------- helpers
@@ -711,14 +821,6 @@ __global__ void k_fill_zero(size_t n, float* __restrict__ out) {
     out[i] = 0.f;
 }
 
-// perm[side][h][.] = pos[2h + side][.]
-__global__ void k_split_out(int H, int N, const int32_t* __restrict__ pos,
-                            int32_t* __restrict__ perm_q, int32_t* __restrict__ perm_k) {
-  const size_t p = blockIdx.y;
-  int32_t* dst = ((p & 1) ? perm_k : perm_q) + (p >> 1) * (size_t)N;
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < N; i += gridDim.x * 256) dst[i] = pos[p * N + i];
-}
-
 // keys[p][pos] = proj[p][level][in[p][pos]]
 __global__ void k_gather_keys(int N, int L, int level, const float* __restrict__ proj,
                               const int32_t* __restrict__ in, float* __restrict__ keys) {
@@ -728,7 +830,8 @@ __global__ void k_gather_keys(int N, int L, int level, const float* __restrict__
 }
 
 struct RebLayout {
-  size_t mom, mom_partial, msplit, inv_n, ysum, pos0, pos1, keys, mu0, mu1, wdir, partial, total;
+  size_t mom, mom_partial, msplit, inv_n, ysum, mu_root, tmp, keys, mu, wdir, partial, lists,
+      total;
   int L, G, nch_mom, nch_n;
 };
 
@@ -740,7 +843,7 @@ RebLayout reb_layout(int H, int N, int D) {
   r.L = tree_levels((int)nb);
   r.G = r.L > 0 ? (1 << (r.L - 1)) : 1;
   r.nch_mom = ceil_div(N, kMomChunk);
-  r.nch_n = (int)nb;
+  r.nch_n = D == 128 ? ceil_div(N, kNormTok) : (int)nb;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += al(bytes); return o; };
   r.mom = take((size_t)H * 2 * D * D * 4);
@@ -748,15 +851,22 @@ RebLayout reb_layout(int H, int N, int D) {
   r.msplit = take((size_t)H * 2 * 3 * D * D * 2);
   r.inv_n = take(P * N * 4);
   r.ysum = take(P * r.nch_n * D * 4);
-  r.pos0 = take(P * N * 4);
-  r.pos1 = take(P * N * 4);
+  r.mu_root = take(P * D * 4);
+  r.tmp = take(P * N * 4);
   r.keys = take(P * N * 4);
-  r.mu0 = take(P * r.G * D * 4);
-  r.mu1 = take(P * r.G * D * 4);
+  r.mu = take(P * ((size_t)1 << r.L) * D * 4);
   r.wdir = take(P * r.G * D * 4);
   r.partial = take(P * kSlots * (size_t)(D * D + D) * 4);
+  r.lists = take((size_t)std::max(r.L, 1) * r.G * 4);
   r.total = off;
   return r;
+}
+
+// number of active (m >= 2) nodes of a level
+int active_count(int nb, int level) {
+  int c = 0, b0, m;
+  for (int g = 0; g < (1 << level); ++g) c += group_geom(nb, level, g, b0, m) == kGroupSplit;
+  return c;
 }
 
 template <typename T, int D>
@@ -765,14 +875,13 @@ hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm
   const RebLayout R = reb_layout(H, N, D);
   char* w = static_cast<char*>(ws);
   const int P = 2 * H, nb = N / kBlk;
-  const dim3 gridN(min(ceil_div(N, 256), 1024), P);
   float* mom = reinterpret_cast<float*>(w + R.mom);
   uint16_t* msplit = sizeof(T) == 2 ? reinterpret_cast<uint16_t*>(w + R.msplit) : nullptr;
   k_moments<T, D><<<dim3(R.nch_mom, 2, H), 256, 0, s>>>(
       static_cast<const T*>(q), static_cast<const T*>(k), N,
       reinterpret_cast<float*>(w + R.mom_partial));
-  k_moments_finish<D><<<dim3(2, H), 256, 0, s>>>(reinterpret_cast<float*>(w + R.mom_partial),
-                                                 R.nch_mom, N, mom, msplit);
+  k_moments_finish<D><<<dim3(D * D / 256, 2, H), 256, 0, s>>>(
+      reinterpret_cast<float*>(w + R.mom_partial), R.nch_mom, N, mom, msplit);
   ProblemArgs a{};
   a.q = q;
   a.k = k;
@@ -782,93 +891,102 @@ hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm
   a.L = R.L;
   a.mom = mom;
   a.inv_n = reinterpret_cast<float*>(w + R.inv_n);
+  a.perm_q = perm_q;
+  a.perm_k = perm_k;
+  a.tmp = reinterpret_cast<int32_t*>(w + R.tmp);
   a.keys = reinterpret_cast<float*>(w + R.keys);
+  a.mu = reinterpret_cast<float*>(w + R.mu);
+  a.mu_root = reinterpret_cast<float*>(w + R.mu_root);
   a.wdir = reinterpret_cast<float*>(w + R.wdir);
   a.partial = reinterpret_cast<float*>(w + R.partial);
+  a.lists = reinterpret_cast<int*>(w + R.lists);
   a.proj = proj_opt;
   a.G = R.G;
-  float* mu[2] = {reinterpret_cast<float*>(w + R.mu0), reinterpret_cast<float*>(w + R.mu1)};
-  int32_t* pos[2] = {reinterpret_cast<int32_t*>(w + R.pos0), reinterpret_cast<int32_t*>(w + R.pos1)};
   float* ysum = reinterpret_cast<float*>(w + R.ysum);
   if (sizeof(T) == 2)
     k_norms_bf16<<<dim3(R.nch_n, P), 256, 0, s>>>(a, msplit, reinterpret_cast<float*>(w + R.inv_n),
                                                   ysum);
   else
     k_norms_f32<<<dim3(R.nch_n, P), 256, 0, s>>>(a, reinterpret_cast<float*>(w + R.inv_n), ysum);
-  // level -1 parent mean = mean of all y (the mean of level 0's single group)
-  k_root_mean<D><<<P, 128, 0, s>>>(ysum, R.nch_n, N, R.G, mu[1]);
+  k_root_mean<D><<<P, 128, 0, s>>>(ysum, R.nch_n, N, reinterpret_cast<float*>(w + R.mu_root));
   if (proj_opt && R.L > 0) {
     const size_t n = (size_t)P * R.L * N;
     k_fill_zero<<<(unsigned)std::min<size_t>((n + 255) / 256, 4096), 256, 0, s>>>(n, proj_opt);
   }
-  k_fill_identity<<<gridN, 256, 0, s>>>(N, pos[0]);
-  for (int level = 0; level < R.L; ++level) {
+  const dim3 gridN(std::min(ceil_div(N, 256), 1024), H);
+  k_fill_identity<<<gridN, 256, 0, s>>>(N, perm_q);
+  k_fill_identity<<<gridN, 256, 0, s>>>(N, perm_k);
+  if (R.L > 0) k_group_lists<<<R.L, 256, 0, s>>>(nb, R.G, reinterpret_cast<int*>(w + R.lists));
+  // levels whose groups are large are split over several workgroups; below that one
+  // workgroup per group, and from the first level whose groups fit in kSmallBlocks blocks,
+  // one workgroup per subtree down to the leaves.
+  int level = 0;
+  for (; level < R.L; ++level) {
+    const int min_m = nb >> level;
+    const int slices = std::min(kSlots >> std::min(level, 5), min_m);
+    if (slices <= 1) break;
     a.level = level;
-    a.in = pos[level & 1];
-    a.out = pos[(level + 1) & 1];
-    a.mu_prev = mu[(level + 1) & 1];
-    a.mu_cur = mu[level & 1];
-    const int G = 1 << level;
-    const int min_m = nb >> level;  // smallest group size at this level
-    int slices = min(kSlots >> min(level, 5), min_m);
-    if (slices < 1) slices = 1;
     a.slices = slices;
-    if (slices > 1) {
-      k_wide_stats<T, D><<<dim3(slices, G, P), 256, 0, s>>>(a);
-      k_wide_dir<T, D><<<dim3(G, P), 256, 0, s>>>(a);
-      k_wide_proj<T, D><<<dim3(nb, P), 256, 0, s>>>(a);
-      k_wide_split<<<dim3(G, P), 256, 0, s>>>(a);
-    } else {
-      k_narrow_level<T, D><<<dim3(G, P), 256, 0, s>>>(a);
-    }
+    const int G = 1 << level;
+    k_wide_stats<T, D><<<dim3(slices, G, P), 256, 0, s>>>(a);
+    k_wide_dir<T, D><<<dim3(G, P), 256, 0, s>>>(a);
+    k_wide_proj<T, D><<<dim3(nb, P), 256, 0, s>>>(a);
+    k_wide_split<<<dim3(G, P), 1024, 0, s>>>(a);
   }
-  k_split_out<<<gridN, 256, 0, s>>>(H, N, pos[R.L & 1], perm_q, perm_k);
+  for (; level < R.L; ++level) {
+    const int roots = active_count(nb, level);
+    if (roots == 0) continue;
+    if (ceil_div(nb, 1 << level) <= kSmallBlocks) {
+      k_subtree_small<T, D><<<dim3(roots, P), 256, 0, s>>>(a, level);
+      break;
+    }
+    k_subtree<T, D><<<dim3(roots, P), 256, 0, s>>>(a, level, level + 1);
+  }
   return hipGetLastError();
 }
 
 // ------------------------------------------------------- partition from given projections
-// One workgroup per (group, problem) of a level, keys already gathered by position.
-__global__ __launch_bounds__(256) void k_split_level(int N, int nb, int level,
+// One workgroup per active group of a level, keys already gathered by position; in place.
+__global__ __launch_bounds__(256) void k_split_level(int N, int nb, int level, int G,
+                                                     const int* __restrict__ lists,
                                                      const float* __restrict__ keys,
-                                                     const int32_t* __restrict__ in,
-                                                     int32_t* __restrict__ out) {
+                                                     int32_t* __restrict__ pos,
+                                                     int32_t* __restrict__ tmp) {
   __shared__ int hist[256];
   __shared__ int sm[8];
-  const int g = blockIdx.x;
+  const int g = lists[(size_t)level * G + blockIdx.x];
   const size_t p = blockIdx.y;
   int b0, m;
-  const int kind = group_geom(nb, level, g, b0, m);
-  if (kind == kGroupNone) return;
+  group_geom(nb, level, g, b0, m);
   const size_t base = p * N + (size_t)b0 * kBlk;
-  const int n = m * kBlk;
-  if (kind == kGroupCopy) {
-    for (int i = threadIdx.x; i < n; i += 256) out[base + i] = in[base + i];
-    return;
-  }
-  const int want = (m >> 1) * kBlk;
+  const int n = m * kBlk, want = (m >> 1) * kBlk;
   int take;
   const uint32_t T = block_select_smallest(keys + base, n, want, hist, sm, &take);
-  block_partition(keys + base, in + base, out + base, n, want, T, take, sm);
+  partition_in_place(keys + base, pos + base, tmp + base, n, want, T, take, sm);
 }
 
 }  // namespace
 
-size_t partition_ws_bytes(int P, int N) { return size_t(P) * N * 8 + 512; }
+size_t partition_ws_bytes(int P, int N) {
+  const int nb = N / kBlk, L = tree_levels(nb), G = L > 0 ? 1 << (L - 1) : 1;
+  return al(size_t(P) * N * 4) * 2 + al((size_t)std::max(L, 1) * G * 4);
+}
 
 hipError_t launch_partition_from_proj(int P, int N, const float* proj, int32_t* perm, void* ws,
                                       hipStream_t s) {
-  const int nb = N / kBlk, L = tree_levels(nb);
-  int32_t* tmp = static_cast<int32_t*>(ws);
-  float* keys = reinterpret_cast<float*>(static_cast<char*>(ws) + size_t(P) * N * 4 + 256);
-  int32_t* buf[2];
-  buf[L & 1] = perm;
-  buf[(L + 1) & 1] = tmp;
-  const dim3 grid_n(min(ceil_div(N, 256), 1024), P);
-  k_fill_identity<<<grid_n, 256, 0, s>>>(N, buf[0]);
+  const int nb = N / kBlk, L = tree_levels(nb), G = L > 0 ? 1 << (L - 1) : 1;
+  char* w = static_cast<char*>(ws);
+  int32_t* tmp = reinterpret_cast<int32_t*>(w);
+  float* keys = reinterpret_cast<float*>(w + al(size_t(P) * N * 4));
+  int* lists = reinterpret_cast<int*>(w + 2 * al(size_t(P) * N * 4));
+  const dim3 grid_n(std::min(ceil_div(N, 256), 1024), P);
+  k_fill_identity<<<grid_n, 256, 0, s>>>(N, perm);
+  if (L > 0) k_group_lists<<<L, 256, 0, s>>>(nb, G, lists);
   for (int level = 0; level < L; ++level) {
-    k_gather_keys<<<grid_n, 256, 0, s>>>(N, L, level, proj, buf[level & 1], keys);
-    k_split_level<<<dim3(1 << level, P), 256, 0, s>>>(N, nb, level, keys, buf[level & 1],
-                                                      buf[(level + 1) & 1]);
+    k_gather_keys<<<grid_n, 256, 0, s>>>(N, L, level, proj, perm, keys);
+    const int roots = active_count(nb, level);
+    if (roots > 0)
+      k_split_level<<<dim3(roots, P), 256, 0, s>>>(N, nb, level, G, lists, keys, perm, tmp);
   }
   return hipGetLastError();
 }

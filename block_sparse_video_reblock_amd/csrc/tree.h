@@ -154,4 +154,182 @@ BSA_DEV void block_partition(const float* keys, const int32_t* in, int32_t* out,
   }
 }
 
+
+// Exclusive scan of one int per thread over an NT-thread workgroup (NT/64 ints of LDS in sm).
+template <int NT>
+BSA_DEV int block_excl_scan_n(int v, int* sm, int* total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  __syncthreads();
+  if (lane == 63) sm[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int s = sm[w];
+    before += (w < wave) ? s : 0;
+    all += s;
+  }
+  *total = all;
+  return before + incl - v;
+}
+
+// ---------------------------------------------------------------------------------------
+// Wave-parallel variants for any workgroup size NT (a multiple of 64).
+
+// Radix select as above, with one private histogram per wave (less atomic contention) and
+// coalesced reads.  hist: NT/64 * 256 ints of LDS; sm: NT/64 + 2 ints.
+template <int NT>
+BSA_DEV uint32_t select_smallest_w(const float* keys, int n, int want, int* hist, int* sm,
+                                   int* take) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  uint32_t prefix = 0, pmask = 0;
+  int remaining = want;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int b = tid; b < NW * 256; b += NT) hist[b] = 0;
+    __syncthreads();
+    int* hw = hist + wave * 256;
+    for (int i = tid; i < n; i += NT) {
+      const uint32_t key = orderable_key(keys[i]);
+      if ((key & pmask) == prefix) atomicAdd(&hw[(key >> shift) & 255], 1);
+    }
+    __syncthreads();
+    if (tid < 256) {
+      int c = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) c += hist[w * 256 + tid];
+      hist[tid] = c;  // merged into wave 0's histogram (each thread only touches bin tid)
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // wave 0 scans the 256 bins: lane l owns bins 4l .. 4l+3
+      int c[4], local = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        c[u] = hist[4 * tid + u];
+        local += c[u];
+      }
+      int incl = local;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(incl, o, 64);
+        if (tid >= o) incl += t;
+      }
+      const uint64_t hit = __ballot(incl >= remaining);
+      const int src = __ffsll((unsigned long long)hit) - 1;
+      if (tid == src) {
+        int run = incl - local;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (run + c[u] >= remaining) {
+            sm[0] = 4 * tid + u;
+            sm[1] = run;
+            break;
+          }
+          run += c[u];
+        }
+      }
+    }
+    __syncthreads();
+    const int digit = sm[0];
+    remaining -= sm[1];
+    prefix |= uint32_t(digit) << shift;
+    pmask |= 255u << shift;
+    __syncthreads();
+  }
+  *take = remaining;
+  return prefix;
+}
+
+// Stable two-way partition (same result as block_partition).  Wave w streams one contiguous
+// range of 64-element steps with coalesced loads; ballots give in-order ranks.  sm: 2*NW ints.
+template <int NT>
+BSA_DEV void partition_w(const float* keys, const int32_t* in, int32_t* out, int n, int want,
+                         uint32_t T, int take, int* sm) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int steps = (n + 63) / 64;
+  const int per = (steps + NW - 1) / NW;
+  const int i0 = min(n, wave * per * 64), i1 = min(n, i0 + per * 64);
+  int c_lt = 0, c_eq = 0;
+  for (int base = i0; base < i1; base += 64) {
+    const int i = base + lane;
+    const uint32_t key = i < i1 ? orderable_key(keys[i]) : 0xFFFFFFFFu;
+    c_lt += __popcll(__ballot(i < i1 && key < T));
+    c_eq += __popcll(__ballot(i < i1 && key == T));
+  }
+  if (lane == 0) {
+    sm[wave] = c_lt;
+    sm[NW + wave] = c_eq;
+  }
+  __syncthreads();
+  int left_before = 0, eq_before = 0;
+  for (int w = 0; w < wave; ++w) {
+    const int lt = sm[w], eq = sm[NW + w];
+    left_before += lt + max(0, min(take - eq_before, eq));
+    eq_before += eq;
+  }
+  int left_run = 0, eq_seen = eq_before;
+  for (int base = i0; base < i1; base += 64) {
+    const int i = base + lane;
+    const bool ok = i < i1;
+    const uint32_t key = ok ? orderable_key(keys[i]) : 0xFFFFFFFFu;
+    const bool eq = ok && key == T;
+    const uint64_t eqm = __ballot(eq);
+    const bool left = ok && (key < T || (eq && eq_seen + lanes_below(eqm) < take));
+    const uint64_t lm = __ballot(left);
+    if (ok) {
+      const int lb = left_before + left_run + lanes_below(lm);  // lefts before i
+      out[left ? lb : want + (i - lb)] = in[i];
+    }
+    left_run += __popcll(lm);
+    eq_seen += __popcll(eqm);
+  }
+  __syncthreads();
+}
+
+// Small groups (n <= 2 * NT), everything in LDS: rank each element against all others, then a
+// stable scatter.  keys, pos, tmp: LDS arrays of n.  sm: NT/64 ints.  On exit pos holds the
+// partitioned order.
+template <int NT>
+BSA_DEV void small_split(const float* keys, int32_t* pos, int32_t* tmp, int n, int want,
+                         int* sm) {
+  const int tid = threadIdx.x;
+  bool left[2] = {false, false};
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int i = tid + u * NT;
+    if (i < n) {
+      const uint32_t ki = orderable_key(keys[i]);
+      int rank = 0;
+      for (int j = 0; j < n; ++j) {
+        const uint32_t kj = orderable_key(keys[j]);
+        rank += (kj < ki) || (kj == ki && j < i);
+      }
+      left[u] = rank < want;
+    }
+  }
+  int tot0, tot1;
+  const int ex0 = block_excl_scan_n<NT>(left[0] ? 1 : 0, sm, &tot0);
+  const int ex1 = block_excl_scan_n<NT>(left[1] ? 1 : 0, sm, &tot1) + tot0;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int i = tid + u * NT;
+    if (i < n) {
+      const int lb = u == 0 ? ex0 : ex1;
+      tmp[left[u] ? lb : want + (i - lb)] = pos[i];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += NT) pos[i] = tmp[i];
+  __syncthreads();
+}
+
 }  // namespace bsa
