@@ -27,7 +27,7 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kMaxSelWords = (1 << 22) / 64 / 32;   // bitmap words for the largest nb
+constexpr int kMaxSelWords = (1 << 19) / 64 / 32;   // bitmap words for the largest nb
 
 BSA_DEV bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
@@ -67,6 +67,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
   __shared__ float sm_l[4][64];
   __shared__ float sm_o[64 * 129];
   __shared__ uint4 sq[2][8][64];  // the queries in B-operand order (see below)
+  extern __shared__ float sbias[];  // [ntiles * 64] summary-row bias * log2 e, -inf if selected
 
   const int logical = xcd_remap(blockIdx.x, H * nb);
   const int h = logical / nb, i = logical - h * nb;
@@ -89,6 +90,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
   // head-dim elements 16c + 8g .. +8
   // (sq[n][c][lane] = the 8 elements 16c + 8g .. +8 of query 32n + l32), loaded once
   const int32_t* pq = perm_q + (size_t)h * N + (size_t)i * kBlk;
+  const float* bias_h = bias + (size_t)h * ntiles * 64;
+  if (n_comp > 0) {
+    __syncthreads();  // bitmap complete
+    for (int key = tid; key < ntiles * 64; key += 256) {
+      const bool sel = (sel_bits[key >> 5] >> (key & 31)) & 1u;
+      sbias[key] = sel ? -INFINITY : bias_h[key] * kLog2e;  // padding rows hold -inf already
+    }
+  }
   for (int u = tid; u < 2 * 8 * 64; u += 256) {
     const int n = u >> 9, c = (u >> 6) & 7, ln = u & 63;
     const int tok = pq[32 * n + (ln & 31)];
@@ -107,7 +116,6 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
   float l_run[2] = {0.f, 0.f};
 
   const int n_items = n_exact + n_comp;
-  const float* bias_h = bias + (size_t)h * ntiles * 64;
   for (int it = wave; it < n_items; it += 4) {
     const bool exact = it < n_exact;
     const uint4 *kb, *vb;
@@ -160,13 +168,15 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
           mx *= scale_log2;
         } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            // rows past nb carry bias -inf (padding); selected blocks are masked here
-            const int key = key0 + 32 * hh + 8 * (r >> 2) + 4 * g + (r & 3);
-            const float bv = bias_h[key] * kLog2e;
-            const bool sel = (sel_bits[key >> 5] >> (key & 31)) & 1u;
-            s[n][r] = fmaf(s[n][r], scale_log2, sel ? -INFINITY : bv);
-            mx = fmaxf(mx, s[n][r]);
+          for (int j = 0; j < 4; ++j) {
+            const float4 b4 =
+                *reinterpret_cast<const float4*>(&sbias[key0 + 32 * hh + 8 * j + 4 * g]);
+            const float bj[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              s[n][4 * j + u] = fmaf(s[n][4 * j + u], scale_log2, bj[u]);
+              mx = fmaxf(mx, s[n][4 * j + u]);
+            }
           }
         }
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
@@ -371,7 +381,8 @@ __global__ __launch_bounds__(64) void k_attn_f32(
 
 hipError_t launch_attn_bf16(const AttnLaunch& a, hipStream_t s) {
   const int grid = a.H * a.nb;
-  k_attn_bf16<<<grid, 256, 0, s>>>(
+  const size_t dyn = (size_t)summary_tiles(a.nb) * 64 * sizeof(float);
+  k_attn_bf16<<<grid, 256, dyn, s>>>(
       static_cast<const uint16_t*>(a.q), a.perm_q, static_cast<const uint4*>(a.ksw),
       static_cast<const uint4*>(a.vsw), static_cast<const uint4*>(a.ktsw),
       static_cast<const uint4*>(a.vtsw), a.bias, a.lists, a.H, a.N, a.nb, a.topk, a.n_exact,

@@ -89,33 +89,74 @@ BSA_DEV void load_row<float, 16>(const float* p, float* out) {
   }
 }
 
-// One 64-position chunk of the covariance accumulation.  Thread (s = tid/4, q = tid%4) stages
-// token s, elements [q E, q E + E) of d = x * scale - shift; dpart accumulates d.
+// One 64-position chunk of the covariance accumulation.  Thread t stages the token pair
+// (2 (t%32), 2 (t%32) + 1) for the DPT = D/8 elements of element group t/32 (see stat_dim):
+// d = x * scale - shift, split into bf16 terms written as packed pairs of tokens, so the
+// transposed staging rows of the two groups of a wave sit 8 rows (32 banks) apart.
 // tokmap == nullptr means position = token id; inv_n == nullptr means scale 1.
 // TERMS = 1: d is exact in bf16 (raw bf16 inputs).  TERMS = 3: d = hi + mid + lo (bf16 each,
 // 24 significant bits) and the products hi hi, hi mid, mid hi, hi lo, lo hi, mid mid are
 // accumulated; the dropped terms are below fp32 rounding of the sum.
+template <int D>
+BSA_DEV int stat_dim(int dg, int j) {
+  return D == 128 ? ((j < 8) ? dg * 8 + j : 64 + dg * 8 + (j - 8)) : dg * 8 + j;
+}
+
+template <typename T, int D>
+BSA_DEV void load_dims(const T* row, int dg, float* out);
+template <>
+BSA_DEV void load_dims<uint16_t, 128>(const uint16_t* row, int dg, float* out) {
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const uint4 u = *reinterpret_cast<const uint4*>(row + h2 * 64 + dg * 8);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[h2 * 8 + 2 * i] = __uint_as_float(w[i] << 16);
+      out[h2 * 8 + 2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  }
+}
+template <>
+BSA_DEV void load_dims<float, 64>(const float* row, int dg, float* out) {
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+    const float4 u = *reinterpret_cast<const float4*>(row + dg * 8 + 4 * h2);
+    out[4 * h2] = u.x;
+    out[4 * h2 + 1] = u.y;
+    out[4 * h2 + 2] = u.z;
+    out[4 * h2 + 3] = u.w;
+  }
+}
+
 template <typename T, int D, int TERMS>
 BSA_DEV void stats_chunk(const T* __restrict__ X, const int32_t* __restrict__ tokmap,
                          const float* __restrict__ inv_n, int c0, const float* sh_shift,
                          StageLds<D>& st, f32x16_t* acc, float* dpart) {
-  constexpr int E = D / 4;
-  const int tid = threadIdx.x, s = tid >> 2, q = tid & 3;
-  const int tok = tokmap ? tokmap[c0 + s] : c0 + s;
-  const float sc = inv_n ? inv_n[tok] : 1.f;
-  float xv[E];
-  load_row<T, E>(X + (size_t)tok * D + q * E, xv);
+  constexpr int DPT = D / 8;
+  const int tid = threadIdx.x, tp = tid & 31, dg = tid >> 5;
+  float xv[2][DPT], sc[2];
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const float d = xv[e] * sc - sh_shift[q * E + e];
-    dpart[e] += d;
-    const uint16_t h = f32_to_bf16(d);
-    st.hi[q * E + e][s] = h;
+  for (int u = 0; u < 2; ++u) {
+    const int pos = c0 + 2 * tp + u;
+    const int tok = tokmap ? tokmap[pos] : pos;
+    sc[u] = inv_n ? inv_n[tok] : 1.f;
+    load_dims<T, D>(X + (size_t)tok * D, dg, xv[u]);
+  }
+#pragma unroll
+  for (int j = 0; j < DPT; ++j) {
+    const int e = stat_dim<D>(dg, j);
+    const float sh = sh_shift[e];
+    const float d0 = xv[0][j] * sc[0] - sh, d1 = xv[1][j] * sc[1] - sh;
+    dpart[j] += d0 + d1;
+    const uint16_t h0 = f32_to_bf16(d0), h1 = f32_to_bf16(d1);
+    reinterpret_cast<uint32_t*>(&st.hi[e][0])[tp] = uint32_t(h0) | (uint32_t(h1) << 16);
     if (TERMS == 3) {
-      const float r1 = d - bf16_to_f32(h);
-      const uint16_t m = f32_to_bf16(r1);
-      st.mid[q * E + e][s] = m;
-      st.lo[q * E + e][s] = f32_to_bf16(r1 - bf16_to_f32(m));
+      const float r0 = d0 - bf16_to_f32(h0), r1 = d1 - bf16_to_f32(h1);
+      const uint16_t m0 = f32_to_bf16(r0), m1 = f32_to_bf16(r1);
+      reinterpret_cast<uint32_t*>(&st.mid[e][0])[tp] = uint32_t(m0) | (uint32_t(m1) << 16);
+      const uint16_t l0 = f32_to_bf16(r0 - bf16_to_f32(m0)), l1 = f32_to_bf16(r1 - bf16_to_f32(m1));
+      reinterpret_cast<uint32_t*>(&st.lo[e][0])[tp] = uint32_t(l0) | (uint32_t(l1) << 16);
     }
   }
   __syncthreads();
@@ -153,29 +194,22 @@ BSA_DEV void zero_acc(f32x16_t* acc) {
     for (int r = 0; r < 16; ++r) acc[t][r] = 0.f;
 }
 
-// Sum the per-thread d partials over the 64 token slots: result in out[D] (LDS).
-// red needs 4*D floats of LDS.
+// Sum the per-thread d partials over the 32 token pairs: result in out[D] (LDS).  Each
+// element group lives in one half-wave, so a 32-lane reduction suffices.  red is unused.
 template <int D>
 BSA_DEV void reduce_dpart(const float* dpart, float* red, float* out) {
-  constexpr int E = D / 4;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, q = tid & 3;
-  float v[E];
+  constexpr int DPT = D / 8;
+  const int tid = threadIdx.x, tp = tid & 31, dg = tid >> 5;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    float x = dpart[e];
-    // lanes with the same q: xor over lane bits 2..5
+  for (int j = 0; j < DPT; ++j) {
+    float x = dpart[j];
+    x += __shfl_xor(x, 1, 64);
+    x += __shfl_xor(x, 2, 64);
     x += __shfl_xor(x, 4, 64);
     x += __shfl_xor(x, 8, 64);
     x += __shfl_xor(x, 16, 64);
-    x += __shfl_xor(x, 32, 64);
-    v[e] = x;
+    if (tp == 0) out[stat_dim<D>(dg, j)] = x;
   }
-  if (lane < 4) {
-#pragma unroll
-    for (int e = 0; e < E; ++e) red[w * D + q * E + e] = v[e];
-  }
-  __syncthreads();
-  for (int d = tid; d < D; d += 256) out[d] = red[d] + red[D + d] + red[2 * D + d] + red[3 * D + d];
   __syncthreads();
 }
 
@@ -447,9 +481,9 @@ __global__ __launch_bounds__(256) void k_moments(const T* __restrict__ q,
   __syncthreads();
   f32x16_t acc[Cov<D>::TILES];
   zero_acc<D>(acc);
-  float dpart[D / 4];
+  float dpart[D / 8];
 #pragma unroll
-  for (int e = 0; e < D / 4; ++e) dpart[e] = 0.f;
+  for (int e = 0; e < D / 8; ++e) dpart[e] = 0.f;
   const int t1 = min(N, (chunk + 1) * kMomChunk);
   for (int c0 = chunk * kMomChunk; c0 < t1; c0 += kBlk)
     stats_chunk<T, D, TERMS>(X, nullptr, nullptr, c0, zero, st, acc, dpart);
@@ -635,9 +669,9 @@ __global__ __launch_bounds__(256) void k_wide_stats(ProblemArgs a) {
   __syncthreads();
   f32x16_t acc[Cov<D>::TILES];
   zero_acc<D>(acc);
-  float dpart[D / 4];
+  float dpart[D / 8];
 #pragma unroll
-  for (int e = 0; e < D / 4; ++e) dpart[e] = 0.f;
+  for (int e = 0; e < D / 8; ++e) dpart[e] = 0.f;
   for (int b = sb0; b < sb1; ++b)
     stats_chunk<T, D, 3>(X, tokmap, inv_n, b * kBlk, shift, st, acc, dpart);
   reduce_dpart<D>(dpart, red, dsum);
@@ -736,9 +770,9 @@ __global__ __launch_bounds__(256, 2) void k_subtree(ProblemArgs a, int ls, int l
       f32x16_t acc[Cov<D>::TILES];
       zero_acc<D>(acc);
       {
-        float dpart[D / 4];
+        float dpart[D / 8];
 #pragma unroll
-        for (int e = 0; e < D / 4; ++e) dpart[e] = 0.f;
+        for (int e = 0; e < D / 8; ++e) dpart[e] = 0.f;
         for (int b = b0; b < b0 + m; ++b)
           stats_chunk<T, D, 3>(X, pos, inv_n, b * kBlk, L.shift, st, acc, dpart);
         reduce_dpart<D>(dpart, L.red, L.mu);
@@ -760,7 +794,7 @@ __global__ __launch_bounds__(256, 2) void k_subtree(ProblemArgs a, int ls, int l
 }
 
 // grid (roots, P): subtrees whose root spans at most kSmallBlocks blocks.  The root's positions
-// and keys stay in LDS for all remaining levels; splits use rank selection (small_split).
+// and keys stay in LDS for all remaining levels.
 constexpr int kSmallBlocks = 8;
 template <typename T, int D>
 __global__ __launch_bounds__(256, 2) void k_subtree_small(ProblemArgs a, int ls) {
@@ -769,7 +803,8 @@ __global__ __launch_bounds__(256, 2) void k_subtree_small(ProblemArgs a, int ls)
   __shared__ int32_t spos[kSmallBlocks * kBlk];
   __shared__ int32_t stmp[kSmallBlocks * kBlk];
   __shared__ float skeys[kSmallBlocks * kBlk];
-  __shared__ int sm[8];
+  __shared__ int hist[4 * 256];
+  __shared__ int sm[16];
   const int g0 = a.lists[(size_t)ls * a.G + blockIdx.x], p = blockIdx.y;
   int rb0, rm;
   group_geom(a.nb, ls, g0, rb0, rm);
@@ -791,9 +826,9 @@ __global__ __launch_bounds__(256, 2) void k_subtree_small(ProblemArgs a, int ls)
       f32x16_t acc[Cov<D>::TILES];
       zero_acc<D>(acc);
       {
-        float dpart[D / 4];
+        float dpart[D / 8];
 #pragma unroll
-        for (int e = 0; e < D / 4; ++e) dpart[e] = 0.f;
+        for (int e = 0; e < D / 8; ++e) dpart[e] = 0.f;
         for (int b = lb0; b < lb0 + m; ++b)
           stats_chunk<T, D, 3>(X, spos, inv_n, b * kBlk, L.shift, st, acc, dpart);
         reduce_dpart<D>(dpart, L.red, L.mu);
@@ -804,7 +839,12 @@ __global__ __launch_bounds__(256, 2) void k_subtree_small(ProblemArgs a, int ls)
       for (int b = lb0; b < lb0 + m; ++b)
         project_chunk<T, D>(X, spos, inv_n, b * kBlk, L.w, skeys, proj);
       __syncthreads();
-      small_split<256>(skeys + lb0 * kBlk, spos + lb0 * kBlk, stmp, n, (m >> 1) * kBlk, sm);
+      const int want = (m >> 1) * kBlk;
+      int take;
+      const uint32_t T_ = select_smallest_w<256>(skeys + lb0 * kBlk, n, want, hist, sm, &take);
+      partition_w<256>(skeys + lb0 * kBlk, spos + lb0 * kBlk, stmp, n, want, T_, take, sm);
+      for (int i = threadIdx.x; i < n; i += 256) spos[lb0 * kBlk + i] = stmp[i];
+      __syncthreads();
     }
   }
   for (int i = threadIdx.x; i < rm * kBlk; i += 256) pos[i] = spos[i];

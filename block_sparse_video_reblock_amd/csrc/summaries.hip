@@ -150,6 +150,118 @@ __global__ __launch_bounds__(256) void k_summaries(
   }
 }
 
+
+// bf16, D = 128: 16-byte gathers, bf16 tiles in LDS, K's swizzled copy written straight from the
+// gathered registers (a K-layout piece is one 16-byte chunk of one row).  grid (nb, H).
+__global__ __launch_bounds__(256) void k_summaries_bf16(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ perm_k, const float* __restrict__ anchor, int N, float scale,
+    int meanpool, float* __restrict__ kt, float* __restrict__ vt, float* __restrict__ bias,
+    int ldb, uint4* __restrict__ ksw, uint4* __restrict__ vsw) {
+  constexpr int D = 128;
+  __shared__ uint4 sk[64][17];  // row r: 16 chunks of 8 bf16 (+1 pad)
+  __shared__ uint4 sv[64][17];
+  __shared__ float sw[64];
+  __shared__ float s_lse;
+  __shared__ float sred[2][D];
+  const int j = blockIdx.x, h = blockIdx.y, nb = gridDim.x;
+  const int tid = threadIdx.x;
+  const int32_t* pk = perm_k + (size_t)h * N + (size_t)j * kBlk;
+  uint4* kdst = ksw ? ksw + ((size_t)h * nb + j) * 1024 : nullptr;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = tid + 256 * u;  // chunk e: row e / 16, 16-byte column e % 16
+    const int r = e >> 4, cj = e & 15;
+    const size_t src = ((size_t)h * N + pk[r]) * (D / 8) + cj;
+    const uint4 kv = reinterpret_cast<const uint4*>(k)[src];
+    const uint4 vv = reinterpret_cast<const uint4*>(v)[src];
+    sk[r][cj] = kv;
+    sv[r][cj] = vv;
+    if (kdst) {
+      // K layout: piece (r/32)*8 + cj/2, lane (r%32) + 32*(cj%2)
+      kdst[((r >> 5) * 8 + (cj >> 1)) * 64 + (r & 31) + 32 * (cj & 1)] = kv;
+    }
+  }
+  __syncthreads();
+  auto kel = [&](int r, int d) -> float {
+    const uint16_t* row = reinterpret_cast<const uint16_t*>(&sk[r][0]);
+    return bf16_to_f32(row[d]);
+  };
+  auto vel = [&](int r, int d) -> float {
+    const uint16_t* row = reinterpret_cast<const uint16_t*>(&sv[r][0]);
+    return bf16_to_f32(row[d]);
+  };
+  if (tid < 64) {
+    float w;
+    if (meanpool) {
+      w = 1.f / 64.f;
+      if (tid == 0) s_lse = logf(64.f);
+    } else {
+      const float* qa = anchor + (size_t)h * D;
+      float x = 0.f;
+      for (int d = 0; d < D; ++d) x = fmaf(qa[d], kel(tid, d), x);
+      x *= scale;
+      const float mx = wave_max(x);
+      const float ex = expf(x - mx);
+      const float se = wave_sum(ex);
+      w = ex / se;
+      if (tid == 0) s_lse = mx + logf(se);
+    }
+    sw[tid] = w;
+  }
+  __syncthreads();
+  // weighted sums: thread -> (element d, half of the rows); halves combined in LDS
+  {
+    const int d = tid & (D - 1), half = tid >> 7;
+    float a = 0.f, b = 0.f;
+    for (int r = 32 * half; r < 32 * half + 32; ++r) {
+      a = fmaf(sw[r], kel(r, d), a);
+      b = fmaf(sw[r], vel(r, d), b);
+    }
+    if (half == 1) {
+      sred[0][d] = a;
+      sred[1][d] = b;
+    }
+    __syncthreads();
+    if (half == 0) {
+      a += sred[0][d];
+      b += sred[1][d];
+      const size_t dst = ((size_t)h * nb + j) * D + d;
+      kt[dst] = a;
+      vt[dst] = b;
+    }
+    __syncthreads();
+    if (half == 0) sred[0][d] = a;
+    __syncthreads();
+  }
+  if (tid < 64) {
+    float b;
+    if (meanpool) {
+      b = s_lse;
+    } else {
+      const float* qa = anchor + (size_t)h * D;
+      float x = 0.f;
+      for (int d = tid; d < D; d += 64) x = fmaf(qa[d], sred[0][d], x);
+      x = wave_sum(x);
+      b = s_lse - scale * x;
+    }
+    if (tid == 0) bias[(size_t)h * ldb + j] = b;
+  }
+  if (vsw) {
+    uint4* vdst = vsw + ((size_t)h * nb + j) * 1024;
+    for (int u = tid; u < 1024; u += 256) {
+      const int p = u >> 6, l = u & 63, g = l >> 5, l32 = l & 31;
+      const int a = p >> 2, c = p & 3, d = 32 * a + l32;
+      uint4 o;
+      o.x = uint32_t(f32_to_bf16(vel(vrow(c, g, 0), d))) | (uint32_t(f32_to_bf16(vel(vrow(c, g, 1), d))) << 16);
+      o.y = uint32_t(f32_to_bf16(vel(vrow(c, g, 2), d))) | (uint32_t(f32_to_bf16(vel(vrow(c, g, 3), d))) << 16);
+      o.z = uint32_t(f32_to_bf16(vel(vrow(c, g, 4), d))) | (uint32_t(f32_to_bf16(vel(vrow(c, g, 5), d))) << 16);
+      o.w = uint32_t(f32_to_bf16(vel(vrow(c, g, 6), d))) | (uint32_t(f32_to_bf16(vel(vrow(c, g, 7), d))) << 16);
+      vdst[u] = o;
+    }
+  }
+}
+
 // ------------------------------------------------- swizzled bf16 summary tiles (D = 128)
 // grid (tiles, H), 256 threads
 __global__ __launch_bounds__(256) void k_summary_tiles(const float* __restrict__ kt,
@@ -217,7 +329,7 @@ hipError_t launch_summaries(bool bf16, const void* k, const void* v, const int32
                             hipStream_t s) {
   dim3 grid(N / kBlk, H);
   if (bf16)
-    k_summaries<uint16_t, 128><<<grid, 256, 0, s>>>(
+    k_summaries_bf16<<<grid, 256, 0, s>>>(
         static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), perm_k, anchor, N,
         scale, meanpool ? 1 : 0, kt, vt, bias, ldb, static_cast<uint4*>(ksw),
         static_cast<uint4*>(vsw));

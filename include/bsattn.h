@@ -55,7 +55,7 @@ typedef enum {
 typedef enum { BSA_F32 = 0, BSA_BF16 = 1 } bsa_dtype;
 
 #define BSA_BLOCK 64
-#define BSA_MAX_TOKENS (1 << 22)
+#define BSA_MAX_TOKENS (1 << 19)
 
 typedef struct {
   int32_t heads;     /* >= 1 */
