@@ -336,10 +336,10 @@ struct DirLds {
 // On exit L.w holds the direction w (zero for a group without spread) and L.mu the mean.
 // Power step (w form): z = C_y w, t = M z, w <- t / sqrt(z . t); the normalisation is applied
 // when the next step reads t.
-template <typename T, int D>
-BSA_DEV void group_direction(f32x16_t* acc, DirLds& L, const MRegs<D>& M, int n,
-                             const T* __restrict__ X, const int32_t* __restrict__ tokmap,
-                             const float* __restrict__ inv_n, int pos0) {
+// Centre the statistics: acc = sum (y - shift)(y - shift)^T and L.mu = sum (y - shift) over n
+// tokens become the covariance C = acc / n - delta delta^T and the mean shift + delta.
+template <int D>
+BSA_DEV void finish_stats(f32x16_t* acc, DirLds& L, int n) {
   const int tid = threadIdx.x;
   const float inv = 1.f / float(n);
   if (tid < D) L.z[tid] = L.mu[tid] * inv;  // delta = mean - shift
@@ -351,6 +351,27 @@ BSA_DEV void group_direction(f32x16_t* acc, DirLds& L, const MRegs<D>& M, int n,
       acc[t][r] = acc[t][r] * inv - L.z[acc_row<D>(t, r)] * L.z[acc_col<D>(t)];
   if (tid < D) L.mu[tid] = L.shift[tid] + L.z[tid];
   __syncthreads();
+}
+
+template <typename T, int D>
+BSA_DEV void power_direction(f32x16_t* acc, DirLds& L, const MRegs<D>& M, int n,
+                             const T* __restrict__ X, const int32_t* __restrict__ tokmap,
+                             const float* __restrict__ inv_n, int pos0);
+
+template <typename T, int D>
+BSA_DEV void group_direction(f32x16_t* acc, DirLds& L, const MRegs<D>& M, int n,
+                             const T* __restrict__ X, const int32_t* __restrict__ tokmap,
+                             const float* __restrict__ inv_n, int pos0) {
+  finish_stats<D>(acc, L, n);
+  power_direction<T, D>(acc, L, M, n, X, tokmap, inv_n, pos0);
+}
+
+// Given the centred covariance in acc and the mean in L.mu, find the split direction L.w.
+template <typename T, int D>
+BSA_DEV void power_direction(f32x16_t* acc, DirLds& L, const MRegs<D>& M, int n,
+                             const T* __restrict__ X, const int32_t* __restrict__ tokmap,
+                             const float* __restrict__ inv_n, int pos0) {
+  const int tid = threadIdx.x;
   // start vector: the first position (smallest token id) whose centred vector is non-zero
   bool found = false;
   for (int p = pos0; p < pos0 + n; ++p) {
@@ -427,6 +448,9 @@ struct ProblemArgs {
   const float* mu_root;    // [P][D] mean of all y (the parent shift of level 0)
   float* wdir;             // [P][G][D]
   float* partial;          // [P][kSlots][D*D + D]
+  const float* cov_prev;   // [P][Gw][D*D] centred covariances of the previous wide level
+  float* cov_cur;          // [P][Gw][D*D] this level's, for the next level's right children
+  int gw, left_only;
   const int* lists;        // [L][G] active (m >= 2) nodes per level, ascending
   float* proj;             // optional [H][2][L][N]
   int level, G, slices;
@@ -658,7 +682,7 @@ __global__ __launch_bounds__(256) void k_wide_stats(ProblemArgs a) {
   __shared__ float shift[D];
   __shared__ float red[4 * D];
   __shared__ float dsum[D];
-  const int s = blockIdx.x, g = blockIdx.y, p = blockIdx.z;
+  const int s = blockIdx.x, g = a.left_only ? 2 * blockIdx.y : blockIdx.y, p = blockIdx.z;
   int b0, m;
   if (group_geom(a.nb, a.level, g, b0, m) != kGroupSplit) return;
   const int sb0 = b0 + (int)((long)s * m / a.slices), sb1 = b0 + (int)((long)(s + 1) * m / a.slices);
@@ -675,38 +699,66 @@ __global__ __launch_bounds__(256) void k_wide_stats(ProblemArgs a) {
   for (int b = sb0; b < sb1; ++b)
     stats_chunk<T, D, 3>(X, tokmap, inv_n, b * kBlk, shift, st, acc, dpart);
   reduce_dpart<D>(dpart, red, dsum);
-  float* slot = a.partial + ((size_t)p * kSlots + g * a.slices + s) * (D * D + D);
+  float* slot = a.partial + ((size_t)p * kSlots + blockIdx.y * a.slices + s) * (D * D + D);
   store_acc<D>(slot, acc);
   if (threadIdx.x < D) slot[D * D + threadIdx.x] = dsum[threadIdx.x];
 }
 
-// grid (G, P): reduce the slices of a group and find its direction
+// grid (G, P) or, for left-only levels, (G/2, P): reduce the slices of a group and find its
+// direction.  On left-only levels the statistics were accumulated for the left child only;
+// the right child's follow from the parent's centred covariance C_P:
+//   sum_R (y - mu_P)(y - mu_P)^T = n_P C_P - sum_L (y - mu_P)(y - mu_P)^T,
+//   sum_R (y - mu_P) = -sum_L (y - mu_P).
+// Each group's centred covariance is kept for the next level.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_wide_dir(ProblemArgs a) {
   __shared__ DirLds L;
-  const int g = blockIdx.x, p = blockIdx.y;
-  int b0, m;
-  if (group_geom(a.nb, a.level, g, b0, m) != kGroupSplit) return;
-  f32x16_t acc[Cov<D>::TILES];
-  zero_acc<D>(acc);
-  const float* base = a.partial + ((size_t)p * kSlots + g * a.slices) * (D * D + D);
-  float ds = 0.f;
-  for (int s = 0; s < a.slices; ++s) {
-    add_acc<D>(base + (size_t)s * (D * D + D), acc);
-    if (threadIdx.x < D) ds += base[(size_t)s * (D * D + D) + D * D + threadIdx.x];
-  }
-  if (threadIdx.x < D) {
-    L.mu[threadIdx.x] = ds;
-    L.shift[threadIdx.x] = parent_mean<D>(a, p, a.level, g)[threadIdx.x];
-  }
-  __syncthreads();
+  const int p = blockIdx.y;
+  const int g0 = a.left_only ? 2 * blockIdx.x : blockIdx.x;
   MRegs<D> M;
   M.load(problem_metric<D>(a, p));
-  group_direction<T, D>(acc, L, M, m * kBlk, problem_x<T, D>(a, p), problem_pos(a, p),
-                        a.inv_n + (size_t)p * a.N, b0 * kBlk);
-  if (threadIdx.x < D) {
-    group_mean<D>(a, p, a.level, g)[threadIdx.x] = L.mu[threadIdx.x];
-    a.wdir[((size_t)p * a.G + g) * D + threadIdx.x] = L.w[threadIdx.x];
+  const T* X = problem_x<T, D>(a, p);
+  const int32_t* pos = problem_pos(a, p);
+  const float* inv_n = a.inv_n + (size_t)p * a.N;
+  int pb0, pm;
+  if (a.left_only) group_geom(a.nb, a.level - 1, blockIdx.x, pb0, pm);
+  for (int child = 0; child < (a.left_only ? 2 : 1); ++child) {
+    const int g = g0 + child;
+    int b0, m;
+    if (group_geom(a.nb, a.level, g, b0, m) != kGroupSplit) continue;
+    f32x16_t acc[Cov<D>::TILES];
+    zero_acc<D>(acc);
+    const float* base = a.partial + ((size_t)p * kSlots + blockIdx.x * a.slices) * (D * D + D);
+    float ds = 0.f;
+    for (int s = 0; s < a.slices; ++s) {
+      add_acc<D>(base + (size_t)s * (D * D + D), acc);
+      if (threadIdx.x < D) ds += base[(size_t)s * (D * D + D) + D * D + threadIdx.x];
+    }
+    if (child == 1) {
+      // right child: n_P C_P - S_L, and the negated sum
+      const float* cp = a.cov_prev + ((size_t)p * a.gw + blockIdx.x) * D * D;
+      const float np = float(pm * kBlk);
+      const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+      for (int t = 0; t < Cov<D>::TILES; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          acc[t][r] = np * cp[((w * Cov<D>::TILES + t) * 16 + r) * 64 + lane] - acc[t][r];
+      ds = -ds;
+    }
+    if (threadIdx.x < D) {
+      L.mu[threadIdx.x] = ds;
+      L.shift[threadIdx.x] = parent_mean<D>(a, p, a.level, g)[threadIdx.x];
+    }
+    __syncthreads();
+    finish_stats<D>(acc, L, m * kBlk);
+    if (a.cov_cur) store_acc<D>(a.cov_cur + ((size_t)p * a.gw + g) * D * D, acc);
+    power_direction<T, D>(acc, L, M, m * kBlk, X, pos, inv_n, b0 * kBlk);
+    if (threadIdx.x < D) {
+      group_mean<D>(a, p, a.level, g)[threadIdx.x] = L.mu[threadIdx.x];
+      a.wdir[((size_t)p * a.G + g) * D + threadIdx.x] = L.w[threadIdx.x];
+    }
+    __syncthreads();
   }
 }
 
@@ -871,8 +923,8 @@ __global__ void k_gather_keys(int N, int L, int level, const float* __restrict__
 
 struct RebLayout {
   size_t mom, mom_partial, msplit, inv_n, ysum, mu_root, tmp, keys, mu, wdir, partial, lists,
-      total;
-  int L, G, nch_mom, nch_n;
+      cov0, cov1, total;
+  int L, G, nch_mom, nch_n, gw;
 };
 
 size_t al(size_t x) { return (x + 255) & ~size_t(255); }
@@ -898,6 +950,9 @@ RebLayout reb_layout(int H, int N, int D) {
   r.wdir = take(P * r.G * D * 4);
   r.partial = take(P * kSlots * (size_t)(D * D + D) * 4);
   r.lists = take((size_t)std::max(r.L, 1) * r.G * 4);
+  r.gw = std::min(r.G, kSlots / 2);  // wide levels have at most kSlots / 2 groups
+  r.cov0 = take(P * r.gw * (size_t)D * D * 4);
+  r.cov1 = take(P * r.gw * (size_t)D * D * 4);
   r.total = off;
   return r;
 }
@@ -941,6 +996,7 @@ hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm
   a.partial = reinterpret_cast<float*>(w + R.partial);
   a.lists = reinterpret_cast<int*>(w + R.lists);
   a.proj = proj_opt;
+  a.gw = R.gw;
   a.G = R.G;
   float* ysum = reinterpret_cast<float*>(w + R.ysum);
   if (sizeof(T) == 2)
@@ -968,8 +1024,12 @@ hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm
     a.level = level;
     a.slices = slices;
     const int G = 1 << level;
-    k_wide_stats<T, D><<<dim3(slices, G, P), 256, 0, s>>>(a);
-    k_wide_dir<T, D><<<dim3(G, P), 256, 0, s>>>(a);
+    a.left_only = level > 0 ? 1 : 0;
+    a.cov_prev = reinterpret_cast<float*>(w + ((level & 1) ? R.cov0 : R.cov1));
+    a.cov_cur = reinterpret_cast<float*>(w + ((level & 1) ? R.cov1 : R.cov0));
+    const int Gs = a.left_only ? G / 2 : G;
+    k_wide_stats<T, D><<<dim3(slices, Gs, P), 256, 0, s>>>(a);
+    k_wide_dir<T, D><<<dim3(Gs, P), 256, 0, s>>>(a);
     k_wide_proj<T, D><<<dim3(nb, P), 256, 0, s>>>(a);
     k_wide_split<<<dim3(G, P), 1024, 0, s>>>(a);
   }
