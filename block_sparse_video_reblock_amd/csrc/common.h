@@ -48,6 +48,28 @@ BSA_DEV float wave_max(float v) {
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
 }
+// DPP lane move within rows of 16 lanes (all lanes active).  CTRL: 0xB1 = lane ^ 1,
+// 0x4E = lane ^ 2 (quad permutations), 0x141 = mirror within 8 lanes, 0x140 = mirror within 16.
+template <int CTRL>
+BSA_DEV float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// sum over each row of 16 lanes, on every lane of the row
+BSA_DEV float row16_sum(float x) {
+  x += dpp_mov<0xB1>(x);
+  x += dpp_mov<0x4E>(x);
+  x += dpp_mov<0x141>(x);
+  x += dpp_mov<0x140>(x);
+  return x;
+}
+// wave64 sum, wave-uniform result (DPP within rows, then the four row totals)
+BSA_DEV float lane_value(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+BSA_DEV float wave_total(float x) {
+  x = row16_sum(x);
+  return (lane_value(x, 0) + lane_value(x, 16)) + (lane_value(x, 32) + lane_value(x, 48));
+}
 BSA_DEV int wave_sum_i(int v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -18,11 +18,12 @@
 // and the projection u_i . v = y_i . w.  So no factorisation of M is needed: the kernels keep
 // the group covariance of y (C_y) and M, both 128 x 128 fp32.
 //
-// Per level and group: C_y is accumulated by MFMA from bf16 splits of the centred values
-// d = y - shift (shift = the parent group's mean, so cancellation stays small):
-// d = hi + mid + lo (three bf16 terms) and the six products down to 2^-24 relative size are
-// accumulated in fp32 (two terms, dropping lo lo^T, leave errors near 1e-5 in the projections of
-// ill-conditioned groups; three terms match an exact covariance).  Wide levels
+// Per level and group: C_y is accumulated by MFMA from 16-bit splits of the centred values
+// d = y - shift (shift = the parent group's mean, so cancellation stays small): s d = hi + mid
+// with two fp16 terms under a power-of-two scale s per problem, and the three products down to
+// 2^-22 relative size accumulated in fp32 (a two-term bf16 split, 16 bits, leaves errors near
+// 1e-4 in the projections of ill-conditioned groups; 22 bits match an exact covariance to fp32
+// rounding of the projections).  Wide levels
 // (few large groups) split each group over several workgroups and reduce the partials in a fixed
 // order; narrow levels run one fused workgroup per group.  All reductions have a fixed order,
 // so results are deterministic.
@@ -44,72 +45,83 @@ BSA_DEV bf16x8_t lds_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
 }
 
-// Register-resident D x D accumulator: 4 waves, each holding TILES 32 x 32 MFMA tiles.
+// Register-resident D x D accumulator: 4 waves, each holding TILES 32 x 32 MFMA tiles.  For
+// D = 128 wave w holds the column block w of every row block (FULL_COLS): each lane then holds
+// a whole column of the symmetric matrix over its two half-waves, so a product C v needs no
+// exchange between waves.  For D = 64 wave w holds the single tile (w / 2, w % 2).
 template <int D>
 struct Cov {
   static constexpr int AC = D / 32;
   static constexpr int TILES = AC * AC / 4;
-  BSA_DEV static int ac(int w, int t) { return D == 128 ? w : (w >> 1); }
-  BSA_DEV static int bc(int w, int t) { return D == 128 ? t : (w & 1); }
+  static constexpr bool FULL_COLS = (D == 128);
+  BSA_DEV static int ac(int w, int t) { return D == 128 ? t : (w >> 1); }
+  BSA_DEV static int bc(int w, int t) { return D == 128 ? w : (w & 1); }
 };
 
-template <int D>
+// How the centred values d of a chunk are split into 16-bit MFMA operands:
+//  kExact:   one bf16 term; d is exact in bf16 (raw bf16 inputs, no scale, no shift).
+//  kBf16x3:  d = hi + mid + lo, bf16 each (24 significant bits); the products hi hi, hi mid,
+//            mid hi, hi lo, lo hi, mid mid are accumulated, the dropped ones lie below fp32
+//            rounding of the sum.
+//  kF16x2:   s d = hi + mid, fp16 each, with s a power of two per problem chosen so that
+//            |s d| <= 2^14 for every token (no overflow).  hi and mid carry 11 significant bits
+//            each, so hi + mid represents s d to about 2^-22 relative (or 2^-25 absolute where
+//            mid is subnormal); the products hi hi, hi mid, mid hi are accumulated (mid mid is
+//            below 2^-22 relative) and the sum is multiplied by 1 / s^2 (exact).  Half the
+//            MFMA work of kBf16x3 for a covariance accurate to a few parts in 10^7.
+constexpr int kExact = 1, kF16x2 = 2, kBf16x3 = 3;
+template <int MODE>
+constexpr int split_terms() { return MODE == kExact ? 1 : (MODE == kF16x2 ? 2 : 3); }
+
+template <int D, int NT>
 struct StageLds {
-  uint16_t hi[D][kStageStride];
-  uint16_t mid[D][kStageStride];
-  uint16_t lo[D][kStageStride];
+  uint16_t t[NT][D][kStageStride];
 };
 
-template <typename T, int E>
-BSA_DEV void load_row(const T* p, float* out);
-template <>
-BSA_DEV void load_row<uint16_t, 32>(const uint16_t* p, float* out) {
-  const uint4* v = reinterpret_cast<const uint4*>(p);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint4 u = v[i];
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      out[8 * i + 2 * j] = __uint_as_float(w[j] << 16);
-      out[8 * i + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
-    }
-  }
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+BSA_DEV f16x8_t lds_f16x8(const uint16_t* p) {
+  return __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(p));
 }
-template <>
-BSA_DEV void load_row<float, 16>(const float* p, float* out) {
-  const float4* v = reinterpret_cast<const float4*>(p);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float4 u = v[i];
-    out[4 * i] = u.x;
-    out[4 * i + 1] = u.y;
-    out[4 * i + 2] = u.z;
-    out[4 * i + 3] = u.w;
-  }
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+// round-to-nearest-even pack of two floats to fp16 (v_cvt_pk_f16_f32)
+BSA_DEV uint32_t cvt_pk_f16(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
+}
+BSA_DEV f32x2_t unpack_f16x2(uint32_t u) {
+  return __builtin_convertvector(__builtin_bit_cast(f16x2_t, u), f32x2_t);
 }
 
 // One 64-position chunk of the covariance accumulation.  Thread t stages the token pair
 // (2 (t%32), 2 (t%32) + 1) for the DPT = D/8 elements of element group t/32 (see stat_dim):
-// d = x * scale - shift, split into bf16 terms written as packed pairs of tokens, so the
+// d = x * scale - shift, split into 16-bit terms written as packed pairs of tokens, so the
 // transposed staging rows of the two groups of a wave sit 8 rows (32 banks) apart.
 // tokmap == nullptr means position = token id; inv_n == nullptr means scale 1.
-// TERMS = 1: d is exact in bf16 (raw bf16 inputs).  TERMS = 3: d = hi + mid + lo (bf16 each,
-// 24 significant bits) and the products hi hi, hi mid, mid hi, hi lo, lo hi, mid mid are
-// accumulated; the dropped terms are below fp32 rounding of the sum.
 template <int D>
 BSA_DEV int stat_dim(int dg, int j) {
   return D == 128 ? ((j < 8) ? dg * 8 + j : 64 + dg * 8 + (j - 8)) : dg * 8 + j;
 }
 
+// The DPT elements of element group dg of one row, as two 16-byte pieces (raw input bits).
 template <typename T, int D>
-BSA_DEV void load_dims(const T* row, int dg, float* out);
+BSA_DEV void load_dims(const T* row, int dg, uint4* raw);
 template <>
-BSA_DEV void load_dims<uint16_t, 128>(const uint16_t* row, int dg, float* out) {
+BSA_DEV void load_dims<uint16_t, 128>(const uint16_t* row, int dg, uint4* raw) {
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) raw[h2] = *reinterpret_cast<const uint4*>(row + h2 * 64 + dg * 8);
+}
+template <>
+BSA_DEV void load_dims<float, 64>(const float* row, int dg, uint4* raw) {
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) raw[h2] = *reinterpret_cast<const uint4*>(row + dg * 8 + 4 * h2);
+}
+template <typename T, int D>
+BSA_DEV void unpack_dims(const uint4* raw, float* out);
+template <>
+BSA_DEV void unpack_dims<uint16_t, 128>(const uint4* raw, float* out) {
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2) {
-    const uint4 u = *reinterpret_cast<const uint4*>(row + h2 * 64 + dg * 8);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    const uint32_t w[4] = {raw[h2].x, raw[h2].y, raw[h2].z, raw[h2].w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       out[h2 * 8 + 2 * i] = __uint_as_float(w[i] << 16);
@@ -118,63 +130,102 @@ BSA_DEV void load_dims<uint16_t, 128>(const uint16_t* row, int dg, float* out) {
   }
 }
 template <>
-BSA_DEV void load_dims<float, 64>(const float* row, int dg, float* out) {
+BSA_DEV void unpack_dims<float, 64>(const uint4* raw, float* out) {
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2) {
-    const float4 u = *reinterpret_cast<const float4*>(row + dg * 8 + 4 * h2);
-    out[4 * h2] = u.x;
-    out[4 * h2 + 1] = u.y;
-    out[4 * h2 + 2] = u.z;
-    out[4 * h2 + 3] = u.w;
+    out[4 * h2] = __uint_as_float(raw[h2].x);
+    out[4 * h2 + 1] = __uint_as_float(raw[h2].y);
+    out[4 * h2 + 2] = __uint_as_float(raw[h2].z);
+    out[4 * h2 + 3] = __uint_as_float(raw[h2].w);
   }
 }
 
-template <typename T, int D, int TERMS>
-BSA_DEV void stats_chunk(const T* __restrict__ X, const int32_t* __restrict__ tokmap,
-                         const float* __restrict__ inv_n, int c0, const float* sh_shift,
-                         StageLds<D>& st, f32x16_t* acc, float* dpart) {
-  constexpr int DPT = D / 8;
-  const int tid = threadIdx.x, tp = tid & 31, dg = tid >> 5;
-  float xv[2][DPT], sc[2];
+// Raw inputs of one chunk for one thread: its two tokens' DPT elements (input bits, 16
+// registers) and scales.
+template <typename T, int D>
+struct ChunkRegs {
+  uint4 raw[2][2];
+  float sc[2];
+};
+
+template <typename T, int D>
+BSA_DEV void stats_load(const T* __restrict__ X, const int32_t* __restrict__ tokmap,
+                        const float* __restrict__ inv_n, int c0, ChunkRegs<T, D>& r) {
+  const int tp = threadIdx.x & 31, dg = threadIdx.x >> 5;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int pos = c0 + 2 * tp + u;
     const int tok = tokmap ? tokmap[pos] : pos;
-    sc[u] = inv_n ? inv_n[tok] : 1.f;
-    load_dims<T, D>(X + (size_t)tok * D, dg, xv[u]);
+    r.sc[u] = inv_n ? inv_n[tok] : 1.f;
+    load_dims<T, D>(X + (size_t)tok * D, dg, r.raw[u]);
   }
+}
+
+// Stage one chunk (centred, split) into LDS and accumulate d; no barrier.  ysc: the kF16x2
+// scale s.
+template <typename T, int D, int MODE>
+BSA_DEV void stats_stage(const ChunkRegs<T, D>& r, const float* sh_shift, float ysc,
+                         StageLds<D, split_terms<MODE>()>& st, float* dpart) {
+  constexpr int DPT = D / 8;
+  const int tp = threadIdx.x & 31, dg = threadIdx.x >> 5;
+  float xv[2][DPT];
+  unpack_dims<T, D>(r.raw[0], xv[0]);
+  unpack_dims<T, D>(r.raw[1], xv[1]);
 #pragma unroll
   for (int j = 0; j < DPT; ++j) {
     const int e = stat_dim<D>(dg, j);
     const float sh = sh_shift[e];
-    const float d0 = xv[0][j] * sc[0] - sh, d1 = xv[1][j] * sc[1] - sh;
+    const float d0 = xv[0][j] * r.sc[0] - sh, d1 = xv[1][j] * r.sc[1] - sh;
     dpart[j] += d0 + d1;
-    const uint16_t h0 = f32_to_bf16(d0), h1 = f32_to_bf16(d1);
-    reinterpret_cast<uint32_t*>(&st.hi[e][0])[tp] = uint32_t(h0) | (uint32_t(h1) << 16);
-    if (TERMS == 3) {
-      const float r0 = d0 - bf16_to_f32(h0), r1 = d1 - bf16_to_f32(h1);
-      const uint16_t m0 = f32_to_bf16(r0), m1 = f32_to_bf16(r1);
-      reinterpret_cast<uint32_t*>(&st.mid[e][0])[tp] = uint32_t(m0) | (uint32_t(m1) << 16);
-      const uint16_t l0 = f32_to_bf16(r0 - bf16_to_f32(m0)), l1 = f32_to_bf16(r1 - bf16_to_f32(m1));
-      reinterpret_cast<uint32_t*>(&st.lo[e][0])[tp] = uint32_t(l0) | (uint32_t(l1) << 16);
+    // round-to-nearest-even packs (one instruction per token pair and term)
+    if (MODE == kF16x2) {
+      const float s0 = d0 * ysc, s1 = d1 * ysc;  // exact: ysc is a power of two
+      const uint32_t hp = cvt_pk_f16(s0, s1);
+      const f32x2_t hv = unpack_f16x2(hp);
+      reinterpret_cast<uint32_t*>(&st.t[0][e][0])[tp] = hp;
+      reinterpret_cast<uint32_t*>(&st.t[1][e][0])[tp] = cvt_pk_f16(s0 - hv.x, s1 - hv.y);
+    } else {
+      const uint32_t hp = cvt_pk_bf16(d0, d1);
+      reinterpret_cast<uint32_t*>(&st.t[0][e][0])[tp] = hp;
+      if (MODE == kBf16x3) {
+        const float r0 = d0 - __uint_as_float(hp << 16);
+        const float r1 = d1 - __uint_as_float(hp & 0xFFFF0000u);
+        const uint32_t mp = cvt_pk_bf16(r0, r1);
+        reinterpret_cast<uint32_t*>(&st.t[1][e][0])[tp] = mp;
+        reinterpret_cast<uint32_t*>(&st.t[2][e][0])[tp] =
+            cvt_pk_bf16(r0 - __uint_as_float(mp << 16), r1 - __uint_as_float(mp & 0xFFFF0000u));
+      }
     }
   }
-  __syncthreads();
-  const int lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+}
+
+template <int D, int MODE>
+BSA_DEV void stats_mfma(const StageLds<D, split_terms<MODE>()>& st, f32x16_t* acc) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, g = lane >> 5, l32 = lane & 31;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
     for (int t = 0; t < Cov<D>::TILES; ++t) {
       const int ra = 32 * Cov<D>::ac(w, t) + l32, rb = 32 * Cov<D>::bc(w, t) + l32;
       const int col = 16 * ks + 8 * g;
-      const bf16x8_t aH = lds_bf16x8(&st.hi[ra][col]);
-      const bf16x8_t bH = lds_bf16x8(&st.hi[rb][col]);
+      if (MODE == kF16x2) {
+        const f16x8_t aH = lds_f16x8(&st.t[0][ra][col]);
+        const f16x8_t bH = lds_f16x8(&st.t[0][rb][col]);
+        const f16x8_t aM = lds_f16x8(&st.t[1][ra][col]);
+        const f16x8_t bM = lds_f16x8(&st.t[1][rb][col]);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aH, bH, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aH, bM, acc[t], 0, 0, 0);
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(aM, bH, acc[t], 0, 0, 0);
+        continue;
+      }
+      const bf16x8_t aH = lds_bf16x8(&st.t[0][ra][col]);
+      const bf16x8_t bH = lds_bf16x8(&st.t[0][rb][col]);
       acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aH, bH, acc[t], 0, 0, 0);
-      if (TERMS == 3) {
-        const bf16x8_t aM = lds_bf16x8(&st.mid[ra][col]);
-        const bf16x8_t bM = lds_bf16x8(&st.mid[rb][col]);
-        const bf16x8_t aL = lds_bf16x8(&st.lo[ra][col]);
-        const bf16x8_t bL = lds_bf16x8(&st.lo[rb][col]);
+      if (MODE == kBf16x3) {
+        const bf16x8_t aM = lds_bf16x8(&st.t[1][ra][col]);
+        const bf16x8_t bM = lds_bf16x8(&st.t[1][rb][col]);
+        const bf16x8_t aL = lds_bf16x8(&st.t[2][ra][col]);
+        const bf16x8_t bL = lds_bf16x8(&st.t[2][rb][col]);
         acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aH, bM, acc[t], 0, 0, 0);
         acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aM, bH, acc[t], 0, 0, 0);
         acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aH, bL, acc[t], 0, 0, 0);
@@ -183,7 +234,27 @@ BSA_DEV void stats_chunk(const T* __restrict__ X, const int32_t* __restrict__ to
       }
     }
   }
-  __syncthreads();
+}
+
+// Accumulate the chunks [blk0, blk1) (64-position blocks).  With PREFETCH the next chunk's
+// inputs are loaded into registers while the current chunk's MFMAs run (for kernels with
+// registers to spare); without it each chunk's loads complete before it is staged.
+template <typename T, int D, int MODE, bool PREFETCH>
+BSA_DEV void stats_range(const T* __restrict__ X, const int32_t* __restrict__ tokmap,
+                         const float* __restrict__ inv_n, int blk0, int blk1,
+                         const float* sh_shift, float ysc, StageLds<D, split_terms<MODE>()>& st,
+                         f32x16_t* acc, float* dpart) {
+  if (blk0 >= blk1) return;
+  ChunkRegs<T, D> cur;
+  if (PREFETCH) stats_load<T, D>(X, tokmap, inv_n, blk0 * kBlk, cur);
+  for (int b = blk0; b < blk1; ++b) {
+    if (!PREFETCH) stats_load<T, D>(X, tokmap, inv_n, b * kBlk, cur);
+    stats_stage<T, D, MODE>(cur, sh_shift, ysc, st, dpart);
+    __syncthreads();
+    if (PREFETCH && b + 1 < blk1) stats_load<T, D>(X, tokmap, inv_n, (b + 1) * kBlk, cur);
+    stats_mfma<D, MODE>(st, acc);
+    __syncthreads();
+  }
 }
 
 template <int D>
@@ -202,11 +273,7 @@ BSA_DEV void reduce_dpart(const float* dpart, float* red, float* out) {
   const int tid = threadIdx.x, tp = tid & 31, dg = tid >> 5;
 #pragma unroll
   for (int j = 0; j < DPT; ++j) {
-    float x = dpart[j];
-    x += __shfl_xor(x, 1, 64);
-    x += __shfl_xor(x, 2, 64);
-    x += __shfl_xor(x, 4, 64);
-    x += __shfl_xor(x, 8, 64);
+    float x = row16_sum(dpart[j]);
     x += __shfl_xor(x, 16, 64);
     if (tp == 0) out[stat_dim<D>(dg, j)] = x;
   }
@@ -243,26 +310,47 @@ BSA_DEV int acc_col(int t) {
   return 32 * Cov<D>::bc(w, t) + (lane & 31);
 }
 
-// out = C v for the symmetric register-resident C (column form).  red: AC*D floats of LDS.
+// out = vs * C v for the symmetric register-resident C (column form; v, out 16-byte aligned).
+// red: AC*D floats of LDS (used when a wave does not hold whole columns).
 template <int D>
 BSA_DEV void cov_matvec(const f32x16_t* acc, const float* v, float vs, float* out, float* red) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if constexpr (Cov<D>::FULL_COLS) {
+    // lane: column 32 w + lane % 32, rows 32 t + 8 j + 4 (lane / 32) + {0..3} of every tile t
+    float s[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int t = 0; t < Cov<D>::TILES; ++t) {
-    float s = 0.f;
+    for (int t = 0; t < Cov<D>::TILES; ++t) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s = fmaf(acc[t][r], v[acc_row<D>(t, r)] * vs, s);
-    s += __shfl_xor(s, 32, 64);
-    if (lane < 32) red[Cov<D>::ac(w, t) * D + acc_col<D>(t)] = s;
+      for (int j = 0; j < 4; ++j) {
+        const float4 vv = *reinterpret_cast<const float4*>(v + 32 * t + 8 * j + 4 * (lane >> 5));
+        s[j] = fmaf(acc[t][4 * j], vv.x, s[j]);
+        s[j] = fmaf(acc[t][4 * j + 1], vv.y, s[j]);
+        s[j] = fmaf(acc[t][4 * j + 2], vv.z, s[j]);
+        s[j] = fmaf(acc[t][4 * j + 3], vv.w, s[j]);
+      }
+    }
+    float z = (s[0] + s[1]) + (s[2] + s[3]);
+    z += __shfl_xor(z, 32, 64);
+    if (lane < 32) out[32 * w + lane] = z * vs;
+    __syncthreads();
+  } else {
+#pragma unroll
+    for (int t = 0; t < Cov<D>::TILES; ++t) {
+      float s = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s = fmaf(acc[t][r], v[acc_row<D>(t, r)], s);
+      s += __shfl_xor(s, 32, 64);
+      if (lane < 32) red[Cov<D>::ac(w, t) * D + acc_col<D>(t)] = s;
+    }
+    __syncthreads();
+    for (int b = threadIdx.x; b < D; b += 256) {
+      float s = 0.f;
+#pragma unroll
+      for (int a = 0; a < Cov<D>::AC; ++a) s += red[a * D + b];
+      out[b] = s * vs;
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  for (int b = threadIdx.x; b < D; b += 256) {
-    float s = 0.f;
-#pragma unroll
-    for (int a = 0; a < Cov<D>::AC; ++a) s += red[a * D + b];
-    out[b] = s;
-  }
-  __syncthreads();
 }
 
 // M held in registers: thread t owns row t / R, columns [(t % R) * D / R, +D / R), R = 256 / D.
@@ -276,33 +364,42 @@ struct MRegs {
 #pragma unroll
     for (int i = 0; i < W; ++i) m[i] = M[row * D + c0 + i];
   }
+  // (M v)[row] on every thread of the row's R lanes (v 16-byte aligned LDS)
+  BSA_DEV float row_product(const float* v) const {
+    const int c0 = (threadIdx.x % R) * W;
+    float s[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < W; i += 4) {
+      const float4 vv = *reinterpret_cast<const float4*>(v + c0 + i);
+      float& a = s[(i >> 2) & 3];
+      a = fmaf(m[i], vv.x, a);
+      a = fmaf(m[i + 1], vv.y, a);
+      a = fmaf(m[i + 2], vv.z, a);
+      a = fmaf(m[i + 3], vv.w, a);
+    }
+    float r = (s[0] + s[1]) + (s[2] + s[3]);
+    r += dpp_mov<0xB1>(r);                 // lane ^ 1
+    if (R == 4) r += dpp_mov<0x4E>(r);     // lane ^ 2
+    return r;
+  }
   BSA_DEV void matvec(const float* v, float* out) const {
-    const int row = threadIdx.x / R, c0 = (threadIdx.x % R) * W;
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < W; ++i) s = fmaf(m[i], v[c0 + i], s);
-#pragma unroll
-    for (int o = 1; o < R; o <<= 1) s += __shfl_xor(s, o, 64);
-    if (threadIdx.x % R == 0) out[row] = s;
+    const float s = row_product(v);
+    if (threadIdx.x % R == 0) out[threadIdx.x / R] = s;
     __syncthreads();
   }
   // out = M v, and returns v . out to every thread (sm: 4 floats of LDS).  One barrier.
   BSA_DEV float matvec_dot(const float* v, float* out, float* sm) const {
-    const int row = threadIdx.x / R, c0 = (threadIdx.x % R) * W;
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < W; ++i) s = fmaf(m[i], v[c0 + i], s);
-#pragma unroll
-    for (int o = 1; o < R; o <<= 1) s += __shfl_xor(s, o, 64);
+    const int row = threadIdx.x / R;
+    const float s = row_product(v);
     float d = 0.f;
     if (threadIdx.x % R == 0) {
       out[row] = s;
       d = s * v[row];
     }
-    d = wave_sum(d);
+    d = wave_total(d);
     if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = d;
     __syncthreads();
-    return sm[0] + sm[1] + sm[2] + sm[3];
+    return (sm[0] + sm[1]) + (sm[2] + sm[3]);
   }
 };
 
@@ -319,7 +416,7 @@ BSA_DEV float block_dot(const float* a, const float* b, float* sm) {
   return r;
 }
 
-struct DirLds {
+struct __align__(16) DirLds {
   float shift[128];
   float mu[128];
   float e0[128];
@@ -336,19 +433,27 @@ struct DirLds {
 // On exit L.w holds the direction w (zero for a group without spread) and L.mu the mean.
 // Power step (w form): z = C_y w, t = M z, w <- t / sqrt(z . t); the normalisation is applied
 // when the next step reads t.
-// Centre the statistics: acc = sum (y - shift)(y - shift)^T and L.mu = sum (y - shift) over n
-// tokens become the covariance C = acc / n - delta delta^T and the mean shift + delta.
+// Centre the statistics: acc_scale * acc = sum (y - shift)(y - shift)^T and L.mu = sum (y - shift)
+// over n tokens become the covariance C = acc_scale * acc / n - delta delta^T and the mean
+// shift + delta.
 template <int D>
-BSA_DEV void finish_stats(f32x16_t* acc, DirLds& L, int n) {
+BSA_DEV void finish_stats(f32x16_t* acc, DirLds& L, int n, float acc_scale) {
   const int tid = threadIdx.x;
-  const float inv = 1.f / float(n);
+  const float inv = 1.f / float(n), inv_acc = acc_scale * inv;
   if (tid < D) L.z[tid] = L.mu[tid] * inv;  // delta = mean - shift
   __syncthreads();
 #pragma unroll
-  for (int t = 0; t < Cov<D>::TILES; ++t)
+  for (int t = 0; t < Cov<D>::TILES; ++t) {
+    const float zc = L.z[acc_col<D>(t)];
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      acc[t][r] = acc[t][r] * inv - L.z[acc_row<D>(t, r)] * L.z[acc_col<D>(t)];
+    for (int j = 0; j < 4; ++j) {
+      const float4 zr = *reinterpret_cast<const float4*>(&L.z[acc_row<D>(t, 4 * j)]);
+      acc[t][4 * j] = acc[t][4 * j] * inv_acc - zr.x * zc;
+      acc[t][4 * j + 1] = acc[t][4 * j + 1] * inv_acc - zr.y * zc;
+      acc[t][4 * j + 2] = acc[t][4 * j + 2] * inv_acc - zr.z * zc;
+      acc[t][4 * j + 3] = acc[t][4 * j + 3] * inv_acc - zr.w * zc;
+    }
+  }
   if (tid < D) L.mu[tid] = L.shift[tid] + L.z[tid];
   __syncthreads();
 }
@@ -359,10 +464,10 @@ BSA_DEV void power_direction(f32x16_t* acc, DirLds& L, const MRegs<D>& M, int n,
                              const float* __restrict__ inv_n, int pos0);
 
 template <typename T, int D>
-BSA_DEV void group_direction(f32x16_t* acc, DirLds& L, const MRegs<D>& M, int n,
+BSA_DEV void group_direction(f32x16_t* acc, DirLds& L, const MRegs<D>& M, int n, float acc_scale,
                              const T* __restrict__ X, const int32_t* __restrict__ tokmap,
                              const float* __restrict__ inv_n, int pos0) {
-  finish_stats<D>(acc, L, n);
+  finish_stats<D>(acc, L, n, acc_scale);
   power_direction<T, D>(acc, L, M, n, X, tokmap, inv_n, pos0);
 }
 
@@ -412,25 +517,65 @@ BSA_DEV void power_direction(f32x16_t* acc, DirLds& L, const MRegs<D>& M, int n,
   __syncthreads();
 }
 
-// projections of 64 positions [c0, c0+64): key = inv_n * (x . w); 4 threads per position
-template <typename T, int D>
-BSA_DEV void project_chunk(const T* __restrict__ X, const int32_t* __restrict__ tokmap,
-                           const float* __restrict__ inv_n, int c0, const float* w,
+// Projections of the positions of blocks [blk0, blk1): key = inv_n * (x . w), 4 threads per
+// position (a quarter row each); the loads of CH blocks are issued together.
+template <typename T, int D, int CH = 4>
+BSA_DEV void project_range(const T* __restrict__ X, const int32_t* __restrict__ tokmap,
+                           const float* __restrict__ inv_n, int blk0, int blk1, const float* w,
                            float* __restrict__ keys, float* __restrict__ proj_out) {
-  constexpr int E = D / 4;
+  constexpr int E = D / 4;                 // elements per quarter row
+  constexpr int NV = E * sizeof(T) / 16;   // 16-byte pieces per quarter row
   const int tid = threadIdx.x, s = tid >> 2, q = tid & 3;
-  const int tok = tokmap[c0 + s];
-  float xv[E];
-  load_row<T, E>(X + (size_t)tok * D + q * E, xv);
-  float a = 0.f;
+  for (int b = blk0; b < blk1; b += CH) {
+    const int nbk = min(CH, blk1 - b);
+    int tok[CH];
+    uint4 raw[CH][NV];
+    float sc[CH];
 #pragma unroll
-  for (int e = 0; e < E; ++e) a = fmaf(xv[e], w[q * E + e], a);
-  a += __shfl_xor(a, 1, 64);
-  a += __shfl_xor(a, 2, 64);
-  if (q == 0) {
-    const float key = a * inv_n[tok];
-    keys[c0 + s] = key;
-    if (proj_out) proj_out[tok] = key;
+    for (int c = 0; c < CH; ++c)
+      if (c < nbk) tok[c] = tokmap[(b + c) * kBlk + s];
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+      if (c < nbk) {
+        const uint4* src = reinterpret_cast<const uint4*>(X + (size_t)tok[c] * D + q * E);
+#pragma unroll
+        for (int i = 0; i < NV; ++i) raw[c][i] = src[i];
+        sc[c] = inv_n[tok[c]];
+      }
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+      if (c < nbk) {
+        float xv[E];
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int i = 0; i < NV; ++i) {
+            const uint32_t u[4] = {raw[c][i].x, raw[c][i].y, raw[c][i].z, raw[c][i].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              xv[8 * i + 2 * j] = __uint_as_float(u[j] << 16);
+              xv[8 * i + 2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < NV; ++i) {
+            xv[4 * i] = __uint_as_float(raw[c][i].x);
+            xv[4 * i + 1] = __uint_as_float(raw[c][i].y);
+            xv[4 * i + 2] = __uint_as_float(raw[c][i].z);
+            xv[4 * i + 3] = __uint_as_float(raw[c][i].w);
+          }
+        }
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) a = fmaf(xv[e], w[q * E + e], a);
+        a += dpp_mov<0xB1>(a);  // lane ^ 1
+        a += dpp_mov<0x4E>(a);  // lane ^ 2
+        if (q == 0) {
+          const float key = a * sc[c];
+          keys[(b + c) * kBlk + s] = key;
+          if (proj_out) proj_out[tok[c]] = key;
+        }
+      }
   }
 }
 
@@ -446,6 +591,7 @@ struct ProblemArgs {
   float* keys;             // [P][N] projections by position
   float* mu;               // [P][2^L][D] group means, heap order (node (l, g) at 2^l - 1 + g)
   const float* mu_root;    // [P][D] mean of all y (the parent shift of level 0)
+  const float* yscale;     // [P][2]: the power-of-two scale s of the fp16 split and 1 / s^2
   float* wdir;             // [P][G][D]
   float* partial;          // [P][kSlots][D*D + D]
   const float* cov_prev;   // [P][Gw][D*D] centred covariances of the previous wide level
@@ -496,8 +642,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void k_moments(const T* __restrict__ q,
                                                  const T* __restrict__ k, int N,
                                                  float* __restrict__ partial) {
-  constexpr int TERMS = sizeof(T) == 4 ? 3 : 1;
-  __shared__ StageLds<D> st;
+  constexpr int MODE = sizeof(T) == 4 ? kBf16x3 : kExact;
+  __shared__ StageLds<D, split_terms<MODE>()> st;
   __shared__ float zero[D];
   const int chunk = blockIdx.x, side = blockIdx.y, h = blockIdx.z, nch = gridDim.x;
   const T* X = (side ? k : q) + (size_t)h * N * D;
@@ -509,8 +655,8 @@ __global__ __launch_bounds__(256) void k_moments(const T* __restrict__ q,
 #pragma unroll
   for (int e = 0; e < D / 8; ++e) dpart[e] = 0.f;
   const int t1 = min(N, (chunk + 1) * kMomChunk);
-  for (int c0 = chunk * kMomChunk; c0 < t1; c0 += kBlk)
-    stats_chunk<T, D, TERMS>(X, nullptr, nullptr, c0, zero, st, acc, dpart);
+  stats_range<T, D, MODE, true>(X, nullptr, nullptr, chunk * kMomChunk / kBlk, t1 / kBlk, zero,
+                                1.f, st, acc, dpart);
   store_acc<D>(partial + (((size_t)h * 2 + side) * nch + chunk) * D * D, acc);
 }
 
@@ -529,7 +675,7 @@ __global__ __launch_bounds__(256) void k_moments_finish(const float* __restrict_
   // register-dump index -> (wave, tile, reg, lane) -> (a, b)
   const int lane = e & 63, r = (e >> 6) & 15, wt = e >> 10;
   const int w = wt / Cov<D>::TILES, t = wt % Cov<D>::TILES;
-  const int ac = D == 128 ? w : (w >> 1), bc = D == 128 ? t : (w & 1);
+  const int ac = Cov<D>::ac(w, t), bc = Cov<D>::bc(w, t);
   const int a = 32 * ac + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), b = 32 * bc + (lane & 31);
   mom[mi * D * D + a * D + b] = m;
   if (msplit) {
@@ -550,9 +696,11 @@ __global__ __launch_bounds__(256) void k_moments_finish(const float* __restrict_
 constexpr int kNormTok = 512;
 __global__ __launch_bounds__(256) void k_norms_bf16(ProblemArgs a, const uint16_t* __restrict__ msplit,
                                                     float* __restrict__ inv_n_out,
-                                                    float* __restrict__ ysum) {
+                                                    float* __restrict__ ysum,
+                                                    float* __restrict__ ymax) {
   constexpr int D = 128;
   __shared__ float red[4][32];
+  __shared__ float s_max[4];
   __shared__ float s_inv[32];
   __shared__ float s_half[D];
   const int chunk = blockIdx.x, p = blockIdx.y, nch = gridDim.x;
@@ -567,7 +715,7 @@ __global__ __launch_bounds__(256) void k_norms_bf16(ProblemArgs a, const uint16_
     for (int c = 0; c < 8; ++c)
       mreg[s][c] = lds_bf16x8(Ms + (size_t)s * D * D + (32 * w + l32) * D + 16 * c + 8 * g);
   const int d = tid & (D - 1), half = tid >> 7;
-  float ys = 0.f;
+  float ys = 0.f, ym = 0.f;
   const int t_end = min(a.N, (chunk + 1) * kNormTok);
   for (int c0 = chunk * kNormTok; c0 < t_end; c0 += 32) {
     const int tok = c0 + l32;
@@ -602,18 +750,31 @@ __global__ __launch_bounds__(256) void k_norms_bf16(ProblemArgs a, const uint16_
       inv_n_out[(size_t)p * a.N + c0 + tid] = inv;
     }
     __syncthreads();
-    for (int t = 16 * half; t < 16 * half + 16; ++t)
-      ys = fmaf(bf16_to_f32(X[(size_t)(c0 + t) * D + d]), s_inv[t], ys);
+    for (int t = 16 * half; t < 16 * half + 16; ++t) {
+      const float y = bf16_to_f32(X[(size_t)(c0 + t) * D + d]) * s_inv[t];
+      ys += y;
+      ym = fmaxf(ym, fabsf(y));
+    }
   }
   if (half == 1) s_half[d] = ys;
+  ym = fmaxf(ym, __shfl_xor(ym, 32, 64));
+  ym = fmaxf(ym, __shfl_xor(ym, 16, 64));
+  ym = fmaxf(ym, __shfl_xor(ym, 8, 64));
+  ym = fmaxf(ym, __shfl_xor(ym, 4, 64));
+  ym = fmaxf(ym, __shfl_xor(ym, 2, 64));
+  ym = fmaxf(ym, __shfl_xor(ym, 1, 64));
+  if (lane == 0) s_max[w] = ym;
   __syncthreads();
   if (half == 0) ysum[((size_t)p * nch + chunk) * D + d] = ys + s_half[d];
+  if (tid == 0)
+    ymax[(size_t)p * nch + chunk] = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
 }
 
 // fp32 path (D = 64): plain FMA, M in LDS; thread (s = tid/4, q = tid%4) -> token s, rows
 // [16q, 16q+16) of M x.  One workgroup per 64 tokens.
 __global__ __launch_bounds__(256) void k_norms_f32(ProblemArgs a, float* __restrict__ inv_n_out,
-                                                   float* __restrict__ ysum) {
+                                                   float* __restrict__ ysum,
+                                                   float* __restrict__ ymax) {
   constexpr int D = 64;
   __shared__ float sm[D][D + 1];
   __shared__ float sx[64][D + 1];
@@ -640,22 +801,39 @@ __global__ __launch_bounds__(256) void k_norms_f32(ProblemArgs a, float* __restr
     inv_n_out[(size_t)p * a.N + c0 + s] = inv;
   }
   __syncthreads();
+  float ym = 0.f;
   if (tid < D) {
     float acc = 0.f;
-    for (int t = 0; t < 64; ++t) acc = fmaf(sx[t][tid], s_inv[t], acc);
+    for (int t = 0; t < 64; ++t) {
+      acc = fmaf(sx[t][tid], s_inv[t], acc);
+      ym = fmaxf(ym, fabsf(sx[t][tid] * s_inv[t]));
+    }
     ysum[((size_t)p * nch + chunk) * D + tid] = acc;
   }
+  ym = wave_max(ym);
+  if (tid == 0) ymax[(size_t)p * nch + chunk] = ym;  // threads < D = 64 are wave 0
 }
 
 // mu_root[p] = (1/N) sum of the chunk sums
 template <int D>
-__global__ void k_root_mean(const float* __restrict__ ysum, int nch, int N,
-                            float* __restrict__ mu_root) {
+__global__ void k_root_mean(const float* __restrict__ ysum, const float* __restrict__ ymax,
+                            int nch, int N, float* __restrict__ mu_root,
+                            float* __restrict__ yscale) {
   const int p = blockIdx.x, d = threadIdx.x;
   if (d >= D) return;
   float s = 0.f;
   for (int c = 0; c < nch; ++c) s += ysum[((size_t)p * nch + c) * D + d];
   mu_root[(size_t)p * D + d] = s / float(N);
+  if (d == 0) {
+    // every centred value satisfies |y - shift| <= 2 max|y| <= 2^e; s = 2^(14 - e)
+    float m = 0.f;
+    for (int c = 0; c < nch; ++c) m = fmaxf(m, ymax[(size_t)p * nch + c]);
+    int e = 0;
+    frexpf(2.f * m, &e);
+    e = max(-100, min(100, e));
+    yscale[2 * p] = ldexpf(1.f, 14 - e);
+    yscale[2 * p + 1] = ldexpf(1.f, 2 * (e - 14));
+  }
 }
 
 // active-node lists: lists[l][0..count) = the nodes g of level l with m >= 2, ascending
@@ -678,7 +856,7 @@ __global__ __launch_bounds__(256) void k_group_lists(int nb, int G, int* __restr
 // grid (slices, G, P): partial statistics of one slice of one group
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_wide_stats(ProblemArgs a) {
-  __shared__ StageLds<D> st;
+  __shared__ StageLds<D, 2> st;
   __shared__ float shift[D];
   __shared__ float red[4 * D];
   __shared__ float dsum[D];
@@ -696,8 +874,8 @@ __global__ __launch_bounds__(256) void k_wide_stats(ProblemArgs a) {
   float dpart[D / 8];
 #pragma unroll
   for (int e = 0; e < D / 8; ++e) dpart[e] = 0.f;
-  for (int b = sb0; b < sb1; ++b)
-    stats_chunk<T, D, 3>(X, tokmap, inv_n, b * kBlk, shift, st, acc, dpart);
+  stats_range<T, D, kF16x2, true>(X, tokmap, inv_n, sb0, sb1, shift, a.yscale[2 * p], st, acc,
+                                  dpart);
   reduce_dpart<D>(dpart, red, dsum);
   float* slot = a.partial + ((size_t)p * kSlots + blockIdx.y * a.slices + s) * (D * D + D);
   store_acc<D>(slot, acc);
@@ -734,6 +912,11 @@ __global__ __launch_bounds__(256) void k_wide_dir(ProblemArgs a) {
       add_acc<D>(base + (size_t)s * (D * D + D), acc);
       if (threadIdx.x < D) ds += base[(size_t)s * (D * D + D) + D * D + threadIdx.x];
     }
+    const float inv_s2 = a.yscale[2 * p + 1];
+#pragma unroll
+    for (int t = 0; t < Cov<D>::TILES; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[t][r] *= inv_s2;
     if (child == 1) {
       // right child: n_P C_P - S_L, and the negated sum
       const float* cp = a.cov_prev + ((size_t)p * a.gw + blockIdx.x) * D * D;
@@ -751,7 +934,7 @@ __global__ __launch_bounds__(256) void k_wide_dir(ProblemArgs a) {
       L.shift[threadIdx.x] = parent_mean<D>(a, p, a.level, g)[threadIdx.x];
     }
     __syncthreads();
-    finish_stats<D>(acc, L, m * kBlk);
+    finish_stats<D>(acc, L, m * kBlk, 1.f);
     if (a.cov_cur) store_acc<D>(a.cov_cur + ((size_t)p * a.gw + g) * D * D, acc);
     power_direction<T, D>(acc, L, M, m * kBlk, X, pos, inv_n, b0 * kBlk);
     if (threadIdx.x < D) {
@@ -772,8 +955,8 @@ __global__ __launch_bounds__(256) void k_wide_proj(ProblemArgs a) {
   if (g < 0 || m < 2) return;
   if (threadIdx.x < D) w[threadIdx.x] = a.wdir[((size_t)p * a.G + g) * D + threadIdx.x];
   __syncthreads();
-  project_chunk<T, D>(problem_x<T, D>(a, p), problem_pos(a, p), a.inv_n + (size_t)p * a.N,
-                      blk * kBlk, w, a.keys + (size_t)p * a.N, problem_proj(a, p, a.level));
+  project_range<T, D, 1>(problem_x<T, D>(a, p), problem_pos(a, p), a.inv_n + (size_t)p * a.N,
+                         blk, blk + 1, w, a.keys + (size_t)p * a.N, problem_proj(a, p, a.level));
 }
 
 // grid (G, P), 1024 threads: split threshold and stable in-place partition of one group
@@ -799,7 +982,7 @@ __global__ __launch_bounds__(1024) void k_wide_split(ProblemArgs a) {
 // every split of levels [ls, le) inside it, one group at a time, in place.
 template <typename T, int D>
 __global__ __launch_bounds__(256, 2) void k_subtree(ProblemArgs a, int ls, int le) {
-  __shared__ StageLds<D> st;
+  __shared__ StageLds<D, 2> st;
   __shared__ DirLds L;
   __shared__ int hist[4 * 256];
   __shared__ int sm[16];
@@ -809,6 +992,7 @@ __global__ __launch_bounds__(256, 2) void k_subtree(ProblemArgs a, int ls, int l
   int32_t* tmp = a.tmp + (size_t)p * a.N;
   float* keys = a.keys + (size_t)p * a.N;
   const float* inv_n = a.inv_n + (size_t)p * a.N;
+  const float ysc = a.yscale[2 * p], inv_s2 = a.yscale[2 * p + 1];
   MRegs<D> M;
   M.load(problem_metric<D>(a, p));
   for (int level = ls; level < le; ++level) {
@@ -825,14 +1009,12 @@ __global__ __launch_bounds__(256, 2) void k_subtree(ProblemArgs a, int ls, int l
         float dpart[D / 8];
 #pragma unroll
         for (int e = 0; e < D / 8; ++e) dpart[e] = 0.f;
-        for (int b = b0; b < b0 + m; ++b)
-          stats_chunk<T, D, 3>(X, pos, inv_n, b * kBlk, L.shift, st, acc, dpart);
+        stats_range<T, D, kF16x2, true>(X, pos, inv_n, b0, b0 + m, L.shift, ysc, st, acc, dpart);
         reduce_dpart<D>(dpart, L.red, L.mu);
       }
-      group_direction<T, D>(acc, L, M, n, X, pos, inv_n, b0 * kBlk);
+      group_direction<T, D>(acc, L, M, n, inv_s2, X, pos, inv_n, b0 * kBlk);
       if (threadIdx.x < D) group_mean<D>(a, p, level, g)[threadIdx.x] = L.mu[threadIdx.x];
-      for (int b = b0; b < b0 + m; ++b)
-        project_chunk<T, D>(X, pos, inv_n, b * kBlk, L.w, keys, problem_proj(a, p, level));
+      project_range<T, D>(X, pos, inv_n, b0, b0 + m, L.w, keys, problem_proj(a, p, level));
       __syncthreads();
       const size_t off = (size_t)b0 * kBlk;
       const int want = (m >> 1) * kBlk;
@@ -850,7 +1032,7 @@ __global__ __launch_bounds__(256, 2) void k_subtree(ProblemArgs a, int ls, int l
 constexpr int kSmallBlocks = 8;
 template <typename T, int D>
 __global__ __launch_bounds__(256, 2) void k_subtree_small(ProblemArgs a, int ls) {
-  __shared__ StageLds<D> st;
+  __shared__ StageLds<D, 2> st;
   __shared__ DirLds L;
   __shared__ int32_t spos[kSmallBlocks * kBlk];
   __shared__ int32_t stmp[kSmallBlocks * kBlk];
@@ -863,6 +1045,7 @@ __global__ __launch_bounds__(256, 2) void k_subtree_small(ProblemArgs a, int ls)
   const T* X = problem_x<T, D>(a, p);
   int32_t* pos = problem_pos(a, p) + (size_t)rb0 * kBlk;
   const float* inv_n = a.inv_n + (size_t)p * a.N;
+  const float ysc = a.yscale[2 * p], inv_s2 = a.yscale[2 * p + 1];
   for (int i = threadIdx.x; i < rm * kBlk; i += 256) spos[i] = pos[i];
   MRegs<D> M;
   M.load(problem_metric<D>(a, p));
@@ -881,15 +1064,14 @@ __global__ __launch_bounds__(256, 2) void k_subtree_small(ProblemArgs a, int ls)
         float dpart[D / 8];
 #pragma unroll
         for (int e = 0; e < D / 8; ++e) dpart[e] = 0.f;
-        for (int b = lb0; b < lb0 + m; ++b)
-          stats_chunk<T, D, 3>(X, spos, inv_n, b * kBlk, L.shift, st, acc, dpart);
+        stats_range<T, D, kF16x2, true>(X, spos, inv_n, lb0, lb0 + m, L.shift, ysc, st, acc,
+                                         dpart);
         reduce_dpart<D>(dpart, L.red, L.mu);
       }
-      group_direction<T, D>(acc, L, M, n, X, spos, inv_n, lb0 * kBlk);
+      group_direction<T, D>(acc, L, M, n, inv_s2, X, spos, inv_n, lb0 * kBlk);
       if (threadIdx.x < D) group_mean<D>(a, p, level, g)[threadIdx.x] = L.mu[threadIdx.x];
       float* proj = problem_proj(a, p, level);
-      for (int b = lb0; b < lb0 + m; ++b)
-        project_chunk<T, D>(X, spos, inv_n, b * kBlk, L.w, skeys, proj);
+      project_range<T, D>(X, spos, inv_n, lb0, lb0 + m, L.w, skeys, proj);
       __syncthreads();
       const int want = (m >> 1) * kBlk;
       int take;
@@ -922,8 +1104,8 @@ __global__ void k_gather_keys(int N, int L, int level, const float* __restrict__
 }
 
 struct RebLayout {
-  size_t mom, mom_partial, msplit, inv_n, ysum, mu_root, tmp, keys, mu, wdir, partial, lists,
-      cov0, cov1, total;
+  size_t mom, mom_partial, msplit, inv_n, ysum, ymax, yscale, mu_root, tmp, keys, mu, wdir,
+      partial, lists, cov0, cov1, total;
   int L, G, nch_mom, nch_n, gw;
 };
 
@@ -943,6 +1125,8 @@ RebLayout reb_layout(int H, int N, int D) {
   r.msplit = take((size_t)H * 2 * 3 * D * D * 2);
   r.inv_n = take(P * N * 4);
   r.ysum = take(P * r.nch_n * D * 4);
+  r.ymax = take(P * r.nch_n * 4);
+  r.yscale = take(P * 2 * 4);
   r.mu_root = take(P * D * 4);
   r.tmp = take(P * N * 4);
   r.keys = take(P * N * 4);
@@ -992,6 +1176,7 @@ hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm
   a.keys = reinterpret_cast<float*>(w + R.keys);
   a.mu = reinterpret_cast<float*>(w + R.mu);
   a.mu_root = reinterpret_cast<float*>(w + R.mu_root);
+  a.yscale = reinterpret_cast<float*>(w + R.yscale);
   a.wdir = reinterpret_cast<float*>(w + R.wdir);
   a.partial = reinterpret_cast<float*>(w + R.partial);
   a.lists = reinterpret_cast<int*>(w + R.lists);
@@ -999,12 +1184,16 @@ hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm
   a.gw = R.gw;
   a.G = R.G;
   float* ysum = reinterpret_cast<float*>(w + R.ysum);
+  float* ymax = reinterpret_cast<float*>(w + R.ymax);
   if (sizeof(T) == 2)
     k_norms_bf16<<<dim3(R.nch_n, P), 256, 0, s>>>(a, msplit, reinterpret_cast<float*>(w + R.inv_n),
-                                                  ysum);
+                                                  ysum, ymax);
   else
-    k_norms_f32<<<dim3(R.nch_n, P), 256, 0, s>>>(a, reinterpret_cast<float*>(w + R.inv_n), ysum);
-  k_root_mean<D><<<P, 128, 0, s>>>(ysum, R.nch_n, N, reinterpret_cast<float*>(w + R.mu_root));
+    k_norms_f32<<<dim3(R.nch_n, P), 256, 0, s>>>(a, reinterpret_cast<float*>(w + R.inv_n), ysum,
+                                                 ymax);
+  k_root_mean<D><<<P, 128, 0, s>>>(ysum, ymax, R.nch_n, N,
+                                   reinterpret_cast<float*>(w + R.mu_root),
+                                   reinterpret_cast<float*>(w + R.yscale));
   if (proj_opt && R.L > 0) {
     const size_t n = (size_t)P * R.L * N;
     k_fill_zero<<<(unsigned)std::min<size_t>((n + 255) / 256, 4096), 256, 0, s>>>(n, proj_opt);
