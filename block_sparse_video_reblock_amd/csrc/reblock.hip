@@ -690,19 +690,24 @@ __global__ __launch_bounds__(256) void k_moments_finish(const float* __restrict_
 }
 
 // ---------------------------------------------------------------- metric norms (bf16)
-// inv_n[p][t] = 1 / sqrt(x_t^T M x_t) (0 if that is 0) and per-workgroup sums of y = x inv_n.
+// inv_n[p][t] = 1 / sqrt(x_t^T M x_t) (0 if that is 0), per-workgroup sums of y = x inv_n and
+// the per-workgroup max |y| (for the scale of the fp16 covariance split).
 // Y^T = M X^T by MFMA with M in three bf16 terms held in registers: wave w owns rows
-// [32w, 32w+32) of M; the workgroup walks kNormTok tokens in tiles of 32.
+// [32w, 32w+32) of M.  The workgroup walks kNormTok tokens in tiles of 64 staged once in LDS
+// (16-byte coalesced loads, the next tile's loads in flight while the current one is used).
 constexpr int kNormTok = 512;
+constexpr int kNormTile = 64;
+constexpr int kNormStride = 136;  // bf16 per LDS row: 4-bank skew between rows
 __global__ __launch_bounds__(256) void k_norms_bf16(ProblemArgs a, const uint16_t* __restrict__ msplit,
                                                     float* __restrict__ inv_n_out,
                                                     float* __restrict__ ysum,
                                                     float* __restrict__ ymax) {
   constexpr int D = 128;
-  __shared__ float red[4][32];
+  __shared__ __align__(16) uint16_t xs[kNormTile][kNormStride];
+  __shared__ float red[4][kNormTile];
+  __shared__ float s_inv[kNormTile];
+  __shared__ float s_ys[4][D];
   __shared__ float s_max[4];
-  __shared__ float s_inv[32];
-  __shared__ float s_half[D];
   const int chunk = blockIdx.x, p = blockIdx.y, nch = gridDim.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const uint16_t* X = problem_x<uint16_t, D>(a, p);
@@ -714,64 +719,84 @@ __global__ __launch_bounds__(256) void k_norms_bf16(ProblemArgs a, const uint16_
 #pragma unroll
     for (int c = 0; c < 8; ++c)
       mreg[s][c] = lds_bf16x8(Ms + (size_t)s * D * D + (32 * w + l32) * D + 16 * c + 8 * g);
-  const int d = tid & (D - 1), half = tid >> 7;
-  float ys = 0.f, ym = 0.f;
-  const int t_end = min(a.N, (chunk + 1) * kNormTok);
-  for (int c0 = chunk * kNormTok; c0 < t_end; c0 += 32) {
-    const int tok = c0 + l32;
-    const uint16_t* xr = X + (size_t)tok * D;
-    f32x16_t acc;
+  const int t0 = chunk * kNormTok, t_end = min(a.N, t0 + kNormTok);  // N is a multiple of 64
+  // tile loads: piece q = tid + 256 i (i < 4) is token q / 16, elements 8 (q % 16) .. + 8
+  uint4 nxt[4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  for (int i = 0; i < 4; ++i)
+    nxt[i] = *reinterpret_cast<const uint4*>(X + (size_t)t0 * D + (size_t)(tid + 256 * i) * 8);
+  const int d2 = lane;  // this thread's element pair (2 d2, 2 d2 + 1) for the sums of y
+  float ys0 = 0.f, ys1 = 0.f, ym = 0.f;
+  for (int c0 = t0; c0 < t_end; c0 += kNormTile) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const bf16x8_t xb = lds_bf16x8(xr + 16 * c + 8 * g);
-#pragma unroll
-      for (int s = 0; s < 3; ++s)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mreg[s][c], xb, acc, 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const int q = tid + 256 * i;
+      *reinterpret_cast<uint4*>(&xs[q >> 4][8 * (q & 15)]) = nxt[i];
     }
-    // lane holds (M x_tok)[b] for b = 32w + 8j + 4g + i
-    float part = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint2 u = *reinterpret_cast<const uint2*>(xr + 32 * w + 8 * j + 4 * g);
-      part = fmaf(acc[4 * j + 0], __uint_as_float(u.x << 16), part);
-      part = fmaf(acc[4 * j + 1], __uint_as_float(u.x & 0xFFFF0000u), part);
-      part = fmaf(acc[4 * j + 2], __uint_as_float(u.y << 16), part);
-      part = fmaf(acc[4 * j + 3], __uint_as_float(u.y & 0xFFFF0000u), part);
-    }
-    part += __shfl_xor(part, 32, 64);
-    if (g == 0) red[w][l32] = part;
     __syncthreads();
-    if (tid < 32) {
+    if (c0 + kNormTile < t_end) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        nxt[i] = *reinterpret_cast<const uint4*>(X + (size_t)(c0 + kNormTile) * D +
+                                                 (size_t)(tid + 256 * i) * 8);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int tok = 32 * h + l32;
+      f32x16_t acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const bf16x8_t xb = lds_bf16x8(&xs[tok][16 * c + 8 * g]);
+#pragma unroll
+        for (int s = 0; s < 3; ++s)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mreg[s][c], xb, acc, 0, 0, 0);
+      }
+      // lane holds (M x_tok)[b] for b = 32w + 8j + 4g + i
+      float part = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint2 u = *reinterpret_cast<const uint2*>(&xs[tok][32 * w + 8 * j + 4 * g]);
+        part = fmaf(acc[4 * j + 0], __uint_as_float(u.x << 16), part);
+        part = fmaf(acc[4 * j + 1], __uint_as_float(u.x & 0xFFFF0000u), part);
+        part = fmaf(acc[4 * j + 2], __uint_as_float(u.y << 16), part);
+        part = fmaf(acc[4 * j + 3], __uint_as_float(u.y & 0xFFFF0000u), part);
+      }
+      part += __shfl_xor(part, 32, 64);
+      if (g == 0) red[w][tok] = part;
+    }
+    __syncthreads();
+    if (tid < kNormTile) {
       const float n2 = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
       const float inv = n2 > 0.f ? 1.f / sqrtf(n2) : 0.f;
       s_inv[tid] = inv;
       inv_n_out[(size_t)p * a.N + c0 + tid] = inv;
     }
     __syncthreads();
-    for (int t = 16 * half; t < 16 * half + 16; ++t) {
-      const float y = bf16_to_f32(X[(size_t)(c0 + t) * D + d]) * s_inv[t];
-      ys += y;
-      ym = fmaxf(ym, fabsf(y));
+    // wave w sums tokens [16w, 16w + 16) of the tile for elements 2 d2, 2 d2 + 1
+#pragma unroll 4
+    for (int t = 16 * w; t < 16 * w + 16; ++t) {
+      const uint32_t u = *reinterpret_cast<const uint32_t*>(&xs[t][2 * d2]);
+      const float sc = s_inv[t];
+      const float y0 = __uint_as_float(u << 16) * sc, y1 = __uint_as_float(u & 0xFFFF0000u) * sc;
+      ys0 += y0;
+      ys1 += y1;
+      ym = fmaxf(ym, fmaxf(fabsf(y0), fabsf(y1)));
     }
+    __syncthreads();
   }
-  if (half == 1) s_half[d] = ys;
-  ym = fmaxf(ym, __shfl_xor(ym, 32, 64));
-  ym = fmaxf(ym, __shfl_xor(ym, 16, 64));
-  ym = fmaxf(ym, __shfl_xor(ym, 8, 64));
-  ym = fmaxf(ym, __shfl_xor(ym, 4, 64));
-  ym = fmaxf(ym, __shfl_xor(ym, 2, 64));
-  ym = fmaxf(ym, __shfl_xor(ym, 1, 64));
+  s_ys[w][2 * d2] = ys0;
+  s_ys[w][2 * d2 + 1] = ys1;
+  ym = wave_max(ym);
   if (lane == 0) s_max[w] = ym;
   __syncthreads();
-  if (half == 0) ysum[((size_t)p * nch + chunk) * D + d] = ys + s_half[d];
+  if (tid < D)
+    ysum[((size_t)p * nch + chunk) * D + tid] = (s_ys[0][tid] + s_ys[1][tid]) +
+                                                (s_ys[2][tid] + s_ys[3][tid]);
   if (tid == 0)
     ymax[(size_t)p * nch + chunk] = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
 }
-
-// fp32 path (D = 64): plain FMA, M in LDS; thread (s = tid/4, q = tid%4) -> token s, rows
-// [16q, 16q+16) of M x.  One workgroup per 64 tokens.
 __global__ __launch_bounds__(256) void k_norms_f32(ProblemArgs a, float* __restrict__ inv_n_out,
                                                    float* __restrict__ ysum,
                                                    float* __restrict__ ymax) {
@@ -816,20 +841,33 @@ __global__ __launch_bounds__(256) void k_norms_f32(ProblemArgs a, float* __restr
 
 // mu_root[p] = (1/N) sum of the chunk sums
 template <int D>
-__global__ void k_root_mean(const float* __restrict__ ysum, const float* __restrict__ ymax,
-                            int nch, int N, float* __restrict__ mu_root,
-                            float* __restrict__ yscale) {
-  const int p = blockIdx.x, d = threadIdx.x;
-  if (d >= D) return;
+__global__ __launch_bounds__(256) void k_root_mean(const float* __restrict__ ysum,
+                                                   const float* __restrict__ ymax, int nch, int N,
+                                                   float* __restrict__ mu_root,
+                                                   float* __restrict__ yscale) {
+  constexpr int R = 256 / D;  // chunk strides per element
+  __shared__ float part[R][D];
+  __shared__ float s_max[4];
+  const int p = blockIdx.x, d = threadIdx.x % D, r = threadIdx.x / D;
   float s = 0.f;
-  for (int c = 0; c < nch; ++c) s += ysum[((size_t)p * nch + c) * D + d];
-  mu_root[(size_t)p * D + d] = s / float(N);
-  if (d == 0) {
+  for (int c = r; c < nch; c += R) s += ysum[((size_t)p * nch + c) * D + d];
+  part[r][d] = s;
+  float m = 0.f;
+  for (int c = threadIdx.x; c < nch; c += 256) m = fmaxf(m, ymax[(size_t)p * nch + c]);
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) s_max[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < R; ++i) t += part[i][threadIdx.x];
+    mu_root[(size_t)p * D + threadIdx.x] = t / float(N);
+  }
+  if (threadIdx.x == 0) {
     // every centred value satisfies |y - shift| <= 2 max|y| <= 2^e; s = 2^(14 - e)
-    float m = 0.f;
-    for (int c = 0; c < nch; ++c) m = fmaxf(m, ymax[(size_t)p * nch + c]);
+    const float mx = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
     int e = 0;
-    frexpf(2.f * m, &e);
+    frexpf(2.f * mx, &e);
     e = max(-100, min(100, e));
     yscale[2 * p] = ldexpf(1.f, 14 - e);
     yscale[2 * p + 1] = ldexpf(1.f, 2 * (e - 14));
@@ -1191,7 +1229,7 @@ hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm
   else
     k_norms_f32<<<dim3(R.nch_n, P), 256, 0, s>>>(a, reinterpret_cast<float*>(w + R.inv_n), ysum,
                                                  ymax);
-  k_root_mean<D><<<P, 128, 0, s>>>(ysum, ymax, R.nch_n, N,
+  k_root_mean<D><<<P, 256, 0, s>>>(ysum, ymax, R.nch_n, N,
                                    reinterpret_cast<float*>(w + R.mu_root),
                                    reinterpret_cast<float*>(w + R.yscale));
   if (proj_opt && R.L > 0) {
