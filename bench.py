@@ -6,6 +6,7 @@ HBM: reblock (both layouts of every head), block scoring + top-K, summaries, and
 attention with merge and inverse permutation.  Timed with HIP events on the stream the library
 launches on.  Prints one JSON line (the last line of stdout).
 
+Default (the headline): 24 heads x 72,576 tokens x 128, bf16, 10 % density.
   value      dense-equivalent effective TFLOP/s = 4 N^2 D H / layer time
   roofline   the attention kernel (the dominant one): algorithmic flops of the exact and
              compressed branches per launch / its mean launch time, against the bf16 MFMA peak
@@ -13,12 +14,19 @@ launches on.  Prints one JSON line (the last line of stdout).
              softmax attention), timed on the same GPU
   cpu_baseline  the CPU oracle (fp64 numpy) on one head of the same workload, extrapolated to
              all heads
+Other modes (each prints its own JSON line):
+  --workload clip14s_bf16   four independently generated 103,680-token layers back to back,
+                            reblock recomputed per layer; value per layer
+  --sweep                   the 16,384-token shape at densities 0.1 / 0.2 / 0.3 / 1.0, with
+                            Reblock layouts and with the fixed-tile baseline (positional 4x4x4
+                            cubes, mean-pooled summaries); layer time and attention-mass recall
+                            against dense softmax, both measured on the GPU
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
-import math
 import os
 import sys
 import time
@@ -58,12 +66,330 @@ def cpu_baseline(wl, q, k, v):
     return time.perf_counter() - t0, threads
 
 
+class Layer:
+    """Device buffers and the four stage calls of one layer (Reblock or fixed-tile layouts)."""
+
+    def __init__(self, ops, torch, wl, q, k, v, topk, fixed_tiles=False, ws=None):
+        self.ops, self.torch = ops, torch
+        dev = torch.device("cuda:0")
+        dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+        self.wl = wl
+        self.H, self.N = wl.heads, wl.tokens
+        self.nb = self.N // 64
+        self.topk = topk
+        self.qd, self.kd, self.vd = (torch.from_numpy(x).to(dev).to(dt) for x in (q, k, v))
+        self.d = ops.desc_for(self.qd)
+        self.ws = ops.workspace(self.d, dev) if ws is None else ws
+        self.perm_q = torch.empty(self.H, self.N, dtype=torch.int32, device=dev)
+        self.perm_k = torch.empty_like(self.perm_q)
+        self.lists = torch.empty(self.H, self.nb, topk, dtype=torch.int32, device=dev)
+        self.out = torch.empty_like(self.qd)
+        self.fixed = fixed_tiles
+        self.flags = ops.BSA_MEANPOOL if fixed_tiles else 0
+        self.L = ops.lib()
+        self.stream = ops._stream()
+
+    @staticmethod
+    def p(t):
+        return ctypes.c_void_p(t.data_ptr())
+
+    def layout(self):
+        p, ops = self.p, self.ops
+        if self.fixed:
+            T, Hh, W = self.wl.grid
+            ops.check(self.L.bsa_tile_layout(self.H, T, Hh, W, 4, 4, 4, p(self.perm_q),
+                                             self.stream))
+            ops.check(self.L.bsa_tile_layout(self.H, T, Hh, W, 4, 4, 4, p(self.perm_k),
+                                             self.stream))
+        else:
+            ops.check(self.L.bsa_reblock(ctypes.byref(self.d), p(self.qd), p(self.kd),
+                                         p(self.perm_q), p(self.perm_k), None, p(self.ws),
+                                         self.ws.numel(), self.stream))
+
+    def select(self):
+        p = self.p
+        self.ops.check(self.L.bsa_select(ctypes.byref(self.d), p(self.qd), p(self.kd),
+                                         p(self.perm_q), p(self.perm_k), 0.0, self.topk,
+                                         p(self.lists), None, p(self.ws), self.ws.numel(),
+                                         self.stream))
+
+    def prepare(self, pk=None, flags=None):
+        p = self.p
+        self.ops.check(self.L.bsa_prepare_kv(ctypes.byref(self.d), p(self.qd), p(self.kd),
+                                             p(self.vd), p(self.perm_k if pk is None else pk),
+                                             self.flags if flags is None else flags, 0.0,
+                                             p(self.ws), self.ws.numel(), self.stream))
+
+    def attend(self, pq=None, pk=None, ls=None, flags=None, lse=None):
+        p = self.p
+        ls = self.lists if ls is None else ls
+        self.ops.check(self.L.bsa_attend(ctypes.byref(self.d), p(self.qd), p(self.kd),
+                                         p(self.vd), p(self.perm_q if pq is None else pq),
+                                         p(self.perm_k if pk is None else pk), p(ls),
+                                         int(ls.shape[-1]), self.flags if flags is None else flags,
+                                         0.0, p(self.out), None if lse is None else p(lse),
+                                         p(self.ws), self.ws.numel(), self.stream))
+
+    def stages(self):
+        return (("layout" if self.fixed else "reblock", self.layout), ("select", self.select),
+                ("prepare", self.prepare), ("attend", self.attend))
+
+    def dense_inputs(self):
+        torch, dev = self.torch, self.qd.device
+        ident = torch.arange(self.N, dtype=torch.int32, device=dev).repeat(self.H, 1).contiguous()
+        every = torch.arange(self.nb, dtype=torch.int32,
+                             device=dev).repeat(self.H, self.nb, 1).contiguous()
+        return ident, every
+
+    def recall(self, lse_dense):
+        """Mean over heads and queries of exp(lse over the selected blocks - dense lse): the
+        dense softmax mass that the selected blocks capture."""
+        torch = self.torch
+        lse = torch.empty(self.H, self.N, dtype=torch.float32, device=self.qd.device)
+        self.prepare()
+        self.attend(flags=self.ops.BSA_EXACT_ONLY | (self.flags & self.ops.BSA_MEANPOOL), lse=lse)
+        return float(torch.exp(lse - lse_dense).mean().item())
+
+    def dense_lse(self):
+        torch = self.torch
+        ident, every = self.dense_inputs()
+        lse = torch.empty(self.H, self.N, dtype=torch.float32, device=self.qd.device)
+        self.prepare(pk=ident, flags=self.ops.BSA_EXACT_ONLY)
+        self.attend(pq=ident, pk=ident, ls=every, flags=self.ops.BSA_EXACT_ONLY, lse=lse)
+        return lse
+
+
+def time_steps(torch, fns_per_step, steps, warmup):
+    """Time `steps` steps, each the list of (name, fn) calls; returns (ms per step, {name: mean
+    ms}, {name: [ms per step]})."""
+    import numpy as np
+    for _ in range(warmup):
+        for _, f in fns_per_step:
+            f()
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    n = len(fns_per_step)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(cur)
+    for s in range(steps):
+        ev[s][0].record(cur)
+        for i, (_, f) in enumerate(fns_per_step):
+            f()
+            ev[s][i + 1].record(cur)
+    stop.record(cur)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / steps
+    per = {}
+    for i, (name, _) in enumerate(fns_per_step):
+        per.setdefault(name, []).append([ev[s][i].elapsed_time(ev[s][i + 1])
+                                         for s in range(steps)])
+    means = {k: float(np.mean(np.sum(v, axis=0))) for k, v in per.items()}
+    series = {k: list(np.sum(v, axis=0)) for k, v in per.items()}
+    return ms_step, means, series
+
+
+def main_headline(args, ops, synth, torch, np):
+    wl = synth.WORKLOADS[args.workload]
+    H, N, D = wl.heads, wl.tokens, wl.head_dim
+    nb = N // 64
+    topk = ops.topk_count(nb, wl.topk_ratio)
+    log(f"[bench] workload {wl.name}: H={H} N={N} D={D} nb={nb} topk={topk} dtype={wl.dtype}")
+    t0 = time.perf_counter()
+    q, k, v = synth.make_qkv(wl)
+    log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
+    lay = Layer(ops, torch, wl, q, k, v, topk)
+    ms_step, stage_ms, series = time_steps(torch, lay.stages(), args.steps, args.warmup)
+    assert torch.isfinite(lay.out.float()).all().item(), "non-finite output"
+    log(f"[bench] layer {ms_step:.3f} ms/step; stages " +
+        ", ".join(f"{k} {v:.3f}" for k, v in stage_ms.items()))
+
+    exact_f, comp_f = attention_flops(H, N, D, topk)
+    attn_ms = stage_ms["attend"]
+    achieved = (exact_f + comp_f) / (attn_ms * 1e-3) / 1e12
+    dense_flops = 4.0 * N * N * D * H
+    eff = dense_flops / (ms_step * 1e-3) / 1e12
+
+    # HBM-bound stages: algorithmic bytes (inputs read once per pass the algorithm needs)
+    elt = 2 if wl.dtype == "bf16" else 4
+    x_bytes = H * N * D * elt
+    levels = max(0, (nb - 1).bit_length())
+    hbm = {
+        "reblock": {"bytes": (2 + 2 * levels) * 2 * x_bytes,
+                    "passes": "moments, norms, and per tree level a statistics and a "
+                              "projection pass over Q and K"},
+        "select": {"bytes": 2 * x_bytes + H * nb * nb * 4, "passes": "Q, K once; scores"},
+        "prepare": {"bytes": 3 * x_bytes, "passes": "Q (anchor), K, V once"},
+    }
+    for name, h in hbm.items():
+        gbs = h["bytes"] / (stage_ms[name] * 1e-3) / 1e9
+        h.update({"ms": stage_ms[name], "GB/s": gbs, "frac": gbs / HBM_PEAK_GBS})
+
+    dense = None
+    if not args.no_dense:
+        ident, every = lay.dense_inputs()
+        lay.prepare(pk=ident, flags=ops.BSA_EXACT_ONLY)
+        cur = torch.cuda.current_stream()
+        times = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(cur)
+            lay.attend(pq=ident, pk=ident, ls=every, flags=ops.BSA_EXACT_ONLY)
+            e1.record(cur)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        dense_ms = float(min(times[1:]))
+        dense = {"ms": dense_ms, "tflops": dense_flops / (dense_ms * 1e-3) / 1e12,
+                 "speedup_of_sparse_layer": dense_ms / ms_step,
+                 "kernel": "same attention kernel, every block selected, identity layouts"}
+        log(f"[bench] dense attention {dense_ms:.2f} ms ({dense['tflops']:.0f} TFLOP/s); "
+            f"sparse layer speed-up {dense_ms / ms_step:.2f}x")
+        del every
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on head 0 ...")
+        t_head, threads = cpu_baseline(wl, q, k, v)
+        layer_s = t_head * H
+        cpu = {"value": dense_flops / layer_s / 1e12, "unit": "TFLOP/s", "cores": threads,
+               "kind": "oracle", "ms_per_layer": layer_s * 1e3,
+               "sample": f"fp64 numpy oracle, full layer (reblock both sides, scores, top-K, "
+                         f"summaries, exact + compressed attention) on head 0 of {H}: "
+                         f"{t_head:.1f} s, extrapolated x{H}"}
+        log(f"[bench] oracle head 0: {t_head:.1f} s -> {layer_s * 1e3:.0f} ms per layer")
+
+    return {
+        "metric": METRIC,
+        "value": eff,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "heads": H, "tokens": N, "head_dim": D,
+                   "topk_ratio": wl.topk_ratio, "topk_blocks": topk, "grid": list(wl.grid),
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": None, "kernel": "k_attn_bf16", "launch_ms": attn_ms,
+                     "launch_ms_min": float(min(series["attend"])),
+                     "flops_per_launch": exact_f + comp_f},
+        "stages_ms": stage_ms,
+        "hbm": hbm,
+        "dense": dense,
+        "cpu_baseline": cpu,
+    }
+
+
+def main_layers(args, ops, synth, torch, np):
+    """Several independently generated layers back to back (the long-clip workload)."""
+    wl = synth.WORKLOADS[args.workload]
+    H, N, D = wl.heads, wl.tokens, wl.head_dim
+    nb = N // 64
+    topk = ops.topk_count(nb, wl.topk_ratio)
+    log(f"[bench] workload {wl.name}: {wl.layers} layers, H={H} N={N} D={D} nb={nb} "
+        f"topk={topk}")
+    layers = []
+    ws = None
+    for layer in range(wl.layers):
+        t0 = time.perf_counter()
+        q, k, v = synth.make_qkv(wl, layer=layer)
+        lay = Layer(ops, torch, wl, q, k, v, topk, ws=ws)
+        ws = lay.ws  # layers run one after another: one workspace serves them all
+        layers.append(lay)
+        log(f"[bench] layer {layer} inputs generated in {time.perf_counter() - t0:.1f} s")
+    fns = [(f"L{i}.{name}", f) for i, lay in enumerate(layers) for name, f in lay.stages()]
+    ms_step, stage_ms, _ = time_steps(torch, fns, args.steps, args.warmup)
+    for lay in layers:
+        assert torch.isfinite(lay.out.float()).all().item(), "non-finite output"
+    per_layer = ms_step / wl.layers
+    by_stage = {s: float(np.mean([stage_ms[f"L{i}.{s}"] for i in range(wl.layers)]))
+                for s in ("reblock", "select", "prepare", "attend")}
+    exact_f, comp_f = attention_flops(H, N, D, topk)
+    dense_flops = 4.0 * N * N * D * H
+    log(f"[bench] {wl.layers} layers {ms_step:.3f} ms/step, {per_layer:.3f} ms per layer; "
+        "per-layer stages " + ", ".join(f"{k} {v:.3f}" for k, v in by_stage.items()))
+    achieved = (exact_f + comp_f) / (by_stage["attend"] * 1e-3) / 1e12
+    return {
+        "metric": f"sparse attn layer ms + effective TFLOP/s at {N:,} tok, "
+                  f"{int(round(100 * wl.topk_ratio))}% density, {wl.layers} layers back to back",
+        "value": dense_flops / (per_layer * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step, "ms_per_layer": per_layer,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "layers": wl.layers, "heads": H, "tokens": N,
+                   "head_dim": D, "topk_ratio": wl.topk_ratio, "topk_blocks": topk,
+                   "grid": list(wl.grid), "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": None, "kernel": "k_attn_bf16", "launch_ms": by_stage["attend"],
+                     "flops_per_launch": exact_f + comp_f},
+        "stages_ms_per_layer": by_stage,
+    }
+
+
+def main_sweep(args, ops, synth, torch, np):
+    """Density sweep with Reblock layouts and with the fixed-tile baseline."""
+    wl = synth.WORKLOADS["mid_bf16"]
+    H, N, D = wl.heads, wl.tokens, wl.head_dim
+    nb = N // 64
+    q, k, v = synth.make_qkv(wl)
+    log(f"[bench] sweep on {wl.name}: H={H} N={N} D={D} nb={nb}")
+    base = Layer(ops, torch, wl, q, k, v, nb)
+    lse_dense = base.dense_lse()
+    ident, every = base.dense_inputs()
+    base.prepare(pk=ident, flags=ops.BSA_EXACT_ONLY)
+    dense_ms, _, _ = time_steps(
+        torch, [("dense", lambda: base.attend(pq=ident, pk=ident, ls=every,
+                                              flags=ops.BSA_EXACT_ONLY))], 3, 1)
+    rows = []
+    for ratio in synth.SWEEP_RATIOS:
+        topk = ops.topk_count(nb, ratio)
+        for fixed in (False, True):
+            lay = Layer(ops, torch, wl, q, k, v, topk, fixed_tiles=fixed, ws=base.ws)
+            ms_step, stage_ms, _ = time_steps(torch, lay.stages(), args.steps, args.warmup)
+            rec = lay.recall(lse_dense)
+            row = {"topk_ratio": ratio, "topk_blocks": topk,
+                   "layout": "fixed 4x4x4 tiles, mean-pooled summaries" if fixed else
+                             "reblock, reweighted summaries",
+                   "layer_ms": ms_step, "stages_ms": stage_ms, "recall": rec,
+                   "speedup_vs_dense_attention": dense_ms / ms_step}
+            rows.append(row)
+            log(f"[bench] ratio {ratio:.1f} {'fixed  ' if fixed else 'reblock'}: layer "
+                f"{ms_step:.3f} ms, recall {rec:.4f}")
+            del lay
+    return {
+        "metric": "density sweep at 16,384 tok: layer ms and attention-mass recall vs dense "
+                  "softmax, reblock vs fixed tiles",
+        "value": rows[0]["recall"], "unit": "recall at 10% density (reblock)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": wl.dtype, "data": "synthetic",
+        "config": {"workload": wl.name, "heads": H, "tokens": N, "head_dim": D,
+                   "grid": list(wl.grid), "ratios": list(synth.SWEEP_RATIOS),
+                   "parallelism": "single GPU"},
+        "dense_attention_ms": dense_ms,
+        "sweep": rows,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="clip10s_bf16")
+    ap.add_argument("--sweep", action="store_true",
+                    help="density sweep with Reblock and fixed-tile layouts on 16,384 tokens")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -92,160 +418,12 @@ def main():
     from block_sparse_video_reblock_amd import _lib as ops
     from block_sparse_video_reblock_amd import synth
 
-    wl = synth.WORKLOADS[args.workload]
-    H, N, D = wl.heads, wl.tokens, wl.head_dim
-    nb = N // 64
-    topk = ops.topk_count(nb, wl.topk_ratio)
-    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-    log(f"[bench] workload {wl.name}: H={H} N={N} D={D} nb={nb} topk={topk} dtype={wl.dtype}")
-
-    t0 = time.perf_counter()
-    q, k, v = synth.make_qkv(wl)
-    log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
-    dev = torch.device("cuda:0")
-    qd, kd, vd = (torch.from_numpy(x).to(dev).to(dt) for x in (q, k, v))
-    d = ops.desc_for(qd)
-    ws = ops.workspace(d, dev)
-    perm_q = torch.empty(H, N, dtype=torch.int32, device=dev)
-    perm_k = torch.empty_like(perm_q)
-    lists = torch.empty(H, nb, topk, dtype=torch.int32, device=dev)
-    out = torch.empty_like(qd)
-    L = ops.lib()
-    stream = ops._stream()
-    import ctypes
-
-    def p(t):
-        return ctypes.c_void_p(t.data_ptr())
-
-    def reblock():
-        ops.check(L.bsa_reblock(ctypes.byref(d), p(qd), p(kd), p(perm_q), p(perm_k), None, p(ws),
-                                ws.numel(), stream))
-
-    def select():
-        ops.check(L.bsa_select(ctypes.byref(d), p(qd), p(kd), p(perm_q), p(perm_k),
-                               float(wl.topk_ratio), 0, p(lists), None, p(ws), ws.numel(),
-                               stream))
-
-    def prepare(pk=None, flags=0):
-        ops.check(L.bsa_prepare_kv(ctypes.byref(d), p(qd), p(kd), p(vd),
-                                   p(perm_k if pk is None else pk), flags, 0.0, p(ws), ws.numel(),
-                                   stream))
-
-    def attend(pq=None, pk=None, ls=None, flags=0):
-        ls = lists if ls is None else ls
-        ops.check(L.bsa_attend(ctypes.byref(d), p(qd), p(kd), p(vd),
-                               p(perm_q if pq is None else pq), p(perm_k if pk is None else pk),
-                               p(ls), int(ls.shape[-1]), flags, 0.0, p(out), None, p(ws),
-                               ws.numel(), stream))
-
-    stages = ("reblock", "select", "prepare", "attend")
-    fns = (reblock, select, prepare, attend)
-    for _ in range(args.warmup):
-        for f in fns:
-            f()
-    torch.cuda.synchronize()
-    cur = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(cur)
-    for s in range(args.steps):
-        ev[s][0].record(cur)
-        for i, f in enumerate(fns):
-            f()
-            ev[s][i + 1].record(cur)
-    stop.record(cur)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    ms_step = total_ms / args.steps
-    stage_ms = {name: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1])
-                                     for s in range(args.steps)]))
-                for i, name in enumerate(stages)}
-    attn_ms_all = [ev[s][3].elapsed_time(ev[s][4]) for s in range(args.steps)]
-    assert torch.isfinite(out.float()).all().item(), "non-finite output"
-    log(f"[bench] layer {ms_step:.3f} ms/step; stages " +
-        ", ".join(f"{k} {v:.3f}" for k, v in stage_ms.items()))
-
-    exact_f, comp_f = attention_flops(H, N, D, topk)
-    attn_ms = float(np.mean(attn_ms_all))
-    achieved = (exact_f + comp_f) / (attn_ms * 1e-3) / 1e12
-    dense_flops = 4.0 * N * N * D * H
-    eff = dense_flops / (ms_step * 1e-3) / 1e12
-
-    # HBM-bound stages: algorithmic bytes (inputs read once per pass the algorithm needs)
-    elt = 2 if wl.dtype == "bf16" else 4
-    x_bytes = H * N * D * elt
-    levels = max(0, (nb - 1).bit_length())
-    hbm = {
-        "reblock": {"bytes": (2 + 2 * levels) * 2 * x_bytes,
-                    "passes": "moments, norms, and per tree level a statistics and a "
-                              "projection pass over Q and K"},
-        "select": {"bytes": 2 * x_bytes + H * nb * nb * 4, "passes": "Q, K once; scores"},
-        "prepare": {"bytes": 3 * x_bytes, "passes": "Q (anchor), K, V once"},
-    }
-    for name, h in hbm.items():
-        gbs = h["bytes"] / (stage_ms[name] * 1e-3) / 1e9
-        h.update({"ms": stage_ms[name], "GB/s": gbs, "frac": gbs / HBM_PEAK_GBS})
-
-    dense = None
-    if not args.no_dense:
-        ident = torch.arange(N, dtype=torch.int32, device=dev).repeat(H, 1).contiguous()
-        all_lists = torch.arange(nb, dtype=torch.int32, device=dev).repeat(H, nb, 1).contiguous()
-        prepare(pk=ident)
-        times = []
-        for _ in range(3):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(cur)
-            attend(pq=ident, pk=ident, ls=all_lists, flags=ops.BSA_EXACT_ONLY)
-            e1.record(cur)
-            torch.cuda.synchronize()
-            times.append(e0.elapsed_time(e1))
-        dense_ms = float(min(times[1:]))
-        dense = {"ms": dense_ms, "tflops": dense_flops / (dense_ms * 1e-3) / 1e12,
-                 "speedup_of_sparse_layer": dense_ms / ms_step,
-                 "kernel": "same attention kernel, every block selected, identity layouts"}
-        log(f"[bench] dense attention {dense_ms:.2f} ms ({dense['tflops']:.0f} TFLOP/s); "
-            f"sparse layer speed-up {dense_ms / ms_step:.2f}x")
-        del all_lists
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on head 0 ...")
-        t_head, threads = cpu_baseline(wl, q, k, v)
-        layer_s = t_head * H
-        cpu = {"value": dense_flops / layer_s / 1e12, "unit": "TFLOP/s", "cores": threads,
-               "kind": "oracle", "ms_per_layer": layer_s * 1e3,
-               "sample": f"fp64 numpy oracle, full layer (reblock both sides, scores, top-K, "
-                         f"summaries, exact + compressed attention) on head 0 of {H}: "
-                         f"{t_head:.1f} s, extrapolated x{H}"}
-        log(f"[bench] oracle head 0: {t_head:.1f} s -> {layer_s * 1e3:.0f} ms per layer")
-
-    res = {
-        "metric": METRIC,
-        "value": eff,
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": wl.dtype,
-        "data": "synthetic",
-        "config": {"workload": wl.name, "heads": H, "tokens": N, "head_dim": D,
-                   "topk_ratio": wl.topk_ratio, "topk_blocks": topk, "grid": list(wl.grid),
-                   "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": None, "kernel": "k_attn_bf16", "launch_ms": attn_ms,
-                     "flops_per_launch": exact_f + comp_f},
-        "stages_ms": stage_ms,
-        "hbm": hbm,
-        "dense": dense,
-        "cpu_baseline": cpu,
-    }
+    if args.sweep:
+        res = main_sweep(args, ops, synth, torch, np)
+    elif synth.WORKLOADS[args.workload].layers > 1:
+        res = main_layers(args, ops, synth, torch, np)
+    else:
+        res = main_headline(args, ops, synth, torch, np)
     print(json.dumps(res), flush=True)
 
 

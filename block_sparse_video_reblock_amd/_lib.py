@@ -51,6 +51,7 @@ _SIGS = {
     "bsa_partition_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int32]),
     "bsa_reblock_from_projections": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
                                                       ctypes.c_size_t, _P]),
+    "bsa_tile_layout": (ctypes.c_int32, [ctypes.c_int32] * 7 + [_P, _P]),
     "bsa_topk_from_scores": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P,
                                               _P, _P]),
 }
@@ -241,3 +242,12 @@ def topk_from_scores(scores, topk):
     check(lib().bsa_topk_from_scores(rows, nb, topk, _dev_ptr(scores, torch.float32),
                                      _dev_ptr(lists), _stream()))
     return lists
+
+
+def tile_layout(heads, grid, tile=(4, 4, 4), device="cuda"):
+    """Fixed-tile layout int32 [heads][T H W] (the positional baseline)."""
+    torch = _torch()
+    T, H, W = grid
+    perm = torch.empty(heads, T * H * W, dtype=torch.int32, device=device)
+    check(lib().bsa_tile_layout(heads, T, H, W, *tile, _dev_ptr(perm), _stream()))
+    return perm

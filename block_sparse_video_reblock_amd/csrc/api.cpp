@@ -431,4 +431,27 @@ bsa_status bsa_topk_from_scores(int32_t rows, int32_t n_blocks, int32_t topk,
                     "top-K launch");
 }
 
+bsa_status bsa_tile_layout(int32_t heads, int32_t grid_t, int32_t grid_h, int32_t grid_w,
+                           int32_t tile_t, int32_t tile_h, int32_t tile_w, int32_t* perm,
+                           hipStream_t stream) {
+  if (heads < 1) return fail(BSA_E_ARG, "heads must be >= 1");
+  if (grid_t < 1 || grid_h < 1 || grid_w < 1 || tile_t < 1 || tile_h < 1 || tile_w < 1)
+    return fail(BSA_E_ARG, "grid and tile sides must be >= 1");
+  if ((int64_t)tile_t * tile_h * tile_w != BSA_BLOCK)
+    return fail(BSA_E_ARG, "tile %dx%dx%d does not hold %d tokens", tile_t, tile_h, tile_w,
+                BSA_BLOCK);
+  if (grid_t % tile_t || grid_h % tile_h || grid_w % tile_w)
+    return fail(BSA_E_ARG, "tile %dx%dx%d does not divide grid %dx%dx%d", tile_t, tile_h, tile_w,
+                grid_t, grid_h, grid_w);
+  const int64_t n = (int64_t)grid_t * grid_h * grid_w;
+  if (n > BSA_MAX_TOKENS) return fail(BSA_E_ARG, "grid has %lld tokens (max %d)", (long long)n,
+                                      BSA_MAX_TOKENS);
+  if (!perm) return fail(BSA_E_ARG, "null tensor pointer");
+  bsa_status st = check_device();
+  if (st != BSA_OK) return st;
+  return hip_status(bsa::launch_tile_layout(heads, grid_t, grid_h, grid_w, tile_t, tile_h, tile_w,
+                                            perm, stream),
+                    "tile layout launch");
+}
+
 }  // extern "C"

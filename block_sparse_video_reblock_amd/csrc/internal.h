@@ -53,6 +53,8 @@ hipError_t launch_block_means(bool bf16, const void* x, const int32_t* perm, int
                               float* means, hipStream_t s);
 hipError_t launch_block_scores(const float* qm, const float* km, int H, int nb, int D,
                                float scale, float* scores, hipStream_t s);
+hipError_t launch_tile_layout(int heads, int T, int H, int W, int tt, int th, int tw,
+                              int32_t* perm, hipStream_t s);
 hipError_t launch_topk(const float* scores, int rows, int nb, int k, int32_t* lists,
                        hipStream_t s);
 

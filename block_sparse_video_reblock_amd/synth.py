@@ -182,14 +182,3 @@ def make_qkv(wl: Workload, layer: int = 0, heads=None):
 
 def identity_perm(heads: int, tokens: int) -> np.ndarray:
     return np.tile(np.arange(tokens, dtype=np.int32), (heads, 1))
-
-
-def fixed_tile_perm(grid, tile=(4, 4, 4)) -> np.ndarray:
-    """Positional baseline layout: 64-token spatiotemporal cubes of the latent grid, cubes in
-    raster order, tokens in raster order inside a cube.  Returns token ids by position."""
-    T, H, W = grid
-    a, b, c = tile
-    if a * b * c != BLOCK or T % a or H % b or W % c:
-        raise ValueError(f"tile {tile} does not tile grid {grid} into {BLOCK}-token blocks")
-    ids = np.arange(T * H * W, dtype=np.int32).reshape(T // a, a, H // b, b, W // c, c)
-    return np.ascontiguousarray(ids.transpose(0, 2, 4, 1, 3, 5)).reshape(-1)

@@ -141,6 +141,19 @@ bsa_status bsa_summaries(const bsa_desc* desc, const void* q, const void* k, con
                          float* kt, float* vt, float* bias,
                          void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Fixed-tile layout: the positional baseline that (1) replaces.  [comfyui-wiki.com
+ * "Spark-H3 ...", "What Spark-Attn changes": Reblock takes the place of fixed spatiotemporal
+ * tiles; comfy.icu page, "What it's doing under the hood": recall against fixed blocks]
+ * The latent grid (grid_t, grid_h, grid_w), token id (t grid_h + y) grid_w + x, is cut into
+ * tile_t x tile_h x tile_w cubes of 64 tokens: position p holds cube p / 64 (cubes in raster
+ * order of their corner), token p % 64 of it (raster order inside the cube).
+ * perm: int32 [heads][grid_t grid_h grid_w], the same layout for every head; use it as both
+ * perm_q and perm_k.  BSA_E_ARG unless tile_t tile_h tile_w = 64, each tile side divides its
+ * grid side and the grid holds at most BSA_MAX_TOKENS tokens. */
+bsa_status bsa_tile_layout(int32_t heads, int32_t grid_t, int32_t grid_h, int32_t grid_w,
+                           int32_t tile_t, int32_t tile_h, int32_t tile_w, int32_t* perm,
+                           hipStream_t stream);
+
 /* Parity hook for (1): the tree partition with every level's projections supplied.
  * proj: float [problems][levels][tokens] by token id (levels = ceil(log2(tokens/64)));
  * perm: int32 [problems][tokens].  Each split sends the floor(m/2)*64 tokens of smallest

@@ -16,7 +16,7 @@ __all__ = [
     "split_direction", "partition", "partition_from_projections", "reblock_head",
     "topk_count", "block_means", "block_scores", "topk_lists", "summaries",
     "sparse_attention_head", "dense_attention_head", "recall_head", "log_mass_error_head",
-    "logsumexp",
+    "logsumexp", "fixed_tile_perm",
 ]
 
 LEAF = 64
@@ -249,7 +249,7 @@ def _softmax_branch(logits: np.ndarray, values: np.ndarray):
 
 
 def sparse_attention_head(Q, K, V, perm_q, perm_k, lists, scale=None, mode="reweight",
-                          leaf: int = LEAF, summ=None, return_branches=False):
+                          leaf: int = LEAF, summ=None, return_branches=False, blocks=None):
     """One head of the two-branch layer, output in token order.
 
     [P1] "What Spark-Attn changes": an exact branch fully computes the top-ranked K/V blocks
@@ -260,7 +260,8 @@ def sparse_attention_head(Q, K, V, perm_q, perm_k, lists, scale=None, mode="rewe
                   -> (O_c, lse_c); no unselected block gives lse_c = -inf
       merge:      lse = logaddexp(lse_e, lse_c), O = e^(lse_e-lse) O_e + e^(lse_c-lse) O_c
       inverse permutation: row p of the block goes to token perm_q[p].
-    Returns (O, lse) or, with return_branches, (O, lse, O_e, lse_e, O_c, lse_c)."""
+    Returns (O, lse) or, with return_branches, (O, lse, O_e, lse_e, O_c, lse_c).  With
+    blocks (query block indices) only those blocks' rows are computed; the others hold NaN."""
     Q = np.asarray(Q, np.float64)
     K = np.asarray(K, np.float64)
     V = np.asarray(V, np.float64)
@@ -271,10 +272,11 @@ def sparse_attention_head(Q, K, V, perm_q, perm_k, lists, scale=None, mode="rewe
     perm_k = np.asarray(perm_k)
     kt, vt, b = summaries(Q, K, V, perm_k, s, mode, leaf) if summ is None else summ
     key_rows = perm_k.reshape(nb, leaf)
-    O = np.empty((N, D))
-    lse = np.empty(N)
-    parts = [np.empty((N, D)), np.empty(N), np.empty((N, D)), np.empty(N)]
-    for i in range(nb):
+    O = np.full((N, D), np.nan)
+    lse = np.full(N, np.nan)
+    parts = [np.full((N, D), np.nan), np.full(N, np.nan), np.full((N, D), np.nan),
+             np.full(N, np.nan)]
+    for i in (range(nb) if blocks is None else blocks):
         rows = perm_q[i * leaf:(i + 1) * leaf]
         q = Q[rows]
         sel = np.asarray(lists[i])
@@ -307,6 +309,29 @@ def dense_attention_head(Q, K, V, scale=None, rows=None, chunk: int = 1024):
         lse[sl] = logsumexp(lg, axis=1)
         O[sl] = np.exp(lg - lse[sl, None]) @ V
     return O, lse
+
+
+# ------------------------------------------------------------ fixed-tile baseline layout
+
+def fixed_tile_perm(grid, tile=(4, 4, 4)) -> np.ndarray:
+    """Positional layout that Reblock replaces ([P1] "What Spark-Attn changes": fixed
+    spatiotemporal tiles; [P2] "What it's doing under the hood": recall against fixed blocks).
+    The latent grid (T, H, W), token id (t H + y) W + x, is cut into a x b x c cubes of 64
+    tokens; blocks are the cubes in raster order of their corner, tokens in raster order inside
+    a cube.  Returns token ids by position."""
+    T, H, W = grid
+    a, b, c = tile
+    if a * b * c != LEAF or T % a or H % b or W % c:
+        raise ValueError(f"tile {tile} does not cut grid {grid} into {LEAF}-token cubes")
+    out = []
+    for ct in range(T // a):
+        for cy in range(H // b):
+            for cx in range(W // c):
+                for t in range(ct * a, ct * a + a):
+                    for y in range(cy * b, cy * b + b):
+                        for x in range(cx * c, cx * c + c):
+                            out.append((t * H + y) * W + x)
+    return np.asarray(out, dtype=np.int32)
 
 
 # ------------------------------------------------------------------ measurements ([P2])

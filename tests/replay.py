@@ -10,15 +10,16 @@ import numpy as np
 import oracle as O
 
 
-def replay_partition(U, perm, proj=None, tol=1e-5, leaf=64):
+def replay_partition(U, perm, proj=None, tol=1e-5, leaf=64, max_level=None):
     """U: oracle unit vectors [N][D]; perm: GPU permutation; proj: GPU projections [L][N] by
-    token id or None.  Returns a dict of statistics; raises AssertionError on a bad split."""
+    token id or None; max_level: replay only the first levels.  Returns a dict of statistics;
+    raises AssertionError on a bad split."""
     N = U.shape[0]
     nb = N // leaf
     L = O.tree_levels(nb)
     stats = {"splits": 0, "mismatched_splits": 0, "max_proj_err": 0.0, "min_gap": np.inf}
     groups = [(0, nb)]
-    for lvl in range(L):
+    for lvl in range(L if max_level is None else min(L, max_level)):
         nxt = []
         for b0, m in groups:
             if m < 2:

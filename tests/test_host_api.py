@@ -129,6 +129,19 @@ def test_reblock_and_hook_argument_errors(L):
                            None) == _lib.BSA_E_ARG
 
 
+def test_tile_layout_argument_errors(L):
+    ok = (2, 16, 32, 32, 4, 4, 4)
+    assert L.bsa_tile_layout(*ok, None, None) == _lib.BSA_E_ARG            # null perm
+    for bad in ((0, 16, 32, 32, 4, 4, 4),       # no heads
+                (2, 16, 32, 32, 4, 4, 2),       # 32-token tile
+                (2, 16, 32, 30, 4, 4, 4),       # 4 does not divide 30
+                (2, 21, 48, 72, 4, 4, 4),       # 4 does not divide 21
+                (2, 0, 32, 32, 4, 4, 4),
+                (2, 512, 512, 512, 4, 4, 4)):   # too many tokens
+        assert L.bsa_tile_layout(*bad, FAKE, None) == _lib.BSA_E_ARG, bad
+        assert L.bsa_last_error()
+
+
 def test_architecture_is_checked(L, monkeypatch):
     monkeypatch.setenv("BSATTN_ARCH_OVERRIDE", "gfx942")
     st = L.bsa_topk_from_scores(4, 10, 3, FAKE, FAKE, None)

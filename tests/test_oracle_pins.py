@@ -300,7 +300,7 @@ def test_recall_rises_with_density_and_reblock_beats_fixed_tiles(tiny_inputs):
            for r in (0.1, 0.2, 0.3, 1.0)]
     assert rec[0] < rec[1] < rec[2] < rec[3]
     assert abs(rec[3] - 1) < 1e-12
-    fp = synth.fixed_tile_perm(wl.grid)
+    fp = O.fixed_tile_perm(wl.grid)
     k = O.topk_count(nb, wl.topk_ratio)
     Sf = O.block_scores(Q, K, fp, fp).astype(np.float32)
     r_fixed = O.recall_head(Q, K, fp, fp, O.topk_lists(Sf, k))
@@ -316,3 +316,34 @@ def test_reweight_lowers_log_mass_error(tiny_inputs):
     e_rw = O.log_mass_error_head(Q, K, V, pq, pk, lists, mode="reweight")
     e_mp = O.log_mass_error_head(Q, K, V, pq, pk, lists, mode="meanpool")
     assert e_rw < e_mp
+
+
+# ------------------------------------------------------------ fixed-tile baseline layout
+
+@pytest.mark.parametrize("grid,tile", [((16, 32, 32), (4, 4, 4)), ((4, 8, 16), (1, 8, 8)),
+                                       ((8, 4, 16), (2, 2, 16))])
+def test_fixed_tile_perm_is_cubes_in_raster_order(grid, tile):
+    """Every block of the fixed-tile layout is one whole a x b x c cube of the grid, blocks
+    follow the raster order of their corners and tokens the raster order inside a cube."""
+    T, H, W = grid
+    a, b, c = tile
+    perm = O.fixed_tile_perm(grid, tile)
+    assert np.array_equal(np.sort(perm), np.arange(T * H * W))
+    t, rem = np.divmod(perm, H * W)
+    y, x = np.divmod(rem, W)
+    corners = []
+    for blk in range(perm.size // 64):
+        sl = slice(64 * blk, 64 * blk + 64)
+        t0, y0, x0 = t[sl].min(), y[sl].min(), x[sl].min()
+        assert t0 % a == 0 and y0 % b == 0 and x0 % c == 0
+        assert np.all(t[sl] < t0 + a) and np.all(y[sl] < y0 + b) and np.all(x[sl] < x0 + c)
+        assert np.all(np.diff(perm[sl]) > 0)        # raster order = ascending token id
+        corners.append((t0, y0, x0))
+    assert corners == sorted(corners)
+
+
+def test_fixed_tile_perm_rejects_bad_tiles():
+    with pytest.raises(ValueError):
+        O.fixed_tile_perm((16, 32, 32), (4, 4, 2))
+    with pytest.raises(ValueError):
+        O.fixed_tile_perm((21, 48, 72), (4, 4, 4))
