@@ -1016,52 +1016,105 @@ __global__ __launch_bounds__(1024) void k_wide_split(ProblemArgs a) {
 }
 
 // ------------------------------------------------------------------ subtree levels
-// grid (roots, P): each workgroup owns the subtree of one active node of level `ls` and does
-// every split of levels [ls, le) inside it, one group at a time, in place.
+// Split of one group from its raw statistics: acc holds s^2 sum (y - shift)(y - shift)^T times
+// acc_scale = 1 / s^2 (or the sum itself with acc_scale 1), L.shift the shift and L.mu the sum
+// of y - shift.  Centres the statistics, stores the centred covariance to cov_out (if given,
+// for the children's right-child statistics), finds the direction, projects the group's
+// positions and partitions them in place (stable, ascending token id within each side).
 template <typename T, int D>
-__global__ __launch_bounds__(256, 2) void k_subtree(ProblemArgs a, int ls, int le) {
-  __shared__ StageLds<D, 2> st;
-  __shared__ DirLds L;
-  __shared__ int hist[4 * 256];
-  __shared__ int sm[16];
-  const int g0 = a.lists[(size_t)ls * a.G + blockIdx.x], p = blockIdx.y;
+BSA_DEV void split_group(const ProblemArgs& a, int p, int level, int g, int b0, int m,
+                         f32x16_t* acc, float acc_scale, DirLds& L, const MRegs<D>& M,
+                         float* cov_out, int* hist, int* sm) {
   const T* X = problem_x<T, D>(a, p);
   int32_t* pos = problem_pos(a, p);
   int32_t* tmp = a.tmp + (size_t)p * a.N;
   float* keys = a.keys + (size_t)p * a.N;
   const float* inv_n = a.inv_n + (size_t)p * a.N;
+  const int n = m * kBlk;
+  finish_stats<D>(acc, L, n, acc_scale);
+  if (cov_out) store_acc<D>(cov_out, acc);
+  power_direction<T, D>(acc, L, M, n, X, pos, inv_n, b0 * kBlk);
+  if (threadIdx.x < D) group_mean<D>(a, p, level, g)[threadIdx.x] = L.mu[threadIdx.x];
+  project_range<T, D>(X, pos, inv_n, b0, b0 + m, L.w, keys, problem_proj(a, p, level));
+  __syncthreads();
+  const size_t off = (size_t)b0 * kBlk;
+  const int want = (m >> 1) * kBlk;
+  int take;
+  const uint32_t T_ = select_smallest_w<256>(keys + off, n, want, hist, sm, &take);
+  partition_w<256>(keys + off, pos + off, tmp + off, n, want, T_, take, sm);
+  for (int i = threadIdx.x; i < n; i += 256) pos[off + i] = tmp[off + i];
+  __syncthreads();
+}
+
+// grid (parents, P): one workgroup per active group gp of level - 1 (lists[level - 1]); it
+// splits both children of gp at `level`.  Only the left child's statistics are accumulated
+// (relative to the parent mean); the right child's follow as n_P C_P - S_L with C_P the
+// parent's centred covariance (stored by the level above in cov_prev) and its sum of
+// (y - mu_P) as minus the left child's.  Each child's centred covariance goes to cov_cur for
+// the level below.  Covariance slots: [P][cov_g][D * D] in register-dump order.
+template <typename T, int D>
+__global__ __launch_bounds__(256, 2) void k_subtree_pair(ProblemArgs a, int level, int cov_g) {
+  __shared__ StageLds<D, 2> st;
+  __shared__ DirLds L;
+  __shared__ float dsl[D];
+  __shared__ int hist[4 * 256];
+  __shared__ int sm[16];
+  const int gp = a.lists[(size_t)(level - 1) * a.G + blockIdx.x], p = blockIdx.y;
+  int pb0, pm;
+  group_geom(a.nb, level - 1, gp, pb0, pm);
+  if (pm < 3) return;  // both children are leaves
+  const int gl = 2 * gp, gr = 2 * gp + 1;
+  int lb0, lm, rb0, rm;
+  group_geom(a.nb, level, gl, lb0, lm);
+  group_geom(a.nb, level, gr, rb0, rm);
+  const T* X = problem_x<T, D>(a, p);
+  const int32_t* pos = problem_pos(a, p);
+  const float* inv_n = a.inv_n + (size_t)p * a.N;
   const float ysc = a.yscale[2 * p], inv_s2 = a.yscale[2 * p + 1];
+  float* cov_l = a.cov_cur + ((size_t)p * cov_g + gl) * D * D;
+  float* cov_r = a.cov_cur + ((size_t)p * cov_g + gr) * D * D;
+  const float* cov_p = a.cov_prev + ((size_t)p * cov_g + gp) * D * D;
   MRegs<D> M;
   M.load(problem_metric<D>(a, p));
-  for (int level = ls; level < le; ++level) {
-    const int depth = level - ls;
-    for (int g = g0 << depth; g < ((g0 + 1) << depth); ++g) {
-      int b0, m;
-      if (group_geom(a.nb, level, g, b0, m) != kGroupSplit) continue;
-      const int n = m * kBlk;
-      if (threadIdx.x < D) L.shift[threadIdx.x] = parent_mean<D>(a, p, level, g)[threadIdx.x];
-      __syncthreads();
-      f32x16_t acc[Cov<D>::TILES];
-      zero_acc<D>(acc);
-      {
-        float dpart[D / 8];
+  if (threadIdx.x < D) L.shift[threadIdx.x] = group_mean<D>(a, p, level - 1, gp)[threadIdx.x];
+  __syncthreads();
+  f32x16_t acc[Cov<D>::TILES];
+  zero_acc<D>(acc);
+  {
+    float dpart[D / 8];
 #pragma unroll
-        for (int e = 0; e < D / 8; ++e) dpart[e] = 0.f;
-        stats_range<T, D, kF16x2, true>(X, pos, inv_n, b0, b0 + m, L.shift, ysc, st, acc, dpart);
-        reduce_dpart<D>(dpart, L.red, L.mu);
+    for (int e = 0; e < D / 8; ++e) dpart[e] = 0.f;
+    stats_range<T, D, kF16x2, true>(X, pos, inv_n, lb0, lb0 + lm, L.shift, ysc, st, acc, dpart);
+    reduce_dpart<D>(dpart, L.red, L.mu);
+  }
+  // keep S_L (unscaled) and its sum for the right child: S_L in the right child's covariance
+  // slot (each thread later reads back exactly the elements it wrote)
+  if (rm >= 2) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+    for (int t = 0; t < Cov<D>::TILES; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        cov_r[((w * Cov<D>::TILES + t) * 16 + r) * 64 + lane] = acc[t][r] * inv_s2;
+    if (threadIdx.x < D) dsl[threadIdx.x] = L.mu[threadIdx.x];
+  }
+  if (lm >= 2) split_group<T, D>(a, p, level, gl, lb0, lm, acc, inv_s2, L, M, cov_l, hist, sm);
+  if (rm >= 2) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const float np = float(pm * kBlk);
+#pragma unroll
+    for (int t = 0; t < Cov<D>::TILES; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const size_t e = ((w * Cov<D>::TILES + t) * 16 + r) * 64 + lane;
+        acc[t][r] = np * cov_p[e] - cov_r[e];
       }
-      group_direction<T, D>(acc, L, M, n, inv_s2, X, pos, inv_n, b0 * kBlk);
-      if (threadIdx.x < D) group_mean<D>(a, p, level, g)[threadIdx.x] = L.mu[threadIdx.x];
-      project_range<T, D>(X, pos, inv_n, b0, b0 + m, L.w, keys, problem_proj(a, p, level));
-      __syncthreads();
-      const size_t off = (size_t)b0 * kBlk;
-      const int want = (m >> 1) * kBlk;
-      int take;
-      const uint32_t T_ = select_smallest_w<256>(keys + off, n, want, hist, sm, &take);
-      partition_w<256>(keys + off, pos + off, tmp + off, n, want, T_, take, sm);
-      for (int i = threadIdx.x; i < n; i += 256) pos[off + i] = tmp[off + i];
-      __syncthreads();
+    if (threadIdx.x < D) {
+      L.shift[threadIdx.x] = group_mean<D>(a, p, level - 1, gp)[threadIdx.x];
+      L.mu[threadIdx.x] = -dsl[threadIdx.x];
     }
+    __syncthreads();
+    split_group<T, D>(a, p, level, gr, rb0, rm, acc, 1.f, L, M, cov_r, hist, sm);
   }
 }
 
@@ -1172,7 +1225,15 @@ RebLayout reb_layout(int H, int N, int D) {
   r.wdir = take(P * r.G * D * 4);
   r.partial = take(P * kSlots * (size_t)(D * D + D) * 4);
   r.lists = take((size_t)std::max(r.L, 1) * r.G * 4);
-  r.gw = std::min(r.G, kSlots / 2);  // wide levels have at most kSlots / 2 groups
+  // covariance slots per problem: the groups of the deepest level that stores them (the last
+  // wide level or the last one-workgroup-per-parent level)
+  int last = 0;
+  for (int level = 0; level < r.L; ++level) {
+    const int slices = std::min(kSlots >> std::min(level, 5), (int)(nb >> level));
+    if (slices > 1 || ceil_div((int)nb, 1 << level) > kSmallBlocks) last = level;
+    else break;
+  }
+  r.gw = 1 << last;
   r.cov0 = take(P * r.gw * (size_t)D * D * 4);
   r.cov1 = take(P * r.gw * (size_t)D * D * 4);
   r.total = off;
@@ -1260,6 +1321,8 @@ hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm
     k_wide_proj<T, D><<<dim3(nb, P), 256, 0, s>>>(a);
     k_wide_split<<<dim3(G, P), 1024, 0, s>>>(a);
   }
+  // narrow levels: one workgroup per parent, left-only statistics; the covariance slots
+  // alternate between the two buffers (the last wide level stored its groups' covariances)
   for (; level < R.L; ++level) {
     const int roots = active_count(nb, level);
     if (roots == 0) continue;
@@ -1267,7 +1330,9 @@ hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm
       k_subtree_small<T, D><<<dim3(roots, P), 256, 0, s>>>(a, level);
       break;
     }
-    k_subtree<T, D><<<dim3(roots, P), 256, 0, s>>>(a, level, level + 1);
+    a.cov_prev = reinterpret_cast<float*>(w + ((level & 1) ? R.cov0 : R.cov1));
+    a.cov_cur = reinterpret_cast<float*>(w + ((level & 1) ? R.cov1 : R.cov0));
+    k_subtree_pair<T, D><<<dim3(active_count(nb, level - 1), P), 256, 0, s>>>(a, level, R.gw);
   }
   return hipGetLastError();
 }

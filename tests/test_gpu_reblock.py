@@ -75,6 +75,24 @@ def test_reblock_bf16_mid(mid):
     assert st["mismatched_splits"] <= 0.02 * st["splits"]
 
 
+@pytest.mark.parametrize("n_blocks", [600, 1134])
+def test_reblock_bf16_narrow_levels(n_blocks):
+    """Enough blocks for the one-workgroup-per-parent levels (left-only statistics, right
+    child from the parent's covariance) between the wide levels and the subtree kernel: every
+    split of both sides replayed on the oracle."""
+    rng = np.random.default_rng(n_blocks)
+    wl = synth.WORKLOADS["clip10s_bf16"]
+    q, k, _ = synth.make_qkv(wl, heads=[5])
+    sel = np.sort(rng.choice(wl.tokens, size=64 * n_blocks, replace=False))
+    q, k = q[:, sel], k[:, sel]
+    pq, pk, proj = ops.reblock(to_dev(q, torch.bfloat16), to_dev(k, torch.bfloat16),
+                               with_proj=True)
+    st = _check_layouts(q, k, pq.cpu().numpy(), pk.cpu().numpy(), proj.cpu().numpy(),
+                        tol_proj=3e-5)
+    print("narrow replay", st)
+    assert st["mismatched_splits"] <= 0.02 * st["splits"]
+
+
 def test_reblock_deterministic(mid):
     wl, q, k, v = mid
     dt = torch.bfloat16
