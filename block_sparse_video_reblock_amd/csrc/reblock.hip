@@ -927,24 +927,27 @@ __global__ __launch_bounds__(256) void k_wide_stats(ProblemArgs a) {
 //   sum_R (y - mu_P) = -sum_L (y - mu_P).
 // Each group's centred covariance is kept for the next level.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_wide_dir(ProblemArgs a) {
+__global__ __launch_bounds__(256, 2) void k_wide_dir(ProblemArgs a) {
   __shared__ DirLds L;
   const int p = blockIdx.y;
-  const int g0 = a.left_only ? 2 * blockIdx.x : blockIdx.x;
+  // left-only levels: workgroup 2 j + c handles child c of parent j (both children read the
+  // left child's partial sums); otherwise workgroup g handles group g
+  const int par = a.left_only ? (int)(blockIdx.x >> 1) : (int)blockIdx.x;
+  const int child = a.left_only ? (int)(blockIdx.x & 1) : 0;
   MRegs<D> M;
   M.load(problem_metric<D>(a, p));
   const T* X = problem_x<T, D>(a, p);
   const int32_t* pos = problem_pos(a, p);
   const float* inv_n = a.inv_n + (size_t)p * a.N;
   int pb0, pm;
-  if (a.left_only) group_geom(a.nb, a.level - 1, blockIdx.x, pb0, pm);
-  for (int child = 0; child < (a.left_only ? 2 : 1); ++child) {
-    const int g = g0 + child;
+  if (a.left_only) group_geom(a.nb, a.level - 1, par, pb0, pm);
+  {
+    const int g = a.left_only ? 2 * par + child : par;
     int b0, m;
-    if (group_geom(a.nb, a.level, g, b0, m) != kGroupSplit) continue;
+    if (group_geom(a.nb, a.level, g, b0, m) != kGroupSplit) return;
     f32x16_t acc[Cov<D>::TILES];
     zero_acc<D>(acc);
-    const float* base = a.partial + ((size_t)p * kSlots + blockIdx.x * a.slices) * (D * D + D);
+    const float* base = a.partial + ((size_t)p * kSlots + par * a.slices) * (D * D + D);
     float ds = 0.f;
     for (int s = 0; s < a.slices; ++s) {
       add_acc<D>(base + (size_t)s * (D * D + D), acc);
@@ -957,7 +960,7 @@ __global__ __launch_bounds__(256) void k_wide_dir(ProblemArgs a) {
       for (int r = 0; r < 16; ++r) acc[t][r] *= inv_s2;
     if (child == 1) {
       // right child: n_P C_P - S_L, and the negated sum
-      const float* cp = a.cov_prev + ((size_t)p * a.gw + blockIdx.x) * D * D;
+      const float* cp = a.cov_prev + ((size_t)p * a.gw + par) * D * D;
       const float np = float(pm * kBlk);
       const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
@@ -1317,7 +1320,7 @@ hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm
     a.cov_cur = reinterpret_cast<float*>(w + ((level & 1) ? R.cov1 : R.cov0));
     const int Gs = a.left_only ? G / 2 : G;
     k_wide_stats<T, D><<<dim3(slices, Gs, P), 256, 0, s>>>(a);
-    k_wide_dir<T, D><<<dim3(Gs, P), 256, 0, s>>>(a);
+    k_wide_dir<T, D><<<dim3(a.left_only ? 2 * Gs : Gs, P), 256, 0, s>>>(a);
     k_wide_proj<T, D><<<dim3(nb, P), 256, 0, s>>>(a);
     k_wide_split<<<dim3(G, P), 1024, 0, s>>>(a);
   }
