@@ -34,6 +34,10 @@ import time
 METRIC = "sparse attn layer ms + effective TFLOP/s at 72,576 tok, 10% density, vs dense"
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 HBM_PEAK_GBS = 8000.0
+# Bytes one attention launch moves between L2 and memory on the headline workload: rocprofv3
+# FETCH_SIZE x 2 + WRITE_SIZE x 1 (the factors a plain 1 GiB copy gives those counters), taken
+# on the current attention kernel; to be retaken whenever that kernel changes.
+ATTN_TRAFFIC_BYTES = {"clip10s_bf16": 5.90e10}
 
 
 def log(*a):
@@ -278,8 +282,8 @@ def main_headline(args, ops, synth, torch, np):
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": None, "kernel": "k_attn_bf16", "launch_ms": attn_ms,
-                     "launch_ms_min": float(min(series["attend"])),
+                     "traffic": ATTN_TRAFFIC_BYTES.get(wl.name), "kernel": "k_attn_bf16",
+                     "launch_ms": attn_ms, "launch_ms_min": float(min(series["attend"])),
                      "flops_per_launch": exact_f + comp_f},
         "stages_ms": stage_ms,
         "hbm": hbm,
