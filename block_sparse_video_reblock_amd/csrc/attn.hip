@@ -179,7 +179,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
             }
           }
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        mx = xor32_max(mx);
         // lazy rescale: move the running max only when it grows by more than kMaxSlack
         const bool grow = mx > m_run[n] + kMaxSlack;
         if (__any(grow)) {
@@ -193,24 +193,23 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
             for (int r = 0; r < 16; ++r) acc[a][n][r] *= alpha;
         }
         const float m_use = (m_run[n] == -INFINITY) ? 0.f : m_run[n];
-        float rs = 0.f;
+        float rs4[4] = {0.f, 0.f, 0.f, 0.f};  // four short chains instead of one of 16
         if (exact) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const float pr = __builtin_amdgcn_exp2f(fmaf(s[n][r], scale_log2, -m_use));
             s[n][r] = pr;
-            rs += pr;
+            rs4[r & 3] += pr;
           }
         } else {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const float pr = __builtin_amdgcn_exp2f(s[n][r] - m_use);
             s[n][r] = pr;
-            rs += pr;
+            rs4[r & 3] += pr;
           }
         }
-        rs += __shfl_xor(rs, 32, 64);
-        l_run[n] += rs;
+        l_run[n] += xor32_sum((rs4[0] + rs4[1]) + (rs4[2] + rs4[3]));
       }
       // O^T[d chunk a][n] += V^T[a][key chunk c] P^T[c][n], c = 2hh + cc; the B operand of
       // chunk c is registers 8cc..8cc+8 of S^T[n]

@@ -62,6 +62,18 @@ BSA_DEV float row16_sum(float x) {
   x += dpp_mov<0x140>(x);
   return x;
 }
+// Combine each lane with lane ^ 32 (v_permlane32_swap: with both operands x, the two results
+// hold x of the other half-wave in one and x itself in the other, on every lane)
+BSA_DEV float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+BSA_DEV float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 // wave64 sum, wave-uniform result (DPP within rows, then the four row totals)
 BSA_DEV float lane_value(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));

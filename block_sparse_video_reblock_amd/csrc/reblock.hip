@@ -329,8 +329,7 @@ BSA_DEV void cov_matvec(const f32x16_t* acc, const float* v, float vs, float* ou
         s[j] = fmaf(acc[t][4 * j + 3], vv.w, s[j]);
       }
     }
-    float z = (s[0] + s[1]) + (s[2] + s[3]);
-    z += __shfl_xor(z, 32, 64);
+    const float z = xor32_sum((s[0] + s[1]) + (s[2] + s[3]));
     if (lane < 32) out[32 * w + lane] = z * vs;
     __syncthreads();
   } else {
@@ -339,7 +338,7 @@ BSA_DEV void cov_matvec(const f32x16_t* acc, const float* v, float vs, float* ou
       float s = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) s = fmaf(acc[t][r], v[acc_row<D>(t, r)], s);
-      s += __shfl_xor(s, 32, 64);
+      s = xor32_sum(s);
       if (lane < 32) red[Cov<D>::ac(w, t) * D + acc_col<D>(t)] = s;
     }
     __syncthreads();
@@ -763,7 +762,7 @@ __global__ __launch_bounds__(256) void k_norms_bf16(ProblemArgs a, const uint16_
         part = fmaf(acc[4 * j + 2], __uint_as_float(u.y << 16), part);
         part = fmaf(acc[4 * j + 3], __uint_as_float(u.y & 0xFFFF0000u), part);
       }
-      part += __shfl_xor(part, 32, 64);
+      part = xor32_sum(part);
       if (g == 0) red[w][tok] = part;
     }
     __syncthreads();
