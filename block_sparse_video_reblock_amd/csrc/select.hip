@@ -32,10 +32,12 @@ __global__ __launch_bounds__(128) void k_block_means(const T* __restrict__ x,
 __global__ __launch_bounds__(256) void k_block_scores(const float* __restrict__ qm,
                                                       const float* __restrict__ km, int nb, int D,
                                                       float scale, float* __restrict__ S) {
+  // one 64 x 64 tile of S per workgroup; wave w computes the 32 x 32 sub-tile (w / 2, w % 2)
+  // with v_mfma_f32_32x32x2f32 (fp32 products and sums) over pairs of dimensions
   __shared__ float sq[64][129];
   __shared__ float sk[64][129];
   const int ti = blockIdx.x, tj = blockIdx.y, h = blockIdx.z;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   for (int e = tid; e < 64 * D; e += 256) {
     const int r = e / D, d = e - r * D;
     const int i = ti * 64 + r, j = tj * 64 + r;
@@ -43,29 +45,21 @@ __global__ __launch_bounds__(256) void k_block_scores(const float* __restrict__ 
     sk[r][d] = j < nb ? km[((size_t)h * nb + j) * D + d] : 0.f;
   }
   __syncthreads();
-  const int ri = (tid >> 4) * 4, rj = (tid & 15) * 4;
-  float acc[4][4] = {};
-  for (int d = 0; d < D; ++d) {
-    float a[4], b[4];
+  const int wi = w >> 1, wj = w & 1;
+  // A[i][k] = query mean 32 wi + i, dimension d + k; B[k][j] = key mean 32 wj + j, same
+  const float* qa = &sq[32 * wi + (lane & 31)][lane >> 5];
+  const float* kb = &sk[32 * wj + (lane & 31)][lane >> 5];
+  f32x16_t acc;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      a[u] = sq[ri + u][d];
-      b[u] = sk[rj + u][d];
-    }
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  for (int d = 0; d < D; d += 2)
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[d], kb[d], acc, 0, 0, 0);
+  // lane holds S[32 wi + 8 (r/4) + 4 (lane/32) + r%4][32 wj + lane%32]
+  const int j = tj * 64 + 32 * wj + (lane & 31);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(a[u], b[v], acc[u][v]);
-  }
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int i = ti * 64 + ri + u;
-    if (i >= nb) continue;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int j = tj * 64 + rj + v;
-      if (j < nb) S[((size_t)h * nb + i) * nb + j] = acc[u][v] * scale;
-    }
+  for (int r = 0; r < 16; ++r) {
+    const int i = ti * 64 + 32 * wi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    if (i < nb && j < nb) S[((size_t)h * nb + i) * nb + j] = acc[r] * scale;
   }
 }
 

@@ -26,19 +26,41 @@ BSA_DEV int vrow(int c, int g, int t) { return 16 * c + 8 * (t >> 2) + 4 * g + (
 template <typename T>
 __global__ __launch_bounds__(256) void k_colsum(const T* __restrict__ x, int N, int D,
                                                 float* __restrict__ partial) {
-  // grid (chunks, H); thread -> column d (D <= 128), 2 row phases
+  // grid (chunks, H).  16 threads per row, each loading 16 bytes (E elements) of a row, 16 rows
+  // per pass (D * sizeof(T) = 256 bytes for both supported shapes); per-thread column sums of
+  // the chunk, then a fixed-order sum over the 16 row phases.
+  constexpr int E = 16 / sizeof(T);
   const int chunk = blockIdx.x, h = blockIdx.y, nch = gridDim.x;
-  const int d = threadIdx.x % D, ph = threadIdx.x / D, nph = 256 / D;
+  const int c16 = threadIdx.x & 15, ph = threadIdx.x >> 4;
   const int t0 = chunk * kColChunk, t1 = min(N, t0 + kColChunk);
-  __shared__ float red[256];
-  float acc = 0.f;
-  for (int t = t0 + ph; t < t1; t += nph) acc += load_as_f32(x + ((size_t)h * N + t) * D + d);
-  red[threadIdx.x] = acc;
+  __shared__ float red[16][129];
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int t = t0 + ph; t < t1; t += 16) {
+    const uint4 u = *reinterpret_cast<const uint4*>(x + ((size_t)h * N + t) * D + c16 * E);
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += __uint_as_float(wv[i] << 16);
+        acc[2 * i + 1] += __uint_as_float(wv[i] & 0xFFFF0000u);
+      }
+    } else {
+      acc[0] += __uint_as_float(u.x);
+      acc[1] += __uint_as_float(u.y);
+      acc[2] += __uint_as_float(u.z);
+      acc[3] += __uint_as_float(u.w);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) red[ph][c16 * E + e] = acc[e];
   __syncthreads();
-  if (ph == 0) {
+  if (threadIdx.x < D) {
     float s = 0.f;
-    for (int p = 0; p < nph; ++p) s += red[p * D + d];
-    partial[((size_t)h * nch + chunk) * D + d] = s;
+#pragma unroll
+    for (int p = 0; p < 16; ++p) s += red[p][threadIdx.x];
+    partial[((size_t)h * nch + chunk) * D + threadIdx.x] = s;
   }
 }
 
