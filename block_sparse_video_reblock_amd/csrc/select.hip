@@ -14,23 +14,54 @@ namespace {
 
 // grid (nb, H); thread -> element d.  Means in a fixed summation order.
 template <typename T>
-__global__ __launch_bounds__(128) void k_block_means(const T* __restrict__ x,
+__global__ __launch_bounds__(256) void k_block_means(const T* __restrict__ x,
                                                      const int32_t* __restrict__ perm, int N,
                                                      int D, float* __restrict__ means) {
-  const int j = blockIdx.x, h = blockIdx.y, nb = gridDim.x, d = threadIdx.x;
+  // 16 threads per row, each summing 16 bytes (E elements) of 4 of the block's 64 rows; then a
+  // fixed-order sum over the 16 row phases (D * sizeof(T) = 256 bytes for both shapes)
+  constexpr int E = 16 / sizeof(T);
+  const int j = blockIdx.x, h = blockIdx.y, nb = gridDim.x;
+  const int c16 = threadIdx.x & 15, ph = threadIdx.x >> 4;
   __shared__ int32_t rows[64];
+  __shared__ float red[16][129];
   if (threadIdx.x < 64) rows[threadIdx.x] = perm[(size_t)h * N + (size_t)j * kBlk + threadIdx.x];
   __syncthreads();
-  if (d >= D) return;
-  float s = 0.f;
-  for (int r = 0; r < 64; ++r) s += load_as_f32(x + ((size_t)h * N + rows[r]) * D + d);
-  means[((size_t)h * nb + j) * D + d] = s * (1.f / 64.f);
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int r = 16 * p + ph;
+    const uint4 u = *reinterpret_cast<const uint4*>(x + ((size_t)h * N + rows[r]) * D + c16 * E);
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += __uint_as_float(wv[i] << 16);
+        acc[2 * i + 1] += __uint_as_float(wv[i] & 0xFFFF0000u);
+      }
+    } else {
+      acc[0] += __uint_as_float(u.x);
+      acc[1] += __uint_as_float(u.y);
+      acc[2] += __uint_as_float(u.z);
+      acc[3] += __uint_as_float(u.w);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) red[ph][c16 * E + e] = acc[e];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float t = 0.f;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) t += red[q][threadIdx.x];
+    means[((size_t)h * nb + j) * D + threadIdx.x] = t * (1.f / 64.f);
+  }
 }
 
-// S[h][i][j] = scale * qm[h][i] . km[h][j]; 64 x 64 output tile per workgroup, 4 x 4 per thread,
-// fp32 FMA in ascending d.
+// S[h][i][j] = scale * qm[h][i] . km[h][j].
+template <int D>
 __global__ __launch_bounds__(256) void k_block_scores(const float* __restrict__ qm,
-                                                      const float* __restrict__ km, int nb, int D,
+                                                      const float* __restrict__ km, int nb,
                                                       float scale, float* __restrict__ S) {
   // one 64 x 64 tile of S per workgroup; wave w computes the 32 x 32 sub-tile (w / 2, w % 2)
   // with v_mfma_f32_32x32x2f32 (fp32 products and sums) over pairs of dimensions
@@ -38,11 +69,22 @@ __global__ __launch_bounds__(256) void k_block_scores(const float* __restrict__ 
   __shared__ float sk[64][129];
   const int ti = blockIdx.x, tj = blockIdx.y, h = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  for (int e = tid; e < 64 * D; e += 256) {
-    const int r = e / D, d = e - r * D;
+  constexpr int V = D / 4;  // float4 per row
+#pragma unroll
+  for (int e = tid; e < 64 * V; e += 256) {
+    const int r = e / V, c = e % V;
     const int i = ti * 64 + r, j = tj * 64 + r;
-    sq[r][d] = i < nb ? qm[((size_t)h * nb + i) * D + d] : 0.f;
-    sk[r][d] = j < nb ? km[((size_t)h * nb + j) * D + d] : 0.f;
+    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 a = i < nb ? reinterpret_cast<const float4*>(qm + ((size_t)h * nb + i) * D)[c] : zero;
+    const float4 b = j < nb ? reinterpret_cast<const float4*>(km + ((size_t)h * nb + j) * D)[c] : zero;
+    sq[r][4 * c] = a.x;
+    sq[r][4 * c + 1] = a.y;
+    sq[r][4 * c + 2] = a.z;
+    sq[r][4 * c + 3] = a.w;
+    sk[r][4 * c] = b.x;
+    sk[r][4 * c + 1] = b.y;
+    sk[r][4 * c + 2] = b.z;
+    sk[r][4 * c + 3] = b.w;
   }
   __syncthreads();
   const int wi = w >> 1, wj = w & 1;
@@ -52,6 +94,7 @@ __global__ __launch_bounds__(256) void k_block_scores(const float* __restrict__ 
   f32x16_t acc;
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll 8
   for (int d = 0; d < D; d += 2)
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[d], kb[d], acc, 0, 0, 0);
   // lane holds S[32 wi + 8 (r/4) + 4 (lane/32) + r%4][32 wj + lane%32]
@@ -144,17 +187,20 @@ hipError_t launch_block_means(bool bf16, const void* x, const int32_t* perm, int
                               float* means, hipStream_t s) {
   dim3 grid(N / kBlk, H);
   if (bf16)
-    k_block_means<uint16_t><<<grid, 128, 0, s>>>(static_cast<const uint16_t*>(x), perm, N, D,
+    k_block_means<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), perm, N, D,
                                                  means);
   else
-    k_block_means<float><<<grid, 128, 0, s>>>(static_cast<const float*>(x), perm, N, D, means);
+    k_block_means<float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), perm, N, D, means);
   return hipGetLastError();
 }
 
 hipError_t launch_block_scores(const float* qm, const float* km, int H, int nb, int D,
                                float scale, float* scores, hipStream_t s) {
   dim3 grid(ceil_div(nb, 64), ceil_div(nb, 64), H);
-  k_block_scores<<<grid, 256, 0, s>>>(qm, km, nb, D, scale, scores);
+  if (D == 128)
+    k_block_scores<128><<<grid, 256, 0, s>>>(qm, km, nb, scale, scores);
+  else
+    k_block_scores<64><<<grid, 256, 0, s>>>(qm, km, nb, scale, scores);
   return hipGetLastError();
 }
 
