@@ -74,7 +74,7 @@ template <int MODE>
 constexpr int split_terms() { return MODE == kExact ? 1 : (MODE == kF16x2 ? 2 : 3); }
 
 template <int D, int NT>
-struct StageLds {
+struct __align__(16) StageLds {
   uint16_t t[NT][D][kStageStride];
 };
 
@@ -308,6 +308,215 @@ template <int D>
 BSA_DEV int acc_col(int t) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   return 32 * Cov<D>::bc(w, t) + (lane & 31);
+}
+
+// ------------------------------------------------- symmetric covariance statistics
+// The group statistics D D^T (D: centred values, d x tokens) are symmetric, so only the upper
+// triangle of its (d/16) x (d/16) grid of 16 x 16 tiles is accumulated, with
+// v_mfma_f32_16x16x32_f16: lane l of an operand holds row (or column) l % 16 and the 8 tokens
+// 8 (l / 16) .. + 8 of a 32-token step, so the operand of block x serves as A for tile row x
+// and as B for tile column x.  The tiles are dealt to the 4 waves so that each wave touches
+// few blocks: for d = 128 waves 0 and 1 take the triangles of blocks 0-3 and 4-7 (10 tiles
+// each), waves 2 and 3 the rectangles {0,1} x {4..7} and {2,3} x {4..7} (8 tiles each).
+// The result lane l of a tile holds column l % 16 and rows 4 (l / 16) .. + 4.
+template <int D> struct SymPlan;
+template <> struct SymPlan<128> {
+  static constexpr int NB = 8, MAXT = 10;
+  static constexpr int nt[4] = {10, 10, 8, 8};
+  static constexpr int a[4][10] = {{0, 0, 0, 0, 1, 1, 1, 2, 2, 3}, {4, 4, 4, 4, 5, 5, 5, 6, 6, 7},
+                                   {0, 0, 0, 0, 1, 1, 1, 1, 0, 0}, {2, 2, 2, 2, 3, 3, 3, 3, 0, 0}};
+  static constexpr int b[4][10] = {{0, 1, 2, 3, 1, 2, 3, 2, 3, 3}, {4, 5, 6, 7, 5, 6, 7, 6, 7, 7},
+                                   {4, 5, 6, 7, 4, 5, 6, 7, 0, 0}, {4, 5, 6, 7, 4, 5, 6, 7, 0, 0}};
+};
+template <> struct SymPlan<64> {
+  static constexpr int NB = 4, MAXT = 3;
+  static constexpr int nt[4] = {3, 3, 2, 2};
+  static constexpr int a[4][3] = {{0, 0, 1}, {2, 2, 3}, {0, 0, 0}, {1, 1, 0}};
+  static constexpr int b[4][3] = {{0, 1, 1}, {2, 3, 3}, {2, 3, 0}, {2, 3, 0}};
+};
+template <int D, int W>
+constexpr bool sym_is_row(int x) {
+  for (int t = 0; t < SymPlan<D>::nt[W]; ++t)
+    if (SymPlan<D>::a[W][t] == x) return true;
+  return false;
+}
+template <int D, int W>
+constexpr bool sym_uses(int x) {
+  for (int t = 0; t < SymPlan<D>::nt[W]; ++t)
+    if (SymPlan<D>::a[W][t] == x || SymPlan<D>::b[W][t] == x) return true;
+  return false;
+}
+
+template <int D>
+struct SymAcc {
+  f32x4_t t[SymPlan<D>::MAXT];
+  BSA_DEV void zero() {
+#pragma unroll
+    for (int i = 0; i < SymPlan<D>::MAXT; ++i) t[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+};
+
+// one 64-token chunk (two 32-token steps) of the staged fp16 split into wave W's tiles
+template <int D, int W>
+BSA_DEV void sym_mfma_wave(const StageLds<D, 2>& st, SymAcc<D>& acc) {
+  using P = SymPlan<D>;
+  const int lane = threadIdx.x & 63, r16 = lane & 15, kg = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    // operands of the row blocks first; a column block that is not also a row block is read
+    // just before its tiles (the tiles are listed by column within each row run)
+    f16x8_t oh[P::NB], om[P::NB];
+#pragma unroll
+    for (int x = 0; x < P::NB; ++x)
+      if (sym_is_row<D, W>(x)) {
+        oh[x] = lds_f16x8(&st.t[0][16 * x + r16][32 * ks + 8 * kg]);
+        om[x] = lds_f16x8(&st.t[1][16 * x + r16][32 * ks + 8 * kg]);
+      }
+#pragma unroll
+    for (int b = 0; b < P::NB; ++b) {
+      if (!sym_uses<D, W>(b)) continue;
+      f16x8_t bh = oh[b], bm = om[b];
+      if (!sym_is_row<D, W>(b)) {
+        bh = lds_f16x8(&st.t[0][16 * b + r16][32 * ks + 8 * kg]);
+        bm = lds_f16x8(&st.t[1][16 * b + r16][32 * ks + 8 * kg]);
+      }
+#pragma unroll
+      for (int t = 0; t < P::nt[W]; ++t) {
+        if (P::b[W][t] != b) continue;
+        const int a = P::a[W][t];
+        acc.t[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(oh[a], bh, acc.t[t], 0, 0, 0);
+        acc.t[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(oh[a], bm, acc.t[t], 0, 0, 0);
+        acc.t[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(om[a], bh, acc.t[t], 0, 0, 0);
+      }
+    }
+  }
+}
+template <int D>
+BSA_DEV void sym_mfma(const StageLds<D, 2>& st, SymAcc<D>& acc) {
+  switch (threadIdx.x >> 6) {
+    case 0: sym_mfma_wave<D, 0>(st, acc); break;
+    case 1: sym_mfma_wave<D, 1>(st, acc); break;
+    case 2: sym_mfma_wave<D, 2>(st, acc); break;
+    default: sym_mfma_wave<D, 3>(st, acc); break;
+  }
+}
+
+// Accumulate the chunks [blk0, blk1) with the fp16 two-term split (see stats_range).
+template <typename T, int D, bool PREFETCH>
+BSA_DEV void sym_stats_range(const T* __restrict__ X, const int32_t* __restrict__ tokmap,
+                             const float* __restrict__ inv_n, int blk0, int blk1,
+                             const float* sh_shift, float ysc, StageLds<D, 2>& st, SymAcc<D>& acc,
+                             float* dpart) {
+  if (blk0 >= blk1) return;
+  ChunkRegs<T, D> cur;
+  if (PREFETCH) stats_load<T, D>(X, tokmap, inv_n, blk0 * kBlk, cur);
+  for (int b = blk0; b < blk1; ++b) {
+    if (!PREFETCH) stats_load<T, D>(X, tokmap, inv_n, b * kBlk, cur);
+    stats_stage<T, D, kF16x2>(cur, sh_shift, ysc, st, dpart);
+    __syncthreads();
+    if (PREFETCH && b + 1 < blk1) stats_load<T, D>(X, tokmap, inv_n, (b + 1) * kBlk, cur);
+    sym_mfma<D>(st, acc);
+    __syncthreads();
+  }
+}
+
+// Write wave W's tiles, times f, as the full symmetric matrix: out(r, c) at
+// F[(c - c0) * ld + r] for the columns c in [c0, c0 + ncols) (every element exactly once).
+template <int D, int W>
+BSA_DEV void sym_store_wave(const SymAcc<D>& acc, float f, float* F, int ld, int c0, int ncols) {
+  using P = SymPlan<D>;
+  const int lane = threadIdx.x & 63, r16 = lane & 15, kg = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < P::nt[W]; ++t) {
+    const int a = P::a[W][t], b = P::b[W][t];
+    const f32x4_t v = acc.t[t] * f;
+    // tile element (16 a + 4 kg + i, 16 b + r16): as column 16 b + r16, rows 16 a + 4 kg + i
+    const int cb = 16 * b + r16 - c0;
+    if (16 * b >= c0 && 16 * b < c0 + ncols)
+      *reinterpret_cast<f32x4_t*>(F + (size_t)cb * ld + 16 * a + 4 * kg) = v;
+    // its mirror (16 b + r16, 16 a + 4 kg + i): column 16 a + 4 kg + i, row 16 b + r16
+    if (a != b && 16 * a >= c0 && 16 * a < c0 + ncols) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) F[(size_t)(16 * a + 4 * kg + i - c0) * ld + 16 * b + r16] = v[i];
+    }
+  }
+}
+template <int D>
+BSA_DEV void sym_store(const SymAcc<D>& acc, float f, float* F, int ld, int c0, int ncols) {
+  switch (threadIdx.x >> 6) {
+    case 0: sym_store_wave<D, 0>(acc, f, F, ld, c0, ncols); break;
+    case 1: sym_store_wave<D, 1>(acc, f, F, ld, c0, ncols); break;
+    case 2: sym_store_wave<D, 2>(acc, f, F, ld, c0, ncols); break;
+    default: sym_store_wave<D, 3>(acc, f, F, ld, c0, ncols); break;
+  }
+}
+
+// Position of element (row, col) in the register dump order of Cov<D> (store_acc / add_acc).
+template <int D>
+BSA_DEV int dump_index(int row, int col) {
+  const int w = D == 128 ? (col >> 5) : 2 * (row >> 5) + (col >> 5);
+  const int t = D == 128 ? (row >> 5) : 0;
+  const int r = 4 * ((row >> 3) & 3) + (row & 3), lane = (col & 31) + 32 * ((row >> 2) & 1);
+  return ((w * Cov<D>::TILES + t) * 16 + r) * 64 + lane;
+}
+// Wave W's tiles (times f) as the full symmetric matrix in that dump order.
+template <int D, int W>
+BSA_DEV void sym_store_dump_wave(const SymAcc<D>& acc, float f, float* dst) {
+  using P = SymPlan<D>;
+  const int lane = threadIdx.x & 63, r16 = lane & 15, kg = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < P::nt[W]; ++t) {
+    const int a = P::a[W][t], b = P::b[W][t];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v = acc.t[t][i] * f;
+      const int row = 16 * a + 4 * kg + i, col = 16 * b + r16;
+      dst[dump_index<D>(row, col)] = v;
+      if (a != b) dst[dump_index<D>(col, row)] = v;
+    }
+  }
+}
+template <int D>
+BSA_DEV void sym_store_dump(const SymAcc<D>& acc, float f, float* dst) {
+  switch (threadIdx.x >> 6) {
+    case 0: sym_store_dump_wave<D, 0>(acc, f, dst); break;
+    case 1: sym_store_dump_wave<D, 1>(acc, f, dst); break;
+    case 2: sym_store_dump_wave<D, 2>(acc, f, dst); break;
+    default: sym_store_dump_wave<D, 3>(acc, f, dst); break;
+  }
+}
+
+// acc (register layout of Cov<D>) from a symmetric matrix stored by columns: element (r, c) at
+// F[(c - c0) * ld + r]; only the registers whose column lies in [c0, c0 + ncols).  ADD sums
+// into acc instead.
+template <int D, bool ADD>
+BSA_DEV void load_cols(f32x16_t* acc, const float* F, int ld, int c0, int ncols) {
+#pragma unroll
+  for (int t = 0; t < Cov<D>::TILES; ++t) {
+    const int c = acc_col<D>(t);
+    if (c < c0 || c >= c0 + ncols) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f32x4_t v = *reinterpret_cast<const f32x4_t*>(F + (size_t)(c - c0) * ld + acc_row<D>(t, 4 * j));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[t][4 * j + i] = ADD ? acc[t][4 * j + i] + v[i] : v[i];
+    }
+  }
+}
+
+// Symmetric tiles (times f) into the register layout of Cov<D>, through the staging LDS in
+// passes of 64 columns (stored by columns, D + 4 floats apart: conflict-free 16-byte reads).
+template <int D>
+BSA_DEV void sym_to_regs(const SymAcc<D>& sacc, float f, StageLds<D, 2>& st, f32x16_t* acc) {
+  constexpr int ld = D + 4;
+  static_assert(64 * ld * 4 <= sizeof(StageLds<D, 2>), "one pass fits the staging area");
+  float* G = reinterpret_cast<float*>(&st);
+  for (int c0 = 0; c0 < D; c0 += 64) {
+    sym_store<D>(sacc, f, G, ld, c0, 64);
+    __syncthreads();
+    load_cols<D, false>(acc, G, ld, c0, 64);
+    __syncthreads();
+  }
 }
 
 // out = vs * C v for the symmetric register-resident C (column form; v, out 16-byte aligned).
@@ -892,7 +1101,7 @@ __global__ __launch_bounds__(256) void k_group_lists(int nb, int G, int* __restr
 // ---------------------------------------------------------------------- wide levels
 // grid (slices, G, P): partial statistics of one slice of one group
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_wide_stats(ProblemArgs a) {
+__global__ __launch_bounds__(256, 3) void k_wide_stats(ProblemArgs a) {
   __shared__ StageLds<D, 2> st;
   __shared__ float shift[D];
   __shared__ float red[4 * D];
@@ -906,16 +1115,17 @@ __global__ __launch_bounds__(256) void k_wide_stats(ProblemArgs a) {
   const float* inv_n = a.inv_n + (size_t)p * a.N;
   if (threadIdx.x < D) shift[threadIdx.x] = parent_mean<D>(a, p, a.level, g)[threadIdx.x];
   __syncthreads();
-  f32x16_t acc[Cov<D>::TILES];
-  zero_acc<D>(acc);
+  SymAcc<D> acc;
+  acc.zero();
   float dpart[D / 8];
 #pragma unroll
   for (int e = 0; e < D / 8; ++e) dpart[e] = 0.f;
-  stats_range<T, D, kF16x2, true>(X, tokmap, inv_n, sb0, sb1, shift, a.yscale[2 * p], st, acc,
-                                  dpart);
+  sym_stats_range<T, D, true>(X, tokmap, inv_n, sb0, sb1, shift, a.yscale[2 * p], st, acc, dpart);
   reduce_dpart<D>(dpart, red, dsum);
+  // the slot holds the full symmetric D x D sum (scaled by s^2) in register dump order, then the
+  // D sums of d
   float* slot = a.partial + ((size_t)p * kSlots + blockIdx.y * a.slices + s) * (D * D + D);
-  store_acc<D>(slot, acc);
+  sym_store_dump<D>(acc, 1.f, slot);
   if (threadIdx.x < D) slot[D * D + threadIdx.x] = dsum[threadIdx.x];
 }
 
@@ -1025,8 +1235,8 @@ __global__ __launch_bounds__(1024) void k_wide_split(ProblemArgs a) {
 // positions and partitions them in place (stable, ascending token id within each side).
 template <typename T, int D>
 BSA_DEV void split_group(const ProblemArgs& a, int p, int level, int g, int b0, int m,
-                         f32x16_t* acc, float acc_scale, DirLds& L, const MRegs<D>& M,
-                         float* cov_out, int* hist, int* sm) {
+                         f32x16_t* acc, float acc_scale, DirLds& L, float* cov_out, int* hist,
+                         int* sm) {
   const T* X = problem_x<T, D>(a, p);
   int32_t* pos = problem_pos(a, p);
   int32_t* tmp = a.tmp + (size_t)p * a.N;
@@ -1035,7 +1245,12 @@ BSA_DEV void split_group(const ProblemArgs& a, int p, int level, int g, int b0, 
   const int n = m * kBlk;
   finish_stats<D>(acc, L, n, acc_scale);
   if (cov_out) store_acc<D>(cov_out, acc);
-  power_direction<T, D>(acc, L, M, n, X, pos, inv_n, b0 * kBlk);
+  {
+    // M is read (from L2) for the power steps only, so it holds no registers elsewhere
+    MRegs<D> M;
+    M.load(problem_metric<D>(a, p));
+    power_direction<T, D>(acc, L, M, n, X, pos, inv_n, b0 * kBlk);
+  }
   if (threadIdx.x < D) group_mean<D>(a, p, level, g)[threadIdx.x] = L.mu[threadIdx.x];
   project_range<T, D>(X, pos, inv_n, b0, b0 + m, L.w, keys, problem_proj(a, p, level));
   __syncthreads();
@@ -1076,31 +1291,26 @@ __global__ __launch_bounds__(256, 2) void k_subtree_pair(ProblemArgs a, int leve
   float* cov_l = a.cov_cur + ((size_t)p * cov_g + gl) * D * D;
   float* cov_r = a.cov_cur + ((size_t)p * cov_g + gr) * D * D;
   const float* cov_p = a.cov_prev + ((size_t)p * cov_g + gp) * D * D;
-  MRegs<D> M;
-  M.load(problem_metric<D>(a, p));
   if (threadIdx.x < D) L.shift[threadIdx.x] = group_mean<D>(a, p, level - 1, gp)[threadIdx.x];
   __syncthreads();
   f32x16_t acc[Cov<D>::TILES];
-  zero_acc<D>(acc);
   {
+    SymAcc<D> sacc;
+    sacc.zero();
     float dpart[D / 8];
 #pragma unroll
     for (int e = 0; e < D / 8; ++e) dpart[e] = 0.f;
-    stats_range<T, D, kF16x2, true>(X, pos, inv_n, lb0, lb0 + lm, L.shift, ysc, st, acc, dpart);
+    sym_stats_range<T, D, true>(X, pos, inv_n, lb0, lb0 + lm, L.shift, ysc, st, sacc, dpart);
     reduce_dpart<D>(dpart, L.red, L.mu);
+    sym_to_regs<D>(sacc, inv_s2, st, acc);  // S_L, unscaled
   }
-  // keep S_L (unscaled) and its sum for the right child: S_L in the right child's covariance
-  // slot (each thread later reads back exactly the elements it wrote)
+  // keep S_L and its sum for the right child: S_L in the right child's covariance slot (each
+  // thread later reads back exactly the elements it wrote)
   if (rm >= 2) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-    for (int t = 0; t < Cov<D>::TILES; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        cov_r[((w * Cov<D>::TILES + t) * 16 + r) * 64 + lane] = acc[t][r] * inv_s2;
+    store_acc<D>(cov_r, acc);
     if (threadIdx.x < D) dsl[threadIdx.x] = L.mu[threadIdx.x];
   }
-  if (lm >= 2) split_group<T, D>(a, p, level, gl, lb0, lm, acc, inv_s2, L, M, cov_l, hist, sm);
+  if (lm >= 2) split_group<T, D>(a, p, level, gl, lb0, lm, acc, 1.f, L, cov_l, hist, sm);
   if (rm >= 2) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const float np = float(pm * kBlk);
@@ -1116,7 +1326,7 @@ __global__ __launch_bounds__(256, 2) void k_subtree_pair(ProblemArgs a, int leve
       L.mu[threadIdx.x] = -dsl[threadIdx.x];
     }
     __syncthreads();
-    split_group<T, D>(a, p, level, gr, rb0, rm, acc, 1.f, L, M, cov_r, hist, sm);
+    split_group<T, D>(a, p, level, gr, rb0, rm, acc, 1.f, L, cov_r, hist, sm);
   }
 }
 
@@ -1140,8 +1350,6 @@ __global__ __launch_bounds__(256, 2) void k_subtree_small(ProblemArgs a, int ls)
   const float* inv_n = a.inv_n + (size_t)p * a.N;
   const float ysc = a.yscale[2 * p], inv_s2 = a.yscale[2 * p + 1];
   for (int i = threadIdx.x; i < rm * kBlk; i += 256) spos[i] = pos[i];
-  MRegs<D> M;
-  M.load(problem_metric<D>(a, p));
   __syncthreads();
   for (int level = ls; level < a.L; ++level) {
     const int depth = level - ls;
@@ -1152,16 +1360,21 @@ __global__ __launch_bounds__(256, 2) void k_subtree_small(ProblemArgs a, int ls)
       if (threadIdx.x < D) L.shift[threadIdx.x] = parent_mean<D>(a, p, level, g)[threadIdx.x];
       __syncthreads();
       f32x16_t acc[Cov<D>::TILES];
-      zero_acc<D>(acc);
       {
+        SymAcc<D> sacc;
+        sacc.zero();
         float dpart[D / 8];
 #pragma unroll
         for (int e = 0; e < D / 8; ++e) dpart[e] = 0.f;
-        stats_range<T, D, kF16x2, true>(X, spos, inv_n, lb0, lb0 + m, L.shift, ysc, st, acc,
-                                         dpart);
+        sym_stats_range<T, D, true>(X, spos, inv_n, lb0, lb0 + m, L.shift, ysc, st, sacc, dpart);
         reduce_dpart<D>(dpart, L.red, L.mu);
+        sym_to_regs<D>(sacc, inv_s2, st, acc);
       }
-      group_direction<T, D>(acc, L, M, n, inv_s2, X, spos, inv_n, lb0 * kBlk);
+      // M is read (from L2) only for the power steps, so it holds no registers during the
+      // statistics
+      MRegs<D> M;
+      M.load(problem_metric<D>(a, p));
+      group_direction<T, D>(acc, L, M, n, 1.f, X, spos, inv_n, lb0 * kBlk);
       if (threadIdx.x < D) group_mean<D>(a, p, level, g)[threadIdx.x] = L.mu[threadIdx.x];
       float* proj = problem_proj(a, p, level);
       project_range<T, D>(X, spos, inv_n, lb0, lb0 + m, L.w, skeys, proj);
