@@ -402,14 +402,17 @@ BSA_DEV void sym_mfma(const StageLds<D, 2>& st, SymAcc<D>& acc) {
 }
 
 // Accumulate the chunks [blk0, blk1) with the fp16 two-term split (see stats_range).
+// sh_shift (LDS) receives the shift sh_val of the calling thread (threads < D) once the first
+// chunk's loads are in flight.
 template <typename T, int D, bool PREFETCH>
 BSA_DEV void sym_stats_range(const T* __restrict__ X, const int32_t* __restrict__ tokmap,
                              const float* __restrict__ inv_n, int blk0, int blk1,
-                             const float* sh_shift, float ysc, StageLds<D, 2>& st, SymAcc<D>& acc,
-                             float* dpart) {
-  if (blk0 >= blk1) return;
+                             float* sh_shift, float sh_val, float ysc, StageLds<D, 2>& st,
+                             SymAcc<D>& acc, float* dpart) {
   ChunkRegs<T, D> cur;
-  if (PREFETCH) stats_load<T, D>(X, tokmap, inv_n, blk0 * kBlk, cur);
+  if (PREFETCH && blk0 < blk1) stats_load<T, D>(X, tokmap, inv_n, blk0 * kBlk, cur);
+  if (threadIdx.x < D) sh_shift[threadIdx.x] = sh_val;
+  __syncthreads();
   for (int b = blk0; b < blk1; ++b) {
     if (!PREFETCH) stats_load<T, D>(X, tokmap, inv_n, b * kBlk, cur);
     stats_stage<T, D, kF16x2>(cur, sh_shift, ysc, st, dpart);
@@ -669,37 +672,46 @@ BSA_DEV void finish_stats(f32x16_t* acc, DirLds& L, int n, float acc_scale) {
 template <typename T, int D>
 BSA_DEV void power_direction(f32x16_t* acc, DirLds& L, const MRegs<D>& M, int n,
                              const T* __restrict__ X, const int32_t* __restrict__ tokmap,
-                             const float* __restrict__ inv_n, int pos0);
+                             const float* __restrict__ inv_n, int pos0, float y_first);
 
 template <typename T, int D>
 BSA_DEV void group_direction(f32x16_t* acc, DirLds& L, const MRegs<D>& M, int n, float acc_scale,
                              const T* __restrict__ X, const int32_t* __restrict__ tokmap,
-                             const float* __restrict__ inv_n, int pos0) {
+                             const float* __restrict__ inv_n, int pos0, float y_first) {
   finish_stats<D>(acc, L, n, acc_scale);
-  power_direction<T, D>(acc, L, M, n, X, tokmap, inv_n, pos0);
+  power_direction<T, D>(acc, L, M, n, X, tokmap, inv_n, pos0, y_first);
+}
+
+// The scaled input y = x inv_n of token tokmap[pos] at element threadIdx.x (threads < D), for a
+// caller that loads the first start candidate ahead of time.
+template <typename T, int D>
+BSA_DEV float first_candidate(const T* __restrict__ X, const int32_t* __restrict__ tokmap,
+                              const float* __restrict__ inv_n, int pos) {
+  if (threadIdx.x >= D) return 0.f;
+  const int tok = tokmap[pos];
+  return load_as_f32(X + (size_t)tok * D + threadIdx.x) * inv_n[tok];
 }
 
 // Given the centred covariance in acc and the mean in L.mu, find the split direction L.w.
+// y_first: first_candidate(X, tokmap, inv_n, pos0) of the calling thread.
 template <typename T, int D>
 BSA_DEV void power_direction(f32x16_t* acc, DirLds& L, const MRegs<D>& M, int n,
                              const T* __restrict__ X, const int32_t* __restrict__ tokmap,
-                             const float* __restrict__ inv_n, int pos0) {
+                             const float* __restrict__ inv_n, int pos0, float y_first) {
   const int tid = threadIdx.x;
   // start vector: the first position (smallest token id) whose centred vector is non-zero
   bool found = false;
   for (int p = pos0; p < pos0 + n; ++p) {
-    const int tok = tokmap[p];
-    if (tid == 0) L.flag = 0;
-    __syncthreads();
+    float e = 0.f;
     if (tid < D) {
-      const float e = load_as_f32(X + (size_t)tok * D + tid) * inv_n[tok] - L.mu[tid];
+      const float y = p == pos0 ? y_first : first_candidate<T, D>(X, tokmap, inv_n, p);
+      e = y - L.mu[tid];
       L.e0[tid] = e;
-      if (e != 0.f) L.flag = 1;
     }
-    __syncthreads();
-    found = L.flag != 0;
-    __syncthreads();
-    if (found) break;
+    if (__syncthreads_or(e != 0.f)) {  // uniform: a workgroup-wide vote
+      found = true;
+      break;
+    }
   }
   if (!found) {
     if (tid < D) L.w[tid] = 0.f;
@@ -1113,14 +1125,14 @@ __global__ __launch_bounds__(256, 3) void k_wide_stats(ProblemArgs a) {
   const T* X = problem_x<T, D>(a, p);
   const int32_t* tokmap = problem_pos(a, p);
   const float* inv_n = a.inv_n + (size_t)p * a.N;
-  if (threadIdx.x < D) shift[threadIdx.x] = parent_mean<D>(a, p, a.level, g)[threadIdx.x];
-  __syncthreads();
+  const float shv = threadIdx.x < D ? parent_mean<D>(a, p, a.level, g)[threadIdx.x] : 0.f;
   SymAcc<D> acc;
   acc.zero();
   float dpart[D / 8];
 #pragma unroll
   for (int e = 0; e < D / 8; ++e) dpart[e] = 0.f;
-  sym_stats_range<T, D, true>(X, tokmap, inv_n, sb0, sb1, shift, a.yscale[2 * p], st, acc, dpart);
+  sym_stats_range<T, D, true>(X, tokmap, inv_n, sb0, sb1, shift, shv, a.yscale[2 * p], st, acc,
+                              dpart);
   reduce_dpart<D>(dpart, red, dsum);
   // the slot holds the full symmetric D x D sum (scaled by s^2) in register dump order, then the
   // D sums of d
@@ -1154,6 +1166,7 @@ __global__ __launch_bounds__(256, 2) void k_wide_dir(ProblemArgs a) {
     const int g = a.left_only ? 2 * par + child : par;
     int b0, m;
     if (group_geom(a.nb, a.level, g, b0, m) != kGroupSplit) return;
+    const float y_first = first_candidate<T, D>(X, pos, inv_n, b0 * kBlk);
     f32x16_t acc[Cov<D>::TILES];
     zero_acc<D>(acc);
     const float* base = a.partial + ((size_t)p * kSlots + par * a.slices) * (D * D + D);
@@ -1186,7 +1199,7 @@ __global__ __launch_bounds__(256, 2) void k_wide_dir(ProblemArgs a) {
     __syncthreads();
     finish_stats<D>(acc, L, m * kBlk, 1.f);
     if (a.cov_cur) store_acc<D>(a.cov_cur + ((size_t)p * a.gw + g) * D * D, acc);
-    power_direction<T, D>(acc, L, M, m * kBlk, X, pos, inv_n, b0 * kBlk);
+    power_direction<T, D>(acc, L, M, m * kBlk, X, pos, inv_n, b0 * kBlk, y_first);
     if (threadIdx.x < D) {
       group_mean<D>(a, p, a.level, g)[threadIdx.x] = L.mu[threadIdx.x];
       a.wdir[((size_t)p * a.G + g) * D + threadIdx.x] = L.w[threadIdx.x];
@@ -1236,7 +1249,7 @@ __global__ __launch_bounds__(1024) void k_wide_split(ProblemArgs a) {
 template <typename T, int D>
 BSA_DEV void split_group(const ProblemArgs& a, int p, int level, int g, int b0, int m,
                          f32x16_t* acc, float acc_scale, DirLds& L, float* cov_out, int* hist,
-                         int* sm) {
+                         int* sm, float y_first) {
   const T* X = problem_x<T, D>(a, p);
   int32_t* pos = problem_pos(a, p);
   int32_t* tmp = a.tmp + (size_t)p * a.N;
@@ -1249,7 +1262,7 @@ BSA_DEV void split_group(const ProblemArgs& a, int p, int level, int g, int b0, 
     // M is read (from L2) for the power steps only, so it holds no registers elsewhere
     MRegs<D> M;
     M.load(problem_metric<D>(a, p));
-    power_direction<T, D>(acc, L, M, n, X, pos, inv_n, b0 * kBlk);
+    power_direction<T, D>(acc, L, M, n, X, pos, inv_n, b0 * kBlk, y_first);
   }
   if (threadIdx.x < D) group_mean<D>(a, p, level, g)[threadIdx.x] = L.mu[threadIdx.x];
   project_range<T, D>(X, pos, inv_n, b0, b0 + m, L.w, keys, problem_proj(a, p, level));
@@ -1291,8 +1304,9 @@ __global__ __launch_bounds__(256, 2) void k_subtree_pair(ProblemArgs a, int leve
   float* cov_l = a.cov_cur + ((size_t)p * cov_g + gl) * D * D;
   float* cov_r = a.cov_cur + ((size_t)p * cov_g + gr) * D * D;
   const float* cov_p = a.cov_prev + ((size_t)p * cov_g + gp) * D * D;
-  if (threadIdx.x < D) L.shift[threadIdx.x] = group_mean<D>(a, p, level - 1, gp)[threadIdx.x];
-  __syncthreads();
+  const float shv = threadIdx.x < D ? group_mean<D>(a, p, level - 1, gp)[threadIdx.x] : 0.f;
+  const float yl = first_candidate<T, D>(X, pos, inv_n, lb0 * kBlk);
+  const float yr = first_candidate<T, D>(X, pos, inv_n, rb0 * kBlk);
   f32x16_t acc[Cov<D>::TILES];
   {
     SymAcc<D> sacc;
@@ -1300,7 +1314,7 @@ __global__ __launch_bounds__(256, 2) void k_subtree_pair(ProblemArgs a, int leve
     float dpart[D / 8];
 #pragma unroll
     for (int e = 0; e < D / 8; ++e) dpart[e] = 0.f;
-    sym_stats_range<T, D, true>(X, pos, inv_n, lb0, lb0 + lm, L.shift, ysc, st, sacc, dpart);
+    sym_stats_range<T, D, true>(X, pos, inv_n, lb0, lb0 + lm, L.shift, shv, ysc, st, sacc, dpart);
     reduce_dpart<D>(dpart, L.red, L.mu);
     sym_to_regs<D>(sacc, inv_s2, st, acc);  // S_L, unscaled
   }
@@ -1310,7 +1324,7 @@ __global__ __launch_bounds__(256, 2) void k_subtree_pair(ProblemArgs a, int leve
     store_acc<D>(cov_r, acc);
     if (threadIdx.x < D) dsl[threadIdx.x] = L.mu[threadIdx.x];
   }
-  if (lm >= 2) split_group<T, D>(a, p, level, gl, lb0, lm, acc, 1.f, L, cov_l, hist, sm);
+  if (lm >= 2) split_group<T, D>(a, p, level, gl, lb0, lm, acc, 1.f, L, cov_l, hist, sm, yl);
   if (rm >= 2) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const float np = float(pm * kBlk);
@@ -1326,7 +1340,7 @@ __global__ __launch_bounds__(256, 2) void k_subtree_pair(ProblemArgs a, int leve
       L.mu[threadIdx.x] = -dsl[threadIdx.x];
     }
     __syncthreads();
-    split_group<T, D>(a, p, level, gr, rb0, rm, acc, 1.f, L, cov_r, hist, sm);
+    split_group<T, D>(a, p, level, gr, rb0, rm, acc, 1.f, L, cov_r, hist, sm, yr);
   }
 }
 
@@ -1357,24 +1371,25 @@ __global__ __launch_bounds__(256, 2) void k_subtree_small(ProblemArgs a, int ls)
       int b0, m;
       if (group_geom(a.nb, level, g, b0, m) != kGroupSplit) continue;
       const int lb0 = b0 - rb0, n = m * kBlk;
-      if (threadIdx.x < D) L.shift[threadIdx.x] = parent_mean<D>(a, p, level, g)[threadIdx.x];
-      __syncthreads();
+      const float shv = threadIdx.x < D ? parent_mean<D>(a, p, level, g)[threadIdx.x] : 0.f;
+      const float y_first = first_candidate<T, D>(X, spos, inv_n, lb0 * kBlk);
       f32x16_t acc[Cov<D>::TILES];
+      // M is read (from L2) only for the power steps, so it holds no registers during the
+      // statistics
+      MRegs<D> M;
       {
         SymAcc<D> sacc;
         sacc.zero();
         float dpart[D / 8];
 #pragma unroll
         for (int e = 0; e < D / 8; ++e) dpart[e] = 0.f;
-        sym_stats_range<T, D, true>(X, spos, inv_n, lb0, lb0 + m, L.shift, ysc, st, sacc, dpart);
+        sym_stats_range<T, D, true>(X, spos, inv_n, lb0, lb0 + m, L.shift, shv, ysc, st, sacc,
+                                    dpart);
         reduce_dpart<D>(dpart, L.red, L.mu);
         sym_to_regs<D>(sacc, inv_s2, st, acc);
       }
-      // M is read (from L2) only for the power steps, so it holds no registers during the
-      // statistics
-      MRegs<D> M;
-      M.load(problem_metric<D>(a, p));
-      group_direction<T, D>(acc, L, M, n, 1.f, X, spos, inv_n, lb0 * kBlk);
+      M.load(problem_metric<D>(a, p));  // overlaps the centring in group_direction
+      group_direction<T, D>(acc, L, M, n, 1.f, X, spos, inv_n, lb0 * kBlk, y_first);
       if (threadIdx.x < D) group_mean<D>(a, p, level, g)[threadIdx.x] = L.mu[threadIdx.x];
       float* proj = problem_proj(a, p, level);
       project_range<T, D>(X, spos, inv_n, lb0, lb0 + m, L.w, skeys, proj);
