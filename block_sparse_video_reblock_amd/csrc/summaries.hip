@@ -64,13 +64,20 @@ __global__ __launch_bounds__(256) void k_colsum(const T* __restrict__ x, int N, 
   }
 }
 
-__global__ void k_colsum_finish(const float* __restrict__ partial, int nch, int N, int D,
-                                float* __restrict__ out) {
-  const int h = blockIdx.x, d = threadIdx.x;
-  if (d >= D) return;
+__global__ __launch_bounds__(256) void k_colsum_finish(const float* __restrict__ partial, int nch,
+                                                       int N, int D, float* __restrict__ out) {
+  // D columns x (256 / D) interleaved chunk strides, then a fixed-order sum of the strides
+  __shared__ float red[256];
+  const int h = blockIdx.x, R = 256 / D, d = threadIdx.x % D, r = threadIdx.x / D;
   float s = 0.f;
-  for (int c = 0; c < nch; ++c) s += partial[((size_t)h * nch + c) * D + d];
-  out[(size_t)h * D + d] = s / float(N);
+  for (int c = r; c < nch; c += R) s += partial[((size_t)h * nch + c) * D + d];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float t = 0.f;
+    for (int i = 0; i < R; ++i) t += red[i * D + threadIdx.x];
+    out[(size_t)h * D + threadIdx.x] = t / float(N);
+  }
 }
 
 // ----------------------------------------------------------- per key block summaries
@@ -341,7 +348,7 @@ hipError_t launch_anchor(bool bf16, const void* x, int H, int N, int D, float* p
     k_colsum<uint16_t><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(x), N, D, partial);
   else
     k_colsum<float><<<grid, 256, 0, s>>>(static_cast<const float*>(x), N, D, partial);
-  k_colsum_finish<<<H, 128, 0, s>>>(partial, nch, N, D, anchor);
+  k_colsum_finish<<<H, 256, 0, s>>>(partial, nch, N, D, anchor);
   return hipGetLastError();
 }
 
