@@ -34,6 +34,23 @@ BSA_DEV bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 // word 3 of a raw buffer resource: 32-bit data format (untyped loads need a nonzero format)
 constexpr int kBufferDword3 = 0x00020000;
 
+template <bool B>
+struct KindTag {
+  static constexpr bool value = B;
+};
+
+// sum of the eight bf16 values of an MFMA operand, in fp32 (v_dot2_f32_bf16 with ones)
+BSA_DEV float row_sum_bf16(const bf16x8_t& p) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf2;
+  const uint4 u = __builtin_bit_cast(uint4, p);
+  const bf2 one = __builtin_bit_cast(bf2, 0x3F803F80u);
+  float a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.x), one, 0.f, false);
+  float b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.y), one, 0.f, false);
+  a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.z), one, a, false);
+  b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.w), one, b, false);
+  return a + b;
+}
+
 // Running-max slack: the online softmax keeps a stale maximum until a row's new maximum exceeds
 // it by more than this (log2 units), so probabilities stay below 2^8 and the accumulator is
 // rescaled only when the maximum really moves.  The result is the same softmax.
@@ -118,150 +135,144 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.f, 0.f};
 
-  // work items of this wave: it = wave, wave + 4, ...; each is processed as two 32-key
-  // halves, and the keys of the next half are loaded while the current one finishes
+  // work items of this wave: it = wave, wave + 4, ... over the exact tiles and then the
+  // summary tiles; each is processed as two 32-key halves, and the keys of the next half are
+  // loaded while the current one finishes.  The two kinds run in separate loops (compiled
+  // separately), so neither carries the other's arithmetic or register copies.
   const int n_items = n_exact + n_comp;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const uint4 *kb = nullptr, *vb = nullptr;
-  int key0 = 0;
-  auto tile_ptrs = [&](int it, const uint4*& kp, const uint4*& vp, int& k0) {
-    if (it < n_exact) {
-      const size_t blk = (size_t)h * nb + list[it];
-      kp = ksw + blk * 1024;
-      vp = vsw + blk * 1024;
-      k0 = 0;
-    } else {
-      const int tau = it - n_exact;
-      const size_t blk = (size_t)h * ntiles + tau;
-      kp = ktsw + blk * 1024;
-      vp = vtsw + blk * 1024;
-      k0 = tau * 64;
-    }
-  };
-  uint4 kr[8];
-  if (wv < n_items) {
-    tile_ptrs(wv, kb, vb, key0);
+  auto run = [&](auto kind, int it, int it_end) {
+    constexpr bool EXACT = decltype(kind)::value;
+    if (it >= it_end) return;
+    auto tile_ptrs = [&](int t, const uint4*& kp, const uint4*& vp, int& k0) {
+      if (EXACT) {
+        const size_t blk = (size_t)h * nb + list[t];
+        kp = ksw + blk * 1024;
+        vp = vsw + blk * 1024;
+        k0 = 0;
+      } else {
+        const int tau = t - n_exact;
+        const size_t blk = (size_t)h * ntiles + tau;
+        kp = ktsw + blk * 1024;
+        vp = vtsw + blk * 1024;
+        k0 = tau * 64;
+      }
+    };
+    const uint4 *kb, *vb;
+    int key0;
+    tile_ptrs(it, kb, vb, key0);
+    uint4 kr[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) kr[c] = kb[c * 64 + lane];
-  }
-  int it = wv, hh = 0;
+    int hh = 0;
 #pragma unroll 1
-  while (it < n_items) {
-    const bool exact = it < n_exact;
-    // the next half of this wave (scalar work, ahead of the vector code); past the last item
-    // it points at a valid tile, and the keys loaded from there go unused
-    int it_n = it, hh_n = hh + 1;
-    const uint4 *kb_n = kb, *vb_n = vb;
-    int key0_n = key0;
-    if (hh_n == 2) {
-      it_n += 4;
-      hh_n = 0;
-      if (it_n < n_items) tile_ptrs(it_n, kb_n, vb_n, key0_n);
-    }
-    // keep the query operands in LDS: re-read them per use instead of pinning 64 registers
-    asm volatile("" ::: "memory");
-    // S^T[n]: lane holds query 32n + l32 and keys 32hh + 8(r/4) + 4g + (r%4), r = 0..15
-    f32x16_t s[2];
+    while (it < it_end) {
+      // the next half of this wave (scalar work, ahead of the vector code); past the last
+      // item it points at a valid tile, and the keys loaded from there go unused
+      int it_n = it, hh_n = hh + 1;
+      const uint4 *kb_n = kb, *vb_n = vb;
+      int key0_n = key0;
+      if (hh_n == 2) {
+        it_n += 4;
+        hh_n = 0;
+        if (it_n < it_end) tile_ptrs(it_n, kb_n, vb_n, key0_n);
+      }
+      // keep the query operands in LDS: re-read them per use instead of pinning 64 registers
+      asm volatile("" ::: "memory");
+      // S^T[n]: lane holds query 32n + l32 and keys 32hh + 8(r/4) + 4g + (r%4), r = 0..15
+      f32x16_t s[2];
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      f32x16_t t;
+      for (int n = 0; n < 2; ++n) {
+        f32x16_t t;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) t[r] = 0.f;
+        for (int r = 0; r < 16; ++r) t[r] = 0.f;
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[c]), as_bf16x8(sq[n][c][lane]),
-                                                    t, 0, 0, 0);
-      s[n] = t;
-    }
-    uint4 vr[8];
+        for (int c = 0; c < 8; ++c)
+          t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[c]),
+                                                      as_bf16x8(sq[n][c][lane]), t, 0, 0, 0);
+        s[n] = t;
+      }
+      uint4 vr[8];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) vr[a * 2 + cc] = vb[(a * 4 + 2 * hh + cc) * 64 + lane];
-    // logits in log2 units: s * scale_log2, plus bias * log2 e for summary rows (-inf if
-    // the block is selected or past the end)
+        for (int cc = 0; cc < 2; ++cc) vr[a * 2 + cc] = vb[(a * 4 + 2 * hh + cc) * 64 + lane];
+      // P^T in bf16: the B operand of key chunk c = 2hh + cc is registers 8cc..8cc+8 of S^T[n]
+      bf16x8_t pb[2][2];
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      float mx = -INFINITY;
-      if (exact) {
+      for (int n = 0; n < 2; ++n) {
+        // logits in log2 units: s * scale_log2, plus bias * log2 e for summary rows (-inf if
+        // the block is selected or past the end)
+        float mx = -INFINITY;
+        if (EXACT) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[n][r]);
-        mx *= scale_log2;
-      } else {
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[n][r]);
+          mx *= scale_log2;
+        } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float4 b4 =
-              *reinterpret_cast<const float4*>(&sbias[key0 + 32 * hh + 8 * j + 4 * g]);
-          const float bj[4] = {b4.x, b4.y, b4.z, b4.w};
+          for (int j = 0; j < 4; ++j) {
+            const float4 b4 =
+                *reinterpret_cast<const float4*>(&sbias[key0 + 32 * hh + 8 * j + 4 * g]);
+            const float bj[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            s[n][4 * j + u] = fmaf(s[n][4 * j + u], scale_log2, bj[u]);
-            mx = fmaxf(mx, s[n][4 * j + u]);
+            for (int u = 0; u < 4; ++u) {
+              s[n][4 * j + u] = fmaf(s[n][4 * j + u], scale_log2, bj[u]);
+              mx = fmaxf(mx, s[n][4 * j + u]);
+            }
           }
         }
-      }
-      mx = xor32_max(mx);
-      // lazy rescale: move the running max only when it grows by more than kMaxSlack
-      const bool grow = mx > m_run[n] + kMaxSlack;
-      if (__any(grow)) {
-        const float m_new = grow ? mx : m_run[n];
-        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[n] - m_new) : 1.f;
-        m_run[n] = m_new;
-        l_run[n] *= alpha;
+        mx = xor32_max(mx);
+        // lazy rescale: move the running max only when it grows by more than kMaxSlack
+        const bool grow = mx > m_run[n] + kMaxSlack;
+        if (__any(grow)) {
+          const float m_new = grow ? mx : m_run[n];
+          const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[n] - m_new) : 1.f;
+          m_run[n] = m_new;
+          l_run[n] *= alpha;
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+          for (int a = 0; a < 4; ++a)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[a][n][r] *= alpha;
-      }
-      const float m_use = (m_run[n] == -INFINITY) ? 0.f : m_run[n];
-      float rs4[4] = {0.f, 0.f, 0.f, 0.f};  // four short chains instead of one of 16
-      if (exact) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pr = __builtin_amdgcn_exp2f(fmaf(s[n][r], scale_log2, -m_use));
-          s[n][r] = pr;
-          rs4[r & 3] += pr;
+            for (int r = 0; r < 16; ++r) acc[a][n][r] *= alpha;
         }
-      } else {
+        const float m_use = (m_run[n] == -INFINITY) ? 0.f : m_run[n];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pr = __builtin_amdgcn_exp2f(s[n][r] - m_use);
-          s[n][r] = pr;
-          rs4[r & 3] += pr;
-        }
+        for (int r = 0; r < 16; ++r)
+          s[n][r] = __builtin_amdgcn_exp2f(EXACT ? fmaf(s[n][r], scale_log2, -m_use)
+                                                 : s[n][r] - m_use);
+        pb[0][n] = pack8(s[n], 0);
+        pb[1][n] = pack8(s[n], 8);
+        // row sum of the bf16 probabilities the value products use (bf16 dot products with
+        // ones, fp32 accumulation)
+        l_run[n] += xor32_sum(row_sum_bf16(pb[0][n]) + row_sum_bf16(pb[1][n]));
       }
-      l_run[n] += xor32_sum((rs4[0] + rs4[1]) + (rs4[2] + rs4[3]));
+      // the next half's keys load during the value products of this one (buffer loads:
+      // plain loads here would be merged with the ones before the loop into one load at the
+      // loop head, after the wait)
+      const __amdgpu_buffer_rsrc_t rk =
+          __builtin_amdgcn_make_buffer_rsrc((void*)kb_n, 0, 1024 * 16, kBufferDword3);
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        kr[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rk, lane * 16, (hh_n * 8 + c) * 1024, 0));
+      // O^T[d chunk a][n] += V^T[a][key chunk c] P^T[c][n]
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+            acc[a][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vr[a * 2 + cc]),
+                                                                pb[cc][n], acc[a][n], 0, 0, 0);
+      it = it_n;
+      hh = hh_n;
+      kb = kb_n;
+      vb = vb_n;
+      key0 = key0_n;
     }
-    // P^T in bf16: the B operand of key chunk c = 2hh + cc is registers 8cc..8cc+8 of S^T[n]
-    bf16x8_t pb[2][2];
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-      for (int n = 0; n < 2; ++n) pb[cc][n] = pack8(s[n], 8 * cc);
-    // the next half's keys load during the value products of this one (buffer loads: plain
-    // loads here would be merged with the ones before the loop into one load at the loop head,
-    // after the wait)
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc((void*)kb_n, 0, 1024 * 16, kBufferDword3);
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-      kr[c] = __builtin_bit_cast(
-          uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, ((hh_n * 8 + c) * 64 + lane) * 16, 0, 0));
-    // O^T[d chunk a][n] += V^T[a][key chunk c] P^T[c][n]
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-      for (int n = 0; n < 2; ++n)
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-          acc[a][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vr[a * 2 + cc]),
-                                                              pb[cc][n], acc[a][n], 0, 0, 0);
-    it = it_n;
-    hh = hh_n;
-    kb = kb_n;
-    vb = vb_n;
-    key0 = key0_n;
-  }
+  };
+  run(KindTag<true>{}, wv, n_exact);
+  // the first summary item of this wave in the same round-robin sequence
+  run(KindTag<false>{}, wv + 4 * ((max(n_exact - wv, 0) + 3) / 4), n_items);
 
   // merge the four waves' online-softmax states
   if (g == 0) {
