@@ -39,16 +39,16 @@ struct KindTag {
   static constexpr bool value = B;
 };
 
-// sum of the eight bf16 values of an MFMA operand, in fp32 (v_dot2_f32_bf16 with ones)
-BSA_DEV float row_sum_bf16(const bf16x8_t& p) {
+// acc + the sum of the eight bf16 values of an MFMA operand, in fp32 (v_dot2_f32_bf16 with
+// ones)
+BSA_DEV float row_sum_bf16(const bf16x8_t& p, float acc) {
   typedef __attribute__((ext_vector_type(2))) __bf16 bf2;
   const uint4 u = __builtin_bit_cast(uint4, p);
   const bf2 one = __builtin_bit_cast(bf2, 0x3F803F80u);
-  float a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.x), one, 0.f, false);
-  float b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.y), one, 0.f, false);
-  a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.z), one, a, false);
-  b = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.w), one, b, false);
-  return a + b;
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.x), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.y), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.z), one, acc, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, u.w), one, acc, false);
 }
 
 // Running-max slack: the online softmax keeps a stale maximum until a row's new maximum exceeds
@@ -133,6 +133,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][n][r] = 0.f;
   float m_run[2] = {-INFINITY, -INFINITY};
+  // this lane's part of the row sums (its half of every key chunk); the two halves of a row
+  // are added at the end
   float l_run[2] = {0.f, 0.f};
 
   // work items of this wave: it = wave, wave + 4, ... over the exact tiles and then the
@@ -180,9 +182,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
       // keep the query operands in LDS: re-read them per use instead of pinning 64 registers
       asm volatile("" ::: "memory");
       // S^T[n]: lane holds query 32n + l32 and keys 32hh + 8(r/4) + 4g + (r%4), r = 0..15
-      f32x16_t s[2];
-#pragma unroll
-      for (int n = 0; n < 2; ++n) {
+      auto scores = [&](int n) {
         f32x16_t t;
 #pragma unroll
         for (int r = 0; r < 16; ++r) t[r] = 0.f;
@@ -190,23 +190,15 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
         for (int c = 0; c < 8; ++c)
           t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[c]),
                                                       as_bf16x8(sq[n][c][lane]), t, 0, 0, 0);
-        s[n] = t;
-      }
-      uint4 vr[8];
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) vr[a * 2 + cc] = vb[(a * 4 + 2 * hh + cc) * 64 + lane];
-      // P^T in bf16: the B operand of key chunk c = 2hh + cc is registers 8cc..8cc+8 of S^T[n]
-      bf16x8_t pb[2][2];
-#pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        // logits in log2 units: s * scale_log2, plus bias * log2 e for summary rows (-inf if
-        // the block is selected or past the end)
+        return t;
+      };
+      // logits in log2 units (s * scale_log2, plus bias * log2 e for summary rows, -inf if the
+      // block is selected or past the end); returns the max the exponentials subtract
+      auto row_max = [&](int n, f32x16_t& t) {
         float mx = -INFINITY;
         if (EXACT) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[n][r]);
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, t[r]);
           mx *= scale_log2;
         } else {
 #pragma unroll
@@ -216,8 +208,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
             const float bj[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-              s[n][4 * j + u] = fmaf(s[n][4 * j + u], scale_log2, bj[u]);
-              mx = fmaxf(mx, s[n][4 * j + u]);
+              t[4 * j + u] = fmaf(t[4 * j + u], scale_log2, bj[u]);
+              mx = fmaxf(mx, t[4 * j + u]);
             }
           }
         }
@@ -234,17 +226,46 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][n][r] *= alpha;
         }
-        const float m_use = (m_run[n] == -INFINITY) ? 0.f : m_run[n];
+        return (m_run[n] == -INFINITY) ? 0.f : m_run[n];
+      };
+      // P^T in bf16: the B operand of key chunk c = 2hh + cc is registers 8cc..8cc+8 of S^T[n]
+      bf16x8_t pb[2][2];
+      auto probs = [&](int n, f32x16_t& t, float m_use) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          s[n][r] = __builtin_amdgcn_exp2f(EXACT ? fmaf(s[n][r], scale_log2, -m_use)
-                                                 : s[n][r] - m_use);
-        pb[0][n] = pack8(s[n], 0);
-        pb[1][n] = pack8(s[n], 8);
+          t[r] = __builtin_amdgcn_exp2f(EXACT ? fmaf(t[r], scale_log2, -m_use) : t[r] - m_use);
+        pb[0][n] = pack8(t, 0);
+        pb[1][n] = pack8(t, 8);
         // row sum of the bf16 probabilities the value products use (bf16 dot products with
         // ones, fp32 accumulation)
-        l_run[n] += xor32_sum(row_sum_bf16(pb[0][n]) + row_sum_bf16(pb[1][n]));
-      }
+        l_run[n] = row_sum_bf16(pb[1][n], row_sum_bf16(pb[0][n], l_run[n]));
+      };
+      uint4 vr[8];
+      // O^T[d chunk a][n] += V^T[a][key chunk c] P^T[c][n]
+      auto values = [&](int n) {
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+            acc[a][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vr[a * 2 + cc]),
+                                                                pb[cc][n], acc[a][n], 0, 0, 0);
+      };
+      // order: the score products of rows 32..63 run while the vector unit exponentiates rows
+      // 0..31, and the value products of rows 0..31 while it exponentiates rows 32..63
+      f32x16_t s0 = scores(0);
+      const float m0 = row_max(0, s0);
+      f32x16_t s1 = scores(1);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) vr[a * 2 + cc] = vb[(a * 4 + 2 * hh + cc) * 64 + lane];
+      probs(0, s0, m0);
+      // (an empty use keeps the exponentials of rows 0..31 ahead of the branch below, in the
+      // block of the score products they overlap)
+      asm volatile("" ::"v"(pb[0][0]), "v"(pb[1][0]));
+      const float m1 = row_max(1, s1);
+      values(0);
+      probs(1, s1, m1);
       // the next half's keys load during the value products of this one (buffer loads:
       // plain loads here would be merged with the ones before the loop into one load at the
       // loop head, after the wait)
@@ -254,15 +275,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
       for (int c = 0; c < 8; ++c)
         kr[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                               rk, lane * 16, (hh_n * 8 + c) * 1024, 0));
-      // O^T[d chunk a][n] += V^T[a][key chunk c] P^T[c][n]
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-#pragma unroll
-          for (int a = 0; a < 4; ++a)
-            acc[a][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vr[a * 2 + cc]),
-                                                                pb[cc][n], acc[a][n], 0, 0, 0);
+      values(1);
       it = it_n;
       hh = hh_n;
       kb = kb_n;
@@ -275,6 +288,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
   run(KindTag<false>{}, wv + 4 * ((max(n_exact - wv, 0) + 3) / 4), n_items);
 
   // merge the four waves' online-softmax states
+#pragma unroll
+  for (int n = 0; n < 2; ++n) l_run[n] = xor32_sum(l_run[n]);
   if (g == 0) {
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
