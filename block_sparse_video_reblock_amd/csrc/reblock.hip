@@ -940,40 +940,49 @@ __global__ __launch_bounds__(256) void k_norms_bf16(ProblemArgs a, const uint16_
     for (int c = 0; c < 8; ++c)
       mreg[s][c] = lds_bf16x8(Ms + (size_t)s * D * D + (32 * w + l32) * D + 16 * c + 8 * g);
   const int t0 = chunk * kNormTok, t_end = min(a.N, t0 + kNormTok);  // N is a multiple of 64
-  // tile loads: piece q = tid + 256 i (i < 4) is token q / 16, elements 8 (q % 16) .. + 8
-  uint4 nxt[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    nxt[i] = *reinterpret_cast<const uint4*>(X + (size_t)t0 * D + (size_t)(tid + 256 * i) * 8);
+  // tile loads: piece q = tid + 256 i (i < 4) is token q / 16, elements 8 (q % 16) .. + 8.
+  // The next tile is loaded while the current one is used; after the last tile the loads
+  // repeat it (valid memory, unused), so that they need no branch.
+  const uint4* xv = reinterpret_cast<const uint4*>(X) + tid;
+  uint4 n0 = xv[(size_t)t0 * 16], n1 = xv[(size_t)t0 * 16 + 256], n2 = xv[(size_t)t0 * 16 + 512],
+        n3 = xv[(size_t)t0 * 16 + 768];
   const int d2 = lane;  // this thread's element pair (2 d2, 2 d2 + 1) for the sums of y
   float ys0 = 0.f, ys1 = 0.f, ym = 0.f;
   for (int c0 = t0; c0 < t_end; c0 += kNormTile) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = tid + 256 * i;
-      *reinterpret_cast<uint4*>(&xs[q >> 4][8 * (q & 15)]) = nxt[i];
-    }
+    *reinterpret_cast<uint4*>(&xs[tid >> 4][8 * (tid & 15)]) = n0;
+    *reinterpret_cast<uint4*>(&xs[(tid >> 4) + 16][8 * (tid & 15)]) = n1;
+    *reinterpret_cast<uint4*>(&xs[(tid >> 4) + 32][8 * (tid & 15)]) = n2;
+    *reinterpret_cast<uint4*>(&xs[(tid >> 4) + 48][8 * (tid & 15)]) = n3;
     __syncthreads();
-    if (c0 + kNormTile < t_end) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        nxt[i] = *reinterpret_cast<const uint4*>(X + (size_t)(c0 + kNormTile) * D +
-                                                 (size_t)(tid + 256 * i) * 8);
+    {
+      const size_t cn = (size_t)(c0 + kNormTile < t_end ? c0 + kNormTile : c0) * 16;
+      n0 = xv[cn];
+      n1 = xv[cn + 256];
+      n2 = xv[cn + 512];
+      n3 = xv[cn + 768];
     }
+    // tokens l32 and 32 + l32: two independent accumulation chains, interleaved
+    f32x16_t acc0, acc1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      acc0[r] = 0.f;
+      acc1[r] = 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const bf16x8_t x0 = lds_bf16x8(&xs[l32][16 * c + 8 * g]);
+      const bf16x8_t x1 = lds_bf16x8(&xs[32 + l32][16 * c + 8 * g]);
+#pragma unroll
+      for (int s = 0; s < 3; ++s) {
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mreg[s][c], x0, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mreg[s][c], x1, acc1, 0, 0, 0);
+      }
+    }
+    // lane holds (M x_tok)[b] for b = 32w + 8j + 4g + i
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int tok = 32 * h + l32;
-      f32x16_t acc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const bf16x8_t xb = lds_bf16x8(&xs[tok][16 * c + 8 * g]);
-#pragma unroll
-        for (int s = 0; s < 3; ++s)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mreg[s][c], xb, acc, 0, 0, 0);
-      }
-      // lane holds (M x_tok)[b] for b = 32w + 8j + 4g + i
+      const f32x16_t& acc = h ? acc1 : acc0;
       float part = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -988,8 +997,8 @@ __global__ __launch_bounds__(256) void k_norms_bf16(ProblemArgs a, const uint16_
     }
     __syncthreads();
     if (tid < kNormTile) {
-      const float n2 = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
-      const float inv = n2 > 0.f ? 1.f / sqrtf(n2) : 0.f;
+      const float n2v = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+      const float inv = n2v > 0.f ? 1.f / sqrtf(n2v) : 0.f;
       s_inv[tid] = inv;
       inv_n_out[(size_t)p * a.N + c0 + tid] = inv;
     }
@@ -1070,6 +1079,8 @@ __global__ __launch_bounds__(256) void k_root_mean(const float* __restrict__ ysu
   __shared__ float s_max[4];
   const int p = blockIdx.x, d = threadIdx.x % D, r = threadIdx.x / D;
   float s = 0.f;
+  // (unrolled so that the loads are in flight together; the additions keep their order)
+#pragma unroll 8
   for (int c = r; c < nch; c += R) s += ysum[((size_t)p * nch + c) * D + d];
   part[r][d] = s;
   float m = 0.f;
