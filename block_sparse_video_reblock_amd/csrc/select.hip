@@ -65,26 +65,24 @@ __global__ __launch_bounds__(256) void k_block_scores(const float* __restrict__ 
                                                       float scale, float* __restrict__ S) {
   // one 64 x 64 tile of S per workgroup; wave w computes the 32 x 32 sub-tile (w / 2, w % 2)
   // with v_mfma_f32_32x32x2f32 (fp32 products and sums) over pairs of dimensions
-  __shared__ float sq[64][129];
-  __shared__ float sk[64][129];
+  // rows padded to 132 floats: 16-byte aligned for the tile stores, and the MFMA operand reads
+  // (lane: row lane % 32, column lane / 32) fall into 2-way bank groups
+  __shared__ __align__(16) float sq[64][132];
+  __shared__ __align__(16) float sk[64][132];
   const int ti = blockIdx.x, tj = blockIdx.y, h = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   constexpr int V = D / 4;  // float4 per row
 #pragma unroll
   for (int e = tid; e < 64 * V; e += 256) {
     const int r = e / V, c = e % V;
+    // rows past nb read row nb - 1 (valid memory) and are zeroed after the load
     const int i = ti * 64 + r, j = tj * 64 + r;
-    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4 a = i < nb ? reinterpret_cast<const float4*>(qm + ((size_t)h * nb + i) * D)[c] : zero;
-    const float4 b = j < nb ? reinterpret_cast<const float4*>(km + ((size_t)h * nb + j) * D)[c] : zero;
-    sq[r][4 * c] = a.x;
-    sq[r][4 * c + 1] = a.y;
-    sq[r][4 * c + 2] = a.z;
-    sq[r][4 * c + 3] = a.w;
-    sk[r][4 * c] = b.x;
-    sk[r][4 * c + 1] = b.y;
-    sk[r][4 * c + 2] = b.z;
-    sk[r][4 * c + 3] = b.w;
+    float4 a = reinterpret_cast<const float4*>(qm + ((size_t)h * nb + min(i, nb - 1)) * D)[c];
+    float4 b = reinterpret_cast<const float4*>(km + ((size_t)h * nb + min(j, nb - 1)) * D)[c];
+    if (i >= nb) a = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (j >= nb) b = make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4*>(&sq[r][4 * c]) = a;
+    *reinterpret_cast<float4*>(&sk[r][4 * c]) = b;
   }
   __syncthreads();
   const int wi = w >> 1, wj = w & 1;
@@ -108,25 +106,48 @@ __global__ __launch_bounds__(256) void k_block_scores(const float* __restrict__ 
 
 // One wave per row: MSB-first radix select (8-bit digits) of the k-th largest orderable key,
 // then an ordered ballot pass that keeps every key above the threshold and the lowest-index
-// keys equal to it.
-__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ scores, int rows, int nb,
-                                              int k, int32_t* __restrict__ lists) {
-  __shared__ int hist[4][256];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + wave;
-  const bool valid = row < rows;   // all waves keep to the same barrier sequence
-  const float* srow = scores + (size_t)(valid ? row : 0) * nb;
-  int* hw = hist[wave];
+// keys equal to it.  The waves of a workgroup work on separate rows and separate histograms,
+// so they never synchronise with each other (LDS operations of one wave complete in order).
+// Rows of up to 64 * kTopkRegs keys are read once into registers; longer rows are re-read from
+// memory in every pass.
+constexpr int kTopkRegs = 32;
+
+template <bool CACHED>
+__device__ __forceinline__ void topk_row(const float* __restrict__ srow, int nb, int k,
+                                         int* __restrict__ hw, int32_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  uint32_t kc[CACHED ? kTopkRegs : 1];
+  if (CACHED) {
+#pragma unroll
+    for (int u = 0; u < kTopkRegs; ++u) {
+      const int j = lane + 64 * u;
+      kc[u] = j < nb ? orderable_key(srow[j]) : 0u;
+    }
+  }
+  // key of column lane + 64 u (u < ceil(nb / 64)); only called for columns < nb
+  auto key_at = [&](int u) { return CACHED ? kc[u] : orderable_key(srow[lane + 64 * u]); };
+  const int nu = (nb + 63) >> 6;
   uint32_t prefix = 0, pmask = 0;
   int remaining = k;
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int b = lane; b < 256; b += 64) hw[b] = 0;
-    __syncthreads();
-    for (int j = lane; valid && j < nb; j += 64) {
-      const uint32_t key = orderable_key(srow[j]);
-      if ((key & pmask) == prefix) atomicAdd(&hw[(key >> shift) & 255], 1);
+    __builtin_amdgcn_wave_barrier();
+    if (CACHED) {
+#pragma unroll
+      for (int u = 0; u < kTopkRegs; ++u) {
+        const int j = lane + 64 * u;
+        if (j < nb && (kc[u] & pmask) == prefix) atomicAdd(&hw[(kc[u] >> shift) & 255], 1);
+      }
+    } else {
+      for (int u = 0; u < nu; ++u) {
+        const int j = lane + 64 * u;
+        if (j < nb) {
+          const uint32_t key = key_at(u);
+          if ((key & pmask) == prefix) atomicAdd(&hw[(key >> shift) & 255], 1);
+        }
+      }
     }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
     // lane l owns bins 255-4l .. 252-4l (descending); inclusive scan of counts from the top
     int c[4], local = 0;
 #pragma unroll
@@ -162,15 +183,13 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ scores, 
     remaining -= above;
     prefix |= uint32_t(digit) << shift;
     pmask |= 255u << shift;
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();  // the histogram reads above precede the next clearing
   }
-  if (!valid) return;
   // prefix is the threshold key T; take every key > T and the `remaining` lowest-index keys == T
-  int32_t* out = lists + (size_t)row * k;
   int taken = 0, eq_before = 0;
-  for (int base = 0; base < nb; base += 64) {
-    const int j = base + lane;
-    const uint32_t key = j < nb ? orderable_key(srow[j]) : 0u;
+  auto emit = [&](int u) {
+    const int j = lane + 64 * u;
+    const uint32_t key = j < nb ? key_at(u) : 0u;
     const bool eq = j < nb && key == prefix;
     const uint64_t eqm = __ballot(eq);
     const bool sel = j < nb && (key > prefix || (eq && eq_before + lanes_below(eqm) < remaining));
@@ -178,7 +197,28 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ scores, 
     if (sel) out[taken + lanes_below(selm)] = j;
     taken += __popcll(selm);
     eq_before += __popcll(eqm);
+  };
+  if (CACHED) {
+#pragma unroll
+    for (int u = 0; u < kTopkRegs; ++u)
+      if (u < nu) emit(u);
+  } else {
+    for (int u = 0; u < nu; ++u) emit(u);
   }
+}
+
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ scores, int rows, int nb,
+                                              int k, int32_t* __restrict__ lists) {
+  __shared__ int hist[4][256];
+  const int wave = threadIdx.x >> 6;
+  const int row = blockIdx.x * 4 + wave;
+  if (row >= rows) return;
+  const float* srow = scores + (size_t)row * nb;
+  int32_t* out = lists + (size_t)row * k;
+  if (nb <= 64 * kTopkRegs)
+    topk_row<true>(srow, nb, k, hist[wave], out);
+  else
+    topk_row<false>(srow, nb, k, hist[wave], out);
 }
 
 }  // namespace

@@ -55,8 +55,10 @@ def tiny():
 
 # ----------------------------------------------------------------------- top-K hook
 
+# rows of up to 2,048 blocks are selected from registers, longer ones re-read memory per pass
 @pytest.mark.parametrize("rows,nb,k", [(37, 64, 16), (300, 256, 51), (50, 1134, 113),
-                                       (9, 70, 70), (5, 1, 1), (64, 1620, 162)])
+                                       (9, 70, 70), (5, 1, 1), (64, 1620, 162), (6, 2048, 205),
+                                       (7, 2049, 300), (3, 4100, 410)])
 def test_topk_hook_bitexact(rows, nb, k):
     rng = np.random.default_rng(rows * 7 + nb)
     S = rng.standard_normal((rows, nb)).astype(np.float32)
