@@ -37,7 +37,22 @@ namespace bsa {
 namespace {
 
 constexpr int kMomChunk = 2048;   // tokens per partial of the second-moment reduction
-constexpr int kSlots = 32;        // workgroups per problem at the wide levels
+constexpr int kSlots = 32;        // workgroups per problem at the widest levels
+#ifndef BSA_LAST_WIDE
+#define BSA_LAST_WIDE 5
+#endif
+// Levels 0..kLastWide are wide (each group's statistics split over several workgroups, then
+// a direction, a projection and a split kernel); deeper levels run one workgroup per parent
+// or per subtree.
+constexpr int kLastWide = BSA_LAST_WIDE;
+// partial covariances per problem: every left group of the deepest wide level, 2 slices each
+constexpr int kPartialSlots = kLastWide > 4 ? (1 << kLastWide) : kSlots;
+
+// workgroups per group at a wide level (1: the level is not wide)
+inline int wide_slices(int level, int nb) {
+  if (level > kLastWide) return 1;
+  return std::min(kSlots >> std::min(level, 4), nb >> level);
+}
 constexpr int kIters = 8;         // power steps per split
 constexpr int kStageStride = 72;  // bf16 elements per LDS row of the staged (transposed) chunk
 
@@ -813,7 +828,7 @@ struct ProblemArgs {
   const float* mu_root;    // [P][D] mean of all y (the parent shift of level 0)
   const float* yscale;     // [P][2]: the power-of-two scale s of the fp16 split and 1 / s^2
   float* wdir;             // [P][G][D]
-  float* partial;          // [P][kSlots][D*D + D]
+  float* partial;          // [P][kPartialSlots][D*D + D]
   const float* cov_prev;   // [P][Gw][D*D] centred covariances of the previous wide level
   float* cov_cur;          // [P][Gw][D*D] this level's, for the next level's right children
   int gw, left_only;
@@ -1147,7 +1162,7 @@ __global__ __launch_bounds__(256, 3) void k_wide_stats(ProblemArgs a) {
   reduce_dpart<D>(dpart, red, dsum);
   // the slot holds the full symmetric D x D sum (scaled by s^2) in register dump order, then the
   // D sums of d
-  float* slot = a.partial + ((size_t)p * kSlots + blockIdx.y * a.slices + s) * (D * D + D);
+  float* slot = a.partial + ((size_t)p * kPartialSlots + blockIdx.y * a.slices + s) * (D * D + D);
   sym_store_dump<D>(acc, 1.f, slot);
   if (threadIdx.x < D) slot[D * D + threadIdx.x] = dsum[threadIdx.x];
 }
@@ -1180,7 +1195,7 @@ __global__ __launch_bounds__(256, 2) void k_wide_dir(ProblemArgs a) {
     const float y_first = first_candidate<T, D>(X, pos, inv_n, b0 * kBlk);
     f32x16_t acc[Cov<D>::TILES];
     zero_acc<D>(acc);
-    const float* base = a.partial + ((size_t)p * kSlots + par * a.slices) * (D * D + D);
+    const float* base = a.partial + ((size_t)p * kPartialSlots + par * a.slices) * (D * D + D);
     float ds = 0.f;
     for (int s = 0; s < a.slices; ++s) {
       add_acc<D>(base + (size_t)s * (D * D + D), acc);
@@ -1464,13 +1479,13 @@ RebLayout reb_layout(int H, int N, int D) {
   r.keys = take(P * N * 4);
   r.mu = take(P * ((size_t)1 << r.L) * D * 4);
   r.wdir = take(P * r.G * D * 4);
-  r.partial = take(P * kSlots * (size_t)(D * D + D) * 4);
+  r.partial = take(P * kPartialSlots * (size_t)(D * D + D) * 4);
   r.lists = take((size_t)std::max(r.L, 1) * r.G * 4);
   // covariance slots per problem: the groups of the deepest level that stores them (the last
   // wide level or the last one-workgroup-per-parent level)
   int last = 0;
   for (int level = 0; level < r.L; ++level) {
-    const int slices = std::min(kSlots >> std::min(level, 5), (int)(nb >> level));
+    const int slices = wide_slices(level, (int)nb);
     if (slices > 1 || ceil_div((int)nb, 1 << level) > kSmallBlocks) last = level;
     else break;
   }
@@ -1547,8 +1562,7 @@ hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm
   // one workgroup per subtree down to the leaves.
   int level = 0;
   for (; level < R.L; ++level) {
-    const int min_m = nb >> level;
-    const int slices = std::min(kSlots >> std::min(level, 5), min_m);
+    const int slices = wide_slices(level, nb);
     if (slices <= 1) break;
     a.level = level;
     a.slices = slices;
