@@ -175,6 +175,23 @@ BSA_DEV void stats_load(const T* __restrict__ X, const int32_t* __restrict__ tok
     load_dims<T, D>(X + (size_t)tok * D, dg, r.raw[u]);
   }
 }
+// The two token ids this thread loads for the chunk at position c0 (see stats_load).
+BSA_DEV void chunk_tokens(const int32_t* __restrict__ tokmap, int c0, int (&tok)[2]) {
+  const int tp = threadIdx.x & 31;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) tok[u] = tokmap ? tokmap[c0 + 2 * tp + u] : c0 + 2 * tp + u;
+}
+// stats_load with the token ids already read
+template <typename T, int D>
+BSA_DEV void stats_load_tok(const T* __restrict__ X, const float* __restrict__ inv_n,
+                            const int (&tok)[2], ChunkRegs<T, D>& r) {
+  const int dg = threadIdx.x >> 5;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    r.sc[u] = inv_n ? inv_n[tok[u]] : 1.f;
+    load_dims<T, D>(X + (size_t)tok[u] * D, dg, r.raw[u]);
+  }
+}
 
 // Stage one chunk (centred, split) into LDS and accumulate d; no barrier.  ysc: the kF16x2
 // scale s.
@@ -425,14 +442,25 @@ BSA_DEV void sym_stats_range(const T* __restrict__ X, const int32_t* __restrict_
                              float* sh_shift, float sh_val, float ysc, StageLds<D, 2>& st,
                              SymAcc<D>& acc, float* dpart) {
   ChunkRegs<T, D> cur;
-  if (PREFETCH && blk0 < blk1) stats_load<T, D>(X, tokmap, inv_n, blk0 * kBlk, cur);
+  // with PREFETCH, a block's rows are loaded one block ahead and its token ids two blocks
+  // ahead, so the id lookup and the row load do not follow each other on the critical path
+  int tnext[2];
+  if (PREFETCH && blk0 < blk1) {
+    int t0[2];
+    chunk_tokens(tokmap, blk0 * kBlk, t0);
+    stats_load_tok<T, D>(X, inv_n, t0, cur);
+    chunk_tokens(tokmap, min(blk0 + 1, blk1 - 1) * kBlk, tnext);
+  }
   if (threadIdx.x < D) sh_shift[threadIdx.x] = sh_val;
   __syncthreads();
   for (int b = blk0; b < blk1; ++b) {
     if (!PREFETCH) stats_load<T, D>(X, tokmap, inv_n, b * kBlk, cur);
     stats_stage<T, D, kF16x2>(cur, sh_shift, ysc, st, dpart);
     __syncthreads();
-    if (PREFETCH && b + 1 < blk1) stats_load<T, D>(X, tokmap, inv_n, (b + 1) * kBlk, cur);
+    if (PREFETCH && b + 1 < blk1) {
+      stats_load_tok<T, D>(X, inv_n, tnext, cur);
+      chunk_tokens(tokmap, min(b + 2, blk1 - 1) * kBlk, tnext);
+    }
     sym_mfma<D>(st, acc);
     __syncthreads();
   }
