@@ -780,6 +780,41 @@ BSA_DEV void power_direction(f32x16_t* acc, DirLds& L, const MRegs<D>& M, int n,
   __syncthreads();
 }
 
+// x . w of one position from its four threads' quarter rows (raw: this thread's quarter, NV
+// 16-byte pieces); the full sum on every thread of the four.
+template <typename T, int D>
+BSA_DEV float quarter_dot(const uint4* raw, const float* w) {
+  constexpr int E = D / 4;                 // elements per quarter row
+  constexpr int NV = E * sizeof(T) / 16;   // 16-byte pieces per quarter row
+  const int q = threadIdx.x & 3;
+  float xv[E];
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const uint32_t u[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        xv[8 * i + 2 * j] = __uint_as_float(u[j] << 16);
+        xv[8 * i + 2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      xv[4 * i] = __uint_as_float(raw[i].x);
+      xv[4 * i + 1] = __uint_as_float(raw[i].y);
+      xv[4 * i + 2] = __uint_as_float(raw[i].z);
+      xv[4 * i + 3] = __uint_as_float(raw[i].w);
+    }
+  }
+  float a = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) a = fmaf(xv[e], w[q * E + e], a);
+  a += dpp_mov<0xB1>(a);  // lane ^ 1
+  a += dpp_mov<0x4E>(a);  // lane ^ 2
+  return a;
+}
+
 // Projections of the positions of blocks [blk0, blk1): key = inv_n * (x . w), 4 threads per
 // position (a quarter row each); the loads of CH blocks are issued together.
 template <typename T, int D, int CH = 4>
@@ -808,31 +843,7 @@ BSA_DEV void project_range(const T* __restrict__ X, const int32_t* __restrict__ 
 #pragma unroll
     for (int c = 0; c < CH; ++c)
       if (c < nbk) {
-        float xv[E];
-        if constexpr (sizeof(T) == 2) {
-#pragma unroll
-          for (int i = 0; i < NV; ++i) {
-            const uint32_t u[4] = {raw[c][i].x, raw[c][i].y, raw[c][i].z, raw[c][i].w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              xv[8 * i + 2 * j] = __uint_as_float(u[j] << 16);
-              xv[8 * i + 2 * j + 1] = __uint_as_float(u[j] & 0xFFFF0000u);
-            }
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < NV; ++i) {
-            xv[4 * i] = __uint_as_float(raw[c][i].x);
-            xv[4 * i + 1] = __uint_as_float(raw[c][i].y);
-            xv[4 * i + 2] = __uint_as_float(raw[c][i].z);
-            xv[4 * i + 3] = __uint_as_float(raw[c][i].w);
-          }
-        }
-        float a = 0.f;
-#pragma unroll
-        for (int e = 0; e < E; ++e) a = fmaf(xv[e], w[q * E + e], a);
-        a += dpp_mov<0xB1>(a);  // lane ^ 1
-        a += dpp_mov<0x4E>(a);  // lane ^ 2
+        const float a = quarter_dot<T, D>(raw[c], w);
         if (q == 0) {
           const float key = a * sc[c];
           keys[(b + c) * kBlk + s] = key;
@@ -1266,14 +1277,29 @@ __global__ __launch_bounds__(256, 2) void k_wide_dir(ProblemArgs a) {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_wide_proj(ProblemArgs a) {
   __shared__ float w[D];
+  constexpr int E = D / 4, NV = E * sizeof(T) / 16;
   const int blk = blockIdx.x, p = blockIdx.y;
   int b0, m;
   const int g = group_of_block(a.nb, a.level, blk, b0, m);
   if (g < 0 || m < 2) return;
+  // as project_range over this one block, with the position's row and norm loads issued
+  // before the direction's load and barrier
+  const int s = threadIdx.x >> 2, q = threadIdx.x & 3;
+  const int tok = problem_pos(a, p)[blk * kBlk + s];
+  const uint4* src = reinterpret_cast<const uint4*>(problem_x<T, D>(a, p) + (size_t)tok * D + q * E);
+  uint4 raw[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) raw[i] = src[i];
+  const float sc = a.inv_n[(size_t)p * a.N + tok];
   if (threadIdx.x < D) w[threadIdx.x] = a.wdir[((size_t)p * a.G + g) * D + threadIdx.x];
   __syncthreads();
-  project_range<T, D, 1>(problem_x<T, D>(a, p), problem_pos(a, p), a.inv_n + (size_t)p * a.N,
-                         blk, blk + 1, w, a.keys + (size_t)p * a.N, problem_proj(a, p, a.level));
+  const float d = quarter_dot<T, D>(raw, w);
+  if (q == 0) {
+    const float key = d * sc;
+    a.keys[(size_t)p * a.N + blk * kBlk + s] = key;
+    float* proj = problem_proj(a, p, a.level);
+    if (proj) proj[tok] = key;
+  }
 }
 
 // grid (G, P), 1024 threads: split threshold and stable in-place partition of one group
