@@ -944,6 +944,8 @@ __global__ __launch_bounds__(256) void k_moments_finish(const float* __restrict_
   const int side = blockIdx.y, h = blockIdx.z;
   const size_t mi = (size_t)h * 2 + side;
   float s = 0.f;
+  // (unrolled so that the loads are in flight together; the additions keep their order)
+#pragma unroll 8
   for (int c = 0; c < nch; ++c) s += partial[(mi * nch + c) * D * D + e];
   const float m = s / float(N);
   // register-dump index -> (wave, tile, reg, lane) -> (a, b)
