@@ -73,7 +73,8 @@ def cpu_baseline(wl, q, k, v):
 class Layer:
     """Device buffers and the four stage calls of one layer (Reblock or fixed-tile layouts)."""
 
-    def __init__(self, ops, torch, wl, q, k, v, topk, fixed_tiles=False, ws=None):
+    def __init__(self, ops, torch, wl, q, k, v, topk, fixed_tiles=False, ws=None,
+                 layout="separate"):
         self.ops, self.torch = ops, torch
         dev = torch.device("cuda:0")
         dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
@@ -89,6 +90,7 @@ class Layer:
         self.lists = torch.empty(self.H, self.nb, topk, dtype=torch.int32, device=dev)
         self.out = torch.empty_like(self.qd)
         self.fixed = fixed_tiles
+        self.reblock_layout = ops._LAYOUTS[layout]
         self.flags = ops.BSA_MEANPOOL if fixed_tiles else 0
         self.L = ops.lib()
         self.stream = ops._stream()
@@ -106,9 +108,10 @@ class Layer:
             ops.check(self.L.bsa_tile_layout(self.H, T, Hh, W, 4, 4, 4, p(self.perm_k),
                                              self.stream))
         else:
-            ops.check(self.L.bsa_reblock(ctypes.byref(self.d), p(self.qd), p(self.kd),
-                                         p(self.perm_q), p(self.perm_k), None, p(self.ws),
-                                         self.ws.numel(), self.stream))
+            ops.check(self.L.bsa_reblock_layout(ctypes.byref(self.d), p(self.qd), p(self.kd),
+                                                self.reblock_layout, p(self.perm_q),
+                                                p(self.perm_k), None, p(self.ws),
+                                                self.ws.numel(), self.stream))
 
     def select(self):
         p = self.p
@@ -204,7 +207,7 @@ def main_headline(args, ops, synth, torch, np):
     t0 = time.perf_counter()
     q, k, v = synth.make_qkv(wl)
     log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
-    lay = Layer(ops, torch, wl, q, k, v, topk)
+    lay = Layer(ops, torch, wl, q, k, v, topk, layout=args.layout)
     ms_step, stage_ms, series = time_steps(torch, lay.stages(), args.steps, args.warmup)
     assert torch.isfinite(lay.out.float()).all().item(), "non-finite output"
     log(f"[bench] layer {ms_step:.3f} ms/step; stages " +
@@ -220,10 +223,11 @@ def main_headline(args, ops, synth, torch, np):
     elt = 2 if wl.dtype == "bf16" else 4
     x_bytes = H * N * D * elt
     levels = max(0, (nb - 1).bit_length())
+    sides = 1 if args.layout == "q_reuse_k" else 2
     hbm = {
-        "reblock": {"bytes": (2 + 2 * levels) * 2 * x_bytes,
+        "reblock": {"bytes": (2 + 2 * levels) * sides * x_bytes,
                     "passes": "moments, norms, and per tree level a statistics and a "
-                              "projection pass over Q and K"},
+                              "projection pass over " + ("K" if sides == 1 else "Q and K")},
         "select": {"bytes": 2 * x_bytes + H * nb * nb * 4, "passes": "Q, K once; scores"},
         "prepare": {"bytes": 3 * x_bytes, "passes": "Q (anchor), K, V once"},
     }
@@ -279,7 +283,7 @@ def main_headline(args, ops, synth, torch, np):
         "data": "synthetic",
         "config": {"workload": wl.name, "heads": H, "tokens": N, "head_dim": D,
                    "topk_ratio": wl.topk_ratio, "topk_blocks": topk, "grid": list(wl.grid),
-                   "parallelism": "single GPU"},
+                   "reblock_layout": args.layout, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                      "traffic": ATTN_TRAFFIC_BYTES.get(wl.name), "kernel": "k_attn_bf16",
@@ -358,22 +362,25 @@ def main_sweep(args, ops, synth, torch, np):
     rows = []
     for ratio in synth.SWEEP_RATIOS:
         topk = ops.topk_count(nb, ratio)
-        for fixed in (False, True):
-            lay = Layer(ops, torch, wl, q, k, v, topk, fixed_tiles=fixed, ws=base.ws)
+        for fixed, layout, name in ((False, "separate", "reblock, reweighted summaries"),
+                                    (False, "q_reuse_k", "reblock of the keys reused for the "
+                                                         "queries, reweighted summaries"),
+                                    (True, "separate", "fixed 4x4x4 tiles, mean-pooled "
+                                                       "summaries")):
+            lay = Layer(ops, torch, wl, q, k, v, topk, fixed_tiles=fixed, ws=base.ws,
+                        layout=layout)
             ms_step, stage_ms, _ = time_steps(torch, lay.stages(), args.steps, args.warmup)
             rec = lay.recall(lse_dense)
-            row = {"topk_ratio": ratio, "topk_blocks": topk,
-                   "layout": "fixed 4x4x4 tiles, mean-pooled summaries" if fixed else
-                             "reblock, reweighted summaries",
+            row = {"topk_ratio": ratio, "topk_blocks": topk, "layout": name,
                    "layer_ms": ms_step, "stages_ms": stage_ms, "recall": rec,
                    "speedup_vs_dense_attention": dense_ms / ms_step}
             rows.append(row)
-            log(f"[bench] ratio {ratio:.1f} {'fixed  ' if fixed else 'reblock'}: layer "
-                f"{ms_step:.3f} ms, recall {rec:.4f}")
+            tag = "fixed    " if fixed else ("reblock  " if layout == "separate" else "q_reuse_k")
+            log(f"[bench] ratio {ratio:.1f} {tag}: layer {ms_step:.3f} ms, recall {rec:.4f}")
             del lay
     return {
         "metric": "density sweep at 16,384 tok: layer ms and attention-mass recall vs dense "
-                  "softmax, reblock vs fixed tiles",
+                  "softmax, reblock (separate or key layout reused) vs fixed tiles",
         "value": rows[0]["recall"], "unit": "recall at 10% density (reblock)",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -394,6 +401,9 @@ def main():
     ap.add_argument("--workload", default="clip10s_bf16")
     ap.add_argument("--sweep", action="store_true",
                     help="density sweep with Reblock and fixed-tile layouts on 16,384 tokens")
+    ap.add_argument("--layout", choices=("separate", "q_reuse_k"), default="separate",
+                    help="reblock layouts: one tree per side (default), or the key tree "
+                         "reused for the queries")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",

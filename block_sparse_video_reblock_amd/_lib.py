@@ -36,6 +36,8 @@ _SIGS = {
     "bsa_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(BsaDesc)]),
     "bsa_reblock": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), _P, _P, _P, _P, _P, _P,
                                      ctypes.c_size_t, _P]),
+    "bsa_reblock_layout": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), _P, _P, ctypes.c_int32, _P,
+                                            _P, _P, _P, ctypes.c_size_t, _P]),
     "bsa_select": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), _P, _P, _P, _P, ctypes.c_float,
                                     ctypes.c_int32, _P, _P, _P, ctypes.c_size_t, _P]),
     "bsa_sparse_attn": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), _P, _P, _P, _P, _P, _P,
@@ -131,9 +133,18 @@ def topk_count(n_blocks: int, ratio: float) -> int:
     return int(lib().bsa_topk_count(n_blocks, ratio))
 
 
-def reblock(q, k, ws=None, with_proj=False):
-    """(perm_q, perm_k[, proj]) int32 [H][N] (and float [H][2][levels][N])."""
+BSA_LAYOUT_SEPARATE = 0
+BSA_LAYOUT_Q_REUSE_K = 1
+_LAYOUTS = {"separate": BSA_LAYOUT_SEPARATE, "q_reuse_k": BSA_LAYOUT_Q_REUSE_K}
+
+
+def reblock(q, k, ws=None, with_proj=False, layout="separate"):
+    """(perm_q, perm_k[, proj]) int32 [H][N] (and float [H][2][levels][N]).
+    layout "separate" (bsa_reblock) or "q_reuse_k" (bsa_reblock_layout: perm_q is a copy of the
+    key layout)."""
     torch = _torch()
+    if layout not in _LAYOUTS:
+        raise BsaError(BSA_E_ARG, f"unknown layout {layout!r}")
     d = desc_for(q)
     ws = workspace(d, q.device) if ws is None else ws
     H, N = q.shape[0], q.shape[1]
@@ -141,9 +152,9 @@ def reblock(q, k, ws=None, with_proj=False):
     perm_k = torch.empty_like(perm_q)
     levels = max(0, (N // BLOCK - 1).bit_length())
     proj = torch.empty(H, 2, levels, N, dtype=torch.float32, device=q.device) if with_proj else None
-    check(lib().bsa_reblock(ctypes.byref(d), _dev_ptr(q, q.dtype), _dev_ptr(k, q.dtype),
-                            _dev_ptr(perm_q), _dev_ptr(perm_k), _dev_ptr(proj), _dev_ptr(ws),
-                            ws.numel(), _stream()))
+    check(lib().bsa_reblock_layout(ctypes.byref(d), _dev_ptr(q, q.dtype), _dev_ptr(k, q.dtype),
+                                   _LAYOUTS[layout], _dev_ptr(perm_q), _dev_ptr(perm_k),
+                                   _dev_ptr(proj), _dev_ptr(ws), ws.numel(), _stream()))
     return (perm_q, perm_k, proj) if with_proj else (perm_q, perm_k)
 
 

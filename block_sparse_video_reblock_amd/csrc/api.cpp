@@ -192,19 +192,31 @@ size_t bsa_workspace_bytes(const bsa_desc* d) {
   return m > r ? m : r;
 }
 
-bsa_status bsa_reblock(const bsa_desc* d, const void* q, const void* k, int32_t* perm_q,
-                       int32_t* perm_k, float* proj_opt, void* ws, size_t ws_bytes,
-                       hipStream_t stream) {
+bsa_status bsa_reblock_layout(const bsa_desc* d, const void* q, const void* k, int32_t layout,
+                              int32_t* perm_q, int32_t* perm_k, float* proj_opt, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
   bsa_status st = check_desc(d);
   if (st != BSA_OK) return st;
+  if (layout != BSA_LAYOUT_SEPARATE && layout != BSA_LAYOUT_Q_REUSE_K)
+    return fail(BSA_E_ARG, "unknown layout %d", (int)layout);
   if (!q || !k || !perm_q || !perm_k) return fail(BSA_E_ARG, "null tensor pointer");
+  if (layout == BSA_LAYOUT_SEPARATE && perm_q == perm_k)
+    return fail(BSA_E_ARG, "separate layouts need two permutation buffers");
   st = check_ws(ws, ws_bytes, bsa::reblock_ws_bytes(d->heads, d->tokens, d->head_dim));
   if (st != BSA_OK) return st;
   st = check_device();
   if (st != BSA_OK) return st;
   return hip_status(bsa::launch_reblock(is_bf16(d), q, k, d->heads, d->tokens, d->head_dim,
-                                        perm_q, perm_k, proj_opt, ws, stream),
+                                        perm_q, perm_k, proj_opt,
+                                        layout == BSA_LAYOUT_Q_REUSE_K, ws, stream),
                     "reblock launch");
+}
+
+bsa_status bsa_reblock(const bsa_desc* d, const void* q, const void* k, int32_t* perm_q,
+                       int32_t* perm_k, float* proj_opt, void* ws, size_t ws_bytes,
+                       hipStream_t stream) {
+  return bsa_reblock_layout(d, q, k, BSA_LAYOUT_SEPARATE, perm_q, perm_k, proj_opt, ws,
+                            ws_bytes, stream);
 }
 
 bsa_status bsa_select(const bsa_desc* d, const void* q, const void* k, const int32_t* perm_q,

@@ -874,7 +874,12 @@ struct ProblemArgs {
   const int* lists;        // [L][G] active (m >= 2) nodes per level, ascending
   float* proj;             // optional [H][2][L][N]
   int level, G, slices;
+  // problems launched: p = p0 + pstep * (grid index); all 2H (0, 1), or the key sides only
+  // (1, 2) when the queries reuse the key layout
+  int p0, pstep;
 };
+
+BSA_DEV int problem_of(const ProblemArgs& a, int b) { return a.p0 + a.pstep * b; }
 
 // problem p = 2h + side; side 0 partitions the queries under M_K, side 1 the keys under M_Q
 template <typename T, int D>
@@ -919,6 +924,7 @@ __global__ __launch_bounds__(256) void k_moments(const T* __restrict__ q,
   constexpr int MODE = sizeof(T) == 4 ? kBf16x3 : kExact;
   __shared__ StageLds<D, split_terms<MODE>()> st;
   __shared__ float zero[D];
+  // side = blockIdx.y: 0 = M_Q, 1 = M_K (a grid of one side computes M_Q only)
   const int chunk = blockIdx.x, side = blockIdx.y, h = blockIdx.z, nch = gridDim.x;
   const T* X = (side ? k : q) + (size_t)h * N * D;
   if (threadIdx.x < D) zero[threadIdx.x] = 0.f;
@@ -984,7 +990,7 @@ __global__ __launch_bounds__(256) void k_norms_bf16(ProblemArgs a, const uint16_
   __shared__ float s_inv[kNormTile];
   __shared__ float s_ys[4][D];
   __shared__ float s_max[4];
-  const int chunk = blockIdx.x, p = blockIdx.y, nch = gridDim.x;
+  const int chunk = blockIdx.x, p = problem_of(a, blockIdx.y), nch = gridDim.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
   const uint16_t* X = problem_x<uint16_t, D>(a, p);
   const int mi = (p >> 1) * 2 + ((p & 1) ? 0 : 1);
@@ -1089,7 +1095,7 @@ __global__ __launch_bounds__(256) void k_norms_f32(ProblemArgs a, float* __restr
   __shared__ float sm[D][D + 1];
   __shared__ float sx[64][D + 1];
   __shared__ float s_inv[64];
-  const int chunk = blockIdx.x, p = blockIdx.y, nch = gridDim.x;
+  const int chunk = blockIdx.x, p = problem_of(a, blockIdx.y), nch = gridDim.x;
   const int tid = threadIdx.x, s = tid >> 2, q = tid & 3;
   const float* X = problem_x<float, D>(a, p);
   const float* M = problem_metric<D>(a, p);
@@ -1128,12 +1134,12 @@ __global__ __launch_bounds__(256) void k_norms_f32(ProblemArgs a, float* __restr
 template <int D>
 __global__ __launch_bounds__(256) void k_root_mean(const float* __restrict__ ysum,
                                                    const float* __restrict__ ymax, int nch, int N,
-                                                   float* __restrict__ mu_root,
+                                                   int p0, int pstep, float* __restrict__ mu_root,
                                                    float* __restrict__ yscale) {
   constexpr int R = 256 / D;  // chunk strides per element
   __shared__ float part[R][D];
   __shared__ float s_max[4];
-  const int p = blockIdx.x, d = threadIdx.x % D, r = threadIdx.x / D;
+  const int p = p0 + pstep * (int)blockIdx.x, d = threadIdx.x % D, r = threadIdx.x / D;
   float s = 0.f;
   // (unrolled so that the loads are in flight together; the additions keep their order)
 #pragma unroll 8
@@ -1185,7 +1191,8 @@ __global__ __launch_bounds__(256, 3) void k_wide_stats(ProblemArgs a) {
   __shared__ float shift[D];
   __shared__ float red[4 * D];
   __shared__ float dsum[D];
-  const int s = blockIdx.x, g = a.left_only ? 2 * blockIdx.y : blockIdx.y, p = blockIdx.z;
+  const int s = blockIdx.x, g = a.left_only ? 2 * blockIdx.y : blockIdx.y,
+            p = problem_of(a, blockIdx.z);
   int b0, m;
   if (group_geom(a.nb, a.level, g, b0, m) != kGroupSplit) return;
   const int sb0 = b0 + (int)((long)s * m / a.slices), sb1 = b0 + (int)((long)(s + 1) * m / a.slices);
@@ -1217,7 +1224,7 @@ __global__ __launch_bounds__(256, 3) void k_wide_stats(ProblemArgs a) {
 template <typename T, int D>
 __global__ __launch_bounds__(256, 2) void k_wide_dir(ProblemArgs a) {
   __shared__ DirLds L;
-  const int p = blockIdx.y;
+  const int p = problem_of(a, blockIdx.y);
   // left-only levels: workgroup 2 j + c handles child c of parent j (both children read the
   // left child's partial sums); otherwise workgroup g handles group g
   const int par = a.left_only ? (int)(blockIdx.x >> 1) : (int)blockIdx.x;
@@ -1280,7 +1287,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void k_wide_proj(ProblemArgs a) {
   __shared__ float w[D];
   constexpr int E = D / 4, NV = E * sizeof(T) / 16;
-  const int blk = blockIdx.x, p = blockIdx.y;
+  const int blk = blockIdx.x, p = problem_of(a, blockIdx.y);
   int b0, m;
   const int g = group_of_block(a.nb, a.level, blk, b0, m);
   if (g < 0 || m < 2) return;
@@ -1308,7 +1315,7 @@ __global__ __launch_bounds__(256) void k_wide_proj(ProblemArgs a) {
 __global__ __launch_bounds__(1024) void k_wide_split(ProblemArgs a) {
   __shared__ int hist[16 * 256];
   __shared__ int sm[40];
-  const int g = blockIdx.x, p = blockIdx.y;
+  const int g = blockIdx.x, p = problem_of(a, blockIdx.y);
   int b0, m;
   if (group_geom(a.nb, a.level, g, b0, m) != kGroupSplit) return;
   const size_t off = (size_t)b0 * kBlk;
@@ -1371,7 +1378,7 @@ __global__ __launch_bounds__(256, 2) void k_subtree_pair(ProblemArgs a, int leve
   __shared__ float dsl[D];
   __shared__ int hist[4 * 256];
   __shared__ int sm[16];
-  const int gp = a.lists[(size_t)(level - 1) * a.G + blockIdx.x], p = blockIdx.y;
+  const int gp = a.lists[(size_t)(level - 1) * a.G + blockIdx.x], p = problem_of(a, blockIdx.y);
   int pb0, pm;
   group_geom(a.nb, level - 1, gp, pb0, pm);
   if (pm < 3) return;  // both children are leaves
@@ -1438,7 +1445,7 @@ __global__ __launch_bounds__(256, 2) void k_subtree_small(ProblemArgs a, int ls)
   __shared__ float skeys[kSmallBlocks * kBlk];
   __shared__ int hist[4 * 256];
   __shared__ int sm[16];
-  const int g0 = a.lists[(size_t)ls * a.G + blockIdx.x], p = blockIdx.y;
+  const int g0 = a.lists[(size_t)ls * a.G + blockIdx.x], p = problem_of(a, blockIdx.y);
   int rb0, rm;
   group_geom(a.nb, ls, g0, rb0, rm);
   const T* X = problem_x<T, D>(a, p);
@@ -1491,6 +1498,13 @@ __global__ __launch_bounds__(256, 2) void k_subtree_small(ProblemArgs a, int ls)
 __global__ void k_fill_identity(int N, int32_t* __restrict__ out) {
   const size_t p = blockIdx.y;
   for (int i = blockIdx.x * 256 + threadIdx.x; i < N; i += gridDim.x * 256) out[p * N + i] = i;
+}
+
+// out[p][i] = in[p][i], grid (x, P)
+__global__ void k_copy_i32(int N, const int32_t* __restrict__ in, int32_t* __restrict__ out) {
+  const size_t p = blockIdx.y;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < N; i += gridDim.x * 256)
+    out[p * N + i] = in[p * N + i];
 }
 
 __global__ void k_fill_zero(size_t n, float* __restrict__ out) {
@@ -1561,16 +1575,19 @@ int active_count(int nb, int level) {
 
 template <typename T, int D>
 hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm_q,
-                       int32_t* perm_k, float* proj_opt, void* ws, hipStream_t s) {
+                       int32_t* perm_k, float* proj_opt, bool keys_only, void* ws,
+                       hipStream_t s) {
   const RebLayout R = reb_layout(H, N, D);
   char* w = static_cast<char*>(ws);
-  const int P = 2 * H, nb = N / kBlk;
+  // keys_only: only the key trees (problems 2h + 1, under M_Q) are built, and the query
+  // layouts are copies of them; M_K and the query norms are then not needed either
+  const int P = keys_only ? H : 2 * H, nb = N / kBlk, sides = keys_only ? 1 : 2;
   float* mom = reinterpret_cast<float*>(w + R.mom);
   uint16_t* msplit = sizeof(T) == 2 ? reinterpret_cast<uint16_t*>(w + R.msplit) : nullptr;
-  k_moments<T, D><<<dim3(R.nch_mom, 2, H), 256, 0, s>>>(
+  k_moments<T, D><<<dim3(R.nch_mom, sides, H), 256, 0, s>>>(
       static_cast<const T*>(q), static_cast<const T*>(k), N,
       reinterpret_cast<float*>(w + R.mom_partial));
-  k_moments_finish<D><<<dim3(D * D / 256, 2, H), 256, 0, s>>>(
+  k_moments_finish<D><<<dim3(D * D / 256, sides, H), 256, 0, s>>>(
       reinterpret_cast<float*>(w + R.mom_partial), R.nch_mom, N, mom, msplit);
   ProblemArgs a{};
   a.q = q;
@@ -1594,6 +1611,8 @@ hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm
   a.proj = proj_opt;
   a.gw = R.gw;
   a.G = R.G;
+  a.p0 = keys_only ? 1 : 0;
+  a.pstep = keys_only ? 2 : 1;
   float* ysum = reinterpret_cast<float*>(w + R.ysum);
   float* ymax = reinterpret_cast<float*>(w + R.ymax);
   if (sizeof(T) == 2)
@@ -1602,15 +1621,15 @@ hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm
   else
     k_norms_f32<<<dim3(R.nch_n, P), 256, 0, s>>>(a, reinterpret_cast<float*>(w + R.inv_n), ysum,
                                                  ymax);
-  k_root_mean<D><<<P, 256, 0, s>>>(ysum, ymax, R.nch_n, N,
+  k_root_mean<D><<<P, 256, 0, s>>>(ysum, ymax, R.nch_n, N, a.p0, a.pstep,
                                    reinterpret_cast<float*>(w + R.mu_root),
                                    reinterpret_cast<float*>(w + R.yscale));
   if (proj_opt && R.L > 0) {
-    const size_t n = (size_t)P * R.L * N;
+    const size_t n = (size_t)2 * H * R.L * N;
     k_fill_zero<<<(unsigned)std::min<size_t>((n + 255) / 256, 4096), 256, 0, s>>>(n, proj_opt);
   }
   const dim3 gridN(std::min(ceil_div(N, 256), 1024), H);
-  k_fill_identity<<<gridN, 256, 0, s>>>(N, perm_q);
+  if (!keys_only) k_fill_identity<<<gridN, 256, 0, s>>>(N, perm_q);
   k_fill_identity<<<gridN, 256, 0, s>>>(N, perm_k);
   if (R.L > 0) k_group_lists<<<R.L, 256, 0, s>>>(nb, R.G, reinterpret_cast<int*>(w + R.lists));
   // levels whose groups are large are split over several workgroups; below that one
@@ -1645,6 +1664,7 @@ hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm
     a.cov_cur = reinterpret_cast<float*>(w + ((level & 1) ? R.cov1 : R.cov0));
     k_subtree_pair<T, D><<<dim3(active_count(nb, level - 1), P), 256, 0, s>>>(a, level, R.gw);
   }
+  if (keys_only && perm_q != perm_k) k_copy_i32<<<gridN, 256, 0, s>>>(N, perm_k, perm_q);
   return hipGetLastError();
 }
 
@@ -1697,10 +1717,11 @@ hipError_t launch_partition_from_proj(int P, int N, const float* proj, int32_t* 
 size_t reblock_ws_bytes(int H, int N, int D) { return reb_layout(H, N, D).total; }
 
 hipError_t launch_reblock(bool bf16, const void* q, const void* k, int H, int N, int D,
-                          int32_t* perm_q, int32_t* perm_k, float* proj_opt, void* ws,
-                          hipStream_t s) {
-  if (bf16) return run_reblock<uint16_t, 128>(q, k, H, N, perm_q, perm_k, proj_opt, ws, s);
-  return run_reblock<float, 64>(q, k, H, N, perm_q, perm_k, proj_opt, ws, s);
+                          int32_t* perm_q, int32_t* perm_k, float* proj_opt, bool keys_only,
+                          void* ws, hipStream_t s) {
+  if (bf16)
+    return run_reblock<uint16_t, 128>(q, k, H, N, perm_q, perm_k, proj_opt, keys_only, ws, s);
+  return run_reblock<float, 64>(q, k, H, N, perm_q, perm_k, proj_opt, keys_only, ws, s);
 }
 
 }  // namespace bsa

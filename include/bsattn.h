@@ -91,6 +91,20 @@ bsa_status bsa_reblock(const bsa_desc* desc, const void* q, const void* k,
                        int32_t* perm_q, int32_t* perm_k, float* proj_opt,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* (1') Reblock with a layout choice.  [comfyui-wiki.com "Spark-H3 ...", "Workflows" ("工作流")]:
+ * every shipped workflow pins reblock_layout = q_reuse_k; the pages do not define it, and the
+ * reading taken here is its name: the queries reuse the key layout.
+ *   BSA_LAYOUT_SEPARATE  exactly bsa_reblock (perm_q and perm_k must be distinct buffers).
+ *   BSA_LAYOUT_Q_REUSE_K only the key trees are built (keys under M_Q, as in bsa_reblock, with
+ *                        the identical result for perm_k); perm_q receives a copy of perm_k,
+ *                        and perm_q may be the same buffer as perm_k.  proj_opt then holds
+ *                        the key side only (the query side is left 0).
+ * Same workspace, leaf order and errors as bsa_reblock; an unknown layout is BSA_E_ARG. */
+typedef enum { BSA_LAYOUT_SEPARATE = 0, BSA_LAYOUT_Q_REUSE_K = 1 } bsa_layout;
+bsa_status bsa_reblock_layout(const bsa_desc* desc, const void* q, const void* k, int32_t layout,
+                              int32_t* perm_q, int32_t* perm_k, float* proj_opt,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* (2) Select.  Block scores S[h][i][j] = s * mean(query block i) . mean(key block j) with
  * s = 1/sqrt(D); per row the K largest (ties to the lower j), written ascending to
  * lists[h][i][0..K).  K = topk_blocks if topk_blocks > 0 (must be <= nb), else

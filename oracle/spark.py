@@ -162,13 +162,21 @@ def partition_from_projections(proj: np.ndarray, n_tokens: int, leaf: int = LEAF
 
 
 def reblock_head(Q: np.ndarray, K: np.ndarray, leaf: int = LEAF, iters: int = POWER_ITERS,
-                 kind: str = "eigh"):
+                 kind: str = "eigh", layout: str = "separate"):
     """Query layout from M_K, key layout from M_Q, each partitioned on its own ([P2]).
-    Returns (perm_q, perm_k, proj_q, proj_k).  Q/K/V values are untouched."""
+    Returns (perm_q, perm_k, proj_q, proj_k).  Q/K/V values are untouched.
+
+    layout "q_reuse_k" ([P1] "Workflows": every shipped workflow pins reblock_layout =
+    q_reuse_k; the pages do not define it, and the reading taken is its name): only the key
+    layout is partitioned and the queries reuse it, perm_q = perm_k; proj_q is then None."""
+    if layout not in ("separate", "q_reuse_k"):
+        raise ValueError(f"unknown layout {layout!r}")
     M_q = second_moment(Q)
+    perm_k, proj_k = partition(metric_embed(K, M_q, kind), leaf, iters)
+    if layout == "q_reuse_k":
+        return perm_k.copy(), perm_k, None, proj_k
     M_k = second_moment(K)
     perm_q, proj_q = partition(metric_embed(Q, M_k, kind), leaf, iters)
-    perm_k, proj_k = partition(metric_embed(K, M_q, kind), leaf, iters)
     return perm_q, perm_k, proj_q, proj_k
 
 

@@ -155,3 +155,44 @@ def test_full_layer_bf16_mid(mid):
         assert np.linalg.norm(o[h] - ro) / np.linalg.norm(ro) < 1e-2
         assert np.max(np.abs(o[h] - ro)) < 3e-2
         assert np.max(np.abs(lse[h] - rl)) < 3e-2
+
+
+# --------------------------------------------------------------- queries reuse the key layout
+
+@pytest.mark.parametrize("which", ["tiny", "mid"])
+def test_reblock_q_reuse_k_equals_key_layout(which, tiny, mid):
+    """Key-reuse layout: perm_q is a copy of perm_k, and perm_k is bit-identical to the key
+    layout of the separate reblock (the key trees are the same computation)."""
+    wl, q, k, v = tiny if which == "tiny" else mid
+    dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    qd, kd = to_dev(q, dt), to_dev(k, dt)
+    sq, sk = ops.reblock(qd, kd)
+    rq, rk, proj = ops.reblock(qd, kd, layout="q_reuse_k", with_proj=True)
+    assert torch.equal(rk, sk)
+    assert torch.equal(rq, rk)
+    proj = proj.cpu().numpy()
+    assert not proj[:, 0].any()                      # the query side is not partitioned
+    # the key side against the oracle, split by split
+    for h in range(q.shape[0]):
+        st = replay_partition(O.metric_embed(k[h].astype(np.float64),
+                                             O.second_moment(q[h].astype(np.float64))),
+                              rk[h].cpu().numpy(), proj[h, 1])
+        assert st["max_proj_err"] < 3e-5, st
+        assert st["mismatched_splits"] <= 0.02 * st["splits"]
+
+
+def test_full_layer_q_reuse_k_bf16_mid(mid):
+    wl, q, k, v = mid
+    dt = torch.bfloat16
+    qd, kd, vd = to_dev(q, dt), to_dev(k, dt), to_dev(v, dt)
+    pq, pk = ops.reblock(qd, kd, layout="q_reuse_k")
+    lists = ops.select(qd, kd, pq, pk, topk_ratio=wl.topk_ratio)
+    o, lse = ops.sparse_attn(qd, kd, vd, pq, pk, lists, with_lse=True)
+    pq, pk, lists = pq.cpu().numpy(), pk.cpu().numpy(), lists.cpu().numpy()
+    o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
+    assert np.array_equal(pq, pk)
+    for h in range(q.shape[0]):
+        ro, rl = O.sparse_attention_head(q[h], k[h], v[h], pq[h], pk[h], lists[h])
+        assert np.linalg.norm(o[h] - ro) / np.linalg.norm(ro) < 1e-2
+        assert np.max(np.abs(o[h] - ro)) < 3e-2
+        assert np.max(np.abs(lse[h] - rl)) < 3e-2

@@ -17,6 +17,7 @@ def L():
 
 
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails before any device work
+FAKE2 = ctypes.c_void_p(0x2000)
 
 
 def desc(h=2, n=4096, d=128, dt=_lib.BSA_BF16):
@@ -114,8 +115,18 @@ def test_select_argument_errors(L):
 def test_reblock_and_hook_argument_errors(L):
     big = 1 << 40
     assert L.bsa_reblock(desc(), None, FAKE, FAKE, FAKE, None, FAKE, big, None) == _lib.BSA_E_ARG
-    assert L.bsa_reblock(desc(), FAKE, FAKE, FAKE, FAKE, None, FAKE, 8,
+    assert L.bsa_reblock(desc(), FAKE, FAKE, FAKE, FAKE2, None, FAKE, 8,
                          None) == _lib.BSA_E_WORKSPACE
+    # separate layouts need two permutation buffers
+    assert L.bsa_reblock(desc(), FAKE, FAKE, FAKE, FAKE, None, FAKE, big, None) == _lib.BSA_E_ARG
+    # layout choice: unknown value, then the key-reuse layout, whose one buffer may serve both
+    for bad in (-1, 2):
+        assert L.bsa_reblock_layout(desc(), FAKE, FAKE, bad, FAKE, FAKE2, None, FAKE, big,
+                                    None) == _lib.BSA_E_ARG
+    assert L.bsa_reblock_layout(desc(), FAKE, FAKE, _lib.BSA_LAYOUT_Q_REUSE_K, FAKE, FAKE, None,
+                                FAKE, 8, None) == _lib.BSA_E_WORKSPACE
+    assert L.bsa_reblock_layout(desc(), FAKE, FAKE, _lib.BSA_LAYOUT_Q_REUSE_K, None, FAKE, None,
+                                FAKE, big, None) == _lib.BSA_E_ARG
     assert L.bsa_reblock_from_projections(0, 128, FAKE, FAKE, FAKE, big, None) == _lib.BSA_E_ARG
     assert L.bsa_reblock_from_projections(2, 100, FAKE, FAKE, FAKE, big, None) == _lib.BSA_E_ARG
     assert L.bsa_reblock_from_projections(2, 128, None, FAKE, FAKE, big, None) == _lib.BSA_E_ARG

@@ -144,6 +144,23 @@ def test_reblock_invariances(tiny_inputs):
         assert np.array_equal(variant[1], base[1])
 
 
+def test_q_reuse_k_layout(tiny_inputs):
+    """Key-reuse layout ([P1] "Workflows", reading: the queries reuse the key layout): the key
+    tree is the separate layout's key tree and the query layout is a copy of it; with Q = K the
+    two separate layouts coincide, so there the reuse changes nothing."""
+    wl, Q, K, V = tiny_inputs
+    pq, pk, prq, prk = O.reblock_head(Q, K, layout="q_reuse_k")
+    sq, sk, _, sprk = O.reblock_head(Q, K)
+    assert prq is None
+    assert np.array_equal(pq, pk) and pq is not pk
+    assert np.array_equal(pk, sk) and np.array_equal(prk, sprk)
+    same = O.reblock_head(K, K)
+    assert np.array_equal(same[0], same[1])
+    assert np.array_equal(O.reblock_head(K, K, layout="q_reuse_k")[0], same[0])
+    with pytest.raises(ValueError):
+        O.reblock_head(Q, K, layout="q_reuse_q")
+
+
 def _naive_tree(X, M, leaf):
     """Independent partitioner: explicit Mahalanobis-cosine Gram matrix, principal direction
     from numpy.linalg.eigh of the centred Gram (kernel PCA), full stable sort."""
