@@ -257,7 +257,8 @@ def _softmax_branch(logits: np.ndarray, values: np.ndarray):
 
 
 def sparse_attention_head(Q, K, V, perm_q, perm_k, lists, scale=None, mode="reweight",
-                          leaf: int = LEAF, summ=None, return_branches=False, blocks=None):
+                          leaf: int = LEAF, summ=None, return_branches=False, blocks=None,
+                          tail: str = "token"):
     """One head of the two-branch layer, output in token order.
 
     [P1] "What Spark-Attn changes": an exact branch fully computes the top-ranked K/V blocks
@@ -268,8 +269,14 @@ def sparse_attention_head(Q, K, V, perm_q, perm_k, lists, scale=None, mode="rewe
                   -> (O_c, lse_c); no unselected block gives lse_c = -inf
       merge:      lse = logaddexp(lse_e, lse_c), O = e^(lse_e-lse) O_e + e^(lse_c-lse) O_c
       inverse permutation: row p of the block goes to token perm_q[p].
+    tail = "block" is the tail_granularity option of [P2] "What it's doing under the hood"
+    (ComfyUI's block-level behaviour): the compressed branch of every query of block i uses
+    one pooled query, the mean of the block's queries, in place of the query's own; the exact
+    branch and the merge are unchanged.  Reading: "pooled" is the plain mean.
     Returns (O, lse) or, with return_branches, (O, lse, O_e, lse_e, O_c, lse_c).  With
     blocks (query block indices) only those blocks' rows are computed; the others hold NaN."""
+    if tail not in ("token", "block"):
+        raise ValueError(f"unknown tail granularity {tail!r}")
     Q = np.asarray(Q, np.float64)
     K = np.asarray(K, np.float64)
     V = np.asarray(V, np.float64)
@@ -292,7 +299,8 @@ def sparse_attention_head(Q, K, V, perm_q, perm_k, lists, scale=None, mode="rewe
         Oe, le = _softmax_branch(s * q @ K[keys].T, V[keys])
         mask = np.ones(nb, dtype=bool)
         mask[sel] = False
-        Oc, lc = _softmax_branch(s * q @ kt[mask].T + b[mask][None, :], vt[mask])
+        qc = q if tail == "token" else np.repeat(q.mean(axis=0, keepdims=True), leaf, axis=0)
+        Oc, lc = _softmax_branch(s * qc @ kt[mask].T + b[mask][None, :], vt[mask])
         lt = np.logaddexp(le, lc)
         O[rows] = np.exp(le - lt)[:, None] * Oe + np.exp(lc - lt)[:, None] * Oc
         lse[rows] = lt

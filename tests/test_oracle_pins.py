@@ -161,6 +161,55 @@ def test_q_reuse_k_layout(tiny_inputs):
         O.reblock_head(Q, K, layout="q_reuse_q")
 
 
+def test_tail_block_granularity(tiny_inputs):
+    """Block-level compressed branch ([P2] "What it's doing under the hood": tail_granularity
+    switches to one pooled query per query block).  Pinned by:
+      * all queries equal: pooled = own query, so both granularities give dense attention;
+      * block-constant queries under a shuffled layout: the two granularities coincide, while
+        on generic queries they differ (the option does something);
+      * one unselected block: the compressed output is that block's value summary, and the
+        pooled log-mass is the block mean of the per-query ones (the logit is linear in q);
+      * several unselected blocks: log-sum-exp of affine functions is convex in q, so the
+        pooled log-mass is below the block mean of the per-query ones (Jensen);
+      * the exact branch does not change."""
+    wl, Q, K, V = tiny_inputs
+    N, nb = wl.tokens, wl.n_blocks
+    rng = np.random.default_rng(11)
+    pq, pk = rng.permutation(N), rng.permutation(N)
+    lists = np.sort(np.stack([rng.choice(nb, 6, replace=False) for _ in range(nb)]), axis=1)
+
+    Qc = np.tile(Q[77], (N, 1))
+    out, _ = O.sparse_attention_head(Qc, K, V, pq, pk, lists, tail="block")
+    assert np.max(np.abs(out - _sdpa(Qc, K, V))) < 1e-10
+
+    Qb = np.empty_like(Q)
+    Qb[pq] = np.repeat(Q[rng.choice(N, nb)], 64, axis=0)
+    ob, lb = O.sparse_attention_head(Qb, K, V, pq, pk, lists, tail="block")
+    ot, lt = O.sparse_attention_head(Qb, K, V, pq, pk, lists)
+    assert np.max(np.abs(ob - ot)) < 1e-12 and np.max(np.abs(lb - lt)) < 1e-12
+    og, _ = O.sparse_attention_head(Q, K, V, pq, pk, lists, tail="block")
+    assert np.max(np.abs(og - O.sparse_attention_head(Q, K, V, pq, pk, lists)[0])) > 1e-3
+
+    rows = pq.reshape(nb, 64)
+    one = np.stack([np.delete(np.arange(nb), rng.integers(nb)) for _ in range(nb)])
+    kt, vt, _ = O.summaries(Q, K, V, pk)
+    rb = O.sparse_attention_head(Q, K, V, pq, pk, one, tail="block", return_branches=True)
+    rt = O.sparse_attention_head(Q, K, V, pq, pk, one, return_branches=True)
+    for i in range(nb):
+        j = np.setdiff1d(np.arange(nb), one[i])[0]
+        assert np.max(np.abs(rb[4][rows[i]] - vt[j])) < 1e-12
+        assert np.max(np.abs(rb[5][rows[i]] - rt[5][rows[i]].mean())) < 1e-10
+
+    rb = O.sparse_attention_head(Q, K, V, pq, pk, lists, tail="block", return_branches=True)
+    rt = O.sparse_attention_head(Q, K, V, pq, pk, lists, return_branches=True)
+    for i in range(nb):
+        assert np.ptp(rb[5][rows[i]]) == 0.0
+        assert rb[5][rows[i][0]] < rt[5][rows[i]].mean() - 1e-9
+    assert np.array_equal(rb[2], rt[2]) and np.array_equal(rb[3], rt[3])
+    with pytest.raises(ValueError):
+        O.sparse_attention_head(Q, K, V, pq, pk, lists, tail="query")
+
+
 def _naive_tree(X, M, leaf):
     """Independent partitioner: explicit Mahalanobis-cosine Gram matrix, principal direction
     from numpy.linalg.eigh of the centred Gram (kernel PCA), full stable sort."""
