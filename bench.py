@@ -44,10 +44,13 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def attention_flops(H, N, D, topk):
+def attention_flops(H, N, D, topk, tail="token"):
+    """Algorithmic flops of one attend: 4 D per (query, key) pair for the exact branch and per
+    (query, summary) pair for the compressed one (one pooled query per block with tail "block")."""
     nb = N // 64
     exact = 4.0 * N * (topk * 64) * D * H
-    compressed = 4.0 * N * (nb - topk) * D * H
+    rows = N if tail == "token" else nb
+    compressed = 4.0 * rows * (nb - topk) * D * H
     return exact, compressed
 
 
@@ -74,7 +77,7 @@ class Layer:
     """Device buffers and the four stage calls of one layer (Reblock or fixed-tile layouts)."""
 
     def __init__(self, ops, torch, wl, q, k, v, topk, fixed_tiles=False, ws=None,
-                 layout="separate"):
+                 layout="separate", tail="token"):
         self.ops, self.torch = ops, torch
         dev = torch.device("cuda:0")
         dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
@@ -91,7 +94,8 @@ class Layer:
         self.out = torch.empty_like(self.qd)
         self.fixed = fixed_tiles
         self.reblock_layout = ops._LAYOUTS[layout]
-        self.flags = ops.BSA_MEANPOOL if fixed_tiles else 0
+        self.flags = ((ops.BSA_MEANPOOL if fixed_tiles else 0) |
+                      (ops.BSA_TAIL_BLOCK if tail == "block" else 0))
         self.L = ops.lib()
         self.stream = ops._stream()
 
@@ -207,13 +211,13 @@ def main_headline(args, ops, synth, torch, np):
     t0 = time.perf_counter()
     q, k, v = synth.make_qkv(wl)
     log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
-    lay = Layer(ops, torch, wl, q, k, v, topk, layout=args.layout)
+    lay = Layer(ops, torch, wl, q, k, v, topk, layout=args.layout, tail=args.tail)
     ms_step, stage_ms, series = time_steps(torch, lay.stages(), args.steps, args.warmup)
     assert torch.isfinite(lay.out.float()).all().item(), "non-finite output"
     log(f"[bench] layer {ms_step:.3f} ms/step; stages " +
         ", ".join(f"{k} {v:.3f}" for k, v in stage_ms.items()))
 
-    exact_f, comp_f = attention_flops(H, N, D, topk)
+    exact_f, comp_f = attention_flops(H, N, D, topk, args.tail)
     attn_ms = stage_ms["attend"]
     achieved = (exact_f + comp_f) / (attn_ms * 1e-3) / 1e12
     dense_flops = 4.0 * N * N * D * H
@@ -283,7 +287,8 @@ def main_headline(args, ops, synth, torch, np):
         "data": "synthetic",
         "config": {"workload": wl.name, "heads": H, "tokens": N, "head_dim": D,
                    "topk_ratio": wl.topk_ratio, "topk_blocks": topk, "grid": list(wl.grid),
-                   "reblock_layout": args.layout, "parallelism": "single GPU"},
+                   "reblock_layout": args.layout, "tail_granularity": args.tail,
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                      "traffic": ATTN_TRAFFIC_BYTES.get(wl.name), "kernel": "k_attn_bf16",
@@ -404,6 +409,9 @@ def main():
     ap.add_argument("--layout", choices=("separate", "q_reuse_k"), default="separate",
                     help="reblock layouts: one tree per side (default), or the key tree "
                          "reused for the queries")
+    ap.add_argument("--tail", choices=("token", "block"), default="token",
+                    help="compressed branch per query (default) or per query block "
+                         "(the block's mean query)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",

@@ -13,7 +13,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "bsattn.h")
 
 BSA_OK, BSA_E_ARG, BSA_E_UNSUPPORTED, BSA_E_WORKSPACE, BSA_E_HIP = 0, -1, -2, -3, -4
 BSA_F32, BSA_BF16 = 0, 1
-BSA_MEANPOOL, BSA_EXACT_ONLY, BSA_COMPRESSED_ONLY = 1, 2, 4
+BSA_MEANPOOL, BSA_EXACT_ONLY, BSA_COMPRESSED_ONLY, BSA_TAIL_BLOCK = 1, 2, 4, 8
 BLOCK = 64
 
 

@@ -91,7 +91,8 @@ float resolve_scale(const bsa_desc* d, float scale) {
 
 // ----------------------------------------------------------------- workspace layouts
 struct AttnWs {
-  size_t anchor_partial, anchor, kt, vt, bias, ktsw, vtsw, ksw, vsw, total;
+  size_t anchor_partial, anchor, kt, vt, bias, ktsw, vtsw, ksw, vsw, qbar, tbits, tail_o,
+      tail_lse, total;
 };
 
 AttnWs attn_layout(const bsa_desc* d) {
@@ -110,6 +111,14 @@ AttnWs attn_layout(const bsa_desc* d) {
     w.vtsw = take(H * nt * 64 * D * 2);
     w.ksw = take(H * N * D * 2);
     w.vsw = take(H * N * D * 2);
+  }
+  // block-level compressed branch: pooled queries; for bf16 also the selection bitmaps and
+  // the per-block compressed state
+  w.qbar = take(H * nb * D * 4);
+  if (is_bf16(d)) {
+    w.tbits = take(H * nb * 2 * nt * 4);
+    w.tail_o = take(H * nb * D * 4);
+    w.tail_lse = take(H * nb * 4);
   }
   w.total = off;
   return w;
@@ -284,7 +293,7 @@ bsa_status check_attn_args(const bsa_desc* d, const void* q, const void* k, cons
   bsa_status st = check_desc(d);
   if (st != BSA_OK) return st;
   if (!q || !k || !v || !perm_k) return fail(BSA_E_ARG, "null tensor pointer");
-  const uint32_t known = BSA_MEANPOOL | BSA_EXACT_ONLY | BSA_COMPRESSED_ONLY;
+  const uint32_t known = BSA_MEANPOOL | BSA_EXACT_ONLY | BSA_COMPRESSED_ONLY | BSA_TAIL_BLOCK;
   if (flags & ~known) return fail(BSA_E_ARG, "unknown flags 0x%x", flags);
   if ((flags & BSA_EXACT_ONLY) && (flags & BSA_COMPRESSED_ONLY))
     return fail(BSA_E_ARG, "BSA_EXACT_ONLY and BSA_COMPRESSED_ONLY are exclusive");
@@ -335,11 +344,30 @@ hipError_t do_attend(const bsa_desc* d, const AttnWs& L, void* ws, const void* q
   a.bias = reinterpret_cast<const float*>(at(ws, L.bias));
   a.o = o;
   a.lse = lse;
+  // block-level compressed branch: pooled query of every query block (the block means the
+  // select stage scores with)
+  const bool tail_block = (flags & BSA_TAIL_BLOCK) && a.n_comp > 0;
+  float* qbar = reinterpret_cast<float*>(at(ws, L.qbar));
+  if (tail_block) {
+    hipError_t e = bsa::launch_block_means(is_bf16(d), q, perm_q, d->heads, d->tokens,
+                                           d->head_dim, qbar, stream);
+    if (e != hipSuccess) return e;
+  }
   if (is_bf16(d)) {
     a.ksw = at(ws, L.ksw);
     a.vsw = at(ws, L.vsw);
     a.ktsw = at(ws, L.ktsw);
     a.vtsw = at(ws, L.vtsw);
+    if (tail_block) {
+      float* tail_o = reinterpret_cast<float*>(at(ws, L.tail_o));
+      float* tail_lse = reinterpret_cast<float*>(at(ws, L.tail_lse));
+      hipError_t e = bsa::launch_tail_block_bf16(
+          a, qbar, reinterpret_cast<uint32_t*>(at(ws, L.tbits)), tail_o, tail_lse, stream);
+      if (e != hipSuccess) return e;
+      a.tail_o = tail_o;
+      a.tail_lse = tail_lse;
+      a.n_comp = 0;
+    }
     return bsa::launch_attn_bf16(a, stream);
   }
   a.k = k;
@@ -347,6 +375,7 @@ hipError_t do_attend(const bsa_desc* d, const AttnWs& L, void* ws, const void* q
   a.perm_k = perm_k;
   a.kt = reinterpret_cast<const float*>(at(ws, L.kt));
   a.vt = reinterpret_cast<const float*>(at(ws, L.vt));
+  a.qbar = tail_block ? qbar : nullptr;
   return bsa::launch_attn_f32(a, stream);
 }
 

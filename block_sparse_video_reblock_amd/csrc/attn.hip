@@ -79,13 +79,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
     const uint4* __restrict__ ksw, const uint4* __restrict__ vsw,
     const uint4* __restrict__ ktsw, const uint4* __restrict__ vtsw,
     const float* __restrict__ bias, const int32_t* __restrict__ lists, int H, int N, int nb,
-    int topk, int n_exact, int n_comp, float scale_log2, uint16_t* __restrict__ o,
-    float* __restrict__ lse) {
+    int topk, int n_exact, int n_comp, float scale_log2, const float* __restrict__ tail_o,
+    const float* __restrict__ tail_lse, uint16_t* __restrict__ o, float* __restrict__ lse) {
   constexpr int D = 128;
   __shared__ uint32_t sel_bits[kMaxSelWords];
   __shared__ float sm_m[4][64];
   __shared__ float sm_l[4][64];
   __shared__ float sm_o[64 * 129];
+  __shared__ float sm_tail[D];  // block-level compressed output of this query block
   __shared__ uint4 sq[2][8][64];  // the queries in B-operand order (see below)
   extern __shared__ float sbias[];  // [ntiles * 64] summary-row bias * log2 e, -inf if selected
 
@@ -98,31 +99,33 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
 
   // bitmap of this query block's selected key blocks (masks them in the compressed branch);
   // cleared over every summary row, padding included
-  const int words = (summary_tiles(nb) * 64 + 31) >> 5;
-  for (int w = tid; w < words; w += 256) sel_bits[w] = 0u;
-  __syncthreads();
-  for (int t = tid; t < topk; t += 256) {
-    const int j = list[t];
-    atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
-  }
-
-  // queries of the block, as the B operand of S^T = K Q^T: lane holds query 32n + l32,
-  // head-dim elements 16c + 8g .. +8
-  // (sq[n][c][lane] = the 8 elements 16c + 8g .. +8 of query 32n + l32), loaded once
   const int32_t* pq = perm_q + (size_t)h * N + (size_t)i * kBlk;
   const float* bias_h = bias + (size_t)h * ntiles * 64;
   if (n_comp > 0) {
+    const int words = (summary_tiles(nb) * 64 + 31) >> 5;
+    for (int w = tid; w < words; w += 256) sel_bits[w] = 0u;
+    __syncthreads();
+    for (int t = tid; t < topk; t += 256) {
+      const int j = list[t];
+      atomicOr(&sel_bits[j >> 5], 1u << (j & 31));
+    }
     __syncthreads();  // bitmap complete
     for (int key = tid; key < ntiles * 64; key += 256) {
       const bool sel = (sel_bits[key >> 5] >> (key & 31)) & 1u;
       sbias[key] = sel ? -INFINITY : bias_h[key] * kLog2e;  // padding rows hold -inf already
     }
   }
+  // queries of the block, as the B operand of S^T = K Q^T: lane holds query 32n + l32,
+  // head-dim elements 16c + 8g .. +8
+  // (sq[n][c][lane] = the 8 elements 16c + 8g .. +8 of query 32n + l32), loaded once
   for (int u = tid; u < 2 * 8 * 64; u += 256) {
     const int n = u >> 9, c = (u >> 6) & 7, ln = u & 63;
     const int tok = pq[32 * n + (ln & 31)];
     sq[n][c][ln] = reinterpret_cast<const uint4*>(q + ((size_t)h * N + tok) * D)[2 * c + (ln >> 5)];
   }
+  const bool tail = tail_o != nullptr;
+  if (tail && tid < D) sm_tail[tid] = tail_o[((size_t)h * nb + i) * D + tid];
+  const float lc = tail ? tail_lse[(size_t)h * nb + i] : -INFINITY;
   __syncthreads();
 
   f32x16_t acc[4][2];
@@ -298,17 +301,22 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
     }
   }
   __syncthreads();
+  // (with a block-level compressed state, that state is a fifth softmax part: max lc, sum 1,
+  // output sm_tail)
+  float wc[2];
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
     const int qq = 32 * n + l32;
-    float M = -INFINITY;
+    float M = lc;
 #pragma unroll
     for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][qq]);
     const float Mu = (M == -INFINITY) ? 0.f : M;
-    float L = 0.f;
+    const float lt = __builtin_amdgcn_exp2f(lc - Mu);
+    float L = lt;
 #pragma unroll
     for (int w = 0; w < 4; ++w) L += sm_l[w][qq] * __builtin_amdgcn_exp2f(sm_m[w][qq] - Mu);
     const float f = (L > 0.f) ? __builtin_amdgcn_exp2f(m_run[n] - Mu) / L : 0.f;
+    wc[n] = (L > 0.f) ? lt / L : 0.f;
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -322,8 +330,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
         for (int a = 0; a < 4; ++a)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int idx = (32 * n + l32) * 129 + 32 * a + 8 * (r >> 2) + 4 * g + (r & 3);
-            sm_o[idx] = (w == 0) ? acc[a][n][r] : sm_o[idx] + acc[a][n][r];
+            const int d = 32 * a + 8 * (r >> 2) + 4 * g + (r & 3);
+            const int idx = (32 * n + l32) * 129 + d;
+            sm_o[idx] = (w == 0) ? (tail ? fmaf(wc[n], sm_tail[d], acc[a][n][r]) : acc[a][n][r])
+                                 : sm_o[idx] + acc[a][n][r];
           }
     }
     __syncthreads();
@@ -345,10 +355,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
       dst[v] = u;
     }
     if (lse != nullptr && part == 0) {
-      float M = -INFINITY;
+      float M = lc;
       for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][qq]);
       const float Mu = (M == -INFINITY) ? 0.f : M;
-      float L = 0.f;
+      float L = __builtin_amdgcn_exp2f(lc - Mu);
       for (int w = 0; w < 4; ++w) L += sm_l[w][qq] * __builtin_amdgcn_exp2f(sm_m[w][qq] - Mu);
       lse[(size_t)h * N + tok] = (L > 0.f) ? (Mu + __log2f(L)) * kLn2 : -INFINITY;
     }
@@ -362,7 +372,8 @@ __global__ __launch_bounds__(64) void k_attn_f32(
     const int32_t* __restrict__ perm_q, const int32_t* __restrict__ perm_k,
     const float* __restrict__ kt, const float* __restrict__ vt, const float* __restrict__ bias,
     const int32_t* __restrict__ lists, int H, int N, int nb, int topk, int n_exact, int n_comp,
-    float scale_log2, float* __restrict__ o, float* __restrict__ lse) {
+    float scale_log2, const float* __restrict__ qbar, float* __restrict__ o,
+    float* __restrict__ lse) {
   constexpr int D = 64;
   __shared__ float sk[64][D + 1];
   __shared__ float sv[64][D + 1];
@@ -389,6 +400,11 @@ __global__ __launch_bounds__(64) void k_attn_f32(
   const float* bias_h = bias + (size_t)h * ntiles * 64;
   for (int it = 0; it < n_exact + n_comp; ++it) {
     const bool exact = it < n_exact;
+    // block-level compressed branch: the summary tiles see the block's pooled query
+    if (qbar != nullptr && it == n_exact) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) qv[d] = qbar[((size_t)h * nb + i) * D + d];
+    }
     __syncthreads();
     if (exact) {
       const int j = list[it];
@@ -439,16 +455,264 @@ __global__ __launch_bounds__(64) void k_attn_f32(
     lse[(size_t)h * N + tok] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
 }
 
+// ------------------------------------------------ block-level compressed branch (bf16 path)
+//
+// [comfy.icu "MiniMax H3 Spark Attention (SM89)", "What it's doing under the hood"]: the node's
+// tail_granularity option switches the compressed branch to one pooled query per query block.
+// Every query of block i then sees the same compressed state, so it is computed once per block:
+// a small masked attention of the nb pooled queries of a head over its summary tiles, whose
+// result the attention kernel merges in place of its summary tiles.
+
+// bits[h][i][w]: bit b set iff key block 32 w + b is in lists[h][i] (lists ascending)
+__global__ __launch_bounds__(256) void k_tail_bits(const int32_t* __restrict__ lists, size_t rows,
+                                                  int topk, int W, uint32_t* __restrict__ bits) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= rows * W) return;
+  const size_t row = idx / W;
+  const int w = int(idx - row * W), lo_key = 32 * w;
+  const int32_t* l = lists + row * topk;
+  int lo = 0, hi = topk;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (l[mid] < lo_key) lo = mid + 1; else hi = mid;
+  }
+  uint32_t word = 0u;
+  for (int t = lo; t < topk && l[t] < lo_key + 32; ++t) word |= 1u << (l[t] - lo_key);
+  bits[idx] = word;
+}
+
+// One workgroup per (64 pooled queries, head): rows i0 .. i0+63 of the head's query blocks.
+// The 4 waves take every 4th summary tile, each over all 64 rows, with the score / value MFMA
+// layout of k_attn_bf16; the pooled queries enter as bf16 hi + lo pairs (fp32 accuracy in the
+// logits, whose keys are the bf16 summary tiles).  Row r masks the blocks of its own list.
+// Output per row: the normalised compressed output and its log2-sum-exp (-inf if every block
+// is selected).
+__global__ __launch_bounds__(256, 1) void k_tail_block_bf16(
+    const float* __restrict__ qbar, const uint32_t* __restrict__ bits,
+    const uint4* __restrict__ ktsw, const uint4* __restrict__ vtsw,
+    const float* __restrict__ bias, int nb, int ntiles, float scale_log2,
+    float* __restrict__ tail_o, float* __restrict__ tail_lse) {
+  constexpr int D = 128;
+  // the query operands (32 KiB) and, after the tile loop, the merged outputs share one buffer
+  __shared__ __align__(16) float sm_o[64 * 129];
+  __shared__ float sm_m[4][64];
+  __shared__ float sm_l[4][64];
+  uint4 (*sqh)[8][64] = reinterpret_cast<uint4 (*)[8][64]>(sm_o);
+  uint4 (*sql)[8][64] = sqh + 2;
+  const int h = blockIdx.y, i0 = blockIdx.x * 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int W = 2 * ntiles;
+
+  // sqh/sql[n][c][lane]: elements 16c + 8g .. +8 of pooled row 32n + l32, split x = hi + lo
+  for (int u = tid; u < 2 * 8 * 64; u += 256) {
+    const int n = u >> 9, c = (u >> 6) & 7, ln = u & 63;
+    const int row = i0 + 32 * n + (ln & 31);
+    float x[8];
+    if (row < nb) {
+      const float4* src =
+          reinterpret_cast<const float4*>(qbar + ((size_t)h * nb + row) * D + 16 * c + 8 * (ln >> 5));
+      const float4 a = src[0], b = src[1];
+      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+      x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    }
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      hw[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+      const float r0 = x[2 * e] - bf16_to_f32(uint16_t(hw[e] & 0xFFFFu));
+      const float r1 = x[2 * e + 1] - bf16_to_f32(uint16_t(hw[e] >> 16));
+      lw[e] = pack_bf16x2(r0, r1);
+    }
+    sqh[n][c][ln] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    sql[n][c][ln] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+  }
+  __syncthreads();
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][n][r] = 0.f;
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.f, 0.f};
+  // selection words of this lane's rows (clamped: rows past nb compute unused values)
+  const uint32_t* bits_row[2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n)
+    bits_row[n] = bits + ((size_t)h * nb + min(i0 + 32 * n + l32, nb - 1)) * W;
+  const float* bias_h = bias + (size_t)h * ntiles * 64;
+
+#pragma unroll 1
+  for (int tau = wave; tau < ntiles; tau += 4) {
+    const uint4* kb = ktsw + ((size_t)h * ntiles + tau) * 1024;
+    const uint4* vb = vtsw + ((size_t)h * ntiles + tau) * 1024;
+#pragma unroll 1
+    for (int hh = 0; hh < 2; ++hh) {
+      uint4 kr[8], vr[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) kr[c] = kb[(hh * 8 + c) * 64 + lane];
+      // S^T: lane holds row 32n + l32 and keys 32hh + 8(r/4) + 4g + (r%4) of the tile
+      f32x16_t st[2];
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        f32x16_t t;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t[r] = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[c]), as_bf16x8(sqh[n][c][lane]),
+                                                      t, 0, 0, 0);
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(kr[c]), as_bf16x8(sql[n][c][lane]),
+                                                      t, 0, 0, 0);
+        st[n] = t;
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) vr[a * 2 + cc] = vb[(a * 4 + 2 * hh + cc) * 64 + lane];
+      const int key0 = tau * 64 + 32 * hh;
+      float bj[16];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 b4 = *reinterpret_cast<const float4*>(bias_h + key0 + 8 * j + 4 * g);
+        bj[4 * j + 0] = b4.x * kLog2e;
+        bj[4 * j + 1] = b4.y * kLog2e;
+        bj[4 * j + 2] = b4.z * kLog2e;
+        bj[4 * j + 3] = b4.w * kLog2e;
+      }
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        f32x16_t& t = st[n];
+        const uint32_t word = bits_row[n][2 * tau + hh];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int r = 4 * j + u;
+            const bool sel = (word >> (8 * j + 4 * g + u)) & 1u;
+            t[r] = sel ? -INFINITY : fmaf(t[r], scale_log2, bj[r]);
+            mx = fmaxf(mx, t[r]);
+          }
+        mx = xor32_max(mx);
+        const float m_new = fmaxf(m_run[n], mx);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run[n] - m_use);
+        m_run[n] = m_new;
+        l_run[n] *= alpha;
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[a][n][r] *= alpha;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) t[r] = __builtin_amdgcn_exp2f(t[r] - m_use);
+        const bf16x8_t p0 = pack8(t, 0), p1 = pack8(t, 8);
+        l_run[n] = row_sum_bf16(p1, row_sum_bf16(p0, l_run[n]));
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          acc[a][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vr[a * 2]), p0, acc[a][n],
+                                                              0, 0, 0);
+          acc[a][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vr[a * 2 + 1]), p1,
+                                                              acc[a][n], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // merge the four waves and write the rows of this group (the barrier also ends every
+  // wave's use of the query operands, whose memory the outputs reuse)
+#pragma unroll
+  for (int n = 0; n < 2; ++n) l_run[n] = xor32_sum(l_run[n]);
+  if (g == 0) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      sm_m[wave][32 * n + l32] = m_run[n];
+      sm_l[wave][32 * n + l32] = l_run[n];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    const int qq = 32 * n + l32;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][qq]);
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) L += sm_l[w][qq] * __builtin_amdgcn_exp2f(sm_m[w][qq] - Mu);
+    const float f = (L > 0.f) ? __builtin_amdgcn_exp2f(m_run[n] - Mu) / L : 0.f;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][n][r] *= f;
+  }
+  for (int w = 0; w < 4; ++w) {
+    if (wave == w) {
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int idx = (32 * n + l32) * 129 + 32 * a + 8 * (r >> 2) + 4 * g + (r & 3);
+            sm_o[idx] = (w == 0) ? acc[a][n][r] : sm_o[idx] + acc[a][n][r];
+          }
+    }
+    __syncthreads();
+  }
+  {
+    const int qq = tid >> 2, part = tid & 3, row = i0 + qq;
+    if (row < nb) {
+      float4* dst = reinterpret_cast<float4*>(tail_o + ((size_t)h * nb + row) * D + part * 32);
+      const float* src = sm_o + qq * 129 + part * 32;
+#pragma unroll
+      for (int v = 0; v < 8; ++v)
+        dst[v] = make_float4(src[4 * v], src[4 * v + 1], src[4 * v + 2], src[4 * v + 3]);
+      if (part == 0) {
+        float M = -INFINITY;
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][qq]);
+        const float Mu = (M == -INFINITY) ? 0.f : M;
+        float L = 0.f;
+        for (int w = 0; w < 4; ++w) L += sm_l[w][qq] * __builtin_amdgcn_exp2f(sm_m[w][qq] - Mu);
+        tail_lse[(size_t)h * nb + row] = (L > 0.f) ? Mu + __log2f(L) : -INFINITY;
+      }
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_tail_block_bf16(const AttnLaunch& a, const float* qbar, uint32_t* bits,
+                                  float* tail_o, float* tail_lse, hipStream_t s) {
+  const int nt = summary_tiles(a.nb);
+  const size_t rows = (size_t)a.H * a.nb;
+  const size_t words = rows * 2 * nt;
+  k_tail_bits<<<ceil_div(long(words), 256), 256, 0, s>>>(a.lists, rows, a.topk, 2 * nt, bits);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  k_tail_block_bf16<<<dim3(ceil_div(a.nb, 64), a.H), 256, 0, s>>>(
+      qbar, bits, static_cast<const uint4*>(a.ktsw), static_cast<const uint4*>(a.vtsw), a.bias,
+      a.nb, nt, a.scale * kLog2e, tail_o, tail_lse);
+  return hipGetLastError();
+}
 
 hipError_t launch_attn_bf16(const AttnLaunch& a, hipStream_t s) {
   const int grid = a.H * a.nb;
-  const size_t dyn = (size_t)summary_tiles(a.nb) * 64 * sizeof(float);
+  const size_t dyn = a.n_comp > 0 ? (size_t)summary_tiles(a.nb) * 64 * sizeof(float) : 0;
   k_attn_bf16<<<grid, 256, dyn, s>>>(
       static_cast<const uint16_t*>(a.q), a.perm_q, static_cast<const uint4*>(a.ksw),
       static_cast<const uint4*>(a.vsw), static_cast<const uint4*>(a.ktsw),
       static_cast<const uint4*>(a.vtsw), a.bias, a.lists, a.H, a.N, a.nb, a.topk, a.n_exact,
-      a.n_comp, a.scale * kLog2e, static_cast<uint16_t*>(a.o), a.lse);
+      a.n_comp, a.scale * kLog2e, a.tail_o, a.tail_lse, static_cast<uint16_t*>(a.o), a.lse);
   return hipGetLastError();
 }
 
@@ -457,7 +721,8 @@ hipError_t launch_attn_f32(const AttnLaunch& a, hipStream_t s) {
   k_attn_f32<<<grid, 64, 0, s>>>(
       static_cast<const float*>(a.q), static_cast<const float*>(a.k),
       static_cast<const float*>(a.v), a.perm_q, a.perm_k, a.kt, a.vt, a.bias, a.lists, a.H, a.N,
-      a.nb, a.topk, a.n_exact, a.n_comp, a.scale * kLog2e, static_cast<float*>(a.o), a.lse);
+      a.nb, a.topk, a.n_exact, a.n_comp, a.scale * kLog2e, a.qbar, static_cast<float*>(a.o),
+      a.lse);
   return hipGetLastError();
 }
 

@@ -44,9 +44,19 @@ struct AttnLaunch {
   const void *k, *v;
   const int32_t* perm_k;
   const float *kt, *vt;
+  // block-level compressed branch (null: per-query).  bf16: the compressed state of every query
+  // block, tail_o [H][nb][D] (normalised) and tail_lse [H][nb] (log2 units), merged in place of
+  // the summary tiles (n_comp = 0); f32: the pooled queries qbar [H][nb][D], used for the
+  // summary tiles in place of each query's own.
+  const float *tail_o, *tail_lse, *qbar;
 };
 hipError_t launch_attn_bf16(const AttnLaunch& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnLaunch& a, hipStream_t s);
+// Block-level compressed branch (bf16): from the pooled queries qbar [H][nb][D] (fp32), the
+// lists and the summary tiles of the launch `a` (n_comp ignored), the per-block state
+// tail_o / tail_lse; bits [H][nb][2 * tiles] is scratch for the selection bitmaps.
+hipError_t launch_tail_block_bf16(const AttnLaunch& a, const float* qbar, uint32_t* bits,
+                                  float* tail_o, float* tail_lse, hipStream_t s);
 
 // ------------------------------------------------------------------- select (stage 2)
 hipError_t launch_block_means(bool bf16, const void* x, const int32_t* perm, int H, int N, int D,

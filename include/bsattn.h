@@ -68,6 +68,12 @@ typedef struct {
 #define BSA_MEANPOOL 1u        /* fixed-block baseline: mean-pooled summaries, bias ln 64 */
 #define BSA_EXACT_ONLY 2u      /* debug: output only the exact branch (O_e, lse_e) */
 #define BSA_COMPRESSED_ONLY 4u /* debug: output only the compressed branch (O_c, lse_c) */
+/* tail_granularity = block (comfy.icu page, "What it's doing under the hood": the node option
+ * that switches to ComfyUI's block-level compressed branch).  Every query of query block i uses
+ * the block's pooled query, the mean of its 64 queries (in fp32), in place of its own in the
+ * compressed branch: logit s qbar_i.kt_j + b_j.  The exact branch and the merge are unchanged.
+ * bsa_prepare_kv ignores this flag. */
+#define BSA_TAIL_BLOCK 8u
 
 const char* bsa_status_str(int32_t status);
 /* Message describing the last failed call on this thread ("" if none). */
@@ -123,8 +129,8 @@ bsa_status bsa_select(const bsa_desc* desc, const void* q, const void* k,
  * bsa_summaries; the branches merge by log-sum-exp and row p of block i is written to output
  * row perm_q[h][p].  o has the input dtype, [heads][tokens][head_dim]; lse_opt (float
  * [heads][tokens], natural log) receives the merged log-sum-exp of the scaled logits.
- * scale = 0 means 1/sqrt(D).  flags: BSA_MEANPOOL, and at most one of BSA_EXACT_ONLY /
- * BSA_COMPRESSED_ONLY (an empty branch gives lse = -inf and a zero row).  With
+ * scale = 0 means 1/sqrt(D).  flags: BSA_MEANPOOL, BSA_TAIL_BLOCK, and at most one of
+ * BSA_EXACT_ONLY / BSA_COMPRESSED_ONLY (an empty branch gives lse = -inf and a zero row).  With
  * topk = nb (every block selected) this is dense softmax attention. */
 bsa_status bsa_sparse_attn(const bsa_desc* desc, const void* q, const void* k, const void* v,
                            const int32_t* perm_q, const int32_t* perm_k,
@@ -136,8 +142,10 @@ bsa_status bsa_sparse_attn(const bsa_desc* desc, const void* q, const void* k, c
  * prepared key side.  bsa_prepare_kv computes the anchor and the block summaries (and, for
  * bf16, block-contiguous copies of K and V in the MFMA operand order) into ws;
  * bsa_attend then runs the attention kernel alone.  bsa_attend must receive the same desc, k, v,
- * perm_k, flags and scale as the bsa_prepare_kv call that filled ws, with nothing else written
- * to ws in between; with that, prepare followed by attend equals bsa_sparse_attn. */
+ * perm_k, flags (BSA_TAIL_BLOCK aside) and scale as the bsa_prepare_kv call that filled ws, with
+ * nothing else written to ws in between; with that, prepare followed by attend equals
+ * bsa_sparse_attn.  With BSA_TAIL_BLOCK bsa_attend launches three more kernels (block means,
+ * selection bitmaps, the per-block compressed branch) before the attention kernel. */
 bsa_status bsa_prepare_kv(const bsa_desc* desc, const void* q, const void* k, const void* v,
                           const int32_t* perm_k, uint32_t flags, float scale,
                           void* ws, size_t ws_bytes, hipStream_t stream);

@@ -113,9 +113,10 @@ def test_summaries_parity(mid, tiny, mode):
 
 # ------------------------------------------------------------------------ attention
 
-def _oracle_attn(q, k, v, pq, pk, lists, mode="reweight", branches=False):
+def _oracle_attn(q, k, v, pq, pk, lists, mode="reweight", branches=False, tail="token"):
     outs = [O.sparse_attention_head(q[h], k[h], v[h], pq[h], pk[h], lists[h], mode=mode,
-                                    return_branches=branches) for h in range(q.shape[0])]
+                                    return_branches=branches, tail=tail)
+            for h in range(q.shape[0])]
     return [np.stack([o[i] for o in outs]) for i in range(len(outs[0]))]
 
 
@@ -192,6 +193,72 @@ def test_attention_ragged_shapes_bf16(n_blocks, topk):
                              torch.from_numpy(pq).to(DEV), torch.from_numpy(pk).to(DEV),
                              torch.from_numpy(lists).to(DEV), with_lse=True)
     ro, rl = _oracle_attn(q, k, v, pq, pk, lists)
+    g = o.float().cpu().numpy()
+    assert rel_l2(g, ro) < 1e-2 and np.max(np.abs(g - ro)) < 3e-2
+    assert np.max(np.abs(lse.cpu().numpy() - rl)) < 3e-2
+
+
+# ------------------------------------------- block-level compressed branch (tail granularity)
+
+@pytest.mark.parametrize("mode", ["reweight", "meanpool"])
+def test_attention_tail_block_bf16_mid(mid, mode):
+    """BSA_TAIL_BLOCK: the compressed branch of every query of a block uses the block's mean
+    query; the merged output, and the compressed branch alone, against the oracle's
+    tail="block"."""
+    wl, q, k, v, pq, pk, lists = mid
+    base = ops.BSA_TAIL_BLOCK | (ops.BSA_MEANPOOL if mode == "meanpool" else 0)
+    dt = torch.bfloat16
+    args = (to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), torch.from_numpy(pq).to(DEV),
+            torch.from_numpy(pk).to(DEV), torch.from_numpy(lists).to(DEV))
+    o, lse = ops.sparse_attn(*args, flags=base, with_lse=True)
+    oc, lc = ops.sparse_attn(*args, flags=base | ops.BSA_COMPRESSED_ONLY, with_lse=True)
+    ro, rl, _, _, ro_c, rl_c = _oracle_attn(q, k, v, pq, pk, lists, mode=mode, branches=True,
+                                            tail="block")
+    for got, ref in ((o, ro), (oc, ro_c)):
+        g = got.float().cpu().numpy()
+        assert rel_l2(g, ref) < 1e-2 and np.max(np.abs(g - ref)) < 3e-2
+    assert np.max(np.abs(lse.cpu().numpy() - rl)) < 3e-2
+    assert np.max(np.abs(lc.cpu().numpy() - rl_c)) < 3e-2
+    # one state per block: every row of a block holds the same compressed branch
+    H, N, D = q.shape
+    rows = torch.from_numpy(pq.astype(np.int64)).to(DEV)
+    blk = oc.float().gather(1, rows[..., None].expand(H, N, D)).view(H, N // 64, 64, D)
+    assert torch.equal(blk, blk[:, :, :1].expand_as(blk))
+    # differs from the per-query branch
+    o_tok = ops.sparse_attn(*args, flags=base & ~ops.BSA_TAIL_BLOCK)
+    assert (o.float() - o_tok.float()).abs().max().item() > 1e-2
+
+
+def test_attention_tail_block_f32_tiny(tiny):
+    wl, q, k, v, pq, pk, lists = tiny
+    dt = torch.float32
+    o, lse = ops.sparse_attn(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt),
+                             torch.from_numpy(pq).to(DEV), torch.from_numpy(pk).to(DEV),
+                             torch.from_numpy(lists).to(DEV), flags=ops.BSA_TAIL_BLOCK,
+                             with_lse=True)
+    ro, rl = _oracle_attn(q, k, v, pq, pk, lists, tail="block")
+    assert np.max(np.abs(o.cpu().numpy() - ro)) < 1e-4
+    assert np.max(np.abs(lse.cpu().numpy() - rl)) < 1e-4
+
+
+@pytest.mark.parametrize("n_blocks,topk", [(70, 9), (1, 1), (2, 1), (65, 65), (130, 3)])
+def test_attention_tail_block_ragged_bf16(n_blocks, topk):
+    """Block groups with a ragged last group of pooled queries, a single block, every block
+    selected (an empty compressed branch), three groups."""
+    rng = np.random.default_rng(100 + n_blocks)
+    H, N, D = 2, 64 * n_blocks, 128
+    q, k, v = (synth.bf16_round(rng.standard_normal((H, N, D)).astype(np.float32) * s)
+               for s in (0.3, 1.0, 1.0))
+    pq = np.stack([rng.permutation(N) for _ in range(H)]).astype(np.int32)
+    pk = np.stack([rng.permutation(N) for _ in range(H)]).astype(np.int32)
+    lists = np.sort(np.stack([[rng.choice(n_blocks, topk, replace=False) for _ in range(n_blocks)]
+                              for _ in range(H)]), axis=-1).astype(np.int32)
+    dt = torch.bfloat16
+    o, lse = ops.sparse_attn(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt),
+                             torch.from_numpy(pq).to(DEV), torch.from_numpy(pk).to(DEV),
+                             torch.from_numpy(lists).to(DEV), flags=ops.BSA_TAIL_BLOCK,
+                             with_lse=True)
+    ro, rl = _oracle_attn(q, k, v, pq, pk, lists, tail="block")
     g = o.float().cpu().numpy()
     assert rel_l2(g, ro) < 1e-2 and np.max(np.abs(g - ro)) < 3e-2
     assert np.max(np.abs(lse.cpu().numpy() - rl)) < 3e-2

@@ -113,10 +113,12 @@ def _full_layer(wl, layer):
     pq, pk = ops.reblock(qd, kd, ws=ws)
     lists, scores = ops.select(qd, kd, pq, pk, topk_ratio=wl.topk_ratio, ws=ws, with_scores=True)
     out = torch.empty_like(qd)
+    out_tb = torch.empty_like(qd)
     ops.prepare_kv(qd, kd, vd, pk, ws=ws)
     ops.attend(qd, kd, vd, pq, pk, lists, ws=ws, out=out)
+    ops.attend(qd, kd, vd, pq, pk, lists, ws=ws, out=out_tb, flags=ops.BSA_TAIL_BLOCK)
     torch.cuda.synchronize()
-    return q, k, v, pq.cpu().numpy(), pk.cpu().numpy(), lists.cpu().numpy(), scores, out
+    return q, k, v, pq.cpu().numpy(), pk.cpu().numpy(), lists.cpu().numpy(), scores, out, out_tb
 
 
 @pytest.mark.parametrize("name,layer", [("clip10s_bf16", 0), ("clip14s_bf16", 3)])
@@ -124,7 +126,7 @@ def test_full_size_layer_sampled(name, layer):
     wl = synth.WORKLOADS[name]
     H, N, nb = wl.heads, wl.tokens, wl.n_blocks
     K = O.topk_count(nb, wl.topk_ratio)
-    q, k, v, pq, pk, lists, scores, out = _full_layer(wl, layer)
+    q, k, v, pq, pk, lists, scores, out, out_tb = _full_layer(wl, layer)
     print(f"{name} layer {layer}: H={H} N={N} nb={nb} K={K}", flush=True)
     ident = np.arange(N)
     for h in range(H):
@@ -143,11 +145,14 @@ def test_full_size_layer_sampled(name, layer):
         assert np.array_equal(lists[h], O.topk_lists(got_s, K))
         lists_agree(lists[h], S, K)
         blocks = np.sort(rng.choice(nb, size=6, replace=False))
-        ro, _ = O.sparse_attention_head(Qh, Kh, Vh, pq[h], pk[h], lists[h], blocks=blocks)
         rows = np.concatenate([pq[h][64 * i:64 * i + 64] for i in blocks])
-        got = out[h, torch.from_numpy(rows).to(DEV)].float().cpu().numpy()
-        assert rel_l2(got, ro[rows]) < 1e-2, (h, rel_l2(got, ro[rows]))
-        assert np.max(np.abs(got - ro[rows])) < 3e-2
+        # per-query compressed branch, then the block-level one (tail granularity "block")
+        for o_dev, tail in ((out, "token"), (out_tb, "block")):
+            ro, _ = O.sparse_attention_head(Qh, Kh, Vh, pq[h], pk[h], lists[h], blocks=blocks,
+                                            tail=tail)
+            got = o_dev[h, torch.from_numpy(rows).to(DEV)].float().cpu().numpy()
+            assert rel_l2(got, ro[rows]) < 1e-2, (h, tail, rel_l2(got, ro[rows]))
+            assert np.max(np.abs(got - ro[rows])) < 3e-2, (h, tail)
     # the first three tree levels of head 0's query side, replayed on the oracle
     U = O.metric_embed(q[0].astype(np.float64), O.second_moment(k[0].astype(np.float64)))
     st = replay_partition(U, pq[0], None, max_level=3)

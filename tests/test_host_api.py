@@ -85,11 +85,10 @@ def test_sparse_attn_argument_errors(L):
     for k in (0, 65):
         assert L.bsa_sparse_attn(desc(), *args, k, 0, 0.0, FAKE, None, FAKE, big,
                                  None) == _lib.BSA_E_ARG
-    # unknown and exclusive flags
-    assert L.bsa_sparse_attn(desc(), *args, 4, 8, 0.0, FAKE, None, FAKE, big,
-                             None) == _lib.BSA_E_ARG
-    assert L.bsa_sparse_attn(desc(), *args, 4, 6, 0.0, FAKE, None, FAKE, big,
-                             None) == _lib.BSA_E_ARG
+    # unknown and exclusive flags (BSA_TAIL_BLOCK = 8 combines with the others)
+    for fl in (16, 1 << 31, 6, 6 | _lib.BSA_TAIL_BLOCK):
+        assert L.bsa_sparse_attn(desc(), *args, 4, fl, 0.0, FAKE, None, FAKE, big,
+                                 None) == _lib.BSA_E_ARG
     # bad scale
     for sc in (-1.0, float("nan"), float("inf")):
         assert L.bsa_sparse_attn(desc(), *args, 4, 0, sc, FAKE, None, FAKE, big,
