@@ -13,6 +13,8 @@ Sources (cited by page title and section):
        the hood" (M_K = E[k k^T] for queries, M_Q for keys; exactly-64-token leaves; only the
        permutation changes; the approximate branch keeps a real Q per query) and section
        "Inputs you'll actually set" (topk_ratio / topk_blocks budgets).
+  [P3] h3vid.app guide, section "Warmup and step counts need explicit definitions" (exact
+       handling of text, audio and conditioning context while the video grid is sparsified).
 Where the pages leave a step open the oracle takes one plain reading; each is listed in the
 functions' docstrings.  Parity-unpinned readings (fixed only by this reading, no page value):
 the power-iteration count T = 8 and its start vector, the budget rounding, the block-score

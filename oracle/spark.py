@@ -15,7 +15,8 @@ __all__ = [
     "LEAF", "second_moment", "metric_factor", "metric_embed", "tree_levels",
     "split_direction", "partition", "partition_from_projections", "reblock_head",
     "topk_count", "block_means", "block_scores", "topk_lists", "summaries",
-    "sparse_attention_head", "dense_attention_head", "recall_head", "log_mass_error_head",
+    "sparse_attention_head", "mixed_attention_head", "dense_attention_head", "recall_head",
+    "log_mass_error_head",
     "logsumexp", "fixed_tile_perm",
 ]
 
@@ -258,7 +259,7 @@ def _softmax_branch(logits: np.ndarray, values: np.ndarray):
 
 def sparse_attention_head(Q, K, V, perm_q, perm_k, lists, scale=None, mode="reweight",
                           leaf: int = LEAF, summ=None, return_branches=False, blocks=None,
-                          tail: str = "token"):
+                          tail: str = "token", ctx=None):
     """One head of the two-branch layer, output in token order.
 
     [P1] "What Spark-Attn changes": an exact branch fully computes the top-ranked K/V blocks
@@ -273,6 +274,9 @@ def sparse_attention_head(Q, K, V, perm_q, perm_k, lists, scale=None, mode="rewe
     (ComfyUI's block-level behaviour): the compressed branch of every query of block i uses
     one pooled query, the mean of the block's queries, in place of the query's own; the exact
     branch and the merge are unchanged.  Reading: "pooled" is the plain mean.
+    ctx = (K_ctx, V_ctx), context keys and values (text, audio, conditioning) that every
+    query attends exactly ([P3] "Warmup and step counts need explicit definitions": exact
+    handling of that context while the video grid is sparsified): they join the exact branch.
     Returns (O, lse) or, with return_branches, (O, lse, O_e, lse_e, O_c, lse_c).  With
     blocks (query block indices) only those blocks' rows are computed; the others hold NaN."""
     if tail not in ("token", "block"):
@@ -296,7 +300,11 @@ def sparse_attention_head(Q, K, V, perm_q, perm_k, lists, scale=None, mode="rewe
         q = Q[rows]
         sel = np.asarray(lists[i])
         keys = key_rows[sel].ravel()
-        Oe, le = _softmax_branch(s * q @ K[keys].T, V[keys])
+        Ke, Ve = K[keys], V[keys]
+        if ctx is not None:
+            Ke = np.concatenate([Ke, np.asarray(ctx[0], np.float64)])
+            Ve = np.concatenate([Ve, np.asarray(ctx[1], np.float64)])
+        Oe, le = _softmax_branch(s * q @ Ke.T, Ve)
         mask = np.ones(nb, dtype=bool)
         mask[sel] = False
         qc = q if tail == "token" else np.repeat(q.mean(axis=0, keepdims=True), leaf, axis=0)
@@ -325,6 +333,25 @@ def dense_attention_head(Q, K, V, scale=None, rows=None, chunk: int = 1024):
         lse[sl] = logsumexp(lg, axis=1)
         O[sl] = np.exp(lg - lse[sl, None]) @ V
     return O, lse
+
+
+def mixed_attention_head(Qv, Kv, Vv, Qc, Kc, Vc, perm_q, perm_k, lists, scale=None,
+                         mode="reweight", tail: str = "token", leaf: int = LEAF):
+    """One head of a mixed sequence: a video grid (Qv, Kv, Vv, [N][D], laid out by perm_q /
+    perm_k with block lists) and context tokens (Qc, Kc, Vc, [n_ctx][D]: text, audio,
+    conditioning).  [P3] "Warmup and step counts need explicit definitions": the context is
+    handled exactly while only the video grid is sparsified; [P1] "What Spark-Attn changes":
+    the Reweight anchor is the mean of the video queries.  Reading:
+      video queries:   the sparse layer over the video grid, with every context key added to
+                       the exact branch (summaries from the video tokens only);
+      context queries: dense softmax attention over all keys, context and video.
+    Returns (O_video, lse_video, O_ctx, lse_ctx), each in token order."""
+    Ov, lv = sparse_attention_head(Qv, Kv, Vv, perm_q, perm_k, lists, scale, mode, leaf,
+                                   tail=tail, ctx=(Kc, Vc))
+    Kall = np.concatenate([np.asarray(Kc, np.float64), np.asarray(Kv, np.float64)])
+    Vall = np.concatenate([np.asarray(Vc, np.float64), np.asarray(Vv, np.float64)])
+    Oc, lc = dense_attention_head(Qc, Kall, Vall, scale)
+    return Ov, lv, Oc, lc
 
 
 # ------------------------------------------------------------ fixed-tile baseline layout

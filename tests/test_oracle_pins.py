@@ -210,6 +210,45 @@ def test_tail_block_granularity(tiny_inputs):
         O.sparse_attention_head(Q, K, V, pq, pk, lists, tail="query")
 
 
+def test_mixed_sequence_context_is_exact(tiny_inputs):
+    """Mixed sequences ([P3]: exact context, sparse video grid; [P1]: anchor = mean video
+    query).  Pinned by:
+      * every video block selected: the layer is dense attention over the concatenated
+        sequence (torch SDPA), for the video and the context queries;
+      * any budget: the video output is the log-sum-exp merge of the video-only layer and
+        dense attention of the video queries over the context alone;
+      * identical video queries (context queries random): the compressed branch is exact only
+        if the anchor is the mean of the video queries, and the video output is again dense;
+      * a single context token."""
+    wl, Q, K, V = tiny_inputs
+    N, nb, D = wl.tokens, wl.n_blocks, Q.shape[1]
+    rng = np.random.default_rng(5)
+    for n_ctx in (77, 1):
+        Qc, Kc, Vc = (rng.standard_normal((n_ctx, D)) * sd for sd in (Q.std(), K.std(), V.std()))
+        pq, pk = rng.permutation(N), rng.permutation(N)
+        every = np.tile(np.arange(nb), (nb, 1))
+        Ov, lv, Oc, lc = O.mixed_attention_head(Q, K, V, Qc, Kc, Vc, pq, pk, every)
+        Kall, Vall = np.concatenate([Kc, K]), np.concatenate([Vc, V])
+        assert np.max(np.abs(Ov - _sdpa(Q, Kall, Vall))) < 1e-10
+        assert np.max(np.abs(Oc - _sdpa(Qc, Kall, Vall))) < 1e-10
+        s = 1.0 / math.sqrt(D)
+        ref_lc = torch.logsumexp(torch.from_numpy(s * Qc @ Kall.T), dim=1).numpy()
+        assert np.max(np.abs(lc - ref_lc)) < 1e-10
+
+        lists = np.sort(np.stack([rng.choice(nb, 5, replace=False) for _ in range(nb)]), axis=1)
+        Ov, lv, _, _ = O.mixed_attention_head(Q, K, V, Qc, Kc, Vc, pq, pk, lists)
+        Ol, ll = O.sparse_attention_head(Q, K, V, pq, pk, lists)
+        Ox = _sdpa(Q, Kc, Vc)
+        lx = torch.logsumexp(torch.from_numpy(s * Q @ Kc.T), dim=1).numpy()
+        lt = np.logaddexp(ll, lx)
+        ref = np.exp(ll - lt)[:, None] * Ol + np.exp(lx - lt)[:, None] * Ox
+        assert np.max(np.abs(Ov - ref)) < 1e-10 and np.max(np.abs(lv - lt)) < 1e-10
+
+        Qv = np.tile(Q[5], (N, 1))
+        Ov, _, _, _ = O.mixed_attention_head(Qv, K, V, Qc, Kc, Vc, pq, pk, lists)
+        assert np.max(np.abs(Ov - _sdpa(Qv, Kall, Vall))) < 1e-10
+
+
 def _naive_tree(X, M, leaf):
     """Independent partitioner: explicit Mahalanobis-cosine Gram matrix, principal direction
     from numpy.linalg.eigh of the centred Gram (kernel PCA), full stable sort."""
