@@ -77,7 +77,7 @@ class Layer:
     """Device buffers and the four stage calls of one layer (Reblock or fixed-tile layouts)."""
 
     def __init__(self, ops, torch, wl, q, k, v, topk, fixed_tiles=False, ws=None,
-                 layout="separate", tail="token"):
+                 layout="separate", tail="token", ctx=None):
         self.ops, self.torch = ops, torch
         dev = torch.device("cuda:0")
         dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
@@ -87,7 +87,14 @@ class Layer:
         self.topk = topk
         self.qd, self.kd, self.vd = (torch.from_numpy(x).to(dev).to(dt) for x in (q, k, v))
         self.d = ops.desc_for(self.qd)
-        self.ws = ops.workspace(self.d, dev) if ws is None else ws
+        # context tokens of a mixed sequence (exact), or none
+        self.n_ctx = 0 if ctx is None else ctx[0].shape[1]
+        if self.n_ctx:
+            self.qcd, self.kcd, self.vcd = (torch.from_numpy(x).to(dev).to(dt) for x in ctx)
+            self.out_ctx = torch.empty_like(self.qcd)
+            self.ws = ops.workspace_ctx(self.d, self.n_ctx, dev)
+        else:
+            self.ws = ops.workspace(self.d, dev) if ws is None else ws
         self.perm_q = torch.empty(self.H, self.N, dtype=torch.int32, device=dev)
         self.perm_k = torch.empty_like(self.perm_q)
         self.lists = torch.empty(self.H, self.nb, topk, dtype=torch.int32, device=dev)
@@ -126,6 +133,13 @@ class Layer:
 
     def prepare(self, pk=None, flags=None):
         p = self.p
+        if self.n_ctx:
+            self.ops.check(self.L.bsa_prepare_kv_ctx(
+                ctypes.byref(self.d), self.n_ctx, p(self.qd), p(self.kd), p(self.vd),
+                p(self.kcd), p(self.vcd), p(self.perm_k if pk is None else pk),
+                self.flags if flags is None else flags, 0.0, p(self.ws), self.ws.numel(),
+                self.stream))
+            return
         self.ops.check(self.L.bsa_prepare_kv(ctypes.byref(self.d), p(self.qd), p(self.kd),
                                              p(self.vd), p(self.perm_k if pk is None else pk),
                                              self.flags if flags is None else flags, 0.0,
@@ -134,6 +148,15 @@ class Layer:
     def attend(self, pq=None, pk=None, ls=None, flags=None, lse=None):
         p = self.p
         ls = self.lists if ls is None else ls
+        if self.n_ctx:
+            self.ops.check(self.L.bsa_attend_ctx(
+                ctypes.byref(self.d), self.n_ctx, p(self.qd), p(self.kd), p(self.vd),
+                p(self.qcd), p(self.kcd), p(self.vcd), p(self.perm_q if pq is None else pq),
+                p(self.perm_k if pk is None else pk), p(ls), int(ls.shape[-1]),
+                self.flags if flags is None else flags, 0.0, p(self.out), p(self.out_ctx),
+                None if lse is None else p(lse), None, p(self.ws), self.ws.numel(),
+                self.stream))
+            return
         self.ops.check(self.L.bsa_attend(ctypes.byref(self.d), p(self.qd), p(self.kd),
                                          p(self.vd), p(self.perm_q if pq is None else pq),
                                          p(self.perm_k if pk is None else pk), p(ls),
@@ -211,16 +234,19 @@ def main_headline(args, ops, synth, torch, np):
     t0 = time.perf_counter()
     q, k, v = synth.make_qkv(wl)
     log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
-    lay = Layer(ops, torch, wl, q, k, v, topk, layout=args.layout, tail=args.tail)
+    ctx = synth.make_ctx(wl, args.ctx, (q, k, v)) if args.ctx else None
+    lay = Layer(ops, torch, wl, q, k, v, topk, layout=args.layout, tail=args.tail, ctx=ctx)
     ms_step, stage_ms, series = time_steps(torch, lay.stages(), args.steps, args.warmup)
     assert torch.isfinite(lay.out.float()).all().item(), "non-finite output"
     log(f"[bench] layer {ms_step:.3f} ms/step; stages " +
         ", ".join(f"{k} {v:.3f}" for k, v in stage_ms.items()))
 
     exact_f, comp_f = attention_flops(H, N, D, topk, args.tail)
+    # context tokens: video queries x context keys, context queries x every key
+    exact_f += 4.0 * (N * args.ctx + args.ctx * (N + args.ctx)) * D * H
     attn_ms = stage_ms["attend"]
     achieved = (exact_f + comp_f) / (attn_ms * 1e-3) / 1e12
-    dense_flops = 4.0 * N * N * D * H
+    dense_flops = 4.0 * (N + args.ctx) ** 2 * D * H
     eff = dense_flops / (ms_step * 1e-3) / 1e12
 
     # HBM-bound stages: algorithmic bytes (inputs read once per pass the algorithm needs)
@@ -233,14 +259,16 @@ def main_headline(args, ops, synth, torch, np):
                     "passes": "moments, norms, and per tree level a statistics and a "
                               "projection pass over " + ("K" if sides == 1 else "Q and K")},
         "select": {"bytes": 2 * x_bytes + H * nb * nb * 4, "passes": "Q, K once; scores"},
-        "prepare": {"bytes": 3 * x_bytes, "passes": "Q (anchor), K, V once"},
+        "prepare": {"bytes": 3 * x_bytes + 2 * H * args.ctx * D * elt,
+                    "passes": "Q (anchor), K, V once" + (", context K, V once" if args.ctx
+                                                         else "")},
     }
     for name, h in hbm.items():
         gbs = h["bytes"] / (stage_ms[name] * 1e-3) / 1e9
         h.update({"ms": stage_ms[name], "GB/s": gbs, "frac": gbs / HBM_PEAK_GBS})
 
     dense = None
-    if not args.no_dense:
+    if not args.no_dense and not args.ctx:
         ident, every = lay.dense_inputs()
         lay.prepare(pk=ident, flags=ops.BSA_EXACT_ONLY)
         cur = torch.cuda.current_stream()
@@ -261,7 +289,7 @@ def main_headline(args, ops, synth, torch, np):
         del every
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.ctx:
         log("[bench] timing the CPU oracle on head 0 ...")
         t_head, threads = cpu_baseline(wl, q, k, v)
         layer_s = t_head * H
@@ -288,6 +316,7 @@ def main_headline(args, ops, synth, torch, np):
         "config": {"workload": wl.name, "heads": H, "tokens": N, "head_dim": D,
                    "topk_ratio": wl.topk_ratio, "topk_blocks": topk, "grid": list(wl.grid),
                    "reblock_layout": args.layout, "tail_granularity": args.tail,
+                   "context_tokens": args.ctx,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
@@ -412,6 +441,9 @@ def main():
     ap.add_argument("--tail", choices=("token", "block"), default="token",
                     help="compressed branch per query (default) or per query block "
                          "(the block's mean query)")
+    ap.add_argument("--ctx", type=int, default=0, metavar="N",
+                    help="mixed sequence: N exact context tokens (text, audio, conditioning) "
+                         "beside the video grid")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",

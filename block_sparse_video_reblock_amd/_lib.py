@@ -50,6 +50,17 @@ _SIGS = {
                                     ctypes.c_size_t, _P]),
     "bsa_summaries": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), _P, _P, _P, _P, ctypes.c_uint32,
                                        ctypes.c_float, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "bsa_workspace_bytes_ctx": (ctypes.c_size_t, [ctypes.POINTER(BsaDesc), ctypes.c_int32]),
+    "bsa_sparse_attn_ctx": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), ctypes.c_int32, _P, _P, _P,
+                                             _P, _P, _P, _P, _P, _P, ctypes.c_int32,
+                                             ctypes.c_uint32, ctypes.c_float, _P, _P, _P, _P, _P,
+                                             ctypes.c_size_t, _P]),
+    "bsa_prepare_kv_ctx": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), ctypes.c_int32, _P, _P, _P,
+                                            _P, _P, _P, ctypes.c_uint32, ctypes.c_float, _P,
+                                            ctypes.c_size_t, _P]),
+    "bsa_attend_ctx": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), ctypes.c_int32, _P, _P, _P, _P,
+                                        _P, _P, _P, _P, _P, ctypes.c_int32, ctypes.c_uint32,
+                                        ctypes.c_float, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "bsa_partition_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int32, ctypes.c_int32]),
     "bsa_reblock_from_projections": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
                                                       ctypes.c_size_t, _P]),
@@ -191,6 +202,42 @@ def sparse_attn(q, k, v, perm_q, perm_k, lists, flags=0, scale=0.0, ws=None, wit
                                 _dev_ptr(o, q.dtype), _dev_ptr(lse), _dev_ptr(ws), ws.numel(),
                                 _stream()))
     return (o, lse) if with_lse else o
+
+
+def workspace_ctx(desc: BsaDesc, n_ctx: int, device="cuda"):
+    n = lib().bsa_workspace_bytes_ctx(ctypes.byref(desc), int(n_ctx))
+    if n == 0:
+        raise BsaError(BSA_E_ARG, "invalid descriptor or context length")
+    return _torch().empty(n, dtype=_torch().uint8, device=device)
+
+
+def sparse_attn_ctx(q, k, v, q_ctx, k_ctx, v_ctx, perm_q, perm_k, lists, flags=0, scale=0.0,
+                    ws=None, with_lse=False):
+    """Mixed sequence: video q, k, v [H][N][D] (sparse, laid out by perm_q / perm_k and lists)
+    and context q_ctx, k_ctx, v_ctx [H][n_ctx][D] (exact).  Returns (o, o_ctx) or, with_lse,
+    (o, o_ctx, lse, lse_ctx)."""
+    torch = _torch()
+    d = desc_for(q)
+    H, N, D = q.shape
+    n_ctx = q_ctx.shape[1]
+    for t in (q_ctx, k_ctx, v_ctx):
+        if tuple(t.shape) != (H, n_ctx, D):
+            raise ValueError(f"context tensors must be [{H}][n_ctx][{D}], got {tuple(t.shape)}")
+    ws = workspace_ctx(d, n_ctx, q.device) if ws is None else ws
+    o = torch.empty_like(q)
+    o_ctx = torch.empty_like(q_ctx)
+    lse = lse_ctx = None
+    if with_lse:
+        lse = torch.empty(H, N, dtype=torch.float32, device=q.device)
+        lse_ctx = torch.empty(H, n_ctx, dtype=torch.float32, device=q.device)
+    check(lib().bsa_sparse_attn_ctx(
+        ctypes.byref(d), int(n_ctx), _dev_ptr(q, q.dtype), _dev_ptr(k, q.dtype),
+        _dev_ptr(v, q.dtype), _dev_ptr(q_ctx, q.dtype), _dev_ptr(k_ctx, q.dtype),
+        _dev_ptr(v_ctx, q.dtype), _dev_ptr(perm_q, torch.int32), _dev_ptr(perm_k, torch.int32),
+        _dev_ptr(lists, torch.int32), int(lists.shape[-1]), int(flags), float(scale),
+        _dev_ptr(o, q.dtype), _dev_ptr(o_ctx, q.dtype), _dev_ptr(lse), _dev_ptr(lse_ctx),
+        _dev_ptr(ws), ws.numel(), _stream()))
+    return (o, o_ctx, lse, lse_ctx) if with_lse else (o, o_ctx)
 
 
 def prepare_kv(q, k, v, perm_k, ws, flags=0, scale=0.0):

@@ -92,10 +92,10 @@ float resolve_scale(const bsa_desc* d, float scale) {
 // ----------------------------------------------------------------- workspace layouts
 struct AttnWs {
   size_t anchor_partial, anchor, kt, vt, bias, ktsw, vtsw, ksw, vsw, qbar, tbits, tail_o,
-      tail_lse, total;
+      tail_lse, ctsw, cvsw, total;
 };
 
-AttnWs attn_layout(const bsa_desc* d) {
+AttnWs attn_layout(const bsa_desc* d, int n_ctx = 0) {
   const size_t H = d->heads, N = d->tokens, D = d->head_dim, nb = N / 64;
   const size_t nt = bsa::summary_tiles(int(nb));
   AttnWs w{};
@@ -120,9 +120,23 @@ AttnWs attn_layout(const bsa_desc* d) {
     w.tail_o = take(H * nb * D * 4);
     w.tail_lse = take(H * nb * 4);
   }
+  // context tokens (bf16 path): swizzled 64-row tiles of their keys and values
+  if (is_bf16(d) && n_ctx > 0) {
+    const size_t nc = bsa::ceil_div(n_ctx, 64);
+    w.ctsw = take(H * nc * 64 * D * 2);
+    w.cvsw = take(H * nc * 64 * D * 2);
+  }
   w.total = off;
   return w;
 }
+
+// context tokens of a mixed sequence (n = 0: none)
+struct Ctx {
+  int n;
+  const void *q, *k, *v;
+  void* o;
+  float* lse;
+};
 
 struct SelWs {
   size_t qm, km, scores, total;
@@ -311,7 +325,7 @@ bsa_status check_attend_args(const bsa_desc* d, const int32_t* perm_q, const int
 
 hipError_t do_prepare(const bsa_desc* d, const AttnWs& L, void* ws, const void* q,
                       const void* k, const void* v, const int32_t* perm_k, uint32_t flags,
-                      float sc, hipStream_t stream) {
+                      float sc, hipStream_t stream, const Ctx& ctx = Ctx{}) {
   const bool bf = is_bf16(d);
   const int nb = d->tokens / BSA_BLOCK, nt = bsa::summary_tiles(nb);
   float* kt = reinterpret_cast<float*>(at(ws, L.kt));
@@ -322,21 +336,44 @@ hipError_t do_prepare(const bsa_desc* d, const AttnWs& L, void* ws, const void* 
   if (e == hipSuccess && bf)
     e = bsa::launch_summary_tiles(kt, vt, bias, d->heads, nb, at(ws, L.ktsw), at(ws, L.vtsw),
                                   stream);
+  if (e == hipSuccess && bf && ctx.n > 0)
+    e = bsa::launch_ctx_tiles(ctx.k, ctx.v, d->heads, ctx.n, at(ws, L.ctsw), at(ws, L.cvsw),
+                              stream);
   return e;
 }
 
 hipError_t do_attend(const bsa_desc* d, const AttnWs& L, void* ws, const void* q,
                      const void* k, const void* v, const int32_t* perm_q,
                      const int32_t* perm_k, const int32_t* lists, int32_t topk, uint32_t flags,
-                     float sc, void* o, float* lse, hipStream_t stream) {
+                     float sc, void* o, float* lse, hipStream_t stream,
+                     const Ctx& ctx = Ctx{}) {
   const int nb = d->tokens / BSA_BLOCK, nt = bsa::summary_tiles(nb);
+  const int nt_c = ctx.n > 0 ? bsa::ceil_div(ctx.n, 64) : 0;
+  const bool exact_on = !(flags & BSA_COMPRESSED_ONLY), comp_on = !(flags & BSA_EXACT_ONLY);
+  // block-level compressed branch: pooled query of every query block (the block means the
+  // select stage scores with)
+  const bool tail_block = (flags & BSA_TAIL_BLOCK) && comp_on;
   bsa::AttnLaunch a{};
   a.H = d->heads;
   a.N = d->tokens;
   a.nb = nb;
   a.topk = topk;
-  a.n_exact = (flags & BSA_COMPRESSED_ONLY) ? 0 : topk;
-  a.n_comp = (flags & BSA_EXACT_ONLY) ? 0 : nt;
+  // video queries: exact tiles, then the biased tiles (summary tiles unless the compressed
+  // branch is off or computed per block on the bf16 path, then context tiles, which belong to
+  // the exact branch)
+  a.n_exact = exact_on ? topk : 0;
+  const bool summ_tiles = comp_on && !(tail_block && is_bf16(d));
+  a.tau0 = summ_tiles ? 0 : nt;
+  a.n_comp = (summ_tiles ? nt : 0) + (exact_on ? nt_c : 0);
+  // context queries: every video block and every context tile, all exact
+  a.n_ctx = ctx.n;
+  a.ctx_n_exact = exact_on ? nb : 0;
+  a.ctx_n_comp = exact_on ? nt_c : 0;
+  a.q_ctx = ctx.q;
+  a.k_ctx = ctx.k;
+  a.v_ctx = ctx.v;
+  a.o_ctx = ctx.o;
+  a.lse_ctx = ctx.lse;
   a.scale = sc;
   a.q = q;
   a.perm_q = perm_q;
@@ -344,9 +381,6 @@ hipError_t do_attend(const bsa_desc* d, const AttnWs& L, void* ws, const void* q
   a.bias = reinterpret_cast<const float*>(at(ws, L.bias));
   a.o = o;
   a.lse = lse;
-  // block-level compressed branch: pooled query of every query block (the block means the
-  // select stage scores with)
-  const bool tail_block = (flags & BSA_TAIL_BLOCK) && a.n_comp > 0;
   float* qbar = reinterpret_cast<float*>(at(ws, L.qbar));
   if (tail_block) {
     hipError_t e = bsa::launch_block_means(is_bf16(d), q, perm_q, d->heads, d->tokens,
@@ -358,6 +392,10 @@ hipError_t do_attend(const bsa_desc* d, const AttnWs& L, void* ws, const void* q
     a.vsw = at(ws, L.vsw);
     a.ktsw = at(ws, L.ktsw);
     a.vtsw = at(ws, L.vtsw);
+    if (ctx.n > 0) {
+      a.ctsw = at(ws, L.ctsw);
+      a.cvsw = at(ws, L.cvsw);
+    }
     if (tail_block) {
       float* tail_o = reinterpret_cast<float*>(at(ws, L.tail_o));
       float* tail_lse = reinterpret_cast<float*>(at(ws, L.tail_lse));
@@ -366,7 +404,6 @@ hipError_t do_attend(const bsa_desc* d, const AttnWs& L, void* ws, const void* q
       if (e != hipSuccess) return e;
       a.tail_o = tail_o;
       a.tail_lse = tail_lse;
-      a.n_comp = 0;
     }
     return bsa::launch_attn_bf16(a, stream);
   }
@@ -431,6 +468,87 @@ bsa_status bsa_sparse_attn(const bsa_desc* d, const void* q, const void* k, cons
   if (e != hipSuccess) return hip_status(e, "prepare launch");
   return hip_status(do_attend(d, L, ws, q, k, v, perm_q, perm_k, lists, topk, flags, sc, o,
                               lse_opt, stream),
+                    "attention launch");
+}
+
+size_t bsa_workspace_bytes_ctx(const bsa_desc* d, int32_t n_ctx) {
+  const size_t base = bsa_workspace_bytes(d);
+  if (base == 0 || n_ctx < 0 || n_ctx > BSA_MAX_TOKENS ||
+      (int64_t)d->heads * n_ctx > (int64_t)1 << 30)
+    return 0;
+  const size_t a = attn_layout(d, n_ctx).total;
+  return a > base ? a : base;
+}
+
+namespace {
+
+// the checks shared by the mixed-sequence calls (phase: 0 both, 1 prepare, 2 attend)
+bsa_status check_ctx_call(const bsa_desc* d, int32_t n_ctx, const void* q, const void* k,
+                          const void* v, const void* q_ctx, const void* k_ctx, const void* v_ctx,
+                          const int32_t* perm_q, const int32_t* perm_k, const int32_t* lists,
+                          int32_t topk, uint32_t flags, float scale, const void* o,
+                          const void* o_ctx, const void* ws, size_t ws_bytes, int phase) {
+  bsa_status st = check_attn_args(d, q, k, v, perm_k, flags, scale);
+  if (st != BSA_OK) return st;
+  if (phase != 1) {
+    st = check_attend_args(d, perm_q, lists, topk, const_cast<void*>(o));
+    if (st != BSA_OK) return st;
+  }
+  if (n_ctx < 0 || n_ctx > BSA_MAX_TOKENS || (int64_t)d->heads * n_ctx > (int64_t)1 << 30)
+    return fail(BSA_E_ARG, "n_ctx = %d is out of range", n_ctx);
+  if (n_ctx > 0 && (!k_ctx || !v_ctx || (phase != 1 && (!q_ctx || !o_ctx))))
+    return fail(BSA_E_ARG, "null context tensor pointer");
+  st = check_ws(ws, ws_bytes, attn_layout(d, n_ctx).total);
+  if (st != BSA_OK) return st;
+  return check_device();
+}
+
+}  // namespace
+
+bsa_status bsa_sparse_attn_ctx(const bsa_desc* d, int32_t n_ctx, const void* q, const void* k,
+                               const void* v, const void* q_ctx, const void* k_ctx,
+                               const void* v_ctx, const int32_t* perm_q, const int32_t* perm_k,
+                               const int32_t* lists, int32_t topk, uint32_t flags, float scale,
+                               void* o, void* o_ctx, float* lse_opt, float* lse_ctx_opt,
+                               void* ws, size_t ws_bytes, hipStream_t stream) {
+  bsa_status st = check_ctx_call(d, n_ctx, q, k, v, q_ctx, k_ctx, v_ctx, perm_q, perm_k, lists,
+                                 topk, flags, scale, o, o_ctx, ws, ws_bytes, 0);
+  if (st != BSA_OK) return st;
+  const AttnWs L = attn_layout(d, n_ctx);
+  const float sc = resolve_scale(d, scale);
+  const Ctx ctx{n_ctx, q_ctx, k_ctx, v_ctx, o_ctx, lse_ctx_opt};
+  hipError_t e = do_prepare(d, L, ws, q, k, v, perm_k, flags, sc, stream, ctx);
+  if (e != hipSuccess) return hip_status(e, "prepare launch");
+  return hip_status(do_attend(d, L, ws, q, k, v, perm_q, perm_k, lists, topk, flags, sc, o,
+                              lse_opt, stream, ctx),
+                    "attention launch");
+}
+
+bsa_status bsa_prepare_kv_ctx(const bsa_desc* d, int32_t n_ctx, const void* q, const void* k,
+                              const void* v, const void* k_ctx, const void* v_ctx,
+                              const int32_t* perm_k, uint32_t flags, float scale, void* ws,
+                              size_t ws_bytes, hipStream_t stream) {
+  bsa_status st = check_ctx_call(d, n_ctx, q, k, v, nullptr, k_ctx, v_ctx, nullptr, perm_k,
+                                 nullptr, 0, flags, scale, nullptr, nullptr, ws, ws_bytes, 1);
+  if (st != BSA_OK) return st;
+  const Ctx ctx{n_ctx, nullptr, k_ctx, v_ctx, nullptr, nullptr};
+  return hip_status(do_prepare(d, attn_layout(d, n_ctx), ws, q, k, v, perm_k, flags,
+                               resolve_scale(d, scale), stream, ctx),
+                    "prepare launch");
+}
+
+bsa_status bsa_attend_ctx(const bsa_desc* d, int32_t n_ctx, const void* q, const void* k,
+                          const void* v, const void* q_ctx, const void* k_ctx, const void* v_ctx,
+                          const int32_t* perm_q, const int32_t* perm_k, const int32_t* lists,
+                          int32_t topk, uint32_t flags, float scale, void* o, void* o_ctx,
+                          float* lse_opt, float* lse_ctx_opt, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  bsa_status st = check_ctx_call(d, n_ctx, q, k, v, q_ctx, k_ctx, v_ctx, perm_q, perm_k, lists,
+                                 topk, flags, scale, o, o_ctx, ws, ws_bytes, 2);
+  if (st != BSA_OK) return st;
+  const Ctx ctx{n_ctx, q_ctx, k_ctx, v_ctx, o_ctx, lse_ctx_opt};
+  return hip_status(do_attend(d, attn_layout(d, n_ctx), ws, q, k, v, perm_q, perm_k, lists,
+                              topk, flags, resolve_scale(d, scale), o, lse_opt, stream, ctx),
                     "attention launch");
 }
 

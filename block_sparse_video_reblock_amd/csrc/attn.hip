@@ -31,6 +31,12 @@ constexpr int kMaxSelWords = (1 << 19) / 64 / 32;   // bitmap words for the larg
 
 BSA_DEV bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// A wave-uniform read of memory that no kernel writes while it runs, through the constant
+// address space: a scalar load (counted by lgkmcnt, so waiting for it never waits for the
+// vector loads in flight).
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+BSA_DEV int load_uniform(const int32_t* p) { return *(const_i32_ptr)p; }
+
 // word 3 of a raw buffer resource: 32-bit data format (untyped loads need a nonzero format)
 constexpr int kBufferDword3 = 0x00020000;
 
@@ -74,13 +80,37 @@ BSA_DEV int xcd_remap(int bid, int total) {
   return x * q + min(x, r) + k;
 }
 
-__global__ __launch_bounds__(256, 2) void k_attn_bf16(
-    const uint16_t* __restrict__ q, const int32_t* __restrict__ perm_q,
-    const uint4* __restrict__ ksw, const uint4* __restrict__ vsw,
-    const uint4* __restrict__ ktsw, const uint4* __restrict__ vtsw,
-    const float* __restrict__ bias, const int32_t* __restrict__ lists, int H, int N, int nb,
-    int topk, int n_exact, int n_comp, float scale_log2, const float* __restrict__ tail_o,
-    const float* __restrict__ tail_lse, uint16_t* __restrict__ o, float* __restrict__ lse) {
+// One set of query blocks of an attention launch and the work list of each block.
+struct QSide {
+  const uint16_t* q;     // [H][rows][D]
+  const int32_t* perm;   // [H][rows] layout (block i = rows perm[64 i ..]), or null: block i
+                         // holds rows 64 i .. 64 i + 63; rows past `rows` are padding, not written
+  bool listed;           // exact key blocks from the kernel's lists [H][nbq][topk]; else
+                         // blocks 0 .. n_exact - 1
+  const float* tail_o;   // block-level compressed state [H][nbq][D], [H][nbq] (log2), or null
+  const float* tail_lse;
+  uint16_t* o;           // [H][rows][D]
+  float* lse;            // [H][rows] (natural log) or null
+  int rows, nbq, topk;
+  int n_exact;           // exact key tiles per block
+  int n_comp, tau0;      // biased tiles tau0 .. tau0 + n_comp - 1: summary tiles 0 .. nt_s - 1,
+                         // then context tiles nt_s .. nt_s + nt_c - 1
+};
+// The key side: key / value blocks, summary tiles and context tiles, all in MFMA operand order.
+struct KSide {
+  const uint4 *ksw, *vsw;    // [H][nb][1024]
+  const uint4 *ktsw, *vtsw;  // [H][nt_s][1024]
+  const float* bias;         // [H][nt_s * 64] summary bias, -inf on padding rows
+  const uint4 *ctsw, *cvsw;  // [H][nt_c][1024], rows past n_ctx zero
+  int nb, nt_s, nt_c, n_ctx;
+};
+
+// Workgroups 0 .. wg_c - 1 take the query blocks of side `cs` (context queries: few, long
+// blocks, dispatched first and spread over every XCD), the rest those of side `vs`.  The lists
+// are a separate read-only argument so that the work loop reads them with scalar loads.
+__global__ __launch_bounds__(256, 2) void k_attn_bf16(QSide cs, QSide vs, int wg_c, KSide ks,
+                                                       const int32_t* __restrict__ lists, int H,
+                                                       float scale_log2) {
   constexpr int D = 128;
   __shared__ uint32_t sel_bits[kMaxSelWords];
   __shared__ float sm_m[4][64];
@@ -88,21 +118,26 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
   __shared__ float sm_o[64 * 129];
   __shared__ float sm_tail[D];  // block-level compressed output of this query block
   __shared__ uint4 sq[2][8][64];  // the queries in B-operand order (see below)
-  extern __shared__ float sbias[];  // [ntiles * 64] summary-row bias * log2 e, -inf if selected
+  // [nt_s * 64] summary-row bias * log2 e (-inf if selected), then with context tiles two
+  // 64-row masks: 0 for a full context tile, 0 / -inf for the valid / padding rows of the last
+  extern __shared__ float sbias[];
 
-  const int logical = xcd_remap(blockIdx.x, H * nb);
-  const int h = logical / nb, i = logical - h * nb;
+  const bool is_ctx = blockIdx.x < wg_c;
+  const QSide S = is_ctx ? cs : vs;
+  const int local = is_ctx ? blockIdx.x : xcd_remap(blockIdx.x - wg_c, H * vs.nbq);
+  const int h = local / S.nbq, i = local - h * S.nbq;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
-  const int ntiles = summary_tiles(nb);
-  const int32_t* list = lists + ((size_t)h * nb + i) * topk;
+  const int ntiles = ks.nt_s, nb = ks.nb;
+  const int n_exact = S.n_exact, n_comp = S.n_comp, tau0 = S.tau0, topk = S.topk;
+  const int32_t* list = S.listed ? lists + ((size_t)h * S.nbq + i) * topk : nullptr;
 
   // bitmap of this query block's selected key blocks (masks them in the compressed branch);
   // cleared over every summary row, padding included
-  const int32_t* pq = perm_q + (size_t)h * N + (size_t)i * kBlk;
-  const float* bias_h = bias + (size_t)h * ntiles * 64;
-  if (n_comp > 0) {
-    const int words = (summary_tiles(nb) * 64 + 31) >> 5;
+  const int32_t* pq = S.perm ? S.perm + (size_t)h * S.rows + (size_t)i * kBlk : nullptr;
+  const float* bias_h = ks.bias + (size_t)h * ntiles * 64;
+  if (n_comp > 0 && tau0 < ntiles) {
+    const int words = (ntiles * 64 + 31) >> 5;
     for (int w = tid; w < words; w += 256) sel_bits[w] = 0u;
     __syncthreads();
     for (int t = tid; t < topk; t += 256) {
@@ -115,17 +150,22 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
       sbias[key] = sel ? -INFINITY : bias_h[key] * kLog2e;  // padding rows hold -inf already
     }
   }
+  if (n_comp > 0 && ks.nt_c > 0 && tid < 128) {
+    const int last_rows = ks.n_ctx - (ks.nt_c - 1) * 64;
+    sbias[ntiles * 64 + tid] = (tid < 64 || tid - 64 < last_rows) ? 0.f : -INFINITY;
+  }
   // queries of the block, as the B operand of S^T = K Q^T: lane holds query 32n + l32,
   // head-dim elements 16c + 8g .. +8
   // (sq[n][c][lane] = the 8 elements 16c + 8g .. +8 of query 32n + l32), loaded once
   for (int u = tid; u < 2 * 8 * 64; u += 256) {
     const int n = u >> 9, c = (u >> 6) & 7, ln = u & 63;
-    const int tok = pq[32 * n + (ln & 31)];
-    sq[n][c][ln] = reinterpret_cast<const uint4*>(q + ((size_t)h * N + tok) * D)[2 * c + (ln >> 5)];
+    const int r = 32 * n + (ln & 31);
+    const int tok = pq ? pq[r] : min(i * kBlk + r, S.rows - 1);
+    sq[n][c][ln] =
+        reinterpret_cast<const uint4*>(S.q + ((size_t)h * S.rows + tok) * D)[2 * c + (ln >> 5)];
   }
-  const bool tail = tail_o != nullptr;
-  if (tail && tid < D) sm_tail[tid] = tail_o[((size_t)h * nb + i) * D + tid];
-  const float lc = tail ? tail_lse[(size_t)h * nb + i] : -INFINITY;
+  const bool tail = S.tail_o != nullptr;
+  if (tail && tid < D) sm_tail[tid] = S.tail_o[((size_t)h * S.nbq + i) * D + tid];
   __syncthreads();
 
   f32x16_t acc[4][2];
@@ -151,16 +191,24 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
     if (it >= it_end) return;
     auto tile_ptrs = [&](int t, const uint4*& kp, const uint4*& vp, int& k0) {
       if (EXACT) {
-        const size_t blk = (size_t)h * nb + list[t];
-        kp = ksw + blk * 1024;
-        vp = vsw + blk * 1024;
+        const size_t blk = (size_t)h * nb + (list ? load_uniform(list + t) : t);
+        kp = ks.ksw + blk * 1024;
+        vp = ks.vsw + blk * 1024;
         k0 = 0;
       } else {
-        const int tau = t - n_exact;
-        const size_t blk = (size_t)h * ntiles + tau;
-        kp = ktsw + blk * 1024;
-        vp = vtsw + blk * 1024;
-        k0 = tau * 64;
+        const int tau = t - n_exact + tau0;
+        if (tau < ntiles) {
+          const size_t blk = (size_t)h * ntiles + tau;
+          kp = ks.ktsw + blk * 1024;
+          vp = ks.vtsw + blk * 1024;
+          k0 = tau * 64;
+        } else {
+          const int ct = tau - ntiles;
+          const size_t blk = (size_t)h * ks.nt_c + ct;
+          kp = ks.ctsw + blk * 1024;
+          vp = ks.cvsw + blk * 1024;
+          k0 = (ntiles + (ct == ks.nt_c - 1 ? 1 : 0)) * 64;
+        }
       }
     };
     const uint4 *kb, *vb;
@@ -303,6 +351,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
   __syncthreads();
   // (with a block-level compressed state, that state is a fifth softmax part: max lc, sum 1,
   // output sm_tail)
+  const float lc = tail ? S.tail_lse[(size_t)h * S.nbq + i] : -INFINITY;
   float wc[2];
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
@@ -340,10 +389,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
   }
 
   // inverse permutation: row qq of the block is token perm_q[64 i + qq]
-  {
-    const int qq = tid >> 2, part = tid & 3;
-    const int tok = pq[qq];
-    uint4* dst = reinterpret_cast<uint4*>(o + ((size_t)h * N + tok) * D + part * 32);
+  const int qq = tid >> 2, part = tid & 3;
+  const int tok = pq ? pq[qq] : i * kBlk + qq;
+  if (tok < S.rows) {
+    uint4* dst = reinterpret_cast<uint4*>(S.o + ((size_t)h * S.rows + tok) * D + part * 32);
     const float* src = sm_o + qq * 129 + part * 32;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
@@ -354,74 +403,105 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
       u.w = pack_bf16x2(src[8 * v + 6], src[8 * v + 7]);
       dst[v] = u;
     }
-    if (lse != nullptr && part == 0) {
+    if (S.lse != nullptr && part == 0) {
       float M = lc;
       for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][qq]);
       const float Mu = (M == -INFINITY) ? 0.f : M;
       float L = __builtin_amdgcn_exp2f(lc - Mu);
       for (int w = 0; w < 4; ++w) L += sm_l[w][qq] * __builtin_amdgcn_exp2f(sm_m[w][qq] - Mu);
-      lse[(size_t)h * N + tok] = (L > 0.f) ? (Mu + __log2f(L)) * kLn2 : -INFINITY;
+      S.lse[(size_t)h * S.rows + tok] = (L > 0.f) ? (Mu + __log2f(L)) * kLn2 : -INFINITY;
     }
   }
 }
 
 // fp32 path (D = 64): one wave per (head, query block), one query per lane, K/V tiles staged
-// in LDS.  Plain fp32 FMA arithmetic.
-__global__ __launch_bounds__(64) void k_attn_f32(
-    const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    const int32_t* __restrict__ perm_q, const int32_t* __restrict__ perm_k,
-    const float* __restrict__ kt, const float* __restrict__ vt, const float* __restrict__ bias,
-    const int32_t* __restrict__ lists, int H, int N, int nb, int topk, int n_exact, int n_comp,
-    float scale_log2, const float* __restrict__ qbar, float* __restrict__ o,
-    float* __restrict__ lse) {
+// in LDS.  Plain fp32 FMA arithmetic.  Query and key sides as in the bf16 kernel, with plain
+// row-major tensors in place of the swizzled tiles.
+struct QSide32 {
+  const float* q;        // [H][rows][D]
+  const int32_t* perm;   // [H][rows] or null (identity blocks, padding rows not written)
+  const int32_t* lists;  // [H][nbq][topk] or null (blocks 0 .. n_exact - 1)
+  const float* qbar;     // pooled query per block [H][nbq][D] for the summary tiles, or null
+  float* o;              // [H][rows][D]
+  float* lse;            // [H][rows] or null
+  int rows, nbq, topk, n_exact, n_comp, tau0;
+};
+struct KSide32 {
+  const float *k, *v;       // video keys / values [H][N][D]
+  const int32_t* perm_k;    // [H][N]
+  const float *kt, *vt;     // summaries [H][nb][D]
+  const float* bias;        // [H][nt_s * 64]
+  const float *kc, *vc;     // context keys / values [H][n_ctx][D]
+  int N, nb, nt_s, nt_c, n_ctx;
+};
+
+__global__ __launch_bounds__(64) void k_attn_f32(QSide32 cs, QSide32 vs, int wg_c, KSide32 ks,
+                                                 int H, float scale_log2) {
   constexpr int D = 64;
   __shared__ float sk[64][D + 1];
   __shared__ float sv[64][D + 1];
   __shared__ float sb[64];
   __shared__ uint32_t sel_bits[kMaxSelWords];
-  const int logical = xcd_remap(blockIdx.x, H * nb);
-  const int h = logical / nb, i = logical - h * nb;
+  const bool is_ctx = blockIdx.x < wg_c;
+  const QSide32 S = is_ctx ? cs : vs;
+  const int local = is_ctx ? blockIdx.x : xcd_remap(blockIdx.x - wg_c, H * vs.nbq);
+  const int h = local / S.nbq, i = local - h * S.nbq;
   const int t = threadIdx.x;
-  const int ntiles = summary_tiles(nb);
-  const int32_t* list = lists + ((size_t)h * nb + i) * topk;
+  const int nb = ks.nb, ntiles = ks.nt_s, N = ks.N;
+  const int n_exact = S.n_exact, n_comp = S.n_comp, tau0 = S.tau0, topk = S.topk;
+  const int32_t* list = S.lists ? S.lists + ((size_t)h * S.nbq + i) * topk : nullptr;
   const int words = (nb + 31) >> 5;
   for (int w = t; w < words; w += 64) sel_bits[w] = 0u;
   __syncthreads();
-  for (int x = t; x < topk; x += 64) atomicOr(&sel_bits[list[x] >> 5], 1u << (list[x] & 31));
+  if (list != nullptr)
+    for (int x = t; x < topk; x += 64) atomicOr(&sel_bits[list[x] >> 5], 1u << (list[x] & 31));
 
-  const int tok = perm_q[(size_t)h * N + (size_t)i * kBlk + t];
+  const int row = i * kBlk + t;
+  const int tok = S.perm ? S.perm[(size_t)h * S.rows + row] : min(row, S.rows - 1);
+  const float* qrow = S.q + ((size_t)h * S.rows + tok) * D;
   float qv[D], acc[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
-    qv[d] = q[((size_t)h * N + tok) * D + d];
+    qv[d] = qrow[d];
     acc[d] = 0.f;
   }
   float m_run = -INFINITY, l_run = 0.f;
-  const float* bias_h = bias + (size_t)h * ntiles * 64;
+  const float* bias_h = ks.bias + (size_t)h * ntiles * 64;
   for (int it = 0; it < n_exact + n_comp; ++it) {
     const bool exact = it < n_exact;
-    // block-level compressed branch: the summary tiles see the block's pooled query
-    if (qbar != nullptr && it == n_exact) {
+    const int tau = it - n_exact + tau0;
+    // block-level compressed branch: the summary tiles see the block's pooled query, the
+    // context tiles (exact) the query's own
+    if (S.qbar != nullptr && !exact && (tau == 0 || tau == ntiles)) {
+      const float* src = tau == 0 ? S.qbar + ((size_t)h * S.nbq + i) * D : qrow;
 #pragma unroll
-      for (int d = 0; d < D; ++d) qv[d] = qbar[((size_t)h * nb + i) * D + d];
+      for (int d = 0; d < D; ++d) qv[d] = src[d];
     }
     __syncthreads();
     if (exact) {
-      const int j = list[it];
-      const int ktok = perm_k[(size_t)h * N + (size_t)j * kBlk + t];
+      const int j = list ? list[it] : it;
+      const int ktok = ks.perm_k[(size_t)h * N + (size_t)j * kBlk + t];
       for (int d = 0; d < D; ++d) {
-        sk[t][d] = k[((size_t)h * N + ktok) * D + d];
-        sv[t][d] = v[((size_t)h * N + ktok) * D + d];
+        sk[t][d] = ks.k[((size_t)h * N + ktok) * D + d];
+        sv[t][d] = ks.v[((size_t)h * N + ktok) * D + d];
       }
       sb[t] = 0.f;
-    } else {
-      const int key = (it - n_exact) * 64 + t;
+    } else if (tau < ntiles) {
+      const int key = tau * 64 + t;
       const bool masked = key >= nb || ((sel_bits[key >> 5] >> (key & 31)) & 1u);
       for (int d = 0; d < D; ++d) {
-        sk[t][d] = key < nb ? kt[((size_t)h * nb + key) * D + d] : 0.f;
-        sv[t][d] = key < nb ? vt[((size_t)h * nb + key) * D + d] : 0.f;
+        sk[t][d] = key < nb ? ks.kt[((size_t)h * nb + key) * D + d] : 0.f;
+        sv[t][d] = key < nb ? ks.vt[((size_t)h * nb + key) * D + d] : 0.f;
       }
       sb[t] = masked ? -INFINITY : bias_h[key] * kLog2e;
+    } else {
+      const int r = (tau - ntiles) * 64 + t;
+      const bool ok = r < ks.n_ctx;
+      for (int d = 0; d < D; ++d) {
+        sk[t][d] = ok ? ks.kc[((size_t)h * ks.n_ctx + r) * D + d] : 0.f;
+        sv[t][d] = ok ? ks.vc[((size_t)h * ks.n_ctx + r) * D + d] : 0.f;
+      }
+      sb[t] = ok ? 0.f : -INFINITY;
     }
     __syncthreads();
     float x[64];
@@ -449,10 +529,11 @@ __global__ __launch_bounds__(64) void k_attn_f32(
     }
     m_run = m_new;
   }
+  if (S.perm == nullptr && row >= S.rows) return;  // padding row of a context block
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-  for (int d = 0; d < D; ++d) o[((size_t)h * N + tok) * D + d] = acc[d] * inv;
-  if (lse != nullptr)
-    lse[(size_t)h * N + tok] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
+  for (int d = 0; d < D; ++d) S.o[((size_t)h * S.rows + tok) * D + d] = acc[d] * inv;
+  if (S.lse != nullptr)
+    S.lse[(size_t)h * S.rows + tok] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : -INFINITY;
 }
 
 // ------------------------------------------------ block-level compressed branch (bf16 path)
@@ -706,23 +787,55 @@ hipError_t launch_tail_block_bf16(const AttnLaunch& a, const float* qbar, uint32
 }
 
 hipError_t launch_attn_bf16(const AttnLaunch& a, hipStream_t s) {
-  const int grid = a.H * a.nb;
-  const size_t dyn = a.n_comp > 0 ? (size_t)summary_tiles(a.nb) * 64 * sizeof(float) : 0;
-  k_attn_bf16<<<grid, 256, dyn, s>>>(
-      static_cast<const uint16_t*>(a.q), a.perm_q, static_cast<const uint4*>(a.ksw),
-      static_cast<const uint4*>(a.vsw), static_cast<const uint4*>(a.ktsw),
-      static_cast<const uint4*>(a.vtsw), a.bias, a.lists, a.H, a.N, a.nb, a.topk, a.n_exact,
-      a.n_comp, a.scale * kLog2e, a.tail_o, a.tail_lse, static_cast<uint16_t*>(a.o), a.lse);
+  const int nt_s = summary_tiles(a.nb), nt_c = a.n_ctx > 0 ? ceil_div(a.n_ctx, 64) : 0;
+  KSide ks{};
+  ks.ksw = static_cast<const uint4*>(a.ksw);
+  ks.vsw = static_cast<const uint4*>(a.vsw);
+  ks.ktsw = static_cast<const uint4*>(a.ktsw);
+  ks.vtsw = static_cast<const uint4*>(a.vtsw);
+  ks.bias = a.bias;
+  ks.ctsw = static_cast<const uint4*>(a.ctsw);
+  ks.cvsw = static_cast<const uint4*>(a.cvsw);
+  ks.nb = a.nb;
+  ks.nt_s = nt_s;
+  ks.nt_c = nt_c;
+  ks.n_ctx = a.n_ctx;
+  QSide vs{static_cast<const uint16_t*>(a.q), a.perm_q, true, a.tail_o, a.tail_lse,
+           static_cast<uint16_t*>(a.o), a.lse, a.N, a.nb, a.topk, a.n_exact, a.n_comp, a.tau0};
+  QSide cs{static_cast<const uint16_t*>(a.q_ctx), nullptr, false, nullptr, nullptr,
+           static_cast<uint16_t*>(a.o_ctx), a.lse_ctx, a.n_ctx, nt_c, 0, a.ctx_n_exact,
+           a.ctx_n_comp, nt_s};
+  const int wg_c = a.H * nt_c;
+  const bool biased = a.n_comp > 0 || (nt_c > 0 && a.ctx_n_comp > 0);
+  const size_t dyn = biased ? (size_t)(nt_s + (nt_c > 0 ? 2 : 0)) * 64 * sizeof(float) : 0;
+  k_attn_bf16<<<wg_c + a.H * a.nb, 256, dyn, s>>>(cs, vs, wg_c, ks, a.lists, a.H,
+                                                  a.scale * kLog2e);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_f32(const AttnLaunch& a, hipStream_t s) {
-  const int grid = a.H * a.nb;
-  k_attn_f32<<<grid, 64, 0, s>>>(
-      static_cast<const float*>(a.q), static_cast<const float*>(a.k),
-      static_cast<const float*>(a.v), a.perm_q, a.perm_k, a.kt, a.vt, a.bias, a.lists, a.H, a.N,
-      a.nb, a.topk, a.n_exact, a.n_comp, a.scale * kLog2e, a.qbar, static_cast<float*>(a.o),
-      a.lse);
+  const int nt_s = summary_tiles(a.nb), nt_c = a.n_ctx > 0 ? ceil_div(a.n_ctx, 64) : 0;
+  KSide32 ks{};
+  ks.k = static_cast<const float*>(a.k);
+  ks.v = static_cast<const float*>(a.v);
+  ks.perm_k = a.perm_k;
+  ks.kt = a.kt;
+  ks.vt = a.vt;
+  ks.bias = a.bias;
+  ks.kc = static_cast<const float*>(a.k_ctx);
+  ks.vc = static_cast<const float*>(a.v_ctx);
+  ks.N = a.N;
+  ks.nb = a.nb;
+  ks.nt_s = nt_s;
+  ks.nt_c = nt_c;
+  ks.n_ctx = a.n_ctx;
+  QSide32 vs{static_cast<const float*>(a.q), a.perm_q, a.lists, a.qbar, static_cast<float*>(a.o),
+             a.lse, a.N, a.nb, a.topk, a.n_exact, a.n_comp, a.tau0};
+  QSide32 cs{static_cast<const float*>(a.q_ctx), nullptr, nullptr, nullptr,
+             static_cast<float*>(a.o_ctx), a.lse_ctx, a.n_ctx, nt_c, 0, a.ctx_n_exact,
+             a.ctx_n_comp, nt_s};
+  const int wg_c = a.H * nt_c;
+  k_attn_f32<<<wg_c + a.H * a.nb, 64, 0, s>>>(cs, vs, wg_c, ks, a.H, a.scale * kLog2e);
   return hipGetLastError();
 }
 

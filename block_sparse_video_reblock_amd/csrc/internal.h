@@ -27,10 +27,16 @@ hipError_t launch_summaries(bool bf16, const void* k, const void* v, const int32
 // swizzled bf16 summary tiles for the attention kernel; pads bias rows >= nb with -inf
 hipError_t launch_summary_tiles(const float* kt, const float* vt, float* bias, int H, int nb,
                                 void* ktsw, void* vtsw, hipStream_t s);
+// swizzled bf16 context tiles [H][ceil(n_ctx/64)][1024] from bf16 k_ctx, v_ctx [H][n_ctx][128];
+// rows past n_ctx are zero
+hipError_t launch_ctx_tiles(const void* k_ctx, const void* v_ctx, int H, int n_ctx, void* ctsw,
+                            void* cvsw, hipStream_t s);
 
 // ------------------------------------------------------------ attention (stages 3, 4, 5)
 struct AttnLaunch {
-  int H, N, nb, topk, n_exact, n_comp;     // n_exact = topk or 0, n_comp = tiles or 0
+  // video queries: exact tiles n_exact (= topk or 0), biased tiles tau0 .. tau0 + n_comp - 1
+  // (summary tiles 0 .. tiles - 1, then context tiles)
+  int H, N, nb, topk, n_exact, n_comp, tau0;
   float scale;
   const void* q;
   const int32_t* perm_q;
@@ -46,9 +52,16 @@ struct AttnLaunch {
   const float *kt, *vt;
   // block-level compressed branch (null: per-query).  bf16: the compressed state of every query
   // block, tail_o [H][nb][D] (normalised) and tail_lse [H][nb] (log2 units), merged in place of
-  // the summary tiles (n_comp = 0); f32: the pooled queries qbar [H][nb][D], used for the
-  // summary tiles in place of each query's own.
+  // the summary tiles; f32: the pooled queries qbar [H][nb][D], used for the summary tiles in
+  // place of each query's own.
   const float *tail_o, *tail_lse, *qbar;
+  // context tokens (n_ctx = 0: none): [H][n_ctx][D] each; context queries attend ctx_n_exact
+  // video blocks (nb or 0) and ctx_n_comp context tiles (all or 0)
+  int n_ctx, ctx_n_exact, ctx_n_comp;
+  const void *q_ctx, *k_ctx, *v_ctx;
+  const void *ctsw, *cvsw;                  // bf16 path: swizzled context tiles
+  void* o_ctx;
+  float* lse_ctx;
 };
 hipError_t launch_attn_bf16(const AttnLaunch& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnLaunch& a, hipStream_t s);

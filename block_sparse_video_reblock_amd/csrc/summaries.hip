@@ -291,10 +291,12 @@ __global__ __launch_bounds__(256) void k_summaries_bf16(
   }
 }
 
-// ------------------------------------------------- swizzled bf16 summary tiles (D = 128)
-// grid (tiles, H), 256 threads
-__global__ __launch_bounds__(256) void k_summary_tiles(const float* __restrict__ kt,
-                                                       const float* __restrict__ vt,
+// --------------------------------- swizzled bf16 summary and context tiles (D = 128)
+// Rows [H][nb][D] (fp32 summaries, or bf16 context keys / values) in 64-row tiles, rows past nb
+// zero; with bias, padding rows get bias -inf.  grid (tiles, H), 256 threads
+template <typename T>
+__global__ __launch_bounds__(256) void k_summary_tiles(const T* __restrict__ kt,
+                                                       const T* __restrict__ vt,
                                                        float* __restrict__ bias, int nb,
                                                        uint4* __restrict__ ktsw,
                                                        uint4* __restrict__ vtsw) {
@@ -307,10 +309,11 @@ __global__ __launch_bounds__(256) void k_summary_tiles(const float* __restrict__
     const int r = e / D, d = e - r * D;
     const int row = tau * 64 + r;
     const bool ok = row < nb;
-    sk[r][d] = ok ? kt[((size_t)h * nb + row) * D + d] : 0.f;
-    sv[r][d] = ok ? vt[((size_t)h * nb + row) * D + d] : 0.f;
+    sk[r][d] = ok ? load_as_f32(kt + ((size_t)h * nb + row) * D + d) : 0.f;
+    sv[r][d] = ok ? load_as_f32(vt + ((size_t)h * nb + row) * D + d) : 0.f;
   }
-  if (tid < 64 && tau * 64 + tid >= nb) bias[(size_t)h * ntiles * 64 + tau * 64 + tid] = -INFINITY;
+  if (bias != nullptr && tid < 64 && tau * 64 + tid >= nb)
+    bias[(size_t)h * ntiles * 64 + tau * 64 + tid] = -INFINITY;
   __syncthreads();
   uint4* kdst = ktsw + ((size_t)h * ntiles + tau) * 1024;
   uint4* vdst = vtsw + ((size_t)h * ntiles + tau) * 1024;
@@ -372,8 +375,17 @@ hipError_t launch_summaries(bool bf16, const void* k, const void* v, const int32
 hipError_t launch_summary_tiles(const float* kt, const float* vt, float* bias, int H, int nb,
                                 void* ktsw, void* vtsw, hipStream_t s) {
   dim3 grid(summary_tiles(nb), H);
-  k_summary_tiles<<<grid, 256, 0, s>>>(kt, vt, bias, nb, static_cast<uint4*>(ktsw),
-                                       static_cast<uint4*>(vtsw));
+  k_summary_tiles<float><<<grid, 256, 0, s>>>(kt, vt, bias, nb, static_cast<uint4*>(ktsw),
+                                              static_cast<uint4*>(vtsw));
+  return hipGetLastError();
+}
+
+hipError_t launch_ctx_tiles(const void* k_ctx, const void* v_ctx, int H, int n_ctx, void* ctsw,
+                            void* cvsw, hipStream_t s) {
+  dim3 grid(ceil_div(n_ctx, 64), H);
+  k_summary_tiles<uint16_t><<<grid, 256, 0, s>>>(
+      static_cast<const uint16_t*>(k_ctx), static_cast<const uint16_t*>(v_ctx), nullptr, n_ctx,
+      static_cast<uint4*>(ctsw), static_cast<uint4*>(cvsw));
   return hipGetLastError();
 }
 

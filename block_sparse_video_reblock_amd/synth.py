@@ -71,6 +71,9 @@ WORKLOADS = {
 }
 # the density sweep reuses the mid-size tensors at these budgets
 SWEEP_RATIOS = (0.1, 0.2, 0.3, 1.0)
+# context tokens of the mixed-sequence workloads (text, audio, conditioning): a count that is
+# not a multiple of 64, so the last context tile is ragged
+CTX_TOKENS = 1000
 
 
 def _rng(*words) -> np.random.Generator:
@@ -177,6 +180,32 @@ def make_qkv(wl: Workload, layer: int = 0, heads=None):
     workers = max(1, min(len(heads), 16, len(os.sched_getaffinity(0))))
     with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
         list(ex.map(one_head, range(len(heads))))
+    return out[0], out[1], out[2]
+
+
+def make_ctx(wl: Workload, n_ctx: int, like, layer: int = 0, heads=None):
+    """Context tokens for a mixed sequence: (q, k, v) float32 [len(heads)][n_ctx][D].
+
+    Two token types, a prefix of round(0.3 n_ctx) "text" tokens and the rest "audio /
+    conditioning", with type means N(0, I) shared by the heads (SeedSequence([workload, layer,
+    1000])), plus per-head noise N(0, 0.5^2) (SeedSequence([workload, layer, 1001 + h])); each
+    tensor is then scaled to the RMS of the same head's video tensor in `like` = (q, k, v)
+    (arrays over the same heads), and bf16 workloads are rounded to bf16."""
+    if heads is None:
+        heads = range(wl.heads)
+    heads = list(heads)
+    D = wl.head_dim
+    gl = _rng(wl.seed_id, layer, 1000)
+    means = [gl.standard_normal((2, D)).astype(np.float32) for _ in range(3)]
+    kind = (np.arange(n_ctx) >= round(0.3 * n_ctx)).astype(np.int64)
+    out = np.empty((3, len(heads), n_ctx, D), dtype=np.float32)
+    for slot, h in enumerate(heads):
+        gh = _rng(wl.seed_id, layer, 1001 + h)
+        for x in range(3):
+            y = means[x][kind] + np.float32(0.5) * gh.standard_normal((n_ctx, D), dtype=np.float32)
+            ref = np.sqrt(np.mean(np.square(like[x][slot], dtype=np.float64)))
+            y *= np.float32(ref / np.sqrt(np.mean(np.square(y, dtype=np.float64))))
+            out[x, slot] = bf16_round(y) if wl.dtype == "bf16" else y
     return out[0], out[1], out[2]
 
 

@@ -154,6 +154,41 @@ bsa_status bsa_attend(const bsa_desc* desc, const void* q, const void* k, const 
                       const int32_t* lists, int32_t topk, uint32_t flags, float scale,
                       void* o, float* lse_opt, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* (3')+(4)+(5) Mixed sequences: a video grid plus context tokens (text, audio, conditioning).
+ * [h3vid.app guide, "Warmup and step counts need explicit definitions"]: the context is handled
+ * exactly while only the video grid is sparsified; [comfyui-wiki.com "Spark-H3 ...", "What
+ * Spark-Attn changes"]: the Reweight anchor is the mean of the video queries.
+ * q, k, v, perm_q, perm_k, lists, topk, o, lse_opt: the video grid exactly as in bsa_sparse_attn
+ * (reblock and select it with bsa_reblock / bsa_select on the video tensors alone).
+ * q_ctx, k_ctx, v_ctx: [heads][n_ctx][head_dim], desc's dtype, n_ctx >= 0 (any count; 0 = none,
+ * then the context pointers may be null and this is bsa_sparse_attn).
+ * Each video query attends every context key in its exact branch; each context query attends
+ * every key (context and video) densely, output o_ctx [heads][n_ctx][head_dim] and
+ * lse_ctx_opt [heads][n_ctx].  Flags as in bsa_sparse_attn; the context keys belong to the
+ * exact branch (BSA_COMPRESSED_ONLY drops them and leaves the context rows zero with
+ * lse -inf).  ws must hold bsa_workspace_bytes_ctx(desc, n_ctx) bytes. */
+size_t bsa_workspace_bytes_ctx(const bsa_desc* desc, int32_t n_ctx);
+bsa_status bsa_sparse_attn_ctx(const bsa_desc* desc, int32_t n_ctx, const void* q, const void* k,
+                               const void* v, const void* q_ctx, const void* k_ctx,
+                               const void* v_ctx, const int32_t* perm_q, const int32_t* perm_k,
+                               const int32_t* lists, int32_t topk, uint32_t flags, float scale,
+                               void* o, void* o_ctx, float* lse_opt, float* lse_ctx_opt,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
+/* Two-phase form of bsa_sparse_attn_ctx, with the same contract as bsa_prepare_kv /
+ * bsa_attend: the prepare phase also lays out the context keys and values (k_ctx, v_ctx) in
+ * ws, and bsa_attend_ctx must receive the same desc, n_ctx, k, v, k_ctx, v_ctx, perm_k, flags
+ * (BSA_TAIL_BLOCK aside) and scale, with nothing else written to ws in between. */
+bsa_status bsa_prepare_kv_ctx(const bsa_desc* desc, int32_t n_ctx, const void* q, const void* k,
+                              const void* v, const void* k_ctx, const void* v_ctx,
+                              const int32_t* perm_k, uint32_t flags, float scale, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
+bsa_status bsa_attend_ctx(const bsa_desc* desc, int32_t n_ctx, const void* q, const void* k,
+                          const void* v, const void* q_ctx, const void* k_ctx, const void* v_ctx,
+                          const int32_t* perm_q, const int32_t* perm_k, const int32_t* lists,
+                          int32_t topk, uint32_t flags, float scale, void* o, void* o_ctx,
+                          float* lse_opt, float* lse_ctx_opt, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
 /* (4) Block summaries alone (the compressed branch's keys, values and biases), fp32:
  * kt[h][j][D], vt[h][j][D], bias[h][j].  Reweight (default): anchor qa = mean of the head's
  * queries, x_t = s qa.k_t over block j's keys, w = softmax(x), kt = sum w_t k_t,

@@ -264,6 +264,120 @@ def test_attention_tail_block_ragged_bf16(n_blocks, topk):
     assert np.max(np.abs(lse.cpu().numpy() - rl)) < 3e-2
 
 
+# ------------------------------------------------- mixed sequences (exact context tokens)
+
+def _oracle_mixed(q, k, v, qc, kc, vc, pq, pk, lists, **kw):
+    outs = [O.mixed_attention_head(q[h], k[h], v[h], qc[h], kc[h], vc[h], pq[h], pk[h],
+                                   lists[h], **kw) for h in range(q.shape[0])]
+    return [np.stack([o[i] for o in outs]) for i in range(4)]
+
+
+def _check_bf16(got, ref):
+    g = got.float().cpu().numpy()
+    assert rel_l2(g, ref) < 1e-2 and np.max(np.abs(g - ref)) < 3e-2
+
+
+@pytest.mark.parametrize("tail", ["token", "block"])
+def test_mixed_sequence_bf16_mid(mid, tail):
+    """1,000 context tokens beside the 16,384-token grid: video queries add every context key
+    to their exact branch, context queries attend densely to all keys."""
+    wl, q, k, v, pq, pk, lists = mid
+    qc, kc, vc = synth.make_ctx(wl, synth.CTX_TOKENS, (q, k, v), heads=[0, 1])
+    dt = torch.bfloat16
+    flags = ops.BSA_TAIL_BLOCK if tail == "block" else 0
+    o, oc, lse, lc = ops.sparse_attn_ctx(
+        *(to_dev(x, dt) for x in (q, k, v, qc, kc, vc)), torch.from_numpy(pq).to(DEV),
+        torch.from_numpy(pk).to(DEV), torch.from_numpy(lists).to(DEV), flags=flags,
+        with_lse=True)
+    ro, rl, roc, rlc = _oracle_mixed(q, k, v, qc, kc, vc, pq, pk, lists, tail=tail)
+    _check_bf16(o, ro)
+    _check_bf16(oc, roc)
+    assert np.max(np.abs(lse.cpu().numpy() - rl)) < 3e-2
+    assert np.max(np.abs(lc.cpu().numpy() - rlc)) < 3e-2
+
+
+@pytest.mark.parametrize("n_ctx", [1, 63, 64, 65, 200])
+def test_mixed_sequence_ragged_bf16(n_ctx):
+    """Context lengths around the 64-row tile, on a 70-block grid (ragged summary tiles), with
+    the branch flags: context keys belong to the exact branch."""
+    rng = np.random.default_rng(500 + n_ctx)
+    H, nbk, topk, D = 2, 70, 9, 128
+    N = 64 * nbk
+    q, k, v, qc, kc, vc = (synth.bf16_round(rng.standard_normal((H, n, D)).astype(np.float32) * s)
+                           for n, s in ((N, 0.3), (N, 1.0), (N, 1.0), (n_ctx, 0.3),
+                                        (n_ctx, 1.0), (n_ctx, 1.0)))
+    pq = np.stack([rng.permutation(N) for _ in range(H)]).astype(np.int32)
+    pk = np.stack([rng.permutation(N) for _ in range(H)]).astype(np.int32)
+    lists = np.sort(np.stack([[rng.choice(nbk, topk, replace=False) for _ in range(nbk)]
+                              for _ in range(H)]), axis=-1).astype(np.int32)
+    dt = torch.bfloat16
+    args = (*(to_dev(x, dt) for x in (q, k, v, qc, kc, vc)), torch.from_numpy(pq).to(DEV),
+            torch.from_numpy(pk).to(DEV), torch.from_numpy(lists).to(DEV))
+    o, oc, lse, lc = ops.sparse_attn_ctx(*args, with_lse=True)
+    ro, rl, roc, rlc = _oracle_mixed(q, k, v, qc, kc, vc, pq, pk, lists)
+    _check_bf16(o, ro)
+    _check_bf16(oc, roc)
+    assert np.max(np.abs(lse.cpu().numpy() - rl)) < 3e-2
+    assert np.max(np.abs(lc.cpu().numpy() - rlc)) < 3e-2
+    # branches: the exact branch holds the context keys; context queries have no compressed
+    # branch
+    ctx = [(kc[h], vc[h]) for h in range(H)]
+    br = [O.sparse_attention_head(q[h], k[h], v[h], pq[h], pk[h], lists[h], ctx=ctx[h],
+                                  return_branches=True) for h in range(H)]
+    oe, _, le, _ = ops.sparse_attn_ctx(*args, flags=ops.BSA_EXACT_ONLY, with_lse=True)
+    _check_bf16(oe, np.stack([b[2] for b in br]))
+    assert np.max(np.abs(le.cpu().numpy() - np.stack([b[3] for b in br]))) < 3e-2
+    ocmp, occ, lcmp, lcc = ops.sparse_attn_ctx(*args, flags=ops.BSA_COMPRESSED_ONLY,
+                                               with_lse=True)
+    _check_bf16(ocmp, np.stack([b[4] for b in br]))
+    assert torch.all(occ.float() == 0).item() and torch.all(torch.isinf(lcc)).item()
+
+
+def test_mixed_sequence_f32_tiny(tiny):
+    wl, q, k, v, pq, pk, lists = tiny
+    qc, kc, vc = synth.make_ctx(wl, 77, (q, k, v))
+    dt = torch.float32
+    for flags, tail in ((0, "token"), (ops.BSA_TAIL_BLOCK, "block")):
+        o, oc, lse, lc = ops.sparse_attn_ctx(
+            *(to_dev(x, dt) for x in (q, k, v, qc, kc, vc)), torch.from_numpy(pq).to(DEV),
+            torch.from_numpy(pk).to(DEV), torch.from_numpy(lists).to(DEV), flags=flags,
+            with_lse=True)
+        ro, rl, roc, rlc = _oracle_mixed(q, k, v, qc, kc, vc, pq, pk, lists, tail=tail)
+        for got, ref in ((o, ro), (oc, roc), (lse, rl), (lc, rlc)):
+            assert np.max(np.abs(got.cpu().numpy() - ref)) < 1e-4
+
+
+def test_mixed_sequence_two_phase_equals_one_call(mid):
+    wl, q, k, v, pq, pk, lists = mid
+    qc, kc, vc = synth.make_ctx(wl, 300, (q, k, v), heads=[0, 1])
+    dt = torch.bfloat16
+    t = [to_dev(x, dt) for x in (q, k, v, qc, kc, vc)]
+    perms = [torch.from_numpy(x).to(DEV) for x in (pq, pk, lists)]
+    o1, oc1 = ops.sparse_attn_ctx(*t, *perms)
+    d = ops.desc_for(t[0])
+    ws = ops.workspace_ctx(d, 300, DEV)
+    o2, oc2 = torch.empty_like(t[0]), torch.empty_like(t[3])
+    L, P = ops.lib(), ops._dev_ptr
+    ops.check(L.bsa_prepare_kv_ctx(d, 300, P(t[0]), P(t[1]), P(t[2]), P(t[4]), P(t[5]),
+                                   P(perms[1]), 0, 0.0, P(ws), ws.numel(), ops._stream()))
+    ops.check(L.bsa_attend_ctx(d, 300, *(P(x) for x in t), *(P(x) for x in perms),
+                               int(lists.shape[-1]), 0, 0.0, P(o2), P(oc2), None, None, P(ws),
+                               ws.numel(), ops._stream()))
+    assert torch.equal(o1, o2) and torch.equal(oc1, oc2)
+
+
+def test_mixed_sequence_without_context_is_the_plain_layer(mid):
+    wl, q, k, v, pq, pk, lists = mid
+    dt = torch.bfloat16
+    args = (to_dev(q, dt), to_dev(k, dt), to_dev(v, dt))
+    empty = torch.empty(q.shape[0], 0, q.shape[2], dtype=dt, device=DEV)
+    perms = (torch.from_numpy(pq).to(DEV), torch.from_numpy(pk).to(DEV),
+             torch.from_numpy(lists).to(DEV))
+    o, oc = ops.sparse_attn_ctx(*args, empty, empty, empty, *perms)
+    assert oc.numel() == 0
+    assert torch.equal(o, ops.sparse_attn(*args, *perms))
+
+
 def test_attention_is_deterministic(mid):
     wl, q, k, v, pq, pk, lists = mid
     dt = torch.bfloat16

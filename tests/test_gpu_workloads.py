@@ -158,3 +158,34 @@ def test_full_size_layer_sampled(name, layer):
     st = replay_partition(U, pq[0], None, max_level=3)
     print("replay", st, flush=True)
     assert st["splits"] == 7 and st["mismatched_splits"] == 0, st
+
+
+def test_full_size_mixed_sequence_sampled():
+    """The 72,576-token grid with 1,000 exact context tokens, in the launch configuration the
+    benchmark times with --ctx: sampled video blocks and context rows against the oracle."""
+    wl = synth.WORKLOADS["clip10s_bf16"]
+    H, N, nb = wl.heads, wl.tokens, wl.n_blocks
+    q, k, v = synth.make_qkv(wl)
+    qc, kc, vc = synth.make_ctx(wl, synth.CTX_TOKENS, (q, k, v))
+    print(f"mixed: H={H} N={N} n_ctx={qc.shape[1]}", flush=True)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    pq, pk = ops.reblock(qd, kd)
+    lists = ops.select(qd, kd, pq, pk, topk_ratio=wl.topk_ratio)
+    o, oc = ops.sparse_attn_ctx(qd, kd, vd, to_dev(qc), to_dev(kc), to_dev(vc), pq, pk, lists)
+    torch.cuda.synchronize()
+    pq, pk, lists = pq.cpu().numpy(), pk.cpu().numpy(), lists.cpu().numpy()
+    assert torch.isfinite(o.float()).all().item() and torch.isfinite(oc.float()).all().item()
+    rng = np.random.default_rng(21)
+    for h in (0, H - 1):
+        Qh, Kh, Vh = (x[h].astype(np.float64) for x in (q, k, v))
+        blocks = np.sort(rng.choice(nb, size=4, replace=False))
+        ro, _ = O.sparse_attention_head(Qh, Kh, Vh, pq[h], pk[h], lists[h], blocks=blocks,
+                                        ctx=(kc[h], vc[h]))
+        rows = np.concatenate([pq[h][64 * i:64 * i + 64] for i in blocks])
+        got = o[h, torch.from_numpy(rows).to(DEV)].float().cpu().numpy()
+        assert rel_l2(got, ro[rows]) < 1e-2 and np.max(np.abs(got - ro[rows])) < 3e-2
+        crow = np.sort(rng.choice(qc.shape[1], size=64, replace=False))
+        rc, _ = O.dense_attention_head(qc[h], np.concatenate([kc[h], Kh]),
+                                       np.concatenate([vc[h], Vh]), rows=crow)
+        gotc = oc[h, torch.from_numpy(crow).to(DEV)].float().cpu().numpy()
+        assert rel_l2(gotc, rc) < 1e-2 and np.max(np.abs(gotc - rc)) < 3e-2

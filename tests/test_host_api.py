@@ -100,6 +100,29 @@ def test_sparse_attn_argument_errors(L):
                              None) == _lib.BSA_E_ARG
 
 
+def test_mixed_sequence_argument_errors(L):
+    big = 1 << 40
+    v3, c3 = [FAKE] * 3, [FAKE2] * 3
+    perms = [FAKE] * 3
+
+    def call(n_ctx, ctx=c3, o_ctx=FAKE2, ws=big, flags=0):
+        return L.bsa_sparse_attn_ctx(desc(), n_ctx, *v3, *ctx, *perms, 4, flags, 0.0, FAKE,
+                                     o_ctx, None, None, FAKE, ws, None)
+    for n in (-1, (1 << 19) + 1):
+        assert call(n) == _lib.BSA_E_ARG
+    assert call(10, ctx=[FAKE2, None, FAKE2]) == _lib.BSA_E_ARG
+    assert call(10, o_ctx=None) == _lib.BSA_E_ARG
+    assert call(10, flags=16) == _lib.BSA_E_ARG
+    # the context tiles need room beyond the plain layer's workspace once they outgrow it
+    plain = L.bsa_workspace_bytes(desc())
+    assert L.bsa_workspace_bytes_ctx(desc(), 0) == plain
+    assert L.bsa_workspace_bytes_ctx(desc(), 1000) >= plain
+    need = L.bsa_workspace_bytes_ctx(desc(), 200000)
+    assert need > plain
+    assert L.bsa_workspace_bytes_ctx(desc(), -1) == 0
+    assert call(200000, ws=need - 1) == _lib.BSA_E_WORKSPACE
+
+
 def test_select_argument_errors(L):
     big = 1 << 40
     a = [FAKE] * 4
