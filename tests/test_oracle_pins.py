@@ -344,6 +344,33 @@ def test_partition_matches_brute_force_on_planted_clusters():
     assert _brute_force_leaves(Q, np.linalg.inv(Mk)) != planted
     perm_q = O.reblock_head(Q, K, leaf=4)[0]
     assert sorted(tuple(sorted(g)) for g in perm_q.reshape(-1, 4)) == planted
+    # the Lite power-step count still finds well-separated clusters
+    perm_lite = O.reblock_head(Q, K, leaf=4, iters=2)[0]
+    assert sorted(tuple(sorted(g)) for g in perm_lite.reshape(-1, 4)) == planted
+
+
+def test_power_steps_raise_the_rayleigh_quotient(tiny_inputs):
+    """Lite reblock (fewer power steps, [P1] "Benchmarks" names the variant only): the split
+    direction after T steps is a power iterate of the centred covariance C, so its Rayleigh
+    quotient v.Cv is non-decreasing in T (C is positive semi-definite), stays below the top
+    eigenvalue (numpy.linalg.eigh), and approaches it; T = 0 is the start vector itself."""
+    wl, Q, K, V = tiny_inputs
+    U = O.metric_embed(Q, O.second_moment(K))
+    rng = np.random.default_rng(2)
+    for ids in (np.arange(U.shape[0]), np.sort(rng.choice(U.shape[0], 256, replace=False))):
+        Ug = U[ids]
+        d = Ug - Ug.mean(axis=0)
+        C = d.T @ d / Ug.shape[0]
+        top = np.linalg.eigh(C)[0][-1]
+        rq = []
+        for T in range(0, 13):
+            v = O.split_direction(Ug, iters=T)
+            assert abs(np.linalg.norm(v) - 1.0) < 1e-12 or T == 0
+            rq.append(v @ C @ v / (v @ v))
+        assert np.all(np.diff(rq) >= -1e-12 * top) and rq[-1] <= top * (1 + 1e-12)
+        assert rq[-1] > 0.99 * top and rq[2] < rq[-1]
+        d0 = d[np.flatnonzero(np.any(d != 0, axis=1))[0]]
+        assert np.allclose(O.split_direction(Ug, iters=0), d0)
 
 
 def test_split_tie_break_and_odd_sizes():
