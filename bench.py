@@ -77,7 +77,7 @@ class Layer:
     """Device buffers and the four stage calls of one layer (Reblock or fixed-tile layouts)."""
 
     def __init__(self, ops, torch, wl, q, k, v, topk, fixed_tiles=False, ws=None,
-                 layout="separate", tail="token", ctx=None):
+                 layout="separate", tail="token", ctx=None, power_iters=8):
         self.ops, self.torch = ops, torch
         dev = torch.device("cuda:0")
         dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
@@ -101,6 +101,7 @@ class Layer:
         self.out = torch.empty_like(self.qd)
         self.fixed = fixed_tiles
         self.reblock_layout = ops._LAYOUTS[layout]
+        self.power_iters = power_iters
         self.flags = ((ops.BSA_MEANPOOL if fixed_tiles else 0) |
                       (ops.BSA_TAIL_BLOCK if tail == "block" else 0))
         self.L = ops.lib()
@@ -119,10 +120,10 @@ class Layer:
             ops.check(self.L.bsa_tile_layout(self.H, T, Hh, W, 4, 4, 4, p(self.perm_k),
                                              self.stream))
         else:
-            ops.check(self.L.bsa_reblock_layout(ctypes.byref(self.d), p(self.qd), p(self.kd),
-                                                self.reblock_layout, p(self.perm_q),
-                                                p(self.perm_k), None, p(self.ws),
-                                                self.ws.numel(), self.stream))
+            ops.check(self.L.bsa_reblock_ex(ctypes.byref(self.d), p(self.qd), p(self.kd),
+                                            self.reblock_layout, self.power_iters,
+                                            p(self.perm_q), p(self.perm_k), None, p(self.ws),
+                                            self.ws.numel(), self.stream))
 
     def select(self):
         p = self.p
@@ -235,7 +236,8 @@ def main_headline(args, ops, synth, torch, np):
     q, k, v = synth.make_qkv(wl)
     log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
     ctx = synth.make_ctx(wl, args.ctx, (q, k, v)) if args.ctx else None
-    lay = Layer(ops, torch, wl, q, k, v, topk, layout=args.layout, tail=args.tail, ctx=ctx)
+    lay = Layer(ops, torch, wl, q, k, v, topk, layout=args.layout, tail=args.tail, ctx=ctx,
+                power_iters=ops.BSA_POWER_ITERS_LITE if args.lite else ops.BSA_POWER_ITERS)
     ms_step, stage_ms, series = time_steps(torch, lay.stages(), args.steps, args.warmup)
     assert torch.isfinite(lay.out.float()).all().item(), "non-finite output"
     log(f"[bench] layer {ms_step:.3f} ms/step; stages " +
@@ -317,6 +319,7 @@ def main_headline(args, ops, synth, torch, np):
                    "topk_ratio": wl.topk_ratio, "topk_blocks": topk, "grid": list(wl.grid),
                    "reblock_layout": args.layout, "tail_granularity": args.tail,
                    "context_tokens": args.ctx,
+                   "reblock_power_iters": lay.power_iters,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
@@ -396,20 +399,22 @@ def main_sweep(args, ops, synth, torch, np):
     rows = []
     for ratio in synth.SWEEP_RATIOS:
         topk = ops.topk_count(nb, ratio)
-        for fixed, layout, name in ((False, "separate", "reblock, reweighted summaries"),
-                                    (False, "q_reuse_k", "reblock of the keys reused for the "
-                                                         "queries, reweighted summaries"),
-                                    (True, "separate", "fixed 4x4x4 tiles, mean-pooled "
-                                                       "summaries")):
+        for fixed, layout, iters, name in (
+                (False, "separate", 8, "reblock, reweighted summaries"),
+                (False, "separate", 2, "Lite reblock (2 power steps), reweighted summaries"),
+                (False, "q_reuse_k", 8, "reblock of the keys reused for the queries, "
+                                        "reweighted summaries"),
+                (True, "separate", 8, "fixed 4x4x4 tiles, mean-pooled summaries")):
             lay = Layer(ops, torch, wl, q, k, v, topk, fixed_tiles=fixed, ws=base.ws,
-                        layout=layout)
+                        layout=layout, power_iters=iters)
             ms_step, stage_ms, _ = time_steps(torch, lay.stages(), args.steps, args.warmup)
             rec = lay.recall(lse_dense)
             row = {"topk_ratio": ratio, "topk_blocks": topk, "layout": name,
                    "layer_ms": ms_step, "stages_ms": stage_ms, "recall": rec,
                    "speedup_vs_dense_attention": dense_ms / ms_step}
             rows.append(row)
-            tag = "fixed    " if fixed else ("reblock  " if layout == "separate" else "q_reuse_k")
+            tag = "fixed    " if fixed else ("q_reuse_k" if layout == "q_reuse_k" else
+                                              "reblock  " if iters == 8 else "lite     ")
             log(f"[bench] ratio {ratio:.1f} {tag}: layer {ms_step:.3f} ms, recall {rec:.4f}")
             del lay
     return {
@@ -444,6 +449,8 @@ def main():
     ap.add_argument("--ctx", type=int, default=0, metavar="N",
                     help="mixed sequence: N exact context tokens (text, audio, conditioning) "
                          "beside the video grid")
+    ap.add_argument("--lite", action="store_true",
+                    help="Lite reblock: 2 power steps per split instead of 8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",

@@ -38,6 +38,8 @@ _SIGS = {
                                      ctypes.c_size_t, _P]),
     "bsa_reblock_layout": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), _P, _P, ctypes.c_int32, _P,
                                             _P, _P, _P, ctypes.c_size_t, _P]),
+    "bsa_reblock_ex": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), _P, _P, ctypes.c_int32,
+                                        ctypes.c_int32, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "bsa_select": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), _P, _P, _P, _P, ctypes.c_float,
                                     ctypes.c_int32, _P, _P, _P, ctypes.c_size_t, _P]),
     "bsa_sparse_attn": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), _P, _P, _P, _P, _P, _P,
@@ -149,10 +151,13 @@ BSA_LAYOUT_Q_REUSE_K = 1
 _LAYOUTS = {"separate": BSA_LAYOUT_SEPARATE, "q_reuse_k": BSA_LAYOUT_Q_REUSE_K}
 
 
-def reblock(q, k, ws=None, with_proj=False, layout="separate"):
+BSA_POWER_ITERS, BSA_POWER_ITERS_LITE = 8, 2
+
+
+def reblock(q, k, ws=None, with_proj=False, layout="separate", power_iters=BSA_POWER_ITERS):
     """(perm_q, perm_k[, proj]) int32 [H][N] (and float [H][2][levels][N]).
-    layout "separate" (bsa_reblock) or "q_reuse_k" (bsa_reblock_layout: perm_q is a copy of the
-    key layout)."""
+    layout "separate" (bsa_reblock) or "q_reuse_k" (perm_q is a copy of the key layout);
+    power_iters: power steps per split (BSA_POWER_ITERS_LITE for the Lite reblock)."""
     torch = _torch()
     if layout not in _LAYOUTS:
         raise BsaError(BSA_E_ARG, f"unknown layout {layout!r}")
@@ -163,9 +168,10 @@ def reblock(q, k, ws=None, with_proj=False, layout="separate"):
     perm_k = torch.empty_like(perm_q)
     levels = max(0, (N // BLOCK - 1).bit_length())
     proj = torch.empty(H, 2, levels, N, dtype=torch.float32, device=q.device) if with_proj else None
-    check(lib().bsa_reblock_layout(ctypes.byref(d), _dev_ptr(q, q.dtype), _dev_ptr(k, q.dtype),
-                                   _LAYOUTS[layout], _dev_ptr(perm_q), _dev_ptr(perm_k),
-                                   _dev_ptr(proj), _dev_ptr(ws), ws.numel(), _stream()))
+    check(lib().bsa_reblock_ex(ctypes.byref(d), _dev_ptr(q, q.dtype), _dev_ptr(k, q.dtype),
+                               _LAYOUTS[layout], int(power_iters), _dev_ptr(perm_q),
+                               _dev_ptr(perm_k), _dev_ptr(proj), _dev_ptr(ws), ws.numel(),
+                               _stream()))
     return (perm_q, perm_k, proj) if with_proj else (perm_q, perm_k)
 
 

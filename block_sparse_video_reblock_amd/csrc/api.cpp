@@ -218,10 +218,20 @@ size_t bsa_workspace_bytes(const bsa_desc* d) {
 bsa_status bsa_reblock_layout(const bsa_desc* d, const void* q, const void* k, int32_t layout,
                               int32_t* perm_q, int32_t* perm_k, float* proj_opt, void* ws,
                               size_t ws_bytes, hipStream_t stream) {
+  return bsa_reblock_ex(d, q, k, layout, BSA_POWER_ITERS, perm_q, perm_k, proj_opt, ws, ws_bytes,
+                        stream);
+}
+
+bsa_status bsa_reblock_ex(const bsa_desc* d, const void* q, const void* k, int32_t layout,
+                          int32_t power_iters, int32_t* perm_q, int32_t* perm_k, float* proj_opt,
+                          void* ws, size_t ws_bytes, hipStream_t stream) {
   bsa_status st = check_desc(d);
   if (st != BSA_OK) return st;
   if (layout != BSA_LAYOUT_SEPARATE && layout != BSA_LAYOUT_Q_REUSE_K)
     return fail(BSA_E_ARG, "unknown layout %d", (int)layout);
+  if (power_iters < 1 || power_iters > BSA_MAX_POWER_ITERS)
+    return fail(BSA_E_ARG, "power_iters = %d is not in [1, %d]", (int)power_iters,
+                BSA_MAX_POWER_ITERS);
   if (!q || !k || !perm_q || !perm_k) return fail(BSA_E_ARG, "null tensor pointer");
   if (layout == BSA_LAYOUT_SEPARATE && perm_q == perm_k)
     return fail(BSA_E_ARG, "separate layouts need two permutation buffers");
@@ -231,7 +241,8 @@ bsa_status bsa_reblock_layout(const bsa_desc* d, const void* q, const void* k, i
   if (st != BSA_OK) return st;
   return hip_status(bsa::launch_reblock(is_bf16(d), q, k, d->heads, d->tokens, d->head_dim,
                                         perm_q, perm_k, proj_opt,
-                                        layout == BSA_LAYOUT_Q_REUSE_K, ws, stream),
+                                        layout == BSA_LAYOUT_Q_REUSE_K, power_iters, ws,
+                                        stream),
                     "reblock launch");
 }
 

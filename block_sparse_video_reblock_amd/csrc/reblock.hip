@@ -53,7 +53,7 @@ inline int wide_slices(int level, int nb) {
   if (level > kLastWide) return 1;
   return std::min(kSlots >> std::min(level, 4), nb >> level);
 }
-constexpr int kIters = 8;         // power steps per split
+constexpr int kIters = 8;         // power steps per split (the default; Lite takes fewer)
 constexpr int kStageStride = 72;  // bf16 elements per LDS row of the staged (transposed) chunk
 
 BSA_DEV bf16x8_t lds_bf16x8(const uint16_t* p) {
@@ -715,14 +715,15 @@ BSA_DEV void finish_stats(f32x16_t* acc, DirLds& L, int n, float acc_scale) {
 template <typename T, int D>
 BSA_DEV void power_direction(f32x16_t* acc, DirLds& L, const MRegs<D>& M, int n,
                              const T* __restrict__ X, const int32_t* __restrict__ tokmap,
-                             const float* __restrict__ inv_n, int pos0, float y_first);
+                             const float* __restrict__ inv_n, int pos0, float y_first, int iters);
 
 template <typename T, int D>
 BSA_DEV void group_direction(f32x16_t* acc, DirLds& L, const MRegs<D>& M, int n, float acc_scale,
                              const T* __restrict__ X, const int32_t* __restrict__ tokmap,
-                             const float* __restrict__ inv_n, int pos0, float y_first) {
+                             const float* __restrict__ inv_n, int pos0, float y_first,
+                             int iters) {
   finish_stats<D>(acc, L, n, acc_scale);
-  power_direction<T, D>(acc, L, M, n, X, tokmap, inv_n, pos0, y_first);
+  power_direction<T, D>(acc, L, M, n, X, tokmap, inv_n, pos0, y_first, iters);
 }
 
 // The scaled input y = x inv_n of token tokmap[pos] at element threadIdx.x (threads < D), for a
@@ -735,12 +736,13 @@ BSA_DEV float first_candidate(const T* __restrict__ X, const int32_t* __restrict
   return load_as_f32(X + (size_t)tok * D + threadIdx.x) * inv_n[tok];
 }
 
-// Given the centred covariance in acc and the mean in L.mu, find the split direction L.w.
-// y_first: first_candidate(X, tokmap, inv_n, pos0) of the calling thread.
+// Given the centred covariance in acc and the mean in L.mu, find the split direction L.w after
+// `iters` power steps.  y_first: first_candidate(X, tokmap, inv_n, pos0) of the calling thread.
 template <typename T, int D>
 BSA_DEV void power_direction(f32x16_t* acc, DirLds& L, const MRegs<D>& M, int n,
                              const T* __restrict__ X, const int32_t* __restrict__ tokmap,
-                             const float* __restrict__ inv_n, int pos0, float y_first) {
+                             const float* __restrict__ inv_n, int pos0, float y_first,
+                             int iters) {
   const int tid = threadIdx.x;
   // start vector: the first position (smallest token id) whose centred vector is non-zero
   bool found = false;
@@ -763,7 +765,7 @@ BSA_DEV void power_direction(f32x16_t* acc, DirLds& L, const MRegs<D>& M, int n,
   }
   M.matvec(L.e0, L.t);
   float rn = 1.f;
-  for (int it = 0; it < kIters; ++it) {
+  for (int it = 0; it < iters; ++it) {
     cov_matvec<D>(acc, L.t, rn, L.z, L.red);
     const float nrm2 = M.matvec_dot(L.z, L.t, L.sm);
     if (!(nrm2 > 0.f)) {
@@ -877,6 +879,7 @@ struct ProblemArgs {
   // problems launched: p = p0 + pstep * (grid index); all 2H (0, 1), or the key sides only
   // (1, 2) when the queries reuse the key layout
   int p0, pstep;
+  int iters;               // power steps per split
 };
 
 BSA_DEV int problem_of(const ProblemArgs& a, int b) { return a.p0 + a.pstep * b; }
@@ -1273,7 +1276,8 @@ __global__ __launch_bounds__(256, 2) void k_wide_dir(ProblemArgs a) {
     __syncthreads();
     finish_stats<D>(acc, L, m * kBlk, 1.f);
     if (a.cov_cur) store_acc<D>(a.cov_cur + ((size_t)p * a.gw + g) * D * D, acc);
-    power_direction<T, D>(acc, L, M, m * kBlk, X, pos, inv_n, b0 * kBlk, y_first);
+    power_direction<T, D>(acc, L, M, m * kBlk, X, pos, inv_n, b0 * kBlk, y_first,
+                          a.iters);
     if (threadIdx.x < D) {
       group_mean<D>(a, p, a.level, g)[threadIdx.x] = L.mu[threadIdx.x];
       a.wdir[((size_t)p * a.G + g) * D + threadIdx.x] = L.w[threadIdx.x];
@@ -1351,7 +1355,7 @@ BSA_DEV void split_group(const ProblemArgs& a, int p, int level, int g, int b0, 
     // M is read (from L2) for the power steps only, so it holds no registers elsewhere
     MRegs<D> M;
     M.load(problem_metric<D>(a, p));
-    power_direction<T, D>(acc, L, M, n, X, pos, inv_n, b0 * kBlk, y_first);
+    power_direction<T, D>(acc, L, M, n, X, pos, inv_n, b0 * kBlk, y_first, a.iters);
   }
   if (threadIdx.x < D) group_mean<D>(a, p, level, g)[threadIdx.x] = L.mu[threadIdx.x];
   project_range<T, D>(X, pos, inv_n, b0, b0 + m, L.w, keys, problem_proj(a, p, level));
@@ -1478,7 +1482,8 @@ __global__ __launch_bounds__(256, 2) void k_subtree_small(ProblemArgs a, int ls)
         sym_to_regs<D>(sacc, inv_s2, st, acc);
       }
       M.load(problem_metric<D>(a, p));  // overlaps the centring in group_direction
-      group_direction<T, D>(acc, L, M, n, 1.f, X, spos, inv_n, lb0 * kBlk, y_first);
+      group_direction<T, D>(acc, L, M, n, 1.f, X, spos, inv_n, lb0 * kBlk, y_first,
+                            a.iters);
       if (threadIdx.x < D) group_mean<D>(a, p, level, g)[threadIdx.x] = L.mu[threadIdx.x];
       float* proj = problem_proj(a, p, level);
       project_range<T, D>(X, spos, inv_n, lb0, lb0 + m, L.w, skeys, proj);
@@ -1575,7 +1580,7 @@ int active_count(int nb, int level) {
 
 template <typename T, int D>
 hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm_q,
-                       int32_t* perm_k, float* proj_opt, bool keys_only, void* ws,
+                       int32_t* perm_k, float* proj_opt, bool keys_only, int iters, void* ws,
                        hipStream_t s) {
   const RebLayout R = reb_layout(H, N, D);
   char* w = static_cast<char*>(ws);
@@ -1590,6 +1595,7 @@ hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm
   k_moments_finish<D><<<dim3(D * D / 256, sides, H), 256, 0, s>>>(
       reinterpret_cast<float*>(w + R.mom_partial), R.nch_mom, N, mom, msplit);
   ProblemArgs a{};
+  a.iters = iters;
   a.q = q;
   a.k = k;
   a.H = H;
@@ -1718,10 +1724,11 @@ size_t reblock_ws_bytes(int H, int N, int D) { return reb_layout(H, N, D).total;
 
 hipError_t launch_reblock(bool bf16, const void* q, const void* k, int H, int N, int D,
                           int32_t* perm_q, int32_t* perm_k, float* proj_opt, bool keys_only,
-                          void* ws, hipStream_t s) {
+                          int iters, void* ws, hipStream_t s) {
   if (bf16)
-    return run_reblock<uint16_t, 128>(q, k, H, N, perm_q, perm_k, proj_opt, keys_only, ws, s);
-  return run_reblock<float, 64>(q, k, H, N, perm_q, perm_k, proj_opt, keys_only, ws, s);
+    return run_reblock<uint16_t, 128>(q, k, H, N, perm_q, perm_k, proj_opt, keys_only, iters,
+                                      ws, s);
+  return run_reblock<float, 64>(q, k, H, N, perm_q, perm_k, proj_opt, keys_only, iters, ws, s);
 }
 
 }  // namespace bsa

@@ -111,6 +111,19 @@ bsa_status bsa_reblock_layout(const bsa_desc* desc, const void* q, const void* k
                               int32_t* perm_q, int32_t* perm_k, float* proj_opt,
                               void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* (1'') Reblock with a layout choice and a power-step count per split.  BSA_POWER_ITERS (8) is
+ * bsa_reblock_layout.  Lite: [comfyui-wiki.com "Spark-H3 ...", "Benchmarks" ("基准测试")]
+ * names a lighter Spark-H3-Lite that halves the reblock latency for a small fidelity loss at
+ * 20 % and 30 % density and does not say how; the reading taken here is fewer power steps per
+ * split (BSA_POWER_ITERS_LITE = 2) from the same start vector, every other step of the tree
+ * unchanged.  power_iters outside [1, BSA_MAX_POWER_ITERS] is BSA_E_ARG. */
+#define BSA_POWER_ITERS 8
+#define BSA_POWER_ITERS_LITE 2
+#define BSA_MAX_POWER_ITERS 64
+bsa_status bsa_reblock_ex(const bsa_desc* desc, const void* q, const void* k, int32_t layout,
+                          int32_t power_iters, int32_t* perm_q, int32_t* perm_k, float* proj_opt,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* (2) Select.  Block scores S[h][i][j] = s * mean(query block i) . mean(key block j) with
  * s = 1/sqrt(D); per row the K largest (ties to the lower j), written ascending to
  * lists[h][i][0..K).  K = topk_blocks if topk_blocks > 0 (must be <= nb), else

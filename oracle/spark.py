@@ -12,7 +12,7 @@ import math
 import numpy as np
 
 __all__ = [
-    "LEAF", "second_moment", "metric_factor", "metric_embed", "tree_levels",
+    "LEAF", "POWER_ITERS", "second_moment", "metric_factor", "metric_embed", "tree_levels",
     "split_direction", "partition", "partition_from_projections", "reblock_head",
     "topk_count", "block_means", "block_scores", "topk_lists", "summaries",
     "sparse_attention_head", "mixed_attention_head", "dense_attention_head", "recall_head",

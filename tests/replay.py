@@ -10,7 +10,8 @@ import numpy as np
 import oracle as O
 
 
-def replay_partition(U, perm, proj=None, tol=1e-5, leaf=64, max_level=None):
+def replay_partition(U, perm, proj=None, tol=1e-5, leaf=64, max_level=None,
+                     iters=O.POWER_ITERS):
     """U: oracle unit vectors [N][D]; perm: GPU permutation; proj: GPU projections [L][N] by
     token id or None; max_level: replay only the first levels.  Returns a dict of statistics;
     raises AssertionError on a bad split."""
@@ -26,7 +27,7 @@ def replay_partition(U, perm, proj=None, tol=1e-5, leaf=64, max_level=None):
                 nxt.append((b0, m))
                 continue
             ids = np.sort(perm[b0 * leaf:(b0 + m) * leaf])
-            v = O.split_direction(U[ids])
+            v = O.split_direction(U[ids], iters=iters)
             p = U[ids] @ v
             cut = (m // 2) * leaf
             left = set(perm[b0 * leaf:b0 * leaf + cut].tolist())

@@ -23,7 +23,7 @@ def to_dev(x, dtype):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV).to(dtype)
 
 
-def _check_layouts(q, k, perm_q, perm_k, proj, tol_proj):
+def _check_layouts(q, k, perm_q, perm_k, proj, tol_proj, iters=O.POWER_ITERS):
     """Replay both sides of every head; returns the summed statistics."""
     total = {"splits": 0, "mismatched_splits": 0, "max_proj_err": 0.0}
     for h in range(q.shape[0]):
@@ -33,7 +33,7 @@ def _check_layouts(q, k, perm_q, perm_k, proj, tol_proj):
             assert np.array_equal(np.sort(perm), np.arange(X.shape[0]))
             assert np.all(np.diff(perm.reshape(-1, 64), axis=1) > 0)
             st = replay_partition(O.metric_embed(X, Mo), perm,
-                                  None if proj is None else proj[h, side])
+                                  None if proj is None else proj[h, side], iters=iters)
             for key in ("splits", "mismatched_splits"):
                 total[key] += st[key]
             total["max_proj_err"] = max(total["max_proj_err"], st["max_proj_err"])
@@ -53,30 +53,36 @@ def mid():
     return (wl,) + synth.make_qkv(wl, heads=[0, 1])
 
 
-def test_reblock_f32_tiny(tiny):
+# power steps per split: the default and the Lite reblock's
+ITERS = [O.POWER_ITERS, ops.BSA_POWER_ITERS_LITE]
+
+
+@pytest.mark.parametrize("iters", ITERS)
+def test_reblock_f32_tiny(tiny, iters):
     wl, q, k, v = tiny
     dt = torch.float32
-    pq, pk, proj = ops.reblock(to_dev(q, dt), to_dev(k, dt), with_proj=True)
+    pq, pk, proj = ops.reblock(to_dev(q, dt), to_dev(k, dt), with_proj=True, power_iters=iters)
     pq, pk, proj = pq.cpu().numpy(), pk.cpu().numpy(), proj.cpu().numpy()
-    st = _check_layouts(q, k, pq, pk, proj, tol_proj=3e-5)
-    print("tiny replay", st)
-    rq, rk, _, _ = O.reblock_head(q[0].astype(np.float64), k[0].astype(np.float64))
+    st = _check_layouts(q, k, pq, pk, proj, tol_proj=3e-5, iters=iters)
+    print("tiny replay", iters, st)
+    rq, rk, _, _ = O.reblock_head(q[0].astype(np.float64), k[0].astype(np.float64), iters=iters)
     if st["mismatched_splits"] == 0:
         assert np.array_equal(pq[0], rq) and np.array_equal(pk[0], rk)
 
 
-def test_reblock_bf16_mid(mid):
+@pytest.mark.parametrize("iters", ITERS)
+def test_reblock_bf16_mid(mid, iters):
     wl, q, k, v = mid
     dt = torch.bfloat16
-    pq, pk, proj = ops.reblock(to_dev(q, dt), to_dev(k, dt), with_proj=True)
+    pq, pk, proj = ops.reblock(to_dev(q, dt), to_dev(k, dt), with_proj=True, power_iters=iters)
     pq, pk, proj = pq.cpu().numpy(), pk.cpu().numpy(), proj.cpu().numpy()
-    st = _check_layouts(q, k, pq, pk, proj, tol_proj=3e-5)
-    print("mid replay", st)
+    st = _check_layouts(q, k, pq, pk, proj, tol_proj=3e-5, iters=iters)
+    print("mid replay", iters, st)
     assert st["mismatched_splits"] <= 0.02 * st["splits"]
 
 
-@pytest.mark.parametrize("n_blocks", [600, 1134])
-def test_reblock_bf16_narrow_levels(n_blocks):
+@pytest.mark.parametrize("n_blocks,iters", [(600, 8), (1134, 8), (1134, 2)])
+def test_reblock_bf16_narrow_levels(n_blocks, iters):
     """Enough blocks for the one-workgroup-per-parent levels (left-only statistics, right
     child from the parent's covariance) between the wide levels and the subtree kernel: every
     split of both sides replayed on the oracle."""
@@ -86,14 +92,14 @@ def test_reblock_bf16_narrow_levels(n_blocks):
     sel = np.sort(rng.choice(wl.tokens, size=64 * n_blocks, replace=False))
     q, k = q[:, sel], k[:, sel]
     pq, pk, proj = ops.reblock(to_dev(q, torch.bfloat16), to_dev(k, torch.bfloat16),
-                               with_proj=True)
+                               with_proj=True, power_iters=iters)
     # these levels derive each right child's statistics as n_P C_P - S_L in fp32; where a split
     # separates two children far apart relative to their spread, that subtraction amplifies
     # the fp32 rounding of C_P, so the GPU's projections sit a little further from the fp64
     # oracle's (split decisions are still held to the 1e-5 tie rule)
     st = _check_layouts(q, k, pq.cpu().numpy(), pk.cpu().numpy(), proj.cpu().numpy(),
-                        tol_proj=5e-5)
-    print("narrow replay", st)
+                        tol_proj=5e-5, iters=iters)
+    print("narrow replay", iters, st)
     assert st["mismatched_splits"] <= 0.02 * st["splits"]
 
 

@@ -141,6 +141,10 @@ def test_reblock_and_hook_argument_errors(L):
                          None) == _lib.BSA_E_WORKSPACE
     # separate layouts need two permutation buffers
     assert L.bsa_reblock(desc(), FAKE, FAKE, FAKE, FAKE, None, FAKE, big, None) == _lib.BSA_E_ARG
+    # power steps per split outside [1, 64]
+    for it in (0, -1, 65):
+        assert L.bsa_reblock_ex(desc(), FAKE, FAKE, 0, it, FAKE, FAKE2, None, FAKE, big,
+                                None) == _lib.BSA_E_ARG
     # layout choice: unknown value, then the key-reuse layout, whose one buffer may serve both
     for bad in (-1, 2):
         assert L.bsa_reblock_layout(desc(), FAKE, FAKE, bad, FAKE, FAKE2, None, FAKE, big,
