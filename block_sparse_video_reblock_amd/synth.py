@@ -68,6 +68,9 @@ WORKLOADS = {
     "clip10s_bf16": Workload("clip10s_bf16", 3, "bf16", 24, 128, (21, 48, 72), 32, 0.1, True),
     # 24 heads, 103,680 tokens on 30x48x72 (1,620 blocks), 10 % budget, four layers
     "clip14s_bf16": Workload("clip14s_bf16", 5, "bf16", 24, 128, (30, 48, 72), 32, 0.1, True, 4),
+    # the largest sequence the library accepts: 2 heads, 524,288 tokens on 32x128x128
+    # (8,192 blocks, 13 tree levels), 10 % budget
+    "max_bf16": Workload("max_bf16", 6, "bf16", 2, 128, (32, 128, 128), 32, 0.1, True),
 }
 # the density sweep reuses the mid-size tensors at these budgets
 SWEEP_RATIOS = (0.1, 0.2, 0.3, 1.0)

@@ -189,3 +189,47 @@ def test_full_size_mixed_sequence_sampled():
                                        np.concatenate([vc[h], Vh]), rows=crow)
         gotc = oc[h, torch.from_numpy(crow).to(DEV)].float().cpu().numpy()
         assert rel_l2(gotc, rc) < 1e-2 and np.max(np.abs(gotc - rc)) < 3e-2
+
+
+def test_max_tokens_layer_sampled():
+    """The largest sequence the boundary accepts (524,288 tokens = 8,192 blocks, a 13-level
+    tree, 819 selected blocks per row, 128 summary tiles), two heads: layouts, scores, lists and
+    sampled outputs against the oracle."""
+    wl = synth.WORKLOADS["max_bf16"]
+    H, N, nb = wl.heads, wl.tokens, wl.n_blocks
+    assert N == 1 << 19
+    K = O.topk_count(nb, wl.topk_ratio)
+    props = torch.cuda.get_device_properties(0)
+    print(f"max: H={H} N={N} nb={nb} K={K}; device LDS per block "
+          f"{getattr(props, 'shared_memory_per_block', '?')}", flush=True)
+    q, k, v, pq, pk, lists, scores, out, out_tb = _full_layer(wl, 0)
+    print("max: layer done", flush=True)
+    ident = np.arange(N)
+    for h in range(H):
+        for perm in (pq[h], pk[h]):
+            assert np.array_equal(np.sort(perm), ident)
+            assert np.all(np.diff(perm.reshape(nb, 64), axis=1) > 0)
+    assert lists.shape == (H, nb, K)
+    assert np.all(np.diff(lists, axis=2) > 0) and lists.min() >= 0 and lists.max() < nb
+    assert torch.isfinite(out.float()).all().item() and torch.isfinite(out_tb.float()).all().item()
+    rng = np.random.default_rng(11)
+    for h in range(H):
+        Qh, Kh, Vh = (x[h].astype(np.float64) for x in (q, k, v))
+        rows_s = np.sort(rng.choice(nb, size=4, replace=False))
+        S = O.block_means(Qh, pq[h])[rows_s] @ O.block_means(Kh, pk[h]).T / np.sqrt(Qh.shape[1])
+        got_s = scores[h].cpu().numpy()[rows_s]
+        assert np.max(np.abs(got_s - S)) < 1e-5 * max(1.0, np.abs(S).max())
+        assert np.array_equal(lists[h][rows_s], O.topk_lists(got_s, K))
+        blocks = np.sort(rng.choice(nb, size=3, replace=False))
+        rows = np.concatenate([pq[h][64 * i:64 * i + 64] for i in blocks])
+        summ = O.summaries(Qh, Kh, Vh, pk[h])
+        for o_dev, tail in ((out, "token"), (out_tb, "block")):
+            ro, _ = O.sparse_attention_head(Qh, Kh, Vh, pq[h], pk[h], lists[h], blocks=blocks,
+                                            tail=tail, summ=summ)
+            got = o_dev[h, torch.from_numpy(rows).to(DEV)].float().cpu().numpy()
+            assert rel_l2(got, ro[rows]) < 1e-2 and np.max(np.abs(got - ro[rows])) < 3e-2
+    # the first two tree levels of head 0's key side, replayed on the oracle
+    U = O.metric_embed(k[0].astype(np.float64), O.second_moment(q[0].astype(np.float64)))
+    st = replay_partition(U, pk[0], None, max_level=2)
+    print("replay", st, flush=True)
+    assert st["splits"] == 3 and st["mismatched_splits"] == 0, st
