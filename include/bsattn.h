@@ -15,6 +15,9 @@
  *                 plus a log-mass bias (Spark-Reweight); every query keeps its own Q.
  *                 [comfyui-wiki.com page, "What Spark-Attn changes" and its figure]
  *   (5) log-sum-exp merge of the two branches and the inverse permutation to token order.
+ * Options on the same path: the key layout reused for the queries (bsa_reblock_layout), the
+ * Lite power-step count (bsa_reblock_ex), the block-level compressed branch (BSA_TAIL_BLOCK),
+ * and exact context tokens beside the video grid (bsa_sparse_attn_ctx).
  *
  * Conventions shared by every call
  *   - Tensors are dense, row-major [heads][tokens][head_dim] device buffers, batch 1.
@@ -25,8 +28,8 @@
  *     perm_k; V follows K.  nb = tokens / 64.
  *   - Every pointer is a device pointer owned by the caller; the library allocates nothing and
  *     keeps no state beyond a per-device architecture check.  `ws` is caller-provided
- *     scratch of at least bsa_workspace_bytes(desc) bytes (contents need not be initialised
- *     and are clobbered).
+ *     scratch of at least bsa_workspace_bytes(desc) bytes (bsa_workspace_bytes_ctx for the
+ *     mixed-sequence calls; contents need not be initialised and are clobbered).
  *   - Calls are asynchronous on `stream`.  The return value reports argument validation and
  *     launch errors; argument checks run on the host before any HIP call.  There is no silent
  *     fallback: an unsupported input is an error (BSA_E_ARG / BSA_E_UNSUPPORTED), never a

@@ -121,6 +121,17 @@ def test_mixed_sequence_argument_errors(L):
     assert need > plain
     assert L.bsa_workspace_bytes_ctx(desc(), -1) == 0
     assert call(200000, ws=need - 1) == _lib.BSA_E_WORKSPACE
+    # the two-phase form checks the same things (prepare needs no query or output pointers)
+    assert L.bsa_prepare_kv_ctx(desc(), 10, *v3, FAKE2, None, FAKE, 0, 0.0, FAKE, big,
+                                None) == _lib.BSA_E_ARG
+    assert L.bsa_prepare_kv_ctx(desc(), -1, *v3, FAKE2, FAKE2, FAKE, 0, 0.0, FAKE, big,
+                                None) == _lib.BSA_E_ARG
+    assert L.bsa_prepare_kv_ctx(desc(), 200000, *v3, FAKE2, FAKE2, FAKE, 0, 0.0, FAKE, need - 1,
+                                None) == _lib.BSA_E_WORKSPACE
+    assert L.bsa_attend_ctx(desc(), 10, *v3, *c3, *perms, 4, 0, 0.0, FAKE, None, None, None,
+                            FAKE, big, None) == _lib.BSA_E_ARG
+    assert L.bsa_attend_ctx(desc(), 10, *v3, *c3, *perms, 0, 0, 0.0, FAKE, FAKE2, None, None,
+                            FAKE, big, None) == _lib.BSA_E_ARG
 
 
 def test_select_argument_errors(L):
