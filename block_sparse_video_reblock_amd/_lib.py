@@ -40,6 +40,8 @@ _SIGS = {
                                             _P, _P, _P, ctypes.c_size_t, _P]),
     "bsa_reblock_ex": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), _P, _P, ctypes.c_int32,
                                         ctypes.c_int32, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "bsa_reblock_side": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), _P, _P, ctypes.c_int32,
+                                          ctypes.c_int32, _P, _P, _P, ctypes.c_size_t, _P]),
     "bsa_select": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), _P, _P, _P, _P, ctypes.c_float,
                                     ctypes.c_int32, _P, _P, _P, ctypes.c_size_t, _P]),
     "bsa_sparse_attn": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), _P, _P, _P, _P, _P, _P,
@@ -173,6 +175,23 @@ def reblock(q, k, ws=None, with_proj=False, layout="separate", power_iters=BSA_P
                                _dev_ptr(perm_k), _dev_ptr(proj), _dev_ptr(ws), ws.numel(),
                                _stream()))
     return (perm_q, perm_k, proj) if with_proj else (perm_q, perm_k)
+
+
+def reblock_side(q, k, side, ws=None, power_iters=BSA_POWER_ITERS, with_proj=False):
+    """One side of the reblock: side 0 the query layouts, side 1 the key layouts (int32 [H][N]),
+    and with_proj its projections (float [H][2][levels][N], the other side's rows 0)."""
+    torch = _torch()
+    d = desc_for(q)
+    ws = workspace(d, q.device) if ws is None else ws
+    H, N = q.shape[0], q.shape[1]
+    perm = torch.empty(H, N, dtype=torch.int32, device=q.device)
+    levels = max(0, (N // BLOCK - 1).bit_length())
+    proj = torch.empty(H, 2, levels, N, dtype=torch.float32, device=q.device) if with_proj \
+        else None
+    check(lib().bsa_reblock_side(ctypes.byref(d), _dev_ptr(q, q.dtype), _dev_ptr(k, q.dtype),
+                                 int(side), int(power_iters), _dev_ptr(perm), _dev_ptr(proj),
+                                 _dev_ptr(ws), ws.numel(), _stream()))
+    return (perm, proj) if with_proj else perm
 
 
 def select(q, k, perm_q, perm_k, topk_ratio=0.0, topk_blocks=0, ws=None, with_scores=False):

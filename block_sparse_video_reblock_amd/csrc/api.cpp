@@ -241,8 +241,31 @@ bsa_status bsa_reblock_ex(const bsa_desc* d, const void* q, const void* k, int32
   if (st != BSA_OK) return st;
   return hip_status(bsa::launch_reblock(is_bf16(d), q, k, d->heads, d->tokens, d->head_dim,
                                         perm_q, perm_k, proj_opt,
+                                        layout == BSA_LAYOUT_Q_REUSE_K ? bsa::kSideKeys
+                                                                       : bsa::kSideBoth,
                                         layout == BSA_LAYOUT_Q_REUSE_K, power_iters, ws,
                                         stream),
+                    "reblock launch");
+}
+
+bsa_status bsa_reblock_side(const bsa_desc* d, const void* q, const void* k, int32_t side,
+                            int32_t power_iters, int32_t* perm, float* proj_opt, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  bsa_status st = check_desc(d);
+  if (st != BSA_OK) return st;
+  if (side != 0 && side != 1) return fail(BSA_E_ARG, "side = %d is not 0 or 1", (int)side);
+  if (power_iters < 1 || power_iters > BSA_MAX_POWER_ITERS)
+    return fail(BSA_E_ARG, "power_iters = %d is not in [1, %d]", (int)power_iters,
+                BSA_MAX_POWER_ITERS);
+  if (!q || !k || !perm) return fail(BSA_E_ARG, "null tensor pointer");
+  st = check_ws(ws, ws_bytes, bsa::reblock_ws_bytes(d->heads, d->tokens, d->head_dim));
+  if (st != BSA_OK) return st;
+  st = check_device();
+  if (st != BSA_OK) return st;
+  return hip_status(bsa::launch_reblock(is_bf16(d), q, k, d->heads, d->tokens, d->head_dim,
+                                        perm, perm, proj_opt,
+                                        side ? bsa::kSideKeys : bsa::kSideQueries, false,
+                                        power_iters, ws, stream),
                     "reblock launch");
 }
 

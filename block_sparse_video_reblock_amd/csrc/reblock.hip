@@ -922,13 +922,13 @@ BSA_DEV void partition_in_place(const float* keys, int32_t* pos, int32_t* tmp, i
 // ------------------------------------------------------------------- second moments
 template <typename T, int D>
 __global__ __launch_bounds__(256) void k_moments(const T* __restrict__ q,
-                                                 const T* __restrict__ k, int N,
+                                                 const T* __restrict__ k, int N, int side0,
                                                  float* __restrict__ partial) {
   constexpr int MODE = sizeof(T) == 4 ? kBf16x3 : kExact;
   __shared__ StageLds<D, split_terms<MODE>()> st;
   __shared__ float zero[D];
-  // side = blockIdx.y: 0 = M_Q, 1 = M_K (a grid of one side computes M_Q only)
-  const int chunk = blockIdx.x, side = blockIdx.y, h = blockIdx.z, nch = gridDim.x;
+  // side = side0 + blockIdx.y: 0 = M_Q, 1 = M_K
+  const int chunk = blockIdx.x, side = side0 + blockIdx.y, h = blockIdx.z, nch = gridDim.x;
   const T* X = (side ? k : q) + (size_t)h * N * D;
   if (threadIdx.x < D) zero[threadIdx.x] = 0.f;
   __syncthreads();
@@ -947,10 +947,11 @@ __global__ __launch_bounds__(256) void k_moments(const T* __restrict__ q,
 // and (bf16 path) its 3-term bf16 split.  grid (D*D/256, 2, H).
 template <int D>
 __global__ __launch_bounds__(256) void k_moments_finish(const float* __restrict__ partial,
-                                                        int nch, int N, float* __restrict__ mom,
+                                                        int nch, int N, int side0,
+                                                        float* __restrict__ mom,
                                                         uint16_t* __restrict__ msplit) {
   const int e = blockIdx.x * 256 + threadIdx.x;  // register-dump index
-  const int side = blockIdx.y, h = blockIdx.z;
+  const int side = side0 + blockIdx.y, h = blockIdx.z;
   const size_t mi = (size_t)h * 2 + side;
   float s = 0.f;
   // (unrolled so that the loads are in flight together; the additions keep their order)
@@ -1580,20 +1581,24 @@ int active_count(int nb, int level) {
 
 template <typename T, int D>
 hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm_q,
-                       int32_t* perm_k, float* proj_opt, bool keys_only, int iters, void* ws,
-                       hipStream_t s) {
+                       int32_t* perm_k, float* proj_opt, int sides, bool copy_q, int iters,
+                       void* ws, hipStream_t s) {
   const RebLayout R = reb_layout(H, N, D);
   char* w = static_cast<char*>(ws);
-  // keys_only: only the key trees (problems 2h + 1, under M_Q) are built, and the query
-  // layouts are copies of them; M_K and the query norms are then not needed either
-  const int P = keys_only ? H : 2 * H, nb = N / kBlk, sides = keys_only ? 1 : 2;
+  // sides: kSideQueries builds the query trees only (problems 2h, under M_K), kSideKeys the
+  // key trees only (problems 2h + 1, under M_Q), kSideBoth all 2H; a one-sided run needs one
+  // moment per head (M_K for the queries, M_Q for the keys).  copy_q: the query layouts are
+  // copies of the key layouts afterwards.
+  const bool both = sides == kSideBoth;
+  const int P = both ? 2 * H : H, nb = N / kBlk, msides = both ? 2 : 1;
+  const int mside0 = sides == kSideQueries ? 1 : 0;
   float* mom = reinterpret_cast<float*>(w + R.mom);
   uint16_t* msplit = sizeof(T) == 2 ? reinterpret_cast<uint16_t*>(w + R.msplit) : nullptr;
-  k_moments<T, D><<<dim3(R.nch_mom, sides, H), 256, 0, s>>>(
-      static_cast<const T*>(q), static_cast<const T*>(k), N,
+  k_moments<T, D><<<dim3(R.nch_mom, msides, H), 256, 0, s>>>(
+      static_cast<const T*>(q), static_cast<const T*>(k), N, mside0,
       reinterpret_cast<float*>(w + R.mom_partial));
-  k_moments_finish<D><<<dim3(D * D / 256, sides, H), 256, 0, s>>>(
-      reinterpret_cast<float*>(w + R.mom_partial), R.nch_mom, N, mom, msplit);
+  k_moments_finish<D><<<dim3(D * D / 256, msides, H), 256, 0, s>>>(
+      reinterpret_cast<float*>(w + R.mom_partial), R.nch_mom, N, mside0, mom, msplit);
   ProblemArgs a{};
   a.iters = iters;
   a.q = q;
@@ -1617,8 +1622,8 @@ hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm
   a.proj = proj_opt;
   a.gw = R.gw;
   a.G = R.G;
-  a.p0 = keys_only ? 1 : 0;
-  a.pstep = keys_only ? 2 : 1;
+  a.p0 = sides == kSideKeys ? 1 : 0;
+  a.pstep = both ? 1 : 2;
   float* ysum = reinterpret_cast<float*>(w + R.ysum);
   float* ymax = reinterpret_cast<float*>(w + R.ymax);
   if (sizeof(T) == 2)
@@ -1635,8 +1640,8 @@ hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm
     k_fill_zero<<<(unsigned)std::min<size_t>((n + 255) / 256, 4096), 256, 0, s>>>(n, proj_opt);
   }
   const dim3 gridN(std::min(ceil_div(N, 256), 1024), H);
-  if (!keys_only) k_fill_identity<<<gridN, 256, 0, s>>>(N, perm_q);
-  k_fill_identity<<<gridN, 256, 0, s>>>(N, perm_k);
+  if (sides & kSideQueries) k_fill_identity<<<gridN, 256, 0, s>>>(N, perm_q);
+  if (sides & kSideKeys) k_fill_identity<<<gridN, 256, 0, s>>>(N, perm_k);
   if (R.L > 0) k_group_lists<<<R.L, 256, 0, s>>>(nb, R.G, reinterpret_cast<int*>(w + R.lists));
   // levels whose groups are large are split over several workgroups; below that one
   // workgroup per group, and from the first level whose groups fit in kSmallBlocks blocks,
@@ -1670,7 +1675,7 @@ hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm
     a.cov_cur = reinterpret_cast<float*>(w + ((level & 1) ? R.cov1 : R.cov0));
     k_subtree_pair<T, D><<<dim3(active_count(nb, level - 1), P), 256, 0, s>>>(a, level, R.gw);
   }
-  if (keys_only && perm_q != perm_k) k_copy_i32<<<gridN, 256, 0, s>>>(N, perm_k, perm_q);
+  if (copy_q && perm_q != perm_k) k_copy_i32<<<gridN, 256, 0, s>>>(N, perm_k, perm_q);
   return hipGetLastError();
 }
 
@@ -1723,12 +1728,13 @@ hipError_t launch_partition_from_proj(int P, int N, const float* proj, int32_t* 
 size_t reblock_ws_bytes(int H, int N, int D) { return reb_layout(H, N, D).total; }
 
 hipError_t launch_reblock(bool bf16, const void* q, const void* k, int H, int N, int D,
-                          int32_t* perm_q, int32_t* perm_k, float* proj_opt, bool keys_only,
-                          int iters, void* ws, hipStream_t s) {
+                          int32_t* perm_q, int32_t* perm_k, float* proj_opt, int sides,
+                          bool copy_q, int iters, void* ws, hipStream_t s) {
   if (bf16)
-    return run_reblock<uint16_t, 128>(q, k, H, N, perm_q, perm_k, proj_opt, keys_only, iters,
-                                      ws, s);
-  return run_reblock<float, 64>(q, k, H, N, perm_q, perm_k, proj_opt, keys_only, iters, ws, s);
+    return run_reblock<uint16_t, 128>(q, k, H, N, perm_q, perm_k, proj_opt, sides, copy_q,
+                                      iters, ws, s);
+  return run_reblock<float, 64>(q, k, H, N, perm_q, perm_k, proj_opt, sides, copy_q, iters, ws,
+                                s);
 }
 
 }  // namespace bsa

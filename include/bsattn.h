@@ -100,7 +100,7 @@ bsa_status bsa_reblock(const bsa_desc* desc, const void* q, const void* k,
                        int32_t* perm_q, int32_t* perm_k, float* proj_opt,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* (1') Reblock with a layout choice.  [comfyui-wiki.com "Spark-H3 ...", "Workflows" ("工作流")]:
+/* (1a) Reblock with a layout choice.  [comfyui-wiki.com "Spark-H3 ...", "Workflows" ("工作流")]:
  * every shipped workflow pins reblock_layout = q_reuse_k; the pages do not define it, and the
  * reading taken here is its name: the queries reuse the key layout.
  *   BSA_LAYOUT_SEPARATE  exactly bsa_reblock (perm_q and perm_k must be distinct buffers).
@@ -114,7 +114,7 @@ bsa_status bsa_reblock_layout(const bsa_desc* desc, const void* q, const void* k
                               int32_t* perm_q, int32_t* perm_k, float* proj_opt,
                               void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* (1'') Reblock with a layout choice and a power-step count per split.  BSA_POWER_ITERS (8) is
+/* (1b) Reblock with a layout choice and a power-step count per split.  BSA_POWER_ITERS (8) is
  * bsa_reblock_layout.  Lite: [comfyui-wiki.com "Spark-H3 ...", "Benchmarks" ("基准测试")]
  * names a lighter Spark-H3-Lite that halves the reblock latency for a small fidelity loss at
  * 20 % and 30 % density and does not say how; the reading taken here is fewer power steps per
@@ -126,6 +126,17 @@ bsa_status bsa_reblock_layout(const bsa_desc* desc, const void* q, const void* k
 bsa_status bsa_reblock_ex(const bsa_desc* desc, const void* q, const void* k, int32_t layout,
                           int32_t power_iters, int32_t* perm_q, int32_t* perm_k, float* proj_opt,
                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* (1c) One side of the reblock: side 0 builds the query layouts (queries under M_K) into
+ * perm, side 1 the key layouts (keys under M_Q); each equals the corresponding output of
+ * bsa_reblock_ex with the same power_iters.  The two sides are independent, so a caller may
+ * run them on two streams (each with its own ws) and start bsa_prepare_kv once the key side is
+ * done.  proj_opt, if non-null, receives this side's projections in the same
+ * [heads][2][levels][tokens] layout (the other side's rows are left 0).  Errors as
+ * bsa_reblock_ex; a side other than 0 or 1 is BSA_E_ARG. */
+bsa_status bsa_reblock_side(const bsa_desc* desc, const void* q, const void* k, int32_t side,
+                            int32_t power_iters, int32_t* perm, float* proj_opt, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
 
 /* (2) Select.  Block scores S[h][i][j] = s * mean(query block i) . mean(key block j) with
  * s = 1/sqrt(D); per row the K largest (ties to the lower j), written ascending to

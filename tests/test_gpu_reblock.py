@@ -202,3 +202,19 @@ def test_full_layer_q_reuse_k_bf16_mid(mid):
         assert np.linalg.norm(o[h] - ro) / np.linalg.norm(ro) < 1e-2
         assert np.max(np.abs(o[h] - ro)) < 3e-2
         assert np.max(np.abs(lse[h] - rl)) < 3e-2
+
+
+@pytest.mark.parametrize("which", ["tiny", "mid"])
+def test_reblock_one_side_equals_both(which, tiny, mid):
+    """bsa_reblock_side builds each side alone, bit-identical to the two-sided call (the Lite
+    step count too), with this side's projections and the other side's left 0."""
+    wl, q, k, v = tiny if which == "tiny" else mid
+    dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    qd, kd = to_dev(q, dt), to_dev(k, dt)
+    for iters in ITERS:
+        pq, pk, proj = ops.reblock(qd, kd, with_proj=True, power_iters=iters)
+        for side, ref in ((0, pq), (1, pk)):
+            perm, pr = ops.reblock_side(qd, kd, side, power_iters=iters, with_proj=True)
+            assert torch.equal(perm, ref), (side, iters)
+            assert torch.equal(pr[:, side], proj[:, side])
+            assert torch.all(pr[:, 1 - side] == 0).item()

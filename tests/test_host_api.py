@@ -152,6 +152,16 @@ def test_reblock_and_hook_argument_errors(L):
                          None) == _lib.BSA_E_WORKSPACE
     # separate layouts need two permutation buffers
     assert L.bsa_reblock(desc(), FAKE, FAKE, FAKE, FAKE, None, FAKE, big, None) == _lib.BSA_E_ARG
+    # one-sided reblock: side must be 0 or 1
+    for side in (-1, 2):
+        assert L.bsa_reblock_side(desc(), FAKE, FAKE, side, 8, FAKE, None, FAKE, big,
+                                  None) == _lib.BSA_E_ARG
+    assert L.bsa_reblock_side(desc(), FAKE, FAKE, 0, 0, FAKE, None, FAKE, big,
+                              None) == _lib.BSA_E_ARG
+    assert L.bsa_reblock_side(desc(), FAKE, FAKE, 1, 8, None, None, FAKE, big,
+                              None) == _lib.BSA_E_ARG
+    assert L.bsa_reblock_side(desc(), FAKE, FAKE, 1, 8, FAKE, None, FAKE, 8,
+                              None) == _lib.BSA_E_WORKSPACE
     # power steps per split outside [1, 64]
     for it in (0, -1, 65):
         assert L.bsa_reblock_ex(desc(), FAKE, FAKE, 0, it, FAKE, FAKE2, None, FAKE, big,
