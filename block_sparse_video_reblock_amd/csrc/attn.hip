@@ -107,7 +107,10 @@ struct KSide {
 
 // Workgroups 0 .. wg_c - 1 take the query blocks of side `cs` (context queries: few, long
 // blocks, dispatched first and spread over every XCD), the rest those of side `vs`.  The lists
-// are a separate read-only argument so that the work loop reads them with scalar loads.
+// are a separate read-only argument so that the work loop reads them with scalar loads.  CTX
+// false compiles the launch without context tokens (no context side, every block listed, no
+// context tiles), whose work loops carry none of the context branches.
+template <bool CTX>
 __global__ __launch_bounds__(256, 2) void k_attn_bf16(QSide cs, QSide vs, int wg_c, KSide ks,
                                                        const int32_t* __restrict__ lists, int H,
                                                        float scale_log2) {
@@ -117,12 +120,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(QSide cs, QSide vs, int wg
   __shared__ float sm_l[4][64];
   __shared__ float sm_o[64 * 129];
   __shared__ float sm_tail[D];  // block-level compressed output of this query block
+  __shared__ float sm_wc[64];   // and its weight in each row's merge
   __shared__ uint4 sq[2][8][64];  // the queries in B-operand order (see below)
   // [nt_s * 64] summary-row bias * log2 e (-inf if selected), then with context tiles two
   // 64-row masks: 0 for a full context tile, 0 / -inf for the valid / padding rows of the last
   extern __shared__ float sbias[];
 
-  const bool is_ctx = blockIdx.x < wg_c;
+  const bool is_ctx = CTX && blockIdx.x < wg_c;
   const QSide S = is_ctx ? cs : vs;
   const int local = is_ctx ? blockIdx.x : xcd_remap(blockIdx.x - wg_c, H * vs.nbq);
   const int h = local / S.nbq, i = local - h * S.nbq;
@@ -130,11 +134,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(QSide cs, QSide vs, int wg
   const int g = lane >> 5, l32 = lane & 31;
   const int ntiles = ks.nt_s, nb = ks.nb;
   const int n_exact = S.n_exact, n_comp = S.n_comp, tau0 = S.tau0, topk = S.topk;
-  const int32_t* list = S.listed ? lists + ((size_t)h * S.nbq + i) * topk : nullptr;
+  const bool listed = !CTX || S.listed;
+  const int32_t* list = listed ? lists + ((size_t)h * S.nbq + i) * topk : nullptr;
 
   // bitmap of this query block's selected key blocks (masks them in the compressed branch);
   // cleared over every summary row, padding included
-  const int32_t* pq = S.perm ? S.perm + (size_t)h * S.rows + (size_t)i * kBlk : nullptr;
+  const bool permuted = !CTX || S.perm != nullptr;
+  const int32_t* pq = permuted ? S.perm + (size_t)h * S.rows + (size_t)i * kBlk : nullptr;
   const float* bias_h = ks.bias + (size_t)h * ntiles * 64;
   if (n_comp > 0 && tau0 < ntiles) {
     const int words = (ntiles * 64 + 31) >> 5;
@@ -150,7 +156,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(QSide cs, QSide vs, int wg
       sbias[key] = sel ? -INFINITY : bias_h[key] * kLog2e;  // padding rows hold -inf already
     }
   }
-  if (n_comp > 0 && ks.nt_c > 0 && tid < 128) {
+  if (CTX && n_comp > 0 && ks.nt_c > 0 && tid < 128) {
     const int last_rows = ks.n_ctx - (ks.nt_c - 1) * 64;
     sbias[ntiles * 64 + tid] = (tid < 64 || tid - 64 < last_rows) ? 0.f : -INFINITY;
   }
@@ -160,7 +166,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(QSide cs, QSide vs, int wg
   for (int u = tid; u < 2 * 8 * 64; u += 256) {
     const int n = u >> 9, c = (u >> 6) & 7, ln = u & 63;
     const int r = 32 * n + (ln & 31);
-    const int tok = pq ? pq[r] : min(i * kBlk + r, S.rows - 1);
+    const int tok = permuted ? pq[r] : min(i * kBlk + r, S.rows - 1);
     sq[n][c][ln] =
         reinterpret_cast<const uint4*>(S.q + ((size_t)h * S.rows + tok) * D)[2 * c + (ln >> 5)];
   }
@@ -191,13 +197,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(QSide cs, QSide vs, int wg
     if (it >= it_end) return;
     auto tile_ptrs = [&](int t, const uint4*& kp, const uint4*& vp, int& k0) {
       if (EXACT) {
-        const size_t blk = (size_t)h * nb + (list ? load_uniform(list + t) : t);
+        const size_t blk = (size_t)h * nb + (listed ? load_uniform(list + t) : t);
         kp = ks.ksw + blk * 1024;
         vp = ks.vsw + blk * 1024;
         k0 = 0;
       } else {
         const int tau = t - n_exact + tau0;
-        if (tau < ntiles) {
+        if (!CTX || tau < ntiles) {
           const size_t blk = (size_t)h * ntiles + tau;
           kp = ks.ktsw + blk * 1024;
           vp = ks.vtsw + blk * 1024;
@@ -352,7 +358,6 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(QSide cs, QSide vs, int wg
   // (with a block-level compressed state, that state is a fifth softmax part: max lc, sum 1,
   // output sm_tail)
   const float lc = tail ? S.tail_lse[(size_t)h * S.nbq + i] : -INFINITY;
-  float wc[2];
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
     const int qq = 32 * n + l32;
@@ -365,7 +370,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(QSide cs, QSide vs, int wg
 #pragma unroll
     for (int w = 0; w < 4; ++w) L += sm_l[w][qq] * __builtin_amdgcn_exp2f(sm_m[w][qq] - Mu);
     const float f = (L > 0.f) ? __builtin_amdgcn_exp2f(m_run[n] - Mu) / L : 0.f;
-    wc[n] = (L > 0.f) ? lt / L : 0.f;
+    if (tail && wave == 0 && g == 0) sm_wc[qq] = (L > 0.f) ? lt / L : 0.f;
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -379,10 +384,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(QSide cs, QSide vs, int wg
         for (int a = 0; a < 4; ++a)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int d = 32 * a + 8 * (r >> 2) + 4 * g + (r & 3);
-            const int idx = (32 * n + l32) * 129 + d;
-            sm_o[idx] = (w == 0) ? (tail ? fmaf(wc[n], sm_tail[d], acc[a][n][r]) : acc[a][n][r])
-                                 : sm_o[idx] + acc[a][n][r];
+            const int idx = (32 * n + l32) * 129 + 32 * a + 8 * (r >> 2) + 4 * g + (r & 3);
+            sm_o[idx] = (w == 0) ? acc[a][n][r] : sm_o[idx] + acc[a][n][r];
           }
     }
     __syncthreads();
@@ -390,10 +393,15 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(QSide cs, QSide vs, int wg
 
   // inverse permutation: row qq of the block is token perm_q[64 i + qq]
   const int qq = tid >> 2, part = tid & 3;
-  const int tok = pq ? pq[qq] : i * kBlk + qq;
-  if (tok < S.rows) {
+  const int tok = permuted ? pq[qq] : i * kBlk + qq;
+  if (permuted || tok < S.rows) {
     uint4* dst = reinterpret_cast<uint4*>(S.o + ((size_t)h * S.rows + tok) * D + part * 32);
-    const float* src = sm_o + qq * 129 + part * 32;
+    float* src = sm_o + qq * 129 + part * 32;
+    if (tail) {  // the block-level compressed output, weighted per row
+      const float wq = sm_wc[qq];
+#pragma unroll
+      for (int e = 0; e < 32; ++e) src[e] = fmaf(wq, sm_tail[part * 32 + e], src[e]);
+    }
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       uint4 u;
@@ -808,8 +816,12 @@ hipError_t launch_attn_bf16(const AttnLaunch& a, hipStream_t s) {
   const int wg_c = a.H * nt_c;
   const bool biased = a.n_comp > 0 || (nt_c > 0 && a.ctx_n_comp > 0);
   const size_t dyn = biased ? (size_t)(nt_s + (nt_c > 0 ? 2 : 0)) * 64 * sizeof(float) : 0;
-  k_attn_bf16<<<wg_c + a.H * a.nb, 256, dyn, s>>>(cs, vs, wg_c, ks, a.lists, a.H,
-                                                  a.scale * kLog2e);
+  if (wg_c > 0)
+    k_attn_bf16<true><<<wg_c + a.H * a.nb, 256, dyn, s>>>(cs, vs, wg_c, ks, a.lists, a.H,
+                                                          a.scale * kLog2e);
+  else
+    k_attn_bf16<false><<<a.H * a.nb, 256, dyn, s>>>(cs, vs, 0, ks, a.lists, a.H,
+                                                    a.scale * kLog2e);
   return hipGetLastError();
 }
 
