@@ -12,7 +12,7 @@ import math
 import numpy as np
 
 __all__ = [
-    "LEAF", "POWER_ITERS", "second_moment", "metric_factor", "metric_embed", "tree_levels",
+    "LEAF", "POWER_ITERS", "SMALL_BLOCKS", "shared_root_level", "second_moment", "metric_factor", "metric_embed", "tree_levels",
     "split_direction", "partition", "partition_from_projections", "reblock_head",
     "topk_count", "block_means", "block_scores", "topk_lists", "summaries",
     "sparse_attention_head", "mixed_attention_head", "dense_attention_head", "recall_head",
@@ -110,7 +110,20 @@ def _split_by_rank(ids: np.ndarray, p32: np.ndarray, n_left: int):
     return np.sort(ids[order[:n_left]]), np.sort(ids[order[n_left:]])
 
 
-def partition(U: np.ndarray, leaf: int = LEAF, iters: int = POWER_ITERS):
+SMALL_BLOCKS = 8
+
+
+def shared_root_level(n_blocks: int) -> int:
+    """The first tree level whose groups all hold at most SMALL_BLOCKS blocks (the largest
+    group of level l holds ceil(nb / 2^l) blocks)."""
+    lvl = 0
+    while -(-n_blocks // (1 << lvl)) > SMALL_BLOCKS:
+        lvl += 1
+    return lvl
+
+
+def partition(U: np.ndarray, leaf: int = LEAF, iters: int = POWER_ITERS,
+              shared_deep: bool = False):
     """Capacity-constrained hierarchical tree partition into exactly-`leaf`-token leaves.
 
     [P2] "What it's doing under the hood": a capacity-constrained tree partition down to
@@ -119,6 +132,11 @@ def partition(U: np.ndarray, leaf: int = LEAF, iters: int = POWER_ITERS):
     floor(m/2)*leaf tokens of smallest (p, token id), p = u.v rounded to fp32) and the rest;
     recursion left first; leaves in that depth-first order; ascending token id inside a leaf.
 
+    shared_deep (the Lite tree; [P1] "Benchmarks" names a lighter Spark-H3-Lite without its
+    mechanism): from the first level whose groups hold at most SMALL_BLOCKS blocks, each group
+    takes one direction and its descendants split along the same projections (no new
+    direction), so that subtree is its tokens in (p, token id) order cut into leaves.
+
     Returns (perm, proj): perm[p] = token id at position p; proj[l][i] = the fp32 projection
     token i received at level l (0 where its group was already a leaf)."""
     N = U.shape[0]
@@ -126,7 +144,9 @@ def partition(U: np.ndarray, leaf: int = LEAF, iters: int = POWER_ITERS):
         raise ValueError("token count must be a multiple of the leaf size")
     nb = N // leaf
     L = tree_levels(nb)
+    root = shared_root_level(nb) if shared_deep else L
     proj = np.zeros((L, N), dtype=np.float32)
+    key = np.zeros(N, dtype=np.float32)   # the projections a shared subtree keeps using
     groups = [np.arange(N)]
     for lvl in range(L):
         nxt = []
@@ -135,8 +155,10 @@ def partition(U: np.ndarray, leaf: int = LEAF, iters: int = POWER_ITERS):
             if m < 2:
                 nxt.append(ids)
                 continue
-            v = split_direction(U[ids], iters)
-            p32 = (U[ids] @ v).astype(np.float32)
+            if lvl <= root:
+                v = split_direction(U[ids], iters)
+                key[ids] = (U[ids] @ v).astype(np.float32)
+            p32 = key[ids]
             proj[lvl, ids] = p32
             left, right = _split_by_rank(ids, p32, (m // 2) * leaf)
             nxt += [left, right]
@@ -163,7 +185,7 @@ def partition_from_projections(proj: np.ndarray, n_tokens: int, leaf: int = LEAF
 
 
 def reblock_head(Q: np.ndarray, K: np.ndarray, leaf: int = LEAF, iters: int = POWER_ITERS,
-                 kind: str = "eigh", layout: str = "separate"):
+                 kind: str = "eigh", layout: str = "separate", shared_deep: bool = False):
     """Query layout from M_K, key layout from M_Q, each partitioned on its own ([P2]).
     Returns (perm_q, perm_k, proj_q, proj_k).  Q/K/V values are untouched.
 
@@ -173,11 +195,11 @@ def reblock_head(Q: np.ndarray, K: np.ndarray, leaf: int = LEAF, iters: int = PO
     if layout not in ("separate", "q_reuse_k"):
         raise ValueError(f"unknown layout {layout!r}")
     M_q = second_moment(Q)
-    perm_k, proj_k = partition(metric_embed(K, M_q, kind), leaf, iters)
+    perm_k, proj_k = partition(metric_embed(K, M_q, kind), leaf, iters, shared_deep)
     if layout == "q_reuse_k":
         return perm_k.copy(), perm_k, None, proj_k
     M_k = second_moment(K)
-    perm_q, proj_q = partition(metric_embed(Q, M_k, kind), leaf, iters)
+    perm_q, proj_q = partition(metric_embed(Q, M_k, kind), leaf, iters, shared_deep)
     return perm_q, perm_k, proj_q, proj_k
 
 

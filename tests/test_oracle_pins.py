@@ -249,6 +249,44 @@ def test_mixed_sequence_context_is_exact(tiny_inputs):
         assert np.max(np.abs(Ov - _sdpa(Qv, Kall, Vall))) < 1e-10
 
 
+def _groups_at(nb, level):
+    """(first block, blocks) of every group of a level: each split keeps floor(m/2) left."""
+    groups = [(0, nb)]
+    for _ in range(level):
+        groups = [c for b0, m in groups
+                  for c in (((b0, m // 2), (b0 + m // 2, m - m // 2)) if m >= 2 else ((b0, m),))]
+    return groups
+
+
+def test_lite_tree_cuts_each_small_subtree_along_one_direction(tiny_inputs):
+    """Lite tree (shared_deep): above the first level whose groups hold at most 8 blocks it is
+    the default tree; each group of that level is its tokens sorted by (fp32 projection on the
+    group's own direction, token id), cut into consecutive 64-token leaves, each leaf in
+    ascending token id.  Checked by an explicit sort per subtree on 64 blocks (root level 3)
+    and 8 blocks (one subtree, root level 0)."""
+    wl, Q, K, V = tiny_inputs
+    U = O.metric_embed(Q, O.second_moment(K))
+    for n_tok in (U.shape[0], 512):
+        Ux = U[:n_tok]
+        nb = n_tok // 64
+        root = O.shared_root_level(nb)
+        perm_l, proj_l = O.partition(Ux, shared_deep=True)
+        perm_d, proj_d = O.partition(Ux)
+        assert np.array_equal(proj_l[:root + 1], proj_d[:root + 1])
+        for b0, m in _groups_at(nb, root):
+            seg = perm_l[b0 * 64:(b0 + m) * 64]
+            ids = np.sort(seg)
+            assert np.array_equal(ids, np.sort(perm_d[b0 * 64:(b0 + m) * 64]))
+            p = (Ux[ids] @ O.split_direction(Ux[ids])).astype(np.float32) if m >= 2 else \
+                np.zeros(ids.size, np.float32)
+            ranked = ids[np.lexsort((ids, p))]
+            ref = np.concatenate([np.sort(ranked[64 * j:64 * j + 64]) for j in range(m)])
+            assert np.array_equal(seg, ref), (nb, b0, m)
+        if nb > 8:
+            assert not np.array_equal(perm_l, perm_d)
+    assert [O.shared_root_level(nb) for nb in (1, 8, 9, 256, 1134, 8192)] == [0, 0, 1, 5, 8, 10]
+
+
 def _naive_tree(X, M, leaf):
     """Independent partitioner: explicit Mahalanobis-cosine Gram matrix, principal direction
     from numpy.linalg.eigh of the centred Gram (kernel PCA), full stable sort."""
