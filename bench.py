@@ -77,7 +77,7 @@ class Layer:
     """Device buffers and the four stage calls of one layer (Reblock or fixed-tile layouts)."""
 
     def __init__(self, ops, torch, wl, q, k, v, topk, fixed_tiles=False, ws=None,
-                 layout="separate", tail="token", ctx=None, power_iters=8):
+                 layout="separate", tail="token", ctx=None, power_iters=8, lite_tree=False):
         self.ops, self.torch = ops, torch
         dev = torch.device("cuda:0")
         dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
@@ -102,6 +102,7 @@ class Layer:
         self.fixed = fixed_tiles
         self.reblock_layout = ops._LAYOUTS[layout]
         self.power_iters = power_iters
+        self.tree_flags = ops.BSA_TREE_SHARED_DEEP if lite_tree else 0
         self.flags = ((ops.BSA_MEANPOOL if fixed_tiles else 0) |
                       (ops.BSA_TAIL_BLOCK if tail == "block" else 0))
         self.L = ops.lib()
@@ -122,8 +123,8 @@ class Layer:
         else:
             ops.check(self.L.bsa_reblock_ex(ctypes.byref(self.d), p(self.qd), p(self.kd),
                                             self.reblock_layout, self.power_iters,
-                                            p(self.perm_q), p(self.perm_k), None, p(self.ws),
-                                            self.ws.numel(), self.stream))
+                                            self.tree_flags, p(self.perm_q), p(self.perm_k),
+                                            None, p(self.ws), self.ws.numel(), self.stream))
 
     def select(self):
         p = self.p
@@ -237,7 +238,8 @@ def main_headline(args, ops, synth, torch, np):
     log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
     ctx = synth.make_ctx(wl, args.ctx, (q, k, v)) if args.ctx else None
     lay = Layer(ops, torch, wl, q, k, v, topk, layout=args.layout, tail=args.tail, ctx=ctx,
-                power_iters=ops.BSA_POWER_ITERS_LITE if args.lite else ops.BSA_POWER_ITERS)
+                power_iters=ops.BSA_POWER_ITERS_LITE if args.lite else ops.BSA_POWER_ITERS,
+                lite_tree=args.lite)
     ms_step, stage_ms, series = time_steps(torch, lay.stages(), args.steps, args.warmup)
     assert torch.isfinite(lay.out.float()).all().item(), "non-finite output"
     log(f"[bench] layer {ms_step:.3f} ms/step; stages " +
@@ -320,6 +322,7 @@ def main_headline(args, ops, synth, torch, np):
                    "reblock_layout": args.layout, "tail_granularity": args.tail,
                    "context_tokens": args.ctx,
                    "reblock_power_iters": lay.power_iters,
+                   "reblock_lite_tree": bool(lay.tree_flags),
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
@@ -399,14 +402,18 @@ def main_sweep(args, ops, synth, torch, np):
     rows = []
     for ratio in synth.SWEEP_RATIOS:
         topk = ops.topk_count(nb, ratio)
-        for fixed, layout, iters, name in (
-                (False, "separate", 8, "reblock, reweighted summaries"),
-                (False, "separate", 2, "Lite reblock (2 power steps), reweighted summaries"),
-                (False, "q_reuse_k", 8, "reblock of the keys reused for the queries, "
-                                        "reweighted summaries"),
-                (True, "separate", 8, "fixed 4x4x4 tiles, mean-pooled summaries")):
+        for fixed, layout, iters, shared, name in (
+                (False, "separate", 8, False, "reblock, reweighted summaries"),
+                (False, "separate", 2, False, "reblock with 2 power steps per split, "
+                                              "reweighted summaries"),
+                (False, "separate", 2, True, "Lite reblock (2 power steps, one direction per "
+                                             "subtree of at most 8 blocks), reweighted "
+                                             "summaries"),
+                (False, "q_reuse_k", 8, False, "reblock of the keys reused for the queries, "
+                                               "reweighted summaries"),
+                (True, "separate", 8, False, "fixed 4x4x4 tiles, mean-pooled summaries")):
             lay = Layer(ops, torch, wl, q, k, v, topk, fixed_tiles=fixed, ws=base.ws,
-                        layout=layout, power_iters=iters)
+                        layout=layout, power_iters=iters, lite_tree=shared)
             ms_step, stage_ms, _ = time_steps(torch, lay.stages(), args.steps, args.warmup)
             rec = lay.recall(lse_dense)
             row = {"topk_ratio": ratio, "topk_blocks": topk, "layout": name,
@@ -414,7 +421,8 @@ def main_sweep(args, ops, synth, torch, np):
                    "speedup_vs_dense_attention": dense_ms / ms_step}
             rows.append(row)
             tag = "fixed    " if fixed else ("q_reuse_k" if layout == "q_reuse_k" else
-                                              "reblock  " if iters == 8 else "lite     ")
+                                              "reblock  " if iters == 8 else
+                                              "lite     " if shared else "2 steps  ")
             log(f"[bench] ratio {ratio:.1f} {tag}: layer {ms_step:.3f} ms, recall {rec:.4f}")
             del lay
     return {
@@ -450,7 +458,8 @@ def main():
                     help="mixed sequence: N exact context tokens (text, audio, conditioning) "
                          "beside the video grid")
     ap.add_argument("--lite", action="store_true",
-                    help="Lite reblock: 2 power steps per split instead of 8")
+                    help="Lite reblock: 2 power steps per split and one direction per subtree "
+                         "of at most 8 blocks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",

@@ -39,9 +39,11 @@ _SIGS = {
     "bsa_reblock_layout": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), _P, _P, ctypes.c_int32, _P,
                                             _P, _P, _P, ctypes.c_size_t, _P]),
     "bsa_reblock_ex": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), _P, _P, ctypes.c_int32,
-                                        ctypes.c_int32, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+                                        ctypes.c_int32, ctypes.c_uint32, _P, _P, _P, _P,
+                                        ctypes.c_size_t, _P]),
     "bsa_reblock_side": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), _P, _P, ctypes.c_int32,
-                                          ctypes.c_int32, _P, _P, _P, ctypes.c_size_t, _P]),
+                                          ctypes.c_int32, ctypes.c_uint32, _P, _P, _P,
+                                          ctypes.c_size_t, _P]),
     "bsa_select": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), _P, _P, _P, _P, ctypes.c_float,
                                     ctypes.c_int32, _P, _P, _P, ctypes.c_size_t, _P]),
     "bsa_sparse_attn": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), _P, _P, _P, _P, _P, _P,
@@ -153,13 +155,15 @@ BSA_LAYOUT_Q_REUSE_K = 1
 _LAYOUTS = {"separate": BSA_LAYOUT_SEPARATE, "q_reuse_k": BSA_LAYOUT_Q_REUSE_K}
 
 
-BSA_POWER_ITERS, BSA_POWER_ITERS_LITE = 8, 2
+BSA_POWER_ITERS, BSA_POWER_ITERS_LITE, BSA_TREE_SHARED_DEEP = 8, 2, 1
 
 
-def reblock(q, k, ws=None, with_proj=False, layout="separate", power_iters=BSA_POWER_ITERS):
+def reblock(q, k, ws=None, with_proj=False, layout="separate", power_iters=BSA_POWER_ITERS,
+            shared_deep=False):
     """(perm_q, perm_k[, proj]) int32 [H][N] (and float [H][2][levels][N]).
     layout "separate" (bsa_reblock) or "q_reuse_k" (perm_q is a copy of the key layout);
-    power_iters: power steps per split (BSA_POWER_ITERS_LITE for the Lite reblock)."""
+    power_iters: power steps per split; shared_deep: one direction per subtree of at most 8
+    blocks (the Lite reblock is power_iters=BSA_POWER_ITERS_LITE, shared_deep=True)."""
     torch = _torch()
     if layout not in _LAYOUTS:
         raise BsaError(BSA_E_ARG, f"unknown layout {layout!r}")
@@ -171,13 +175,15 @@ def reblock(q, k, ws=None, with_proj=False, layout="separate", power_iters=BSA_P
     levels = max(0, (N // BLOCK - 1).bit_length())
     proj = torch.empty(H, 2, levels, N, dtype=torch.float32, device=q.device) if with_proj else None
     check(lib().bsa_reblock_ex(ctypes.byref(d), _dev_ptr(q, q.dtype), _dev_ptr(k, q.dtype),
-                               _LAYOUTS[layout], int(power_iters), _dev_ptr(perm_q),
+                               _LAYOUTS[layout], int(power_iters),
+                               BSA_TREE_SHARED_DEEP if shared_deep else 0, _dev_ptr(perm_q),
                                _dev_ptr(perm_k), _dev_ptr(proj), _dev_ptr(ws), ws.numel(),
                                _stream()))
     return (perm_q, perm_k, proj) if with_proj else (perm_q, perm_k)
 
 
-def reblock_side(q, k, side, ws=None, power_iters=BSA_POWER_ITERS, with_proj=False):
+def reblock_side(q, k, side, ws=None, power_iters=BSA_POWER_ITERS, with_proj=False,
+                 shared_deep=False):
     """One side of the reblock: side 0 the query layouts, side 1 the key layouts (int32 [H][N]),
     and with_proj its projections (float [H][2][levels][N], the other side's rows 0)."""
     torch = _torch()
@@ -189,7 +195,9 @@ def reblock_side(q, k, side, ws=None, power_iters=BSA_POWER_ITERS, with_proj=Fal
     proj = torch.empty(H, 2, levels, N, dtype=torch.float32, device=q.device) if with_proj \
         else None
     check(lib().bsa_reblock_side(ctypes.byref(d), _dev_ptr(q, q.dtype), _dev_ptr(k, q.dtype),
-                                 int(side), int(power_iters), _dev_ptr(perm), _dev_ptr(proj),
+                                 int(side), int(power_iters),
+                                 BSA_TREE_SHARED_DEEP if shared_deep else 0, _dev_ptr(perm),
+                                 _dev_ptr(proj),
                                  _dev_ptr(ws), ws.numel(), _stream()))
     return (perm, proj) if with_proj else perm
 

@@ -218,13 +218,14 @@ size_t bsa_workspace_bytes(const bsa_desc* d) {
 bsa_status bsa_reblock_layout(const bsa_desc* d, const void* q, const void* k, int32_t layout,
                               int32_t* perm_q, int32_t* perm_k, float* proj_opt, void* ws,
                               size_t ws_bytes, hipStream_t stream) {
-  return bsa_reblock_ex(d, q, k, layout, BSA_POWER_ITERS, perm_q, perm_k, proj_opt, ws, ws_bytes,
-                        stream);
+  return bsa_reblock_ex(d, q, k, layout, BSA_POWER_ITERS, 0, perm_q, perm_k, proj_opt, ws,
+                        ws_bytes, stream);
 }
 
 bsa_status bsa_reblock_ex(const bsa_desc* d, const void* q, const void* k, int32_t layout,
-                          int32_t power_iters, int32_t* perm_q, int32_t* perm_k, float* proj_opt,
-                          void* ws, size_t ws_bytes, hipStream_t stream) {
+                          int32_t power_iters, uint32_t tree_flags, int32_t* perm_q,
+                          int32_t* perm_k, float* proj_opt, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
   bsa_status st = check_desc(d);
   if (st != BSA_OK) return st;
   if (layout != BSA_LAYOUT_SEPARATE && layout != BSA_LAYOUT_Q_REUSE_K)
@@ -232,6 +233,8 @@ bsa_status bsa_reblock_ex(const bsa_desc* d, const void* q, const void* k, int32
   if (power_iters < 1 || power_iters > BSA_MAX_POWER_ITERS)
     return fail(BSA_E_ARG, "power_iters = %d is not in [1, %d]", (int)power_iters,
                 BSA_MAX_POWER_ITERS);
+  if (tree_flags & ~uint32_t(BSA_TREE_SHARED_DEEP))
+    return fail(BSA_E_ARG, "unknown tree flags 0x%x", tree_flags);
   if (!q || !k || !perm_q || !perm_k) return fail(BSA_E_ARG, "null tensor pointer");
   if (layout == BSA_LAYOUT_SEPARATE && perm_q == perm_k)
     return fail(BSA_E_ARG, "separate layouts need two permutation buffers");
@@ -243,20 +246,22 @@ bsa_status bsa_reblock_ex(const bsa_desc* d, const void* q, const void* k, int32
                                         perm_q, perm_k, proj_opt,
                                         layout == BSA_LAYOUT_Q_REUSE_K ? bsa::kSideKeys
                                                                        : bsa::kSideBoth,
-                                        layout == BSA_LAYOUT_Q_REUSE_K, power_iters, ws,
-                                        stream),
+                                        layout == BSA_LAYOUT_Q_REUSE_K, power_iters,
+                                        (tree_flags & BSA_TREE_SHARED_DEEP) != 0, ws, stream),
                     "reblock launch");
 }
 
 bsa_status bsa_reblock_side(const bsa_desc* d, const void* q, const void* k, int32_t side,
-                            int32_t power_iters, int32_t* perm, float* proj_opt, void* ws,
-                            size_t ws_bytes, hipStream_t stream) {
+                            int32_t power_iters, uint32_t tree_flags, int32_t* perm,
+                            float* proj_opt, void* ws, size_t ws_bytes, hipStream_t stream) {
   bsa_status st = check_desc(d);
   if (st != BSA_OK) return st;
   if (side != 0 && side != 1) return fail(BSA_E_ARG, "side = %d is not 0 or 1", (int)side);
   if (power_iters < 1 || power_iters > BSA_MAX_POWER_ITERS)
     return fail(BSA_E_ARG, "power_iters = %d is not in [1, %d]", (int)power_iters,
                 BSA_MAX_POWER_ITERS);
+  if (tree_flags & ~uint32_t(BSA_TREE_SHARED_DEEP))
+    return fail(BSA_E_ARG, "unknown tree flags 0x%x", tree_flags);
   if (!q || !k || !perm) return fail(BSA_E_ARG, "null tensor pointer");
   st = check_ws(ws, ws_bytes, bsa::reblock_ws_bytes(d->heads, d->tokens, d->head_dim));
   if (st != BSA_OK) return st;
@@ -265,7 +270,8 @@ bsa_status bsa_reblock_side(const bsa_desc* d, const void* q, const void* k, int
   return hip_status(bsa::launch_reblock(is_bf16(d), q, k, d->heads, d->tokens, d->head_dim,
                                         perm, perm, proj_opt,
                                         side ? bsa::kSideKeys : bsa::kSideQueries, false,
-                                        power_iters, ws, stream),
+                                        power_iters, (tree_flags & BSA_TREE_SHARED_DEEP) != 0,
+                                        ws, stream),
                     "reblock launch");
 }
 

@@ -84,11 +84,12 @@ hipError_t launch_topk(const float* scores, int rows, int nb, int k, int32_t* li
 // ------------------------------------------------------------------ reblock (stage 1)
 size_t reblock_ws_bytes(int H, int N, int D);
 // sides: which trees to build (queries under M_K into perm_q, keys under M_Q into perm_k);
-// copy_q: perm_q becomes a copy of perm_k afterwards; iters: power steps per split
+// copy_q: perm_q becomes a copy of perm_k afterwards; iters: power steps per split;
+// shared_deep: the Lite tree (one direction per subtree of at most 8 blocks)
 constexpr int kSideQueries = 1, kSideKeys = 2, kSideBoth = 3;
 hipError_t launch_reblock(bool bf16, const void* q, const void* k, int H, int N, int D,
                           int32_t* perm_q, int32_t* perm_k, float* proj_opt, int sides,
-                          bool copy_q, int iters, void* ws, hipStream_t s);
+                          bool copy_q, int iters, bool shared_deep, void* ws, hipStream_t s);
 size_t partition_ws_bytes(int P, int N);
 hipError_t launch_partition_from_proj(int P, int N, const float* proj, int32_t* perm, void* ws,
                                       hipStream_t s);

@@ -880,6 +880,7 @@ struct ProblemArgs {
   // (1, 2) when the queries reuse the key layout
   int p0, pstep;
   int iters;               // power steps per split
+  int shared_deep;         // Lite tree: below the subtree root, cut along the root's projections
 };
 
 BSA_DEV int problem_of(const ProblemArgs& a, int b) { return a.p0 + a.pstep * b; }
@@ -1441,13 +1442,14 @@ __global__ __launch_bounds__(256, 2) void k_subtree_pair(ProblemArgs a, int leve
 // grid (roots, P): subtrees whose root spans at most kSmallBlocks blocks.  The root's positions
 // and keys stay in LDS for all remaining levels.
 constexpr int kSmallBlocks = 8;
-template <typename T, int D>
+template <typename T, int D, bool SHARED>
 __global__ __launch_bounds__(256, 2) void k_subtree_small(ProblemArgs a, int ls) {
   __shared__ StageLds<D, 2> st;
   __shared__ DirLds L;
   __shared__ int32_t spos[kSmallBlocks * kBlk];
   __shared__ int32_t stmp[kSmallBlocks * kBlk];
   __shared__ float skeys[kSmallBlocks * kBlk];
+  __shared__ float skeys2[kSmallBlocks * kBlk];  // keys in partitioned order (Lite tree)
   __shared__ int hist[4 * 256];
   __shared__ int sm[16];
   const int g0 = a.lists[(size_t)ls * a.G + blockIdx.x], p = problem_of(a, blockIdx.y);
@@ -1459,42 +1461,106 @@ __global__ __launch_bounds__(256, 2) void k_subtree_small(ProblemArgs a, int ls)
   const float ysc = a.yscale[2 * p], inv_s2 = a.yscale[2 * p + 1];
   for (int i = threadIdx.x; i < rm * kBlk; i += 256) spos[i] = pos[i];
   __syncthreads();
-  for (int level = ls; level < a.L; ++level) {
-    const int depth = level - ls;
-    for (int g = g0 << depth; g < ((g0 + 1) << depth); ++g) {
-      int b0, m;
-      if (group_geom(a.nb, level, g, b0, m) != kGroupSplit) continue;
-      const int lb0 = b0 - rb0, n = m * kBlk;
-      const float shv = threadIdx.x < D ? parent_mean<D>(a, p, level, g)[threadIdx.x] : 0.f;
-      const float y_first = first_candidate<T, D>(X, spos, inv_n, lb0 * kBlk);
-      f32x16_t acc[Cov<D>::TILES];
-      // M is read (from L2) only for the power steps, so it holds no registers during the
-      // statistics
-      MRegs<D> M;
-      {
-        SymAcc<D> sacc;
-        sacc.zero();
-        float dpart[D / 8];
+  // (Lite tree) the subtree root's split, with its own direction and projections, which the
+  // partition carries along with the positions
+  auto full_split = [&](int level, int g) {
+    int b0, m;
+    if (group_geom(a.nb, level, g, b0, m) != kGroupSplit) return;
+    const int lb0 = b0 - rb0, n = m * kBlk;
+    const float shv = threadIdx.x < D ? parent_mean<D>(a, p, level, g)[threadIdx.x] : 0.f;
+    const float y_first = first_candidate<T, D>(X, spos, inv_n, lb0 * kBlk);
+    f32x16_t acc[Cov<D>::TILES];
+    // M is read (from L2) only for the power steps, so it holds no registers during the
+    // statistics
+    MRegs<D> M;
+    {
+      SymAcc<D> sacc;
+      sacc.zero();
+      float dpart[D / 8];
 #pragma unroll
-        for (int e = 0; e < D / 8; ++e) dpart[e] = 0.f;
-        sym_stats_range<T, D, true>(X, spos, inv_n, lb0, lb0 + m, L.shift, shv, ysc, st, sacc,
-                                    dpart);
-        reduce_dpart<D>(dpart, L.red, L.mu);
-        sym_to_regs<D>(sacc, inv_s2, st, acc);
+      for (int e = 0; e < D / 8; ++e) dpart[e] = 0.f;
+      sym_stats_range<T, D, true>(X, spos, inv_n, lb0, lb0 + m, L.shift, shv, ysc, st, sacc,
+                                  dpart);
+      reduce_dpart<D>(dpart, L.red, L.mu);
+      sym_to_regs<D>(sacc, inv_s2, st, acc);
+    }
+    M.load(problem_metric<D>(a, p));  // overlaps the centring in group_direction
+    group_direction<T, D>(acc, L, M, n, 1.f, X, spos, inv_n, lb0 * kBlk, y_first, a.iters);
+    if (threadIdx.x < D) group_mean<D>(a, p, level, g)[threadIdx.x] = L.mu[threadIdx.x];
+    float* proj = problem_proj(a, p, level);
+    project_range<T, D>(X, spos, inv_n, lb0, lb0 + m, L.w, skeys, proj);
+    __syncthreads();
+    const int want = (m >> 1) * kBlk;
+    int take;
+    const uint32_t T_ = select_smallest_w<256>(skeys + lb0 * kBlk, n, want, hist, sm, &take);
+    partition_w<256>(skeys + lb0 * kBlk, spos + lb0 * kBlk, stmp, n, want, T_, take, sm, skeys2);
+    for (int i = threadIdx.x; i < n; i += 256) {
+      spos[lb0 * kBlk + i] = stmp[i];
+      skeys[lb0 * kBlk + i] = skeys2[i];
+    }
+    __syncthreads();
+  };
+  // Lite tree: a split of group g along the projections its subtree root computed, which the
+  // partitions carried along with the positions
+  auto rank_split = [&](int level, int g) {
+    int b0, m;
+    if (group_geom(a.nb, level, g, b0, m) != kGroupSplit) return;
+    const int lb0 = b0 - rb0, n = m * kBlk;
+    float* proj = problem_proj(a, p, level);
+    if (proj)
+      for (int i = threadIdx.x; i < n; i += 256) proj[spos[lb0 * kBlk + i]] = skeys[lb0 * kBlk + i];
+    const int want = (m >> 1) * kBlk;
+    int take;
+    const uint32_t T_ = select_smallest_w<256>(skeys + lb0 * kBlk, n, want, hist, sm, &take);
+    partition_w<256>(skeys + lb0 * kBlk, spos + lb0 * kBlk, stmp, n, want, T_, take, sm, skeys2);
+    for (int i = threadIdx.x; i < n; i += 256) {
+      spos[lb0 * kBlk + i] = stmp[i];
+      skeys[lb0 * kBlk + i] = skeys2[i];
+    }
+    __syncthreads();
+  };
+  if constexpr (SHARED) {
+    full_split(ls, g0);
+    for (int level = ls + 1; level < a.L; ++level)
+      for (int g = g0 << (level - ls); g < ((g0 + 1) << (level - ls)); ++g) rank_split(level, g);
+  } else {
+    for (int level = ls; level < a.L; ++level) {
+      const int depth = level - ls;
+      for (int g = g0 << depth; g < ((g0 + 1) << depth); ++g) {
+        int b0, m;
+        if (group_geom(a.nb, level, g, b0, m) != kGroupSplit) continue;
+        const int lb0 = b0 - rb0, n = m * kBlk;
+        const float shv = threadIdx.x < D ? parent_mean<D>(a, p, level, g)[threadIdx.x] : 0.f;
+        const float y_first = first_candidate<T, D>(X, spos, inv_n, lb0 * kBlk);
+        f32x16_t acc[Cov<D>::TILES];
+        // M is read (from L2) only for the power steps, so it holds no registers during the
+        // statistics
+        MRegs<D> M;
+        {
+          SymAcc<D> sacc;
+          sacc.zero();
+          float dpart[D / 8];
+#pragma unroll
+          for (int e = 0; e < D / 8; ++e) dpart[e] = 0.f;
+          sym_stats_range<T, D, true>(X, spos, inv_n, lb0, lb0 + m, L.shift, shv, ysc, st,
+                                      sacc, dpart);
+          reduce_dpart<D>(dpart, L.red, L.mu);
+          sym_to_regs<D>(sacc, inv_s2, st, acc);
+        }
+        M.load(problem_metric<D>(a, p));  // overlaps the centring in group_direction
+        group_direction<T, D>(acc, L, M, n, 1.f, X, spos, inv_n, lb0 * kBlk, y_first,
+                              a.iters);
+        if (threadIdx.x < D) group_mean<D>(a, p, level, g)[threadIdx.x] = L.mu[threadIdx.x];
+        float* proj = problem_proj(a, p, level);
+        project_range<T, D>(X, spos, inv_n, lb0, lb0 + m, L.w, skeys, proj);
+        __syncthreads();
+        const int want = (m >> 1) * kBlk;
+        int take;
+        const uint32_t T_ = select_smallest_w<256>(skeys + lb0 * kBlk, n, want, hist, sm, &take);
+        partition_w<256>(skeys + lb0 * kBlk, spos + lb0 * kBlk, stmp, n, want, T_, take, sm);
+        for (int i = threadIdx.x; i < n; i += 256) spos[lb0 * kBlk + i] = stmp[i];
+        __syncthreads();
       }
-      M.load(problem_metric<D>(a, p));  // overlaps the centring in group_direction
-      group_direction<T, D>(acc, L, M, n, 1.f, X, spos, inv_n, lb0 * kBlk, y_first,
-                            a.iters);
-      if (threadIdx.x < D) group_mean<D>(a, p, level, g)[threadIdx.x] = L.mu[threadIdx.x];
-      float* proj = problem_proj(a, p, level);
-      project_range<T, D>(X, spos, inv_n, lb0, lb0 + m, L.w, skeys, proj);
-      __syncthreads();
-      const int want = (m >> 1) * kBlk;
-      int take;
-      const uint32_t T_ = select_smallest_w<256>(skeys + lb0 * kBlk, n, want, hist, sm, &take);
-      partition_w<256>(skeys + lb0 * kBlk, spos + lb0 * kBlk, stmp, n, want, T_, take, sm);
-      for (int i = threadIdx.x; i < n; i += 256) spos[lb0 * kBlk + i] = stmp[i];
-      __syncthreads();
     }
   }
   for (int i = threadIdx.x; i < rm * kBlk; i += 256) pos[i] = spos[i];
@@ -1582,7 +1648,7 @@ int active_count(int nb, int level) {
 template <typename T, int D>
 hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm_q,
                        int32_t* perm_k, float* proj_opt, int sides, bool copy_q, int iters,
-                       void* ws, hipStream_t s) {
+                       bool shared_deep, void* ws, hipStream_t s) {
   const RebLayout R = reb_layout(H, N, D);
   char* w = static_cast<char*>(ws);
   // sides: kSideQueries builds the query trees only (problems 2h, under M_K), kSideKeys the
@@ -1601,6 +1667,7 @@ hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm
       reinterpret_cast<float*>(w + R.mom_partial), R.nch_mom, N, mside0, mom, msplit);
   ProblemArgs a{};
   a.iters = iters;
+  a.shared_deep = shared_deep ? 1 : 0;
   a.q = q;
   a.k = k;
   a.H = H;
@@ -1649,7 +1716,7 @@ hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm
   int level = 0;
   for (; level < R.L; ++level) {
     const int slices = wide_slices(level, nb);
-    if (slices <= 1) break;
+    if (slices <= 1 || ceil_div(nb, 1 << level) <= kSmallBlocks) break;
     a.level = level;
     a.slices = slices;
     const int G = 1 << level;
@@ -1668,7 +1735,10 @@ hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm
     const int roots = active_count(nb, level);
     if (roots == 0) continue;
     if (ceil_div(nb, 1 << level) <= kSmallBlocks) {
-      k_subtree_small<T, D><<<dim3(roots, P), 256, 0, s>>>(a, level);
+      if (shared_deep)
+        k_subtree_small<T, D, true><<<dim3(roots, P), 256, 0, s>>>(a, level);
+      else
+        k_subtree_small<T, D, false><<<dim3(roots, P), 256, 0, s>>>(a, level);
       break;
     }
     a.cov_prev = reinterpret_cast<float*>(w + ((level & 1) ? R.cov0 : R.cov1));
@@ -1729,12 +1799,12 @@ size_t reblock_ws_bytes(int H, int N, int D) { return reb_layout(H, N, D).total;
 
 hipError_t launch_reblock(bool bf16, const void* q, const void* k, int H, int N, int D,
                           int32_t* perm_q, int32_t* perm_k, float* proj_opt, int sides,
-                          bool copy_q, int iters, void* ws, hipStream_t s) {
+                          bool copy_q, int iters, bool shared_deep, void* ws, hipStream_t s) {
   if (bf16)
     return run_reblock<uint16_t, 128>(q, k, H, N, perm_q, perm_k, proj_opt, sides, copy_q,
-                                      iters, ws, s);
-  return run_reblock<float, 64>(q, k, H, N, perm_q, perm_k, proj_opt, sides, copy_q, iters, ws,
-                                s);
+                                      iters, shared_deep, ws, s);
+  return run_reblock<float, 64>(q, k, H, N, perm_q, perm_k, proj_opt, sides, copy_q, iters,
+                                shared_deep, ws, s);
 }
 
 }  // namespace bsa

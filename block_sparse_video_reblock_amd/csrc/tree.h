@@ -250,9 +250,10 @@ BSA_DEV uint32_t select_smallest_w(const float* keys, int n, int want, int* hist
 
 // Stable two-way partition (same result as block_partition).  Wave w streams one contiguous
 // range of 64-element steps with coalesced loads; ballots give in-order ranks.  sm: 2*NW ints.
+// keys_out, if given, receives the keys in the partitioned order.
 template <int NT>
 BSA_DEV void partition_w(const float* keys, const int32_t* in, int32_t* out, int n, int want,
-                         uint32_t T, int take, int* sm) {
+                         uint32_t T, int take, int* sm, float* keys_out = nullptr) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int steps = (n + 63) / 64;
@@ -280,14 +281,17 @@ BSA_DEV void partition_w(const float* keys, const int32_t* in, int32_t* out, int
   for (int base = i0; base < i1; base += 64) {
     const int i = base + lane;
     const bool ok = i < i1;
-    const uint32_t key = ok ? orderable_key(keys[i]) : 0xFFFFFFFFu;
+    const float kv = ok ? keys[i] : 0.f;
+    const uint32_t key = ok ? orderable_key(kv) : 0xFFFFFFFFu;
     const bool eq = ok && key == T;
     const uint64_t eqm = __ballot(eq);
     const bool left = ok && (key < T || (eq && eq_seen + lanes_below(eqm) < take));
     const uint64_t lm = __ballot(left);
     if (ok) {
       const int lb = left_before + left_run + lanes_below(lm);  // lefts before i
-      out[left ? lb : want + (i - lb)] = in[i];
+      const int dst = left ? lb : want + (i - lb);
+      out[dst] = in[i];
+      if (keys_out != nullptr) keys_out[dst] = kv;
     }
     left_run += __popcll(lm);
     eq_seen += __popcll(eqm);

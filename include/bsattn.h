@@ -16,7 +16,7 @@
  *                 [comfyui-wiki.com page, "What Spark-Attn changes" and its figure]
  *   (5) log-sum-exp merge of the two branches and the inverse permutation to token order.
  * Options on the same path: the key layout reused for the queries (bsa_reblock_layout), the
- * Lite power-step count (bsa_reblock_ex), the block-level compressed branch (BSA_TAIL_BLOCK),
+ * Lite tree (bsa_reblock_ex: power steps per split, one direction per small subtree), the block-level compressed branch (BSA_TAIL_BLOCK),
  * and exact context tokens beside the video grid (bsa_sparse_attn_ctx).
  *
  * Conventions shared by every call
@@ -114,29 +114,37 @@ bsa_status bsa_reblock_layout(const bsa_desc* desc, const void* q, const void* k
                               int32_t* perm_q, int32_t* perm_k, float* proj_opt,
                               void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* (1b) Reblock with a layout choice and a power-step count per split.  BSA_POWER_ITERS (8) is
- * bsa_reblock_layout.  Lite: [comfyui-wiki.com "Spark-H3 ...", "Benchmarks" ("基准测试")]
- * names a lighter Spark-H3-Lite that halves the reblock latency for a small fidelity loss at
- * 20 % and 30 % density and does not say how; the reading taken here is fewer power steps per
- * split (BSA_POWER_ITERS_LITE = 2) from the same start vector, every other step of the tree
- * unchanged.  power_iters outside [1, BSA_MAX_POWER_ITERS] is BSA_E_ARG. */
+/* (1b) Reblock with a layout choice, a power-step count per split and tree flags.
+ * bsa_reblock_layout is power_iters = BSA_POWER_ITERS (8), tree_flags = 0.
+ * BSA_TREE_SHARED_DEEP: from the first level whose groups hold at most 8 blocks, each group
+ * takes one direction and its descendants keep cutting along the same projections (the group's
+ * tokens in (projection, token id) order cut into 64-token leaves); proj_opt then repeats those
+ * projections at the deeper levels.
+ * Lite: [comfyui-wiki.com "Spark-H3 ...", "Benchmarks" ("基准测试")] names a lighter
+ * Spark-H3-Lite that halves the reblock latency for a small fidelity loss at 20 % and 30 %
+ * density and does not say how; the reading taken here is the lighter tree
+ * BSA_TREE_SHARED_DEEP with BSA_POWER_ITERS_LITE (2) power steps per split, the start vector,
+ * capacity cut and leaf order unchanged.  power_iters outside [1, BSA_MAX_POWER_ITERS] or an
+ * unknown tree flag is BSA_E_ARG. */
 #define BSA_POWER_ITERS 8
 #define BSA_POWER_ITERS_LITE 2
 #define BSA_MAX_POWER_ITERS 64
+#define BSA_TREE_SHARED_DEEP 1u
 bsa_status bsa_reblock_ex(const bsa_desc* desc, const void* q, const void* k, int32_t layout,
-                          int32_t power_iters, int32_t* perm_q, int32_t* perm_k, float* proj_opt,
-                          void* ws, size_t ws_bytes, hipStream_t stream);
+                          int32_t power_iters, uint32_t tree_flags, int32_t* perm_q,
+                          int32_t* perm_k, float* proj_opt, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
 
 /* (1c) One side of the reblock: side 0 builds the query layouts (queries under M_K) into
  * perm, side 1 the key layouts (keys under M_Q); each equals the corresponding output of
- * bsa_reblock_ex with the same power_iters.  The two sides are independent, so a caller may
+ * bsa_reblock_ex with the same power_iters and tree_flags.  The two sides are independent, so a caller may
  * run them on two streams (each with its own ws) and start bsa_prepare_kv once the key side is
  * done.  proj_opt, if non-null, receives this side's projections in the same
  * [heads][2][levels][tokens] layout (the other side's rows are left 0).  Errors as
  * bsa_reblock_ex; a side other than 0 or 1 is BSA_E_ARG. */
 bsa_status bsa_reblock_side(const bsa_desc* desc, const void* q, const void* k, int32_t side,
-                            int32_t power_iters, int32_t* perm, float* proj_opt, void* ws,
-                            size_t ws_bytes, hipStream_t stream);
+                            int32_t power_iters, uint32_t tree_flags, int32_t* perm,
+                            float* proj_opt, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* (2) Select.  Block scores S[h][i][j] = s * mean(query block i) . mean(key block j) with
  * s = 1/sqrt(D); per row the K largest (ties to the lower j), written ascending to

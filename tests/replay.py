@@ -11,7 +11,7 @@ import oracle as O
 
 
 def replay_partition(U, perm, proj=None, tol=1e-5, leaf=64, max_level=None,
-                     iters=O.POWER_ITERS):
+                     iters=O.POWER_ITERS, shared_deep=False):
     """U: oracle unit vectors [N][D]; perm: GPU permutation; proj: GPU projections [L][N] by
     token id or None; max_level: replay only the first levels.  Returns a dict of statistics;
     raises AssertionError on a bad split."""
@@ -19,6 +19,9 @@ def replay_partition(U, perm, proj=None, tol=1e-5, leaf=64, max_level=None,
     nb = N // leaf
     L = O.tree_levels(nb)
     stats = {"splits": 0, "mismatched_splits": 0, "max_proj_err": 0.0, "min_gap": np.inf}
+    # Lite tree: below the root level every subtree keeps its root's projections
+    root = O.shared_root_level(nb) if shared_deep else L
+    key = np.zeros(N)
     groups = [(0, nb)]
     for lvl in range(L if max_level is None else min(L, max_level)):
         nxt = []
@@ -27,8 +30,10 @@ def replay_partition(U, perm, proj=None, tol=1e-5, leaf=64, max_level=None,
                 nxt.append((b0, m))
                 continue
             ids = np.sort(perm[b0 * leaf:(b0 + m) * leaf])
-            v = O.split_direction(U[ids], iters=iters)
-            p = U[ids] @ v
+            if lvl <= root:
+                v = O.split_direction(U[ids], iters=iters)
+                key[ids] = U[ids] @ v
+            p = key[ids]
             cut = (m // 2) * leaf
             left = set(perm[b0 * leaf:b0 * leaf + cut].tolist())
             is_left = np.array([i in left for i in ids])

@@ -23,7 +23,7 @@ def to_dev(x, dtype):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV).to(dtype)
 
 
-def _check_layouts(q, k, perm_q, perm_k, proj, tol_proj, iters=O.POWER_ITERS):
+def _check_layouts(q, k, perm_q, perm_k, proj, tol_proj, iters=O.POWER_ITERS, shared=False):
     """Replay both sides of every head; returns the summed statistics."""
     total = {"splits": 0, "mismatched_splits": 0, "max_proj_err": 0.0}
     for h in range(q.shape[0]):
@@ -33,7 +33,8 @@ def _check_layouts(q, k, perm_q, perm_k, proj, tol_proj, iters=O.POWER_ITERS):
             assert np.array_equal(np.sort(perm), np.arange(X.shape[0]))
             assert np.all(np.diff(perm.reshape(-1, 64), axis=1) > 0)
             st = replay_partition(O.metric_embed(X, Mo), perm,
-                                  None if proj is None else proj[h, side], iters=iters)
+                                  None if proj is None else proj[h, side], iters=iters,
+                                  shared_deep=shared)
             for key in ("splits", "mismatched_splits"):
                 total[key] += st[key]
             total["max_proj_err"] = max(total["max_proj_err"], st["max_proj_err"])
@@ -53,36 +54,42 @@ def mid():
     return (wl,) + synth.make_qkv(wl, heads=[0, 1])
 
 
-# power steps per split: the default and the Lite reblock's
-ITERS = [O.POWER_ITERS, ops.BSA_POWER_ITERS_LITE]
+# (power steps per split, one direction per small subtree): the default tree, fewer power
+# steps, and the Lite tree
+TREES = [(O.POWER_ITERS, False), (ops.BSA_POWER_ITERS_LITE, False),
+         (ops.BSA_POWER_ITERS_LITE, True)]
 
 
-@pytest.mark.parametrize("iters", ITERS)
-def test_reblock_f32_tiny(tiny, iters):
+@pytest.mark.parametrize("iters,shared", TREES)
+def test_reblock_f32_tiny(tiny, iters, shared):
     wl, q, k, v = tiny
     dt = torch.float32
-    pq, pk, proj = ops.reblock(to_dev(q, dt), to_dev(k, dt), with_proj=True, power_iters=iters)
+    pq, pk, proj = ops.reblock(to_dev(q, dt), to_dev(k, dt), with_proj=True, power_iters=iters,
+                               shared_deep=shared)
     pq, pk, proj = pq.cpu().numpy(), pk.cpu().numpy(), proj.cpu().numpy()
-    st = _check_layouts(q, k, pq, pk, proj, tol_proj=3e-5, iters=iters)
-    print("tiny replay", iters, st)
-    rq, rk, _, _ = O.reblock_head(q[0].astype(np.float64), k[0].astype(np.float64), iters=iters)
+    st = _check_layouts(q, k, pq, pk, proj, tol_proj=3e-5, iters=iters, shared=shared)
+    print("tiny replay", iters, shared, st)
+    rq, rk, _, _ = O.reblock_head(q[0].astype(np.float64), k[0].astype(np.float64), iters=iters,
+                                  shared_deep=shared)
     if st["mismatched_splits"] == 0:
         assert np.array_equal(pq[0], rq) and np.array_equal(pk[0], rk)
 
 
-@pytest.mark.parametrize("iters", ITERS)
-def test_reblock_bf16_mid(mid, iters):
+@pytest.mark.parametrize("iters,shared", TREES)
+def test_reblock_bf16_mid(mid, iters, shared):
     wl, q, k, v = mid
     dt = torch.bfloat16
-    pq, pk, proj = ops.reblock(to_dev(q, dt), to_dev(k, dt), with_proj=True, power_iters=iters)
+    pq, pk, proj = ops.reblock(to_dev(q, dt), to_dev(k, dt), with_proj=True, power_iters=iters,
+                               shared_deep=shared)
     pq, pk, proj = pq.cpu().numpy(), pk.cpu().numpy(), proj.cpu().numpy()
-    st = _check_layouts(q, k, pq, pk, proj, tol_proj=3e-5, iters=iters)
-    print("mid replay", iters, st)
+    st = _check_layouts(q, k, pq, pk, proj, tol_proj=3e-5, iters=iters, shared=shared)
+    print("mid replay", iters, shared, st)
     assert st["mismatched_splits"] <= 0.02 * st["splits"]
 
 
-@pytest.mark.parametrize("n_blocks,iters", [(600, 8), (1134, 8), (1134, 2)])
-def test_reblock_bf16_narrow_levels(n_blocks, iters):
+@pytest.mark.parametrize("n_blocks,iters,shared", [(600, 8, False), (1134, 8, False),
+                                                   (1134, 2, True)])
+def test_reblock_bf16_narrow_levels(n_blocks, iters, shared):
     """Enough blocks for the one-workgroup-per-parent levels (left-only statistics, right
     child from the parent's covariance) between the wide levels and the subtree kernel: every
     split of both sides replayed on the oracle."""
@@ -92,14 +99,14 @@ def test_reblock_bf16_narrow_levels(n_blocks, iters):
     sel = np.sort(rng.choice(wl.tokens, size=64 * n_blocks, replace=False))
     q, k = q[:, sel], k[:, sel]
     pq, pk, proj = ops.reblock(to_dev(q, torch.bfloat16), to_dev(k, torch.bfloat16),
-                               with_proj=True, power_iters=iters)
+                               with_proj=True, power_iters=iters, shared_deep=shared)
     # these levels derive each right child's statistics as n_P C_P - S_L in fp32; where a split
     # separates two children far apart relative to their spread, that subtraction amplifies
     # the fp32 rounding of C_P, so the GPU's projections sit a little further from the fp64
     # oracle's (split decisions are still held to the 1e-5 tie rule)
     st = _check_layouts(q, k, pq.cpu().numpy(), pk.cpu().numpy(), proj.cpu().numpy(),
-                        tol_proj=5e-5, iters=iters)
-    print("narrow replay", iters, st)
+                        tol_proj=5e-5, iters=iters, shared=shared)
+    print("narrow replay", iters, shared, st)
     assert st["mismatched_splits"] <= 0.02 * st["splits"]
 
 
@@ -211,10 +218,11 @@ def test_reblock_one_side_equals_both(which, tiny, mid):
     wl, q, k, v = tiny if which == "tiny" else mid
     dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
     qd, kd = to_dev(q, dt), to_dev(k, dt)
-    for iters in ITERS:
-        pq, pk, proj = ops.reblock(qd, kd, with_proj=True, power_iters=iters)
+    for iters, shared in TREES:
+        pq, pk, proj = ops.reblock(qd, kd, with_proj=True, power_iters=iters, shared_deep=shared)
         for side, ref in ((0, pq), (1, pk)):
-            perm, pr = ops.reblock_side(qd, kd, side, power_iters=iters, with_proj=True)
+            perm, pr = ops.reblock_side(qd, kd, side, power_iters=iters, with_proj=True,
+                                        shared_deep=shared)
             assert torch.equal(perm, ref), (side, iters)
             assert torch.equal(pr[:, side], proj[:, side])
             assert torch.all(pr[:, 1 - side] == 0).item()

@@ -154,17 +154,19 @@ def test_reblock_and_hook_argument_errors(L):
     assert L.bsa_reblock(desc(), FAKE, FAKE, FAKE, FAKE, None, FAKE, big, None) == _lib.BSA_E_ARG
     # one-sided reblock: side must be 0 or 1
     for side in (-1, 2):
-        assert L.bsa_reblock_side(desc(), FAKE, FAKE, side, 8, FAKE, None, FAKE, big,
+        assert L.bsa_reblock_side(desc(), FAKE, FAKE, side, 8, 0, FAKE, None, FAKE, big,
                                   None) == _lib.BSA_E_ARG
-    assert L.bsa_reblock_side(desc(), FAKE, FAKE, 0, 0, FAKE, None, FAKE, big,
+    assert L.bsa_reblock_side(desc(), FAKE, FAKE, 0, 0, 0, FAKE, None, FAKE, big,
                               None) == _lib.BSA_E_ARG
-    assert L.bsa_reblock_side(desc(), FAKE, FAKE, 1, 8, None, None, FAKE, big,
+    assert L.bsa_reblock_side(desc(), FAKE, FAKE, 0, 8, 2, FAKE, None, FAKE, big,
                               None) == _lib.BSA_E_ARG
-    assert L.bsa_reblock_side(desc(), FAKE, FAKE, 1, 8, FAKE, None, FAKE, 8,
+    assert L.bsa_reblock_side(desc(), FAKE, FAKE, 1, 8, 0, None, None, FAKE, big,
+                              None) == _lib.BSA_E_ARG
+    assert L.bsa_reblock_side(desc(), FAKE, FAKE, 1, 8, 1, FAKE, None, FAKE, 8,
                               None) == _lib.BSA_E_WORKSPACE
-    # power steps per split outside [1, 64]
-    for it in (0, -1, 65):
-        assert L.bsa_reblock_ex(desc(), FAKE, FAKE, 0, it, FAKE, FAKE2, None, FAKE, big,
+    # power steps per split outside [1, 64]; unknown tree flags
+    for it, fl in ((0, 0), (-1, 0), (65, 0), (8, 2), (2, 1 << 31)):
+        assert L.bsa_reblock_ex(desc(), FAKE, FAKE, 0, it, fl, FAKE, FAKE2, None, FAKE, big,
                                 None) == _lib.BSA_E_ARG
     # layout choice: unknown value, then the key-reuse layout, whose one buffer may serve both
     for bad in (-1, 2):
