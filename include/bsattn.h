@@ -16,7 +16,8 @@
  *                 [comfyui-wiki.com page, "What Spark-Attn changes" and its figure]
  *   (5) log-sum-exp merge of the two branches and the inverse permutation to token order.
  * Options on the same path: the key layout reused for the queries (bsa_reblock_layout), the
- * Lite tree (bsa_reblock_ex: power steps per split, one direction per small subtree), the block-level compressed branch (BSA_TAIL_BLOCK),
+ * Lite tree (bsa_reblock_ex: power steps per split, one direction per small subtree), either
+ * side's tree alone (bsa_reblock_side), the block-level compressed branch (BSA_TAIL_BLOCK),
  * and exact context tokens beside the video grid (bsa_sparse_attn_ctx).
  *
  * Conventions shared by every call
