@@ -14,8 +14,10 @@
 //
 // bf16 kernel layout (D = 128): one workgroup of 4 waves per (head, query block).  Every wave
 // keeps all 64 queries of the block in registers and takes every 4th tile of the work list
-// (exact tiles first, then summary tiles), so the waves run independent online softmaxes that
-// are merged at the end.  Scores are computed transposed, S^T = K Q^T, with
+// (exact tiles first, then summary tiles and context tiles), so the waves run independent
+// online softmaxes that are merged at the end.  Options: context query blocks (mixed
+// sequences) in the same launch, and a block-level compressed state computed beforehand
+// (k_tail_block_bf16) merged in place of the summary tiles.  Scores are computed transposed, S^T = K Q^T, with
 // v_mfma_f32_32x32x16_bf16: the accumulator layout of S^T is then directly the B operand of
 // O^T = V^T P^T.  K/V tiles arrive pre-swizzled (see summaries.hip) so that every wave load
 // is 1 KiB contiguous and no LDS transpose is needed.

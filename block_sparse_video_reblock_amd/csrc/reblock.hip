@@ -876,11 +876,10 @@ struct ProblemArgs {
   const int* lists;        // [L][G] active (m >= 2) nodes per level, ascending
   float* proj;             // optional [H][2][L][N]
   int level, G, slices;
-  // problems launched: p = p0 + pstep * (grid index); all 2H (0, 1), or the key sides only
-  // (1, 2) when the queries reuse the key layout
+  // problems launched: p = p0 + pstep * (grid index); all 2H (0, 1), the query sides only
+  // (0, 2) or the key sides only (1, 2)
   int p0, pstep;
   int iters;               // power steps per split
-  int shared_deep;         // Lite tree: below the subtree root, cut along the root's projections
 };
 
 BSA_DEV int problem_of(const ProblemArgs& a, int b) { return a.p0 + a.pstep * b; }
@@ -1667,7 +1666,6 @@ hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm
       reinterpret_cast<float*>(w + R.mom_partial), R.nch_mom, N, mside0, mom, msplit);
   ProblemArgs a{};
   a.iters = iters;
-  a.shared_deep = shared_deep ? 1 : 0;
   a.q = q;
   a.k = k;
   a.H = H;
