@@ -263,9 +263,12 @@ def main_headline(args, ops, synth, torch, np):
                     "passes": "moments, norms, and per tree level a statistics and a "
                               "projection pass over " + ("K" if sides == 1 else "Q and K")},
         "select": {"bytes": 2 * x_bytes + H * nb * nb * 4, "passes": "Q, K once; scores"},
-        "prepare": {"bytes": 3 * x_bytes + 2 * H * args.ctx * D * elt,
-                    "passes": "Q (anchor), K, V once" + (", context K, V once" if args.ctx
-                                                         else "")},
+        # the permutation: K and V written once more in block-contiguous (operand) order
+        "prepare": {"bytes": 5 * x_bytes + 4 * H * args.ctx * D * elt,
+                    "read_only_bytes": 3 * x_bytes + 2 * H * args.ctx * D * elt,
+                    "passes": "Q (anchor), K, V read once; K, V written once in key-block "
+                              "order (the permutation)" +
+                              (", context K, V read and written once" if args.ctx else "")},
     }
     for name, h in hbm.items():
         gbs = h["bytes"] / (stage_ms[name] * 1e-3) / 1e9
