@@ -227,6 +227,41 @@ def time_steps(torch, fns_per_step, steps, warmup):
     return ms_step, means, series
 
 
+def measure_machine(torch, np):
+    """Practical ceilings measured on this GPU in the same run: a large bf16 GEMM (the vendor
+    library's MFMA kernel) and a device-to-device copy, each the best of five."""
+    dev = torch.device("cuda:0")
+    n, kk = 8192, 16384
+    a = torch.randn(n, kk, device=dev).to(torch.bfloat16)
+    b = torch.randn(kk, n, device=dev).to(torch.bfloat16)
+    src = torch.empty(1 << 31, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    cur = torch.cuda.current_stream()
+
+    def best(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(cur)
+            fn()
+            e1.record(cur)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(min(ts))
+    gemm_ms = best(lambda: a @ b)
+    copy_ms = best(lambda: dst.copy_(src))
+    out = {"gemm_bf16_tflops": 2.0 * n * n * kk / (gemm_ms * 1e-3) / 1e12,
+           "gemm": f"torch.matmul bf16 {n}x{kk} @ {kk}x{n}",
+           "copy_gbs": 2.0 * src.numel() / (copy_ms * 1e-3) / 1e9,
+           "copy": "2 GiB device-to-device copy, read + write bytes"}
+    del a, b, src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
 def main_headline(args, ops, synth, torch, np):
     wl = synth.WORKLOADS[args.workload]
     H, N, D = wl.heads, wl.tokens, wl.head_dim
@@ -241,6 +276,7 @@ def main_headline(args, ops, synth, torch, np):
                 power_iters=ops.BSA_POWER_ITERS_LITE if args.lite else ops.BSA_POWER_ITERS,
                 lite_tree=args.lite)
     ms_step, stage_ms, series = time_steps(torch, lay.stages(), args.steps, args.warmup)
+    steps_ms = [sum(x) for x in zip(*series.values())]
     assert torch.isfinite(lay.out.float()).all().item(), "non-finite output"
     log(f"[bench] layer {ms_step:.3f} ms/step; stages " +
         ", ".join(f"{k} {v:.3f}" for k, v in stage_ms.items()))
@@ -273,6 +309,13 @@ def main_headline(args, ops, synth, torch, np):
     for name, h in hbm.items():
         gbs = h["bytes"] / (stage_ms[name] * 1e-3) / 1e9
         h.update({"ms": stage_ms[name], "GB/s": gbs, "frac": gbs / HBM_PEAK_GBS})
+
+    machine = measure_machine(torch, np)
+    log(f"[bench] machine: bf16 GEMM {machine['gemm_bf16_tflops']:.0f} TFLOP/s, copy "
+        f"{machine['copy_gbs']:.0f} GB/s")
+    roof = achieved / machine["gemm_bf16_tflops"]
+    for h in hbm.values():
+        h["frac_of_copy"] = h["GB/s"] / machine["copy_gbs"]
 
     dense = None
     if not args.no_dense and not args.ctx:
@@ -331,8 +374,13 @@ def main_headline(args, ops, synth, torch, np):
                      "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                      "traffic": ATTN_TRAFFIC_BYTES.get(wl.name), "kernel": "k_attn_bf16",
                      "launch_ms": attn_ms, "launch_ms_min": float(min(series["attend"])),
+                     "frac_of_gemm": roof,
                      "flops_per_launch": exact_f + comp_f},
         "stages_ms": stage_ms,
+        "step_ms_median": float(np.median(steps_ms)),
+        "step_ms_min": float(min(steps_ms)),
+        "step_ms_max": float(max(steps_ms)),
+        "machine": machine,
         "hbm": hbm,
         "dense": dense,
         "cpu_baseline": cpu,
