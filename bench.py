@@ -310,12 +310,14 @@ def main_headline(args, ops, synth, torch, np):
         gbs = h["bytes"] / (stage_ms[name] * 1e-3) / 1e9
         h.update({"ms": stage_ms[name], "GB/s": gbs, "frac": gbs / HBM_PEAK_GBS})
 
-    machine = measure_machine(torch, np)
-    log(f"[bench] machine: bf16 GEMM {machine['gemm_bf16_tflops']:.0f} TFLOP/s, copy "
-        f"{machine['copy_gbs']:.0f} GB/s")
-    roof = achieved / machine["gemm_bf16_tflops"]
-    for h in hbm.values():
-        h["frac_of_copy"] = h["GB/s"] / machine["copy_gbs"]
+    machine = roof = None
+    if not args.no_machine:
+        machine = measure_machine(torch, np)
+        log(f"[bench] machine: bf16 GEMM {machine['gemm_bf16_tflops']:.0f} TFLOP/s, copy "
+            f"{machine['copy_gbs']:.0f} GB/s")
+        roof = achieved / machine["gemm_bf16_tflops"]
+        for h in hbm.values():
+            h["frac_of_copy"] = h["GB/s"] / machine["copy_gbs"]
 
     dense = None
     if not args.no_dense and not args.ctx:
@@ -512,6 +514,8 @@ def main():
                     help="Lite reblock: 2 power steps per split and one direction per subtree "
                          "of at most 8 blocks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-machine", action="store_true",
+                    help="skip the GEMM and copy ceilings measured beside the headline")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run three device-to-device copies of MIB MiB (a plain copy kernel "
