@@ -378,6 +378,25 @@ def test_mixed_sequence_without_context_is_the_plain_layer(mid):
     assert torch.equal(o, ops.sparse_attn(*args, *perms))
 
 
+def test_option_paths_are_deterministic(mid):
+    """Two runs of each option path give bitwise-identical results: the Lite tree, the
+    block-level tail, and a mixed sequence (both outputs)."""
+    wl, q, k, v, pq, pk, lists = mid
+    dt = torch.bfloat16
+    qd, kd, vd = to_dev(q, dt), to_dev(k, dt), to_dev(v, dt)
+    perms = (torch.from_numpy(pq).to(DEV), torch.from_numpy(pk).to(DEV),
+             torch.from_numpy(lists).to(DEV))
+    for run in (lambda: ops.reblock(qd, kd, power_iters=ops.BSA_POWER_ITERS_LITE,
+                                    shared_deep=True),
+                lambda: (ops.sparse_attn(qd, kd, vd, *perms, flags=ops.BSA_TAIL_BLOCK),)):
+        a, b = run(), run()
+        assert all(torch.equal(x, y) for x, y in zip(a, b))
+    qc, kc, vc = (to_dev(x, dt) for x in synth.make_ctx(wl, 300, (q, k, v), heads=[0, 1]))
+    a = ops.sparse_attn_ctx(qd, kd, vd, qc, kc, vc, *perms)
+    b = ops.sparse_attn_ctx(qd, kd, vd, qc, kc, vc, *perms)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
 def test_attention_is_deterministic(mid):
     wl, q, k, v, pq, pk, lists = mid
     dt = torch.bfloat16
