@@ -14,12 +14,17 @@ Default (the headline): 24 heads x 72,576 tokens x 128, bf16, 10 % density.
              softmax attention), timed on the same GPU
   cpu_baseline  the CPU oracle (fp64 numpy) on one head of the same workload, extrapolated to
              all heads
+  machine    practical ceilings measured beside it: a vendor bf16 GEMM and a device copy
+Options on the headline (same JSON line, recorded in config): --layout q_reuse_k (queries reuse
+the key layout), --tail block (block-level compressed branch), --ctx N (N exact context tokens
+beside the video grid), --lite (the Lite reblock).
 Other modes (each prints its own JSON line):
   --workload clip14s_bf16   four independently generated 103,680-token layers back to back,
                             reblock recomputed per layer; value per layer
   --sweep                   the 16,384-token shape at densities 0.1 / 0.2 / 0.3 / 1.0, with
-                            Reblock layouts and with the fixed-tile baseline (positional 4x4x4
-                            cubes, mean-pooled summaries); layer time and attention-mass recall
+                            Reblock layouts (default, 2 power steps, Lite, key layout reused)
+                            and with the fixed-tile baseline (positional 4x4x4 cubes,
+                            mean-pooled summaries); layer time and attention-mass recall
                             against dense softmax, both measured on the GPU
 """
 from __future__ import annotations
