@@ -154,32 +154,6 @@ BSA_DEV void block_partition(const float* keys, const int32_t* in, int32_t* out,
   }
 }
 
-
-// Exclusive scan of one int per thread over an NT-thread workgroup (NT/64 ints of LDS in sm).
-template <int NT>
-BSA_DEV int block_excl_scan_n(int v, int* sm, int* total) {
-  constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
-  }
-  __syncthreads();
-  if (lane == 63) sm[wave] = incl;
-  __syncthreads();
-  int before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const int s = sm[w];
-    before += (w < wave) ? s : 0;
-    all += s;
-  }
-  *total = all;
-  return before + incl - v;
-}
-
 // ---------------------------------------------------------------------------------------
 // Wave-parallel variants for any workgroup size NT (a multiple of 64).
 
@@ -296,43 +270,6 @@ BSA_DEV void partition_w(const float* keys, const int32_t* in, int32_t* out, int
     left_run += __popcll(lm);
     eq_seen += __popcll(eqm);
   }
-  __syncthreads();
-}
-
-// Small groups (n <= 2 * NT), everything in LDS: rank each element against all others, then a
-// stable scatter.  keys, pos, tmp: LDS arrays of n.  sm: NT/64 ints.  On exit pos holds the
-// partitioned order.
-template <int NT>
-BSA_DEV void small_split(const float* keys, int32_t* pos, int32_t* tmp, int n, int want,
-                         int* sm) {
-  const int tid = threadIdx.x;
-  bool left[2] = {false, false};
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int i = tid + u * NT;
-    if (i < n) {
-      const uint32_t ki = orderable_key(keys[i]);
-      int rank = 0;
-      for (int j = 0; j < n; ++j) {
-        const uint32_t kj = orderable_key(keys[j]);
-        rank += (kj < ki) || (kj == ki && j < i);
-      }
-      left[u] = rank < want;
-    }
-  }
-  int tot0, tot1;
-  const int ex0 = block_excl_scan_n<NT>(left[0] ? 1 : 0, sm, &tot0);
-  const int ex1 = block_excl_scan_n<NT>(left[1] ? 1 : 0, sm, &tot1) + tot0;
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int i = tid + u * NT;
-    if (i < n) {
-      const int lb = u == 0 ? ex0 : ex1;
-      tmp[left[u] ? lb : want + (i - lb)] = pos[i];
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < n; i += NT) pos[i] = tmp[i];
   __syncthreads();
 }
 
