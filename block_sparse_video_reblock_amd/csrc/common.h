@@ -82,11 +82,6 @@ BSA_DEV float wave_total(float x) {
   x = row16_sum(x);
   return (lane_value(x, 0) + lane_value(x, 16)) + (lane_value(x, 32) + lane_value(x, 48));
 }
-BSA_DEV int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
 
 // Monotone map float -> uint32 (a < b  <=>  key(a) < key(b)); -0.0 maps like +0.0.
 BSA_DEV uint32_t orderable_key(float f) {
