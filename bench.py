@@ -42,7 +42,7 @@ HBM_PEAK_GBS = 8000.0
 # Bytes one attention launch moves between L2 and memory on the headline workload: rocprofv3
 # FETCH_SIZE x 2 + WRITE_SIZE x 1 (the factors a plain 1 GiB copy gives those counters), taken
 # on the current attention kernel; to be retaken whenever that kernel changes.
-ATTN_TRAFFIC_BYTES = {"clip10s_bf16": 5.86e10}
+ATTN_TRAFFIC_BYTES = {"clip10s_bf16": 4.99e10}
 
 
 def log(*a):

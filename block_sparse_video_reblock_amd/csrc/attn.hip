@@ -137,6 +137,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(QSide cs, QSide vs, int wg
   const int ntiles = ks.nt_s, nb = ks.nb;
   const int n_exact = S.n_exact, n_comp = S.n_comp, tau0 = S.tau0, topk = S.topk;
   const bool listed = !CTX || S.listed;
+  // Sparse lists (at most half of the key blocks) are walked from a rotated start: the 64
+  // workgroups that run together on an XCD begin at 64 evenly spaced points of their lists.
+  // (With every block selected the lists coincide and an unrotated walk shares each tile in L2
+  // across those workgroups, so full lists are not rotated.)  The order changes only the
+  // rounding of the sums.
+  const int rot = (!is_ctx && 2 * n_exact <= nb)
+                      ? (((blockIdx.x - wg_c) >> 3) & 63) * n_exact / 64
+                      : 0;
   const int32_t* list = listed ? lists + ((size_t)h * S.nbq + i) * topk : nullptr;
 
   // bitmap of this query block's selected key blocks (masks them in the compressed branch);
@@ -199,7 +207,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(QSide cs, QSide vs, int wg
     if (it >= it_end) return;
     auto tile_ptrs = [&](int t, const uint4*& kp, const uint4*& vp, int& k0) {
       if (EXACT) {
-        const size_t blk = (size_t)h * nb + (listed ? load_uniform(list + t) : t);
+        const int tr = t + rot < n_exact ? t + rot : t + rot - n_exact;
+        const size_t blk = (size_t)h * nb + (listed ? load_uniform(list + tr) : tr);
         kp = ks.ksw + blk * 1024;
         vp = ks.vsw + blk * 1024;
         k0 = 0;
