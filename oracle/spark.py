@@ -12,7 +12,8 @@ import math
 import numpy as np
 
 __all__ = [
-    "LEAF", "POWER_ITERS", "SMALL_BLOCKS", "shared_root_level", "second_moment", "metric_factor", "metric_embed", "tree_levels",
+    "LEAF", "POWER_ITERS", "LITE_SUBTREE_BLOCKS", "shared_root_level", "second_moment",
+    "metric_factor", "metric_embed", "tree_levels",
     "split_direction", "partition", "partition_from_projections", "reblock_head",
     "topk_count", "block_means", "block_scores", "topk_lists", "summaries",
     "sparse_attention_head", "mixed_attention_head", "dense_attention_head", "recall_head",
@@ -110,20 +111,24 @@ def _split_by_rank(ids: np.ndarray, p32: np.ndarray, n_left: int):
     return np.sort(ids[order[:n_left]]), np.sort(ids[order[n_left:]])
 
 
-SMALL_BLOCKS = 8
+# Subtree size of the Lite preset (in blocks).  The pages give no number for it: 8 is a chosen
+# value of this reading, a parameter of the tree, not a fact of the method.
+LITE_SUBTREE_BLOCKS = 8
 
 
-def shared_root_level(n_blocks: int) -> int:
-    """The first tree level whose groups all hold at most SMALL_BLOCKS blocks (the largest
+def shared_root_level(n_blocks: int, subtree_blocks: int = LITE_SUBTREE_BLOCKS) -> int:
+    """The first tree level whose groups all hold at most `subtree_blocks` blocks (the largest
     group of level l holds ceil(nb / 2^l) blocks)."""
+    if subtree_blocks < 1:
+        raise ValueError("subtree_blocks must be >= 1")
     lvl = 0
-    while -(-n_blocks // (1 << lvl)) > SMALL_BLOCKS:
+    while -(-n_blocks // (1 << lvl)) > subtree_blocks:
         lvl += 1
     return lvl
 
 
 def partition(U: np.ndarray, leaf: int = LEAF, iters: int = POWER_ITERS,
-              shared_deep: bool = False):
+              shared_deep: bool = False, subtree_blocks: int = LITE_SUBTREE_BLOCKS):
     """Capacity-constrained hierarchical tree partition into exactly-`leaf`-token leaves.
 
     [P2] "What it's doing under the hood": a capacity-constrained tree partition down to
@@ -133,8 +138,8 @@ def partition(U: np.ndarray, leaf: int = LEAF, iters: int = POWER_ITERS,
     recursion left first; leaves in that depth-first order; ascending token id inside a leaf.
 
     shared_deep (the Lite tree; [P1] "Benchmarks" names a lighter Spark-H3-Lite without its
-    mechanism): from the first level whose groups hold at most SMALL_BLOCKS blocks, each group
-    takes one direction and its descendants split along the same projections (no new
+    mechanism): from the first level whose groups hold at most `subtree_blocks` blocks, each
+    group takes one direction and its descendants split along the same projections (no new
     direction), so that subtree is its tokens in (p, token id) order cut into leaves.
 
     Returns (perm, proj): perm[p] = token id at position p; proj[l][i] = the fp32 projection
@@ -144,7 +149,7 @@ def partition(U: np.ndarray, leaf: int = LEAF, iters: int = POWER_ITERS,
         raise ValueError("token count must be a multiple of the leaf size")
     nb = N // leaf
     L = tree_levels(nb)
-    root = shared_root_level(nb) if shared_deep else L
+    root = shared_root_level(nb, subtree_blocks) if shared_deep else L
     proj = np.zeros((L, N), dtype=np.float32)
     key = np.zeros(N, dtype=np.float32)   # the projections a shared subtree keeps using
     groups = [np.arange(N)]
@@ -185,7 +190,8 @@ def partition_from_projections(proj: np.ndarray, n_tokens: int, leaf: int = LEAF
 
 
 def reblock_head(Q: np.ndarray, K: np.ndarray, leaf: int = LEAF, iters: int = POWER_ITERS,
-                 kind: str = "eigh", layout: str = "separate", shared_deep: bool = False):
+                 kind: str = "eigh", layout: str = "separate", shared_deep: bool = False,
+                 subtree_blocks: int = LITE_SUBTREE_BLOCKS):
     """Query layout from M_K, key layout from M_Q, each partitioned on its own ([P2]).
     Returns (perm_q, perm_k, proj_q, proj_k).  Q/K/V values are untouched.
 
@@ -195,11 +201,13 @@ def reblock_head(Q: np.ndarray, K: np.ndarray, leaf: int = LEAF, iters: int = PO
     if layout not in ("separate", "q_reuse_k"):
         raise ValueError(f"unknown layout {layout!r}")
     M_q = second_moment(Q)
-    perm_k, proj_k = partition(metric_embed(K, M_q, kind), leaf, iters, shared_deep)
+    perm_k, proj_k = partition(metric_embed(K, M_q, kind), leaf, iters, shared_deep,
+                               subtree_blocks)
     if layout == "q_reuse_k":
         return perm_k.copy(), perm_k, None, proj_k
     M_k = second_moment(K)
-    perm_q, proj_q = partition(metric_embed(Q, M_k, kind), leaf, iters, shared_deep)
+    perm_q, proj_q = partition(metric_embed(Q, M_k, kind), leaf, iters, shared_deep,
+                               subtree_blocks)
     return perm_q, perm_k, proj_q, proj_k
 
 

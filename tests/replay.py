@@ -11,7 +11,8 @@ import oracle as O
 
 
 def replay_partition(U, perm, proj=None, tol=1e-5, leaf=64, max_level=None,
-                     iters=O.POWER_ITERS, shared_deep=False):
+                     iters=O.POWER_ITERS, shared_deep=False,
+                     subtree_blocks=O.LITE_SUBTREE_BLOCKS):
     """U: oracle unit vectors [N][D]; perm: GPU permutation; proj: GPU projections [L][N] by
     token id or None; max_level: replay only the first levels.  Returns a dict of statistics;
     raises AssertionError on a bad split."""
@@ -20,7 +21,7 @@ def replay_partition(U, perm, proj=None, tol=1e-5, leaf=64, max_level=None,
     L = O.tree_levels(nb)
     stats = {"splits": 0, "mismatched_splits": 0, "max_proj_err": 0.0, "min_gap": np.inf}
     # Lite tree: below the root level every subtree keeps its root's projections
-    root = O.shared_root_level(nb) if shared_deep else L
+    root = O.shared_root_level(nb, subtree_blocks) if shared_deep else L
     key = np.zeros(N)
     groups = [(0, nb)]
     for lvl in range(L if max_level is None else min(L, max_level)):

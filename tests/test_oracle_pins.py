@@ -258,19 +258,23 @@ def _groups_at(nb, level):
     return groups
 
 
-def test_lite_tree_cuts_each_small_subtree_along_one_direction(tiny_inputs):
-    """Lite tree (shared_deep): above the first level whose groups hold at most 8 blocks it is
-    the default tree; each group of that level is its tokens sorted by (fp32 projection on the
-    group's own direction, token id), cut into consecutive 64-token leaves, each leaf in
-    ascending token id.  Checked by an explicit sort per subtree on 64 blocks (root level 3)
-    and 8 blocks (one subtree, root level 0)."""
+@pytest.mark.parametrize("subtree_blocks", [2, 4, 8, 32])
+def test_lite_tree_cuts_each_small_subtree_along_one_direction(tiny_inputs, subtree_blocks):
+    """Lite tree (shared_deep): above the first level whose groups hold at most
+    `subtree_blocks` blocks it is the default tree; each group of that level is its tokens
+    sorted by (fp32 projection on the group's own direction, token id), cut into consecutive
+    64-token leaves, each leaf in ascending token id.  The subtree size is a parameter of the
+    reading (the pages give none); every size is checked by an explicit sort per subtree on
+    64 blocks and on 8 blocks."""
     wl, Q, K, V = tiny_inputs
     U = O.metric_embed(Q, O.second_moment(K))
     for n_tok in (U.shape[0], 512):
         Ux = U[:n_tok]
         nb = n_tok // 64
-        root = O.shared_root_level(nb)
-        perm_l, proj_l = O.partition(Ux, shared_deep=True)
+        root = O.shared_root_level(nb, subtree_blocks)
+        assert max(m for _, m in _groups_at(nb, root)) <= subtree_blocks
+        assert root == 0 or max(m for _, m in _groups_at(nb, root - 1)) > subtree_blocks
+        perm_l, proj_l = O.partition(Ux, shared_deep=True, subtree_blocks=subtree_blocks)
         perm_d, proj_d = O.partition(Ux)
         assert np.array_equal(proj_l[:root + 1], proj_d[:root + 1])
         for b0, m in _groups_at(nb, root):
@@ -282,18 +286,23 @@ def test_lite_tree_cuts_each_small_subtree_along_one_direction(tiny_inputs):
             ranked = ids[np.lexsort((ids, p))]
             ref = np.concatenate([np.sort(ranked[64 * j:64 * j + 64]) for j in range(m)])
             assert np.array_equal(seg, ref), (nb, b0, m)
-        if nb > 8:
+        # a subtree of 2 blocks has only the one split, so the Lite tree is then the default
+        if 2 < subtree_blocks < nb:
             assert not np.array_equal(perm_l, perm_d)
+        if subtree_blocks <= 2:
+            assert np.array_equal(perm_l, perm_d)
     assert [O.shared_root_level(nb) for nb in (1, 8, 9, 256, 1134, 8192)] == [0, 0, 1, 5, 8, 10]
+    assert [O.shared_root_level(1134, b) for b in (1, 2, 4, 18, 32, 1134)] == \
+        [11, 10, 9, 6, 6, 0]
 
 
-def _naive_tree(X, M, leaf):
-    """Independent partitioner: explicit Mahalanobis-cosine Gram matrix, principal direction
-    from numpy.linalg.eigh of the centred Gram (kernel PCA), full stable sort."""
-    G = X @ M @ X.T
+def _naive_tree(G, leaf):
+    """Independent partitioner: from the Gram matrix G of the tokens' score patterns, the
+    cosine matrix, the principal direction from numpy.linalg.eigh of the centred cosine
+    matrix (kernel PCA), and a full stable sort."""
     d = np.sqrt(np.diag(G))
     Cos = G / np.outer(d, d)
-    out = [np.arange(X.shape[0])]
+    out = [np.arange(G.shape[0])]
     while any(g.size > leaf for g in out):
         nxt = []
         for ids in out:
@@ -304,7 +313,7 @@ def _naive_tree(X, M, leaf):
             n = ids.size
             H = np.eye(n) - 1.0 / n
             Kc = H @ Cos[np.ix_(ids, ids)] @ H
-            lam, E = np.linalg.eigh(Kc)
+            _, E = np.linalg.eigh(Kc)
             e = E[:, -1]
             i0 = np.flatnonzero(np.diag(Kc) > 1e-14)[0]
             if e[i0] < 0:
@@ -317,11 +326,17 @@ def _naive_tree(X, M, leaf):
 
 
 def test_partition_matches_kernel_pca_partitioner(tiny_inputs):
+    """The oracle's query tree against a kernel-PCA partitioner that never forms a second
+    moment: its similarity is the cosine of two queries' raw score rows over all keys ([P1]:
+    queries with alike score patterns belong together), which is what the metric M_K = E[k k^T]
+    of [P2] stands for.  The keys get a large common offset, which a centred moment would
+    discard."""
     wl, Q, K, V = tiny_inputs
     Qs, Ks = Q[:1216], K[:1216]     # 1,216 tokens: 19 leaves, so odd groups occur
-    Mk = O.second_moment(Ks)
-    perm, _ = O.partition(O.metric_embed(Qs, Mk), 64, iters=300)
-    assert np.array_equal(perm, _naive_tree(Qs, Mk, 64))
+    Ks = Ks + 2.0 * Ks.std() * np.random.default_rng(8).standard_normal(Ks.shape[1])
+    perm, _ = O.partition(O.metric_embed(Qs, O.second_moment(Ks)), 64, iters=300)
+    S = Qs @ Ks.T
+    assert np.array_equal(perm, _naive_tree(S @ S.T, 64))
 
 
 def _planted():
@@ -348,11 +363,12 @@ def _planted():
     return Q, K, Mk, label
 
 
-def _brute_force_leaves(Q, M, leaf=4):
-    G = Q @ M @ Q.T
+def _brute_force_leaves(G, leaf=4):
+    """Exhaustive minimiser of the total intra-leaf cosine distance 1 - G_ab / sqrt(G_aa G_bb)
+    over all partitions into leaves of `leaf` tokens."""
     d = np.sqrt(np.diag(G))
     dist = 1 - G / np.outer(d, d)
-    n = Q.shape[0]
+    n = G.shape[0]
     best, arg = np.inf, None
 
     def parts(rest):
@@ -376,15 +392,131 @@ def _brute_force_leaves(Q, M, leaf=4):
 def test_partition_matches_brute_force_on_planted_clusters():
     Q, K, Mk, label = _planted()
     planted = sorted(tuple(np.flatnonzero(label == c)) for c in range(3))
-    assert _brute_force_leaves(Q, Mk) == planted
+    S = Q @ K.T                      # raw score patterns over the keys
+    assert _brute_force_leaves(S @ S.T) == planted
     # the test is sensitive to the metric: plain cosine and the inverse metric disagree
-    assert _brute_force_leaves(Q, np.eye(4)) != planted
-    assert _brute_force_leaves(Q, np.linalg.inv(Mk)) != planted
+    assert _brute_force_leaves(Q @ Q.T) != planted
+    assert _brute_force_leaves(Q @ np.linalg.inv(Mk) @ Q.T) != planted
     perm_q = O.reblock_head(Q, K, leaf=4)[0]
     assert sorted(tuple(sorted(g)) for g in perm_q.reshape(-1, 4)) == planted
     # the Lite power-step count still finds well-separated clusters
     perm_lite = O.reblock_head(Q, K, leaf=4, iters=2)[0]
     assert sorted(tuple(sorted(g)) for g in perm_lite.reshape(-1, 4)) == planted
+
+
+def test_metric_is_the_cosine_of_raw_score_patterns():
+    """[P1] "What Spark-Attn changes": queries are alike when their attention score patterns
+    over the keys are alike; [P2] "What it's doing under the hood": the metric is
+    M_K = E[k k^T], uncentred.  So the Gram matrix of the oracle's unit vectors must be the
+    cosine matrix of the raw score rows (q . k_j)_j, for queries and, symmetrically, for keys.
+    Both sides get a large common offset: a centred moment would give the cosines of
+    mean-removed score rows instead, which differ."""
+    rng = np.random.default_rng(31)
+    Q = rng.standard_normal((96, 8)) + 3.0 * rng.standard_normal(8)
+    K = rng.standard_normal((160, 8)) * np.linspace(0.2, 2.0, 8) + 4.0 * rng.standard_normal(8)
+
+    def cos_rows(S):
+        Sn = S / np.linalg.norm(S, axis=1, keepdims=True)
+        return Sn @ Sn.T
+
+    Uq = O.metric_embed(Q, O.second_moment(K))
+    Uk = O.metric_embed(K, O.second_moment(Q))
+    assert np.max(np.abs(Uq @ Uq.T - cos_rows(Q @ K.T))) < 1e-12
+    assert np.max(np.abs(Uk @ Uk.T - cos_rows(K @ Q.T))) < 1e-12
+    Sc = Q @ K.T
+    Sc = Sc - Sc.mean(axis=1, keepdims=True)
+    assert np.max(np.abs(cos_rows(Sc) - cos_rows(Q @ K.T))) > 0.1
+
+
+def _planted_offset():
+    """12 queries in 3 clusters of 4 that the raw score patterns separate but mean-removed ones
+    do not.  The keys have a large common offset along e3 and little spread there, so a
+    query's e3 component moves all its scores together: the raw pattern sees it, the centred
+    one does not.  Clusters A (e3 > 0) and B (e3 < 0) each hold two queries at angle 0 and two
+    at 40 degrees in the e1-e2 plane; C sits at 120 degrees with e3 = 0."""
+    rng = np.random.default_rng(4)
+    K = rng.standard_normal((400, 3)) * np.array([1.0, 1.0, 0.05]) + np.array([0.0, 0.0, 3.0])
+    spec = [(0, 1), (0, 1), (40, 1), (40, 1), (0, -1), (0, -1), (40, -1), (40, -1),
+            (120, 0), (120, 0), (120, 0), (120, 0)]
+    Q, label = [], []
+    for phi, z in spec:
+        a = math.radians(phi + rng.normal(0.0, 1.0))
+        r = rng.uniform(0.5, 1.0)
+        Q.append([r * math.cos(a), r * math.sin(a), z * rng.uniform(2.0, 2.5) +
+                  rng.normal(0.0, 0.01)])
+        label.append({1: 0, -1: 1, 0: 2}[z])
+    perm = rng.permutation(12)
+    return np.array(Q)[perm], K, np.array(label)[perm]
+
+
+def test_partition_uses_the_uncentred_moment():
+    """Brute force over all 5,775 partitions of 12 tokens into leaves of 4: the minimiser of
+    the raw-score-pattern cosine distance is the planted A/B/C grouping, the minimiser for
+    mean-removed score rows (what a centred moment measures) is not, and the oracle's tree
+    finds the former."""
+    Q, K, label = _planted_offset()
+    planted = sorted(tuple(np.flatnonzero(label == c)) for c in range(3))
+    S = Q @ K.T
+    assert _brute_force_leaves(S @ S.T) == planted
+    Sc = S - S.mean(axis=1, keepdims=True)
+    assert _brute_force_leaves(Sc @ Sc.T) != planted
+    perm_q = O.reblock_head(Q, K, leaf=4)[0]
+    assert sorted(tuple(sorted(g)) for g in perm_q.reshape(-1, 4)) == planted
+
+
+def _softplus(x):
+    return math.log1p(math.exp(x))
+
+
+def test_log_mass_error_closed_form():
+    """A worked example with leaf 2, head_dim 1 and scale 1.  Key block 1 holds the keys 0 and
+    c, so a query q's true log-mass over it is f(q) = log(1 + e^(q c)).  Every query selects
+    key block 0 only, so block 1 is the unselected block of all four queries.
+      Reweight: the anchor is the mean query qa; the summary key is f'(qa) = c sigmoid(qa c)
+      and the bias b = f(qa) - qa f'(qa), so the estimate is the tangent line of f at qa and the
+      error f(q) - f(qa) - f'(qa) (q - qa).
+      Mean pooling: the estimate is q c / 2 + ln 2, and the error f(q) - q c / 2 - ln 2 =
+      log cosh(q c / 2).
+    f is convex, so both errors are >= 0 and the absolute error equals the signed one."""
+    c = 2.0
+    q = np.array([1.5, 0.5, 2.0, 0.0])
+    Q = q[:, None]
+    K = np.array([[-0.7], [0.3], [0.0], [c]])
+    V = np.array([[1.0], [2.0], [3.0], [4.0]])
+    ident = np.arange(4)
+    lists = np.array([[0], [0]])
+    qa = q.mean()
+    sig = 1.0 / (1.0 + math.exp(-qa * c))
+    rw = np.mean([_softplus(x * c) - _softplus(qa * c) - c * sig * (x - qa) for x in q])
+    mp = np.mean([math.log(math.cosh(x * c / 2)) for x in q])
+    got_rw = O.log_mass_error_head(Q, K, V, ident, ident, lists, scale=1.0, leaf=2)
+    got_mp = O.log_mass_error_head(Q, K, V, ident, ident, lists, scale=1.0, leaf=2,
+                                   mode="meanpool")
+    assert abs(got_rw - rw) < 1e-14 and abs(got_mp - mp) < 1e-14
+    assert 0.0 < got_rw < got_mp
+    # the same means worked by hand (c = 2, qa = 1, f(1) = 2.126928, f'(1) = 1.761594;
+    # per-query errors 0.040862, 0.067131, 0.129628, 0.327813 and log cosh 0.855459,
+    # 0.120115, 1.325003, 0)
+    assert abs(rw - 0.141359) < 2e-6 and abs(mp - 0.575144) < 1e-5
+
+
+def test_log_mass_error_zero_at_the_anchor(tiny_inputs):
+    """If every query is the anchor, the Reweight estimate is each block's exact log-mass, so
+    the error is 0 at any budget; mean pooling's error is then the mean Jensen gap
+    log(mean_t e^(x_t)) - mean_t x_t of the anchor logits x_t over each unselected block."""
+    wl, Q, K, V = tiny_inputs
+    N, nb = wl.tokens, wl.n_blocks
+    rng = np.random.default_rng(9)
+    Qa = np.tile(Q[200], (N, 1))
+    pq, pk = rng.permutation(N), rng.permutation(N)
+    lists = np.sort(np.stack([rng.choice(nb, 7, replace=False) for _ in range(nb)]), axis=1)
+    assert O.log_mass_error_head(Qa, K, V, pq, pk, lists) < 1e-12
+    s = 1.0 / math.sqrt(Q.shape[1])
+    x = s * K[pk].reshape(nb, 64, -1) @ Q[200]
+    gap = np.log(np.exp(x).mean(axis=1)) - x.mean(axis=1)
+    ref = np.mean([gap[np.setdiff1d(np.arange(nb), lists[i])].mean() for i in range(nb)])
+    got = O.log_mass_error_head(Qa, K, V, pq, pk, lists, mode="meanpool")
+    assert abs(got - ref) < 1e-12
 
 
 def test_power_steps_raise_the_rayleigh_quotient(tiny_inputs):
