@@ -5,8 +5,9 @@
 // [comfyui-wiki.com "Spark-H3 ...", "What Spark-Attn changes"]: an exact branch fully computes
 // the top-ranked key/value blocks while a compressed branch covers the rest; Spark-Reweight
 // replaces mean-pooled summaries by weighted summaries plus a log-mass bias.
-// [comfy.icu "MiniMax H3 Spark Attention (SM89)", "What it's doing under the hood"]: the
-// approximate branch keeps a real Q per query and downsamples only K/V.
+// [comfy.icu "MiniMax H3 Spark Attention (SM89)", "What it's doing under the hood"]: in the
+// compressed branch each query still uses its own query vector; only the key/value side is
+// pooled per block.
 //
 // Both branches are softmax attentions of the same 64 queries, so a single online softmax over
 // the exact key tiles followed by the summary tiles (selected blocks masked to -inf) is the

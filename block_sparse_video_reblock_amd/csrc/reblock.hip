@@ -3,8 +3,8 @@
 //
 // [comfy.icu "MiniMax H3 Spark Attention (SM89)", "What it's doing under the hood"]: queries are
 // compared through M_K = E[k k^T] and keys through M_Q = E[q q^T] (a Mahalanobis cosine); a
-// capacity-constrained tree partition splits them into exactly-64-token leaves, recomputed per
-// layer, step and head; Q/K/V are never modified, only the permutation.
+// tree partition under a capacity limit cuts them into leaves of 64 tokens each, rebuilt for
+// every layer, step and head; the result is a permutation, and the tensors keep their values.
 // [comfyui-wiki.com "Spark-H3 ...", "What Spark-Attn changes"]: two queries are alike when their
 // attention score patterns over the keys are alike; the partitioner splits until every leaf has
 // the block size, in O(N log N).

@@ -1,8 +1,8 @@
 // Capacity-constrained tree bookkeeping shared by the reblock kernels: group geometry,
 // workgroup scans, the radix select of a split threshold and the stable two-way partition.
 //
-// [comfy.icu "MiniMax H3 Spark Attention (SM89)", "What it's doing under the hood"]: a
-// capacity-constrained tree partition down to exactly 64-token leaves.  Reading used here: a
+// [comfy.icu "MiniMax H3 Spark Attention (SM89)", "What it's doing under the hood"]: the tokens
+// are split by a tree whose leaves each hold 64 tokens (a capacity limit).  Reading used here: a
 // group of m blocks (m >= 2) sends the floor(m/2)*64 tokens of smallest (projection, token id)
 // to its left child, the rest to the right; children are laid out left first, so every group
 // of every level occupies one contiguous position range and the final leaf order is

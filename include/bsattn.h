@@ -5,7 +5,7 @@
  *                 M_Q = E[q q^T] (used to compare keys) define a Mahalanobis cosine; a
  *                 capacity-constrained hierarchical tree partition puts queries, and
  *                 separately keys, into leaves of exactly 64 tokens.  Only a permutation is
- *                 produced; Q/K/V values are never modified.
+ *                 produced; the tensors themselves are left as they are.
  *                 [comfy.icu "MiniMax H3 Spark Attention (SM89)", "What it's doing under the
  *                 hood"; comfyui-wiki.com "Spark-H3 ...", "What Spark-Attn changes"]
  *   (2) select:   block scores and a per-query-block top-K at a topk_ratio (or fixed

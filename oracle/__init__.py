@@ -10,8 +10,9 @@ Sources (cited by page title and section):
        ComfyUI", section "What Spark-Attn changes" (two-branch split; Reblock; Reweight) and
        the figure on exp(E[x]) vs E[exp(x)].
   [P2] comfy.icu node page "MiniMax H3 Spark Attention (SM89)", section "What it's doing under
-       the hood" (M_K = E[k k^T] for queries, M_Q for keys; exactly-64-token leaves; only the
-       permutation changes; the approximate branch keeps a real Q per query) and section
+       the hood" (M_K = E[k k^T] for queries, M_Q for keys; leaves of 64 tokens; the output of
+       the reblock is a permutation only; each query keeps its own vector in the compressed
+       branch) and section
        "Inputs you'll actually set" (topk_ratio / topk_blocks budgets).
   [P3] h3vid.app guide, section "Warmup and step counts need explicit definitions" (exact
        handling of text, audio and conditioning context while the video grid is sparsified).

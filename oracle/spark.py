@@ -131,8 +131,8 @@ def partition(U: np.ndarray, leaf: int = LEAF, iters: int = POWER_ITERS,
               shared_deep: bool = False, subtree_blocks: int = LITE_SUBTREE_BLOCKS):
     """Capacity-constrained hierarchical tree partition into exactly-`leaf`-token leaves.
 
-    [P2] "What it's doing under the hood": a capacity-constrained tree partition down to
-    exactly 64-token leaves; [P1]: groups are split until every leaf has the block size, in
+    [P2] "What it's doing under the hood": a tree partition under a capacity limit whose
+    leaves hold 64 tokens each; [P1]: groups are split until every leaf has the block size, in
     O(N log N).  Reading: a group of m blocks (m >= 2) splits into floor(m/2) blocks (the
     floor(m/2)*leaf tokens of smallest (p, token id), p = u.v rounded to fp32) and the rest;
     recursion left first; leaves in that depth-first order; ascending token id inside a leaf.
@@ -293,8 +293,9 @@ def sparse_attention_head(Q, K, V, perm_q, perm_k, lists, scale=None, mode="rewe
     """One head of the two-branch layer, output in token order.
 
     [P1] "What Spark-Attn changes": an exact branch fully computes the top-ranked K/V blocks
-    and a compressed branch covers the rest; [P2]: the approximate branch keeps every query's
-    own Q and downsamples only K/V.  For query block i and each of its queries q:
+    and a compressed branch covers the rest; [P2]: in the compressed branch each query uses its
+    own vector and only keys and values are pooled.  For query block i and each of its
+    queries q:
       exact:      softmax over s q.k for the keys of the selected blocks -> (O_e, lse_e)
       compressed: softmax over s q.kt_j + b_j for the unselected blocks j, values vt_j
                   -> (O_c, lse_c); no unselected block gives lse_c = -inf
