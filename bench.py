@@ -39,10 +39,75 @@ import time
 METRIC = "sparse attn layer ms + effective TFLOP/s at 72,576 tok, 10% density, vs dense"
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 HBM_PEAK_GBS = 8000.0
-# Bytes one attention launch moves between L2 and memory on the headline workload: rocprofv3
-# FETCH_SIZE x 2 + WRITE_SIZE x 1 (the factors a plain 1 GiB copy gives those counters), taken
-# on the current attention kernel; to be retaken whenever that kernel changes.
-ATTN_TRAFFIC_BYTES = {"clip10s_bf16": 4.99e10}
+# Bytes one attention launch moves between L2 and memory: rocprofv3 FETCH_SIZE x 2 +
+# WRITE_SIZE x 1 (the factors a plain 1 GiB copy gives those counters), per configuration
+# (workload, tail granularity, context tokens, reblock layout), from the counter runs kept in
+# profiles/.  They hold only for the attention source they were taken on: the benchmark
+# reports traffic null when the hash of that source differs.
+ATTN_SOURCES = ("block_sparse_video_reblock_amd/csrc/attn.hip",
+                "block_sparse_video_reblock_amd/csrc/common.h",
+                "block_sparse_video_reblock_amd/csrc/internal.h")
+ATTN_TRAFFIC = {"source_sha16": "0000000000000000", "bytes": {}}
+# The pages' own figures for the method, quoted as context (other hardware, other workloads,
+# end-to-end or attention-op times not always stated): they are not targets for this run.
+PAGE_FIGURES = [
+    {"figure": "2.37x faster than dense attention, fidelity mode (first 20% of evaluations "
+               "dense)", "hardware": "RTX 4090 (SM89), BF16",
+     "workload": "LightX2V 768p 8-step workflow, 1344x768, 345 frames",
+     "source": "comfy.icu 'MiniMax H3 Spark Attention (SM89)', opening paragraph"},
+    {"figure": "4.35x faster than dense attention, speed mode (sparse from the first "
+               "evaluation)", "hardware": "RTX 4090 (SM89), BF16",
+     "workload": "LightX2V 768p 8-step workflow, 1344x768, 345 frames",
+     "source": "comfy.icu 'MiniMax H3 Spark Attention (SM89)', opening paragraph"},
+    {"figure": "+2.94 dB PSNR over Sol-H3 at 10% density, slightly faster",
+     "hardware": "RTX PRO 6000 Blackwell (SM120)",
+     "workload": "VBench prompts, 1344x768, 240 frames, 19-step MiniMax-H3, PSNR against "
+                 "the dense render",
+     "source": "comfyui-wiki.com 'Spark-H3 ...', section 'Benchmarks'"},
+]
+
+
+def source_sha16(paths):
+    """First 16 hex digits of the SHA-256 of the given repository files, concatenated."""
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for rel in paths:
+        with open(os.path.join(root, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def attn_traffic(workload, tail, ctx, layout):
+    """Measured L2<->memory bytes of one attention launch in this configuration, or None when
+    no counter run covers it or the attention source has changed since."""
+    if source_sha16(ATTN_SOURCES) != ATTN_TRAFFIC["source_sha16"]:
+        return None
+    return ATTN_TRAFFIC["bytes"].get(f"{workload}/{tail}/{ctx}/{layout}")
+
+
+# The reblock kernels hold a subtree in LDS from the first level whose groups have at most this
+# many blocks; the levels below it cost one pass over the tensors together.
+ON_CHIP_SUBTREE_BLOCKS = 8
+
+
+def on_chip_root_level(nb):
+    lvl = 0
+    while -(-nb // (1 << lvl)) > ON_CHIP_SUBTREE_BLOCKS:
+        lvl += 1
+    return lvl
+
+
+def reblock_bytes(nb, x_bytes, sides, subtree_root):
+    """Algorithmic HBM bytes of the reblock: per side, one pass over the tensor for the moments,
+    one for the norms, a statistics and a projection pass for every tree level above the first
+    level whose groups are held on chip, and one pass for that on-chip tail of the tree.
+    Also the plain algorithm's count, with the two passes for every level."""
+    levels = max(0, (nb - 1).bit_length())
+    hbm_levels = min(levels, subtree_root)
+    tail = 1 if hbm_levels < levels else 0
+    return (sides * x_bytes * (2 + 2 * hbm_levels + tail),
+            sides * x_bytes * (2 + 2 * levels))
 
 
 def log(*a):
@@ -200,6 +265,34 @@ class Layer:
         return lse
 
 
+def log_mass_error(torch, ops, qd, kd, vd, perm_q, perm_k, lists, meanpool=False, chunk=16):
+    """Mean absolute log-mass error of the compressed branch over (query, unselected block)
+    pairs, measured on the GPU from the library's block summaries (comfy.icu 'MiniMax H3 Spark
+    Attention (SM89)', 'What it's doing under the hood', reports it for Reweight against mean
+    pooling): for query q and key block j the true log-mass is logsumexp_t(s q.k_t) over the
+    block's keys and the estimate s q.kt_j + b_j.  Plain torch in fp32 on the device tensors;
+    a measurement beside the layer, not a step of it."""
+    H, N, D = qd.shape
+    nb = N // 64
+    s = 1.0 / (D ** 0.5)
+    kt, _, b = ops.summaries(qd, kd, vd, perm_k, flags=ops.BSA_MEANPOOL if meanpool else 0)
+    total, count = 0.0, 0
+    for h in range(H):
+        kp = kd[h].float()[perm_k[h].long()]                 # keys in key-block order
+        sel = torch.zeros(nb, nb, dtype=torch.bool, device=qd.device)
+        sel.scatter_(1, lists[h].long(), True)
+        for i0 in range(0, nb, chunk):
+            i1 = min(nb, i0 + chunk)
+            rows = perm_q[h, 64 * i0:64 * i1].long()
+            q = qd[h].float()[rows]
+            true = torch.logsumexp((s * q @ kp.T).view(-1, nb, 64), dim=2)
+            est = s * q @ kt[h].T + b[h][None, :]
+            unsel = (~sel[i0:i1]).repeat_interleave(64, dim=0)
+            total += float((true - est).abs()[unsel].double().sum().item())
+            count += int(unsel.sum().item())
+    return total / max(count, 1)
+
+
 def time_steps(torch, fns_per_step, steps, warmup):
     """Time `steps` steps, each the list of (name, fn) calls; returns (ms per step, {name: mean
     ms}, {name: [ms per step]})."""
@@ -297,12 +390,15 @@ def main_headline(args, ops, synth, torch, np):
     # HBM-bound stages: algorithmic bytes (inputs read once per pass the algorithm needs)
     elt = 2 if wl.dtype == "bf16" else 4
     x_bytes = H * N * D * elt
-    levels = max(0, (nb - 1).bit_length())
     sides = 1 if args.layout == "q_reuse_k" else 2
+    rb_bytes, rb_plain = reblock_bytes(nb, x_bytes, sides, on_chip_root_level(nb))
     hbm = {
-        "reblock": {"bytes": (2 + 2 * levels) * sides * x_bytes,
-                    "passes": "moments, norms, and per tree level a statistics and a "
-                              "projection pass over " + ("K" if sides == 1 else "Q and K")},
+        "reblock": {"bytes": rb_bytes, "plain_passes_bytes": rb_plain,
+                    "passes": "moments, norms, a statistics and a projection pass per tree "
+                              "level until the groups fit on chip, and one pass for the "
+                              "subtrees held on chip, over " +
+                              ("K" if sides == 1 else "Q and K") +
+                              " (plain_passes_bytes: two passes for every level)"},
         "select": {"bytes": 2 * x_bytes + H * nb * nb * 4, "passes": "Q, K once; scores"},
         # the permutation: K and V written once more in block-contiguous (operand) order
         "prepare": {"bytes": 5 * x_bytes + 4 * H * args.ctx * D * elt,
@@ -379,7 +475,9 @@ def main_headline(args, ops, synth, torch, np):
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": ATTN_TRAFFIC_BYTES.get(wl.name), "kernel": "k_attn_bf16",
+                     "traffic": attn_traffic(wl.name, args.tail, args.ctx, args.layout),
+                     "traffic_source_sha16": source_sha16(ATTN_SOURCES),
+                     "kernel": "k_attn_bf16",
                      "launch_ms": attn_ms, "launch_ms_min": float(min(series["attend"])),
                      "frac_of_gemm": roof,
                      "flops_per_launch": exact_f + comp_f},
@@ -391,6 +489,7 @@ def main_headline(args, ops, synth, torch, np):
         "hbm": hbm,
         "dense": dense,
         "cpu_baseline": cpu,
+        "page_figures": PAGE_FIGURES,
     }
 
 
@@ -477,6 +576,18 @@ def main_sweep(args, ops, synth, torch, np):
             row = {"topk_ratio": ratio, "topk_blocks": topk, "layout": name,
                    "layer_ms": ms_step, "stages_ms": stage_ms, "recall": rec,
                    "speedup_vs_dense_attention": dense_ms / ms_step}
+            if ratio < 1.0 and (fixed or (layout == "separate" and iters == 8)):
+                # log-mass error of the compressed branch: Reweight against mean pooling on
+                # the same layouts and lists (the fixed-tile baseline uses mean pooling)
+                lm = {m: log_mass_error(torch, ops, lay.qd, lay.kd, lay.vd, lay.perm_q,
+                                        lay.perm_k, lay.lists, meanpool=(m == "meanpool"))
+                      for m in (("meanpool",) if fixed else ("reweight", "meanpool"))}
+                row["log_mass_error"] = lm
+                if "reweight" in lm:
+                    row["log_mass_error_reweight_vs_meanpool"] = \
+                        lm["reweight"] / lm["meanpool"] - 1.0
+                log(f"[bench]   log-mass error " +
+                    ", ".join(f"{m} {e:.4f}" for m, e in lm.items()))
             rows.append(row)
             tag = "fixed    " if fixed else ("q_reuse_k" if layout == "q_reuse_k" else
                                               "reblock  " if iters == 8 else
