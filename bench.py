@@ -91,9 +91,9 @@ def attn_traffic(workload, tail, ctx, layout):
 ON_CHIP_SUBTREE_BLOCKS = 8
 
 
-def on_chip_root_level(nb):
+def on_chip_root_level(nb, blocks=ON_CHIP_SUBTREE_BLOCKS):
     lvl = 0
-    while -(-nb // (1 << lvl)) > ON_CHIP_SUBTREE_BLOCKS:
+    while -(-nb // (1 << lvl)) > blocks:
         lvl += 1
     return lvl
 
@@ -147,7 +147,8 @@ class Layer:
     """Device buffers and the four stage calls of one layer (Reblock or fixed-tile layouts)."""
 
     def __init__(self, ops, torch, wl, q, k, v, topk, fixed_tiles=False, ws=None,
-                 layout="separate", tail="token", ctx=None, power_iters=8, lite_tree=False):
+                 layout="separate", tail="token", ctx=None, power_iters=8, lite_tree=False,
+                 subtree_blocks=0):
         self.ops, self.torch = ops, torch
         dev = torch.device("cuda:0")
         dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
@@ -172,7 +173,9 @@ class Layer:
         self.fixed = fixed_tiles
         self.reblock_layout = ops._LAYOUTS[layout]
         self.power_iters = power_iters
-        self.tree_flags = ops.BSA_TREE_SHARED_DEEP if lite_tree else 0
+        self.tree_flags = ops.tree_flags(lite_tree, subtree_blocks if lite_tree else 0)
+        self.subtree_blocks = (subtree_blocks or ops.BSA_DEFAULT_SUBTREE_BLOCKS) if lite_tree \
+            else 0
         self.flags = ((ops.BSA_MEANPOOL if fixed_tiles else 0) |
                       (ops.BSA_TAIL_BLOCK if tail == "block" else 0))
         self.L = ops.lib()
@@ -372,7 +375,7 @@ def main_headline(args, ops, synth, torch, np):
     ctx = synth.make_ctx(wl, args.ctx, (q, k, v)) if args.ctx else None
     lay = Layer(ops, torch, wl, q, k, v, topk, layout=args.layout, tail=args.tail, ctx=ctx,
                 power_iters=ops.BSA_POWER_ITERS_LITE if args.lite else ops.BSA_POWER_ITERS,
-                lite_tree=args.lite)
+                lite_tree=args.lite, subtree_blocks=args.lite_subtree)
     ms_step, stage_ms, series = time_steps(torch, lay.stages(), args.steps, args.warmup)
     steps_ms = [sum(x) for x in zip(*series.values())]
     assert torch.isfinite(lay.out.float()).all().item(), "non-finite output"
@@ -391,7 +394,11 @@ def main_headline(args, ops, synth, torch, np):
     elt = 2 if wl.dtype == "bf16" else 4
     x_bytes = H * N * D * elt
     sides = 1 if args.layout == "q_reuse_k" else 2
-    rb_bytes, rb_plain = reblock_bytes(nb, x_bytes, sides, on_chip_root_level(nb))
+    # the Lite tree reads each shared subtree once, from its root level on
+    rb_root = on_chip_root_level(nb)
+    if args.lite:
+        rb_root = min(rb_root, on_chip_root_level(nb, lay.subtree_blocks))
+    rb_bytes, rb_plain = reblock_bytes(nb, x_bytes, sides, rb_root)
     hbm = {
         "reblock": {"bytes": rb_bytes, "plain_passes_bytes": rb_plain,
                     "passes": "moments, norms, a statistics and a projection pass per tree "
@@ -441,6 +448,26 @@ def main_headline(args, ops, synth, torch, np):
             f"sparse layer speed-up {dense_ms / ms_step:.2f}x")
         del every
 
+    recall = None
+    if args.recall and not args.ctx:
+        # attention-mass recall of this run's layouts at the pages' three budgets, measured on
+        # the GPU against dense softmax (the exact branch alone, then every block)
+        lse_dense = lay.dense_lse()
+        recall = {}
+        for r in (0.1, 0.2, 0.3):
+            kr = ops.topk_count(nb, r)
+            lists_r = torch.empty(H, nb, kr, dtype=torch.int32, device=lay.qd.device)
+            ops.check(lay.L.bsa_select(ctypes.byref(lay.d), lay.p(lay.qd), lay.p(lay.kd),
+                                       lay.p(lay.perm_q), lay.p(lay.perm_k), 0.0, kr,
+                                       lay.p(lists_r), None, lay.p(lay.ws), lay.ws.numel(),
+                                       lay.stream))
+            lse = torch.empty(H, N, dtype=torch.float32, device=lay.qd.device)
+            lay.prepare()
+            lay.attend(ls=lists_r, flags=ops.BSA_EXACT_ONLY, lse=lse)
+            recall[str(r)] = float(torch.exp(lse - lse_dense).mean().item())
+            del lists_r
+        log("[bench] recall " + ", ".join(f"{k}: {v:.4f}" for k, v in recall.items()))
+
     cpu = None
     if not args.no_cpu_baseline and not args.ctx:
         log("[bench] timing the CPU oracle on head 0 ...")
@@ -472,6 +499,7 @@ def main_headline(args, ops, synth, torch, np):
                    "context_tokens": args.ctx,
                    "reblock_power_iters": lay.power_iters,
                    "reblock_lite_tree": bool(lay.tree_flags),
+                   "reblock_lite_subtree_blocks": lay.subtree_blocks,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
@@ -488,6 +516,7 @@ def main_headline(args, ops, synth, torch, np):
         "machine": machine,
         "hbm": hbm,
         "dense": dense,
+        "recall": recall,
         "cpu_baseline": cpu,
         "page_figures": PAGE_FIGURES,
     }
@@ -563,14 +592,15 @@ def main_sweep(args, ops, synth, torch, np):
                 (False, "separate", 8, False, "reblock, reweighted summaries"),
                 (False, "separate", 2, False, "reblock with 2 power steps per split, "
                                               "reweighted summaries"),
-                (False, "separate", 2, True, "Lite reblock (2 power steps, one direction per "
-                                             "subtree of at most 8 blocks), reweighted "
-                                             "summaries"),
+                (False, "separate", 2, True, f"Lite reblock (2 power steps, one direction per "
+                                             f"subtree of at most {args.lite_subtree} blocks), "
+                                             "reweighted summaries"),
                 (False, "q_reuse_k", 8, False, "reblock of the keys reused for the queries, "
                                                "reweighted summaries"),
                 (True, "separate", 8, False, "fixed 4x4x4 tiles, mean-pooled summaries")):
             lay = Layer(ops, torch, wl, q, k, v, topk, fixed_tiles=fixed, ws=base.ws,
-                        layout=layout, power_iters=iters, lite_tree=shared)
+                        layout=layout, power_iters=iters, lite_tree=shared,
+                        subtree_blocks=args.lite_subtree)
             ms_step, stage_ms, _ = time_steps(torch, lay.stages(), args.steps, args.warmup)
             rec = lay.recall(lse_dense)
             row = {"topk_ratio": ratio, "topk_blocks": topk, "layout": name,
@@ -628,7 +658,12 @@ def main():
                          "beside the video grid")
     ap.add_argument("--lite", action="store_true",
                     help="Lite reblock: 2 power steps per split and one direction per subtree "
-                         "of at most 8 blocks")
+                         "(of at most --lite-subtree blocks)")
+    ap.add_argument("--lite-subtree", type=int, default=64, metavar="S",
+                    help="blocks of the Lite tree's shared subtrees (2 .. 64; default 64)")
+    ap.add_argument("--recall", action="store_true",
+                    help="also measure the attention-mass recall of the run's layouts at "
+                         "densities 0.1 / 0.2 / 0.3 against dense softmax")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-machine", action="store_true",
                     help="skip the GEMM and copy ceilings measured beside the headline")

@@ -8,12 +8,14 @@ import os
 import re
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libbsattn.so")
+# BSATTN_LIB names another build of the same library (the host-sanitizer build of the tests)
+LIB_PATH = os.environ.get("BSATTN_LIB") or os.path.join(HERE, "libbsattn.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "bsattn.h")
 
 BSA_OK, BSA_E_ARG, BSA_E_UNSUPPORTED, BSA_E_WORKSPACE, BSA_E_HIP = 0, -1, -2, -3, -4
 BSA_F32, BSA_BF16 = 0, 1
 BSA_MEANPOOL, BSA_EXACT_ONLY, BSA_COMPRESSED_ONLY, BSA_TAIL_BLOCK = 1, 2, 4, 8
+BSA_CHECK_LISTS = 16
 BLOCK = 64
 
 
@@ -71,6 +73,9 @@ _SIGS = {
     "bsa_reblock_from_projections": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
                                                       ctypes.c_size_t, _P]),
     "bsa_tile_layout": (ctypes.c_int32, [ctypes.c_int32] * 7 + [_P, _P]),
+    "bsa_check_lists": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P,
+                                         _P]),
+    "bsa_list_status": (ctypes.c_int32, [_P, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int32), _P]),
     "bsa_topk_from_scores": (ctypes.c_int32, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P,
                                               _P, _P]),
 }
@@ -156,14 +161,23 @@ _LAYOUTS = {"separate": BSA_LAYOUT_SEPARATE, "q_reuse_k": BSA_LAYOUT_Q_REUSE_K}
 
 
 BSA_POWER_ITERS, BSA_POWER_ITERS_LITE, BSA_TREE_SHARED_DEEP = 8, 2, 1
+BSA_DEFAULT_SUBTREE_BLOCKS, BSA_MAX_SUBTREE_BLOCKS, BSA_LITE_SUBTREE_BLOCKS = 8, 64, 64
+
+
+def tree_flags(shared_deep=False, subtree_blocks=0):
+    """Reblock tree flags: the Lite tree's shared subtrees, optionally with their size."""
+    if not shared_deep:
+        return 0 if not subtree_blocks else (int(subtree_blocks) << 8)
+    return BSA_TREE_SHARED_DEEP | (int(subtree_blocks) << 8)
 
 
 def reblock(q, k, ws=None, with_proj=False, layout="separate", power_iters=BSA_POWER_ITERS,
-            shared_deep=False):
+            shared_deep=False, subtree_blocks=0):
     """(perm_q, perm_k[, proj]) int32 [H][N] (and float [H][2][levels][N]).
     layout "separate" (bsa_reblock) or "q_reuse_k" (perm_q is a copy of the key layout);
-    power_iters: power steps per split; shared_deep: one direction per subtree of at most 8
-    blocks (the Lite reblock is power_iters=BSA_POWER_ITERS_LITE, shared_deep=True)."""
+    power_iters: power steps per split; shared_deep: one direction per subtree of at most
+    subtree_blocks blocks (0: BSA_DEFAULT_SUBTREE_BLOCKS); the Lite reblock is
+    power_iters=BSA_POWER_ITERS_LITE, shared_deep=True, subtree_blocks=BSA_LITE_SUBTREE_BLOCKS."""
     torch = _torch()
     if layout not in _LAYOUTS:
         raise BsaError(BSA_E_ARG, f"unknown layout {layout!r}")
@@ -176,14 +190,14 @@ def reblock(q, k, ws=None, with_proj=False, layout="separate", power_iters=BSA_P
     proj = torch.empty(H, 2, levels, N, dtype=torch.float32, device=q.device) if with_proj else None
     check(lib().bsa_reblock_ex(ctypes.byref(d), _dev_ptr(q, q.dtype), _dev_ptr(k, q.dtype),
                                _LAYOUTS[layout], int(power_iters),
-                               BSA_TREE_SHARED_DEEP if shared_deep else 0, _dev_ptr(perm_q),
+                               tree_flags(shared_deep, subtree_blocks), _dev_ptr(perm_q),
                                _dev_ptr(perm_k), _dev_ptr(proj), _dev_ptr(ws), ws.numel(),
                                _stream()))
     return (perm_q, perm_k, proj) if with_proj else (perm_q, perm_k)
 
 
 def reblock_side(q, k, side, ws=None, power_iters=BSA_POWER_ITERS, with_proj=False,
-                 shared_deep=False):
+                 shared_deep=False, subtree_blocks=0):
     """One side of the reblock: side 0 the query layouts, side 1 the key layouts (int32 [H][N]),
     and with_proj its projections (float [H][2][levels][N], the other side's rows 0)."""
     torch = _torch()
@@ -196,7 +210,7 @@ def reblock_side(q, k, side, ws=None, power_iters=BSA_POWER_ITERS, with_proj=Fal
         else None
     check(lib().bsa_reblock_side(ctypes.byref(d), _dev_ptr(q, q.dtype), _dev_ptr(k, q.dtype),
                                  int(side), int(power_iters),
-                                 BSA_TREE_SHARED_DEEP if shared_deep else 0, _dev_ptr(perm),
+                                 tree_flags(shared_deep, subtree_blocks), _dev_ptr(perm),
                                  _dev_ptr(proj),
                                  _dev_ptr(ws), ws.numel(), _stream()))
     return (perm, proj) if with_proj else perm
@@ -309,6 +323,23 @@ def summaries(q, k, v, perm_k, flags=0, scale=0.0, ws=None):
                               float(scale), _dev_ptr(kt), _dev_ptr(vt), _dev_ptr(bias),
                               _dev_ptr(ws), ws.numel(), _stream()))
     return kt, vt, bias
+
+
+def check_lists(lists, n_blocks):
+    """bsa_check_lists on int32 lists [..., topk]: (malformed rows, first malformed row or -1)."""
+    torch = _torch()
+    rows = lists.numel() // lists.shape[-1]
+    result = torch.empty(2, dtype=torch.int32, device=lists.device)
+    check(lib().bsa_check_lists(int(rows), int(n_blocks), int(lists.shape[-1]),
+                                _dev_ptr(lists, torch.int32), _dev_ptr(result), _stream()))
+    return tuple(int(x) for x in result.cpu().tolist())
+
+
+def list_status(ws):
+    """bsa_list_status: the list check result of the last BSA_CHECK_LISTS call on ws."""
+    out = (ctypes.c_int32 * 2)()
+    check(lib().bsa_list_status(_dev_ptr(ws), ws.numel(), out, _stream()))
+    return int(out[0]), int(out[1])
 
 
 def reblock_from_projections(proj):

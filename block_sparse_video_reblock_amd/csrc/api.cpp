@@ -91,7 +91,7 @@ float resolve_scale(const bsa_desc* d, float scale) {
 
 // ----------------------------------------------------------------- workspace layouts
 struct AttnWs {
-  size_t anchor_partial, anchor, kt, vt, bias, ktsw, vtsw, ksw, vsw, qbar, tbits, tail_o,
+  size_t status, anchor_partial, anchor, kt, vt, bias, ktsw, vtsw, ksw, vsw, qbar, tbits, tail_o,
       tail_lse, ctsw, cvsw, total;
 };
 
@@ -101,6 +101,8 @@ AttnWs attn_layout(const bsa_desc* d, int n_ctx = 0) {
   AttnWs w{};
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
+  // first, at the same offset for every descriptor: the result of the last list check
+  w.status = take(2 * sizeof(int32_t));
   w.anchor_partial = take(H * bsa::ceil_div(long(N), bsa::kColChunk) * D * 4);
   w.anchor = take(H * D * 4);
   w.kt = take(H * nb * D * 4);
@@ -155,6 +157,22 @@ SelWs select_layout(const bsa_desc* d) {
 }
 
 char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+// The Lite tree's subtree size from the reblock tree flags: 0 for the full tree.
+bsa_status tree_shared_blocks(uint32_t flags, int* blocks) {
+  *blocks = 0;
+  if (flags & ~uint32_t(BSA_TREE_SHARED_DEEP | BSA_TREE_SUBTREE_BLOCKS(0xFF)))
+    return fail(BSA_E_ARG, "unknown tree flags 0x%x", flags);
+  const int b = int((flags >> 8) & 0xFF);
+  if (!(flags & BSA_TREE_SHARED_DEEP)) {
+    if (b != 0) return fail(BSA_E_ARG, "a subtree size needs BSA_TREE_SHARED_DEEP");
+    return ok();
+  }
+  if (b != 0 && (b < 2 || b > BSA_MAX_SUBTREE_BLOCKS))
+    return fail(BSA_E_ARG, "subtree size %d is not in [2, %d]", b, BSA_MAX_SUBTREE_BLOCKS);
+  *blocks = b == 0 ? BSA_DEFAULT_SUBTREE_BLOCKS : b;
+  return ok();
+}
 
 bsa_status check_ws(const void* ws, size_t have, size_t need) {
   if (have < need)
@@ -233,8 +251,9 @@ bsa_status bsa_reblock_ex(const bsa_desc* d, const void* q, const void* k, int32
   if (power_iters < 1 || power_iters > BSA_MAX_POWER_ITERS)
     return fail(BSA_E_ARG, "power_iters = %d is not in [1, %d]", (int)power_iters,
                 BSA_MAX_POWER_ITERS);
-  if (tree_flags & ~uint32_t(BSA_TREE_SHARED_DEEP))
-    return fail(BSA_E_ARG, "unknown tree flags 0x%x", tree_flags);
+  int shared_blocks = 0;
+  st = tree_shared_blocks(tree_flags, &shared_blocks);
+  if (st != BSA_OK) return st;
   if (!q || !k || !perm_q || !perm_k) return fail(BSA_E_ARG, "null tensor pointer");
   if (layout == BSA_LAYOUT_SEPARATE && perm_q == perm_k)
     return fail(BSA_E_ARG, "separate layouts need two permutation buffers");
@@ -247,7 +266,7 @@ bsa_status bsa_reblock_ex(const bsa_desc* d, const void* q, const void* k, int32
                                         layout == BSA_LAYOUT_Q_REUSE_K ? bsa::kSideKeys
                                                                        : bsa::kSideBoth,
                                         layout == BSA_LAYOUT_Q_REUSE_K, power_iters,
-                                        (tree_flags & BSA_TREE_SHARED_DEEP) != 0, ws, stream),
+                                        shared_blocks, ws, stream),
                     "reblock launch");
 }
 
@@ -260,8 +279,9 @@ bsa_status bsa_reblock_side(const bsa_desc* d, const void* q, const void* k, int
   if (power_iters < 1 || power_iters > BSA_MAX_POWER_ITERS)
     return fail(BSA_E_ARG, "power_iters = %d is not in [1, %d]", (int)power_iters,
                 BSA_MAX_POWER_ITERS);
-  if (tree_flags & ~uint32_t(BSA_TREE_SHARED_DEEP))
-    return fail(BSA_E_ARG, "unknown tree flags 0x%x", tree_flags);
+  int shared_blocks = 0;
+  st = tree_shared_blocks(tree_flags, &shared_blocks);
+  if (st != BSA_OK) return st;
   if (!q || !k || !perm) return fail(BSA_E_ARG, "null tensor pointer");
   st = check_ws(ws, ws_bytes, bsa::reblock_ws_bytes(d->heads, d->tokens, d->head_dim));
   if (st != BSA_OK) return st;
@@ -270,8 +290,7 @@ bsa_status bsa_reblock_side(const bsa_desc* d, const void* q, const void* k, int
   return hip_status(bsa::launch_reblock(is_bf16(d), q, k, d->heads, d->tokens, d->head_dim,
                                         perm, perm, proj_opt,
                                         side ? bsa::kSideKeys : bsa::kSideQueries, false,
-                                        power_iters, (tree_flags & BSA_TREE_SHARED_DEEP) != 0,
-                                        ws, stream),
+                                        power_iters, shared_blocks, ws, stream),
                     "reblock launch");
 }
 
@@ -347,7 +366,8 @@ bsa_status check_attn_args(const bsa_desc* d, const void* q, const void* k, cons
   bsa_status st = check_desc(d);
   if (st != BSA_OK) return st;
   if (!q || !k || !v || !perm_k) return fail(BSA_E_ARG, "null tensor pointer");
-  const uint32_t known = BSA_MEANPOOL | BSA_EXACT_ONLY | BSA_COMPRESSED_ONLY | BSA_TAIL_BLOCK;
+  const uint32_t known =
+      BSA_MEANPOOL | BSA_EXACT_ONLY | BSA_COMPRESSED_ONLY | BSA_TAIL_BLOCK | BSA_CHECK_LISTS;
   if (flags & ~known) return fail(BSA_E_ARG, "unknown flags 0x%x", flags);
   if ((flags & BSA_EXACT_ONLY) && (flags & BSA_COMPRESSED_ONLY))
     return fail(BSA_E_ARG, "BSA_EXACT_ONLY and BSA_COMPRESSED_ONLY are exclusive");
@@ -421,6 +441,12 @@ hipError_t do_attend(const bsa_desc* d, const AttnWs& L, void* ws, const void* q
   a.bias = reinterpret_cast<const float*>(at(ws, L.bias));
   a.o = o;
   a.lse = lse;
+  if (flags & BSA_CHECK_LISTS) {
+    int32_t* status = reinterpret_cast<int32_t*>(at(ws, L.status));
+    hipError_t e = bsa::launch_check_lists(lists, d->heads * nb, nb, topk, status, stream);
+    if (e != hipSuccess) return e;
+    a.list_status = status;
+  }
   float* qbar = reinterpret_cast<float*>(at(ws, L.qbar));
   if (tail_block) {
     hipError_t e = bsa::launch_block_means(is_bf16(d), q, perm_q, d->heads, d->tokens,
@@ -590,6 +616,31 @@ bsa_status bsa_attend_ctx(const bsa_desc* d, int32_t n_ctx, const void* q, const
   return hip_status(do_attend(d, attn_layout(d, n_ctx), ws, q, k, v, perm_q, perm_k, lists,
                               topk, flags, resolve_scale(d, scale), o, lse_opt, stream, ctx),
                     "attention launch");
+}
+
+bsa_status bsa_check_lists(int32_t rows, int32_t n_blocks, int32_t topk, const int32_t* lists,
+                           int32_t* result, hipStream_t stream) {
+  if (rows < 1 || n_blocks < 1) return fail(BSA_E_ARG, "rows and n_blocks must be >= 1");
+  if (topk < 1 || topk > n_blocks)
+    return fail(BSA_E_ARG, "topk = %d is not in [1, %d]", topk, n_blocks);
+  if ((int64_t)rows * topk > (int64_t)1 << 31) return fail(BSA_E_ARG, "too many list entries");
+  if (!lists || !result) return fail(BSA_E_ARG, "null tensor pointer");
+  bsa_status st = check_device();
+  if (st != BSA_OK) return st;
+  return hip_status(bsa::launch_check_lists(lists, rows, n_blocks, topk, result, stream),
+                    "list check launch");
+}
+
+bsa_status bsa_list_status(const void* ws, size_t ws_bytes, int32_t* result, hipStream_t stream) {
+  if (!ws || !result) return fail(BSA_E_ARG, "null pointer");
+  if (ws_bytes < 2 * sizeof(int32_t))
+    return fail(BSA_E_WORKSPACE, "workspace of %zu bytes holds no list status", ws_bytes);
+  bsa_status st = check_device();
+  if (st != BSA_OK) return st;
+  // the status is the first item of every attention workspace layout
+  hipError_t e = hipMemcpyAsync(result, ws, 2 * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  return hip_status(e, "list status read");
 }
 
 size_t bsa_partition_workspace_bytes(int32_t problems, int32_t tokens) {

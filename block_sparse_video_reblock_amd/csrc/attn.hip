@@ -106,6 +106,7 @@ struct KSide {
   const float* bias;         // [H][nt_s * 64] summary bias, -inf on padding rows
   const uint4 *ctsw, *cvsw;  // [H][nt_c][1024], rows past n_ctx zero
   int nb, nt_s, nt_c, n_ctx;
+  const int32_t* list_status;  // nonzero: a list is malformed and nothing is computed (or null)
 };
 
 // Workgroups 0 .. wg_c - 1 take the query blocks of side `cs` (context queries: few, long
@@ -129,6 +130,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(QSide cs, QSide vs, int wg
   // 64-row masks: 0 for a full context tile, 0 / -inf for the valid / padding rows of the last
   extern __shared__ float sbias[];
 
+  if (ks.list_status != nullptr && load_uniform(ks.list_status) != 0) return;
   const bool is_ctx = CTX && blockIdx.x < wg_c;
   const QSide S = is_ctx ? cs : vs;
   const int local = is_ctx ? blockIdx.x : xcd_remap(blockIdx.x - wg_c, H * vs.nbq);
@@ -453,6 +455,7 @@ struct KSide32 {
   const float* bias;        // [H][nt_s * 64]
   const float *kc, *vc;     // context keys / values [H][n_ctx][D]
   int N, nb, nt_s, nt_c, n_ctx;
+  const int32_t* list_status;  // nonzero: a list is malformed and nothing is computed (or null)
 };
 
 __global__ __launch_bounds__(64) void k_attn_f32(QSide32 cs, QSide32 vs, int wg_c, KSide32 ks,
@@ -462,6 +465,7 @@ __global__ __launch_bounds__(64) void k_attn_f32(QSide32 cs, QSide32 vs, int wg_
   __shared__ float sv[64][D + 1];
   __shared__ float sb[64];
   __shared__ uint32_t sel_bits[kMaxSelWords];
+  if (ks.list_status != nullptr && load_uniform(ks.list_status) != 0) return;
   const bool is_ctx = blockIdx.x < wg_c;
   const QSide32 S = is_ctx ? cs : vs;
   const int local = is_ctx ? blockIdx.x : xcd_remap(blockIdx.x - wg_c, H * vs.nbq);
@@ -820,6 +824,7 @@ hipError_t launch_attn_bf16(const AttnLaunch& a, hipStream_t s) {
   ks.nt_s = nt_s;
   ks.nt_c = nt_c;
   ks.n_ctx = a.n_ctx;
+  ks.list_status = a.list_status;
   QSide vs{static_cast<const uint16_t*>(a.q), a.perm_q, true, a.tail_o, a.tail_lse,
            static_cast<uint16_t*>(a.o), a.lse, a.N, a.nb, a.topk, a.n_exact, a.n_comp, a.tau0};
   QSide cs{static_cast<const uint16_t*>(a.q_ctx), nullptr, false, nullptr, nullptr,
@@ -853,6 +858,7 @@ hipError_t launch_attn_f32(const AttnLaunch& a, hipStream_t s) {
   ks.nt_s = nt_s;
   ks.nt_c = nt_c;
   ks.n_ctx = a.n_ctx;
+  ks.list_status = a.list_status;
   QSide32 vs{static_cast<const float*>(a.q), a.perm_q, a.lists, a.qbar, static_cast<float*>(a.o),
              a.lse, a.N, a.nb, a.topk, a.n_exact, a.n_comp, a.tau0};
   QSide32 cs{static_cast<const float*>(a.q_ctx), nullptr, nullptr, nullptr,

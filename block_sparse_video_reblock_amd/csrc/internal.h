@@ -62,6 +62,9 @@ struct AttnLaunch {
   const void *ctsw, *cvsw;                  // bf16 path: swizzled context tiles
   void* o_ctx;
   float* lse_ctx;
+  // result of a list check run before the launch (see launch_check_lists), or null: with a
+  // malformed list the attention kernels return at once, before any list entry is read
+  const int32_t* list_status;
 };
 hipError_t launch_attn_bf16(const AttnLaunch& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnLaunch& a, hipStream_t s);
@@ -80,16 +83,21 @@ hipError_t launch_tile_layout(int heads, int T, int H, int W, int tt, int th, in
                               int32_t* perm, hipStream_t s);
 hipError_t launch_topk(const float* scores, int rows, int nb, int k, int32_t* lists,
                        hipStream_t s);
+// result (device, 2 ints): malformed rows of lists [rows][k] (entries outside [0, nb) or not
+// strictly ascending) and the smallest such row (-1 if none)
+hipError_t launch_check_lists(const int32_t* lists, int rows, int nb, int k, int32_t* result,
+                              hipStream_t s);
 
 // ------------------------------------------------------------------ reblock (stage 1)
 size_t reblock_ws_bytes(int H, int N, int D);
 // sides: which trees to build (queries under M_K into perm_q, keys under M_Q into perm_k);
 // copy_q: perm_q becomes a copy of perm_k afterwards; iters: power steps per split;
-// shared_deep: the Lite tree (one direction per subtree of at most 8 blocks)
+// shared_blocks: 0 for the full tree, else the Lite tree with one direction per subtree from
+// the first level whose groups hold at most that many blocks (2 .. 64)
 constexpr int kSideQueries = 1, kSideKeys = 2, kSideBoth = 3;
 hipError_t launch_reblock(bool bf16, const void* q, const void* k, int H, int N, int D,
                           int32_t* perm_q, int32_t* perm_k, float* proj_opt, int sides,
-                          bool copy_q, int iters, bool shared_deep, void* ws, hipStream_t s);
+                          bool copy_q, int iters, int shared_blocks, void* ws, hipStream_t s);
 size_t partition_ws_bytes(int P, int N);
 hipError_t launch_partition_from_proj(int P, int N, const float* proj, int32_t* perm, void* ws,
                                       hipStream_t s);

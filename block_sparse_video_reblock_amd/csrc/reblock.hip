@@ -1438,17 +1438,16 @@ __global__ __launch_bounds__(256, 2) void k_subtree_pair(ProblemArgs a, int leve
   }
 }
 
-// grid (roots, P): subtrees whose root spans at most kSmallBlocks blocks.  The root's positions
-// and keys stay in LDS for all remaining levels.
+// grid (roots, P): subtrees whose root spans at most kSmallBlocks blocks, split down to level
+// `stop` (exclusive).  The root's positions and keys stay in LDS for all of those levels.
 constexpr int kSmallBlocks = 8;
-template <typename T, int D, bool SHARED>
-__global__ __launch_bounds__(256, 2) void k_subtree_small(ProblemArgs a, int ls) {
+template <typename T, int D>
+__global__ __launch_bounds__(256, 2) void k_subtree_small(ProblemArgs a, int ls, int stop) {
   __shared__ StageLds<D, 2> st;
   __shared__ DirLds L;
   __shared__ int32_t spos[kSmallBlocks * kBlk];
   __shared__ int32_t stmp[kSmallBlocks * kBlk];
   __shared__ float skeys[kSmallBlocks * kBlk];
-  __shared__ float skeys2[kSmallBlocks * kBlk];  // keys in partitioned order (Lite tree)
   __shared__ int hist[4 * 256];
   __shared__ int sm[16];
   const int g0 = a.lists[(size_t)ls * a.G + blockIdx.x], p = problem_of(a, blockIdx.y);
@@ -1460,17 +1459,105 @@ __global__ __launch_bounds__(256, 2) void k_subtree_small(ProblemArgs a, int ls)
   const float ysc = a.yscale[2 * p], inv_s2 = a.yscale[2 * p + 1];
   for (int i = threadIdx.x; i < rm * kBlk; i += 256) spos[i] = pos[i];
   __syncthreads();
-  // (Lite tree) the subtree root's split, with its own direction and projections, which the
-  // partition carries along with the positions
-  auto full_split = [&](int level, int g) {
-    int b0, m;
-    if (group_geom(a.nb, level, g, b0, m) != kGroupSplit) return;
-    const int lb0 = b0 - rb0, n = m * kBlk;
-    const float shv = threadIdx.x < D ? parent_mean<D>(a, p, level, g)[threadIdx.x] : 0.f;
-    const float y_first = first_candidate<T, D>(X, spos, inv_n, lb0 * kBlk);
+  for (int level = ls; level < stop; ++level) {
+    const int depth = level - ls;
+    for (int g = g0 << depth; g < ((g0 + 1) << depth); ++g) {
+      int b0, m;
+      if (group_geom(a.nb, level, g, b0, m) != kGroupSplit) continue;
+      const int lb0 = b0 - rb0, n = m * kBlk;
+      const float shv = threadIdx.x < D ? parent_mean<D>(a, p, level, g)[threadIdx.x] : 0.f;
+      const float y_first = first_candidate<T, D>(X, spos, inv_n, lb0 * kBlk);
+      f32x16_t acc[Cov<D>::TILES];
+      // M is read (from L2) only for the power steps, so it holds no registers during the
+      // statistics
+      MRegs<D> M;
+      {
+        SymAcc<D> sacc;
+        sacc.zero();
+        float dpart[D / 8];
+#pragma unroll
+        for (int e = 0; e < D / 8; ++e) dpart[e] = 0.f;
+        sym_stats_range<T, D, true>(X, spos, inv_n, lb0, lb0 + m, L.shift, shv, ysc, st, sacc,
+                                    dpart);
+        reduce_dpart<D>(dpart, L.red, L.mu);
+        sym_to_regs<D>(sacc, inv_s2, st, acc);
+      }
+      M.load(problem_metric<D>(a, p));  // overlaps the centring in group_direction
+      group_direction<T, D>(acc, L, M, n, 1.f, X, spos, inv_n, lb0 * kBlk, y_first, a.iters);
+      if (threadIdx.x < D) group_mean<D>(a, p, level, g)[threadIdx.x] = L.mu[threadIdx.x];
+      float* proj = problem_proj(a, p, level);
+      project_range<T, D>(X, spos, inv_n, lb0, lb0 + m, L.w, skeys, proj);
+      __syncthreads();
+      const int want = (m >> 1) * kBlk;
+      int take;
+      const uint32_t T_ = select_smallest_w<256>(skeys + lb0 * kBlk, n, want, hist, sm, &take);
+      partition_w<256>(skeys + lb0 * kBlk, spos + lb0 * kBlk, stmp, n, want, T_, take, sm);
+      for (int i = threadIdx.x; i < n; i += 256) spos[lb0 * kBlk + i] = stmp[i];
+      __syncthreads();
+    }
+  }
+  for (int i = threadIdx.x; i < rm * kBlk; i += 256) pos[i] = spos[i];
+}
+
+// ------------------------------------------------------------- Lite: shared subtrees
+// From the shared root level on, each group takes one direction (its own split) and its
+// descendants keep cutting along those projections: the subtree is then its tokens in
+// (projection, token id) order cut into 64-token leaves, each leaf in ascending token id.  So
+// one workgroup per root group splits it (statistics, direction, projections) and sorts it.
+constexpr int kMaxSharedBlocks = 64;  // blocks of the largest shared subtree (LDS capacity)
+constexpr int kSharedCap = kMaxSharedBlocks * kBlk;
+
+// the float whose orderable_key is u (-0.0 comes back as +0.0, which sorts equal to it)
+BSA_DEV float key_to_float(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
+// Bitonic sort in LDS over stages with subsequence lengths k = 2 .. kmax (a power of two): with
+// n = kmax it sorts v[0..n) ascending; with n a multiple of kmax it sorts every aligned run of
+// kmax entries ascending (the last merge of every run is ascending).
+BSA_DEV void lds_bitonic(uint64_t* v, int n, int kmax) {
+  for (int k = 2; k <= kmax; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int t = threadIdx.x; t < (n >> 1); t += 256) {
+        const int i = 2 * t - (t & (j - 1)), ip = i + j;
+        const uint64_t x = v[i], y = v[ip];
+        if ((x > y) == (k == kmax || (i & k) == 0)) {
+          v[i] = y;
+          v[ip] = x;
+        }
+      }
+      __syncthreads();
+    }
+}
+
+// grid (roots of level lr, P)
+template <typename T, int D>
+__global__ __launch_bounds__(256, 2) void k_shared_subtree(ProblemArgs a, int lr) {
+  constexpr size_t kRaw = sizeof(StageLds<D, 2>) > kSharedCap * sizeof(uint64_t)
+                              ? sizeof(StageLds<D, 2>)
+                              : kSharedCap * sizeof(uint64_t);
+  // staging area of the statistics, afterwards the sort buffer
+  __shared__ __align__(16) unsigned char sraw[kRaw];
+  __shared__ DirLds L;
+  __shared__ int32_t spos[kSharedCap];
+  __shared__ float skeys[kSharedCap];
+  StageLds<D, 2>& st = *reinterpret_cast<StageLds<D, 2>*>(sraw);
+  uint64_t* sbuf = reinterpret_cast<uint64_t*>(sraw);
+  const int g = a.lists[(size_t)lr * a.G + blockIdx.x], p = problem_of(a, blockIdx.y);
+  int b0, m;
+  group_geom(a.nb, lr, g, b0, m);
+  const int n = m * kBlk;
+  const T* X = problem_x<T, D>(a, p);
+  int32_t* pos = problem_pos(a, p) + (size_t)b0 * kBlk;
+  const float* inv_n = a.inv_n + (size_t)p * a.N;
+  const float ysc = a.yscale[2 * p], inv_s2 = a.yscale[2 * p + 1];
+  for (int i = threadIdx.x; i < n; i += 256) spos[i] = pos[i];
+  __syncthreads();
+  {
+    // the root's own split: statistics relative to the parent's mean, direction, projections
+    const float shv = threadIdx.x < D ? parent_mean<D>(a, p, lr, g)[threadIdx.x] : 0.f;
+    const float y_first = first_candidate<T, D>(X, spos, inv_n, 0);
     f32x16_t acc[Cov<D>::TILES];
-    // M is read (from L2) only for the power steps, so it holds no registers during the
-    // statistics
     MRegs<D> M;
     {
       SymAcc<D> sacc;
@@ -1478,91 +1565,41 @@ __global__ __launch_bounds__(256, 2) void k_subtree_small(ProblemArgs a, int ls)
       float dpart[D / 8];
 #pragma unroll
       for (int e = 0; e < D / 8; ++e) dpart[e] = 0.f;
-      sym_stats_range<T, D, true>(X, spos, inv_n, lb0, lb0 + m, L.shift, shv, ysc, st, sacc,
-                                  dpart);
+      sym_stats_range<T, D, true>(X, spos, inv_n, 0, m, L.shift, shv, ysc, st, sacc, dpart);
       reduce_dpart<D>(dpart, L.red, L.mu);
       sym_to_regs<D>(sacc, inv_s2, st, acc);
     }
-    M.load(problem_metric<D>(a, p));  // overlaps the centring in group_direction
-    group_direction<T, D>(acc, L, M, n, 1.f, X, spos, inv_n, lb0 * kBlk, y_first, a.iters);
-    if (threadIdx.x < D) group_mean<D>(a, p, level, g)[threadIdx.x] = L.mu[threadIdx.x];
-    float* proj = problem_proj(a, p, level);
-    project_range<T, D>(X, spos, inv_n, lb0, lb0 + m, L.w, skeys, proj);
+    M.load(problem_metric<D>(a, p));
+    group_direction<T, D>(acc, L, M, n, 1.f, X, spos, inv_n, 0, y_first, a.iters);
+    if (threadIdx.x < D) group_mean<D>(a, p, lr, g)[threadIdx.x] = L.mu[threadIdx.x];
+    project_range<T, D>(X, spos, inv_n, 0, m, L.w, skeys, problem_proj(a, p, lr));
     __syncthreads();
-    const int want = (m >> 1) * kBlk;
-    int take;
-    const uint32_t T_ = select_smallest_w<256>(skeys + lb0 * kBlk, n, want, hist, sm, &take);
-    partition_w<256>(skeys + lb0 * kBlk, spos + lb0 * kBlk, stmp, n, want, T_, take, sm, skeys2);
+  }
+  // sort by (projection, token id); positions hold ascending token ids, each below 2^19
+  int n2 = kBlk;
+  while (n2 < n) n2 <<= 1;
+  for (int i = threadIdx.x; i < n2; i += 256)
+    sbuf[i] = i < n ? (uint64_t(orderable_key(skeys[i])) << 32) | uint32_t(spos[i]) : ~0ull;
+  __syncthreads();
+  lds_bitonic(sbuf, n2, n2);
+  // the deeper levels' projections are the root's (where the token's group still splits)
+  if (a.proj != nullptr)
     for (int i = threadIdx.x; i < n; i += 256) {
-      spos[lb0 * kBlk + i] = stmp[i];
-      skeys[lb0 * kBlk + i] = skeys2[i];
-    }
-    __syncthreads();
-  };
-  // Lite tree: a split of group g along the projections its subtree root computed, which the
-  // partitions carried along with the positions
-  auto rank_split = [&](int level, int g) {
-    int b0, m;
-    if (group_geom(a.nb, level, g, b0, m) != kGroupSplit) return;
-    const int lb0 = b0 - rb0, n = m * kBlk;
-    float* proj = problem_proj(a, p, level);
-    if (proj)
-      for (int i = threadIdx.x; i < n; i += 256) proj[spos[lb0 * kBlk + i]] = skeys[lb0 * kBlk + i];
-    const int want = (m >> 1) * kBlk;
-    int take;
-    const uint32_t T_ = select_smallest_w<256>(skeys + lb0 * kBlk, n, want, hist, sm, &take);
-    partition_w<256>(skeys + lb0 * kBlk, spos + lb0 * kBlk, stmp, n, want, T_, take, sm, skeys2);
-    for (int i = threadIdx.x; i < n; i += 256) {
-      spos[lb0 * kBlk + i] = stmp[i];
-      skeys[lb0 * kBlk + i] = skeys2[i];
-    }
-    __syncthreads();
-  };
-  if constexpr (SHARED) {
-    full_split(ls, g0);
-    for (int level = ls + 1; level < a.L; ++level)
-      for (int g = g0 << (level - ls); g < ((g0 + 1) << (level - ls)); ++g) rank_split(level, g);
-  } else {
-    for (int level = ls; level < a.L; ++level) {
-      const int depth = level - ls;
-      for (int g = g0 << depth; g < ((g0 + 1) << depth); ++g) {
-        int b0, m;
-        if (group_geom(a.nb, level, g, b0, m) != kGroupSplit) continue;
-        const int lb0 = b0 - rb0, n = m * kBlk;
-        const float shv = threadIdx.x < D ? parent_mean<D>(a, p, level, g)[threadIdx.x] : 0.f;
-        const float y_first = first_candidate<T, D>(X, spos, inv_n, lb0 * kBlk);
-        f32x16_t acc[Cov<D>::TILES];
-        // M is read (from L2) only for the power steps, so it holds no registers during the
-        // statistics
-        MRegs<D> M;
-        {
-          SymAcc<D> sacc;
-          sacc.zero();
-          float dpart[D / 8];
-#pragma unroll
-          for (int e = 0; e < D / 8; ++e) dpart[e] = 0.f;
-          sym_stats_range<T, D, true>(X, spos, inv_n, lb0, lb0 + m, L.shift, shv, ysc, st,
-                                      sacc, dpart);
-          reduce_dpart<D>(dpart, L.red, L.mu);
-          sym_to_regs<D>(sacc, inv_s2, st, acc);
-        }
-        M.load(problem_metric<D>(a, p));  // overlaps the centring in group_direction
-        group_direction<T, D>(acc, L, M, n, 1.f, X, spos, inv_n, lb0 * kBlk, y_first,
-                              a.iters);
-        if (threadIdx.x < D) group_mean<D>(a, p, level, g)[threadIdx.x] = L.mu[threadIdx.x];
-        float* proj = problem_proj(a, p, level);
-        project_range<T, D>(X, spos, inv_n, lb0, lb0 + m, L.w, skeys, proj);
-        __syncthreads();
-        const int want = (m >> 1) * kBlk;
-        int take;
-        const uint32_t T_ = select_smallest_w<256>(skeys + lb0 * kBlk, n, want, hist, sm, &take);
-        partition_w<256>(skeys + lb0 * kBlk, spos + lb0 * kBlk, stmp, n, want, T_, take, sm);
-        for (int i = threadIdx.x; i < n; i += 256) spos[lb0 * kBlk + i] = stmp[i];
-        __syncthreads();
+      const uint64_t e = sbuf[i];
+      const int tok = int(uint32_t(e));
+      const float key = key_to_float(uint32_t(e >> 32));
+      for (int level = lr + 1; level < a.L; ++level) {
+        int gb0, gm;
+        group_of_block(a.nb, level, b0 + i / kBlk, gb0, gm);
+        if (gm >= 2) problem_proj(a, p, level)[tok] = key;
       }
     }
-  }
-  for (int i = threadIdx.x; i < rm * kBlk; i += 256) pos[i] = spos[i];
+  __syncthreads();
+  // leaves: consecutive runs of 64 in that order, each sorted by token id
+  for (int i = threadIdx.x; i < n; i += 256) sbuf[i] = uint32_t(sbuf[i]);
+  __syncthreads();
+  lds_bitonic(sbuf, n, kBlk);
+  for (int i = threadIdx.x; i < n; i += 256) pos[i] = int32_t(uint32_t(sbuf[i]));
 }
 
 // ------------------------------------------------------------------------- helpers
@@ -1637,6 +1674,13 @@ RebLayout reb_layout(int H, int N, int D) {
   return r;
 }
 
+// the first level whose groups all hold at most `blocks` blocks
+int shared_root_level(int nb, int blocks) {
+  int level = 0;
+  while (ceil_div(nb, 1 << level) > blocks) ++level;
+  return level;
+}
+
 // number of active (m >= 2) nodes of a level
 int active_count(int nb, int level) {
   int c = 0, b0, m;
@@ -1647,7 +1691,7 @@ int active_count(int nb, int level) {
 template <typename T, int D>
 hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm_q,
                        int32_t* perm_k, float* proj_opt, int sides, bool copy_q, int iters,
-                       bool shared_deep, void* ws, hipStream_t s) {
+                       int shared_blocks, void* ws, hipStream_t s) {
   const RebLayout R = reb_layout(H, N, D);
   char* w = static_cast<char*>(ws);
   // sides: kSideQueries builds the query trees only (problems 2h, under M_K), kSideKeys the
@@ -1710,9 +1754,11 @@ hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm
   if (R.L > 0) k_group_lists<<<R.L, 256, 0, s>>>(nb, R.G, reinterpret_cast<int*>(w + R.lists));
   // levels whose groups are large are split over several workgroups; below that one
   // workgroup per group, and from the first level whose groups fit in kSmallBlocks blocks,
-  // one workgroup per subtree down to the leaves.
+  // one workgroup per subtree down to the leaves.  The Lite tree stops all of these at the
+  // shared root level lr, where one workgroup per group splits it once and sorts it.
+  const int lr = shared_blocks > 0 ? shared_root_level(nb, shared_blocks) : R.L;
   int level = 0;
-  for (; level < R.L; ++level) {
+  for (; level < R.L && level < lr; ++level) {
     const int slices = wide_slices(level, nb);
     if (slices <= 1 || ceil_div(nb, 1 << level) <= kSmallBlocks) break;
     a.level = level;
@@ -1729,19 +1775,20 @@ hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm
   }
   // narrow levels: one workgroup per parent, left-only statistics; the covariance slots
   // alternate between the two buffers (the last wide level stored its groups' covariances)
-  for (; level < R.L; ++level) {
+  for (; level < R.L && level < lr; ++level) {
     const int roots = active_count(nb, level);
     if (roots == 0) continue;
     if (ceil_div(nb, 1 << level) <= kSmallBlocks) {
-      if (shared_deep)
-        k_subtree_small<T, D, true><<<dim3(roots, P), 256, 0, s>>>(a, level);
-      else
-        k_subtree_small<T, D, false><<<dim3(roots, P), 256, 0, s>>>(a, level);
+      k_subtree_small<T, D><<<dim3(roots, P), 256, 0, s>>>(a, level, std::min(lr, R.L));
       break;
     }
     a.cov_prev = reinterpret_cast<float*>(w + ((level & 1) ? R.cov0 : R.cov1));
     a.cov_cur = reinterpret_cast<float*>(w + ((level & 1) ? R.cov1 : R.cov0));
     k_subtree_pair<T, D><<<dim3(active_count(nb, level - 1), P), 256, 0, s>>>(a, level, R.gw);
+  }
+  if (lr < R.L) {
+    const int roots = active_count(nb, lr);
+    if (roots > 0) k_shared_subtree<T, D><<<dim3(roots, P), 256, 0, s>>>(a, lr);
   }
   if (copy_q && perm_q != perm_k) k_copy_i32<<<gridN, 256, 0, s>>>(N, perm_k, perm_q);
   return hipGetLastError();
@@ -1797,12 +1844,12 @@ size_t reblock_ws_bytes(int H, int N, int D) { return reb_layout(H, N, D).total;
 
 hipError_t launch_reblock(bool bf16, const void* q, const void* k, int H, int N, int D,
                           int32_t* perm_q, int32_t* perm_k, float* proj_opt, int sides,
-                          bool copy_q, int iters, bool shared_deep, void* ws, hipStream_t s) {
+                          bool copy_q, int iters, int shared_blocks, void* ws, hipStream_t s) {
   if (bf16)
     return run_reblock<uint16_t, 128>(q, k, H, N, perm_q, perm_k, proj_opt, sides, copy_q,
-                                      iters, shared_deep, ws, s);
+                                      iters, shared_blocks, ws, s);
   return run_reblock<float, 64>(q, k, H, N, perm_q, perm_k, proj_opt, sides, copy_q, iters,
-                                shared_deep, ws, s);
+                                shared_blocks, ws, s);
 }
 
 }  // namespace bsa

@@ -221,6 +221,37 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ scores, 
     topk_row<false>(srow, nb, k, hist[wave], out);
 }
 
+// ------------------------------------------------------------------ list validation
+// result[0] = rows whose list is malformed (an entry outside [0, nb) or not strictly above its
+// predecessor), result[1] = the smallest such row or -1.  Reads the lists only.
+__global__ void k_check_lists_init(int32_t* __restrict__ result) {
+  if (threadIdx.x == 0) {
+    result[0] = 0;
+    result[1] = INT32_MAX;
+  }
+}
+
+// one wave per row: lane e checks entries e, e + 64, ... against their predecessors
+__global__ __launch_bounds__(256) void k_check_lists(const int32_t* __restrict__ lists, int rows,
+                                                     int nb, int k, int32_t* __restrict__ result) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int32_t* l = lists + (size_t)row * k;
+  bool bad = false;
+  for (int e = lane; e < k; e += 64) {
+    const int32_t v = l[e];
+    bad |= v < 0 || v >= nb || (e > 0 && v <= l[e - 1]);
+  }
+  if (__any(bad) && lane == 0) {
+    atomicAdd(&result[0], 1);
+    atomicMin(&result[1], row);
+  }
+}
+
+__global__ void k_check_lists_finish(int32_t* __restrict__ result) {
+  if (threadIdx.x == 0 && result[0] == 0) result[1] = -1;
+}
+
 }  // namespace
 
 hipError_t launch_block_means(bool bf16, const void* x, const int32_t* perm, int H, int N, int D,
@@ -241,6 +272,14 @@ hipError_t launch_block_scores(const float* qm, const float* km, int H, int nb, 
     k_block_scores<128><<<grid, 256, 0, s>>>(qm, km, nb, scale, scores);
   else
     k_block_scores<64><<<grid, 256, 0, s>>>(qm, km, nb, scale, scores);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_lists(const int32_t* lists, int rows, int nb, int k, int32_t* result,
+                              hipStream_t s) {
+  k_check_lists_init<<<1, 64, 0, s>>>(result);
+  k_check_lists<<<ceil_div(rows, 4), 256, 0, s>>>(lists, rows, nb, k, result);
+  k_check_lists_finish<<<1, 64, 0, s>>>(result);
   return hipGetLastError();
 }
 

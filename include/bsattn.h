@@ -78,6 +78,12 @@ typedef struct {
  * compressed branch: logit s qbar_i.kt_j + b_j.  The exact branch and the merge are unchanged.
  * bsa_prepare_kv ignores this flag. */
 #define BSA_TAIL_BLOCK 8u
+/* strict lists: before the attention kernels, every list is checked on the device (entries in
+ * [0, nb), strictly ascending) and the result kept in ws; with a malformed list the attention
+ * kernels return before reading any list entry, o and lse_opt are left unwritten, and
+ * bsa_list_status reports the first malformed row.  Without this flag the lists are trusted:
+ * a malformed list is outside the contract of the call. */
+#define BSA_CHECK_LISTS 16u
 
 const char* bsa_status_str(int32_t status);
 /* Message describing the last failed call on this thread ("" if none). */
@@ -117,20 +123,28 @@ bsa_status bsa_reblock_layout(const bsa_desc* desc, const void* q, const void* k
 
 /* (1b) Reblock with a layout choice, a power-step count per split and tree flags.
  * bsa_reblock_layout is power_iters = BSA_POWER_ITERS (8), tree_flags = 0.
- * BSA_TREE_SHARED_DEEP: from the first level whose groups hold at most 8 blocks, each group
- * takes one direction and its descendants keep cutting along the same projections (the group's
- * tokens in (projection, token id) order cut into 64-token leaves); proj_opt then repeats those
- * projections at the deeper levels.
+ * BSA_TREE_SHARED_DEEP: from the first level whose groups hold at most S blocks, each group
+ * takes one direction and its descendants keep cutting along the same projections, so the
+ * subtree is the group's tokens in (projection, token id) order cut into 64-token leaves (each
+ * in ascending token id); proj_opt then repeats those projections at the deeper levels.  S is
+ * given as BSA_TREE_SUBTREE_BLOCKS(S) in the same flags, 2 <= S <= BSA_MAX_SUBTREE_BLOCKS;
+ * without it S = BSA_DEFAULT_SUBTREE_BLOCKS.
  * Lite: [comfyui-wiki.com "Spark-H3 ...", "Benchmarks" ("基准测试")] names a lighter
  * Spark-H3-Lite that halves the reblock latency for a small fidelity loss at 20 % and 30 %
  * density and does not say how; the reading taken here is the lighter tree
- * BSA_TREE_SHARED_DEEP with BSA_POWER_ITERS_LITE (2) power steps per split, the start vector,
- * capacity cut and leaf order unchanged.  power_iters outside [1, BSA_MAX_POWER_ITERS] or an
- * unknown tree flag is BSA_E_ARG. */
+ * BSA_TREE_SHARED_DEEP | BSA_TREE_SUBTREE_BLOCKS(BSA_LITE_SUBTREE_BLOCKS) with
+ * BSA_POWER_ITERS_LITE (2) power steps per split, the start vector, capacity cut and leaf
+ * order unchanged (S and the step count are this reading's choices, not page values).
+ * power_iters outside [1, BSA_MAX_POWER_ITERS], an unknown tree flag, a subtree size outside
+ * [2, BSA_MAX_SUBTREE_BLOCKS] or a subtree size without BSA_TREE_SHARED_DEEP is BSA_E_ARG. */
 #define BSA_POWER_ITERS 8
 #define BSA_POWER_ITERS_LITE 2
 #define BSA_MAX_POWER_ITERS 64
 #define BSA_TREE_SHARED_DEEP 1u
+#define BSA_TREE_SUBTREE_BLOCKS(s) ((uint32_t)(s) << 8)
+#define BSA_DEFAULT_SUBTREE_BLOCKS 8
+#define BSA_MAX_SUBTREE_BLOCKS 64
+#define BSA_LITE_SUBTREE_BLOCKS 64
 bsa_status bsa_reblock_ex(const bsa_desc* desc, const void* q, const void* k, int32_t layout,
                           int32_t power_iters, uint32_t tree_flags, int32_t* perm_q,
                           int32_t* perm_k, float* proj_opt, void* ws, size_t ws_bytes,
@@ -257,6 +271,19 @@ size_t bsa_partition_workspace_bytes(int32_t problems, int32_t tokens);
 bsa_status bsa_reblock_from_projections(int32_t problems, int32_t tokens, const float* proj,
                                         int32_t* perm, void* ws, size_t ws_bytes,
                                         hipStream_t stream);
+
+/* Strict check of block lists (the lists argument of bsa_sparse_attn and the calls like it):
+ * lists int32 [rows][topk] on the device, read only.  result (device, 2 int32) receives the
+ * number of rows whose list has an entry outside [0, n_blocks) or an entry not above its
+ * predecessor, and the smallest such row (-1 if none).  Asynchronous on stream; BSA_E_ARG for
+ * rows or n_blocks < 1, topk outside [1, n_blocks], or a null pointer. */
+bsa_status bsa_check_lists(int32_t rows, int32_t n_blocks, int32_t topk, const int32_t* lists,
+                           int32_t* result, hipStream_t stream);
+/* The result of the list check of the last attention call on this ws that was given
+ * BSA_CHECK_LISTS (the same two values as bsa_check_lists), copied to the host array result[2].
+ * Synchronous: waits for stream.  The value is undefined if no such call wrote ws. */
+bsa_status bsa_list_status(const void* ws, size_t ws_bytes, int32_t* result,
+                           hipStream_t stream);
 
 /* Parity hook for (2): top-K of given scores.  scores: float [rows][n_blocks];
  * lists: int32 [rows][topk], each ascending; ties go to the lower block index; -0.0 equals

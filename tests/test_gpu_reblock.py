@@ -23,7 +23,8 @@ def to_dev(x, dtype):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV).to(dtype)
 
 
-def _check_layouts(q, k, perm_q, perm_k, proj, tol_proj, iters=O.POWER_ITERS, shared=False):
+def _check_layouts(q, k, perm_q, perm_k, proj, tol_proj, iters=O.POWER_ITERS, shared=False,
+                   subtree=0):
     """Replay both sides of every head; returns the summed statistics."""
     total = {"splits": 0, "mismatched_splits": 0, "max_proj_err": 0.0}
     for h in range(q.shape[0]):
@@ -34,7 +35,7 @@ def _check_layouts(q, k, perm_q, perm_k, proj, tol_proj, iters=O.POWER_ITERS, sh
             assert np.all(np.diff(perm.reshape(-1, 64), axis=1) > 0)
             st = replay_partition(O.metric_embed(X, Mo), perm,
                                   None if proj is None else proj[h, side], iters=iters,
-                                  shared_deep=shared)
+                                  shared_deep=shared, subtree_blocks=subtree or 8)
             for key in ("splits", "mismatched_splits"):
                 total[key] += st[key]
             total["max_proj_err"] = max(total["max_proj_err"], st["max_proj_err"])
@@ -54,42 +55,49 @@ def mid():
     return (wl,) + synth.make_qkv(wl, heads=[0, 1])
 
 
-# (power steps per split, one direction per small subtree): the default tree, fewer power
-# steps, and the Lite tree
-TREES = [(O.POWER_ITERS, False), (ops.BSA_POWER_ITERS_LITE, False),
-         (ops.BSA_POWER_ITERS_LITE, True)]
+# (power steps per split, one direction per shared subtree, subtree size in blocks; 0 = the
+# default 8): the default tree, fewer power steps, shared subtrees of several sizes (deeper and
+# higher than the on-chip subtree level), and the Lite preset
+TREES = [(O.POWER_ITERS, False, 0), (ops.BSA_POWER_ITERS_LITE, False, 0),
+         (ops.BSA_POWER_ITERS_LITE, True, 0), (O.POWER_ITERS, True, 2),
+         (ops.BSA_POWER_ITERS_LITE, True, 4), (O.POWER_ITERS, True, 16),
+         (ops.BSA_POWER_ITERS_LITE, True, 32),
+         (ops.BSA_POWER_ITERS_LITE, True, ops.BSA_LITE_SUBTREE_BLOCKS)]
 
 
-@pytest.mark.parametrize("iters,shared", TREES)
-def test_reblock_f32_tiny(tiny, iters, shared):
+@pytest.mark.parametrize("iters,shared,subtree", TREES)
+def test_reblock_f32_tiny(tiny, iters, shared, subtree):
     wl, q, k, v = tiny
     dt = torch.float32
     pq, pk, proj = ops.reblock(to_dev(q, dt), to_dev(k, dt), with_proj=True, power_iters=iters,
-                               shared_deep=shared)
+                               shared_deep=shared, subtree_blocks=subtree)
     pq, pk, proj = pq.cpu().numpy(), pk.cpu().numpy(), proj.cpu().numpy()
-    st = _check_layouts(q, k, pq, pk, proj, tol_proj=3e-5, iters=iters, shared=shared)
-    print("tiny replay", iters, shared, st)
+    st = _check_layouts(q, k, pq, pk, proj, tol_proj=3e-5, iters=iters, shared=shared,
+                        subtree=subtree)
+    print("tiny replay", iters, shared, subtree, st)
     rq, rk, _, _ = O.reblock_head(q[0].astype(np.float64), k[0].astype(np.float64), iters=iters,
-                                  shared_deep=shared)
+                                  shared_deep=shared, subtree_blocks=subtree or 8)
     if st["mismatched_splits"] == 0:
         assert np.array_equal(pq[0], rq) and np.array_equal(pk[0], rk)
 
 
-@pytest.mark.parametrize("iters,shared", TREES)
-def test_reblock_bf16_mid(mid, iters, shared):
+@pytest.mark.parametrize("iters,shared,subtree", TREES)
+def test_reblock_bf16_mid(mid, iters, shared, subtree):
     wl, q, k, v = mid
     dt = torch.bfloat16
     pq, pk, proj = ops.reblock(to_dev(q, dt), to_dev(k, dt), with_proj=True, power_iters=iters,
-                               shared_deep=shared)
+                               shared_deep=shared, subtree_blocks=subtree)
     pq, pk, proj = pq.cpu().numpy(), pk.cpu().numpy(), proj.cpu().numpy()
-    st = _check_layouts(q, k, pq, pk, proj, tol_proj=3e-5, iters=iters, shared=shared)
-    print("mid replay", iters, shared, st)
+    st = _check_layouts(q, k, pq, pk, proj, tol_proj=3e-5, iters=iters, shared=shared,
+                        subtree=subtree)
+    print("mid replay", iters, shared, subtree, st)
     assert st["mismatched_splits"] <= 0.02 * st["splits"]
 
 
-@pytest.mark.parametrize("n_blocks,iters,shared", [(600, 8, False), (1134, 8, False),
-                                                   (1134, 2, True)])
-def test_reblock_bf16_narrow_levels(n_blocks, iters, shared):
+@pytest.mark.parametrize("n_blocks,iters,shared,subtree", [
+    (600, 8, False, 0), (1134, 8, False, 0), (1134, 2, True, 0),
+    (1134, 2, True, 32), (1134, 2, True, ops.BSA_LITE_SUBTREE_BLOCKS)])
+def test_reblock_bf16_narrow_levels(n_blocks, iters, shared, subtree):
     """Enough blocks for the one-workgroup-per-parent levels (left-only statistics, right
     child from the parent's covariance) between the wide levels and the subtree kernel: every
     split of both sides replayed on the oracle."""
@@ -99,14 +107,15 @@ def test_reblock_bf16_narrow_levels(n_blocks, iters, shared):
     sel = np.sort(rng.choice(wl.tokens, size=64 * n_blocks, replace=False))
     q, k = q[:, sel], k[:, sel]
     pq, pk, proj = ops.reblock(to_dev(q, torch.bfloat16), to_dev(k, torch.bfloat16),
-                               with_proj=True, power_iters=iters, shared_deep=shared)
+                               with_proj=True, power_iters=iters, shared_deep=shared,
+                               subtree_blocks=subtree)
     # these levels derive each right child's statistics as n_P C_P - S_L in fp32; where a split
     # separates two children far apart relative to their spread, that subtraction amplifies
     # the fp32 rounding of C_P, so the GPU's projections sit a little further from the fp64
     # oracle's (split decisions are still held to the 1e-5 tie rule)
     st = _check_layouts(q, k, pq.cpu().numpy(), pk.cpu().numpy(), proj.cpu().numpy(),
-                        tol_proj=5e-5, iters=iters, shared=shared)
-    print("narrow replay", iters, shared, st)
+                        tol_proj=5e-5, iters=iters, shared=shared, subtree=subtree)
+    print("narrow replay", iters, shared, subtree, st)
     assert st["mismatched_splits"] <= 0.02 * st["splits"]
 
 
@@ -218,11 +227,12 @@ def test_reblock_one_side_equals_both(which, tiny, mid):
     wl, q, k, v = tiny if which == "tiny" else mid
     dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
     qd, kd = to_dev(q, dt), to_dev(k, dt)
-    for iters, shared in TREES:
-        pq, pk, proj = ops.reblock(qd, kd, with_proj=True, power_iters=iters, shared_deep=shared)
+    for iters, shared, subtree in TREES:
+        pq, pk, proj = ops.reblock(qd, kd, with_proj=True, power_iters=iters, shared_deep=shared,
+                                   subtree_blocks=subtree)
         for side, ref in ((0, pq), (1, pk)):
             perm, pr = ops.reblock_side(qd, kd, side, power_iters=iters, with_proj=True,
-                                        shared_deep=shared)
+                                        shared_deep=shared, subtree_blocks=subtree)
             assert torch.equal(perm, ref), (side, iters)
             assert torch.equal(pr[:, side], proj[:, side])
             assert torch.all(pr[:, 1 - side] == 0).item()

@@ -387,7 +387,7 @@ def test_option_paths_are_deterministic(mid):
     perms = (torch.from_numpy(pq).to(DEV), torch.from_numpy(pk).to(DEV),
              torch.from_numpy(lists).to(DEV))
     for run in (lambda: ops.reblock(qd, kd, power_iters=ops.BSA_POWER_ITERS_LITE,
-                                    shared_deep=True),
+                                    shared_deep=True, subtree_blocks=ops.BSA_LITE_SUBTREE_BLOCKS),
                 lambda: (ops.sparse_attn(qd, kd, vd, *perms, flags=ops.BSA_TAIL_BLOCK),)):
         a, b = run(), run()
         assert all(torch.equal(x, y) for x, y in zip(a, b))
@@ -429,3 +429,43 @@ def test_select_parity(mid, tiny):
                     kth = np.sort(S[i])[::-1][K - 1]
                     for j in a ^ b:
                         assert abs(S[i, j] - kth) <= 1e-5
+
+
+# ------------------------------------------------------------------- strict list checks
+
+def test_check_lists_finds_malformed_rows(mid):
+    """bsa_check_lists on valid lists reports none; planted defects (an entry equal to nb, a
+    negative entry, a repeated entry, two entries out of order) are each counted once, and
+    the smallest defective row is reported.  Malformed lists go to the checker only."""
+    wl, q, k, v, pq, pk, lists = mid
+    nb = wl.n_blocks
+    good = torch.from_numpy(lists).to(DEV)
+    assert ops.check_lists(good, nb) == (0, -1)
+    H, R, K = lists.shape
+    for row, fix in ((5, lambda r: r.__setitem__(-1, nb)),
+                     (R + 17, lambda r: r.__setitem__(0, -1)),
+                     (3, lambda r: r.__setitem__(2, r[1])),
+                     (R - 1, lambda r: r.__setitem__(slice(0, 2), r[1::-1].copy()))):
+        bad = lists.copy().reshape(H * R, K)
+        fix(bad[row])
+        assert ops.check_lists(torch.from_numpy(bad).to(DEV), nb) == (1, row)
+    bad = lists.copy().reshape(H * R, K)
+    for row in (40, 7, R + 3):
+        bad[row, -1] = nb + row
+    assert ops.check_lists(torch.from_numpy(bad).to(DEV), nb) == (3, 7)
+
+
+def test_attention_with_list_check_on_valid_lists(mid):
+    """With BSA_CHECK_LISTS and valid lists the output is bit-identical to the unchecked call
+    and the workspace's list status reports no malformed row (bf16 and the block-level tail)."""
+    wl, q, k, v, pq, pk, lists = mid
+    dt = torch.bfloat16
+    qd, kd, vd = to_dev(q, dt), to_dev(k, dt), to_dev(v, dt)
+    perms = (torch.from_numpy(pq).to(DEV), torch.from_numpy(pk).to(DEV),
+             torch.from_numpy(lists).to(DEV))
+    ws = ops.workspace(ops.desc_for(qd), qd.device)
+    for flags in (0, ops.BSA_TAIL_BLOCK):
+        ref = ops.sparse_attn(qd, kd, vd, *perms, flags=flags, ws=ws)
+        got = ops.sparse_attn(qd, kd, vd, *perms, flags=flags | ops.BSA_CHECK_LISTS, ws=ws)
+        assert ops.list_status(ws) == (0, -1)
+        assert torch.equal(ref, got)

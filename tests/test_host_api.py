@@ -86,7 +86,7 @@ def test_sparse_attn_argument_errors(L):
         assert L.bsa_sparse_attn(desc(), *args, k, 0, 0.0, FAKE, None, FAKE, big,
                                  None) == _lib.BSA_E_ARG
     # unknown and exclusive flags (BSA_TAIL_BLOCK = 8 combines with the others)
-    for fl in (16, 1 << 31, 6, 6 | _lib.BSA_TAIL_BLOCK):
+    for fl in (32, 1 << 31, 6, 6 | _lib.BSA_TAIL_BLOCK):
         assert L.bsa_sparse_attn(desc(), *args, 4, fl, 0.0, FAKE, None, FAKE, big,
                                  None) == _lib.BSA_E_ARG
     # bad scale
@@ -112,7 +112,7 @@ def test_mixed_sequence_argument_errors(L):
         assert call(n) == _lib.BSA_E_ARG
     assert call(10, ctx=[FAKE2, None, FAKE2]) == _lib.BSA_E_ARG
     assert call(10, o_ctx=None) == _lib.BSA_E_ARG
-    assert call(10, flags=16) == _lib.BSA_E_ARG
+    assert call(10, flags=32) == _lib.BSA_E_ARG
     # the context tiles need room beyond the plain layer's workspace once they outgrow it
     plain = L.bsa_workspace_bytes(desc())
     assert L.bsa_workspace_bytes_ctx(desc(), 0) == plain
@@ -164,10 +164,19 @@ def test_reblock_and_hook_argument_errors(L):
                               None) == _lib.BSA_E_ARG
     assert L.bsa_reblock_side(desc(), FAKE, FAKE, 1, 8, 1, FAKE, None, FAKE, 8,
                               None) == _lib.BSA_E_WORKSPACE
-    # power steps per split outside [1, 64]; unknown tree flags
-    for it, fl in ((0, 0), (-1, 0), (65, 0), (8, 2), (2, 1 << 31)):
+    # power steps per split outside [1, 64]; unknown tree flags; a shared subtree size outside
+    # [2, 64] or without the shared-subtree flag
+    for it, fl in ((0, 0), (-1, 0), (65, 0), (8, 2), (2, 1 << 31), (2, 1 | (1 << 8)),
+                   (2, 1 | (65 << 8)), (2, 1 | (255 << 8)), (2, 32 << 8)):
         assert L.bsa_reblock_ex(desc(), FAKE, FAKE, 0, it, fl, FAKE, FAKE2, None, FAKE, big,
                                 None) == _lib.BSA_E_ARG
+        assert L.bsa_reblock_side(desc(), FAKE, FAKE, 0, it, fl, FAKE, None, FAKE, big,
+                                  None) == _lib.BSA_E_ARG
+    # valid sizes pass the flag checks and stop at the workspace check
+    for fl in (1, 1 | (2 << 8), 1 | (32 << 8), 1 | (64 << 8)):
+        assert L.bsa_reblock_ex(desc(), FAKE, FAKE, 0, 2, fl, FAKE, FAKE2, None, FAKE, 8,
+                                None) == _lib.BSA_E_WORKSPACE
+    assert _lib.tree_flags(True, _lib.BSA_LITE_SUBTREE_BLOCKS) == 1 | (64 << 8)
     # layout choice: unknown value, then the key-reuse layout, whose one buffer may serve both
     for bad in (-1, 2):
         assert L.bsa_reblock_layout(desc(), FAKE, FAKE, bad, FAKE, FAKE2, None, FAKE, big,
@@ -212,3 +221,23 @@ def test_architecture_is_checked(L, monkeypatch):
 def test_status_strings(L):
     for code in (0, -1, -2, -3, -4):
         assert L.bsa_status_str(code)
+
+
+def test_list_check_argument_errors(L):
+    assert L.bsa_check_lists(0, 10, 1, FAKE, FAKE, None) == _lib.BSA_E_ARG
+    assert L.bsa_check_lists(4, 0, 1, FAKE, FAKE, None) == _lib.BSA_E_ARG
+    assert L.bsa_check_lists(4, 10, 0, FAKE, FAKE, None) == _lib.BSA_E_ARG
+    assert L.bsa_check_lists(4, 10, 11, FAKE, FAKE, None) == _lib.BSA_E_ARG
+    assert L.bsa_check_lists(4, 10, 3, None, FAKE, None) == _lib.BSA_E_ARG
+    assert L.bsa_check_lists(4, 10, 3, FAKE, None, None) == _lib.BSA_E_ARG
+    out = (ctypes.c_int32 * 2)()
+    assert L.bsa_list_status(None, 1 << 20, out, None) == _lib.BSA_E_ARG
+    assert L.bsa_list_status(FAKE, 4, out, None) == _lib.BSA_E_WORKSPACE
+    assert L.bsa_list_status(FAKE, 1 << 20, None, None) == _lib.BSA_E_ARG
+    # the strict-list flag is a known flag: the call gets past the flag check to the workspace
+    st = L.bsa_sparse_attn(desc(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, _lib.BSA_CHECK_LISTS,
+                           0.0, FAKE, None, FAKE, 8, None)
+    assert st == _lib.BSA_E_WORKSPACE
+    st = L.bsa_sparse_attn(desc(), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 32, 0.0, FAKE, None,
+                           FAKE, 1 << 40, None)
+    assert st == _lib.BSA_E_ARG

@@ -258,7 +258,7 @@ def _groups_at(nb, level):
     return groups
 
 
-@pytest.mark.parametrize("subtree_blocks", [2, 4, 8, 32])
+@pytest.mark.parametrize("subtree_blocks", [2, 4, 8, 32, 64])
 def test_lite_tree_cuts_each_small_subtree_along_one_direction(tiny_inputs, subtree_blocks):
     """Lite tree (shared_deep): above the first level whose groups hold at most
     `subtree_blocks` blocks it is the default tree; each group of that level is its tokens
