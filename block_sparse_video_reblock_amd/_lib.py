@@ -58,6 +58,9 @@ _SIGS = {
                                     ctypes.c_size_t, _P]),
     "bsa_summaries": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), _P, _P, _P, _P, ctypes.c_uint32,
                                        ctypes.c_float, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "bsa_summaries_noalloc_bytes": (ctypes.c_size_t, [ctypes.POINTER(BsaDesc)]),
+    "bsa_summaries_noalloc": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), _P, _P, _P, _P,
+                                               ctypes.c_uint32, ctypes.c_float, _P, _P, _P, _P]),
     "bsa_workspace_bytes_ctx": (ctypes.c_size_t, [ctypes.POINTER(BsaDesc), ctypes.c_int32]),
     "bsa_sparse_attn_ctx": (ctypes.c_int32, [ctypes.POINTER(BsaDesc), ctypes.c_int32, _P, _P, _P,
                                              _P, _P, _P, _P, _P, _P, ctypes.c_int32,
@@ -322,6 +325,23 @@ def summaries(q, k, v, perm_k, flags=0, scale=0.0, ws=None):
                               _dev_ptr(v, q.dtype), _dev_ptr(perm_k, torch.int32), int(flags),
                               float(scale), _dev_ptr(kt), _dev_ptr(vt), _dev_ptr(bias),
                               _dev_ptr(ws), ws.numel(), _stream()))
+    return kt, vt, bias
+
+
+def summaries_noalloc(q, k, v, perm_k, flags=0, scale=0.0):
+    """bsa_summaries without a workspace (the library's static device scratch):
+    fp32 (kt [H][nb][D], vt [H][nb][D], bias [H][nb])."""
+    torch = _torch()
+    d = desc_for(q)
+    H, N, D = q.shape
+    nb = N // BLOCK
+    kt = torch.empty(H, nb, D, dtype=torch.float32, device=q.device)
+    vt = torch.empty_like(kt)
+    bias = torch.empty(H, nb, dtype=torch.float32, device=q.device)
+    check(lib().bsa_summaries_noalloc(ctypes.byref(d), _dev_ptr(q, q.dtype), _dev_ptr(k, q.dtype),
+                                      _dev_ptr(v, q.dtype), _dev_ptr(perm_k, torch.int32),
+                                      int(flags), float(scale), _dev_ptr(kt), _dev_ptr(vt),
+                                      _dev_ptr(bias), _stream()))
     return kt, vt, bias
 
 

@@ -15,6 +15,9 @@
 #include "internal.h"
 #include "tree.h"
 
+static_assert(bsa::kNoallocScratchBytes == BSA_NOALLOC_SCRATCH_BYTES,
+              "the header and the library disagree on the static scratch size");
+
 namespace {
 
 thread_local char g_err[320] = "";
@@ -356,6 +359,39 @@ bsa_status bsa_summaries(const bsa_desc* d, const void* q, const void* k, const 
   return hip_status(run_summaries(d, L, ws, q, k, v, perm_k, (flags & BSA_MEANPOOL) != 0,
                                   resolve_scale(d, scale), kt, vt, bias, d->tokens / BSA_BLOCK,
                                   false, stream),
+                    "summaries launch");
+}
+
+size_t bsa_summaries_noalloc_bytes(const bsa_desc* d) {
+  if (check_desc(d) != BSA_OK) return 0;
+  const AttnWs L = attn_layout(d);
+  return L.anchor + align_up(size_t(d->heads) * d->head_dim * 4);
+}
+
+bsa_status bsa_summaries_noalloc(const bsa_desc* d, const void* q, const void* k, const void* v,
+                                 const int32_t* perm_k, uint32_t flags, float scale, float* kt,
+                                 float* vt, float* bias, hipStream_t stream) {
+  bsa_status st = check_desc(d);
+  if (st != BSA_OK) return st;
+  if (!q || !k || !v || !perm_k || !kt || !vt || !bias)
+    return fail(BSA_E_ARG, "null tensor pointer");
+  if (flags & ~uint32_t(BSA_MEANPOOL)) return fail(BSA_E_ARG, "unknown flags 0x%x", flags);
+  if (!(std::isfinite(scale) && scale >= 0.f)) return fail(BSA_E_ARG, "bad scale %g", scale);
+  // the summaries read only the anchor's partial sums and the anchor from the workspace, which
+  // attn_layout places first; that prefix has to fit in the static scratch
+  const size_t need = bsa_summaries_noalloc_bytes(d);
+  if (need > BSA_NOALLOC_SCRATCH_BYTES)
+    return fail(BSA_E_ARG, "heads %d x tokens %d need %zu bytes of scratch, more than the %zu "
+                "of the static scratch", d->heads, d->tokens, need,
+                size_t(BSA_NOALLOC_SCRATCH_BYTES));
+  st = check_device();
+  if (st != BSA_OK) return st;
+  void* ws = nullptr;
+  hipError_t e = bsa::noalloc_scratch(&ws);
+  if (e != hipSuccess) return hip_status(e, "static scratch lookup");
+  return hip_status(run_summaries(d, attn_layout(d), ws, q, k, v, perm_k,
+                                  (flags & BSA_MEANPOOL) != 0, resolve_scale(d, scale), kt, vt,
+                                  bias, d->tokens / BSA_BLOCK, false, stream),
                     "summaries launch");
 }
 

@@ -88,6 +88,13 @@ hipError_t launch_topk(const float* scores, int rows, int nb, int k, int32_t* li
 hipError_t launch_check_lists(const int32_t* lists, int rows, int nb, int k, int32_t* result,
                               hipStream_t s);
 
+// ------------------------------------------------------------- allocation-free scratch
+// Size of the device-resident scratch array behind bsa_summaries_noalloc (one per device).
+constexpr size_t kNoallocScratchBytes = size_t(16) << 20;
+// The calling thread's current device's copy of that array (its address looked up once per
+// device with hipGetSymbolAddress).
+hipError_t noalloc_scratch(void** out);
+
 // ------------------------------------------------------------------ reblock (stage 1)
 size_t reblock_ws_bytes(int H, int N, int D);
 // sides: which trees to build (queries under M_K into perm_q, keys under M_Q into perm_k);

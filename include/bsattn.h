@@ -248,6 +248,24 @@ bsa_status bsa_summaries(const bsa_desc* desc, const void* q, const void* k, con
                          float* kt, float* vt, float* bias,
                          void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate (code under HIP graph capture that must not call
+ * hipMalloc, tight serving loops, harnesses that forbid allocation): bsa_summaries without a
+ * workspace argument.  Its scratch (the anchor's partial column sums) is a device-resident
+ * array inside the library, BSA_NOALLOC_SCRATCH_BYTES bytes per GPU, held from the first call
+ * on a device until the process ends; the call allocates nothing.  Arguments, outputs and
+ * results are those of bsa_summaries (bit-identical: the same kernels).
+ * Limits: the descriptor must need at most BSA_NOALLOC_SCRATCH_BYTES bytes of scratch
+ * (bsa_summaries_noalloc_bytes; 24 heads of up to 524,288 tokens at head_dim 128 fit), else
+ * BSA_E_ARG before any HIP call.  All calls on one GPU share its one array: calls that
+ * overlap in time on one GPU (two streams, two threads) race and must be serialised by the
+ * caller; consecutive calls on one stream are safe. */
+#define BSA_NOALLOC_SCRATCH_BYTES (16u << 20)
+size_t bsa_summaries_noalloc_bytes(const bsa_desc* desc);
+bsa_status bsa_summaries_noalloc(const bsa_desc* desc, const void* q, const void* k,
+                                 const void* v, const int32_t* perm_k, uint32_t flags,
+                                 float scale, float* kt, float* vt, float* bias,
+                                 hipStream_t stream);
+
 /* Fixed-tile layout: the positional baseline that (1) replaces.  [comfyui-wiki.com
  * "Spark-H3 ...", "What Spark-Attn changes": Reblock takes the place of fixed spatiotemporal
  * tiles; comfy.icu page, "What it's doing under the hood": recall against fixed blocks]

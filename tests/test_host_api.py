@@ -223,6 +223,22 @@ def test_status_strings(L):
         assert L.bsa_status_str(code)
 
 
+def test_summaries_noalloc_rejects_sizes_beyond_its_scratch(L):
+    """The allocation-free summaries call checks its fixed scratch size on the host: within the
+    limit it reports the bytes it needs, beyond it BSA_E_ARG before any HIP call."""
+    limit = 16 << 20
+    need = L.bsa_summaries_noalloc_bytes(desc(h=24, n=72576))
+    assert 0 < need <= limit
+    assert L.bsa_summaries_noalloc_bytes(desc(h=24, n=1 << 19)) <= limit
+    big = _lib.BsaDesc(64, 1 << 19, 128, _lib.BSA_BF16)
+    assert L.bsa_summaries_noalloc_bytes(ctypes.byref(big)) > limit
+    st = L.bsa_summaries_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, 0, 0.0, FAKE, FAKE,
+                                 FAKE, None)
+    assert st == _lib.BSA_E_ARG and b"scratch" in L.bsa_last_error()
+    st = L.bsa_summaries_noalloc(desc(), FAKE, FAKE, FAKE, FAKE, 2, 0.0, FAKE, FAKE, FAKE, None)
+    assert st == _lib.BSA_E_ARG
+
+
 def test_list_check_argument_errors(L):
     assert L.bsa_check_lists(0, 10, 1, FAKE, FAKE, None) == _lib.BSA_E_ARG
     assert L.bsa_check_lists(4, 0, 1, FAKE, FAKE, None) == _lib.BSA_E_ARG
