@@ -394,16 +394,22 @@ def main_headline(args, ops, synth, torch, np):
     elt = 2 if wl.dtype == "bf16" else 4
     x_bytes = H * N * D * elt
     sides = 1 if args.layout == "q_reuse_k" else 2
-    # the Lite tree reads each shared subtree once, from its root level on
-    rb_root = on_chip_root_level(nb)
     if args.lite:
-        rb_root = min(rb_root, on_chip_root_level(nb, lay.subtree_blocks))
-    rb_bytes, rb_plain = reblock_bytes(nb, x_bytes, sides, rb_root)
+        # the Lite tree stops at the shared root level, whose groups each take a statistics and
+        # a projection pass and are then sorted on chip
+        lr = on_chip_root_level(nb, lay.subtree_blocks)
+        rb_bytes = sides * x_bytes * (2 + 2 * lr + 2)
+        rb_plain = reblock_bytes(nb, x_bytes, sides, on_chip_root_level(nb))[1]
+    else:
+        rb_bytes, rb_plain = reblock_bytes(nb, x_bytes, sides, on_chip_root_level(nb))
     hbm = {
         "reblock": {"bytes": rb_bytes, "plain_passes_bytes": rb_plain,
-                    "passes": "moments, norms, a statistics and a projection pass per tree "
-                              "level until the groups fit on chip, and one pass for the "
-                              "subtrees held on chip, over " +
+                    "passes": ("moments, norms, a statistics and a projection pass per tree "
+                               "level above the shared root, and a statistics and a "
+                               "projection pass for the shared subtrees" if args.lite else
+                               "moments, norms, a statistics and a projection pass per tree "
+                               "level until the groups fit on chip, and one pass for the "
+                               "subtrees held on chip") + ", over " +
                               ("K" if sides == 1 else "Q and K") +
                               " (plain_passes_bytes: two passes for every level)"},
         "select": {"bytes": 2 * x_bytes + H * nb * nb * 4, "passes": "Q, K once; scores"},

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -95,7 +96,7 @@ float resolve_scale(const bsa_desc* d, float scale) {
 // ----------------------------------------------------------------- workspace layouts
 struct AttnWs {
   size_t status, anchor_partial, anchor, kt, vt, bias, ktsw, vtsw, ksw, vsw, qbar, tbits, tail_o,
-      tail_lse, ctsw, cvsw, total;
+      tail_lse, ctsw, cvsw, pop, walk, total;
 };
 
 AttnWs attn_layout(const bsa_desc* d, int n_ctx = 0) {
@@ -130,6 +131,12 @@ AttnWs attn_layout(const bsa_desc* d, int n_ctx = 0) {
     const size_t nc = bsa::ceil_div(n_ctx, 64);
     w.ctsw = take(H * nc * 64 * D * 2);
     w.cvsw = take(H * nc * 64 * D * 2);
+  }
+  // bf16 path: the exact-tile walk order of sparse lists (selection counts and reordered
+  // lists, for the longest list that gets one)
+  if (is_bf16(d)) {
+    w.pop = take(H * nb * 4);
+    w.walk = take(H * nb * std::min<size_t>(nb, 256) * 4);
   }
   w.total = off;
   return w;
@@ -490,6 +497,14 @@ hipError_t do_attend(const bsa_desc* d, const AttnWs& L, void* ws, const void* q
     if (e != hipSuccess) return e;
   }
   if (is_bf16(d)) {
+    if (exact_on && bsa::list_walk_applies(nb, topk)) {
+      int32_t* walk = reinterpret_cast<int32_t*>(at(ws, L.walk));
+      hipError_t e = bsa::launch_list_walk(lists, d->heads, nb, topk,
+                                           reinterpret_cast<int32_t*>(at(ws, L.pop)), walk,
+                                           stream);
+      if (e != hipSuccess) return e;
+      a.walk = walk;
+    }
     a.ksw = at(ws, L.ksw);
     a.vsw = at(ws, L.vsw);
     a.ktsw = at(ws, L.ktsw);

@@ -22,6 +22,8 @@
 // v_mfma_f32_32x32x16_bf16: the accumulator layout of S^T is then directly the B operand of
 // O^T = V^T P^T.  K/V tiles arrive pre-swizzled (see summaries.hip) so that every wave load
 // is 1 KiB contiguous and no LDS transpose is needed.
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -312,6 +314,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(QSide cs, QSide vs, int wg
         l_run[n] = row_sum_bf16(pb[1][n], row_sum_bf16(pb[0][n], l_run[n]));
       };
       uint4 vr[8];
+      const __amdgpu_buffer_rsrc_t rv =
+          __builtin_amdgcn_make_buffer_rsrc((void*)vb, 0, 1024 * 16, kBufferDword3);
       // O^T[d chunk a][n] += V^T[a][key chunk c] P^T[c][n]
       auto values = [&](int n) {
 #pragma unroll
@@ -329,7 +333,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(QSide cs, QSide vs, int wg
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) vr[a * 2 + cc] = vb[(a * 4 + 2 * hh + cc) * 64 + lane];
+        for (int cc = 0; cc < 2; ++cc)
+          vr[a * 2 + cc] = __builtin_bit_cast(
+              uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, lane * 16,
+                                                           (a * 4 + 2 * hh + cc) * 1024, 0));
       probs(0, s0, m0);
       // (an empty use keeps the exponentials of rows 0..31 ahead of the branch below, in the
       // block of the score products they overlap)
@@ -794,7 +801,91 @@ __global__ __launch_bounds__(256, 1) void k_tail_block_bf16(
   }
 }
 
+// ------------------------------------------------------------- exact-tile walk order
+// The order in which a query block walks its selected key blocks changes only the rounding of
+// its softmax sums.  Walking the blocks that many query blocks of the head selected first makes
+// the workgroups that run together on an XCD request those shared tiles close in time, so more
+// of them come from L2: each list is reordered by (selection count of the key block, highest
+// first; key block index).
+
+__global__ void k_zero_i32(size_t n, int32_t* __restrict__ out) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+    out[i] = 0;
+}
+
+// pop[h][j] = number of lists of head h that contain key block j.  Grid (chunks, H): each
+// workgroup counts its chunk of the head's entries in LDS, then adds its nonzero counts.
+constexpr int kPopMaxBlocks = 8192;  // nb of the largest sequence (LDS histogram)
+__global__ __launch_bounds__(256) void k_list_popularity(const int32_t* __restrict__ lists,
+                                                         int nb, int topk,
+                                                         int32_t* __restrict__ pop) {
+  __shared__ int hist[kPopMaxBlocks];
+  const int h = blockIdx.y;
+  for (int j = threadIdx.x; j < nb; j += 256) hist[j] = 0;
+  __syncthreads();
+  const size_t n = (size_t)nb * topk;
+  const size_t per = (n + gridDim.x - 1) / gridDim.x;
+  const size_t e0 = blockIdx.x * per, e1 = min(n, e0 + per);
+  const int32_t* l = lists + (size_t)h * n;
+  for (size_t e = e0 + threadIdx.x; e < e1; e += 256) {
+    const int j = l[e];
+    if (j >= 0 && j < nb) atomicAdd(&hist[j], 1);
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < nb; j += 256)
+    if (hist[j] != 0) atomicAdd(&pop[(size_t)h * nb + j], hist[j]);
+}
+
+// one 64-thread workgroup per list: sort its entries by (nb - pop, index) in LDS
+constexpr int kWalkMax = 256;  // longest list that gets the popularity order
+__global__ __launch_bounds__(64) void k_list_walk(const int32_t* __restrict__ lists,
+                                                  const int32_t* __restrict__ pop, int nb,
+                                                  int topk, int32_t* __restrict__ walk) {
+  __shared__ uint32_t v[kWalkMax];
+  const size_t row = blockIdx.x;
+  const int h = int(row / (size_t)nb);
+  const int32_t* l = lists + row * topk;
+  int n2 = 1;
+  while (n2 < topk) n2 <<= 1;
+  for (int t = threadIdx.x; t < n2; t += 64) {
+    uint32_t key = 0xFFFFFFFFu;
+    if (t < topk) {
+      const int j = l[t];
+      const int c = (j >= 0 && j < nb) ? pop[(size_t)h * nb + j] : 0;
+      key = (uint32_t(nb - c) << 13) | uint32_t(j & 8191);
+    }
+    v[t] = key;
+  }
+  __syncthreads();
+  for (int k = 2; k <= n2; k <<= 1)
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int t = threadIdx.x; t < (n2 >> 1); t += 64) {
+        const int i = 2 * t - (t & (j - 1)), ip = i + j;
+        const uint32_t x = v[i], y = v[ip];
+        if ((x > y) == ((i & k) == 0)) {
+          v[i] = y;
+          v[ip] = x;
+        }
+      }
+      __syncthreads();
+    }
+  for (int t = threadIdx.x; t < topk; t += 64) walk[row * topk + t] = int32_t(v[t] & 8191u);
+}
+
 }  // namespace
+
+hipError_t launch_list_walk(const int32_t* lists, int H, int nb, int topk, int32_t* pop,
+                            int32_t* walk, hipStream_t s) {
+  const size_t np = (size_t)H * nb;
+  k_zero_i32<<<(unsigned)std::min<size_t>((np + 255) / 256, 1024), 256, 0, s>>>(np, pop);
+  const size_t n = (size_t)nb * topk;
+  k_list_popularity<<<dim3((unsigned)std::min<size_t>((n + 4095) / 4096, 32), H), 256, 0, s>>>(
+      lists, nb, topk, pop);
+  k_list_walk<<<(unsigned)np, 64, 0, s>>>(lists, pop, nb, topk, walk);
+  return hipGetLastError();
+}
+
+bool list_walk_applies(int nb, int topk) { return topk <= kWalkMax && 2 * topk <= nb; }
 
 hipError_t launch_tail_block_bf16(const AttnLaunch& a, const float* qbar, uint32_t* bits,
                                   float* tail_o, float* tail_lse, hipStream_t s) {
@@ -833,11 +924,12 @@ hipError_t launch_attn_bf16(const AttnLaunch& a, hipStream_t s) {
   const int wg_c = a.H * nt_c;
   const bool biased = a.n_comp > 0 || (nt_c > 0 && a.ctx_n_comp > 0);
   const size_t dyn = biased ? (size_t)(nt_s + (nt_c > 0 ? 2 : 0)) * 64 * sizeof(float) : 0;
+  const int32_t* lists = a.walk != nullptr ? a.walk : a.lists;
   if (wg_c > 0)
-    k_attn_bf16<true><<<wg_c + a.H * a.nb, 256, dyn, s>>>(cs, vs, wg_c, ks, a.lists, a.H,
+    k_attn_bf16<true><<<wg_c + a.H * a.nb, 256, dyn, s>>>(cs, vs, wg_c, ks, lists, a.H,
                                                           a.scale * kLog2e);
   else
-    k_attn_bf16<false><<<a.H * a.nb, 256, dyn, s>>>(cs, vs, 0, ks, a.lists, a.H,
+    k_attn_bf16<false><<<a.H * a.nb, 256, dyn, s>>>(cs, vs, 0, ks, lists, a.H,
                                                     a.scale * kLog2e);
   return hipGetLastError();
 }

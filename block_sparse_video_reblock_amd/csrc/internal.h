@@ -65,8 +65,15 @@ struct AttnLaunch {
   // result of a list check run before the launch (see launch_check_lists), or null: with a
   // malformed list the attention kernels return at once, before any list entry is read
   const int32_t* list_status;
+  // the lists in exact-tile walk order (launch_list_walk), or null to walk `lists` as given
+  const int32_t* walk;
 };
 hipError_t launch_attn_bf16(const AttnLaunch& a, hipStream_t s);
+// walk[h][i][.] = lists[h][i][.] ordered by (selection count of the key block among the head's
+// lists, highest first; index); pop [H][nb] is scratch.  Only where list_walk_applies.
+hipError_t launch_list_walk(const int32_t* lists, int H, int nb, int topk, int32_t* pop,
+                            int32_t* walk, hipStream_t s);
+bool list_walk_applies(int nb, int topk);
 hipError_t launch_attn_f32(const AttnLaunch& a, hipStream_t s);
 // Block-level compressed branch (bf16): from the pooled queries qbar [H][nb][D] (fp32), the
 // lists and the summary tiles of the launch `a` (n_comp ignored), the per-block state

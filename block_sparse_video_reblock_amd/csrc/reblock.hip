@@ -1371,13 +1371,13 @@ BSA_DEV void split_group(const ProblemArgs& a, int p, int level, int g, int b0, 
 }
 
 // grid (parents, P): one workgroup per active group gp of level - 1 (lists[level - 1]); it
-// splits both children of gp at `level`.  Only the left child's statistics are accumulated
-// (relative to the parent mean); the right child's follow as n_P C_P - S_L with C_P the
-// parent's centred covariance (stored by the level above in cov_prev) and its sum of
-// (y - mu_P) as minus the left child's.  Each child's centred covariance goes to cov_cur for
-// the level below.  Covariance slots: [P][cov_g][D * D] in register-dump order.
+// splits both children of gp at `level`.  Each child's statistics are accumulated from its own
+// tokens: the left child's relative to the parent's mean, the right child's relative to its
+// own mean, known from the left child's sum (sum_R (y - mu_P) = -sum_L (y - mu_P)).  (Deriving
+// the right child as n_P C_P - S_L instead would carry the parent's fp32 rounding, amplified
+// by n_P, into a child whose spread is small next to its distance from mu_P.)
 template <typename T, int D>
-__global__ __launch_bounds__(256, 2) void k_subtree_pair(ProblemArgs a, int level, int cov_g) {
+__global__ __launch_bounds__(256, 2) void k_subtree_pair(ProblemArgs a, int level) {
   __shared__ StageLds<D, 2> st;
   __shared__ DirLds L;
   __shared__ float dsl[D];
@@ -1395,9 +1395,6 @@ __global__ __launch_bounds__(256, 2) void k_subtree_pair(ProblemArgs a, int leve
   const int32_t* pos = problem_pos(a, p);
   const float* inv_n = a.inv_n + (size_t)p * a.N;
   const float ysc = a.yscale[2 * p], inv_s2 = a.yscale[2 * p + 1];
-  float* cov_l = a.cov_cur + ((size_t)p * cov_g + gl) * D * D;
-  float* cov_r = a.cov_cur + ((size_t)p * cov_g + gr) * D * D;
-  const float* cov_p = a.cov_prev + ((size_t)p * cov_g + gp) * D * D;
   const float shv = threadIdx.x < D ? group_mean<D>(a, p, level - 1, gp)[threadIdx.x] : 0.f;
   const float yl = first_candidate<T, D>(X, pos, inv_n, lb0 * kBlk);
   const float yr = first_candidate<T, D>(X, pos, inv_n, rb0 * kBlk);
@@ -1412,29 +1409,21 @@ __global__ __launch_bounds__(256, 2) void k_subtree_pair(ProblemArgs a, int leve
     reduce_dpart<D>(dpart, L.red, L.mu);
     sym_to_regs<D>(sacc, inv_s2, st, acc);  // S_L, unscaled
   }
-  // keep S_L and its sum for the right child: S_L in the right child's covariance slot (each
-  // thread later reads back exactly the elements it wrote)
+  if (threadIdx.x < D) dsl[threadIdx.x] = L.mu[threadIdx.x];
+  __syncthreads();
+  if (lm >= 2) split_group<T, D>(a, p, level, gl, lb0, lm, acc, 1.f, L, nullptr, hist, sm, yl);
   if (rm >= 2) {
-    store_acc<D>(cov_r, acc);
-    if (threadIdx.x < D) dsl[threadIdx.x] = L.mu[threadIdx.x];
-  }
-  if (lm >= 2) split_group<T, D>(a, p, level, gl, lb0, lm, acc, 1.f, L, cov_l, hist, sm, yl);
-  if (rm >= 2) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const float np = float(pm * kBlk);
+    const float shr =
+        threadIdx.x < D ? shv - dsl[threadIdx.x] * (1.f / float(rm * kBlk)) : 0.f;
+    SymAcc<D> sacc;
+    sacc.zero();
+    float dpart[D / 8];
 #pragma unroll
-    for (int t = 0; t < Cov<D>::TILES; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const size_t e = ((w * Cov<D>::TILES + t) * 16 + r) * 64 + lane;
-        acc[t][r] = np * cov_p[e] - cov_r[e];
-      }
-    if (threadIdx.x < D) {
-      L.shift[threadIdx.x] = group_mean<D>(a, p, level - 1, gp)[threadIdx.x];
-      L.mu[threadIdx.x] = -dsl[threadIdx.x];
-    }
-    __syncthreads();
-    split_group<T, D>(a, p, level, gr, rb0, rm, acc, 1.f, L, cov_r, hist, sm, yr);
+    for (int e = 0; e < D / 8; ++e) dpart[e] = 0.f;
+    sym_stats_range<T, D, true>(X, pos, inv_n, rb0, rb0 + rm, L.shift, shr, ysc, st, sacc, dpart);
+    reduce_dpart<D>(dpart, L.red, L.mu);
+    sym_to_regs<D>(sacc, inv_s2, st, acc);
+    split_group<T, D>(a, p, level, gr, rb0, rm, acc, 1.f, L, nullptr, hist, sm, yr);
   }
 }
 
@@ -1659,13 +1648,12 @@ RebLayout reb_layout(int H, int N, int D) {
   r.wdir = take(P * r.G * D * 4);
   r.partial = take(P * kPartialSlots * (size_t)(D * D + D) * 4);
   r.lists = take((size_t)std::max(r.L, 1) * r.G * 4);
-  // covariance slots per problem: the groups of the deepest level that stores them (the last
-  // wide level or the last one-workgroup-per-parent level)
+  // covariance slots per problem: the groups of the deepest wide level (the wide levels derive
+  // each right child's statistics from its parent's centred covariance)
   int last = 0;
   for (int level = 0; level < r.L; ++level) {
-    const int slices = wide_slices(level, (int)nb);
-    if (slices > 1 || ceil_div((int)nb, 1 << level) > kSmallBlocks) last = level;
-    else break;
+    if (wide_slices(level, (int)nb) <= 1 || ceil_div((int)nb, 1 << level) <= kSmallBlocks) break;
+    last = level;
   }
   r.gw = 1 << last;
   r.cov0 = take(P * r.gw * (size_t)D * D * 4);
@@ -1773,8 +1761,7 @@ hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm
     k_wide_proj<T, D><<<dim3(nb, P), 256, 0, s>>>(a);
     k_wide_split<<<dim3(G, P), 1024, 0, s>>>(a);
   }
-  // narrow levels: one workgroup per parent, left-only statistics; the covariance slots
-  // alternate between the two buffers (the last wide level stored its groups' covariances)
+  // narrow levels: one workgroup per parent, each child's statistics from its own tokens
   for (; level < R.L && level < lr; ++level) {
     const int roots = active_count(nb, level);
     if (roots == 0) continue;
@@ -1782,9 +1769,7 @@ hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm
       k_subtree_small<T, D><<<dim3(roots, P), 256, 0, s>>>(a, level, std::min(lr, R.L));
       break;
     }
-    a.cov_prev = reinterpret_cast<float*>(w + ((level & 1) ? R.cov0 : R.cov1));
-    a.cov_cur = reinterpret_cast<float*>(w + ((level & 1) ? R.cov1 : R.cov0));
-    k_subtree_pair<T, D><<<dim3(active_count(nb, level - 1), P), 256, 0, s>>>(a, level, R.gw);
+    k_subtree_pair<T, D><<<dim3(active_count(nb, level - 1), P), 256, 0, s>>>(a, level);
   }
   if (lr < R.L) {
     const int roots = active_count(nb, lr);

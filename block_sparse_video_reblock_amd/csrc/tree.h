@@ -170,25 +170,9 @@ BSA_DEV uint32_t select_smallest_w(const float* keys, int n, int want, int* hist
     for (int b = tid; b < NW * 256; b += NT) hist[b] = 0;
     __syncthreads();
     int* hw = hist + wave * 256;
-    const int lane = tid & 63;
-    for (int base = tid - lane; base < n; base += NT) {
-      // (loop bounds uniform per wave, so the lane votes below see every lane of the wave)
-      const int i = base + lane;
-      const uint32_t key = i < n ? orderable_key(keys[i]) : 0u;
-      const bool in = i < n && (key & pmask) == prefix;
-      const int bin = int((key >> shift) & 255);
-      // keys of one group share their leading digits, so many lanes hit one bin: each of up
-      // to four leading bins is counted by one atomic of its first lane, the rest singly
-      uint64_t pending = __ballot(in);
-#pragma unroll
-      for (int r = 0; r < 4 && pending; ++r) {
-        const int leader = __ffsll((unsigned long long)pending) - 1;
-        const int b0 = __shfl(bin, leader, 64);
-        const uint64_t same = __ballot(in && bin == b0) & pending;
-        if (lane == leader) atomicAdd(&hw[b0], __popcll(same));
-        pending &= ~same;
-      }
-      if ((pending >> lane) & 1ull) atomicAdd(&hw[bin], 1);
+    for (int i = tid; i < n; i += NT) {
+      const uint32_t key = orderable_key(keys[i]);
+      if ((key & pmask) == prefix) atomicAdd(&hw[(key >> shift) & 255], 1);
     }
     __syncthreads();
     if (tid < 256) {
