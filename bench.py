@@ -47,7 +47,14 @@ HBM_PEAK_GBS = 8000.0
 ATTN_SOURCES = ("block_sparse_video_reblock_amd/csrc/attn.hip",
                 "block_sparse_video_reblock_amd/csrc/common.h",
                 "block_sparse_video_reblock_amd/csrc/internal.h")
-ATTN_TRAFFIC = {"source_sha16": "0000000000000000", "bytes": {}}
+ATTN_TRAFFIC = {"source_sha16": "220cc17b019e2367", "bytes": {
+    # key: workload / tail granularity / context tokens / reblock layout / tree
+    "clip10s_bf16/token/0/separate/full": 4.2349e10,
+    "clip10s_bf16/block/0/separate/full": 3.3707e10,
+    "clip10s_bf16/token/1000/separate/full": 6.0153e10,
+    "clip10s_bf16/token/0/q_reuse_k/full": 5.1832e10,
+    "clip10s_bf16/token/0/separate/lite": 1.9587e10,
+}}
 # The pages' own figures for the method, quoted as context (other hardware, other workloads,
 # end-to-end or attention-op times not always stated): they are not targets for this run.
 PAGE_FIGURES = [
@@ -78,12 +85,13 @@ def source_sha16(paths):
     return h.hexdigest()[:16]
 
 
-def attn_traffic(workload, tail, ctx, layout):
+def attn_traffic(workload, tail, ctx, layout, lite):
     """Measured L2<->memory bytes of one attention launch in this configuration, or None when
     no counter run covers it or the attention source has changed since."""
     if source_sha16(ATTN_SOURCES) != ATTN_TRAFFIC["source_sha16"]:
         return None
-    return ATTN_TRAFFIC["bytes"].get(f"{workload}/{tail}/{ctx}/{layout}")
+    tree = "lite" if lite else "full"
+    return ATTN_TRAFFIC["bytes"].get(f"{workload}/{tail}/{ctx}/{layout}/{tree}")
 
 
 # The reblock kernels hold a subtree in LDS from the first level whose groups have at most this
@@ -509,7 +517,8 @@ def main_headline(args, ops, synth, torch, np):
                    "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": attn_traffic(wl.name, args.tail, args.ctx, args.layout),
+                     "traffic": attn_traffic(wl.name, args.tail, args.ctx, args.layout,
+                                             args.lite),
                      "traffic_source_sha16": source_sha16(ATTN_SOURCES),
                      "kernel": "k_attn_bf16",
                      "launch_ms": attn_ms, "launch_ms_min": float(min(series["attend"])),
