@@ -1427,65 +1427,153 @@ __global__ __launch_bounds__(256, 2) void k_subtree_pair(ProblemArgs a, int leve
   }
 }
 
-// grid (roots, P): subtrees whose root spans at most kSmallBlocks blocks, split down to level
-// `stop` (exclusive).  The root's positions and keys stay in LDS for all of those levels.
-constexpr int kSmallBlocks = 8;
+// ------------------------------------------------------- two splits side by side
+// The deep levels' groups are small, so a split is a chain of short dependent phases whose
+// barriers and latencies, not their arithmetic, set its time.  The subtree kernel therefore
+// takes two independent groups at a time: their statistics and directions one after the other
+// (one covariance in registers at a time; the staging LDS is shared), then the projections,
+// thresholds and partitions of both side by side, each half-workgroup finding its group's
+// threshold with the ballot select (no barriers).  Each group's arithmetic is the one-group
+// path's, in the same order, so the layouts are unchanged.
+
+// One group of a pair: its positions, keys and partition scratch in LDS.
+struct DuoGroup {
+  int32_t* pos;
+  float* keys;
+  int32_t* tmp;
+  int g, m;  // node index at the level, blocks
+};
+
+// centred-statistics accumulation of one group (positions pos[0 .. 64 m)) relative to shv:
+// acc = sum (y - shv)(y - shv)^T (unscaled), L.mu = sum (y - shv), L.shift = shv
 template <typename T, int D>
-__global__ __launch_bounds__(256, 2) void k_subtree_small(ProblemArgs a, int ls, int stop) {
-  __shared__ StageLds<D, 2> st;
-  __shared__ DirLds L;
-  __shared__ int32_t spos[kSmallBlocks * kBlk];
-  __shared__ int32_t stmp[kSmallBlocks * kBlk];
-  __shared__ float skeys[kSmallBlocks * kBlk];
-  __shared__ int hist[4 * 256];
-  __shared__ int sm[16];
-  const int g0 = a.lists[(size_t)ls * a.G + blockIdx.x], p = problem_of(a, blockIdx.y);
-  int rb0, rm;
-  group_geom(a.nb, ls, g0, rb0, rm);
+BSA_DEV void group_stats(const T* __restrict__ X, const int32_t* pos,
+                         const float* __restrict__ inv_n, int m, DirLds& L, float shv, float ysc,
+                         float inv_s2, StageLds<D, 2>& st, f32x16_t* acc) {
+  SymAcc<D> sacc;
+  sacc.zero();
+  float dpart[D / 8];
+#pragma unroll
+  for (int e = 0; e < D / 8; ++e) dpart[e] = 0.f;
+  sym_stats_range<T, D, true>(X, pos, inv_n, 0, m, L.shift, shv, ysc, st, sacc, dpart);
+  reduce_dpart<D>(dpart, L.red, L.mu);
+  sym_to_regs<D>(sacc, inv_s2, st, acc);
+}
+
+// Statistics (relative to shv), centring and direction of one group whose positions are
+// pos[0 .. 64 m): L.w, L.mu as in group_direction.
+template <typename T, int D>
+BSA_DEV void group_direction_small(const ProblemArgs& a, int p, const T* __restrict__ X,
+                                   const int32_t* pos, const float* __restrict__ inv_n, int m,
+                                   DirLds& L, float shv, float ysc, float inv_s2, float y_first,
+                                   StageLds<D, 2>& st) {
+  f32x16_t acc[Cov<D>::TILES];
+  group_stats<T, D>(X, pos, inv_n, m, L, shv, ysc, inv_s2, st, acc);
+  // M is read (from L2) only for the power steps, so it holds no registers during the
+  // statistics
+  MRegs<D> M;
+  M.load(problem_metric<D>(a, p));  // overlaps the centring
+  group_direction<T, D>(acc, L, M, m * kBlk, 1.f, X, pos, inv_n, 0, y_first, a.iters);
+}
+
+// Split group A (and B if `two`) of `level`: statistics relative to the parent's mean, direction,
+// projections (keys in LDS, optional output by token), the capacity cut and the stable
+// partition of the positions in place.  Waves 0-1 select and partition A, waves 2-3 B.
+template <typename T, int D, int KPL>
+BSA_DEV void split_duo(const ProblemArgs& a, int p, int level, const DuoGroup& A,
+                       const DuoGroup& B, bool two, StageLds<D, 2>& st, DirLds* L, int* sm) {
+  const int tid = threadIdx.x;
   const T* X = problem_x<T, D>(a, p);
-  int32_t* pos = problem_pos(a, p) + (size_t)rb0 * kBlk;
   const float* inv_n = a.inv_n + (size_t)p * a.N;
   const float ysc = a.yscale[2 * p], inv_s2 = a.yscale[2 * p + 1];
-  for (int i = threadIdx.x; i < rm * kBlk; i += 256) spos[i] = pos[i];
+  const int nA = A.m * kBlk, nB = two ? B.m * kBlk : 0;
+  const float shA = tid < D ? parent_mean<D>(a, p, level, A.g)[tid] : 0.f;
+  const float shB = two && tid < D ? parent_mean<D>(a, p, level, B.g)[tid] : 0.f;
+  const float yA = first_candidate<T, D>(X, A.pos, inv_n, 0);
+  const float yB = two ? first_candidate<T, D>(X, B.pos, inv_n, 0) : 0.f;
+  // A's statistics and direction, then B's: one covariance in registers at a time
+  group_direction_small<T, D>(a, p, X, A.pos, inv_n, A.m, L[0], shA, ysc, inv_s2, yA, st);
+  if (two) group_direction_small<T, D>(a, p, X, B.pos, inv_n, B.m, L[1], shB, ysc, inv_s2, yB, st);
+  if (tid < D) {
+    group_mean<D>(a, p, level, A.g)[tid] = L[0].mu[tid];
+    if (two) group_mean<D>(a, p, level, B.g)[tid] = L[1].mu[tid];
+  }
+  float* proj = problem_proj(a, p, level);
+  project_range<T, D>(X, A.pos, inv_n, 0, A.m, L[0].w, A.keys, proj);
+  if (two) project_range<T, D>(X, B.pos, inv_n, 0, B.m, L[1].w, B.keys, proj);
+  __syncthreads();
+  // each half-workgroup takes one group: both of its waves find the threshold (no barrier),
+  // then partition together; a half without a group still meets the partition's barriers
+  const int half = tid >> 7;
+  const DuoGroup& S = half ? B : A;
+  const bool active = half == 0 || two;
+  const int n = active ? S.m * kBlk : 0, want = active ? (S.m >> 1) * kBlk : 0;
+  int take = 0;
+  const uint32_t cut = active ? wave_select_smallest<KPL>(S.keys, n, want, &take) : 0u;
+  partition_waves<2>(S.keys, S.pos, S.tmp, n, want, cut, take, sm + 4 * half, (tid >> 6) & 1);
+  for (int i = tid & 127; i < n; i += 128) S.pos[i] = S.tmp[i];
+  __syncthreads();
+}
+
+// grid (ceil(roots / 2), P): two subtrees per workgroup, the active groups 2x and 2x + 1 of
+// level ls (roots of them in all), each of at most kSmallBlocks blocks, split down to level
+// `stop` (exclusive) with their positions and keys in LDS.  At every level the splitting groups
+// of both subtrees are taken two at a time (split_duo).
+constexpr int kSmallBlocks = 8;
+constexpr int kSmallCap = kSmallBlocks * kBlk;
+template <typename T, int D>
+__global__ __launch_bounds__(256, 2) void k_subtree_small(ProblemArgs a, int ls, int stop,
+                                                          int roots) {
+  __shared__ StageLds<D, 2> st;
+  __shared__ DirLds L[2];
+  __shared__ int32_t spos[2][kSmallCap];
+  __shared__ int32_t stmp[2][kSmallCap];
+  __shared__ float skeys[2][kSmallCap];
+  __shared__ int sm[8];
+  const int p = problem_of(a, blockIdx.y);
+  const int nsub = min(2, roots - 2 * (int)blockIdx.x);
+  int g0[2] = {0, 0}, rb0[2] = {0, 0}, rm[2] = {0, 0};
+  for (int s = 0; s < nsub; ++s) {
+    g0[s] = a.lists[(size_t)ls * a.G + 2 * blockIdx.x + s];
+    group_geom(a.nb, ls, g0[s], rb0[s], rm[s]);
+  }
+  int32_t* pos = problem_pos(a, p);
+  for (int s = 0; s < nsub; ++s)
+    for (int i = threadIdx.x; i < rm[s] * kBlk; i += 256)
+      spos[s][i] = pos[(size_t)rb0[s] * kBlk + i];
   __syncthreads();
   for (int level = ls; level < stop; ++level) {
     const int depth = level - ls;
-    for (int g = g0 << depth; g < ((g0 + 1) << depth); ++g) {
-      int b0, m;
-      if (group_geom(a.nb, level, g, b0, m) != kGroupSplit) continue;
-      const int lb0 = b0 - rb0, n = m * kBlk;
-      const float shv = threadIdx.x < D ? parent_mean<D>(a, p, level, g)[threadIdx.x] : 0.f;
-      const float y_first = first_candidate<T, D>(X, spos, inv_n, lb0 * kBlk);
-      f32x16_t acc[Cov<D>::TILES];
-      // M is read (from L2) only for the power steps, so it holds no registers during the
-      // statistics
-      MRegs<D> M;
-      {
-        SymAcc<D> sacc;
-        sacc.zero();
-        float dpart[D / 8];
-#pragma unroll
-        for (int e = 0; e < D / 8; ++e) dpart[e] = 0.f;
-        sym_stats_range<T, D, true>(X, spos, inv_n, lb0, lb0 + m, L.shift, shv, ysc, st, sacc,
-                                    dpart);
-        reduce_dpart<D>(dpart, L.red, L.mu);
-        sym_to_regs<D>(sacc, inv_s2, st, acc);
+    // cursor over this level's splitting groups: subtree cs, node cg (uniform)
+    int cs = 0, cg = g0[0] << depth;
+    auto next = [&](DuoGroup& r) {
+      while (cs < nsub) {
+        if (cg >= ((g0[cs] + 1) << depth)) {
+          if (++cs < nsub) cg = g0[cs] << depth;
+          continue;
+        }
+        const int g = cg++;
+        int b0, m;
+        if (group_geom(a.nb, level, g, b0, m) != kGroupSplit) continue;
+        const int off = (b0 - rb0[cs]) * kBlk;
+        r.pos = &spos[cs][off];
+        r.keys = &skeys[cs][off];
+        r.tmp = &stmp[cs][off];
+        r.g = g;
+        r.m = m;
+        return true;
       }
-      M.load(problem_metric<D>(a, p));  // overlaps the centring in group_direction
-      group_direction<T, D>(acc, L, M, n, 1.f, X, spos, inv_n, lb0 * kBlk, y_first, a.iters);
-      if (threadIdx.x < D) group_mean<D>(a, p, level, g)[threadIdx.x] = L.mu[threadIdx.x];
-      float* proj = problem_proj(a, p, level);
-      project_range<T, D>(X, spos, inv_n, lb0, lb0 + m, L.w, skeys, proj);
-      __syncthreads();
-      const int want = (m >> 1) * kBlk;
-      int take;
-      const uint32_t T_ = select_smallest_w<256>(skeys + lb0 * kBlk, n, want, hist, sm, &take);
-      partition_w<256>(skeys + lb0 * kBlk, spos + lb0 * kBlk, stmp, n, want, T_, take, sm);
-      for (int i = threadIdx.x; i < n; i += 256) spos[lb0 * kBlk + i] = stmp[i];
-      __syncthreads();
+      return false;
+    };
+    DuoGroup A{}, B{};  // (B stays empty when a level's count is odd)
+    while (next(A)) {
+      const bool two = next(B);
+      split_duo<T, D, kSmallBlocks>(a, p, level, A, B, two, st, L, sm);
     }
   }
-  for (int i = threadIdx.x; i < rm * kBlk; i += 256) pos[i] = spos[i];
+  for (int s = 0; s < nsub; ++s)
+    for (int i = threadIdx.x; i < rm[s] * kBlk; i += 256)
+      pos[(size_t)rb0[s] * kBlk + i] = spos[s][i];
 }
 
 // ------------------------------------------------------------- Lite: shared subtrees
@@ -1766,7 +1854,8 @@ hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm
     const int roots = active_count(nb, level);
     if (roots == 0) continue;
     if (ceil_div(nb, 1 << level) <= kSmallBlocks) {
-      k_subtree_small<T, D><<<dim3(roots, P), 256, 0, s>>>(a, level, std::min(lr, R.L));
+      k_subtree_small<T, D><<<dim3(ceil_div(roots, 2), P), 256, 0, s>>>(
+          a, level, std::min(lr, R.L), roots);
       break;
     }
     k_subtree_pair<T, D><<<dim3(active_count(nb, level - 1), P), 256, 0, s>>>(a, level);

@@ -157,53 +157,56 @@ BSA_DEV void block_partition(const float* keys, const int32_t* in, int32_t* out,
 // ---------------------------------------------------------------------------------------
 // Wave-parallel variants for any workgroup size NT (a multiple of 64).
 
-// Radix select as above, with one private histogram per wave (less atomic contention) and
-// coalesced reads.  hist: NT/64 * 256 ints of LDS; sm: NT/64 + 2 ints.
-template <int NT>
-BSA_DEV uint32_t select_smallest_w(const float* keys, int n, int want, int* hist, int* sm,
-                                   int* take) {
-  constexpr int NW = NT / 64;
-  const int tid = threadIdx.x, wave = tid >> 6;
+// Radix select as above by the NW waves that call it with local wave indices 0 .. NW-1, with
+// one private histogram per wave (less atomic contention) and coalesced reads.  hist: NW * 256
+// ints of LDS; sm: 2 ints.  Its barriers are workgroup-wide: every thread of the workgroup must
+// reach them (waves outside the NW may run another select between them).
+template <int NW>
+BSA_DEV uint32_t select_waves(const float* keys, int n, int want, int* hist, int* sm, int* take,
+                              int wave) {
+  constexpr int NT = NW * 64;
+  const int lane = threadIdx.x & 63, ltid = wave * 64 + lane;
   uint32_t prefix = 0, pmask = 0;
   int remaining = want;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int b = tid; b < NW * 256; b += NT) hist[b] = 0;
+    for (int b = ltid; b < NW * 256; b += NT) hist[b] = 0;
     __syncthreads();
     int* hw = hist + wave * 256;
-    for (int i = tid; i < n; i += NT) {
+    for (int i = ltid; i < n; i += NT) {
       const uint32_t key = orderable_key(keys[i]);
       if ((key & pmask) == prefix) atomicAdd(&hw[(key >> shift) & 255], 1);
     }
     __syncthreads();
-    if (tid < 256) {
+    // merged into wave 0's histogram (each bin is read and written by one thread only)
+    for (int b = ltid; b < 256; b += NT) {
       int c = 0;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) c += hist[w * 256 + tid];
-      hist[tid] = c;  // merged into wave 0's histogram (each thread only touches bin tid)
+      for (int w = 0; w < NW; ++w) c += hist[w * 256 + b];
+      hist[b] = c;
     }
     __syncthreads();
-    if (tid < 64) {
+    if (wave == 0) {
       // wave 0 scans the 256 bins: lane l owns bins 4l .. 4l+3
       int c[4], local = 0;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        c[u] = hist[4 * tid + u];
+        c[u] = hist[4 * lane + u];
         local += c[u];
       }
       int incl = local;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
         const int t = __shfl_up(incl, o, 64);
-        if (tid >= o) incl += t;
+        if (lane >= o) incl += t;
       }
       const uint64_t hit = __ballot(incl >= remaining);
       const int src = __ffsll((unsigned long long)hit) - 1;
-      if (tid == src) {
+      if (lane == src) {
         int run = incl - local;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           if (run + c[u] >= remaining) {
-            sm[0] = 4 * tid + u;
+            sm[0] = 4 * lane + u;
             sm[1] = run;
             break;
           }
@@ -222,14 +225,22 @@ BSA_DEV uint32_t select_smallest_w(const float* keys, int n, int want, int* hist
   return prefix;
 }
 
-// Stable two-way partition (same result as block_partition).  Wave w streams one contiguous
-// range of 64-element steps with coalesced loads; ballots give in-order ranks.  sm: 2*NW ints.
-// keys_out, if given, receives the keys in the partitioned order.
+// select_waves by all NT / 64 waves of the workgroup; hist: NT/64 * 256 ints, sm: 2 ints
 template <int NT>
-BSA_DEV void partition_w(const float* keys, const int32_t* in, int32_t* out, int n, int want,
-                         uint32_t T, int take, int* sm, float* keys_out = nullptr) {
-  constexpr int NW = NT / 64;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+BSA_DEV uint32_t select_smallest_w(const float* keys, int n, int want, int* hist, int* sm,
+                                   int* take) {
+  return select_waves<NT / 64>(keys, n, want, hist, sm, take, threadIdx.x >> 6);
+}
+
+// Stable two-way partition (same result as block_partition) by the NW waves that call it with
+// local wave indices 0 .. NW-1.  Wave w streams one contiguous range of 64-element steps with
+// coalesced loads; ballots give in-order ranks.  sm: 2*NW ints.  keys_out, if given, receives
+// the keys in the partitioned order.  Two workgroup barriers, which every thread of the
+// workgroup must reach (waves outside the NW may run another partition between them).
+template <int NW>
+BSA_DEV void partition_waves(const float* keys, const int32_t* in, int32_t* out, int n, int want,
+                             uint32_t T, int take, int* sm, int wave, float* keys_out = nullptr) {
+  const int lane = threadIdx.x & 63;
   const int steps = (n + 63) / 64;
   const int per = (steps + NW - 1) / NW;
   const int i0 = min(n, wave * per * 64), i1 = min(n, i0 + per * 64);
@@ -271,6 +282,45 @@ BSA_DEV void partition_w(const float* keys, const int32_t* in, int32_t* out, int
     eq_seen += __popcll(eqm);
   }
   __syncthreads();
+}
+
+// partition_waves by all NT / 64 waves of the workgroup
+template <int NT>
+BSA_DEV void partition_w(const float* keys, const int32_t* in, int32_t* out, int n, int want,
+                         uint32_t T, int take, int* sm, float* keys_out = nullptr) {
+  partition_waves<NT / 64>(keys, in, out, n, want, T, take, sm, threadIdx.x >> 6, keys_out);
+}
+
+// The threshold of select_smallest_w found by one wave alone, for n <= 64 * KPL keys held in
+// its registers: T (the want-th smallest orderable key) is built bit by bit from the top, each
+// bit decided by counting the keys below the candidate with ballots; take = want minus the
+// keys below T.  No LDS and no barriers; any number of waves may run it at once.
+template <int KPL>
+BSA_DEV uint32_t wave_select_smallest(const float* keys, int n, int want, int* take) {
+  const int lane = threadIdx.x & 63;
+  uint32_t k[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int i = 64 * j + lane;
+    // padding never counts: no candidate exceeds 0xFFFFFFFF
+    k[j] = i < n ? orderable_key(keys[i]) : 0xFFFFFFFFu;
+  }
+  const int used = (n + 63) >> 6;  // registers that hold keys (uniform)
+  uint32_t T = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = T | (1u << b);
+    int below = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j)
+      if (j < used) below += __popcll(__ballot(k[j] < c));
+    if (below < want) T = c;
+  }
+  int below = 0;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j)
+    if (j < used) below += __popcll(__ballot(k[j] < T));
+  *take = want - below;
+  return T;
 }
 
 }  // namespace bsa
