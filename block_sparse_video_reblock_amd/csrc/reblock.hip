@@ -1329,8 +1329,10 @@ __global__ __launch_bounds__(1024) void k_wide_split(ProblemArgs a) {
   int32_t* pos = problem_pos(a, p) + off;
   int32_t* tmp = a.tmp + (size_t)p * a.N + off;
   int take;
-  const uint32_t T = select_smallest_w<1024>(keys, n, want, hist, sm, &take);
-  partition_w<1024>(keys, pos, tmp, n, want, T, take, sm);
+  // large groups: 8 keys (or 64-key steps) per thread in flight, so the passes over the keys in
+  // global memory are not a chain of dependent loads
+  const uint32_t T = select_smallest_w<1024, 8>(keys, n, want, hist, sm, &take);
+  partition_w<1024, 8>(keys, pos, tmp, n, want, T, take, sm);
   for (int i = threadIdx.x; i < n; i += 1024) pos[i] = tmp[i];
 }
 
@@ -1364,8 +1366,9 @@ BSA_DEV void split_group(const ProblemArgs& a, int p, int level, int g, int b0, 
   const size_t off = (size_t)b0 * kBlk;
   const int want = (m >> 1) * kBlk;
   int take;
-  const uint32_t T_ = select_smallest_w<256>(keys + off, n, want, hist, sm, &take);
-  partition_w<256>(keys + off, pos + off, tmp + off, n, want, T_, take, sm);
+  // keys in global memory: 4 per thread (or 64-key steps) in flight per pass
+  const uint32_t T_ = select_smallest_w<256, 4>(keys + off, n, want, hist, sm, &take);
+  partition_w<256, 4>(keys + off, pos + off, tmp + off, n, want, T_, take, sm);
   for (int i = threadIdx.x; i < n; i += 256) pos[off + i] = tmp[off + i];
   __syncthreads();
 }

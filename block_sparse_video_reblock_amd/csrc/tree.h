@@ -161,7 +161,8 @@ BSA_DEV void block_partition(const float* keys, const int32_t* in, int32_t* out,
 // one private histogram per wave (less atomic contention) and coalesced reads.  hist: NW * 256
 // ints of LDS; sm: 2 ints.  Its barriers are workgroup-wide: every thread of the workgroup must
 // reach them (waves outside the NW may run another select between them).
-template <int NW>
+// U keys per thread are loaded before any is counted (U loads in flight per thread).
+template <int NW, int U = 1>
 BSA_DEV uint32_t select_waves(const float* keys, int n, int want, int* hist, int* sm, int* take,
                               int wave) {
   constexpr int NT = NW * 64;
@@ -172,9 +173,14 @@ BSA_DEV uint32_t select_waves(const float* keys, int n, int want, int* hist, int
     for (int b = ltid; b < NW * 256; b += NT) hist[b] = 0;
     __syncthreads();
     int* hw = hist + wave * 256;
-    for (int i = ltid; i < n; i += NT) {
-      const uint32_t key = orderable_key(keys[i]);
-      if ((key & pmask) == prefix) atomicAdd(&hw[(key >> shift) & 255], 1);
+    for (int i0 = ltid; i0 < n; i0 += U * NT) {
+      uint32_t kk[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) kk[u] = i0 + u * NT < n ? orderable_key(keys[i0 + u * NT]) : 0u;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (i0 + u * NT < n && (kk[u] & pmask) == prefix)
+          atomicAdd(&hw[(kk[u] >> shift) & 255], 1);
     }
     __syncthreads();
     // merged into wave 0's histogram (each bin is read and written by one thread only)
@@ -226,10 +232,10 @@ BSA_DEV uint32_t select_waves(const float* keys, int n, int want, int* hist, int
 }
 
 // select_waves by all NT / 64 waves of the workgroup; hist: NT/64 * 256 ints, sm: 2 ints
-template <int NT>
+template <int NT, int U = 1>
 BSA_DEV uint32_t select_smallest_w(const float* keys, int n, int want, int* hist, int* sm,
                                    int* take) {
-  return select_waves<NT / 64>(keys, n, want, hist, sm, take, threadIdx.x >> 6);
+  return select_waves<NT / 64, U>(keys, n, want, hist, sm, take, threadIdx.x >> 6);
 }
 
 // Stable two-way partition (same result as block_partition) by the NW waves that call it with
@@ -237,7 +243,8 @@ BSA_DEV uint32_t select_smallest_w(const float* keys, int n, int want, int* hist
 // coalesced loads; ballots give in-order ranks.  sm: 2*NW ints.  keys_out, if given, receives
 // the keys in the partitioned order.  Two workgroup barriers, which every thread of the
 // workgroup must reach (waves outside the NW may run another partition between them).
-template <int NW>
+// U: 64-element steps whose loads are issued before the first of them is processed.
+template <int NW, int U = 1>
 BSA_DEV void partition_waves(const float* keys, const int32_t* in, int32_t* out, int n, int want,
                              uint32_t T, int take, int* sm, int wave, float* keys_out = nullptr) {
   const int lane = threadIdx.x & 63;
@@ -245,11 +252,19 @@ BSA_DEV void partition_waves(const float* keys, const int32_t* in, int32_t* out,
   const int per = (steps + NW - 1) / NW;
   const int i0 = min(n, wave * per * 64), i1 = min(n, i0 + per * 64);
   int c_lt = 0, c_eq = 0;
-  for (int base = i0; base < i1; base += 64) {
-    const int i = base + lane;
-    const uint32_t key = i < i1 ? orderable_key(keys[i]) : 0xFFFFFFFFu;
-    c_lt += __popcll(__ballot(i < i1 && key < T));
-    c_eq += __popcll(__ballot(i < i1 && key == T));
+  for (int b0 = i0; b0 < i1; b0 += 64 * U) {
+    uint32_t kk[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = b0 + 64 * u + lane;
+      kk[u] = i < i1 ? orderable_key(keys[i]) : 0xFFFFFFFFu;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = b0 + 64 * u + lane;
+      c_lt += __popcll(__ballot(i < i1 && kk[u] < T));
+      c_eq += __popcll(__ballot(i < i1 && kk[u] == T));
+    }
   }
   if (lane == 0) {
     sm[wave] = c_lt;
@@ -263,32 +278,43 @@ BSA_DEV void partition_waves(const float* keys, const int32_t* in, int32_t* out,
     eq_before += eq;
   }
   int left_run = 0, eq_seen = eq_before;
-  for (int base = i0; base < i1; base += 64) {
-    const int i = base + lane;
-    const bool ok = i < i1;
-    const float kv = ok ? keys[i] : 0.f;
-    const uint32_t key = ok ? orderable_key(kv) : 0xFFFFFFFFu;
-    const bool eq = ok && key == T;
-    const uint64_t eqm = __ballot(eq);
-    const bool left = ok && (key < T || (eq && eq_seen + lanes_below(eqm) < take));
-    const uint64_t lm = __ballot(left);
-    if (ok) {
-      const int lb = left_before + left_run + lanes_below(lm);  // lefts before i
-      const int dst = left ? lb : want + (i - lb);
-      out[dst] = in[i];
-      if (keys_out != nullptr) keys_out[dst] = kv;
+  for (int b0 = i0; b0 < i1; b0 += 64 * U) {
+    float kvs[U];
+    int32_t ins[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = b0 + 64 * u + lane;
+      kvs[u] = i < i1 ? keys[i] : 0.f;
+      ins[u] = i < i1 ? in[i] : 0;
     }
-    left_run += __popcll(lm);
-    eq_seen += __popcll(eqm);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = b0 + 64 * u + lane;
+      const bool ok = i < i1;
+      const float kv = kvs[u];
+      const uint32_t key = ok ? orderable_key(kv) : 0xFFFFFFFFu;
+      const bool eq = ok && key == T;
+      const uint64_t eqm = __ballot(eq);
+      const bool left = ok && (key < T || (eq && eq_seen + lanes_below(eqm) < take));
+      const uint64_t lm = __ballot(left);
+      if (ok) {
+        const int lb = left_before + left_run + lanes_below(lm);  // lefts before i
+        const int dst = left ? lb : want + (i - lb);
+        out[dst] = ins[u];
+        if (keys_out != nullptr) keys_out[dst] = kv;
+      }
+      left_run += __popcll(lm);
+      eq_seen += __popcll(eqm);
+    }
   }
   __syncthreads();
 }
 
 // partition_waves by all NT / 64 waves of the workgroup
-template <int NT>
+template <int NT, int U = 1>
 BSA_DEV void partition_w(const float* keys, const int32_t* in, int32_t* out, int n, int want,
                          uint32_t T, int take, int* sm, float* keys_out = nullptr) {
-  partition_waves<NT / 64>(keys, in, out, n, want, T, take, sm, threadIdx.x >> 6, keys_out);
+  partition_waves<NT / 64, U>(keys, in, out, n, want, T, take, sm, threadIdx.x >> 6, keys_out);
 }
 
 // The threshold of select_smallest_w found by one wave alone, for n <= 64 * KPL keys held in
