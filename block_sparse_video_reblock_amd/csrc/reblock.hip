@@ -54,7 +54,12 @@ inline int wide_slices(int level, int nb) {
   return std::min(kSlots >> std::min(level, 4), nb >> level);
 }
 constexpr int kIters = 8;         // power steps per split (the default; Lite takes fewer)
-constexpr int kStageStride = 72;  // bf16 elements per LDS row of the staged (transposed) chunk
+// Elements per LDS row of the staged (transposed) chunk.  Measured on gfx950: the 32 x 32 x 16
+// operand reads of the raw moments (stats_mfma) meet no bank conflicts with 144-byte rows, the
+// 16 x 16 x 32 operand reads of the symmetric statistics (sym_mfma) none with 160-byte rows
+// (four conflict cycles per read with 144-byte rows, and no swizzle of the 16-byte chunks by
+// row removed them).
+constexpr int kMomStride = 72, kSymStride = 80;
 
 BSA_DEV bf16x8_t lds_bf16x8(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
@@ -88,10 +93,13 @@ constexpr int kExact = 1, kF16x2 = 2, kBf16x3 = 3;
 template <int MODE>
 constexpr int split_terms() { return MODE == kExact ? 1 : (MODE == kF16x2 ? 2 : 3); }
 
-template <int D, int NT>
+template <int D, int NT, int S = kMomStride>
 struct __align__(16) StageLds {
-  uint16_t t[NT][D][kStageStride];
+  uint16_t t[NT][D][S];
 };
+// the staging of the symmetric statistics: two fp16 terms, 160-byte rows
+template <int D>
+using SymStage = StageLds<D, 2, kSymStride>;
 
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
 BSA_DEV f16x8_t lds_f16x8(const uint16_t* p) {
@@ -109,8 +117,9 @@ BSA_DEV f32x2_t unpack_f16x2(uint32_t u) {
 
 // One 64-position chunk of the covariance accumulation.  Thread t stages the token pair
 // (2 (t%32), 2 (t%32) + 1) for the DPT = D/8 elements of element group t/32 (see stat_dim):
-// d = x * scale - shift, split into 16-bit terms written as packed pairs of tokens, so the
-// transposed staging rows of the two groups of a wave sit 8 rows (32 banks) apart.
+// d = x * scale - shift, split into 16-bit terms written as packed pairs of tokens; the
+// transposed staging rows of the two groups of a wave sit 8 rows apart (32 banks with 144-byte
+// rows; with 160-byte rows the two halves meet, about 0.8 conflict cycles per write).
 // tokmap == nullptr means position = token id; inv_n == nullptr means scale 1.
 template <int D>
 BSA_DEV int stat_dim(int dg, int j) {
@@ -195,9 +204,9 @@ BSA_DEV void stats_load_tok(const T* __restrict__ X, const float* __restrict__ i
 
 // Stage one chunk (centred, split) into LDS and accumulate d; no barrier.  ysc: the kF16x2
 // scale s.
-template <typename T, int D, int MODE>
+template <typename T, int D, int MODE, int S>
 BSA_DEV void stats_stage(const ChunkRegs<T, D>& r, const float* sh_shift, float ysc,
-                         StageLds<D, split_terms<MODE>()>& st, float* dpart) {
+                         StageLds<D, split_terms<MODE>(), S>& st, float* dpart) {
   constexpr int DPT = D / 8;
   const int tp = threadIdx.x & 31, dg = threadIdx.x >> 5;
   float xv[2][DPT];
@@ -281,7 +290,7 @@ BSA_DEV void stats_range(const T* __restrict__ X, const int32_t* __restrict__ to
   if (PREFETCH) stats_load<T, D>(X, tokmap, inv_n, blk0 * kBlk, cur);
   for (int b = blk0; b < blk1; ++b) {
     if (!PREFETCH) stats_load<T, D>(X, tokmap, inv_n, b * kBlk, cur);
-    stats_stage<T, D, MODE>(cur, sh_shift, ysc, st, dpart);
+    stats_stage<T, D, MODE, kMomStride>(cur, sh_shift, ysc, st, dpart);
     __syncthreads();
     if (PREFETCH && b + 1 < blk1) stats_load<T, D>(X, tokmap, inv_n, (b + 1) * kBlk, cur);
     stats_mfma<D, MODE>(st, acc);
@@ -390,7 +399,7 @@ struct SymAcc {
 
 // one 64-token chunk (two 32-token steps) of the staged fp16 split into wave W's tiles
 template <int D, int W>
-BSA_DEV void sym_mfma_wave(const StageLds<D, 2>& st, SymAcc<D>& acc) {
+BSA_DEV void sym_mfma_wave(const SymStage<D>& st, SymAcc<D>& acc) {
   using P = SymPlan<D>;
   const int lane = threadIdx.x & 63, r16 = lane & 15, kg = lane >> 4;
 #pragma unroll
@@ -424,7 +433,7 @@ BSA_DEV void sym_mfma_wave(const StageLds<D, 2>& st, SymAcc<D>& acc) {
   }
 }
 template <int D>
-BSA_DEV void sym_mfma(const StageLds<D, 2>& st, SymAcc<D>& acc) {
+BSA_DEV void sym_mfma(const SymStage<D>& st, SymAcc<D>& acc) {
   switch (threadIdx.x >> 6) {
     case 0: sym_mfma_wave<D, 0>(st, acc); break;
     case 1: sym_mfma_wave<D, 1>(st, acc); break;
@@ -439,7 +448,7 @@ BSA_DEV void sym_mfma(const StageLds<D, 2>& st, SymAcc<D>& acc) {
 template <typename T, int D, bool PREFETCH>
 BSA_DEV void sym_stats_range(const T* __restrict__ X, const int32_t* __restrict__ tokmap,
                              const float* __restrict__ inv_n, int blk0, int blk1,
-                             float* sh_shift, float sh_val, float ysc, StageLds<D, 2>& st,
+                             float* sh_shift, float sh_val, float ysc, SymStage<D>& st,
                              SymAcc<D>& acc, float* dpart) {
   ChunkRegs<T, D> cur;
   // with PREFETCH, a block's rows are loaded one block ahead and its token ids two blocks
@@ -455,7 +464,7 @@ BSA_DEV void sym_stats_range(const T* __restrict__ X, const int32_t* __restrict_
   __syncthreads();
   for (int b = blk0; b < blk1; ++b) {
     if (!PREFETCH) stats_load<T, D>(X, tokmap, inv_n, b * kBlk, cur);
-    stats_stage<T, D, kF16x2>(cur, sh_shift, ysc, st, dpart);
+    stats_stage<T, D, kF16x2, kSymStride>(cur, sh_shift, ysc, st, dpart);
     __syncthreads();
     if (PREFETCH && b + 1 < blk1) {
       stats_load_tok<T, D>(X, inv_n, tnext, cur);
@@ -553,9 +562,9 @@ BSA_DEV void load_cols(f32x16_t* acc, const float* F, int ld, int c0, int ncols)
 // Symmetric tiles (times f) into the register layout of Cov<D>, through the staging LDS in
 // passes of 64 columns (stored by columns, D + 4 floats apart: conflict-free 16-byte reads).
 template <int D>
-BSA_DEV void sym_to_regs(const SymAcc<D>& sacc, float f, StageLds<D, 2>& st, f32x16_t* acc) {
+BSA_DEV void sym_to_regs(const SymAcc<D>& sacc, float f, SymStage<D>& st, f32x16_t* acc) {
   constexpr int ld = D + 4;
-  static_assert(64 * ld * 4 <= sizeof(StageLds<D, 2>), "one pass fits the staging area");
+  static_assert(64 * ld * 4 <= sizeof(SymStage<D>), "one pass fits the staging area");
   float* G = reinterpret_cast<float*>(&st);
   for (int c0 = 0; c0 < D; c0 += 64) {
     sym_store<D>(sacc, f, G, ld, c0, 64);
@@ -1191,7 +1200,7 @@ __global__ __launch_bounds__(256) void k_group_lists(int nb, int G, int* __restr
 // grid (slices, G, P): partial statistics of one slice of one group
 template <typename T, int D>
 __global__ __launch_bounds__(256, 3) void k_wide_stats(ProblemArgs a) {
-  __shared__ StageLds<D, 2> st;
+  __shared__ SymStage<D> st;
   __shared__ float shift[D];
   __shared__ float red[4 * D];
   __shared__ float dsum[D];
@@ -1381,7 +1390,7 @@ BSA_DEV void split_group(const ProblemArgs& a, int p, int level, int g, int b0, 
 // by n_P, into a child whose spread is small next to its distance from mu_P.)
 template <typename T, int D>
 __global__ __launch_bounds__(256, 2) void k_subtree_pair(ProblemArgs a, int level) {
-  __shared__ StageLds<D, 2> st;
+  __shared__ SymStage<D> st;
   __shared__ DirLds L;
   __shared__ float dsl[D];
   __shared__ int hist[4 * 256];
@@ -1452,7 +1461,7 @@ struct DuoGroup {
 template <typename T, int D>
 BSA_DEV void group_stats(const T* __restrict__ X, const int32_t* pos,
                          const float* __restrict__ inv_n, int m, DirLds& L, float shv, float ysc,
-                         float inv_s2, StageLds<D, 2>& st, f32x16_t* acc) {
+                         float inv_s2, SymStage<D>& st, f32x16_t* acc) {
   SymAcc<D> sacc;
   sacc.zero();
   float dpart[D / 8];
@@ -1469,7 +1478,7 @@ template <typename T, int D>
 BSA_DEV void group_direction_small(const ProblemArgs& a, int p, const T* __restrict__ X,
                                    const int32_t* pos, const float* __restrict__ inv_n, int m,
                                    DirLds& L, float shv, float ysc, float inv_s2, float y_first,
-                                   StageLds<D, 2>& st) {
+                                   SymStage<D>& st) {
   f32x16_t acc[Cov<D>::TILES];
   group_stats<T, D>(X, pos, inv_n, m, L, shv, ysc, inv_s2, st, acc);
   // M is read (from L2) only for the power steps, so it holds no registers during the
@@ -1484,7 +1493,7 @@ BSA_DEV void group_direction_small(const ProblemArgs& a, int p, const T* __restr
 // partition of the positions in place.  Waves 0-1 select and partition A, waves 2-3 B.
 template <typename T, int D, int KPL>
 BSA_DEV void split_duo(const ProblemArgs& a, int p, int level, const DuoGroup& A,
-                       const DuoGroup& B, bool two, StageLds<D, 2>& st, DirLds* L, int* sm) {
+                       const DuoGroup& B, bool two, SymStage<D>& st, DirLds* L, int* sm) {
   const int tid = threadIdx.x;
   const T* X = problem_x<T, D>(a, p);
   const float* inv_n = a.inv_n + (size_t)p * a.N;
@@ -1527,7 +1536,7 @@ constexpr int kSmallCap = kSmallBlocks * kBlk;
 template <typename T, int D>
 __global__ __launch_bounds__(256, 2) void k_subtree_small(ProblemArgs a, int ls, int stop,
                                                           int roots) {
-  __shared__ StageLds<D, 2> st;
+  __shared__ SymStage<D> st;
   __shared__ DirLds L[2];
   __shared__ int32_t spos[2][kSmallCap];
   __shared__ int32_t stmp[2][kSmallCap];
@@ -1613,15 +1622,15 @@ BSA_DEV void lds_bitonic(uint64_t* v, int n, int kmax) {
 // grid (roots of level lr, P)
 template <typename T, int D>
 __global__ __launch_bounds__(256, 2) void k_shared_subtree(ProblemArgs a, int lr) {
-  constexpr size_t kRaw = sizeof(StageLds<D, 2>) > kSharedCap * sizeof(uint64_t)
-                              ? sizeof(StageLds<D, 2>)
+  constexpr size_t kRaw = sizeof(SymStage<D>) > kSharedCap * sizeof(uint64_t)
+                              ? sizeof(SymStage<D>)
                               : kSharedCap * sizeof(uint64_t);
   // staging area of the statistics, afterwards the sort buffer
   __shared__ __align__(16) unsigned char sraw[kRaw];
   __shared__ DirLds L;
   __shared__ int32_t spos[kSharedCap];
   __shared__ float skeys[kSharedCap];
-  StageLds<D, 2>& st = *reinterpret_cast<StageLds<D, 2>*>(sraw);
+  SymStage<D>& st = *reinterpret_cast<SymStage<D>*>(sraw);
   uint64_t* sbuf = reinterpret_cast<uint64_t*>(sraw);
   const int g = a.lists[(size_t)lr * a.G + blockIdx.x], p = problem_of(a, blockIdx.y);
   int b0, m;
