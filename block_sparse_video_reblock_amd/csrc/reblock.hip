@@ -1527,15 +1527,16 @@ BSA_DEV void split_duo(const ProblemArgs& a, int p, int level, const DuoGroup& A
   __syncthreads();
 }
 
-// grid (ceil(roots / 2), P): two subtrees per workgroup, the active groups 2x and 2x + 1 of
-// level ls (roots of them in all), each of at most kSmallBlocks blocks, split down to level
-// `stop` (exclusive) with their positions and keys in LDS.  At every level the splitting groups
-// of both subtrees are taken two at a time (split_duo).
+// grid (ceil(roots / per), P): `per` (1 or 2) subtrees per workgroup, the active groups
+// per x .. per x + per - 1 of level ls (roots of them in all), each of at most kSmallBlocks
+// blocks, split down to level `stop` (exclusive) with their positions and keys in LDS.  At
+// every level the splitting groups of the workgroup's subtrees are taken two at a time
+// (split_duo).
 constexpr int kSmallBlocks = 8;
 constexpr int kSmallCap = kSmallBlocks * kBlk;
 template <typename T, int D>
 __global__ __launch_bounds__(256, 2) void k_subtree_small(ProblemArgs a, int ls, int stop,
-                                                          int roots) {
+                                                          int roots, int per) {
   __shared__ SymStage<D> st;
   __shared__ DirLds L[2];
   __shared__ int32_t spos[2][kSmallCap];
@@ -1543,10 +1544,10 @@ __global__ __launch_bounds__(256, 2) void k_subtree_small(ProblemArgs a, int ls,
   __shared__ float skeys[2][kSmallCap];
   __shared__ int sm[8];
   const int p = problem_of(a, blockIdx.y);
-  const int nsub = min(2, roots - 2 * (int)blockIdx.x);
+  const int nsub = min(per, roots - per * (int)blockIdx.x);
   int g0[2] = {0, 0}, rb0[2] = {0, 0}, rm[2] = {0, 0};
   for (int s = 0; s < nsub; ++s) {
-    g0[s] = a.lists[(size_t)ls * a.G + 2 * blockIdx.x + s];
+    g0[s] = a.lists[(size_t)ls * a.G + per * blockIdx.x + s];
     group_geom(a.nb, ls, g0[s], rb0[s], rm[s]);
   }
   int32_t* pos = problem_pos(a, p);
@@ -1866,8 +1867,11 @@ hipError_t run_reblock(const void* q, const void* k, int H, int N, int32_t* perm
     const int roots = active_count(nb, level);
     if (roots == 0) continue;
     if (ceil_div(nb, 1 << level) <= kSmallBlocks) {
-      k_subtree_small<T, D><<<dim3(ceil_div(roots, 2), P), 256, 0, s>>>(
-          a, level, std::min(lr, R.L), roots);
+      // two subtrees per workgroup while that still leaves two rounds of workgroups for the
+      // whole GPU (256 CUs x 2), else one (its groups are still taken two at a time)
+      const int per = (long)ceil_div(roots, 2) * P >= 1024 ? 2 : 1;
+      k_subtree_small<T, D><<<dim3(ceil_div(roots, per), P), 256, 0, s>>>(
+          a, level, std::min(lr, R.L), roots, per);
       break;
     }
     k_subtree_pair<T, D><<<dim3(active_count(nb, level - 1), P), 256, 0, s>>>(a, level);
