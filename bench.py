@@ -47,13 +47,13 @@ HBM_PEAK_GBS = 8000.0
 ATTN_SOURCES = ("block_sparse_video_reblock_amd/csrc/attn.hip",
                 "block_sparse_video_reblock_amd/csrc/common.h",
                 "block_sparse_video_reblock_amd/csrc/internal.h")
-ATTN_TRAFFIC = {"source_sha16": "220cc17b019e2367", "bytes": {
+ATTN_TRAFFIC = {"source_sha16": "d50ffa2e1cf7a196", "bytes": {
     # key: workload / tail granularity / context tokens / reblock layout / tree
-    "clip10s_bf16/token/0/separate/full": 4.2349e10,
-    "clip10s_bf16/block/0/separate/full": 3.3707e10,
-    "clip10s_bf16/token/1000/separate/full": 6.0153e10,
-    "clip10s_bf16/token/0/q_reuse_k/full": 5.1832e10,
-    "clip10s_bf16/token/0/separate/lite": 1.9587e10,
+    "clip10s_bf16/token/0/separate/full": 4.4008e10,
+    "clip10s_bf16/block/0/separate/full": 3.7701e10,
+    "clip10s_bf16/token/1000/separate/full": 6.0276e10,
+    "clip10s_bf16/token/0/q_reuse_k/full": 5.3572e10,
+    "clip10s_bf16/token/0/separate/lite": 2.0720e10,
 }}
 # The pages' own figures for the method, quoted as context (other hardware, other workloads,
 # end-to-end or attention-op times not always stated): they are not targets for this run.

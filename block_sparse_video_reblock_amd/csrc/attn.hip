@@ -85,6 +85,20 @@ BSA_DEV int xcd_remap(int bid, int total) {
   return x * q + min(x, r) + k;
 }
 
+// The video launch with H a multiple of 4: XCDs 2c and 2c + 1 take heads c, c + 4, c + 8, ...
+// in turn, each a contiguous half of the head's query blocks (half = ceil(nbq / 2) per XCD and
+// head, grid 2 H half).  Each XCD still walks neighbouring query blocks, and only four heads'
+// key and value tiles are in use at a time instead of eight.  False for an id past the last
+// block of its half.
+constexpr int kHeadsPerRound = 4;
+BSA_DEV bool xcd_pair_remap(int bid, int nbq, int& h, int& i) {
+  const int x = bid & 7, k = bid >> 3, half = (nbq + 1) >> 1;
+  const int round = k / half;
+  h = (x >> 1) + kHeadsPerRound * round;
+  i = (x & 1) * half + (k - round * half);
+  return i < nbq;
+}
+
 // One set of query blocks of an attention launch and the work list of each block.
 struct QSide {
   const uint16_t* q;     // [H][rows][D]
@@ -135,8 +149,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(QSide cs, QSide vs, int wg
   if (ks.list_status != nullptr && load_uniform(ks.list_status) != 0) return;
   const bool is_ctx = CTX && blockIdx.x < wg_c;
   const QSide S = is_ctx ? cs : vs;
-  const int local = is_ctx ? blockIdx.x : xcd_remap(blockIdx.x - wg_c, H * vs.nbq);
-  const int h = local / S.nbq, i = local - h * S.nbq;
+  int h, i;
+  if (!CTX && H % kHeadsPerRound == 0) {
+    if (!xcd_pair_remap(blockIdx.x, S.nbq, h, i)) return;
+  } else {
+    const int local = is_ctx ? blockIdx.x : xcd_remap(blockIdx.x - wg_c, H * vs.nbq);
+    h = local / S.nbq;
+    i = local - h * S.nbq;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const int ntiles = ks.nt_s, nb = ks.nb;
@@ -929,8 +949,8 @@ hipError_t launch_attn_bf16(const AttnLaunch& a, hipStream_t s) {
     k_attn_bf16<true><<<wg_c + a.H * a.nb, 256, dyn, s>>>(cs, vs, wg_c, ks, lists, a.H,
                                                           a.scale * kLog2e);
   else
-    k_attn_bf16<false><<<a.H * a.nb, 256, dyn, s>>>(cs, vs, 0, ks, lists, a.H,
-                                                    a.scale * kLog2e);
+    k_attn_bf16<false><<<a.H % kHeadsPerRound == 0 ? 2 * a.H * ((a.nb + 1) / 2) : a.H * a.nb, 256,
+                         dyn, s>>>(cs, vs, 0, ks, lists, a.H, a.scale * kLog2e);
   return hipGetLastError();
 }
 

@@ -177,11 +177,15 @@ def test_density_one_is_dense_bf16(mid):
     assert rel_l2(got, ref) < 1e-2 and np.max(np.abs(got - ref)) < 3e-2
 
 
-@pytest.mark.parametrize("n_blocks,topk", [(70, 9), (1, 1), (2, 1), (65, 65)])
-def test_attention_ragged_shapes_bf16(n_blocks, topk):
-    """Summary tiles with a ragged tail, a single block, density 1 with a partial tile."""
-    rng = np.random.default_rng(n_blocks)
-    H, N, D = 2, 64 * n_blocks, 128
+@pytest.mark.parametrize("n_blocks,topk,H", [(70, 9, 2), (1, 1, 2), (2, 1, 2), (65, 65, 2),
+                                             (37, 5, 4), (1, 1, 4), (70, 9, 8), (2, 1, 12)])
+def test_attention_ragged_shapes_bf16(n_blocks, topk, H):
+    """Summary tiles with a ragged tail, a single block, density 1 with a partial tile.  With H
+    a multiple of 4 the launch deals each head's query blocks to a pair of XCDs in two halves
+    (an odd block count leaves the second half one block short): every row is still written
+    once."""
+    rng = np.random.default_rng(n_blocks + 1000 * H)
+    N, D = 64 * n_blocks, 128
     q, k, v = (synth.bf16_round(rng.standard_normal((H, N, D)).astype(np.float32) * s)
                for s in (0.3, 1.0, 1.0))
     pq = np.stack([rng.permutation(N) for _ in range(H)]).astype(np.int32)
