@@ -864,6 +864,51 @@ BSA_DEV void project_range(const T* __restrict__ X, const int32_t* __restrict__ 
   }
 }
 
+// project_range with the token ids of up to 16 blocks read ahead into registers, so each
+// chunk of row loads waits for one memory round trip instead of two (ids, then rows).
+template <typename T, int D, int CH = 4>
+BSA_DEV void project_range_ids(const T* __restrict__ X, const int32_t* __restrict__ tokmap,
+                               const float* __restrict__ inv_n, int blk0, int blk1,
+                               const float* w, float* __restrict__ keys,
+                               float* __restrict__ proj_out) {
+  constexpr int E = D / 4;                 // elements per quarter row
+  constexpr int NV = E * sizeof(T) / 16;   // 16-byte pieces per quarter row
+  constexpr int IDS = 16;                  // blocks whose ids are read at once
+  static_assert(IDS % CH == 0, "id groups hold whole chunks");
+  const int tid = threadIdx.x, s = tid >> 2, q = tid & 3;
+  for (int g0 = blk0; g0 < blk1; g0 += IDS) {
+    const int ng = min(IDS, blk1 - g0);
+    int ids[IDS];
+#pragma unroll
+    for (int c = 0; c < IDS; ++c)
+      if (c < ng) ids[c] = tokmap[(g0 + c) * kBlk + s];
+#pragma unroll
+    for (int c0 = 0; c0 < IDS; c0 += CH) {
+      if (c0 >= ng) break;
+      uint4 raw[CH][NV];
+      float sc[CH];
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        if (c0 + c < ng) {
+          const uint4* src = reinterpret_cast<const uint4*>(X + (size_t)ids[c0 + c] * D + q * E);
+#pragma unroll
+          for (int i = 0; i < NV; ++i) raw[c][i] = src[i];
+          sc[c] = inv_n[ids[c0 + c]];
+        }
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        if (c0 + c < ng) {
+          const float a = quarter_dot<T, D>(raw[c], w);
+          if (q == 0) {
+            const float key = a * sc[c];
+            keys[(g0 + c0 + c) * kBlk + s] = key;
+            if (proj_out) proj_out[ids[c0 + c]] = key;
+          }
+        }
+    }
+  }
+}
+
 struct ProblemArgs {
   const void* q;
   const void* k;
@@ -1370,7 +1415,7 @@ BSA_DEV void split_group(const ProblemArgs& a, int p, int level, int g, int b0, 
     power_direction<T, D>(acc, L, M, n, X, pos, inv_n, b0 * kBlk, y_first, a.iters);
   }
   if (threadIdx.x < D) group_mean<D>(a, p, level, g)[threadIdx.x] = L.mu[threadIdx.x];
-  project_range<T, D>(X, pos, inv_n, b0, b0 + m, L.w, keys, problem_proj(a, p, level));
+  project_range_ids<T, D>(X, pos, inv_n, b0, b0 + m, L.w, keys, problem_proj(a, p, level));
   __syncthreads();
   const size_t off = (size_t)b0 * kBlk;
   const int want = (m >> 1) * kBlk;
