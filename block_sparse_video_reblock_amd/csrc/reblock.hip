@@ -1561,7 +1561,9 @@ BSA_DEV void split_duo(const ProblemArgs& a, int p, int level, const DuoGroup& A
   __syncthreads();
   // each half-workgroup takes one group: both of its waves find the threshold (no barrier),
   // then partition together; a half without a group still meets the partition's barriers
-  const int half = tid >> 7;
+  // (read as a wave-uniform value, so that the selects' per-register guards and the inactive
+  // half's skips compile to scalar branches rather than per-lane masking)
+  const int half = __builtin_amdgcn_readfirstlane(tid >> 7);
   const DuoGroup& S = half ? B : A;
   const bool active = half == 0 || two;
   const int n = active ? S.m * kBlk : 0, want = active ? (S.m >> 1) * kBlk : 0;

@@ -331,20 +331,19 @@ BSA_DEV uint32_t wave_select_smallest(const float* keys, int n, int want, int* t
     // padding never counts: no candidate exceeds 0xFFFFFFFF
     k[j] = i < n ? orderable_key(keys[i]) : 0xFFFFFFFFu;
   }
-  const int used = (n + 63) >> 6;  // registers that hold keys (uniform)
+  // (every register is counted: padding never falls below a candidate, and a count costs
+  // less than a branch around it)
   uint32_t T = 0;
   for (int b = 31; b >= 0; --b) {
     const uint32_t c = T | (1u << b);
     int below = 0;
 #pragma unroll
-    for (int j = 0; j < KPL; ++j)
-      if (j < used) below += __popcll(__ballot(k[j] < c));
+    for (int j = 0; j < KPL; ++j) below += __popcll(__ballot(k[j] < c));
     if (below < want) T = c;
   }
   int below = 0;
 #pragma unroll
-  for (int j = 0; j < KPL; ++j)
-    if (j < used) below += __popcll(__ballot(k[j] < T));
+  for (int j = 0; j < KPL; ++j) below += __popcll(__ballot(k[j] < T));
   *take = want - below;
   return T;
 }
