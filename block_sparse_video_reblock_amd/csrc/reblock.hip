@@ -1032,41 +1032,59 @@ __global__ __launch_bounds__(256) void k_moments_finish(const float* __restrict_
 // ---------------------------------------------------------------- metric norms (bf16)
 // inv_n[p][t] = 1 / sqrt(x_t^T M x_t) (0 if that is 0), per-workgroup sums of y = x inv_n and
 // the per-workgroup max |y| (for the scale of the fp16 covariance split).
-// Y^T = M X^T by MFMA with M in three bf16 terms held in registers: wave w owns rows
-// [32w, 32w+32) of M.  The workgroup walks kNormTok tokens in tiles of 64 staged once in LDS
+// The products by M run on MFMA with M in three bf16 terms held in registers (exact bf16
+// inputs, fp32 sums).  The workgroup walks kNormTok tokens in tiles of 64 staged once in LDS
 // (16-byte coalesced loads, the next tile's loads in flight while the current one is used).
 constexpr int kNormTok = 512;
 constexpr int kNormTile = 64;
 constexpr int kNormStride = 136;  // bf16 per LDS row: 4-bank skew between rows
-__global__ __launch_bounds__(256) void k_norms_bf16(ProblemArgs a, const uint16_t* __restrict__ msplit,
-                                                    float* __restrict__ inv_n_out,
-                                                    float* __restrict__ ysum,
-                                                    float* __restrict__ ymax) {
+// x^T M x by symmetry: with M's 32 x 32 blocks M_ab, it is the sum over a <= b of
+// x_a^T M'_ab x_b, M'_aa = M_aa and M'_ab = 2 M_ab for a < b: 10 of the 16 blocks, 20 of the
+// 32 column chunks of 16.  The chunks are dealt five to a wave, so that each wave's chunks fall
+// in at most two row blocks (NormPlan); a wave accumulates (M' x) for those rows and dots them
+// with x.  Against all 16 blocks this is 30 MFMAs per wave and tile instead of 48, and at 168
+// registers three workgroups fit per CU.
+struct NormPlan {
+  // unit u of wave w: row block a, column block b, chunk c (16 columns) within b
+  static constexpr int a[4][5] = {{0, 0, 0, 0, 0}, {0, 0, 0, 1, 1}, {1, 1, 1, 1, 2}, {2, 2, 2, 3, 3}};
+  static constexpr int b[4][5] = {{0, 0, 1, 1, 2}, {2, 3, 3, 1, 1}, {2, 2, 3, 3, 2}, {2, 3, 3, 3, 3}};
+  static constexpr int c[4][5] = {{0, 1, 0, 1, 0}, {1, 0, 1, 0, 1}, {0, 1, 0, 1, 0}, {1, 0, 1, 0, 1}};
+  // row block of accumulator slot s of wave w (-1: unused)
+  static constexpr int slot_a[4][2] = {{0, -1}, {0, 1}, {1, 2}, {2, 3}};
+};
+
+template <int W>
+BSA_DEV void norms_sym_body(const ProblemArgs& a, int p, int chunk, int nch,
+                            const uint16_t* __restrict__ Ms, float* __restrict__ inv_n_out,
+                            float* __restrict__ ysum, float* __restrict__ ymax,
+                            uint16_t (*xs)[kNormStride], float (*red)[kNormTile], float* s_inv,
+                            float (*s_ys)[128], float* s_max) {
   constexpr int D = 128;
-  __shared__ __align__(16) uint16_t xs[kNormTile][kNormStride];
-  __shared__ float red[4][kNormTile];
-  __shared__ float s_inv[kNormTile];
-  __shared__ float s_ys[4][D];
-  __shared__ float s_max[4];
-  const int chunk = blockIdx.x, p = problem_of(a, blockIdx.y), nch = gridDim.x;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 5, l32 = lane & 31;
+  using P = NormPlan;
+  constexpr int NS = P::slot_a[W][1] < 0 ? 1 : 2;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, l32 = lane & 31;
   const uint16_t* X = problem_x<uint16_t, D>(a, p);
-  const int mi = (p >> 1) * 2 + ((p & 1) ? 0 : 1);
-  const uint16_t* Ms = msplit + (size_t)mi * 3 * D * D;
-  bf16x8_t mreg[3][8];
+  // A operands: rows 32 a + l32 of M' (three bf16 terms), columns 32 b + 16 c + 8 g .. + 8
+  bf16x8_t mreg[3][5];
 #pragma unroll
   for (int s = 0; s < 3; ++s)
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-      mreg[s][c] = lds_bf16x8(Ms + (size_t)s * D * D + (32 * w + l32) * D + 16 * c + 8 * g);
+    for (int u = 0; u < 5; ++u) {
+      const uint16_t* src =
+          Ms + (size_t)s * D * D + (32 * P::a[W][u] + l32) * D + 32 * P::b[W][u] + 16 * P::c[W][u] + 8 * g;
+      bf16x8_t v = lds_bf16x8(src);
+      if (P::a[W][u] < P::b[W][u]) {
+        // times two: exact in bf16 (the exponent moves by one)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (__bf16)((float)v[e] * 2.f);
+      }
+      mreg[s][u] = v;
+    }
   const int t0 = chunk * kNormTok, t_end = min(a.N, t0 + kNormTok);  // N is a multiple of 64
-  // tile loads: piece q = tid + 256 i (i < 4) is token q / 16, elements 8 (q % 16) .. + 8.
-  // The next tile is loaded while the current one is used; after the last tile the loads
-  // repeat it (valid memory, unused), so that they need no branch.
   const uint4* xv = reinterpret_cast<const uint4*>(X) + tid;
   uint4 n0 = xv[(size_t)t0 * 16], n1 = xv[(size_t)t0 * 16 + 256], n2 = xv[(size_t)t0 * 16 + 512],
         n3 = xv[(size_t)t0 * 16 + 768];
-  const int d2 = lane;  // this thread's element pair (2 d2, 2 d2 + 1) for the sums of y
+  const int d2 = lane;
   float ys0 = 0.f, ys1 = 0.f, ym = 0.f;
   for (int c0 = t0; c0 < t_end; c0 += kNormTile) {
     *reinterpret_cast<uint4*>(&xs[tid >> 4][8 * (tid & 15)]) = n0;
@@ -1081,39 +1099,44 @@ __global__ __launch_bounds__(256) void k_norms_bf16(ProblemArgs a, const uint16_
       n2 = xv[cn + 512];
       n3 = xv[cn + 768];
     }
-    // tokens l32 and 32 + l32: two independent accumulation chains, interleaved
-    f32x16_t acc0, acc1;
+    f32x16_t acc[NS][2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      acc0[r] = 0.f;
-      acc1[r] = 0.f;
-    }
+    for (int sl = 0; sl < NS; ++sl)
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const bf16x8_t x0 = lds_bf16x8(&xs[l32][16 * c + 8 * g]);
-      const bf16x8_t x1 = lds_bf16x8(&xs[32 + l32][16 * c + 8 * g]);
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[sl][h][r] = 0.f;
+#pragma unroll
+    for (int u = 0; u < 5; ++u) {
+      const int sl = (P::a[W][u] == P::slot_a[W][0]) ? 0 : 1;
+      const int col = 32 * P::b[W][u] + 16 * P::c[W][u] + 8 * g;
+      const bf16x8_t x0 = lds_bf16x8(&xs[l32][col]);
+      const bf16x8_t x1 = lds_bf16x8(&xs[32 + l32][col]);
 #pragma unroll
       for (int s = 0; s < 3; ++s) {
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mreg[s][c], x0, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mreg[s][c], x1, acc1, 0, 0, 0);
+        acc[sl][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mreg[s][u], x0, acc[sl][0], 0, 0, 0);
+        acc[sl][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(mreg[s][u], x1, acc[sl][1], 0, 0, 0);
       }
     }
-    // lane holds (M x_tok)[b] for b = 32w + 8j + 4g + i
+    // lane holds (M' x_tok)[r] for r = 32 a + 8 j + 4 g + i, a the slot's row block
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int tok = 32 * h + l32;
-      const f32x16_t& acc = h ? acc1 : acc0;
       float part = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint2 u = *reinterpret_cast<const uint2*>(&xs[tok][32 * w + 8 * j + 4 * g]);
-        part = fmaf(acc[4 * j + 0], __uint_as_float(u.x << 16), part);
-        part = fmaf(acc[4 * j + 1], __uint_as_float(u.x & 0xFFFF0000u), part);
-        part = fmaf(acc[4 * j + 2], __uint_as_float(u.y << 16), part);
-        part = fmaf(acc[4 * j + 3], __uint_as_float(u.y & 0xFFFF0000u), part);
+      for (int sl = 0; sl < NS; ++sl) {
+        const int ra = 32 * P::slot_a[W][sl];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint2 uu = *reinterpret_cast<const uint2*>(&xs[tok][ra + 8 * j + 4 * g]);
+          part = fmaf(acc[sl][h][4 * j + 0], __uint_as_float(uu.x << 16), part);
+          part = fmaf(acc[sl][h][4 * j + 1], __uint_as_float(uu.x & 0xFFFF0000u), part);
+          part = fmaf(acc[sl][h][4 * j + 2], __uint_as_float(uu.y << 16), part);
+          part = fmaf(acc[sl][h][4 * j + 3], __uint_as_float(uu.y & 0xFFFF0000u), part);
+        }
       }
       part = xor32_sum(part);
-      if (g == 0) red[w][tok] = part;
+      if (g == 0) red[W][tok] = part;
     }
     __syncthreads();
     if (tid < kNormTile) {
@@ -1123,9 +1146,8 @@ __global__ __launch_bounds__(256) void k_norms_bf16(ProblemArgs a, const uint16_
       inv_n_out[(size_t)p * a.N + c0 + tid] = inv;
     }
     __syncthreads();
-    // wave w sums tokens [16w, 16w + 16) of the tile for elements 2 d2, 2 d2 + 1
 #pragma unroll 4
-    for (int t = 16 * w; t < 16 * w + 16; ++t) {
+    for (int t = 16 * W; t < 16 * W + 16; ++t) {
       const uint32_t u = *reinterpret_cast<const uint32_t*>(&xs[t][2 * d2]);
       const float sc = s_inv[t];
       const float y0 = __uint_as_float(u << 16) * sc, y1 = __uint_as_float(u & 0xFFFF0000u) * sc;
@@ -1135,16 +1157,37 @@ __global__ __launch_bounds__(256) void k_norms_bf16(ProblemArgs a, const uint16_
     }
     __syncthreads();
   }
-  s_ys[w][2 * d2] = ys0;
-  s_ys[w][2 * d2 + 1] = ys1;
+  s_ys[W][2 * d2] = ys0;
+  s_ys[W][2 * d2 + 1] = ys1;
   ym = wave_max(ym);
-  if (lane == 0) s_max[w] = ym;
+  if (lane == 0) s_max[W] = ym;
   __syncthreads();
   if (tid < D)
     ysum[((size_t)p * nch + chunk) * D + tid] = (s_ys[0][tid] + s_ys[1][tid]) +
                                                 (s_ys[2][tid] + s_ys[3][tid]);
   if (tid == 0)
     ymax[(size_t)p * nch + chunk] = fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+}
+
+__global__ __launch_bounds__(256, 3) void k_norms_bf16(ProblemArgs a, const uint16_t* __restrict__ msplit,
+                                                    float* __restrict__ inv_n_out,
+                                                    float* __restrict__ ysum,
+                                                    float* __restrict__ ymax) {
+  constexpr int D = 128;
+  __shared__ __align__(16) uint16_t xs[kNormTile][kNormStride];
+  __shared__ float red[4][kNormTile];
+  __shared__ float s_inv[kNormTile];
+  __shared__ float s_ys[4][D];
+  __shared__ float s_max[4];
+  const int chunk = blockIdx.x, p = problem_of(a, blockIdx.y), nch = gridDim.x;
+  const int mi = (p >> 1) * 2 + ((p & 1) ? 0 : 1);
+  const uint16_t* Ms = msplit + (size_t)mi * 3 * D * D;
+  switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
+    case 0: norms_sym_body<0>(a, p, chunk, nch, Ms, inv_n_out, ysum, ymax, xs, red, s_inv, s_ys, s_max); break;
+    case 1: norms_sym_body<1>(a, p, chunk, nch, Ms, inv_n_out, ysum, ymax, xs, red, s_inv, s_ys, s_max); break;
+    case 2: norms_sym_body<2>(a, p, chunk, nch, Ms, inv_n_out, ysum, ymax, xs, red, s_inv, s_ys, s_max); break;
+    default: norms_sym_body<3>(a, p, chunk, nch, Ms, inv_n_out, ysum, ymax, xs, red, s_inv, s_ys, s_max); break;
+  }
 }
 __global__ __launch_bounds__(256) void k_norms_f32(ProblemArgs a, float* __restrict__ inv_n_out,
                                                    float* __restrict__ ysum,
