@@ -870,7 +870,7 @@ template <typename T, int D, int CH = 4>
 BSA_DEV void project_range_ids(const T* __restrict__ X, const int32_t* __restrict__ tokmap,
                                const float* __restrict__ inv_n, int blk0, int blk1,
                                const float* w, float* __restrict__ keys,
-                               float* __restrict__ proj_out) {
+                               float* __restrict__ proj_out, int key_blk0 = 0) {
   constexpr int E = D / 4;                 // elements per quarter row
   constexpr int NV = E * sizeof(T) / 16;   // 16-byte pieces per quarter row
   constexpr int IDS = 16;                  // blocks whose ids are read at once
@@ -901,7 +901,7 @@ BSA_DEV void project_range_ids(const T* __restrict__ X, const int32_t* __restric
           const float a = quarter_dot<T, D>(raw[c], w);
           if (q == 0) {
             const float key = a * sc[c];
-            keys[(g0 + c0 + c) * kBlk + s] = key;
+            keys[(g0 + c0 + c - key_blk0) * kBlk + s] = key;
             if (proj_out) proj_out[ids[c0 + c]] = key;
           }
         }
@@ -1439,10 +1439,12 @@ __global__ __launch_bounds__(1024) void k_wide_split(ProblemArgs a) {
 // of y - shift.  Centres the statistics, stores the centred covariance to cov_out (if given,
 // for the children's right-child statistics), finds the direction, projects the group's
 // positions and partitions them in place (stable, ascending token id within each side).
+constexpr int kPairLdsKeys = 2048;  // keys of a pair-kernel group kept in LDS (8 KB)
+
 template <typename T, int D>
 BSA_DEV void split_group(const ProblemArgs& a, int p, int level, int g, int b0, int m,
                          f32x16_t* acc, float acc_scale, DirLds& L, float* cov_out, int* hist,
-                         int* sm, float y_first) {
+                         int* sm, float y_first, float* skeys) {
   const T* X = problem_x<T, D>(a, p);
   int32_t* pos = problem_pos(a, p);
   int32_t* tmp = a.tmp + (size_t)p * a.N;
@@ -1458,14 +1460,19 @@ BSA_DEV void split_group(const ProblemArgs& a, int p, int level, int g, int b0, 
     power_direction<T, D>(acc, L, M, n, X, pos, inv_n, b0 * kBlk, y_first, a.iters);
   }
   if (threadIdx.x < D) group_mean<D>(a, p, level, g)[threadIdx.x] = L.mu[threadIdx.x];
-  project_range_ids<T, D>(X, pos, inv_n, b0, b0 + m, L.w, keys, problem_proj(a, p, level));
-  __syncthreads();
   const size_t off = (size_t)b0 * kBlk;
+  // the group's keys stay in LDS when they fit (the select and the partition then read them
+  // from there), else in global memory
+  const bool in_lds = n <= kPairLdsKeys;
+  float* kk = in_lds ? skeys : keys + off;
+  project_range_ids<T, D>(X, pos, inv_n, b0, b0 + m, L.w, in_lds ? skeys : keys,
+                          problem_proj(a, p, level), in_lds ? b0 : 0);
+  __syncthreads();
   const int want = (m >> 1) * kBlk;
   int take;
   // keys in global memory: 4 per thread (or 64-key steps) in flight per pass
-  const uint32_t T_ = select_smallest_w<256, 4>(keys + off, n, want, hist, sm, &take);
-  partition_w<256, 4>(keys + off, pos + off, tmp + off, n, want, T_, take, sm);
+  const uint32_t T_ = select_smallest_w<256, 4>(kk, n, want, hist, sm, &take);
+  partition_w<256, 4>(kk, pos + off, tmp + off, n, want, T_, take, sm);
   for (int i = threadIdx.x; i < n; i += 256) pos[off + i] = tmp[off + i];
   __syncthreads();
 }
@@ -1483,6 +1490,7 @@ __global__ __launch_bounds__(256, 2) void k_subtree_pair(ProblemArgs a, int leve
   __shared__ float dsl[D];
   __shared__ int hist[4 * 256];
   __shared__ int sm[16];
+  __shared__ float skeys[kPairLdsKeys];
   const int gp = a.lists[(size_t)(level - 1) * a.G + blockIdx.x], p = problem_of(a, blockIdx.y);
   int pb0, pm;
   group_geom(a.nb, level - 1, gp, pb0, pm);
@@ -1511,7 +1519,8 @@ __global__ __launch_bounds__(256, 2) void k_subtree_pair(ProblemArgs a, int leve
   }
   if (threadIdx.x < D) dsl[threadIdx.x] = L.mu[threadIdx.x];
   __syncthreads();
-  if (lm >= 2) split_group<T, D>(a, p, level, gl, lb0, lm, acc, 1.f, L, nullptr, hist, sm, yl);
+  if (lm >= 2)
+    split_group<T, D>(a, p, level, gl, lb0, lm, acc, 1.f, L, nullptr, hist, sm, yl, skeys);
   if (rm >= 2) {
     const float shr =
         threadIdx.x < D ? shv - dsl[threadIdx.x] * (1.f / float(rm * kBlk)) : 0.f;
@@ -1523,7 +1532,7 @@ __global__ __launch_bounds__(256, 2) void k_subtree_pair(ProblemArgs a, int leve
     sym_stats_range<T, D, true>(X, pos, inv_n, rb0, rb0 + rm, L.shift, shr, ysc, st, sacc, dpart);
     reduce_dpart<D>(dpart, L.red, L.mu);
     sym_to_regs<D>(sacc, inv_s2, st, acc);
-    split_group<T, D>(a, p, level, gr, rb0, rm, acc, 1.f, L, nullptr, hist, sm, yr);
+    split_group<T, D>(a, p, level, gr, rb0, rm, acc, 1.f, L, nullptr, hist, sm, yr, skeys);
   }
 }
 
