@@ -59,49 +59,75 @@ __global__ __launch_bounds__(256) void k_block_means(const T* __restrict__ x,
 }
 
 // S[h][i][j] = scale * qm[h][i] . km[h][j].
+// One 128 x 128 tile of S per workgroup; wave w computes the 64 x 64 quarter (w / 2, w % 2) as
+// four 32 x 32 sub-tiles with v_mfma_f32_32x32x2f32 (fp32 products and sums) over pairs of
+// dimensions.  The dimensions are staged 64 at a time (two passes for D = 128); every
+// element's products are accumulated in the same order as over the whole row.
+constexpr int kScoreTile = 128, kScoreChunk = 64;
 template <int D>
 __global__ __launch_bounds__(256) void k_block_scores(const float* __restrict__ qm,
                                                       const float* __restrict__ km, int nb,
                                                       float scale, float* __restrict__ S) {
-  // one 64 x 64 tile of S per workgroup; wave w computes the 32 x 32 sub-tile (w / 2, w % 2)
-  // with v_mfma_f32_32x32x2f32 (fp32 products and sums) over pairs of dimensions
-  // rows padded to 132 floats: 16-byte aligned for the tile stores, and the MFMA operand reads
+  // rows padded to 68 floats: 16-byte aligned for the tile stores, and the MFMA operand reads
   // (lane: row lane % 32, column lane / 32) fall into 2-way bank groups
-  __shared__ __align__(16) float sq[64][132];
-  __shared__ __align__(16) float sk[64][132];
+  __shared__ __align__(16) float sq[kScoreTile][kScoreChunk + 4];
+  __shared__ __align__(16) float sk[kScoreTile][kScoreChunk + 4];
   const int ti = blockIdx.x, tj = blockIdx.y, h = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  constexpr int V = D / 4;  // float4 per row
-#pragma unroll
-  for (int e = tid; e < 64 * V; e += 256) {
-    const int r = e / V, c = e % V;
-    // rows past nb read row nb - 1 (valid memory) and are zeroed after the load
-    const int i = ti * 64 + r, j = tj * 64 + r;
-    float4 a = reinterpret_cast<const float4*>(qm + ((size_t)h * nb + min(i, nb - 1)) * D)[c];
-    float4 b = reinterpret_cast<const float4*>(km + ((size_t)h * nb + min(j, nb - 1)) * D)[c];
-    if (i >= nb) a = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (j >= nb) b = make_float4(0.f, 0.f, 0.f, 0.f);
-    *reinterpret_cast<float4*>(&sq[r][4 * c]) = a;
-    *reinterpret_cast<float4*>(&sk[r][4 * c]) = b;
-  }
-  __syncthreads();
   const int wi = w >> 1, wj = w & 1;
-  // A[i][k] = query mean 32 wi + i, dimension d + k; B[k][j] = key mean 32 wj + j, same
-  const float* qa = &sq[32 * wi + (lane & 31)][lane >> 5];
-  const float* kb = &sk[32 * wj + (lane & 31)][lane >> 5];
-  f32x16_t acc;
+  constexpr int V = kScoreChunk / 4;  // float4 per staged row
+  f32x16_t acc[2][2];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll 8
-  for (int d = 0; d < D; d += 2)
-    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[d], kb[d], acc, 0, 0, 0);
-  // lane holds S[32 wi + 8 (r/4) + 4 (lane/32) + r%4][32 wj + lane%32]
-  const int j = tj * 64 + 32 * wj + (lane & 31);
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int i = ti * 64 + 32 * wi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-    if (i < nb && j < nb) S[((size_t)h * nb + i) * nb + j] = acc[r] * scale;
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+  for (int d0 = 0; d0 < D; d0 += kScoreChunk) {
+    if (d0 > 0) __syncthreads();  // the previous chunk's operands have been read
+#pragma unroll
+    for (int e = tid; e < kScoreTile * V; e += 256) {
+      const int r = e / V, c = e % V;
+      // rows past nb read row nb - 1 (valid memory) and are zeroed after the load
+      const int i = ti * kScoreTile + r, j = tj * kScoreTile + r;
+      float4 a4 = reinterpret_cast<const float4*>(qm + ((size_t)h * nb + min(i, nb - 1)) * D +
+                                                  d0)[c];
+      float4 b4 = reinterpret_cast<const float4*>(km + ((size_t)h * nb + min(j, nb - 1)) * D +
+                                                  d0)[c];
+      if (i >= nb) a4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j >= nb) b4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      *reinterpret_cast<float4*>(&sq[r][4 * c]) = a4;
+      *reinterpret_cast<float4*>(&sk[r][4 * c]) = b4;
+    }
+    __syncthreads();
+    // A[i][k] = query mean 64 wi + 32 a + i, dimension d0 + d + k; B[k][j] likewise for keys
+#pragma unroll 4
+    for (int d = 0; d < kScoreChunk; d += 2) {
+      float qa[2], kb[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        qa[a] = sq[64 * wi + 32 * a + (lane & 31)][d + (lane >> 5)];
+        kb[a] = sk[64 * wj + 32 * a + (lane & 31)][d + (lane >> 5)];
+      }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[a], kb[b], acc[a][b], 0, 0, 0);
+    }
   }
+  // lane holds S[row0 + 8 (r/4) + 4 (lane/32) + r%4][col0 + lane%32] of sub-tile (a, b)
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int j = tj * kScoreTile + 64 * wj + 32 * b + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = ti * kScoreTile + 64 * wi + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (i < nb && j < nb) S[((size_t)h * nb + i) * nb + j] = acc[a][b][r] * scale;
+      }
+    }
 }
 
 // One wave per row: MSB-first radix select (8-bit digits) of the k-th largest orderable key,
@@ -267,7 +293,7 @@ hipError_t launch_block_means(bool bf16, const void* x, const int32_t* perm, int
 
 hipError_t launch_block_scores(const float* qm, const float* km, int H, int nb, int D,
                                float scale, float* scores, hipStream_t s) {
-  dim3 grid(ceil_div(nb, 64), ceil_div(nb, 64), H);
+  dim3 grid(ceil_div(nb, kScoreTile), ceil_div(nb, kScoreTile), H);
   if (D == 128)
     k_block_scores<128><<<grid, 256, 0, s>>>(qm, km, nb, scale, scores);
   else
