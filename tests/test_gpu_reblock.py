@@ -96,21 +96,27 @@ def test_reblock_bf16_mid(mid, iters, shared, subtree):
 
 @pytest.mark.parametrize("n_blocks,iters,shared,subtree", [
     (600, 8, False, 0), (1134, 8, False, 0), (1134, 2, True, 0),
-    (1134, 2, True, 32), (1134, 2, True, ops.BSA_LITE_SUBTREE_BLOCKS)])
+    (1134, 2, True, 32), (1134, 2, True, ops.BSA_LITE_SUBTREE_BLOCKS), (2200, 8, False, 0)])
 def test_reblock_bf16_narrow_levels(n_blocks, iters, shared, subtree):
     """Enough blocks for the one-workgroup-per-parent levels (left-only statistics, right
     child from the parent's covariance) between the wide levels and the subtree kernel: every
-    split of both sides replayed on the oracle."""
+    split of both sides replayed on the oracle.  At 2,200 blocks the first of those levels has
+    groups of more than 2,048 keys, which the kernel selects and partitions from global memory
+    (smaller groups from LDS).  There (140,800 tokens) the GPU's projections sit up to 6.4e-5
+    from the oracle's, measured, against under 3e-5 up to 72,576 tokens: the wide levels' groups
+    are twice as large and accumulate more fp32 rounding.  The bar for that case is 1e-4, and
+    every split must still agree with the oracle's as in the other cases."""
     rng = np.random.default_rng(n_blocks)
-    wl = synth.WORKLOADS["clip10s_bf16"]
-    q, k, _ = synth.make_qkv(wl, heads=[5])
+    wl = synth.WORKLOADS["clip10s_bf16" if 64 * n_blocks <= 72576 else "max_bf16"]
+    q, k, _ = synth.make_qkv(wl, heads=[5 if wl.name == "clip10s_bf16" else 0])
     sel = np.sort(rng.choice(wl.tokens, size=64 * n_blocks, replace=False))
     q, k = q[:, sel], k[:, sel]
     pq, pk, proj = ops.reblock(to_dev(q, torch.bfloat16), to_dev(k, torch.bfloat16),
                                with_proj=True, power_iters=iters, shared_deep=shared,
                                subtree_blocks=subtree)
     st = _check_layouts(q, k, pq.cpu().numpy(), pk.cpu().numpy(), proj.cpu().numpy(),
-                        tol_proj=3e-5, iters=iters, shared=shared, subtree=subtree)
+                        tol_proj=3e-5 if 64 * n_blocks <= 72576 else 1e-4, iters=iters,
+                        shared=shared, subtree=subtree)
     print("narrow replay", iters, shared, subtree, st)
     assert st["mismatched_splits"] <= 0.02 * st["splits"]
 
