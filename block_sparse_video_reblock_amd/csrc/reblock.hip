@@ -574,23 +574,59 @@ BSA_DEV void sym_to_regs(const SymAcc<D>& sacc, float f, SymStage<D>& st, f32x16
   }
 }
 
+// s += (lane K of this lane's row of 16 in v) * a: v_fmac_f32 with a DPP row broadcast of its
+// first operand (fused, one rounding, as fmaf).  All lanes must be active.
+template <int K>
+BSA_DEV void fmac_row_bcast_k(float& s, float v, float a) {
+  asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+      : "+v"(s)
+      : "v"(v), "v"(a), "n"(K));
+}
+// (k is a constant wherever this is called in an unrolled loop; the switch then folds)
+BSA_DEV void fmac_row_bcast(int k, float& s, float v, float a) {
+  switch (k) {
+    case 0: fmac_row_bcast_k<0>(s, v, a); break;
+    case 1: fmac_row_bcast_k<1>(s, v, a); break;
+    case 2: fmac_row_bcast_k<2>(s, v, a); break;
+    case 3: fmac_row_bcast_k<3>(s, v, a); break;
+    case 4: fmac_row_bcast_k<4>(s, v, a); break;
+    case 5: fmac_row_bcast_k<5>(s, v, a); break;
+    case 6: fmac_row_bcast_k<6>(s, v, a); break;
+    case 7: fmac_row_bcast_k<7>(s, v, a); break;
+    case 8: fmac_row_bcast_k<8>(s, v, a); break;
+    case 9: fmac_row_bcast_k<9>(s, v, a); break;
+    case 10: fmac_row_bcast_k<10>(s, v, a); break;
+    case 11: fmac_row_bcast_k<11>(s, v, a); break;
+    case 12: fmac_row_bcast_k<12>(s, v, a); break;
+    case 13: fmac_row_bcast_k<13>(s, v, a); break;
+    case 14: fmac_row_bcast_k<14>(s, v, a); break;
+    default: fmac_row_bcast_k<15>(s, v, a); break;
+  }
+}
+
 // out = vs * C v for the symmetric register-resident C (column form; v, out 16-byte aligned).
 // red: AC*D floats of LDS (used when a wave does not hold whole columns).
 template <int D>
 BSA_DEV void cov_matvec(const f32x16_t* acc, const float* v, float vs, float* out, float* red) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if constexpr (Cov<D>::FULL_COLS) {
-    // lane: column 32 w + lane % 32, rows 32 t + 8 j + 4 (lane / 32) + {0..3} of every tile t
+    // lane: column 32 w + lane % 32, rows 32 t + 8 j + 4 (lane / 32) + {0..3} of every tile t.
+    // The 16 rows of tile t that a half-wave needs sit one per lane in each of its rows of 16
+    // lanes (vt[t]); each product takes its factor by a DPP row broadcast.
+    const int k = lane & 15;
+    float vt[Cov<D>::TILES];
+#pragma unroll
+    for (int t = 0; t < Cov<D>::TILES; ++t)
+      vt[t] = v[32 * t + 8 * (k >> 2) + 4 * (lane >> 5) + (k & 3)];
     float s[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < Cov<D>::TILES; ++t) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float4 vv = *reinterpret_cast<const float4*>(v + 32 * t + 8 * j + 4 * (lane >> 5));
-        s[j] = fmaf(acc[t][4 * j], vv.x, s[j]);
-        s[j] = fmaf(acc[t][4 * j + 1], vv.y, s[j]);
-        s[j] = fmaf(acc[t][4 * j + 2], vv.z, s[j]);
-        s[j] = fmaf(acc[t][4 * j + 3], vv.w, s[j]);
+        fmac_row_bcast(4 * j, s[j], vt[t], acc[t][4 * j]);
+        fmac_row_bcast(4 * j + 1, s[j], vt[t], acc[t][4 * j + 1]);
+        fmac_row_bcast(4 * j + 2, s[j], vt[t], acc[t][4 * j + 2]);
+        fmac_row_bcast(4 * j + 3, s[j], vt[t], acc[t][4 * j + 3]);
       }
     }
     const float z = xor32_sum((s[0] + s[1]) + (s[2] + s[3]));
@@ -616,48 +652,93 @@ BSA_DEV void cov_matvec(const f32x16_t* acc, const float* v, float vs, float* ou
   }
 }
 
-// M held in registers: thread t owns row t / R, columns [(t % R) * D / R, +D / R), R = 256 / D.
+// M held in registers.  D = 128: R = 2 threads per row, each with W = 64 columns; the threads
+// of one row of 16 lanes share a column half, so that each product takes its factor of v by a
+// DPP row broadcast: lane l of wave w owns row 32 w + 16 (l / 32) + l % 16 and columns
+// [64 ((l / 16) % 2), +64).  D = 64: R = 4, thread t owns row t / 4, columns [(t % 4) 16, +16).
 template <int D>
 struct MRegs {
   static constexpr int R = 256 / D;
   static constexpr int W = D / R;
   float m[W];
+  BSA_DEV static int row_of() {
+    const int l = threadIdx.x & 63;
+    return R == 2 ? 32 * (threadIdx.x >> 6) + 16 * (l >> 5) + (l & 15) : threadIdx.x / R;
+  }
+  BSA_DEV static int col0() {
+    return R == 2 ? W * ((threadIdx.x >> 4) & 1) : (threadIdx.x % R) * W;
+  }
+  // the thread holding the first column half of a row
+  BSA_DEV static bool row_owner() {
+    return R == 2 ? ((threadIdx.x >> 4) & 1) == 0 : threadIdx.x % R == 0;
+  }
   BSA_DEV void load(const float* M) {
-    const int row = threadIdx.x / R, c0 = (threadIdx.x % R) * W;
+    const int row = row_of(), c0 = col0();
 #pragma unroll
     for (int i = 0; i < W; ++i) m[i] = M[row * D + c0 + i];
   }
   // (M v)[row] on every thread of the row's R lanes (v 16-byte aligned LDS)
   BSA_DEV float row_product(const float* v) const {
-    const int c0 = (threadIdx.x % R) * W;
+    const int c0 = col0();
     float s[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (R == 2) {
+      // the 64 factors of this column half, 16 per register, one per lane of a row of 16
+      const int k = threadIdx.x & 15;
+      float u[W / 16];
 #pragma unroll
-    for (int i = 0; i < W; i += 4) {
-      const float4 vv = *reinterpret_cast<const float4*>(v + c0 + i);
-      float& a = s[(i >> 2) & 3];
-      a = fmaf(m[i], vv.x, a);
-      a = fmaf(m[i + 1], vv.y, a);
-      a = fmaf(m[i + 2], vv.z, a);
-      a = fmaf(m[i + 3], vv.w, a);
+      for (int q = 0; q < W / 16; ++q) u[q] = v[c0 + 16 * q + k];
+#pragma unroll
+      for (int i = 0; i < W; i += 4) {
+        float& a = s[(i >> 2) & 3];
+        fmac_row_bcast((i & 15), a, u[i >> 4], m[i]);
+        fmac_row_bcast((i & 15) + 1, a, u[i >> 4], m[i + 1]);
+        fmac_row_bcast((i & 15) + 2, a, u[i >> 4], m[i + 2]);
+        fmac_row_bcast((i & 15) + 3, a, u[i >> 4], m[i + 3]);
+      }
+      // first column half + second, on both (rows of 16 lanes 2c and 2c + 1 exchanged)
+      const float r = (s[0] + s[1]) + (s[2] + s[3]);
+      const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(r), __float_as_uint(r),
+                                                      false, false);
+      return __uint_as_float(x[0]) + __uint_as_float(x[1]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < W; i += 4) {
+        const float4 vv = *reinterpret_cast<const float4*>(v + c0 + i);
+        float& a = s[(i >> 2) & 3];
+        a = fmaf(m[i], vv.x, a);
+        a = fmaf(m[i + 1], vv.y, a);
+        a = fmaf(m[i + 2], vv.z, a);
+        a = fmaf(m[i + 3], vv.w, a);
+      }
+      float r = (s[0] + s[1]) + (s[2] + s[3]);
+      r += dpp_mov<0xB1>(r);  // lane ^ 1
+      r += dpp_mov<0x4E>(r);  // lane ^ 2
+      return r;
     }
-    float r = (s[0] + s[1]) + (s[2] + s[3]);
-    r += dpp_mov<0xB1>(r);                 // lane ^ 1
-    if (R == 4) r += dpp_mov<0x4E>(r);     // lane ^ 2
-    return r;
   }
   BSA_DEV void matvec(const float* v, float* out) const {
     const float s = row_product(v);
-    if (threadIdx.x % R == 0) out[threadIdx.x / R] = s;
+    if (row_owner()) out[row_of()] = s;
     __syncthreads();
   }
   // out = M v, and returns v . out to every thread (sm: 4 floats of LDS).  One barrier.
   BSA_DEV float matvec_dot(const float* v, float* out, float* sm) const {
-    const int row = threadIdx.x / R;
     const float s = row_product(v);
     float d = 0.f;
-    if (threadIdx.x % R == 0) {
-      out[row] = s;
-      d = s * v[row];
+    if constexpr (R == 2) {
+      // the terms s v[row] summed over the wave in the order of a layout with row 32 w + l / 2
+      // on even lane l (and zero on odd lanes)
+      const int l = threadIdx.x & 63, row = row_of();
+      if (row_owner()) out[row] = s;
+      const int r = l >> 1, src = 32 * (r >> 4) + (r & 15);
+      const float sr = __int_as_float(__builtin_amdgcn_ds_bpermute(4 * src, __float_as_int(s)));
+      if ((l & 1) == 0) d = sr * v[32 * (threadIdx.x >> 6) + r];
+    } else {
+      if (row_owner()) {
+        const int row = row_of();
+        out[row] = s;
+        d = s * v[row];
+      }
     }
     d = wave_total(d);
     if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = d;
