@@ -49,7 +49,7 @@ ATTN_SOURCES = ("block_sparse_video_reblock_amd/csrc/attn.hip",
                 "block_sparse_video_reblock_amd/csrc/internal.h")
 ATTN_TRAFFIC = {"source_sha16": "d50ffa2e1cf7a196", "bytes": {
     # key: workload / tail granularity / context tokens / reblock layout / tree
-    "clip10s_bf16/token/0/separate/full": 4.4274e10,
+    "clip10s_bf16/token/0/separate/full": 4.4294e10,
     "clip10s_bf16/block/0/separate/full": 3.7701e10,
     "clip10s_bf16/token/1000/separate/full": 6.0276e10,
     "clip10s_bf16/token/0/q_reuse_k/full": 5.3572e10,
